@@ -1,0 +1,265 @@
+"""fp64 CPU oracle of the batched speculative-sampling verifier.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py``, never by the product path.
+
+Sources (cited by page title and section; no source code from the pages is
+used, every step is restated from the mathematics):
+
+* [nalar] "Speculative decoding: memverifikasi token draft sebelum diterima"
+  (nalar.dev).  Subsections "Draft mengubah tebakan serial menjadi batch
+  verifikasi" (one target pass gives the next-token distribution at every
+  draft position, conditioned on the earlier drafts), "Semantik penerimaan
+  bergantung pada algoritma decoding" (greedy: accept while the draft equals
+  the target's greedy choice, the target's choice replaces the first mismatch;
+  sampling: acceptance probability from p and q, then a correction
+  distribution on rejection) and "Penolakan memendekkan pekerjaan speculative
+  yang berguna" (nothing after the first rejection is committed).
+* [RheoSampling] "RheoSampling 2026: Mengatasi Dilema One-Hot pada Stochastic
+  Dynamic-Tree Speculative Decoding, ..." (newsaint.id).  Section 3 (the draft
+  logits are cut to the 128 largest before the softmax, the rest set to -inf),
+  section 4 (RheoVerification: a candidate is accepted with probability
+  min(1, p/q~) where q~ is its true sampling probability; on rejection the
+  residual norm(max(0, p - q~)) is the distribution sampled next), section 6
+  (Theorem 1: the output distribution equals the target's) and section 7
+  (temperature applies at the verification gate).
+* [Acceptance Is Not Speed] newsaint.id article on arXiv:2610.23818, section 1
+  (lossless speculative decoding keeps the target distribution) and the
+  strict branch of the section 6 harness (q <= p always accepts).
+
+Readings where the pages are silent (each is listed in the design doc):
+
+* uniforms ``u[K+1]``: ``u[i]`` (i < K) drives the acceptance test at
+  position i, ``u[K]`` drives the final (correction or bonus) sample;
+* acceptance is the strict test ``u*q < p``;
+* the final sample is the inverse CDF in ascending token id, taking the
+  smallest x with ``C(x) > t`` (strict), ``t = u[K] * S``;
+* a residual of total mass 0 (possible only through rounding) falls back to
+  the target distribution at that position;
+* ``T <= 0`` selects greedy verification; argmax ties go to the lowest id;
+* top-k keeps exactly k ids, ties at the boundary go to the lowest id; it is
+  applied to the draft only and only for ``T > 0`` rows; ``k <= 0`` or
+  ``k >= V`` means no truncation;
+* a draft token outside ``[0, V)`` has p = q = 0 and is rejected.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+BF16 = "bf16"
+F32 = "f32"
+
+
+def decode_logits(raw, dtype: str) -> np.ndarray:
+    """Widen stored logits to float64 exactly.
+
+    bf16 values arrive as their raw 16-bit patterns (uint16); a bf16 number
+    is the upper half of the float32 with the same bits, so the widening is
+    exact.  float32 values widen exactly to float64.
+    """
+    if dtype == BF16:
+        u16 = np.asarray(raw, dtype=np.uint16)
+        return (u16.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    if dtype == F32:
+        return np.asarray(raw, dtype=np.float32).astype(np.float64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def tempered_softmax(logits: np.ndarray, T: float) -> np.ndarray:
+    """softmax(logits / T) in float64; -inf logits get probability 0.
+
+    Temperature is applied to the logits before the softmax at the
+    verification gate ([RheoSampling] section 7).  The largest scaled logit is
+    subtracted before exponentiation, which leaves the result unchanged.
+    At least one logit must be finite.
+    """
+    z = np.asarray(logits, dtype=np.float64) / float(T)
+    zmax = np.max(z)
+    e = np.exp(z - zmax)
+    return e / np.sum(e)
+
+
+def topk_keep_mask(logits: np.ndarray, k: int) -> np.ndarray:
+    """Boolean mask of the k largest logits, ties at the boundary to the lowest id.
+
+    Sparse draft truncation ([RheoSampling] section 3): only the top
+    candidates of the draft survive; every other logit becomes -inf before the
+    softmax.  ``k <= 0`` or ``k >= V`` keeps everything.  A stable sort of the
+    negated logits orders by value descending and, among equal values, by id
+    ascending; the first k of that order are kept.
+    """
+    logits = np.asarray(logits, dtype=np.float64)
+    V = logits.shape[0]
+    keep = np.ones(V, dtype=bool)
+    if k <= 0 or k >= V:
+        return keep
+    order = np.argsort(-logits, kind="stable")
+    keep[:] = False
+    keep[order[:k]] = True
+    return keep
+
+
+@dataclass
+class RowResult:
+    """Outcome of verifying one row, with the diagnostics the parity tests use.
+
+    tokens      int64 [K+1]: accepted drafts, then the final token, then -1.
+    n           number of accepted drafts (0..K).
+    greedy      True when the row was verified greedily (T <= 0).
+    p_d, q_d    float64 [K]: target / draft probability of each draft token
+                (all K positions, also those after the first rejection);
+                NaN for greedy rows.
+    margins     float64 [K]: |u_i*q_i - p_i| for each position (NaN greedy).
+    S           total mass of the final distribution before normalisation
+                (residual mass after a rejection, 1 for the bonus); NaN greedy.
+    gap         distance from t = u_K*S to the nearer edge of the sampled
+                token's CDF interval (probability units); inf for greedy.
+    fallback    True when a zero residual fell back to the target row.
+    """
+
+    tokens: np.ndarray
+    n: int
+    greedy: bool
+    p_d: np.ndarray
+    q_d: np.ndarray
+    margins: np.ndarray
+    S: float
+    gap: float
+    fallback: bool
+
+    def min_margin(self) -> float:
+        """Smallest margin over the decisions this row actually took.
+
+        Those are the acceptance tests at positions 0..n (position n only if
+        n < K, where it is the rejecting test) and the final inverse-CDF
+        sample.  Greedy decisions compare exact values: margin inf.
+        """
+        if self.greedy:
+            return float("inf")
+        K = self.margins.shape[0]
+        reached = self.margins[: min(self.n + 1, K)]
+        m = float(np.min(reached)) if reached.size else float("inf")
+        return min(m, self.gap)
+
+
+def verify_row(tl, dl, d, u, T: float, k: int = 0) -> RowResult:
+    """Verify one row of K draft tokens against K+1 target positions.
+
+    tl  float64 [K+1, V] target logits; row i is the target's next-token
+        logits after the accepted prefix plus drafts d_0..d_{i-1}
+        ([nalar] "Draft mengubah tebakan serial menjadi batch verifikasi");
+        row K is the bonus position.
+    dl  float64 [K, V] draft logits; row i is the distribution d_i was drawn
+        from (may be None when K == 0 or T <= 0).
+    d   int [K] draft tokens.
+    u   float [K+1] uniforms in [0, 1).
+    T   temperature of this row; T <= 0 selects greedy verification.
+    k   sparse draft truncation (0 = none).
+    """
+    tl = np.asarray(tl, dtype=np.float64)
+    Kp1, V = tl.shape
+    K = Kp1 - 1
+    d = np.asarray(d, dtype=np.int64).reshape(K)
+    u = np.asarray(u, dtype=np.float64).reshape(K + 1)
+    tokens = np.full(K + 1, -1, dtype=np.int64)
+    nanK = np.full(K, np.nan)
+
+    if not (T > 0):
+        # Greedy verification ([nalar] "Semantik penerimaan ..."): a draft is
+        # accepted while it equals the target's greedy choice at its position;
+        # the target's greedy choice replaces the first mismatch, and after K
+        # matches the greedy choice at the bonus position is emitted.
+        # np.argmax returns the first (lowest) id among equal maxima.
+        a = [int(np.argmax(tl[i])) for i in range(K + 1)]
+        n = K
+        for i in range(K):
+            if int(d[i]) != a[i]:
+                n = i
+                break
+        tokens[:n] = d[:n]
+        tokens[n] = a[n]
+        return RowResult(tokens, n, True, nanK, nanK.copy(), nanK.copy(),
+                         float("nan"), float("inf"), False)
+
+    dl = np.zeros((0, V)) if K == 0 else np.asarray(dl, dtype=np.float64).reshape(K, V)
+    P =[tempered_softmax(tl[i], T) for i in range(K + 1)]
+    Q = []
+    for i in range(K):
+        keep = topk_keep_mask(dl[i], k)
+        Q.append(tempered_softmax(np.where(keep, dl[i], -np.inf), T))
+
+    # Acceptance scan ([RheoSampling] section 4, step 1): d_i is accepted
+    # with probability min(1, p_i(d_i)/q_i(d_i)); with u_i uniform this is the
+    # event u_i < p/q, written without a division as u_i*q < p (which also
+    # gives the right limit q = 0).  The first rejection ends the committed
+    # prefix ([nalar] "Penolakan memendekkan ...").
+    p_d = np.zeros(K)
+    q_d = np.zeros(K)
+    margins = np.zeros(K)
+    n = K
+    for i in range(K):
+        tok = int(d[i])
+        if 0 <= tok < V:
+            p_d[i] = P[i][tok]
+            q_d[i] = Q[i][tok]
+        margins[i] = abs(u[i] * q_d[i] - p_d[i])
+    for i in range(K):
+        if not (u[i] * q_d[i] < p_d[i]):
+            n = i
+            break
+
+    # Final distribution ([RheoSampling] section 4, step 3): after a rejection
+    # at position n, the residual max(0, p_n - q_n) (normalised); when every
+    # draft was accepted, the target at the bonus position.
+    fallback = False
+    if n < K:
+        w = np.maximum(0.0, P[n] - Q[n])
+        S = float(np.sum(w))
+        if S == 0.0:
+            w = P[n]
+            S = float(np.sum(w))
+            fallback = True
+    else:
+        w = P[K]
+        S = float(np.sum(w))
+
+    # Inverse-CDF sample with u_K: ascending token id, first x whose
+    # cumulative weight exceeds t = u_K * S.
+    t = u[K] * S
+    C = np.cumsum(w)
+    above = np.flatnonzero(C > t)
+    if above.size:
+        x = int(above[0])
+    else:  # t reached the top only through rounding
+        x = int(np.flatnonzero(w > 0)[-1])
+    lo = C[x - 1] if x > 0 else 0.0
+    gap = float(min(t - lo, C[x] - t))
+
+    tokens[:n] = d[:n]
+    tokens[n] = x
+    return RowResult(tokens, n, False, p_d, q_d, margins, S, gap, fallback)
+
+
+def verify(target_raw, draft_raw, draft_tokens, uniforms, temperature,
+           topk: int, dtype: str, rows=None) -> list[RowResult]:
+    """Verify a batch row by row.
+
+    target_raw  [B, K+1, V] stored logits (uint16 bf16 patterns or float32)
+    draft_raw   [B, K, V] stored logits (may be None if K == 0)
+    draft_tokens int [B, K]; uniforms float [B, K+1]; temperature float [B]
+    rows        optional iterable of row indices (default: all rows)
+    """
+    B = target_raw.shape[0]
+    K = target_raw.shape[1] - 1
+    out = []
+    for b in (range(B) if rows is None else rows):
+        tl = decode_logits(target_raw[b], dtype)
+        T = float(temperature[b])
+        dl = None
+        if K > 0 and T > 0:
+            dl = decode_logits(draft_raw[b], dtype)
+        out.append(verify_row(tl, dl, draft_tokens[b], uniforms[b], T, topk))
+    return out

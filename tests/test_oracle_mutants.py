@@ -1,0 +1,91 @@
+"""The oracle's pins catch plausible mistakes.
+
+Each case plants one mistake in a private copy of the oracle's source (on the
+CPU; the real oracle is untouched), rebinds the pin tests to the mutant and
+requires at least one pin to fail.  This shows the pins are not satisfied by
+a wrong oracle: a flipped residual sign, a reused uniform, a shifted slot
+index, a transposed acceptance ratio, a dropped temperature, an off-by-one
+top-k, a non-strict inverse CDF or a wrong greedy replacement.
+"""
+
+from __future__ import annotations
+
+import sys
+import types
+
+import pytest
+
+import oracle.verifier as ov
+import tests.test_oracle_pins as pins
+
+SRC = open(ov.__file__).read()
+
+MUTANTS = {
+    "residual_sign": ("w = np.maximum(0.0, P[n] - Q[n])", "w = np.maximum(0.0, Q[n] - P[n])"),
+    "reuse_u_n": ("    t = u[K] * S\n    C = np.cumsum(w)", "    t = u[n] * S\n    C = np.cumsum(w)"),
+    "shifted_target_slot": ("p_d[i] = P[i][tok]", "p_d[i] = P[min(i + 1, K)][tok]"),
+    "transposed_ratio": ("if not (u[i] * q_d[i] < p_d[i]):", "if not (u[i] * p_d[i] < q_d[i]):"),
+    "draft_without_temperature": ("Q.append(tempered_softmax(np.where(keep, dl[i], -np.inf), T))",
+                                  "Q.append(tempered_softmax(np.where(keep, dl[i], -np.inf), 1.0))"),
+    "bonus_wrong_slot": ("        w = P[K]\n", "        w = P[max(K - 1, 0)]\n"),
+    "topk_off_by_one": ("keep[order[:k]] = True", "keep[order[:k + 1]] = True"),
+    "topk_ties_highest_id": ("order = np.argsort(-logits, kind=\"stable\")",
+                             "order = (V - 1 - np.argsort(-logits[::-1], kind=\"stable\"))"),
+    "cdf_not_strict": ("above = np.flatnonzero(C > t)", "above = np.flatnonzero(C >= t)"),
+    "temperature_multiplies": ("z = np.asarray(logits, dtype=np.float64) / float(T)",
+                               "z = np.asarray(logits, dtype=np.float64) * float(T)"),
+    "greedy_keeps_draft": ("        tokens[n] = a[n]\n", "        tokens[n] = d[n] if n < K else a[n]\n"),
+    "greedy_tie_highest_id": ("a = [int(np.argmax(tl[i])) for i in range(K + 1)]",
+                              "a = [int(V - 1 - np.argmax(tl[i][::-1])) for i in range(K + 1)]"),
+    "residual_unclipped": ("w = np.maximum(0.0, P[n] - Q[n])", "w = np.abs(P[n] - Q[n])"),
+}
+
+
+def _mutant_module(name):
+    old, new = MUTANTS[name]
+    assert SRC.count(old) == 1, f"mutation anchor for {name} not unique/absent"
+    mod = types.ModuleType(f"oracle_mutant_{name}")
+    mod.__file__ = ov.__file__
+    sys.modules[mod.__name__] = mod        # dataclasses resolve annotations through it
+    try:
+        exec(compile(SRC.replace(old, new), f"<mutant {name}>", "exec"), mod.__dict__)
+    finally:
+        del sys.modules[mod.__name__]
+    return mod
+
+
+def _run_pins():
+    """Run a fixed list of pins; return how many fail."""
+    cases = [
+        lambda: pins.test_lossless_enumeration(5, 3, 1.0, 0, 1),
+        lambda: pins.test_lossless_enumeration(6, 3, 0.8, 3, 4),
+        lambda: pins.test_lossless_enumeration(6, 0, 0.9, 0, 6),
+        lambda: pins.test_greedy_equals_greedy_decode_prefix(5, 3, 11),
+        pins.test_greedy_argmax_tie_lowest_id_and_ignores_uniforms,
+        pins.test_early_rejection_golden,
+        pins.test_softmax_closed_forms,
+        lambda: pins.test_topk_matches_brute_force_rank(5),
+        pins.test_topk_ties_lowest_id_and_degenerate_k,
+        pins.test_zero_weight_token_never_emitted_at_u_zero,
+        pins.test_k0_is_textbook_inverse_cdf,
+        pins.test_residual_never_picks_token_where_p_le_q,
+    ]
+    failed = 0
+    for c in cases:
+        try:
+            c()
+        except Exception:
+            failed += 1
+    return failed
+
+
+def test_unmutated_oracle_passes_the_pin_set():
+    assert _run_pins() == 0
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, monkeypatch):
+    mod = _mutant_module(name)
+    for attr in ("verify_row", "tempered_softmax", "topk_keep_mask", "decode_logits"):
+        monkeypatch.setattr(pins, attr, getattr(mod, attr))
+    assert _run_pins() > 0, f"no pin caught the planted mistake {name!r}"

@@ -1,0 +1,456 @@
+"""Pins of the fp64 oracle against facts the pages and the mathematics fix.
+
+None of these tests touches the GPU.  The central pin is losslessness
+([RheoSampling] section 6, Theorem 1; [Acceptance Is Not Speed] section 1):
+the token sequence the verifier emits is distributed exactly as the target
+model's own autoregressive samples.  It is checked by exhaustive enumeration
+of the uniforms' cells on a tiny, prefix-dependent toy model, evaluating the
+oracle function itself at every cell midpoint.  A dropped term, a wrong sign,
+a shifted slot index or a transposed p/q in the oracle changes the emitted
+distribution and fails it.
+"""
+
+from __future__ import annotations
+
+import itertools
+import math
+import os
+from collections import defaultdict
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import verify_row, tempered_softmax, topk_keep_mask, decode_logits
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- helpers
+def softmax_T(l, T):
+    """The test's own tempered softmax (used to define the toy target)."""
+    l = np.asarray(l, dtype=np.float64)
+    finite = np.isfinite(l)
+    e = np.zeros_like(l)
+    e[finite] = np.exp((l[finite] - l[finite].max()) / T)
+    return e / e.sum()
+
+
+class ToyModel:
+    """Prefix-dependent target and draft logits for every prefix of length <= K."""
+
+    def __init__(self, V, K, T, k=0, seed=0, corr=0.6):
+        self.V, self.K, self.T, self.k = V, K, T, k
+        rng = np.random.default_rng(seed)
+        self.lp, self.lq = {}, {}
+        for L in range(K + 1):
+            for pre in itertools.product(range(V), repeat=L):
+                lp = rng.normal(0.0, 1.5, V)
+                lq = corr * lp + rng.normal(0.0, 1.2, V)
+                self.lp[pre] = lp
+                self.lq[pre] = lq
+
+    def p(self, pre):
+        return softmax_T(self.lp[tuple(pre)], self.T)
+
+    def q(self, pre):
+        lq = self.lq[tuple(pre)]
+        if 0 < self.k < self.V:
+            # brute-force rank: count ids that beat this one (larger value, or
+            # equal value and lower id); kept iff fewer than k beat it
+            keep = np.array([
+                sum((lq[j] > lq[x]) or (lq[j] == lq[x] and j < x) for j in range(self.V)) < self.k
+                for x in range(self.V)])
+            lq = np.where(keep, lq, -np.inf)
+        return softmax_T(lq, self.T)
+
+    def inputs(self, d):
+        K = self.K
+        tl = np.stack([self.lp[tuple(d[:i])] for i in range(K + 1)])
+        dl = np.stack([self.lq[tuple(d[:i])] for i in range(K)]) if K else np.zeros((0, self.V))
+        return tl, dl
+
+
+def enumerate_verifier(model: ToyModel):
+    """Exact output distribution of the oracle over drafts and uniforms.
+
+    Drafts are drawn autoregressively from the (truncated, tempered) draft
+    model; for each draft sequence the unit cube of uniforms splits into
+    cells on which the output is constant: u_i below or above the acceptance
+    probability min(1, p/q) at each reached position, and u_K in one interval
+    per token of the normalised final distribution.  The oracle is evaluated
+    at each cell's midpoint and the cell's measure is credited to its output.
+    """
+    V, K = model.V, model.K
+    dist = defaultdict(float)
+    exp_n = 0.0
+    total = 0.0
+    for d in itertools.product(range(V), repeat=K):
+        wd = 1.0
+        for i in range(K):
+            wd *= model.q(d[:i])[d[i]]
+        if wd == 0.0:
+            continue
+        tl, dl = model.inputs(d)
+        P = [model.p(d[:i]) for i in range(K + 1)]
+        Q = [model.q(d[:i]) for i in range(K)]
+        a = [min(1.0, P[i][d[i]] / Q[i][d[i]]) for i in range(K)]
+        for n in range(K + 1):
+            meas = 1.0
+            u = [0.5] * (K + 1)
+            for i in range(n):
+                meas *= a[i]
+                u[i] = a[i] / 2.0
+            if n < K:
+                meas *= 1.0 - a[n]
+                u[n] = (a[n] + 1.0) / 2.0
+            if meas <= 0.0:
+                continue
+            w = np.maximum(0.0, P[n] - Q[n]) if n < K else P[K].copy()
+            w = w / w.sum()
+            cum = np.cumsum(w)
+            for x in range(V):
+                if w[x] <= 0.0:
+                    continue
+                lo = cum[x - 1] if x else 0.0
+                u[K] = (lo + cum[x]) / 2.0
+                r = verify_row(tl, dl, d, u, model.T, model.k)
+                out = tuple(int(t) for t in r.tokens[: r.n + 1])
+                m = wd * meas * w[x]
+                dist[out] += m
+                exp_n += m * r.n
+                total += m
+    return dist, exp_n, total
+
+
+def check_lossless(model: ToyModel, dist, tol=1e-12):
+    """P(len>=m, t_1..m = s) == P(len>=m, t_<m = s_<m) * p(s_m | s_<m) for all m, s."""
+    K, V = model.K, model.V
+    for m in range(1, K + 2):
+        head = defaultdict(float)   # first m tokens of outputs with len >= m
+        pre = defaultdict(float)    # first m-1 tokens of outputs with len >= m
+        for out, mass in dist.items():
+            if len(out) >= m:
+                head[out[:m]] += mass
+                pre[out[: m - 1]] += mass
+        for s_prev, mass_prev in pre.items():
+            p = model.p(s_prev)
+            for x in range(V):
+                lhs = head.get(s_prev + (x,), 0.0)
+                assert abs(lhs - mass_prev * p[x]) < tol, (m, s_prev, x, lhs, mass_prev * p[x])
+
+
+def expected_n_closed_form(model: ToyModel):
+    """E[n] = sum_j sum_{s in V^j} prod_{i<=j} min(p_i(s_i|s_<i), q_i(s_i|s_<i)).
+
+    Position j is reached and accepted with probability q*min(1, p/q) =
+    min(p, q) at each step, so P(n >= j) is that product summed over s.
+    """
+    V, K = model.V, model.K
+    total = 0.0
+    for j in range(1, K + 1):
+        for s in itertools.product(range(V), repeat=j):
+            prod = 1.0
+            for i in range(j):
+                prod *= min(model.p(s[:i])[s[i]], model.q(s[:i])[s[i]])
+            total += prod
+    return total
+
+
+# ----------------------------------------------------- losslessness (Theorem 1)
+@pytest.mark.parametrize("V,K,T,k,seed", [
+    (5, 3, 1.0, 0, 1),
+    (4, 3, 0.7, 0, 2),
+    (8, 2, 1.3, 0, 3),
+    (6, 3, 0.8, 3, 4),     # sparse draft: q~ keeps the top 3 of 6
+    (8, 2, 1.0, 1, 5),     # k = 1: the draft is one-hot
+    (6, 0, 0.9, 0, 6),     # K = 0: plain sampling from p_0
+])
+def test_lossless_enumeration(V, K, T, k, seed):
+    model = ToyModel(V, K, T, k, seed)
+    dist, exp_n, total = enumerate_verifier(model)
+    assert abs(total - 1.0) < 1e-12
+    check_lossless(model, dist)
+    assert abs(exp_n - expected_n_closed_form(model)) < 1e-12
+
+
+def test_expected_n_prefix_independent_geometric():
+    """With prefix-independent p and q, E[n] = alpha (1 - alpha^K) / (1 - alpha),
+    alpha = sum_x min(p(x), q(x))."""
+    V, K, T = 6, 3, 1.0
+    model = ToyModel(V, K, T, 0, seed=7)
+    lp, lq = model.lp[()], model.lq[()]
+    for key in model.lp:
+        model.lp[key] = lp
+        model.lq[key] = lq
+    alpha = float(np.minimum(softmax_T(lp, T), softmax_T(lq, T)).sum())
+    dist, exp_n, total = enumerate_verifier(model)
+    assert abs(exp_n - alpha * (1 - alpha ** K) / (1 - alpha)) < 1e-12
+    check_lossless(model, dist)
+
+
+# ------------------------------------------------------------------ greedy
+@pytest.mark.parametrize("V,K,seed", [(5, 3, 11), (7, 2, 12), (3, 3, 13)])
+def test_greedy_equals_greedy_decode_prefix(V, K, seed):
+    """T = 0: the output is the greedy decode of the target up to and including
+    the first position where the draft disagrees ([nalar] "Semantik ...")."""
+    model = ToyModel(V, K, 1.0, 0, seed)
+    g = []
+    for i in range(K + 1):
+        g.append(int(np.argmax(model.lp[tuple(g)])))
+    for d in itertools.product(range(V), repeat=K):
+        tl, dl = model.inputs(d)
+        r = verify_row(tl, dl, d, np.full(K + 1, 0.5), 0.0)
+        n = 0
+        while n < K and d[n] == g[n]:
+            n += 1
+        assert r.n == n
+        assert list(r.tokens[: n + 1]) == g[: n + 1]
+        assert all(t == -1 for t in r.tokens[n + 1:])
+
+
+def test_greedy_argmax_tie_lowest_id_and_ignores_uniforms():
+    tl = np.array([[0.0, 2.0, 2.0, 1.0], [5.0, 5.0, 0.0, 0.0]])
+    for u in ([0.0, 0.0], [0.999, 0.3]):
+        r = verify_row(tl, None, [2], u, 0.0)        # draft 2 ties with 1 at the max
+        assert r.n == 0 and list(r.tokens) == [1, -1]
+        r = verify_row(tl, None, [1], u, -1.0)       # T < 0 is greedy too
+        assert r.n == 1 and list(r.tokens) == [1, 0]
+
+
+# ------------------------------------------------------------ worked example
+def test_early_rejection_golden():
+    """[nalar] "Penolakan ...": d1 d2 accepted, d3 rejected, d4 unused."""
+    with open(os.path.join(GOLDEN, "early_rejection.txt")) as f:
+        rows = [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
+    status = [s for _, s in rows]
+    K, V = len(rows), 8
+    d = [1, 2, 3, 4]
+    c = 6
+    ninf = -np.inf
+    tl = np.zeros((K + 1, V))
+    dl = np.zeros((K, V))
+    # positions 0, 1: draft equals target -> ratio 1 -> accepted for any u < 1
+    tl[0] = dl[0] = np.linspace(-1, 1, V)
+    tl[1] = dl[1] = np.linspace(1, -1, V)
+    # position 2: the target gives d3 probability 0 and all mass to c; the
+    # draft is one-hot at d3 -> rejected, residual is one-hot at c
+    tl[2] = ninf
+    tl[2, c] = 0.0
+    dl[2] = ninf
+    dl[2, d[2]] = 0.0
+    tl[3] = dl[3] = 0.0
+    u = [0.3, 0.9, 0.1, 0.5, 0.77]
+    r = verify_row(tl, dl, d, u, 1.0)
+    expected = []
+    n_ok = 0
+    for i, s in enumerate(status):
+        if s == "ok":
+            expected.append(d[i])
+            n_ok += 1
+        elif s == "reject":
+            expected.append(c)
+        else:
+            expected.append(-1)
+    expected.append(-1)  # bonus slot unused after a rejection
+    assert status == ["ok", "ok", "reject", "unused"]
+    assert r.n == n_ok == 2
+    assert list(r.tokens) == expected == [1, 2, 6, -1, -1]
+
+
+# -------------------------------------------------------------- softmax pins
+def test_decode_bf16_exact():
+    bits = np.array([0x3F80, 0xC000, 0xFF80, 0x7F80, 0x3F81, 0x0000, 0x8000, 0x4120], dtype=np.uint16)
+    v = decode_logits(bits, oracle.BF16)
+    assert v[0] == 1.0 and v[1] == -2.0 and v[2] == -np.inf and v[3] == np.inf
+    assert v[4] == 1.0 + 2.0 ** -7 and v[5] == 0.0 and v[6] == 0.0 and v[7] == 10.0
+    f = decode_logits(np.array([0.1], dtype=np.float32), oracle.F32)
+    assert f[0] == float(np.float32(0.1))
+
+
+def test_softmax_closed_forms():
+    p = tempered_softmax(np.array([0.0, math.log(2), math.log(3)]), 1.0)
+    np.testing.assert_allclose(p, [1 / 6, 2 / 6, 3 / 6], rtol=0, atol=1e-15)
+    p2 = tempered_softmax(np.array([0.0, 2 * math.log(2), 2 * math.log(3)]), 2.0)
+    np.testing.assert_allclose(p2, [1 / 6, 2 / 6, 3 / 6], rtol=0, atol=1e-15)
+    assert np.all(tempered_softmax(np.full(7, 3.25), 0.6) == 1.0 / 7)
+    oh = tempered_softmax(np.array([-np.inf, 4.0, -np.inf]), 0.5)
+    assert list(oh) == [0.0, 1.0, 0.0]
+    rng = np.random.default_rng(0)
+    l = rng.normal(0, 3, 1000)
+    p = tempered_softmax(l, 0.7)
+    assert abs(p.sum() - 1.0) < 1e-12
+    np.testing.assert_allclose(tempered_softmax(l + 123.0, 0.7), p, rtol=1e-12, atol=0)
+
+
+# ----------------------------------------------------------------- top-k pins
+@pytest.mark.parametrize("k", [1, 2, 5, 17, 64])
+def test_topk_matches_brute_force_rank(k):
+    rng = np.random.default_rng(k)
+    l = rng.integers(-4, 5, size=97).astype(np.float64)   # many exact ties
+    keep = topk_keep_mask(l, k)
+    beats = np.array([np.sum((l > l[x]) | ((l == l[x]) & (np.arange(97) < x))) for x in range(97)])
+    assert np.array_equal(keep, beats < k)
+    assert keep.sum() == k
+
+
+def test_topk_ties_lowest_id_and_degenerate_k():
+    l = np.array([1.0, 3.0, 3.0, 2.0, 3.0, -np.inf])
+    assert list(np.flatnonzero(topk_keep_mask(l, 2))) == [1, 2]
+    assert list(np.flatnonzero(topk_keep_mask(l, 3))) == [1, 2, 4]
+    assert list(np.flatnonzero(topk_keep_mask(l, 4))) == [1, 2, 3, 4]
+    assert topk_keep_mask(l, 0).all() and topk_keep_mask(l, 6).all() and topk_keep_mask(l, 99).all()
+    assert list(np.flatnonzero(topk_keep_mask(l, 1))) == [1]
+
+
+def test_topk_k1_gives_one_hot_draft():
+    rng = np.random.default_rng(3)
+    tl = rng.normal(0, 1, (2, 9))
+    dl = rng.normal(0, 1, (1, 9))
+    top = int(np.argmax(dl[0]))
+    r = verify_row(tl, dl, [top], [0.5, 0.5], 1.0, k=1)
+    assert r.q_d[0] == 1.0
+    other = (top + 1) % 9
+    r = verify_row(tl, dl, [other], [0.0, 0.5], 1.0, k=1)
+    assert r.q_d[0] == 0.0
+
+
+# ------------------------------------------------------------ acceptance pins
+def test_identical_distributions_accept_everything():
+    rng = np.random.default_rng(5)
+    K, V = 4, 50
+    tl = rng.normal(0, 2, (K + 1, V))
+    dl = tl[:K].copy()
+    for _ in range(50):
+        d = rng.integers(0, V, K)
+        u = rng.random(K + 1)
+        u[:K] = np.minimum(u[:K], 1 - 2.0 ** -24)
+        r = verify_row(tl, dl, d, u, 0.9)
+        assert r.n == K
+
+
+def test_disjoint_supports_reject_first():
+    V, K = 10, 3
+    tl = np.full((K + 1, V), -np.inf)
+    tl[:, :5] = 0.0
+    dl = np.full((K, V), -np.inf)
+    dl[:, 5:] = 0.0
+    for d0 in range(5, 10):
+        for u0 in (0.0, 0.5, 0.999):
+            r = verify_row(tl, dl, [d0, 6, 7], [u0, 0.1, 0.1, 0.4], 1.0)
+            assert r.n == 0
+            assert 0 <= r.tokens[0] < 5        # the correction comes from the target's support
+
+
+def test_confident_draft_does_not_force_acceptance():
+    """[nalar] "Model target tetap menjadi otoritas distribusi": a one-hot draft
+    at d is accepted with probability p(d), not 1."""
+    V = 6
+    tl = np.array([[0.0, math.log(3 / 7), math.log(2 / 7), -1.0, -2.0, -3.0], [0.0] * 6])
+    p_d = softmax_T(tl[0], 1.0)[1]
+    dl = np.full((1, V), -np.inf)
+    dl[0, 1] = 0.0
+    M = 20000
+    acc = sum(verify_row(tl, dl, [1], [(j + 0.5) / M, 0.5], 1.0).n for j in range(M))
+    assert abs(acc / M - p_d) <= 1.0 / M
+
+
+def test_strict_branch_q_le_p_always_accepts():
+    """[Acceptance Is Not Speed] section 6 harness, strict branch: q(d) <= p(d) accepts."""
+    rng = np.random.default_rng(9)
+    V = 12
+    for _ in range(200):
+        tl = rng.normal(0, 2, (2, V))
+        dl = rng.normal(0, 2, (1, V))
+        P = softmax_T(tl[0], 1.1)
+        Q = softmax_T(dl[0], 1.1)
+        for x in np.flatnonzero(Q <= P):
+            for u in (0.0, 0.5, 1 - 2.0 ** -24):
+                assert verify_row(tl, dl, [x], [u, 0.5], 1.1).n == 1
+
+
+def test_out_of_range_draft_token_rejected():
+    tl = np.zeros((3, 4))
+    dl = np.zeros((2, 4))
+    for bad in (-1, 4, 1 << 30):
+        r = verify_row(tl, dl, [0, bad], [0.0, 0.0, 0.5], 1.0)
+        assert r.n == 1 and r.p_d[1] == 0.0 and r.q_d[1] == 0.0
+        assert r.tokens[0] == 0 and 0 <= r.tokens[1] < 4 and r.tokens[2] == -1
+
+
+# -------------------------------------------------------------- residual pins
+def test_residual_mass_is_total_variation():
+    """S = sum max(0, p - q) = 1 - sum min(p, q) after a rejection."""
+    rng = np.random.default_rng(21)
+    V = 40
+    hits = 0
+    for _ in range(200):
+        tl = rng.normal(0, 2, (2, V))
+        dl = rng.normal(0, 2, (1, V))
+        P = softmax_T(tl[0], 0.8)
+        Q = softmax_T(dl[0], 0.8)
+        x = int(np.argmax(Q / np.maximum(P, 1e-300)))   # a draft with q > p
+        r = verify_row(tl, dl, [x], [0.999999, 0.5], 0.8)
+        if r.n == 0:
+            hits += 1
+            assert abs(r.S - (1.0 - np.minimum(P, Q).sum())) < 1e-12
+    assert hits > 100
+
+
+def test_residual_never_picks_token_where_p_le_q():
+    rng = np.random.default_rng(22)
+    V = 30
+    tl = rng.normal(0, 2, (2, V))
+    dl = rng.normal(0, 2, (1, V))
+    P, Q = softmax_T(tl[0], 1.0), softmax_T(dl[0], 1.0)
+    x = int(np.argmax(Q - P))
+    for j in range(2000):
+        r = verify_row(tl, dl, [x], [0.9999999, (j + 0.5) / 2000], 1.0)
+        assert r.n == 0
+        y = r.tokens[0]
+        assert P[y] > Q[y]
+
+
+def test_zero_residual_falls_back_to_target():
+    """u = 1 (outside [0, 1)) with p == q forces a rejection with zero residual."""
+    tl = np.array([[0.0, math.log(3.0)], [0.0, 0.0]])
+    dl = tl[:1].copy()
+    r = verify_row(tl, dl, [0], [1.0, 0.3], 1.0)
+    assert r.n == 0 and r.fallback and r.S == 1.0
+    assert r.tokens[0] == 1          # p = [1/4, 3/4]: t = 0.3 falls in token 1's interval
+
+
+# --------------------------------------------------------------- sampler pins
+def test_k0_is_textbook_inverse_cdf():
+    rng = np.random.default_rng(31)
+    V = 25
+    tl = rng.normal(0, 2, (1, V))
+    P = softmax_T(tl[0], 0.9)
+    for u in rng.random(300):
+        r = verify_row(tl, np.zeros((0, V)), [], [u], 0.9)
+        assert r.n == 0
+        assert r.tokens[0] == np.searchsorted(np.cumsum(P), u, side="right")
+
+
+def test_zero_weight_token_never_emitted_at_u_zero():
+    tl = np.array([[-np.inf, 0.0, 0.0]])
+    r = verify_row(tl, np.zeros((0, 3)), [], [0.0], 1.0)
+    assert r.tokens[0] == 1
+
+
+def test_bonus_after_all_accepted_uses_last_position():
+    V = 4
+    tl = np.zeros((3, V))
+    tl[2] = [-np.inf, -np.inf, -np.inf, 0.0]     # bonus position is one-hot at 3
+    dl = np.zeros((2, V))
+    r = verify_row(tl, dl, [1, 2], [0.5, 0.5, 0.5], 1.0)
+    assert r.n == 2 and list(r.tokens) == [1, 2, 3]
+
+
+def test_margins_and_gap_reported():
+    tl = np.array([[0.0, 0.0], [0.0, 0.0]])
+    dl = np.array([[0.0, -np.inf]])
+    r = verify_row(tl, dl, [0], [0.25, 0.5], 1.0)   # p = 0.5, q = 1
+    assert r.n == 1 and abs(r.margins[0] - 0.25) < 1e-15
+    assert abs(r.gap - 0.0) < 1e-15                  # t = 0.5 sits on the edge between 0 and 1
+    assert r.tokens[1] == 1
