@@ -1,0 +1,239 @@
+"""Throughput of the batched speculative-sampling verifier on one MI355X.
+
+One step = one spec_verify call (statistics pass, residual mass, final draw)
+over one synthetic batch already resident in HBM.  Default workload: B=64
+rows, K=5 drafts, V=151,936 bf16 logits, T=0.6 (dense draft).  Inputs rotate
+over enough identical copies that the 256 MB Infinity Cache cannot serve a
+step's reads from the previous steps.
+
+Prints one JSON line: verified draft positions per second (B*K per step),
+the statistics kernel's achieved HBM bandwidth against the 8 TB/s peak, and
+the fp64 CPU oracle's rate on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--config C] [--no-cpu]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified draft positions/sec at 1 GPU + achieved HBM GB/s vs peak"
+HBM_PEAK_GBPS = 8000.0
+MALL_BYTES = 256 << 20
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "rejection_sampling_verifier_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(d) -> dict:
+    """Bytes the method must move: every target logit once, every draft logit
+    of a sampling row once (greedy rows never read the draft), plus tokens,
+    uniforms, temperatures and outputs."""
+    B, Kp1, V = d["target"].shape
+    K = Kp1 - 1
+    esz = d["target"].itemsize
+    n_sampling = int((d["temperature"] > 0).sum())
+    logits = B * Kp1 * V * esz + n_sampling * K * V * esz
+    small = B * K * 4 + B * Kp1 * 4 + B * 4 + B * Kp1 * 4 + B * 4
+    return {"stats_kernel": logits, "m_min": logits + small}
+
+
+def traffic_from_profiles(workload: str):
+    """HBM bytes per launch of the statistics kernel from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"stats_kernel_{workload}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"kernel_source_hash:\s*(\w+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def cpu_baseline(d, budget_s: float):
+    """The fp64 oracle, as it is, over rows in a thread pool; passes over the
+    whole batch until about budget_s seconds have elapsed."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+
+    B, Kp1, _ = d["target"].shape
+    K = Kp1 - 1
+    threads = min(16, os.cpu_count() or 1)
+
+    def one(b):
+        return oracle.verify(d["target"], d["draft"], d["tokens"], d["uniforms"], d["temperature"],
+                             d["topk"], d["dtype"], rows=[b])
+
+    rows_done = 0
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        while True:
+            list(ex.map(one, range(B)))
+            rows_done += B
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    dt = time.perf_counter() - t0
+    return {"value": rows_done * K / dt, "unit": "positions/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows_done // B} full passes over the {B}-row batch ({rows_done} rows, "
+                      f"{rows_done * K} positions) in {dt:.1f} s, rows spread over {threads} threads"}
+
+
+def copy_calibration(nbytes: int, reps: int):
+    """Plain device-to-device copies of a known size (for counter scaling)."""
+    import torch
+
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=1, help="workload index (1 = default bench line)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="also run plain copies of this many MiB (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(rows shard across GPUs without communication; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads as W
+    import rejection_sampling_verifier_amd as rsv
+
+    case = W.CONFIGS[args.config]
+    t0 = time.perf_counter()
+    d = W.make(case)
+    print(f"[bench] generated {case.name} in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    by = algorithmic_bytes(d)
+    copies = max(1, -(-(2 * MALL_BYTES) // by["m_min"]) + (1 if by["m_min"] < 2 * MALL_BYTES else 0))
+    copies = min(copies, 8)
+
+    def upload(a):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        if a.dtype == np.uint16:
+            t = t.view(torch.bfloat16)
+        return t.to(dev)
+
+    base = {k: upload(d[k]) for k in ("target", "draft", "tokens", "uniforms", "temperature")}
+    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(copies - 1)]
+    B, Kp1, V = base["target"].shape
+    K = Kp1 - 1
+    dt_code = rsv.SV_BF16 if d["dtype"] == "bf16" else rsv.SV_F32
+    ws = torch.empty(rsv.workspace_bytes(B, K, V, d["topk"], dt_code), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    nacc = torch.empty((B,), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, timer=None):
+        x = sets[i % copies]
+        fn = timer.run if timer is not None else rsv.verify
+        fn(x["target"], x["draft"], x["tokens"], x["uniforms"], x["temperature"], d["topk"],
+           out_tokens=out, num_accepted=nacc, workspace=ws, stream=stream.cuda_stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # Timed region 1: plain calls, bracketed by events and wall clock.
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - w0) * 1e3
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+
+    # Timed region 2: the same calls with HIP events between the stages, on
+    # the stream the kernels run on, for the per-kernel durations.
+    timers = [rsv.StageTimer() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, timers[i])
+    torch.cuda.synchronize()
+    stages = np.array([t.stage_ms() for t in timers])
+    for t in timers:
+        t.close()
+    stage_ms = stages.mean(axis=0)
+    stats_ms = float(stage_ms[0])
+
+    accepted = float(nacc.float().mean().item())
+    positions = B * K
+    value = positions / (ms_per_step * 1e-3)
+    achieved = by["stats_kernel"] / (stats_ms * 1e-3) / 1e9
+    traffic = traffic_from_profiles(case.name.split("-T")[0] if False else f"B{B}K{K}V{V}")
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": case.name, "B": B, "K": K, "V": V, "logits": d["dtype"],
+                   "temperature": float(case.temperature), "greedy_rows": case.greedy_rows,
+                   "topk_draft": case.topk, "input_copies": copies},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "kernel": "stats_kernel",
+                     "bytes_per_launch": by["stats_kernel"], "avg_launch_ms": round(stats_ms, 5)},
+        "effective_GBps_whole_call": round(by["m_min"] / (ms_per_step * 1e-3) / 1e9, 1),
+        "m_min_bytes": by["m_min"],
+        "stage_ms": {"stats": round(float(stage_ms[0]), 5), "topk_merge": round(float(stage_ms[1]), 5),
+                     "residual": round(float(stage_ms[2]), 5), "sample": round(float(stage_ms[3]), 5)},
+        "wall_ms_per_step": round(wall_ms / args.steps, 5),
+        "mean_accepted": round(accepted, 4),
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if args.copy_calibration_mb:
+        copy_calibration(args.copy_calibration_mb << 20, 5)
+    if not args.no_cpu:
+        print("[bench] timing the CPU oracle ...", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(d, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,156 @@
+/*
+ * spec_verify.h - batched speculative-sampling verifier for AMD MI355X (gfx950).
+ *
+ * One call verifies B rows of K draft tokens against one target pass:
+ *
+ *   - The target scored the prefix extended by the drafts in a single pass,
+ *     so it provides K+1 next-token distributions per row: position i is
+ *     conditioned on drafts d_0..d_{i-1}, position K is the bonus position
+ *     ("Speculative decoding: memverifikasi token draft sebelum diterima",
+ *     subsection "Draft mengubah tebakan serial menjadi batch verifikasi").
+ *   - Both logit sets are turned into probabilities by softmax(l / T), the
+ *     temperature acting at the verification gate (RheoSampling 2026,
+ *     section 7).  The draft may first be cut to its topk_draft largest
+ *     logits, the rest set to -inf, ties at the cut to the lowest id
+ *     (RheoSampling 2026, section 3).
+ *   - Draft d_i is accepted when u_i < min(1, p_i(d_i) / q_i(d_i)), evaluated
+ *     as u_i * q < p; the first rejection ends the committed prefix
+ *     (RheoSampling 2026, section 4, step 1; "Speculative decoding: ...",
+ *     subsection "Penolakan memendekkan pekerjaan speculative yang berguna").
+ *   - After a rejection at position n the final token is drawn from
+ *     norm(max(0, p_n - q_n)); if all K drafts are accepted it is drawn from
+ *     the bonus position p_K (RheoSampling 2026, section 4, step 3).  The
+ *     draw is an inverse CDF in ascending token id with uniform u_K: the
+ *     smallest x whose cumulative weight exceeds u_K * (total weight).
+ *   - A row with T <= 0 is verified greedily: drafts are accepted while they
+ *     equal the target's argmax (lowest id among equal maxima), and the
+ *     target's argmax at the first mismatch (or at the bonus position) is
+ *     emitted ("Speculative decoding: ...", subsection "Semantik penerimaan
+ *     bergantung pada algoritma decoding").  Uniforms and draft logits of
+ *     such rows are not read.
+ *
+ * All pointers are device pointers owned by the caller.  Inputs are read
+ * only; outputs are fully overwritten.  The library allocates nothing, keeps
+ * no mutable global state and never synchronises: every call only enqueues
+ * kernels on `stream`; outputs are valid once the caller has synchronised
+ * that stream.  Calls on different workspaces are reentrant.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage type of both logit tensors. */
+typedef enum { SV_BF16 = 0, SV_F32 = 1 } sv_dtype;
+
+/* Return codes.  No call prints, throws or aborts. */
+typedef enum {
+  SV_OK = 0,
+  SV_ERR_ARG = 1,          /* bad scalar or a NULL pointer that is required      */
+  SV_ERR_WORKSPACE = 2,    /* *workspace_bytes smaller than the size required    */
+  SV_ERR_UNSUPPORTED = 3,  /* 0 < topk_draft < V with topk_draft > SV_MAX_TOPK, or */
+                           /* K > SV_MAX_K                                        */
+  SV_ERR_HIP = 4           /* a kernel launch failed (hipGetLastError)           */
+} sv_status;
+
+#define SV_MAX_TOPK 1024
+#define SV_MAX_K 64
+
+/*
+ * spec_verify - verify B rows; see the description at the top of this file.
+ *
+ * target_logits  [B, K+1, V] device, dtype, row-major contiguous.
+ * draft_logits   [B, K, V]   device, dtype, row-major contiguous; may be NULL
+ *                when K == 0.
+ * draft_tokens   [B, K] int32 device; may be NULL when K == 0.  A token outside
+ *                [0, V) has p = q = 0 and is rejected.
+ * uniforms       [B, K+1] float32 device, each in [0, 1).  u[b][i] (i < K)
+ *                drives the acceptance test at position i; u[b][K] drives the
+ *                final (correction or bonus) draw.
+ * temperature    [B] float32 device; T <= 0 (or NaN) selects greedy for the row.
+ * B >= 1, K in [0, SV_MAX_K], V >= 1.
+ * topk_draft     0 or >= V: dense draft; otherwise keep the topk_draft largest
+ *                draft logits per position (at most SV_MAX_TOPK).
+ * dtype          sv_dtype of both logit tensors.
+ * out_tokens     [B, K+1] int32 device: accepted drafts, the final token,
+ *                then -1 padding.
+ * num_accepted   [B] int32 device: number of accepted drafts, 0..K.
+ * workspace      device scratch of at least *workspace_bytes bytes, 256-byte
+ *                aligned; NULL requests the size only: *workspace_bytes is set
+ *                to the size required and nothing is launched.
+ * workspace_bytes in: bytes available at workspace; out (size query): bytes
+ *                required.  Must not be NULL.
+ * stream         HIP stream to enqueue on (0 = null stream).
+ *
+ * Device data is not validated (that would need a synchronisation): logits
+ * that are all -inf in a position, or NaN anywhere, give unspecified tokens
+ * but every memory access stays in bounds.
+ */
+int spec_verify(const void* target_logits, const void* draft_logits,
+                const int32_t* draft_tokens, const float* uniforms,
+                const float* temperature, int B, int K, int V, int topk_draft,
+                int dtype, int32_t* out_tokens, int32_t* num_accepted,
+                void* workspace, size_t* workspace_bytes, hipStream_t stream);
+
+/*
+ * spec_verify_probe - spec_verify plus diagnostics, for parity tests.  Not
+ * part of the serving API.
+ *
+ * probs_out  [B, K, 2] float32 device or NULL: (p_i(d_i), q_i(d_i)) for every
+ *            position i < K of sampling rows (also after the first
+ *            rejection); 0 for greedy rows.
+ * mass_out   [B] float32 device or NULL: total weight S of the distribution
+ *            the final token was drawn from (residual mass after a rejection,
+ *            about 1 for the bonus); 0 for greedy rows.
+ * Other arguments and return codes as spec_verify.
+ */
+int spec_verify_probe(const void* target_logits, const void* draft_logits,
+                      const int32_t* draft_tokens, const float* uniforms,
+                      const float* temperature, int B, int K, int V,
+                      int topk_draft, int dtype, int32_t* out_tokens,
+                      int32_t* num_accepted, void* workspace,
+                      size_t* workspace_bytes, hipStream_t stream,
+                      float* probs_out, float* mass_out);
+
+/*
+ * spec_verify_timed - spec_verify that also records HIP events between its
+ * kernel launches, for measuring each stage on the caller's stream.
+ *
+ * events     array of n_events events created by the caller (hipEventCreate).
+ *            events[0] is recorded before the first launch and events[j]
+ *            after stage j (1 = statistics pass, 2 = top-k merge, 3 = residual
+ *            mass, 4 = final draw); stages that do not run still record their
+ *            event so indices stay fixed.  n_events must be 0 or 5.
+ * Other arguments and return codes as spec_verify.
+ */
+int spec_verify_timed(const void* target_logits, const void* draft_logits,
+                      const int32_t* draft_tokens, const float* uniforms,
+                      const float* temperature, int B, int K, int V,
+                      int topk_draft, int dtype, int32_t* out_tokens,
+                      int32_t* num_accepted, void* workspace,
+                      size_t* workspace_bytes, hipStream_t stream,
+                      hipEvent_t* events, int n_events);
+
+/*
+ * spec_verify_plan - the vocabulary split the library would use for a shape:
+ * *chunks vocabulary chunks per (row, position), each *chunk_len ids long
+ * (the last one may be shorter).  For tests that need inputs spanning several
+ * chunks and a ragged tail.  Returns SV_OK or SV_ERR_ARG / SV_ERR_UNSUPPORTED.
+ */
+int spec_verify_plan(int B, int K, int V, int topk_draft, int dtype,
+                     int* chunks, int* chunk_len);
+
+/* Static description of a status code (never NULL). */
+const char* spec_verify_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

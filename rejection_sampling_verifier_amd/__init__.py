@@ -1,0 +1,21 @@
+"""Batched speculative-sampling verifier for AMD MI355X (gfx950).
+
+The work happens in ``libspecverify.so`` (hand-written HIP kernels behind a C
+ABI, declared in ``include/spec_verify.h``).  ``binding`` marshals torch
+tensors to that ABI; it never computes anything itself and fails loudly when
+the library is missing.
+"""
+
+from .binding import (  # noqa: F401
+    SV_BF16,
+    SV_F32,
+    SV_MAX_K,
+    SV_MAX_TOPK,
+    SpecVerifyError,
+    StageTimer,
+    load_library,
+    plan,
+    verify,
+    verify_probe,
+    workspace_bytes,
+)

@@ -1,0 +1,207 @@
+"""ctypes binding of libspecverify.so: torch tensors in, device pointers out.
+
+Argument marshalling only.  Every step of the verifier runs in the library's
+HIP kernels; torch provides the device memory and the current HIP stream.
+If the library has not been built the calls raise instead of computing
+anything another way.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libspecverify.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "spec_verify.h")
+
+SV_BF16, SV_F32 = 0, 1
+SV_OK, SV_ERR_ARG, SV_ERR_WORKSPACE, SV_ERR_UNSUPPORTED, SV_ERR_HIP = 0, 1, 2, 3, 4
+
+
+def _header_define(name: str) -> int:
+    with open(HEADER) as f:
+        m = re.search(rf"#define\s+{name}\s+(\d+)", f.read())
+    return int(m.group(1))
+
+
+SV_MAX_TOPK = _header_define("SV_MAX_TOPK")
+SV_MAX_K = _header_define("SV_MAX_K")
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"spec_verify failed: {msg} (status {status})")
+        self.status = status
+
+
+_lib = None
+_vp, _i32, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)
+_COMMON = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp]
+
+
+def load_library(path: str | None = None):
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(
+            f"{p} is missing: build it with `python -m rejection_sampling_verifier_amd.build` "
+            "(there is no fallback implementation)")
+    lib = ctypes.CDLL(p)
+    lib.spec_verify.argtypes = _COMMON
+    lib.spec_verify.restype = _i32
+    lib.spec_verify_probe.argtypes = _COMMON + [_vp, _vp]
+    lib.spec_verify_probe.restype = _i32
+    lib.spec_verify_timed.argtypes = _COMMON + [ctypes.POINTER(_vp), _i32]
+    lib.spec_verify_timed.restype = _i32
+    lib.spec_verify_plan.argtypes = [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32)]
+    lib.spec_verify_plan.restype = _i32
+    lib.spec_verify_status_string.argtypes = [_i32]
+    lib.spec_verify_status_string.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != SV_OK:
+        msg = load_library().spec_verify_status_string(status).decode()
+        raise SpecVerifyError(status, msg)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SV_BF16
+    if t.dtype == torch.float32:
+        return SV_F32
+    raise TypeError(f"logits must be bfloat16 or float32, got {t.dtype}")
+
+
+def plan(B: int, K: int, V: int, topk_draft: int = 0, dtype: int = SV_BF16):
+    """(chunks, chunk_len) of the vocabulary split used for this shape."""
+    c, L = ctypes.c_int(0), ctypes.c_int(0)
+    _check(load_library().spec_verify_plan(B, K, V, topk_draft, dtype, ctypes.byref(c), ctypes.byref(L)))
+    return c.value, L.value
+
+
+def workspace_bytes(B: int, K: int, V: int, topk_draft: int = 0, dtype: int = SV_BF16) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().spec_verify(None, None, None, None, None, B, K, V, topk_draft, dtype,
+                                      None, None, None, ctypes.byref(n), None))
+    return n.value
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _prepare(target, draft, draft_tokens, uniforms, temperature, topk_draft, out_tokens,
+             num_accepted, workspace, stream):
+    if target.dim() != 3:
+        raise ValueError("target_logits must be [B, K+1, V]")
+    B, Kp1, V = target.shape
+    K = Kp1 - 1
+    dev = target.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    dt = _dtype_code(target)
+    tensors = [("target_logits", target, (B, K + 1, V), target.dtype),
+               ("uniforms", uniforms, (B, K + 1), torch.float32),
+               ("temperature", temperature, (B,), torch.float32)]
+    if K > 0:
+        tensors += [("draft_logits", draft, (B, K, V), target.dtype),
+                    ("draft_tokens", draft_tokens, (B, K), torch.int32)]
+    for name, t, shape, dtype in tensors:
+        if t is None or tuple(t.shape) != shape or t.dtype != dtype or t.device != dev or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {shape} on {dev}")
+    if out_tokens is None:
+        out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    if num_accepted is None:
+        num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    nbytes = workspace_bytes(B, K, V, topk_draft, dt)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    ws_n = ctypes.c_size_t(workspace.numel() * workspace.element_size())
+    args = [_ptr(target), _ptr(draft) if K > 0 else None, _ptr(draft_tokens) if K > 0 else None,
+            _ptr(uniforms), _ptr(temperature), B, K, V, topk_draft, dt, _ptr(out_tokens),
+            _ptr(num_accepted), _ptr(workspace), ctypes.byref(ws_n), ctypes.c_void_p(stream)]
+    keep = (target, draft, draft_tokens, uniforms, temperature, workspace)
+    return args, out_tokens, num_accepted, keep
+
+
+def verify(target, draft, draft_tokens, uniforms, temperature, topk_draft: int = 0, *,
+           out_tokens=None, num_accepted=None, workspace=None, stream=None):
+    """Enqueue spec_verify on the current (or given) stream.
+
+    Returns (out_tokens [B, K+1] int32, num_accepted [B] int32); valid after
+    the stream is synchronised.
+    """
+    args, out_tokens, num_accepted, _ = _prepare(target, draft, draft_tokens, uniforms, temperature,
+                                                 topk_draft, out_tokens, num_accepted, workspace, stream)
+    _check(load_library().spec_verify(*args))
+    return out_tokens, num_accepted
+
+
+def verify_probe(target, draft, draft_tokens, uniforms, temperature, topk_draft: int = 0, *,
+                 workspace=None, stream=None):
+    """spec_verify_probe: also returns probs [B, K, 2] = (p_i(d_i), q_i(d_i))
+    and mass [B] = weight of the distribution the final token was drawn from."""
+    args, out_tokens, num_accepted, _ = _prepare(target, draft, draft_tokens, uniforms, temperature,
+                                                 topk_draft, None, None, workspace, stream)
+    B, Kp1 = out_tokens.shape
+    probs = torch.empty((B, Kp1 - 1, 2), dtype=torch.float32, device=target.device)
+    mass = torch.empty((B,), dtype=torch.float32, device=target.device)
+    _check(load_library().spec_verify_probe(*args, _ptr(probs), _ptr(mass)))
+    return out_tokens, num_accepted, probs, mass
+
+
+class StageTimer:
+    """Five HIP events recorded by spec_verify_timed around its stages.
+
+    ``run(...)`` enqueues one verification; ``stage_ms()`` (after the stream is
+    synchronised) returns the duration of each stage in milliseconds:
+    [statistics, top-k merge, residual mass, final draw].
+    """
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(_vp)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), _vp, _vp]
+        self.hip.hipEventDestroy.argtypes = [_vp]
+        self.events = (_vp * 5)()
+        for i in range(5):
+            ev = _vp()
+            if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.events[i] = ev
+
+    def run(self, target, draft, draft_tokens, uniforms, temperature, topk_draft=0, *,
+            out_tokens=None, num_accepted=None, workspace=None, stream=None):
+        args, out_tokens, num_accepted, _ = _prepare(target, draft, draft_tokens, uniforms, temperature,
+                                                     topk_draft, out_tokens, num_accepted, workspace,
+                                                     stream)
+        _check(load_library().spec_verify_timed(*args, self.events, 5))
+        return out_tokens, num_accepted
+
+    def stage_ms(self):
+        out = []
+        for i in range(4):
+            ms = ctypes.c_float(0.0)
+            if self.hip.hipEventElapsedTime(ctypes.byref(ms), self.events[i], self.events[i + 1]) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            out.append(ms.value)
+        return out
+
+    def close(self):
+        for i in range(5):
+            if self.events[i]:
+                self.hip.hipEventDestroy(self.events[i])
+                self.events[i] = None

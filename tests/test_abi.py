@@ -1,0 +1,95 @@
+"""Host-side checks of the C ABI: symbols, plan, workspace query, error codes.
+
+Nothing here launches a kernel: every call returns before the first launch.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from rejection_sampling_verifier_amd import binding as B
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "spec_verify.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\**\s*(spec_verify\w*)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    lib = B.load_library()
+    names = declared_functions()
+    assert {"spec_verify", "spec_verify_probe", "spec_verify_timed", "spec_verify_plan",
+            "spec_verify_status_string"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    lib = B.load_library()
+    for code in range(6):
+        assert lib.spec_verify_status_string(code)
+    assert lib.spec_verify_status_string(B.SV_OK) == b"ok"
+
+
+@pytest.mark.parametrize("V", [1, 7, 100, 1000, 1001, 16384, 16385, 40001, 128256, 151936, 201088])
+@pytest.mark.parametrize("dtype", [B.SV_BF16, B.SV_F32])
+def test_plan_covers_vocabulary(V, dtype):
+    C, L = B.plan(4, 3, V, 0, dtype)
+    vec = 8 if dtype == B.SV_BF16 else 4
+    assert L % vec == 0 and C >= 1
+    assert (C - 1) * L < V <= C * L
+    assert L <= 256 * 8 * vec
+
+
+def test_workspace_query_grows_with_shape():
+    small = B.workspace_bytes(4, 4, 1024, 0, B.SV_F32)
+    big = B.workspace_bytes(256, 7, 201088, 0, B.SV_BF16)
+    assert 0 < small < big
+    assert small % 256 == 0 and big % 256 == 0
+
+
+def _call(lib, B_=4, K=3, V=1000, topk=0, dtype=B.SV_BF16, ptrs=True, ws=None, ws_n=None):
+    p = ctypes.c_void_p(0x100000) if ptrs else None
+    n = None if ws_n is None else ctypes.byref(ctypes.c_size_t(ws_n))
+    return lib.spec_verify(p, p, p, p, p, B_, K, V, topk, dtype, p, p, ws, n, None)
+
+
+def test_argument_errors_without_launch():
+    lib = B.load_library()
+    need = B.workspace_bytes(4, 3, 1000, 0, B.SV_BF16)
+    ws = ctypes.c_void_p(0x200000)
+    assert _call(lib, B_=0, ws=ws, ws_n=need) == B.SV_ERR_ARG
+    assert _call(lib, K=-1, ws=ws, ws_n=need) == B.SV_ERR_ARG
+    assert _call(lib, V=0, ws=ws, ws_n=need) == B.SV_ERR_ARG
+    assert _call(lib, topk=-3, ws=ws, ws_n=need) == B.SV_ERR_ARG
+    assert _call(lib, dtype=7, ws=ws, ws_n=need) == B.SV_ERR_ARG
+    assert _call(lib, ws=ws, ws_n=None) == B.SV_ERR_ARG                     # no size pointer
+    assert _call(lib, ws=ws, ws_n=need - 1) == B.SV_ERR_WORKSPACE
+    assert _call(lib, ptrs=False, ws=ws, ws_n=need) == B.SV_ERR_ARG         # NULL tensors
+    assert _call(lib, ws=ctypes.c_void_p(0x200010), ws_n=need) == B.SV_ERR_ARG  # misaligned
+    assert _call(lib, K=B.SV_MAX_K + 1, ws=ws, ws_n=1 << 40) == B.SV_ERR_UNSUPPORTED
+
+
+def test_size_query_launches_nothing_and_accepts_null_tensors():
+    lib = B.load_library()
+    n = ctypes.c_size_t(0)
+    rc = lib.spec_verify(None, None, None, None, None, 64, 5, 151936, 0, B.SV_BF16,
+                         None, None, None, ctypes.byref(n), None)
+    assert rc == B.SV_OK and n.value > 0
+
+
+def test_topk_at_or_above_vocab_is_dense():
+    assert B.workspace_bytes(4, 3, 500, 500, B.SV_BF16) == B.workspace_bytes(4, 3, 500, 0, B.SV_BF16)
+    assert B.workspace_bytes(4, 3, 500, 10**6, B.SV_BF16) == B.workspace_bytes(4, 3, 500, 0, B.SV_BF16)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError, match="no fallback"):
+        B.load_library(str(tmp_path / "absent.so"))

@@ -1,0 +1,166 @@
+"""GPU parity: the HIP verifier against the fp64 oracle on identical seeded inputs.
+
+Runs through the C ABI (ctypes binding).  Sizes span several vocabulary
+chunks with ragged tails; the five workloads run at full size with the oracle
+on a sample of rows plus structural checks on every row.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from rejection_sampling_verifier_amd import plan, verify, SV_BF16, SV_F32
+from tests.parity import check_rows, check_well_formed, run_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _case(**kw):
+    base = dict(B=6, K=3, V=40000, dtype=W.BF16, draft_sigma=0.8, temperature=0.9, seed=7)
+    base.update(kw)
+    return W.Case(**base)
+
+
+SMALL = {
+    "bf16-3chunks": _case(),
+    "bf16-ragged-unaligned": _case(V=40001, seed=8),
+    "bf16-ragged-aligned": _case(V=40008, seed=9),
+    "f32-3chunks-ragged": _case(dtype=W.F32, V=20001, seed=10),
+    "f32-aligned": _case(dtype=W.F32, V=16384 + 4, seed=11),
+    "tiny-V": _case(V=100, peaks=3, seed=12),
+    "V1": _case(V=1, peaks=0, seed=13),
+    "V7-unaligned": _case(V=7, peaks=0, seed=14),
+    "K0": _case(K=0, seed=15),
+    "B1-K1": _case(B=1, K=1, seed=16),
+    "K12": _case(K=12, V=5000, seed=17),
+    "mixed-greedy": _case(B=12, greedy_rows=6, seed=18),
+    "all-greedy": _case(B=5, greedy_rows=5, seed=19),
+    "hot-T": _case(B=32, temperature=4.0, seed=20),     # flat: most CDF gaps < 1e-5
+    "cold-T": _case(temperature=0.05, seed=21),
+    "low-agreement": _case(draft_sigma=3.0, seed=22),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_small_cases_match_oracle(name):
+    case = SMALL[name]
+    d = W.make(case)
+    C, L = plan(case.B, case.K, case.V, case.topk, SV_BF16 if case.dtype == W.BF16 else SV_F32)
+    _log(f"[parity] {name}: B={case.B} K={case.K} V={case.V} {case.dtype} chunks={C}x{L}")
+    st = {}
+    near = check_rows(d, run_gpu(d), stats=st)
+    _log(f"[parity] {name}: near-boundary rows {near}/{case.B} ({st['near_equal']} equal anyway)")
+    assert near < case.B, "no row was compared exactly"
+
+
+def test_config0_full():
+    d = W.make(0)
+    near = check_rows(d, run_gpu(d))
+    _log(f"[parity] config0: near-boundary rows {near}/4")
+
+
+def _edge_inputs(V=3000, K=3, B=4, dtype=W.BF16, seed=30):
+    return W.make(_case(B=B, K=K, V=V, dtype=dtype, seed=seed))
+
+
+def test_out_of_range_draft_tokens_are_rejected():
+    d = _edge_inputs()
+    V = d["target"].shape[2]
+    d["tokens"][0, 0] = -1
+    d["tokens"][1, 1] = V
+    d["tokens"][2, 2] = 1 << 30
+    d["tokens"][3, 0] = -(1 << 30)
+    gpu = run_gpu(d)
+    out, nacc = gpu[0], gpu[1]
+    assert nacc[0] == 0 and nacc[1] <= 1 and nacc[2] <= 2 and nacc[3] == 0
+    check_rows(d, gpu)
+
+
+def test_neg_inf_logits_and_ties():
+    d = _edge_inputs(V=5000, seed=31)
+    ninf = np.uint16(0xFF80)
+    d["target"][0, :, 1000:4000] = ninf          # a block of -inf inside every position
+    d["draft"][0, :, 2000:] = ninf
+    d["target"][1, :, :] = W.bf16_bits(np.full(5000, 1.5, np.float32))[0]   # constant logits
+    d["draft"][1, :, :] = W.bf16_bits(np.full(5000, 1.5, np.float32))[0]
+    d["target"][2, :, :4096] = ninf               # first full chunk-worth of -inf
+    d["temperature"][3] = 0.0                     # greedy row with a tie at the max
+    d["target"][3, :, 10] = d["target"][3, :, 20] = W.bf16_bits(np.array([30.0], np.float32))[0]
+    d["tokens"][3, :] = [10, 10, 20]
+    gpu = run_gpu(d)
+    check_rows(d, gpu)
+    assert gpu[1][3] == 3 or gpu[0][3][0] == 10
+
+
+def test_greedy_rows_ignore_uniforms_and_drafts():
+    d = W.make(_case(B=8, greedy_rows=8, seed=32))
+    gpu1 = run_gpu(d)
+    d2 = dict(d)
+    d2["uniforms"] = np.zeros_like(d["uniforms"])
+    d2["draft"] = np.zeros_like(d["draft"])
+    gpu2 = run_gpu(d2)
+    assert np.array_equal(gpu1[0], gpu2[0]) and np.array_equal(gpu1[1], gpu2[1])
+    check_rows(d, gpu1)
+
+
+def test_deterministic_bitwise():
+    d = W.make(_case(B=16, V=70000, seed=33))
+    x = to_device(d)
+    a = run_gpu(d, x)
+    b = run_gpu(d, x)
+    for u, v in zip(a, b):
+        assert np.array_equal(u.view(np.uint32) if u.dtype == np.float32 else u,
+                              v.view(np.uint32) if v.dtype == np.float32 else v)
+
+
+def test_outputs_fully_overwritten_and_stream_respected():
+    d = W.make(_case(B=4, seed=34))
+    x = to_device(d)
+    out = torch.full((4, 4), 12345, dtype=torch.int32, device="cuda")
+    nacc = torch.full((4,), 777, dtype=torch.int32, device="cuda")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        verify(x["target"], x["draft"], x["tokens"], x["uniforms"], x["temperature"], 0,
+               out_tokens=out, num_accepted=nacc)
+    s.synchronize()
+    o, n = out.cpu().numpy(), nacc.cpu().numpy()
+    assert not (o == 12345).any() and not (n == 777).any()
+    check_well_formed(d, o, n)
+
+
+# ------------------------------------------------------------------ full size
+_FULL = {}
+
+
+def _full(c):
+    if c not in _FULL:
+        _FULL.clear()
+        _log(f"[parity] generating config {c} ...")
+        _FULL[c] = W.make(c)
+    return _FULL[c]
+
+
+@pytest.mark.parametrize("c", [1, 2, 3])
+def test_full_config_sampled_rows(c):
+    d = _full(c)
+    B = d["target"].shape[0]
+    _log(f"[parity] config {c}: running GPU on all {B} rows")
+    gpu = run_gpu(d)
+    check_well_formed(d, gpu[0], gpu[1])
+    rng = np.random.default_rng(c)
+    T = d["temperature"]
+    rows = sorted(set(rng.choice(B, size=min(B, 40), replace=False).tolist()) | {0, B - 1})
+    if (T <= 0).any():
+        rows = sorted(set(rows) | set(np.flatnonzero(T <= 0)[:64].tolist()))
+    st = {}
+    near = check_rows(d, gpu, rows, stats=st)
+    _log(f"[parity] config {c}: oracle rows {len(rows)}, near-boundary {near} "
+         f"({st['near_equal']} equal anyway), mean accepted {gpu[1].mean():.3f}")
+    assert near <= len(rows) // 2, "too few rows compared exactly"
