@@ -1,7 +1,8 @@
 """Throughput of the batched speculative-sampling verifier on one MI355X.
 
-One step = one spec_verify call (statistics pass, residual mass, final draw)
-over one synthetic batch already resident in HBM.  Default workload: B=64
+One step = one spec_verify call (statistics pass with row completion, then
+residual mass and correction draw for rejected rows) over one synthetic
+batch already resident in HBM.  Default workload: B=64
 rows, K=5 drafts, V=151,936 bf16 logits, T=0.6 (dense draft).  Inputs rotate
 over enough identical copies that the 256 MB Infinity Cache cannot serve a
 step's reads from the previous steps.
@@ -152,7 +153,7 @@ def main():
     B, Kp1, V = base["target"].shape
     K = Kp1 - 1
     dt_code = rsv.SV_BF16 if d["dtype"] == "bf16" else rsv.SV_F32
-    ws = torch.empty(rsv.workspace_bytes(B, K, V, d["topk"], dt_code), dtype=torch.uint8, device=dev)
+    ws = rsv.new_workspace(B, K, V, d["topk"], dt_code, dev)
     out = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
     nacc = torch.empty((B,), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -219,8 +220,9 @@ def main():
                      "bytes_per_launch": by["stats_kernel"], "avg_launch_ms": round(stats_ms, 5)},
         "effective_GBps_whole_call": round(by["m_min"] / (ms_per_step * 1e-3) / 1e9, 1),
         "m_min_bytes": by["m_min"],
-        "stage_ms": {"stats": round(float(stage_ms[0]), 5), "topk_merge": round(float(stage_ms[1]), 5),
-                     "residual": round(float(stage_ms[2]), 5), "sample": round(float(stage_ms[3]), 5)},
+        "stage_ms": {"stats_and_row_completion": round(float(stage_ms[0]), 5),
+                     "topk_merge": round(float(stage_ms[1]), 5),
+                     "residual_and_correction_draw": round(float(stage_ms[2]), 5)},
         "wall_ms_per_step": round(wall_ms / args.steps, 5),
         "mean_accepted": round(accepted, 4),
         "kernel_source_hash": kernel_source_hash(),

@@ -32,8 +32,8 @@
  * All pointers are device pointers owned by the caller.  Inputs are read
  * only; outputs are fully overwritten.  The library allocates nothing, keeps
  * no mutable global state and never synchronises: every call only enqueues
- * kernels on `stream`; outputs are valid once the caller has synchronised
- * that stream.  Calls on different workspaces are reentrant.
+ * two kernels on `stream`; outputs are valid once the caller has
+ * synchronised that stream.  Calls on different workspaces are reentrant.
  */
 #ifndef SPEC_VERIFY_H
 #define SPEC_VERIFY_H
@@ -82,8 +82,13 @@ typedef enum {
  *                then -1 padding.
  * num_accepted   [B] int32 device: number of accepted drafts, 0..K.
  * workspace      device scratch of at least *workspace_bytes bytes, 256-byte
- *                aligned; NULL requests the size only: *workspace_bytes is set
- *                to the size required and nothing is launched.
+ *                aligned, zero-filled before its first use (e.g. hipMemset to
+ *                0 once after allocating it).  Every call leaves it ready for
+ *                the next one (its counters return to zero), so it can be
+ *                reused without clearing.  Calls that overlap in time must use
+ *                different workspaces.  NULL requests the size only:
+ *                *workspace_bytes is set to the size required and nothing is
+ *                launched.
  * workspace_bytes in: bytes available at workspace; out (size query): bytes
  *                required.  Must not be NULL.
  * stream         HIP stream to enqueue on (0 = null stream).
@@ -123,10 +128,13 @@ int spec_verify_probe(const void* target_logits, const void* draft_logits,
  * kernel launches, for measuring each stage on the caller's stream.
  *
  * events     array of n_events events created by the caller (hipEventCreate).
- *            events[0] is recorded before the first launch and events[j]
- *            after stage j (1 = statistics pass, 2 = top-k merge, 3 = residual
- *            mass, 4 = final draw); stages that do not run still record their
- *            event so indices stay fixed.  n_events must be 0 or 5.
+ *            events[0] is recorded before the first launch, events[1] after
+ *            the statistics kernel (which also completes greedy rows and rows
+ *            that accepted every draft), events[2] after the sparse-draft
+ *            merge (recorded right after events[1] when there is none),
+ *            events[3] after the residual kernel (rejected rows: residual
+ *            mass and correction draw) and events[4] at the end.  n_events
+ *            must be 0 or 5.
  * Other arguments and return codes as spec_verify.
  */
 int spec_verify_timed(const void* target_logits, const void* draft_logits,

@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     SpecVerifyError,
     StageTimer,
     load_library,
+    new_workspace,
     plan,
     verify,
     verify_probe,

@@ -97,6 +97,12 @@ def workspace_bytes(B: int, K: int, V: int, topk_draft: int = 0, dtype: int = SV
     return n.value
 
 
+def new_workspace(B: int, K: int, V: int, topk_draft: int = 0, dtype: int = SV_BF16, device="cuda"):
+    """A zero-filled workspace for this shape (reusable across calls on one stream)."""
+    n = workspace_bytes(B, K, V, topk_draft, dtype)
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -126,7 +132,7 @@ def _prepare(target, draft, draft_tokens, uniforms, temperature, topk_draft, out
         num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
     nbytes = workspace_bytes(B, K, V, topk_draft, dt)
     if workspace is None:
-        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        workspace = new_workspace(B, K, V, topk_draft, dt, dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
     ws_n = ctypes.c_size_t(workspace.numel() * workspace.element_size())

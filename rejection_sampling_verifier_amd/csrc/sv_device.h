@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <climits>
 
 namespace sv {
 
@@ -15,6 +16,34 @@ constexpr float NEG_INF = -__builtin_inff();
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---- cross-work-group publication ------------------------------------------
+// Values that another work-group of the same launch reads are written with
+// agent-scope relaxed atomic stores (write-through, coherent across XCDs) and
+// read with agent-scope atomic loads.  A work-group that publishes waits for
+// its stores to complete (vmcnt(0)) before its counter increment, which
+// orders them without writing back the whole L2 as a general release fence
+// would.
+__device__ __forceinline__ void pub_store(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float pub_load(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void pub_store4(float4* p, float4 v) {
+  float* f = reinterpret_cast<float*>(p);
+  pub_store(f + 0, v.x); pub_store(f + 1, v.y); pub_store(f + 2, v.z); pub_store(f + 3, v.w);
+}
+__device__ __forceinline__ float4 pub_load4(const float4* p) {
+  const float* f = reinterpret_cast<const float*>(p);
+  return make_float4(pub_load(f + 0), pub_load(f + 1), pub_load(f + 2), pub_load(f + 3));
+}
+// Wait until every vector memory operation of this wave has completed.
+__device__ __forceinline__ void wait_vmem() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt/lgkmcnt unconstrained
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 // ---- element storage traits ------------------------------------------------
 // Logits arrive as bf16 (raw 16-bit patterns) or float32; a 16-byte vector
@@ -56,13 +85,16 @@ template <typename ET, bool ALIGNED, int NV>
 __device__ __forceinline__ void load_tile(const ET* __restrict__ row, int lo, int len, u32x4 (&r)[NV]) {
   constexpr int VEC = Tr<ET>::VEC;
   const int t = threadIdx.x;
+  const uint32_t f = Tr<ET>::NEG_INF_WORD;
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int e = (j * WG + t) * VEC;
-    if (ALIGNED && e + VEC <= len) {
-      r[j] = *reinterpret_cast<const u32x4*>(row + lo + e);
+    if (ALIGNED) {
+      // Aligned rows hold a multiple of VEC logits and chunks start on VEC
+      // boundaries, so a vector is either wholly inside the chunk or past it.
+      if (e < len) r[j] = *reinterpret_cast<const u32x4*>(row + lo + e);
+      else r[j] = u32x4{f, f, f, f};
     } else {
-      const uint32_t f = Tr<ET>::NEG_INF_WORD;
       u32x4 v = {f, f, f, f};
 #pragma unroll
       for (int k = 0; k < VEC; ++k)
@@ -73,27 +105,79 @@ __device__ __forceinline__ void load_tile(const ET* __restrict__ row, int lo, in
 }
 
 // ---- wave64 / block reductions ----------------------------------------------
+// DPP all-reduce: quad swaps, half-row and row mirrors, then the row
+// broadcasts of lane 15 and lane 31; lane 63 ends with the result.  The
+// combination order is fixed, so float sums are reproducible.
+namespace dpp {
+constexpr int QUAD_1032 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int QUAD_2301 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int ROW_HALF_MIRROR = 0x141;
+constexpr int ROW_MIRROR = 0x140;
+constexpr int ROW_BCAST15 = 0x142;
+constexpr int ROW_BCAST31 = 0x143;
+}  // namespace dpp
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f(float identity, float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(identity), __float_as_int(v), CTRL,
+                                                    ROW_MASK, 0xF, false));
+}
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_i(int identity, int v) {
+  return __builtin_amdgcn_update_dpp(identity, v, CTRL, ROW_MASK, 0xF, false);
+}
+__device__ __forceinline__ float lane63(float v) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = fmaxf(v, dpp_f<dpp::QUAD_1032>(NEG_INF, v));
+  v = fmaxf(v, dpp_f<dpp::QUAD_2301>(NEG_INF, v));
+  v = fmaxf(v, dpp_f<dpp::ROW_HALF_MIRROR>(NEG_INF, v));
+  v = fmaxf(v, dpp_f<dpp::ROW_MIRROR>(NEG_INF, v));
+  v = fmaxf(v, dpp_f<dpp::ROW_BCAST15, 0xA>(NEG_INF, v));
+  v = fmaxf(v, dpp_f<dpp::ROW_BCAST31, 0xC>(NEG_INF, v));
+  return lane63(v);
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v += dpp_f<dpp::QUAD_1032>(0.f, v);
+  v += dpp_f<dpp::QUAD_2301>(0.f, v);
+  v += dpp_f<dpp::ROW_HALF_MIRROR>(0.f, v);
+  v += dpp_f<dpp::ROW_MIRROR>(0.f, v);
+  v += dpp_f<dpp::ROW_BCAST15, 0xA>(0.f, v);
+  v += dpp_f<dpp::ROW_BCAST31, 0xC>(0.f, v);
+  return lane63(v);
 }
 // (value, index) argmax: larger value wins, equal values go to the lower index.
 __device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2) {
   if (v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
 }
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ void argmax_step(float& v, int& i) {
+  const float v2 = dpp_f<CTRL, ROW_MASK>(NEG_INF, v);
+  const int i2 = dpp_i<CTRL, ROW_MASK>(INT_MAX, i);
+  argmax_merge(v, i, v2, i2);
+}
 __device__ __forceinline__ void wave_argmax(float& v, int& i) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float v2 = __shfl_xor(v, o, 64);
-    const int i2 = __shfl_xor(i, o, 64);
-    argmax_merge(v, i, v2, i2);
-  }
+  argmax_step<dpp::QUAD_1032>(v, i);
+  argmax_step<dpp::QUAD_2301>(v, i);
+  argmax_step<dpp::ROW_HALF_MIRROR>(v, i);
+  argmax_step<dpp::ROW_MIRROR>(v, i);
+  argmax_step<dpp::ROW_BCAST15, 0xA>(v, i);
+  argmax_step<dpp::ROW_BCAST31, 0xC>(v, i);
+  v = lane63(v);
+  i = __builtin_amdgcn_readlane(i, 63);
+}
+
+// max(a, b, c) issued directly.  The compiler's fmaxf first quiets possible
+// signaling NaNs in operands it cannot prove canonical (such as logits
+// widened from loaded bits); here only a NaN logit could be one, and a NaN
+// logit has no defined result.  Callers must not pass bit patterns that are
+// NaN for other reasons (e.g. a packed pair of bf16 values).
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
 }
 
 // Block reductions combine the four wave results in a fixed order, so every

@@ -164,3 +164,48 @@ def test_full_config_sampled_rows(c):
     _log(f"[parity] config {c}: oracle rows {len(rows)}, near-boundary {near} "
          f"({st['near_equal']} equal anyway), mean accepted {gpu[1].mean():.3f}")
     assert near <= len(rows) // 2, "too few rows compared exactly"
+
+
+def test_workspace_reused_across_calls_and_shapes():
+    """Counters in the workspace return to zero after every call."""
+    import rejection_sampling_verifier_amd as rsv
+    big = rsv.new_workspace(16, 5, 70000, 0, SV_BF16, "cuda")
+    for i, case in enumerate([_case(B=16, K=5, V=70000, seed=40),
+                              _case(B=9, K=2, V=30000, seed=41),
+                              _case(B=16, K=5, V=70000, greedy_rows=5, seed=42),
+                              _case(B=3, K=4, V=50000, temperature=2.0, seed=43)]):
+        d = W.make(case)
+        x = to_device(d)
+        out, nacc, probs, mass = rsv.verify_probe(x["target"], x["draft"], x["tokens"], x["uniforms"],
+                                                  x["temperature"], 0, workspace=big)
+        torch.cuda.synchronize()
+        gpu = (out.cpu().numpy(), nacc.cpu().numpy(), probs.cpu().numpy(), mass.cpu().numpy())
+        check_rows(d, gpu)
+        _log(f"[parity] workspace reuse call {i}: ok")
+
+
+def test_zero_residual_falls_back_to_target():
+    """u = 1 with identical target and draft logits rejects with a zero
+    residual; the correction is then drawn from the target row."""
+    d = W.make(_case(B=4, K=2, V=20000, seed=44))
+    d["draft"][:] = d["target"][:, :2]
+    d["uniforms"][:, 0] = 1.0
+    gpu = run_gpu(d)
+    assert (gpu[1] == 0).all()
+    check_rows(d, gpu)
+
+
+@pytest.mark.parametrize("dtype", [W.BF16, W.F32])
+def test_neg_inf_blocks_at_cold_temperature(dtype):
+    """-inf logits at odd and even ids and a ragged last chunk, at T = 0.05
+    where an underestimated chunk max would overflow exp2."""
+    d = W.make(_case(B=4, K=3, V=40001, dtype=dtype, temperature=0.05, seed=45))
+    ninf = np.uint16(0xFF80) if dtype == W.BF16 else np.float32(-np.inf)
+    d["target"][0, :, 1::2] = ninf
+    d["draft"][0, :, 1::2] = ninf
+    d["target"][1, :, 0::3] = ninf
+    d["target"][2, :, 30000:] = ninf
+    d["draft"][2, :, 29000:] = ninf
+    gpu = run_gpu(d)
+    assert np.isfinite(gpu[3]).all() and np.isfinite(gpu[2]).all()
+    check_rows(d, gpu)
