@@ -10,7 +10,8 @@
 //     diterima" (nalar.dev): batched verification of all draft positions from
 //     one target pass, greedy vs sampling semantics, first-rejection cut.
 //
-// Two launches per call, both on the caller's stream:
+// Two launches per call, both on the caller's stream; no work-group ever
+// waits for another one that may not have started.
 //
 //   A. stats_kernel, one work-group per (row, position, vocabulary chunk).
 //      Streams its chunk of target or draft logits once from HBM (16-byte
@@ -18,14 +19,15 @@
 //      exp2((l - max) * log2(e)/T) -- or, for greedy rows, the chunk argmax.
 //      The chunk holding a position's draft token records that token's
 //      logit; the bonus position also writes 32 sub-block sums for the final
-//      draw.  No work-group waits for or talks to another.
+//      draw.
 //   B. finish_kernel, one work-group per (row, chunk).  Each work-group
-//      merges its row's partials and runs the first-rejection scan.  Greedy
-//      rows and rows that accepted every draft are completed by the row's
-//      work-group 0.  For a rejected row every work-group re-reads target and
-//      draft logits of the rejected position in its chunk and publishes 32
-//      sub-block sums of max(0, p_n - q_n); the last work-group of the row to
-//      finish (atomic counter) draws the correction token.
+//      loads its row's partials into LDS in one round of loads, merges them
+//      and runs the first-rejection scan.  Greedy rows and rows that accepted
+//      every draft are completed by the row's work-group 0.  For a rejected
+//      row every work-group re-reads target and draft logits of the rejected
+//      position in its chunk and publishes 32 sub-block sums of
+//      max(0, p_n - q_n); the last work-group of the row to arrive (atomic
+//      counter) draws the correction token.
 //
 // The final draw is an inverse CDF over a three-level hierarchy: chunk
 // masses (block scan), the 32 sub-block sums of the selected chunk, and a
@@ -39,13 +41,12 @@
 // reductions combine partial results in a fixed order (no float atomics), so
 // outputs are bitwise reproducible.
 //
-// Cross-work-group hand-off inside B: a work-group publishes its 32 sums
-// with write-through agent-scope atomic stores, waits for them to complete,
-// then increments its row's counter; the work-group that observes the final
-// count reads the others' sums with agent-scope atomic loads and resets the
-// counter to zero for the next call.  Nothing ever waits on another
-// work-group.
+// Hand-off inside B: residual sums are published as complemented words with
+// write-through agent-scope atomic stores (a zero word means "not written"),
+// so a producer never waits; the last work-group of the row, which knows its
+// peers have issued their stores, polls them and clears them after use.
 
+#include <algorithm>
 #include <climits>
 #include <cstddef>
 #include <cstdint>
@@ -57,10 +58,21 @@ using namespace sv;
 
 namespace {
 
-constexpr int NV_TILE = 8;                 // 16-byte vectors per thread per chunk
+#ifndef SV_NV_TILE
+#define SV_NV_TILE 8
+#endif
+#ifndef SV_MAX_WAVES
+#define SV_MAX_WAVES 4                      // cap on waves per SIMD (0: none)
+#endif
+constexpr int NV_TILE = SV_NV_TILE;        // 16-byte vectors per thread per chunk
 constexpr int NSUB = NV_TILE * NWAVE;      // sub-blocks per chunk (one wave x one vector row)
 constexpr int MAX_C = 2048;                // vocabulary chunks per position
 constexpr int MAX_SLOTS = 2 * SV_MAX_K + 1;
+constexpr int MAX_CACHE_WORDS = 8192;       // dynamic LDS for a row's published words (32 KiB)
+// Longest wait for another work-group's results: 100 ms of the 100 MHz
+// constant clock.  Every wait ends well before that in a correct launch; the
+// bound only guarantees termination.
+constexpr uint64_t WAIT_TICKS = 10000000ull;
 
 struct Args {
   const void* tgt;           // [B, K+1, V]
@@ -72,16 +84,39 @@ struct Args {
   int32_t* nacc;             // [B]
   float* probs;              // [B, K, 2] or null
   float* mass;               // [B] or null
-  float4* part;              // [B, 2K+1, C] {max | argmax value, sum, argmax id bits, 0}
-  float* ldv;                // [B, 2K+1] logit of the position's draft token
-  float* subK;               // [B, C, NSUB] bonus-position sub-block sums (vs chunk max)
-  float* subR;               // [B, C, NSUB] residual sub-block sums
-  unsigned* cnt;             // [B] zero between calls
+  uint32_t* part;            // [B, 2K+1, C, 4] published {max | argmax value, sum, argmax id, l(d)}
+  uint32_t* subK;            // [B, C, NSUB] published bonus-position sub-block sums (vs chunk max)
+  uint32_t* subR;            // [B, C, NSUB] published residual sub-block sums
+  unsigned* cnt;             // [B] finishing work-groups that have arrived
   int B, K, V, C, CS, topk;
+  int GA;                    // statistics work-groups per row: (2K+1) * C
+  int cache;                 // 1: finishing work-groups keep the row's words in dynamic LDS
 };
 
-__device__ __forceinline__ size_t part_index(const Args& a, int b, int slot, int c) {
-  return ((size_t)b * (2 * a.K + 1) + slot) * (size_t)a.C + c;
+// ---- published words -------------------------------------------------------
+// A value another work-group reads is published as the bitwise complement of
+// its bits with a write-through agent-scope atomic store; a word of zero --
+// the state of the workspace between calls -- therefore means "not written
+// yet", and a reader polls with agent-scope atomic loads until every word it
+// needs is non-zero.  Each word is validated on its own, so no ordering
+// between words is needed and producers never wait.  The last work-group of
+// a row clears the row's words for the next call.
+__device__ __forceinline__ void pub_u32(uint32_t* p, uint32_t bits) {
+  bits = bits == 0xFFFFFFFFu ? 0x7FC00000u : bits;  // a NaN pattern whose complement is 0
+  __hip_atomic_store(p, ~bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void pub_f32(uint32_t* p, float v) { pub_u32(p, __float_as_uint(v)); }
+__device__ __forceinline__ uint32_t peek(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t got_u32(const uint32_t* p) { return ~peek(p); }
+__device__ __forceinline__ float got_f32(const uint32_t* p) { return __uint_as_float(~peek(p)); }
+__device__ __forceinline__ void clear_word(uint32_t* p) {
+  __hip_atomic_store(p, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint32_t* part_words(const Args& a, int b, int slot, int c) {
+  return a.part + (((size_t)b * (2 * a.K + 1) + slot) * (size_t)a.C + c) * 4;
 }
 template <typename ET>
 __device__ __forceinline__ const ET* target_row(const Args& a, int b, int i) {
@@ -140,10 +175,14 @@ __device__ __forceinline__ float tile_max<float, NV_TILE>(const u32x4 (&r)[NV_TI
 }
 
 // ============================================================================
-// Kernel A: per-chunk statistics.
+// Kernel A: statistics of one (row, position, chunk).
 // ============================================================================
 template <typename ET, bool ALIGNED>
-__global__ __launch_bounds__(WG) void stats_kernel(Args a) {
+__global__ __launch_bounds__(WG)
+#if SV_MAX_WAVES > 0
+__attribute__((amdgpu_waves_per_eu(1, SV_MAX_WAVES)))
+#endif
+void stats_kernel(Args a) {
   constexpr int VEC = Tr<ET>::VEC;
   const int S = 2 * a.K + 1;
   const int c = blockIdx.x % a.C;
@@ -167,7 +206,7 @@ __global__ __launch_bounds__(WG) void stats_kernel(Args a) {
   __shared__ float shf[NWAVE];
   __shared__ int shi[NWAVE];
   __shared__ float shsub[NSUB];
-  float4* dst = a.part + part_index(a, b, slot, c);
+  uint32_t* dst = part_words(a, b, slot, c);
 
   if (greedy) {
     // Argmax of raw logits, lowest id among equal maxima.  A thread visits its
@@ -183,16 +222,15 @@ __global__ __launch_bounds__(WG) void stats_kernel(Args a) {
         if (x > bv) { bv = x; bi = lo + (j * WG + t) * VEC + k; }
       }
     block_argmax(bv, bi, shf, shi);
-    if (t == 0) *dst = make_float4(bv, 0.f, __int_as_float(bi), 0.f);
+    if (t == 0) *reinterpret_cast<u32x4*>(dst) = u32x4{__float_as_uint(bv), 0u, (uint32_t)bi, 0u};
     return;
   }
 
   const float m = block_max(tile_max<ET, NV_TILE>(r), shf);
   const float s = LOG2E / T;
-  const float ms = mul_rn(m, s);
   // A chunk of -inf only would give exp2(nan): use the reference 0 then
   // (every term is exp2(-inf) = 0).
-  const float msr = m == NEG_INF ? 0.f : ms;
+  const float msr = m == NEG_INF ? 0.f : mul_rn(m, s);
   float zj[NV_TILE];
 #pragma unroll
   for (int j = 0; j < NV_TILE; ++j) {
@@ -218,20 +256,63 @@ __global__ __launch_bounds__(WG) void stats_kernel(Args a) {
       if (lane == 0) shsub[j * NWAVE + wave] = v;
     }
     __syncthreads();
-    if (t < NSUB) a.subK[((size_t)b * a.C + c) * NSUB + t] = shsub[t];
+    if (t < NSUB) a.subK[((size_t)b * a.C + c) * NSUB + t] = __float_as_uint(shsub[t]);
   }
   if (t == 0) {
-    *dst = make_float4(m, z, 0.f, 0.f);
+    uint32_t ld = 0u;
     if (pos < a.K) {
+      // The chunk holding this position's draft token records its logit.
       const int d = a.tok[(size_t)b * a.K + pos];
-      if (d >= lo && d < lo + len) a.ldv[(size_t)b * S + slot] = Tr<ET>::load1(row + d);
+      if (d >= lo && d < lo + len) ld = __float_as_uint(Tr<ET>::load1(row + d));
     }
+    *reinterpret_cast<u32x4*>(dst) = u32x4{__float_as_uint(m), __float_as_uint(z), 0u, ld};
   }
+  (void)S;
 }
 
 // ============================================================================
-// Row decision from the statistics partials (kernel B, every work-group).
+// Row decision from the published statistics.
 // ============================================================================
+// Where a finishing work-group reads a row's words: copies in LDS when they
+// fit, else global memory.  Partials and bonus sub-block sums were written by
+// the statistics kernel (plain words); residual sub-block sums are published
+// by this kernel's work-groups (complemented words, see pub_u32).
+struct RowView {
+  const uint32_t* pw;    // [(2K+1) * C * 4] partial words, or null
+  const uint32_t* sub;   // [C * NSUB] sub-block sums (plain), or null
+};
+__device__ __forceinline__ float view_part(const Args& a, const RowView& v, int b, int slot, int c, int w) {
+  return __uint_as_float(v.pw ? v.pw[((size_t)slot * a.C + c) * 4 + w] : part_words(a, b, slot, c)[w]);
+}
+__device__ __forceinline__ float view_sub(const RowView& v, const uint32_t* gsub, bool published, int c, int q) {
+  if (v.sub) return __uint_as_float(v.sub[c * NSUB + q]);
+  const uint32_t* p = gsub + (size_t)c * NSUB + q;
+  return __uint_as_float(published ? got_u32(p) : *p);
+}
+
+// Block-wide wait until the words p0[0..n0) and p1[0..n1) are published.
+// Decoded values are left in d0 / d1 (LDS) when those are given.  Returns
+// false (uniformly) if the deadline passed first.
+__device__ bool wait_words(const uint32_t* p0, int n0, uint32_t* d0, const uint32_t* p1, int n1, uint32_t* d1,
+                           uint64_t deadline) {
+  for (;;) {
+    bool ok = true;
+    for (int i = threadIdx.x; i < n0; i += WG) {
+      const uint32_t w = peek(p0 + i);
+      ok &= w != 0u;
+      if (d0) d0[i] = ~w;
+    }
+    for (int i = threadIdx.x; i < n1; i += WG) {
+      const uint32_t w = peek(p1 + i);
+      ok &= w != 0u;
+      if (d1) d1[i] = ~w;
+    }
+    if (__syncthreads_and(ok)) return true;
+    if (__syncthreads_or(wall_clock64() > deadline)) return false;
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
 struct RowShared {
   float M[MAX_SLOTS];    // position max (sampling) or argmax value (greedy)
   float Z[MAX_SLOTS];    // sum of exp2(fma(l, s, -fl(M*s)))
@@ -245,42 +326,35 @@ struct RowShared {
   float s;               // log2(e)/T
 };
 
-__device__ void decide_row(const Args& a, int b, RowShared& rs) {
-  const int K = a.K, C = a.C, S = 2 * K + 1, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+__device__ void decide_row(const Args& a, int b, RowShared& rs, const RowView& v) {
+  const int K = a.K, C = a.C, t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const float T = a.temp[b];
   const bool greedy = !is_sampling_temperature(T);
   const float s = greedy ? 0.f : LOG2E / T;
-  // Per-position inputs, issued before the merge so that their latency
-  // overlaps it.
   int d = -1;
-  float u = 0.f, lt = 0.f, lq = 0.f;
+  float u = 0.f;
   if (t < K) {
     d = a.tok[(size_t)b * K + t];
     u = a.uni[(size_t)b * (K + 1) + t];
-    lt = a.ldv[(size_t)b * S + t];
-    lq = a.ldv[(size_t)b * S + K + 1 + t];
   }
   const int nmerge = (greedy || a.topk > 0) ? K + 1 : 2 * K + 1;
   for (int slot = wave; slot < nmerge; slot += NWAVE) {
-    const float4* p = a.part + part_index(a, b, slot, 0);
     if (greedy) {
       float bv = NEG_INF;
       int bi = INT_MAX;
-      for (int c = lane; c < C; c += 64) {
-        const float4 v = p[c];
-        argmax_merge(bv, bi, v.x, __float_as_int(v.z));
-      }
+      for (int c = lane; c < C; c += 64)
+        argmax_merge(bv, bi, view_part(a, v, b, slot, c, 0), __float_as_int(view_part(a, v, b, slot, c, 2)));
       wave_argmax(bv, bi);
       if (lane == 0) { rs.M[slot] = bv; rs.Z[slot] = 0.f; rs.idx[slot] = bi; }
     } else {
       float m = NEG_INF;
-      for (int c = lane; c < C; c += 64) m = fmaxf(m, p[c].x);
+      for (int c = lane; c < C; c += 64) m = fmaxf(m, view_part(a, v, b, slot, c, 0));
       m = wave_max(m);
       const float MS = mul_rn(m, s);
       float z = 0.f;
       for (int c = lane; c < C; c += 64) {
-        const float4 pc = p[c];
-        if (pc.x != NEG_INF) z += pc.y * exp2_fast(mul_rn(pc.x, s) - MS);
+        const float mc = view_part(a, v, b, slot, c, 0), zc = view_part(a, v, b, slot, c, 1);
+        if (mc != NEG_INF) z += zc * exp2_fast(mul_rn(mc, s) - MS);
       }
       z = wave_sum(z);
       if (lane == 0) { rs.M[slot] = m; rs.Z[slot] = z; rs.idx[slot] = 0; }
@@ -295,6 +369,9 @@ __device__ void decide_row(const Args& a, int b, RowShared& rs) {
     if (t < K) {
       float p = 0.f, q = 0.f;
       if (!greedy && d >= 0 && d < a.V) {
+        const int cd = d / a.CS;
+        const float lt = view_part(a, v, b, t, cd, 3);
+        const float lq = view_part(a, v, b, K + 1 + t, cd, 3);
         p = exp2_fast(fmaf(lt, s, -mul_rn(rs.M[t], s))) / rs.Z[t];
         q = exp2_fast(fmaf(lq, s, -mul_rn(rs.M[K + 1 + t], s))) / rs.Z[K + 1 + t];
       }
@@ -368,110 +445,123 @@ __device__ int range_search(const ET* __restrict__ trow, const ET* __restrict__ 
 }
 
 // ============================================================================
-// Final draw for a sampling row ([RheoSampling] section 4 step 3): from the
-// residual sub-block sums (n < K) or the bonus position's sub-block sums
-// (n == K).  Writes out_tokens / num_accepted / mass.
+// Final draw for a sampling row ([RheoSampling] section 4 step 3).  The
+// weights are the residual max(0, p_n - q_n) after a rejection at n < K, or
+// the bonus position's p_K; their CDF is walked in three levels:
+//   1. chunk masses: one half-wave per chunk scans the chunk's 32 sub-block
+//      sums (residual sums published by kernel B, or bonus sums from the
+//      statistics kernel rescaled from the chunk max); the chunk mass is the
+//      scan's last element;
+//   2. a block scan over the chunk masses; the first chunk whose inclusive
+//      prefix exceeds t = u_K * S is selected;
+//   3. in that chunk, the same half-wave scan picks the sub-block, and a
+//      block prefix sum over its 64 * VEC ids picks the token.
+// A zero residual (reachable only through rounding) falls back to p_n with
+// chunk masses from the partials and a search over the whole chunk.
+// Scratch: `cf` holds 3 * C floats of LDS.  Writes out_tokens, num_accepted
+// and mass.
 // ============================================================================
+__device__ __forceinline__ float halfwave_incl_scan(float v) {
+  const int l = threadIdx.x & 31;
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) {
+    const float u = __shfl_up(v, o, 32);
+    if (l >= o) v += u;
+  }
+  return v;
+}
+
 template <typename ET, bool ALIGNED>
 __device__ void final_draw(const Args& a, int b, int n, float s, float MSt, float rZt, float MSq,
-                           float rZq, float* red) {
+                           float rZq, float* red, const RowView& v, float* cf) {
   constexpr int VEC = Tr<ET>::VEC;
-  __shared__ int sh_i, sh_last;
-  __shared__ float sh_tl;
+  static_assert(NSUB == 32, "one half-wave scans the sub-blocks of a chunk");
+  __shared__ int sh_i, sh_last, sh_q;
+  __shared__ float sh_tl, sh_tq;
   const int K = a.K, C = a.C, t = threadIdx.x;
+  float* raw = cf;           // chunk masses
+  float* inc = cf + C;       // inclusive prefix of chunk masses
+  float* exc = cf + 2 * C;   // exclusive prefix of chunk masses
   const bool reject = n < K;
-  // mode 0: residual sub-block sums; 1: bonus sub-block sums (rescaled from
-  // the chunk max); 2: target chunk masses from the statistics partials
-  // (fallback for a zero residual, reachable only through rounding).
-  int mode = reject ? 0 : 1;
+  const uint32_t* gsub = (reject ? a.subR : a.subK) + (size_t)b * C * NSUB;
   auto bonus_scale = [&](int c) {
-    const float mc = pub_load(&a.part[part_index(a, b, K, c)].x);
+    const float mc = view_part(a, v, b, K, c, 0);
     return mc == NEG_INF ? 0.f : exp2_fast(mul_rn(mc, s) - MSt) * rZt;
   };
-  // Mass of chunk c: the ordered sum of its sub-block sums.
-  auto chunk_mass = [&](int c) {
-    if (c >= C) return 0.f;
-    if (mode == 2) {
-      const float4 v = pub_load4(&a.part[part_index(a, b, n, c)]);
-      return v.x == NEG_INF ? 0.f : v.y * exp2_fast(mul_rn(v.x, s) - MSt) * rZt;
-    }
-    const float* sub = (mode == 0 ? a.subR : a.subK) + ((size_t)b * C + c) * NSUB;
-    const float sc = mode == 0 ? 1.f : bonus_scale(c);
-    float acc = 0.f;
-    for (int q = 0; q < NSUB; ++q) acc += mode == 0 ? pub_load(sub + q) : pub_load(sub + q) * sc;
-    return acc;
+  // Sub-block weight q of chunk c (lane q of a half-wave).
+  auto sub_weight = [&](int c, int q) {
+    return reject ? view_sub(v, gsub, true, c, q) : view_sub(v, gsub, false, c, q) * bonus_scale(c);
   };
-  // Pass 1: total mass S (tiles of WG chunks, block scans in a fixed order).
-  auto total_mass = [&]() {
+  const int hw = t >> 5, l = t & 31;
+  for (int c = hw; c < C; c += WG / 32) {
+    const float m = halfwave_incl_scan(sub_weight(c, l));
+    if (l == 31) raw[c] = m;
+  }
+  __syncthreads();
+  auto scan_chunks = [&]() {
     float carry = 0.f;
     for (int base = 0; base < C; base += WG) {
+      const int c = base + t;
       float ex, tot;
-      block_scan(chunk_mass(base + t), red, ex, tot);
+      const float in = block_scan(c < C ? raw[c] : 0.f, red, ex, tot);
+      if (c < C) { inc[c] = carry + in; exc[c] = carry + ex; }
       carry += tot;
     }
+    __syncthreads();
     return carry;
   };
-  float S = total_mass();
+  float S = scan_chunks();
+  bool fallback = false;
   if (reject && S == 0.f) {
-    mode = 2;
-    S = total_mass();
+    fallback = true;
+    for (int c = t; c < C; c += WG) {
+      const float mc = view_part(a, v, b, n, c, 0), zc = view_part(a, v, b, n, c, 1);
+      raw[c] = mc == NEG_INF ? 0.f : zc * exp2_fast(mul_rn(mc, s) - MSt) * rZt;
+    }
+    __syncthreads();
+    S = scan_chunks();
   }
   const float tv = a.uni[(size_t)b * (K + 1) + K] * S;
-  // Pass 2: the first chunk whose inclusive prefix exceeds t (same sums).
   if (t == 0) { sh_i = INT_MAX; sh_last = 0; }
   __syncthreads();
-  float carry = 0.f;
-  for (int base = 0; base < C; base += WG) {
-    const int c = base + t;
-    const float v = chunk_mass(c);
-    float ex, tot;
-    const float in = block_scan(v, red, ex, tot);
-    if (c < C && v > 0.f) atomicMax(&sh_last, c);
-    if (c < C && carry + in > tv) atomicMin(&sh_i, c);
-    __syncthreads();
-    const int hit = sh_i;
-    if (hit != INT_MAX) {
-      if (c == hit) sh_tl = tv - (carry + ex);
-      break;
-    }
-    carry += tot;
+  for (int c = t; c < C; c += WG) {
+    if (inc[c] > tv) atomicMin(&sh_i, c);
+    if (raw[c] > 0.f) atomicMax(&sh_last, c);
   }
   __syncthreads();
   int cs = sh_i;
-  float t1 = sh_tl;
-  if (cs == INT_MAX) {   // t reached the total only through rounding
-    cs = sh_last;
-    t1 = __builtin_inff();
-  }
-  __syncthreads();
+  float t1 = cs != INT_MAX ? tv - exc[cs] : __builtin_inff();
+  if (cs == INT_MAX) cs = sh_last;  // t reached the total only through rounding
   const int lo = cs * a.CS;
   const int len = min(a.CS, a.V - lo);
   const ET* trow = target_row<ET>(a, b, n);
-  const ET* drow = mode == 0 ? draft_row<ET>(a, b, n) : nullptr;
+  const ET* drow = (reject && !fallback) ? draft_row<ET>(a, b, n) : nullptr;
   int start = lo, slen = len;
   float tl = t1;
-  if (mode != 2) {
-    // Sub-block of the selected chunk, by a sequential scan of its sums
-    // (the same sequence of additions that gave the chunk mass).
-    if (t == 0) {
-      const float* sub = (mode == 0 ? a.subR : a.subK) + ((size_t)b * C + cs) * NSUB;
-      const float sc = mode == 0 ? 1.f : bonus_scale(cs);
-      float cum = 0.f;
-      int qs = -1, qlast = 0;
-      float tq = __builtin_inff();
-      for (int q = 0; q < NSUB; ++q) {
-        const float v = mode == 0 ? pub_load(sub + q) : pub_load(sub + q) * sc;
-        if (v > 0.f) qlast = q;
-        if (qs < 0 && cum + v > t1) { qs = q; tq = t1 - cum; }
-        cum += v;
+  if (!fallback) {
+    if (t < 32) {
+      // Same scan as for the chunk mass, so the sub-level prefix ends at it.
+      const float w = sub_weight(cs, l);
+      const float pin = halfwave_incl_scan(w);
+      const float pex = __shfl_up(pin, 1, 32);
+      const unsigned long long hit = __ballot(pin > t1) & 0xFFFFFFFFull;
+      const unsigned long long pos = __ballot(w > 0.f) & 0xFFFFFFFFull;
+      if (l == 0) {
+        if (hit) {
+          const int q = (int)__builtin_ctzll(hit);
+          sh_q = q;
+          sh_tq = t1;  // refined below by the lane that owns q
+        } else {
+          sh_q = pos ? 63 - (int)__builtin_clzll(pos) : 0;
+          sh_tq = __builtin_inff();
+        }
       }
-      if (qs < 0) qs = qlast;
-      sh_i = qs;
-      sh_tl = tq;
+      // The lane of the selected sub-block subtracts its exclusive prefix.
+      if (hit && l == (int)__builtin_ctzll(hit)) sh_tq = l ? t1 - pex : t1;
     }
     __syncthreads();
-    const int q = sh_i;
-    tl = sh_tl;
+    const int q = sh_q;
+    tl = sh_tq;
     const int j = q / NWAVE, w = q % NWAVE;
     start = lo + (j * WG + w * 64) * VEC;
     slen = max(0, min(64 * VEC, lo + len - start));
@@ -485,22 +575,45 @@ __device__ void final_draw(const Args& a, int b, int n, float s, float MSt, floa
     a.nacc[b] = n;
     if (a.mass) a.mass[b] = S;
   }
+  (void)sh_tl;
 }
 
 // ============================================================================
-// Kernel B: row decision, completion of greedy and bonus rows, residual
-// sub-block sums of rejected rows and their correction draw.
+// Kernel B: finishing work-group (row b, chunk c).  Decides the row from the
+// statistics partials, then: greedy rows and rows that accepted every draft
+// are completed by the row's chunk-0 work-group; for a rejected row each
+// work-group publishes the 32 sub-block sums of max(0, p_n - q_n) over its
+// chunk, and the last of the row's C work-groups to arrive (atomic counter)
+// draws the correction token and clears the row's published words.
 // ============================================================================
+__device__ __forceinline__ void write_failed_row(const Args& a, int b) {
+  // Reached only if a wait ran past its deadline: num_accepted = -1 marks it.
+  for (int i = threadIdx.x; i <= a.K; i += WG) a.out[(size_t)b * (a.K + 1) + i] = -1;
+  if (threadIdx.x == 0) a.nacc[b] = -1;
+}
+
 template <typename ET, bool ALIGNED>
 __global__ __launch_bounds__(WG) void finish_kernel(Args a) {
   constexpr int VEC = Tr<ET>::VEC;
-  const int c = blockIdx.x % a.C;
-  const int b = blockIdx.x / a.C;
-  const int K = a.K, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  extern __shared__ uint32_t row_cache[];
   __shared__ RowShared rs;
   __shared__ float shsub[NSUB];
-  __shared__ int sh_flag;
-  decide_row(a, b, rs);
+  __shared__ int sh_last;
+  const int c = blockIdx.x % a.C;
+  const int b = blockIdx.x / a.C;
+  const int K = a.K, C = a.C, S = 2 * K + 1, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  float* chunk_scratch = reinterpret_cast<float*>(row_cache);
+  uint32_t* cache_pw = a.cache ? row_cache + 3 * C : nullptr;
+  uint32_t* cache_sub = a.cache ? cache_pw + (size_t)S * C * 4 : nullptr;
+  if (cache_pw) {
+    // All partials of the row in one round of loads (also the draft-token
+    // logits, which the decision reads at a token-dependent chunk).
+    const u32x4* src = reinterpret_cast<const u32x4*>(part_words(a, b, 0, 0));
+    for (int i = t; i < S * C; i += WG) reinterpret_cast<u32x4*>(cache_pw)[i] = src[i];
+    __syncthreads();
+  }
+  RowView view{cache_pw, nullptr};
+  decide_row(a, b, rs, view);
   const int n = rs.n;
   if (c == 0 && a.probs && t < K) {
     a.probs[((size_t)b * K + t) * 2 + 0] = rs.greedy ? 0.f : rs.p[t];
@@ -520,7 +633,7 @@ __global__ __launch_bounds__(WG) void finish_kernel(Args a) {
   const float s = rs.s;
   const float MSt = mul_rn(rs.M[n], s), rZt = 1.f / rs.Z[n];
   if (n == K) {
-    if (c == 0) final_draw<ET, ALIGNED>(a, b, n, s, MSt, rZt, 0.f, 0.f, rs.red_f);
+    if (c == 0) final_draw<ET, ALIGNED>(a, b, n, s, MSt, rZt, 0.f, 0.f, rs.red_f, view, chunk_scratch);
     return;
   }
   // Rejected at position n: residual max(0, p_n - q_n) over this chunk.
@@ -546,17 +659,24 @@ __global__ __launch_bounds__(WG) void finish_kernel(Args a) {
     if (lane == 0) shsub[j * NWAVE + wave] = v;
   }
   __syncthreads();
-  if (t < NSUB) pub_store(a.subR + ((size_t)b * a.C + c) * NSUB + t, shsub[t]);
-  if (t < 64) wait_vmem();
-  __syncthreads();
+  uint32_t* subR_row = a.subR + (size_t)b * C * NSUB;
+  if (t < NSUB) pub_f32(subR_row + (size_t)c * NSUB + t, shsub[t]);
+  // Count this work-group.  Its sums need no ordering with the count: the
+  // last work-group polls them until they are published (each of its peers
+  // has already issued its stores, so the wait ends).
   if (t == 0)
-    sh_flag = __hip_atomic_fetch_add(a.cnt + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-              (unsigned)a.C - 1u;
+    sh_last = __hip_atomic_fetch_add(a.cnt + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              (unsigned)C - 1u;
   __syncthreads();
-  if (sh_flag) {
-    final_draw<ET, ALIGNED>(a, b, n, s, MSt, rZt, MSq, rZq, rs.red_f);
-    if (t == 0) a.cnt[b] = 0;
-  }
+  if (!sh_last) return;
+  const bool ok = wait_words(subR_row, C * NSUB, cache_sub, nullptr, 0, nullptr, wall_clock64() + WAIT_TICKS);
+  view.sub = cache_sub;
+  final_draw<ET, ALIGNED>(a, b, n, s, MSt, rZt, MSq, rZq, rs.red_f, view, chunk_scratch);
+  __syncthreads();
+  if (!ok) write_failed_row(a, b);
+  // Clear the row's published sums and counter for the next call.
+  for (int i = t; i < C * NSUB; i += WG) clear_word(subR_row + i);
+  if (t == 0) __hip_atomic_store(a.cnt + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ============================================================================
@@ -564,7 +684,9 @@ __global__ __launch_bounds__(WG) void finish_kernel(Args a) {
 // ============================================================================
 struct Plan {
   int C = 0, CS = 0;
-  size_t off_cnt = 0, off_part = 0, off_ldv = 0, off_subK = 0, off_subR = 0, total = 0;
+  size_t off_cnt = 0, off_part = 0, off_subK = 0, off_subR = 0, total = 0;
+  bool cache = false;       // finishing work-groups copy the row's words to LDS
+  size_t lds_bytes = 0;     // dynamic LDS of the finishing work-groups
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -584,31 +706,33 @@ int make_plan(int B, int K, int V, int topk, int dtype, Plan& pl) {
   pl.C = (int)C;
   pl.CS = (int)CS;
   const size_t S = 2 * (size_t)K + 1;
+  // Every region is zero between calls (see spec_verify.h).
   size_t off = 0;
-  pl.off_cnt = off;   // per-row counters: zero before the first call, zero after every call
+  pl.off_cnt = off;
   off = align256(off + sizeof(unsigned) * (size_t)B);
   pl.off_part = off;
-  off = align256(off + sizeof(float4) * (size_t)B * S * C);
-  pl.off_ldv = off;
-  off = align256(off + sizeof(float) * (size_t)B * S);
+  off = align256(off + 4 * sizeof(uint32_t) * (size_t)B * S * C);
   pl.off_subK = off;
-  off = align256(off + sizeof(float) * (size_t)B * C * NSUB);
+  off = align256(off + sizeof(uint32_t) * (size_t)B * C * NSUB);
   pl.off_subR = off;
-  off = align256(off + sizeof(float) * (size_t)B * C * NSUB);
+  off = align256(off + sizeof(uint32_t) * (size_t)B * C * NSUB);
   pl.total = off;
+  // Dynamic LDS of the finishing work-groups: 3 * C floats of chunk scratch,
+  // plus the row's partials and sub-block sums when they fit.
+  const size_t words = S * C * 4 + (size_t)C * NSUB;
+  pl.cache = words <= (size_t)MAX_CACHE_WORDS;
+  pl.lds_bytes = (3 * (size_t)C + (pl.cache ? words : 0)) * sizeof(uint32_t);
   return SV_OK;
 }
 
 template <typename ET, bool AL>
-int launch_typed(const Args& a, const Plan& pl, hipStream_t st, hipEvent_t* ev) {
-  const dim3 blk(WG);
-  const int S = 2 * a.K + 1;
+int launch_typed(const Args& a, size_t lds, hipStream_t st, hipEvent_t* ev) {
   if (ev && hipEventRecord(ev[0], st) != hipSuccess) return SV_ERR_HIP;
-  hipLaunchKernelGGL((stats_kernel<ET, AL>), dim3(a.B * S * pl.C), blk, 0, st, a);
+  hipLaunchKernelGGL((stats_kernel<ET, AL>), dim3(a.B * a.GA), dim3(WG), 0, st, a);
   if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
   if (ev && hipEventRecord(ev[1], st) != hipSuccess) return SV_ERR_HIP;
   if (ev && hipEventRecord(ev[2], st) != hipSuccess) return SV_ERR_HIP;
-  hipLaunchKernelGGL((finish_kernel<ET, AL>), dim3(a.B * pl.C), blk, 0, st, a);
+  hipLaunchKernelGGL((finish_kernel<ET, AL>), dim3(a.B * a.C), dim3(WG), lds, st, a);
   if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
   if (ev && hipEventRecord(ev[3], st) != hipSuccess) return SV_ERR_HIP;
   if (ev && hipEventRecord(ev[4], st) != hipSuccess) return SV_ERR_HIP;
@@ -637,11 +761,12 @@ int run(const void* tgt, const void* dft, const int32_t* tok, const float* uni, 
   a.out = out; a.nacc = nacc; a.probs = probs; a.mass = mass;
   char* base = static_cast<char*>(ws);
   a.cnt = reinterpret_cast<unsigned*>(base + pl.off_cnt);
-  a.part = reinterpret_cast<float4*>(base + pl.off_part);
-  a.ldv = reinterpret_cast<float*>(base + pl.off_ldv);
-  a.subK = reinterpret_cast<float*>(base + pl.off_subK);
-  a.subR = reinterpret_cast<float*>(base + pl.off_subR);
+  a.part = reinterpret_cast<uint32_t*>(base + pl.off_part);
+  a.subK = reinterpret_cast<uint32_t*>(base + pl.off_subK);
+  a.subR = reinterpret_cast<uint32_t*>(base + pl.off_subR);
   a.B = B; a.K = K; a.V = V; a.C = pl.C; a.CS = pl.CS; a.topk = topk;
+  a.GA = (2 * K + 1) * pl.C;
+  a.cache = pl.cache ? 1 : 0;
   const size_t esz = dtype == SV_BF16 ? 2 : 4;
   const bool aligned = (reinterpret_cast<uintptr_t>(tgt) % 16 == 0) &&
                        (K == 0 || reinterpret_cast<uintptr_t>(dft) % 16 == 0) &&
@@ -649,8 +774,10 @@ int run(const void* tgt, const void* dft, const int32_t* tok, const float* uni, 
   (void)hipGetLastError();  // start from a clean error state
   hipEvent_t* e = nev ? ev : nullptr;
   if (dtype == SV_BF16)
-    return aligned ? launch_typed<uint16_t, true>(a, pl, st, e) : launch_typed<uint16_t, false>(a, pl, st, e);
-  return aligned ? launch_typed<float, true>(a, pl, st, e) : launch_typed<float, false>(a, pl, st, e);
+    return aligned ? launch_typed<uint16_t, true>(a, pl.lds_bytes, st, e)
+                   : launch_typed<uint16_t, false>(a, pl.lds_bytes, st, e);
+  return aligned ? launch_typed<float, true>(a, pl.lds_bytes, st, e)
+                 : launch_typed<float, false>(a, pl.lds_bytes, st, e);
 }
 
 }  // namespace
