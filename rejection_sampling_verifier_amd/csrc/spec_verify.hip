@@ -69,6 +69,9 @@ constexpr int NSUB = NV_TILE * NWAVE;      // sub-blocks per chunk (one wave x o
 constexpr int MAX_C = 2048;                // vocabulary chunks per position
 constexpr int MAX_SLOTS = 2 * SV_MAX_K + 1;
 constexpr int MAX_CACHE_WORDS = 8192;       // dynamic LDS for a row's published words (32 KiB)
+constexpr int TOPK_FAST_MAX = WG;          // sparse drafts: fast chunk selection for k <= 256
+constexpr int CAND_CAP = 1024;             // LDS candidate buffer of the fast chunk selection
+constexpr int MERGE_SORT_MAX = 4096;       // merge by LDS sort up to this many candidates
 // Longest wait for another work-group's results: 100 ms of the 100 MHz
 // constant clock.  Every wait ends well before that in a correct launch; the
 // bound only guarantees termination.
@@ -88,8 +91,12 @@ struct Args {
   uint32_t* subK;            // [B, C, NSUB] published bonus-position sub-block sums (vs chunk max)
   uint32_t* subR;            // [B, C, NSUB] published residual sub-block sums
   unsigned* cnt;             // [B] finishing work-groups that have arrived
+  uint64_t* cand;            // [B, K, C, topk] chunk candidates of sparse drafts (composites)
+  float4* qstat;             // [B, K] sparse draft: {max kept logit, Z_q, q(d_i), kept count}
+  uint2* kept;               // [B, K, topk] sparse draft: kept (id, logit bits), ascending id
   int B, K, V, C, CS, topk;
   int GA;                    // statistics work-groups per row: (2K+1) * C
+  int merge_sort;            // 1: the merge sorts its C * topk candidates in LDS
   int cache;                 // 1: finishing work-groups keep the row's words in dynamic LDS
 };
 
@@ -175,12 +182,124 @@ __device__ __forceinline__ float tile_max<float, NV_TILE>(const u32x4 (&r)[NV_TI
 }
 
 // ============================================================================
+// Sparse draft truncation ([RheoSampling] section 3): each chunk of a draft
+// position contributes its own min(k, len) best logits (larger value first,
+// then lower id); any logit of the position's global top k is among its
+// chunk's top k under the same order, so the union of the chunk lists holds
+// the global top k, which the merge kernel selects.
+// ============================================================================
+// Exact selection by a 32-step binary search on order keys: the largest key
+// tau with at least kk logits >= tau is the kk-th largest; logits above tau
+// are all kept, ties at tau are kept in increasing id order.
+template <typename ET>
+__device__ void topk_chunk_exact(const u32x4 (&r)[NV_TILE], int lo, int len, int k, uint64_t* dst,
+                                 float* red) {
+  constexpr int VEC = Tr<ET>::VEC;
+  __shared__ int s_pos;
+  const int t = threadIdx.x;
+  const int kk = min(k, len);
+  auto count_keys = [&](uint32_t thr, bool strict) {
+    int n = 0;
+#pragma unroll 1
+    for (int j = 0; j < NV_TILE; ++j)
+      for (int e = 0; e < VEC; ++e) {
+        const uint32_t key = order_key(Tr<ET>::at(r[j], e));
+        const bool valid = (j * WG + t) * VEC + e < len;
+        n += valid && (strict ? key > thr : key >= thr);
+      }
+    return (int)block_sum((float)n, red);  // exact: counts are below 2^24
+  };
+  uint32_t tau = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = tau | (1u << bit);
+    if (count_keys(cand, false) >= kk) tau = cand;
+  }
+  const int above = count_keys(tau, true);
+  if (t == 0) s_pos = 0;
+  __syncthreads();
+#pragma unroll 1
+  for (int j = 0; j < NV_TILE; ++j)
+    for (int e = 0; e < VEC; ++e) {
+      const float x = Tr<ET>::at(r[j], e);
+      const int off = (j * WG + t) * VEC + e;
+      if (off < len && order_key(x) > tau) dst[atomicAdd(&s_pos, 1)] = composite(x, lo + off);
+    }
+  const int need = kk - above;
+  float carry = 0.f;
+#pragma unroll 1
+  for (int j = 0; j < NV_TILE; ++j) {
+    int mine = 0;
+    for (int e = 0; e < VEC; ++e)
+      mine += (j * WG + t) * VEC + e < len && order_key(Tr<ET>::at(r[j], e)) == tau;
+    float ex, tot;
+    block_scan((float)mine, red, ex, tot);
+    int rank = (int)(carry + ex);
+    for (int e = 0; e < VEC; ++e) {
+      const float x = Tr<ET>::at(r[j], e);
+      const int off = (j * WG + t) * VEC + e;
+      if (off < len && order_key(x) == tau) {
+        if (rank < need) dst[above + rank] = composite(x, lo + off);
+        ++rank;
+      }
+    }
+    carry += tot;
+  }
+  for (int i = kk + t; i < k; i += WG) dst[i] = 0;
+}
+
+// Chunk candidates: exactly min(k, len) composites, then zero padding to k.
+// Fast path (k <= 256): the k-th largest of the 256 per-thread maxima is a
+// lower bound of the chunk's k-th largest logit (those k maxima are k
+// logits), so every logit of the chunk's top k is at least that bound.  The
+// few logits that pass it are compacted into LDS and sorted exactly.
+template <typename ET>
+__device__ void topk_chunk(const u32x4 (&r)[NV_TILE], int lo, int len, int k, uint64_t* dst, float* red) {
+  constexpr int VEC = Tr<ET>::VEC;
+  __shared__ uint64_t cbuf[CAND_CAP];
+  __shared__ uint32_t tkey[WG];
+  __shared__ int s_cnt;
+  const int t = threadIdx.x;
+  const int kk = min(k, len);
+  bool done = false;
+  if (k <= TOPK_FAST_MAX) {
+    tkey[t] = order_key(tile_max<ET, NV_TILE>(r));  // padding reads as -inf
+    if (t == 0) s_cnt = 0;
+    __syncthreads();
+    bitonic_sort_desc(tkey, WG);
+    const float bound = key_value(tkey[k - 1]);
+#pragma unroll
+    for (int j = 0; j < NV_TILE; ++j)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float x = Tr<ET>::at(r[j], e);
+        const int off = (j * WG + t) * VEC + e;
+        if (off < len && x >= bound) {
+          const int pos = atomicAdd(&s_cnt, 1);
+          if (pos < CAND_CAP) cbuf[pos] = composite(x, lo + off);
+        }
+      }
+    __syncthreads();
+    const int nc = s_cnt;
+    if (nc <= CAND_CAP) {
+      int P = 1;
+      while (P < nc) P <<= 1;
+      for (int i = nc + t; i < P; i += WG) cbuf[i] = 0;
+      __syncthreads();
+      bitonic_sort_desc(cbuf, P);
+      for (int i = t; i < k; i += WG) dst[i] = i < kk ? cbuf[i] : 0;
+      done = true;
+    }
+  }
+  if (!done) topk_chunk_exact<ET>(r, lo, len, k, dst, red);
+}
+
+// ============================================================================
 // Kernel A: statistics of one (row, position, chunk).
 // ============================================================================
 template <typename ET, bool ALIGNED>
 __global__ __launch_bounds__(WG)
 #if SV_MAX_WAVES > 0
-__attribute__((amdgpu_waves_per_eu(1, SV_MAX_WAVES)))
+__attribute__((amdgpu_waves_per_eu(SV_MAX_WAVES, SV_MAX_WAVES)))
 #endif
 void stats_kernel(Args a) {
   constexpr int VEC = Tr<ET>::VEC;
@@ -226,6 +345,10 @@ void stats_kernel(Args a) {
     return;
   }
 
+  if (is_draft && a.topk > 0) {
+    topk_chunk<ET>(r, lo, len, a.topk, a.cand + (((size_t)b * a.K + pos) * a.C + c) * a.topk, shf);
+    return;
+  }
   const float m = block_max(tile_max<ET, NV_TILE>(r), shf);
   const float s = LOG2E / T;
   // A chunk of -inf only would give exp2(nan): use the reference 0 then
@@ -371,9 +494,13 @@ __device__ void decide_row(const Args& a, int b, RowShared& rs, const RowView& v
       if (!greedy && d >= 0 && d < a.V) {
         const int cd = d / a.CS;
         const float lt = view_part(a, v, b, t, cd, 3);
-        const float lq = view_part(a, v, b, K + 1 + t, cd, 3);
         p = exp2_fast(fmaf(lt, s, -mul_rn(rs.M[t], s))) / rs.Z[t];
-        q = exp2_fast(fmaf(lq, s, -mul_rn(rs.M[K + 1 + t], s))) / rs.Z[K + 1 + t];
+        if (a.topk > 0) {
+          q = a.qstat[(size_t)b * K + t].z;  // q~(d_t) of the truncated draft
+        } else {
+          const float lq = view_part(a, v, b, K + 1 + t, cd, 3);
+          q = exp2_fast(fmaf(lq, s, -mul_rn(rs.M[K + 1 + t], s))) / rs.Z[K + 1 + t];
+        }
       }
       rs.p[t] = p;
       rs.q[t] = q;
@@ -400,11 +527,24 @@ __device__ void decide_row(const Args& a, int b, RowShared& rs, const RowView& v
 // ============================================================================
 template <typename ET, bool ALIGNED>
 __device__ int range_search(const ET* __restrict__ trow, const ET* __restrict__ drow, int start, int len,
-                            float tl, float s, float MSt, float rZt, float MSq, float rZq, float* red) {
+                            float tl, float s, float MSt, float rZt, float MSq, float rZq, float* red,
+                            const uint2* kept = nullptr, int nkept = 0) {
   constexpr int VEC = Tr<ET>::VEC;
   __shared__ int sh_first, sh_last;
+  __shared__ float qloc[64 * VEC];
   const int t = threadIdx.x;
   if (t == 0) { sh_first = INT_MAX; sh_last = -1; }
+  if (kept) {
+    // Sparse draft: q~ is non-zero only at kept ids; place those of this
+    // range (at most 64 * VEC ids) into LDS.
+    for (int i = t; i < 64 * VEC; i += WG) qloc[i] = 0.f;
+    __syncthreads();
+    for (int j = t; j < nkept; j += WG) {
+      const int id = (int)kept[j].x;
+      if (id >= start && id < start + len)
+        qloc[id - start] = exp2_fast(fmaf(__uint_as_float(kept[j].y), s, -MSq)) * rZq;
+    }
+  }
   __syncthreads();
   float carry = 0.f;
   int last_pos = -1;
@@ -420,6 +560,7 @@ __device__ int range_search(const ET* __restrict__ trow, const ET* __restrict__ 
       const float p = exp2_fast(fmaf(Tr<ET>::at(vt, k), s, -MSt)) * rZt;
       float wk = p;
       if (drow) wk = fmaxf(0.f, p - exp2_fast(fmaf(Tr<ET>::at(vq, k), s, -MSq)) * rZq);
+      else if (kept) wk = (e + k < len && e + k < 64 * VEC) ? fmaxf(0.f, p - qloc[e + k]) : p;
       w[k] = wk;
       local += wk;
     }
@@ -568,7 +709,12 @@ __device__ void final_draw(const Args& a, int b, int n, float s, float MSt, floa
     __syncthreads();
   }
   int x = lo;
-  if (slen > 0) x = range_search<ET, ALIGNED>(trow, drow, start, slen, tl, s, MSt, rZt, MSq, rZq, red);
+  const bool sparse = reject && !fallback && a.topk > 0;
+  const uint2* kept = sparse ? a.kept + ((size_t)b * K + n) * a.topk : nullptr;
+  const int nkept = sparse ? (int)a.qstat[(size_t)b * K + n].w : 0;
+  if (slen > 0)
+    x = range_search<ET, ALIGNED>(trow, sparse ? nullptr : drow, start, slen, tl, s, MSt, rZt, MSq, rZq, red,
+                                  kept, nkept);
   int32_t* out = a.out + (size_t)b * (K + 1);
   for (int i = t; i <= K; i += WG) out[i] = i < n ? a.tok[(size_t)b * K + i] : (i == n ? x : -1);
   if (t == 0) {
@@ -576,6 +722,87 @@ __device__ void final_draw(const Args& a, int b, int n, float s, float MSt, floa
     if (a.mass) a.mass[b] = S;
   }
   (void)sh_tl;
+}
+
+// ============================================================================
+// Kernel M (sparse drafts only): one work-group per (row, draft position) of
+// a sampling row.  Selects the kk = min(k, V) best of the C * k chunk
+// candidates (ties to the lower id), which define the truncated draft
+// distribution q~ used at verification; writes the kept (id, logit) list in
+// increasing id order, the max kept logit, Z_q = sum over kept of
+// exp2(fma(l, s, -fl(max*s))) and q~(d_i).
+// ============================================================================
+template <typename ET>
+__global__ __launch_bounds__(WG) void merge_kernel(Args a) {
+  extern __shared__ uint64_t mbuf[];
+  __shared__ uint64_t kbuf[SV_MAX_TOPK];
+  __shared__ float red[NWAVE];
+  __shared__ float s_q;
+  const int i = blockIdx.x % a.K, b = blockIdx.x / a.K;
+  const float T = a.temp[b];
+  if (!is_sampling_temperature(T)) return;
+  const int t = threadIdx.x, C = a.C, k = a.topk, N = C * k, kk = min(k, a.V);
+  const uint64_t* cand = a.cand + ((size_t)b * a.K + i) * N;
+  // The kk best composites (composites are distinct; padding is 0 and every
+  // row has at least kk real candidates).
+  if (a.merge_sort) {
+    int P = 1;
+    while (P < N) P <<= 1;
+    for (int j = t; j < P; j += WG) mbuf[j] = j < N ? cand[j] : 0;
+    __syncthreads();
+    bitonic_sort_desc(mbuf, P);
+    for (int j = t; j < kk; j += WG) kbuf[j] = mbuf[j];
+  } else {
+    uint64_t tau = 0;
+    for (int bit = 63; bit >= 0; --bit) {
+      const uint64_t c2 = tau | (1ull << bit);
+      int n = 0;
+      for (int j = t; j < N; j += WG) n += cand[j] >= c2;
+      if ((int)block_sum((float)n, red) >= kk) tau = c2;
+    }
+    __shared__ int s_pos;
+    if (t == 0) s_pos = 0;
+    __syncthreads();
+    for (int j = t; j < N; j += WG)
+      if (cand[j] >= tau) kbuf[atomicAdd(&s_pos, 1)] = cand[j];
+  }
+  __syncthreads();
+  // Largest kept logit, then re-key by id (ascending) for the residual pass.
+  uint64_t best = 0;
+  for (int j = t; j < kk; j += WG) best = max(best, kbuf[j]);
+  float bv = composite_value(best);
+  if (best == 0) bv = NEG_INF;
+  const float m = block_max(bv, red);
+  for (int j = t; j < kk; j += WG) {
+    const uint64_t c = kbuf[j];
+    kbuf[j] = ((uint64_t)(0xFFFFFFFFu - (uint32_t)composite_id(c)) << 32) | __float_as_uint(composite_value(c));
+  }
+  int P = 1;
+  while (P < kk) P <<= 1;
+  for (int j = kk + t; j < P; j += WG) kbuf[j] = 0;
+  __syncthreads();
+  bitonic_sort_desc(kbuf, P);
+  const float s = LOG2E / T;
+  const float ms = mul_rn(m, s);
+  const int d = a.tok[(size_t)b * a.K + i];
+  if (t == 0) s_q = 0.f;
+  uint2* kept = a.kept + ((size_t)b * a.K + i) * k;
+  float z = 0.f;
+  for (int j = t; j < kk; j += WG) {
+    const uint64_t e = kbuf[j];
+    const int id = (int)(0xFFFFFFFFu - (uint32_t)(e >> 32));
+    const float l = __uint_as_float((uint32_t)e);
+    kept[j] = make_uint2((uint32_t)id, (uint32_t)e);
+    z += exp2_fast(fmaf(l, s, -ms));
+  }
+  const float Z = block_sum(z, red);
+  for (int j = t; j < kk; j += WG) {
+    const uint64_t e = kbuf[j];
+    if ((int)(0xFFFFFFFFu - (uint32_t)(e >> 32)) == d)
+      s_q = exp2_fast(fmaf(__uint_as_float((uint32_t)e), s, -ms)) / Z;
+  }
+  __syncthreads();
+  if (t == 0) a.qstat[(size_t)b * a.K + i] = make_float4(m, Z, s_q, (float)kk);
 }
 
 // ============================================================================
@@ -637,28 +864,81 @@ __global__ __launch_bounds__(WG) void finish_kernel(Args a) {
     return;
   }
   // Rejected at position n: residual max(0, p_n - q_n) over this chunk.
-  const float MSq = mul_rn(rs.M[K + 1 + n], s), rZq = 1.f / rs.Z[K + 1 + n];
   const int lo = c * a.CS;
   const int len = min(a.CS, a.V - lo);
-  u32x4 rt[NV_TILE], rq[NV_TILE];
-  load_tile<ET, ALIGNED, NV_TILE>(target_row<ET>(a, b, n), lo, len, rt);
-  load_tile<ET, ALIGNED, NV_TILE>(draft_row<ET>(a, b, n), lo, len, rq);
-#pragma unroll
-  for (int j = 0; j < NV_TILE; ++j) {
-    float w0 = 0.f, w1 = 0.f;
-#pragma unroll
-    for (int k = 0; k < VEC; k += 2) {
-      const float p0 = exp2_fast(fmaf(Tr<ET>::at(rt[j], k), s, -MSt)) * rZt;
-      const float q0 = exp2_fast(fmaf(Tr<ET>::at(rq[j], k), s, -MSq)) * rZq;
-      const float p1 = exp2_fast(fmaf(Tr<ET>::at(rt[j], k + 1), s, -MSt)) * rZt;
-      const float q1 = exp2_fast(fmaf(Tr<ET>::at(rq[j], k + 1), s, -MSq)) * rZq;
-      w0 += fmaxf(0.f, p0 - q0);
-      w1 += fmaxf(0.f, p1 - q1);
+  float MSq, rZq;
+  if (a.topk > 0) {
+    // Sparse draft: q~ is non-zero only at the kept ids, so the residual of
+    // a sub-block is sum(p) - sum over its kept ids of min(p, q~).  Only the
+    // target row is re-read.
+    const float4 qs = a.qstat[(size_t)b * K + n];
+    MSq = mul_rn(qs.x, s);
+    rZq = 1.f / qs.y;
+    const int nkept = (int)qs.w;
+    const uint2* kept = a.kept + ((size_t)b * K + n) * a.topk;
+    const ET* trow = target_row<ET>(a, b, n);
+    u32x4 rt[NV_TILE];
+    load_tile<ET, ALIGNED, NV_TILE>(trow, lo, len, rt);
+    // Correction of each kept id in this chunk, in id order, with its
+    // sub-block (the entries of one sub-block are contiguous).
+    __shared__ float corr[SV_MAX_TOPK];
+    __shared__ int csub[SV_MAX_TOPK];
+    for (int j = t; j < nkept; j += WG) {
+      const int id = (int)kept[j].x;
+      float cv = 0.f;
+      int sb = -1;
+      if (id >= lo && id < lo + len) {
+        const float pv = exp2_fast(fmaf(Tr<ET>::load1(trow + id), s, -MSt)) * rZt;
+        const float qv = exp2_fast(fmaf(__uint_as_float(kept[j].y), s, -MSq)) * rZq;
+        cv = fminf(pv, qv);
+        const int vi = (id - lo) / VEC;            // vector index in the chunk
+        sb = (vi / WG) * NWAVE + (vi % WG) / 64;   // sub-block (j, wave)
+      }
+      corr[j] = cv;
+      csub[j] = sb;
     }
-    const float v = wave_sum(w0 + w1);
-    if (lane == 0) shsub[j * NWAVE + wave] = v;
+#pragma unroll
+    for (int j = 0; j < NV_TILE; ++j) {
+      float w0 = 0.f, w1 = 0.f;
+#pragma unroll
+      for (int k = 0; k < VEC; k += 2) {
+        w0 += exp2_fast(fmaf(Tr<ET>::at(rt[j], k), s, -MSt)) * rZt;
+        w1 += exp2_fast(fmaf(Tr<ET>::at(rt[j], k + 1), s, -MSt)) * rZt;
+      }
+      const float v = wave_sum(w0 + w1);
+      if (lane == 0) shsub[j * NWAVE + wave] = v;
+    }
+    __syncthreads();
+    if (t < NSUB) {
+      float cs = 0.f;
+      for (int j = 0; j < nkept; ++j)
+        if (csub[j] == t) cs += corr[j];
+      shsub[t] = fmaxf(0.f, shsub[t] - cs);
+    }
+    __syncthreads();
+  } else {
+    MSq = mul_rn(rs.M[K + 1 + n], s);
+    rZq = 1.f / rs.Z[K + 1 + n];
+    u32x4 rt[NV_TILE], rq[NV_TILE];
+    load_tile<ET, ALIGNED, NV_TILE>(target_row<ET>(a, b, n), lo, len, rt);
+    load_tile<ET, ALIGNED, NV_TILE>(draft_row<ET>(a, b, n), lo, len, rq);
+#pragma unroll
+    for (int j = 0; j < NV_TILE; ++j) {
+      float w0 = 0.f, w1 = 0.f;
+#pragma unroll
+      for (int k = 0; k < VEC; k += 2) {
+        const float p0 = exp2_fast(fmaf(Tr<ET>::at(rt[j], k), s, -MSt)) * rZt;
+        const float q0 = exp2_fast(fmaf(Tr<ET>::at(rq[j], k), s, -MSq)) * rZq;
+        const float p1 = exp2_fast(fmaf(Tr<ET>::at(rt[j], k + 1), s, -MSt)) * rZt;
+        const float q1 = exp2_fast(fmaf(Tr<ET>::at(rq[j], k + 1), s, -MSq)) * rZq;
+        w0 += fmaxf(0.f, p0 - q0);
+        w1 += fmaxf(0.f, p1 - q1);
+      }
+      const float v = wave_sum(w0 + w1);
+      if (lane == 0) shsub[j * NWAVE + wave] = v;
+    }
+    __syncthreads();
   }
-  __syncthreads();
   uint32_t* subR_row = a.subR + (size_t)b * C * NSUB;
   if (t < NSUB) pub_f32(subR_row + (size_t)c * NSUB + t, shsub[t]);
   // Count this work-group.  Its sums need no ordering with the count: the
@@ -684,7 +964,10 @@ __global__ __launch_bounds__(WG) void finish_kernel(Args a) {
 // ============================================================================
 struct Plan {
   int C = 0, CS = 0;
-  size_t off_cnt = 0, off_part = 0, off_subK = 0, off_subR = 0, total = 0;
+  size_t off_cnt = 0, off_part = 0, off_subK = 0, off_subR = 0, off_cand = 0, off_qstat = 0, off_kept = 0,
+         total = 0;
+  bool merge_sort = false;  // sparse drafts: the merge sorts its candidates in LDS
+  size_t merge_lds = 0;
   bool cache = false;       // finishing work-groups copy the row's words to LDS
   size_t lds_bytes = 0;     // dynamic LDS of the finishing work-groups
 };
@@ -694,7 +977,7 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 int make_plan(int B, int K, int V, int topk, int dtype, Plan& pl) {
   if (B < 1 || K < 0 || V < 1 || topk < 0 || (dtype != SV_BF16 && dtype != SV_F32)) return SV_ERR_ARG;
   if (K > SV_MAX_K) return SV_ERR_UNSUPPORTED;
-  if (topk > 0 && topk < V) return SV_ERR_UNSUPPORTED;  // sparse drafts: not built yet
+  if (topk > SV_MAX_TOPK) return SV_ERR_UNSUPPORTED;
   const long vec = dtype == SV_BF16 ? 8 : 4;
   const long tile = (long)WG * NV_TILE * vec;
   long C = (V + tile - 1) / tile;
@@ -716,6 +999,19 @@ int make_plan(int B, int K, int V, int topk, int dtype, Plan& pl) {
   off = align256(off + sizeof(uint32_t) * (size_t)B * C * NSUB);
   pl.off_subR = off;
   off = align256(off + sizeof(uint32_t) * (size_t)B * C * NSUB);
+  if (topk > 0) {
+    const size_t slots = (size_t)B * K;
+    pl.off_cand = off;
+    off = align256(off + sizeof(uint64_t) * slots * C * topk);
+    pl.off_qstat = off;
+    off = align256(off + sizeof(float4) * slots);
+    pl.off_kept = off;
+    off = align256(off + sizeof(uint2) * slots * topk);
+    long P = 1;
+    while (P < C * (long)topk) P <<= 1;
+    pl.merge_sort = P <= MERGE_SORT_MAX;
+    pl.merge_lds = pl.merge_sort ? (size_t)P * sizeof(uint64_t) : 0;
+  }
   pl.total = off;
   // Dynamic LDS of the finishing work-groups: 3 * C floats of chunk scratch,
   // plus the row's partials and sub-block sums when they fit.
@@ -726,11 +1022,15 @@ int make_plan(int B, int K, int V, int topk, int dtype, Plan& pl) {
 }
 
 template <typename ET, bool AL>
-int launch_typed(const Args& a, size_t lds, hipStream_t st, hipEvent_t* ev) {
+int launch_typed(const Args& a, size_t lds, size_t merge_lds, hipStream_t st, hipEvent_t* ev) {
   if (ev && hipEventRecord(ev[0], st) != hipSuccess) return SV_ERR_HIP;
   hipLaunchKernelGGL((stats_kernel<ET, AL>), dim3(a.B * a.GA), dim3(WG), 0, st, a);
   if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
   if (ev && hipEventRecord(ev[1], st) != hipSuccess) return SV_ERR_HIP;
+  if (a.topk > 0 && a.K > 0) {
+    hipLaunchKernelGGL((merge_kernel<ET>), dim3(a.B * a.K), dim3(WG), merge_lds, st, a);
+    if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
+  }
   if (ev && hipEventRecord(ev[2], st) != hipSuccess) return SV_ERR_HIP;
   hipLaunchKernelGGL((finish_kernel<ET, AL>), dim3(a.B * a.C), dim3(WG), lds, st, a);
   if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
@@ -767,6 +1067,10 @@ int run(const void* tgt, const void* dft, const int32_t* tok, const float* uni, 
   a.B = B; a.K = K; a.V = V; a.C = pl.C; a.CS = pl.CS; a.topk = topk;
   a.GA = (2 * K + 1) * pl.C;
   a.cache = pl.cache ? 1 : 0;
+  a.merge_sort = pl.merge_sort ? 1 : 0;
+  a.cand = topk > 0 ? reinterpret_cast<uint64_t*>(base + pl.off_cand) : nullptr;
+  a.qstat = topk > 0 ? reinterpret_cast<float4*>(base + pl.off_qstat) : nullptr;
+  a.kept = topk > 0 ? reinterpret_cast<uint2*>(base + pl.off_kept) : nullptr;
   const size_t esz = dtype == SV_BF16 ? 2 : 4;
   const bool aligned = (reinterpret_cast<uintptr_t>(tgt) % 16 == 0) &&
                        (K == 0 || reinterpret_cast<uintptr_t>(dft) % 16 == 0) &&
@@ -774,10 +1078,10 @@ int run(const void* tgt, const void* dft, const int32_t* tok, const float* uni, 
   (void)hipGetLastError();  // start from a clean error state
   hipEvent_t* e = nev ? ev : nullptr;
   if (dtype == SV_BF16)
-    return aligned ? launch_typed<uint16_t, true>(a, pl.lds_bytes, st, e)
-                   : launch_typed<uint16_t, false>(a, pl.lds_bytes, st, e);
-  return aligned ? launch_typed<float, true>(a, pl.lds_bytes, st, e)
-                 : launch_typed<float, false>(a, pl.lds_bytes, st, e);
+    return aligned ? launch_typed<uint16_t, true>(a, pl.lds_bytes, pl.merge_lds, st, e)
+                   : launch_typed<uint16_t, false>(a, pl.lds_bytes, pl.merge_lds, st, e);
+  return aligned ? launch_typed<float, true>(a, pl.lds_bytes, pl.merge_lds, st, e)
+                 : launch_typed<float, false>(a, pl.lds_bytes, pl.merge_lds, st, e);
 }
 
 }  // namespace

@@ -238,3 +238,44 @@ __device__ __forceinline__ float block_scan(float v, float* sh, float& excl, flo
 }
 
 }  // namespace sv
+
+namespace sv {
+
+// ---- ordering keys for the sparse-draft (top-k) selection -------------------
+// order_key maps a float to an unsigned key with the same order (-0 and +0
+// map to the same key, as they compare equal).  A candidate is the 64-bit
+// composite (order_key(value) << 32) | ~id: larger composites are better,
+// i.e. a larger value, or an equal value at a lower id.
+__device__ __forceinline__ uint32_t order_key(float v) {
+  uint32_t u = __float_as_uint(v);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+__device__ __forceinline__ uint64_t composite(float v, int id) {
+  return ((uint64_t)order_key(v) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)id);
+}
+__device__ __forceinline__ int composite_id(uint64_t c) { return (int)(0xFFFFFFFFu - (uint32_t)c); }
+__device__ __forceinline__ float composite_value(uint64_t c) { return key_value((uint32_t)(c >> 32)); }
+
+// Bitonic sort of n (a power of two) LDS entries into descending order, by
+// the whole block.
+template <typename T>
+__device__ void bitonic_sort_desc(T* x, int n) {
+  for (int size = 2; size <= n; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = threadIdx.x; i < n / 2; i += WG) {
+        const int lo = 2 * i - (i & (stride - 1));
+        const int hi = lo + stride;
+        const bool desc = (lo & size) == 0;
+        const T u = x[lo], v = x[hi];
+        if ((u < v) == desc) { x[lo] = v; x[hi] = u; }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+}  // namespace sv

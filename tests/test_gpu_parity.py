@@ -45,6 +45,17 @@ SMALL = {
     "hot-T": _case(B=32, temperature=4.0, seed=20),     # flat: most CDF gaps < 1e-5
     "cold-T": _case(temperature=0.05, seed=21),
     "low-agreement": _case(draft_sigma=3.0, seed=22),
+    # sparse drafts (top-k truncation of the draft)
+    "topk128-bf16": _case(B=8, topk=128, seed=23),
+    "topk1": _case(topk=1, seed=24),
+    "topk3-ragged": _case(V=40001, topk=3, seed=25),
+    "topk300-exact-path": _case(topk=300, seed=26),
+    "topk1024-exact-path": _case(B=3, topk=1024, seed=27),
+    "topk-f32": _case(dtype=W.F32, V=20001, topk=64, seed=28),
+    "topk-mixed-greedy": _case(B=10, greedy_rows=4, topk=128, seed=29),
+    "topk-ge-V": _case(V=3000, topk=3000, seed=30),
+    "topk-small-V": _case(V=200, peaks=3, topk=128, seed=31),
+    "topk-K0": _case(K=0, topk=16, seed=32),
 }
 
 
@@ -147,7 +158,7 @@ def _full(c):
     return _FULL[c]
 
 
-@pytest.mark.parametrize("c", [1, 2, 3])
+@pytest.mark.parametrize("c", [1, 2, 3, 4])
 def test_full_config_sampled_rows(c):
     d = _full(c)
     B = d["target"].shape[0]
@@ -208,4 +219,32 @@ def test_neg_inf_blocks_at_cold_temperature(dtype):
     d["draft"][2, :, 29000:] = ninf
     gpu = run_gpu(d)
     assert np.isfinite(gpu[3]).all() and np.isfinite(gpu[2]).all()
+    check_rows(d, gpu)
+
+
+def test_topk_ties_take_lowest_ids():
+    """Draft logits with massive exact ties around the top-k boundary (the
+    fast chunk selection overflows and the exact path decides)."""
+    d = W.make(_case(B=4, K=2, V=30000, topk=100, seed=46))
+    vals = np.array([2.0, 2.0, 3.0, 1.0], np.float32)
+    rng = np.random.default_rng(46)
+    for b in range(4):
+        for i in range(2):
+            row = vals[rng.integers(0, 4, 30000)]
+            d["draft"][b, i] = W.bf16_bits(row)
+            # a draft token inside the kept set: one of the lowest-id 3.0s
+            d["tokens"][b, i] = int(np.flatnonzero(row == 3.0)[b])
+    gpu = run_gpu(d)
+    check_rows(d, gpu)
+
+
+def test_topk_draft_token_outside_kept_set():
+    """A draft token outside the kept set has q~ = 0: it is accepted iff p > 0
+    (the limit of u*q < p)."""
+    d = W.make(_case(B=4, K=3, V=20000, topk=8, seed=47))
+    dv = W.bf16_to_f32(d["draft"])
+    for b in range(4):
+        d["tokens"][b, 0] = int(np.argmin(dv[b, 0]))
+    gpu = run_gpu(d)
+    assert (gpu[2][:, 0, 1] == 0).all()
     check_rows(d, gpu)
