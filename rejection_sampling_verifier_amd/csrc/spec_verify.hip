@@ -71,7 +71,7 @@ constexpr int MAX_SLOTS = 2 * SV_MAX_K + 1;
 constexpr int MAX_CACHE_WORDS = 8192;       // dynamic LDS for a row's published words (32 KiB)
 constexpr int TOPK_FAST_MAX = WG;          // sparse drafts: fast chunk selection for k <= 256
 constexpr int CAND_CAP = 1024;             // LDS candidate buffer of the fast chunk selection
-constexpr int MERGE_SORT_MAX = 4096;       // merge by LDS sort up to this many candidates
+constexpr int MERGE_SORT_MAX = 4096;       // merge candidates held in LDS up to this many
 // Longest wait for another work-group's results: 100 ms of the 100 MHz
 // constant clock.  Every wait ends well before that in a correct launch; the
 // bound only guarantees termination.
@@ -96,7 +96,7 @@ struct Args {
   uint2* kept;               // [B, K, topk] sparse draft: kept (id, logit bits), ascending id
   int B, K, V, C, CS, topk;
   int GA;                    // statistics work-groups per row: (2K+1) * C
-  int merge_sort;            // 1: the merge sorts its C * topk candidates in LDS
+  int merge_sort;            // 1: the merge keeps its C * topk candidates in LDS
   int cache;                 // 1: finishing work-groups keep the row's words in dynamic LDS
 };
 
@@ -188,16 +188,29 @@ __device__ __forceinline__ float tile_max<float, NV_TILE>(const u32x4 (&r)[NV_TI
 // chunk's top k under the same order, so the union of the chunk lists holds
 // the global top k, which the merge kernel selects.
 // ============================================================================
+// Rank selection: entries x[0..n) are distinct composites in LDS; writes the
+// best kk of them to dst in descending order (an entry's rank is the number
+// of entries better than it), then zero padding up to k.
+__device__ void write_ranked(const uint64_t* x, int n, int kk, int k, uint64_t* dst) {
+  for (int i = threadIdx.x; i < n; i += WG) {
+    const uint64_t v = x[i];
+    int rank = 0;
+    for (int j = 0; j < n; ++j) rank += x[j] > v;
+    if (rank < kk) dst[rank] = v;
+  }
+  for (int i = kk + threadIdx.x; i < k; i += WG) dst[i] = 0;
+}
+
 // Exact selection by a 32-step binary search on order keys: the largest key
 // tau with at least kk logits >= tau is the kk-th largest; logits above tau
-// are all kept, ties at tau are kept in increasing id order.
+// are all kept, ties at tau are kept in increasing id order.  The kk kept
+// composites are left in buf[0..kk).
 template <typename ET>
-__device__ void topk_chunk_exact(const u32x4 (&r)[NV_TILE], int lo, int len, int k, uint64_t* dst,
+__device__ void topk_chunk_exact(const u32x4 (&r)[NV_TILE], int lo, int len, int kk, uint64_t* buf,
                                  float* red) {
   constexpr int VEC = Tr<ET>::VEC;
   __shared__ int s_pos;
   const int t = threadIdx.x;
-  const int kk = min(k, len);
   auto count_keys = [&](uint32_t thr, bool strict) {
     int n = 0;
 #pragma unroll 1
@@ -222,7 +235,7 @@ __device__ void topk_chunk_exact(const u32x4 (&r)[NV_TILE], int lo, int len, int
     for (int e = 0; e < VEC; ++e) {
       const float x = Tr<ET>::at(r[j], e);
       const int off = (j * WG + t) * VEC + e;
-      if (off < len && order_key(x) > tau) dst[atomicAdd(&s_pos, 1)] = composite(x, lo + off);
+      if (off < len && order_key(x) > tau) buf[atomicAdd(&s_pos, 1)] = composite(x, lo + off);
     }
   const int need = kk - above;
   float carry = 0.f;
@@ -238,61 +251,72 @@ __device__ void topk_chunk_exact(const u32x4 (&r)[NV_TILE], int lo, int len, int
       const float x = Tr<ET>::at(r[j], e);
       const int off = (j * WG + t) * VEC + e;
       if (off < len && order_key(x) == tau) {
-        if (rank < need) dst[above + rank] = composite(x, lo + off);
+        if (rank < need) buf[above + rank] = composite(x, lo + off);
         ++rank;
       }
     }
     carry += tot;
   }
-  for (int i = kk + t; i < k; i += WG) dst[i] = 0;
+  __syncthreads();
 }
 
-// Chunk candidates: exactly min(k, len) composites, then zero padding to k.
-// Fast path (k <= 256): the k-th largest of the 256 per-thread maxima is a
-// lower bound of the chunk's k-th largest logit (those k maxima are k
-// logits), so every logit of the chunk's top k is at least that bound.  The
-// few logits that pass it are compacted into LDS and sorted exactly.
+// Chunk candidates: exactly min(k, len) composites in descending order, then
+// zero padding to k.  Fast path (k <= 256): in each wave, the ceil(k/4)-th
+// largest of its 64 per-thread maxima is found by a ballot binary search;
+// the smallest of the four is a lower bound of the chunk's k-th largest logit
+// (each wave has ceil(k/4) logits at or above it), so every logit of the
+// chunk's top k passes it.  The few that do are compacted into LDS and
+// ranked exactly.
 template <typename ET>
 __device__ void topk_chunk(const u32x4 (&r)[NV_TILE], int lo, int len, int k, uint64_t* dst, float* red) {
   constexpr int VEC = Tr<ET>::VEC;
   __shared__ uint64_t cbuf[CAND_CAP];
-  __shared__ uint32_t tkey[WG];
-  __shared__ int s_cnt;
-  const int t = threadIdx.x;
+  __shared__ uint32_t wkey[NWAVE];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int kk = min(k, len);
   bool done = false;
   if (k <= TOPK_FAST_MAX) {
-    tkey[t] = order_key(tile_max<ET, NV_TILE>(r));  // padding reads as -inf
-    if (t == 0) s_cnt = 0;
+    const uint32_t key = order_key(tile_max<ET, NV_TILE>(r));  // padding reads as -inf
+    const int m = (k + NWAVE - 1) / NWAVE;
+    uint32_t tau = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = tau | (1u << bit);
+      if (__popcll(__ballot(key >= cand)) >= m) tau = cand;
+    }
+    if (lane == 0) wkey[wave] = tau;
     __syncthreads();
-    bitonic_sort_desc(tkey, WG);
-    const float bound = key_value(tkey[k - 1]);
+    const float bound = key_value(min(min(wkey[0], wkey[1]), min(wkey[2], wkey[3])));
+    // Compaction without atomics: count, block scan, write.
+    int mine = 0;
 #pragma unroll
     for (int j = 0; j < NV_TILE; ++j)
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        const float x = Tr<ET>::at(r[j], e);
-        const int off = (j * WG + t) * VEC + e;
-        if (off < len && x >= bound) {
-          const int pos = atomicAdd(&s_cnt, 1);
-          if (pos < CAND_CAP) cbuf[pos] = composite(x, lo + off);
-        }
-      }
-    __syncthreads();
-    const int nc = s_cnt;
+      for (int e = 0; e < VEC; ++e)
+        mine += (j * WG + t) * VEC + e < len && Tr<ET>::at(r[j], e) >= bound;
+    float ex, tot;
+    block_scan((float)mine, red, ex, tot);
+    const int nc = (int)tot;
     if (nc <= CAND_CAP) {
-      int P = 1;
-      while (P < nc) P <<= 1;
-      for (int i = nc + t; i < P; i += WG) cbuf[i] = 0;
+      int pos = (int)ex;
+#pragma unroll
+      for (int j = 0; j < NV_TILE; ++j)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const float x = Tr<ET>::at(r[j], e);
+          const int off = (j * WG + t) * VEC + e;
+          if (off < len && x >= bound) cbuf[pos++] = composite(x, lo + off);
+        }
       __syncthreads();
-      bitonic_sort_desc(cbuf, P);
-      for (int i = t; i < k; i += WG) dst[i] = i < kk ? cbuf[i] : 0;
+      write_ranked(cbuf, nc, kk, k, dst);
       done = true;
     }
+    __syncthreads();
   }
-  if (!done) topk_chunk_exact<ET>(r, lo, len, k, dst, red);
+  if (!done) {
+    topk_chunk_exact<ET>(r, lo, len, kk, cbuf, red);
+    write_ranked(cbuf, kk, kk, k, dst);
+  }
 }
-
 // ============================================================================
 // Kernel A: statistics of one (row, position, chunk).
 // ============================================================================
@@ -735,72 +759,95 @@ __device__ void final_draw(const Args& a, int b, int n, float s, float MSt, floa
 template <typename ET>
 __global__ __launch_bounds__(WG) void merge_kernel(Args a) {
   extern __shared__ uint64_t mbuf[];
-  __shared__ uint64_t kbuf[SV_MAX_TOPK];
+  __shared__ uint64_t sel[SV_MAX_TOPK];
   __shared__ float red[NWAVE];
   __shared__ float s_q;
   const int i = blockIdx.x % a.K, b = blockIdx.x / a.K;
   const float T = a.temp[b];
   if (!is_sampling_temperature(T)) return;
   const int t = threadIdx.x, C = a.C, k = a.topk, N = C * k, kk = min(k, a.V);
-  const uint64_t* cand = a.cand + ((size_t)b * a.K + i) * N;
-  // The kk best composites (composites are distinct; padding is 0 and every
-  // row has at least kk real candidates).
+  const uint64_t* g = a.cand + ((size_t)b * a.K + i) * N;
   if (a.merge_sort) {
-    int P = 1;
-    while (P < N) P <<= 1;
-    for (int j = t; j < P; j += WG) mbuf[j] = j < N ? cand[j] : 0;
+    // Pairwise merge tree of the C sorted chunk lists, each merge truncated
+    // to kk entries; output position o of a merge is found by a binary search
+    // on how many of its first o entries come from the first list (entries
+    // of the first list go first on ties, which only zero padding has).
+    uint64_t* src = mbuf;
+    uint64_t* dst = mbuf + N;
+    for (int j = t; j < N; j += WG) src[j] = g[j];
     __syncthreads();
-    bitonic_sort_desc(mbuf, P);
-    for (int j = t; j < kk; j += WG) kbuf[j] = mbuf[j];
-  } else {
-    uint64_t tau = 0;
-    for (int bit = 63; bit >= 0; --bit) {
-      const uint64_t c2 = tau | (1ull << bit);
-      int n = 0;
-      for (int j = t; j < N; j += WG) n += cand[j] >= c2;
-      if ((int)block_sum((float)n, red) >= kk) tau = c2;
+    int nl = C, len = k;
+    while (nl > 1) {
+      const int nout = (nl + 1) / 2, lout = min(kk, 2 * len);
+      for (int idx = t; idx < nout * lout; idx += WG) {
+        const int q = idx / lout, o = idx % lout;
+        const uint64_t* A = src + (size_t)(2 * q) * len;
+        uint64_t v;
+        if (2 * q + 1 < nl) {
+          const uint64_t* Bl = A + len;
+          int ilo = max(0, o - len), ihi = min(o, len);
+          while (ilo < ihi) {
+            const int ii = (ilo + ihi + 1) >> 1;
+            if (o - ii >= len || A[ii - 1] >= Bl[o - ii]) ilo = ii; else ihi = ii - 1;
+          }
+          const int ia = ilo, jb = o - ilo;
+          v = (jb >= len || (ia < len && A[ia] >= Bl[jb])) ? A[ia] : Bl[jb];
+        } else {
+          v = o < len ? A[o] : 0;
+        }
+        dst[(size_t)q * lout + o] = v;
+      }
+      __syncthreads();
+      uint64_t* tmp = src; src = dst; dst = tmp;
+      nl = nout;
+      len = lout;
     }
-    __shared__ int s_pos;
-    if (t == 0) s_pos = 0;
-    __syncthreads();
-    for (int j = t; j < N; j += WG)
-      if (cand[j] >= tau) kbuf[atomicAdd(&s_pos, 1)] = cand[j];
+    for (int j = t; j < kk; j += WG) sel[j] = src[j];
+  } else {
+    // Candidates in global memory: global rank of each candidate = its
+    // position in its own sorted list plus, for every other list, the number
+    // of entries above it (binary search).  Composites are distinct.
+    for (int j = t; j < N; j += WG) {
+      const uint64_t v = g[j];
+      if (v == 0) continue;
+      const int c0 = j / k;
+      int rank = j - c0 * k;
+      for (int c = 0; c < C && rank < kk; ++c) {
+        if (c == c0) continue;
+        const uint64_t* L = g + (size_t)c * k;
+        int lo = 0, hi = k;  // first index with L[idx] < v
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (L[mid] > v) lo = mid + 1; else hi = mid;
+        }
+        rank += lo;
+      }
+      if (rank < kk) sel[rank] = v;
+    }
   }
   __syncthreads();
-  // Largest kept logit, then re-key by id (ascending) for the residual pass.
-  uint64_t best = 0;
-  for (int j = t; j < kk; j += WG) best = max(best, kbuf[j]);
-  float bv = composite_value(best);
-  if (best == 0) bv = NEG_INF;
-  const float m = block_max(bv, red);
-  for (int j = t; j < kk; j += WG) {
-    const uint64_t c = kbuf[j];
-    kbuf[j] = ((uint64_t)(0xFFFFFFFFu - (uint32_t)composite_id(c)) << 32) | __float_as_uint(composite_value(c));
-  }
-  int P = 1;
-  while (P < kk) P <<= 1;
-  for (int j = kk + t; j < P; j += WG) kbuf[j] = 0;
-  __syncthreads();
-  bitonic_sort_desc(kbuf, P);
+  const float m = composite_value(sel[0]);  // the largest kept logit
   const float s = LOG2E / T;
   const float ms = mul_rn(m, s);
   const int d = a.tok[(size_t)b * a.K + i];
   if (t == 0) s_q = 0.f;
+  // Kept list in increasing id order (rank among the kept by id).
   uint2* kept = a.kept + ((size_t)b * a.K + i) * k;
   float z = 0.f;
   for (int j = t; j < kk; j += WG) {
-    const uint64_t e = kbuf[j];
-    const int id = (int)(0xFFFFFFFFu - (uint32_t)(e >> 32));
-    const float l = __uint_as_float((uint32_t)e);
-    kept[j] = make_uint2((uint32_t)id, (uint32_t)e);
-    z += exp2_fast(fmaf(l, s, -ms));
+    const uint64_t v = sel[j];
+    const int id = composite_id(v);
+    int pos = 0;
+    for (int q = 0; q < kk; ++q) pos += composite_id(sel[q]) < id;
+    const float l = composite_value(v);
+    kept[pos] = make_uint2((uint32_t)id, __float_as_uint(l));
   }
+  // Z_q in a fixed order: entries of sel[] (descending by value) strided by
+  // thread, then the block sum.
+  for (int j = t; j < kk; j += WG) z += exp2_fast(fmaf(composite_value(sel[j]), s, -ms));
   const float Z = block_sum(z, red);
-  for (int j = t; j < kk; j += WG) {
-    const uint64_t e = kbuf[j];
-    if ((int)(0xFFFFFFFFu - (uint32_t)(e >> 32)) == d)
-      s_q = exp2_fast(fmaf(__uint_as_float((uint32_t)e), s, -ms)) / Z;
-  }
+  for (int j = t; j < kk; j += WG)
+    if (composite_id(sel[j]) == d) s_q = exp2_fast(fmaf(composite_value(sel[j]), s, -ms)) / Z;
   __syncthreads();
   if (t == 0) a.qstat[(size_t)b * a.K + i] = make_float4(m, Z, s_q, (float)kk);
 }
@@ -1007,10 +1054,8 @@ int make_plan(int B, int K, int V, int topk, int dtype, Plan& pl) {
     off = align256(off + sizeof(float4) * slots);
     pl.off_kept = off;
     off = align256(off + sizeof(uint2) * slots * topk);
-    long P = 1;
-    while (P < C * (long)topk) P <<= 1;
-    pl.merge_sort = P <= MERGE_SORT_MAX;
-    pl.merge_lds = pl.merge_sort ? (size_t)P * sizeof(uint64_t) : 0;
+    pl.merge_sort = C * (long)topk <= MERGE_SORT_MAX;
+    pl.merge_lds = pl.merge_sort ? 2 * (size_t)C * topk * sizeof(uint64_t) : 0;
   }
   pl.total = off;
   // Dynamic LDS of the finishing work-groups: 3 * C floats of chunk scratch,
