@@ -70,8 +70,8 @@ constexpr int MAX_C = 2048;                // vocabulary chunks per position
 constexpr int MAX_SLOTS = 2 * SV_MAX_K + 1;
 constexpr int MAX_CACHE_WORDS = 8192;       // dynamic LDS for a row's published words (32 KiB)
 constexpr int TOPK_FAST_MAX = WG;          // sparse drafts: fast chunk selection for k <= 256
-constexpr int CAND_CAP = 1024;             // LDS candidate buffer of the fast chunk selection
-constexpr int MERGE_SORT_MAX = 4096;       // merge candidates held in LDS up to this many
+constexpr int CAND_CAP = SV_MAX_TOPK;      // LDS buffer of the exact chunk selection
+constexpr int WCAP = 256;                  // candidate list length per wave of a chunk
 // Longest wait for another work-group's results: 100 ms of the 100 MHz
 // constant clock.  Every wait ends well before that in a correct launch; the
 // bound only guarantees termination.
@@ -91,12 +91,12 @@ struct Args {
   uint32_t* subK;            // [B, C, NSUB] published bonus-position sub-block sums (vs chunk max)
   uint32_t* subR;            // [B, C, NSUB] published residual sub-block sums
   unsigned* cnt;             // [B] finishing work-groups that have arrived
-  uint64_t* cand;            // [B, K, C, topk] chunk candidates of sparse drafts (composites)
+  uint64_t* cand;            // [B, K, C, NWAVE, WCAP] chunk candidate lists of sparse drafts
+  int* ccnt;                 // [B, K, C, NWAVE] lengths of those lists
   float4* qstat;             // [B, K] sparse draft: {max kept logit, Z_q, q(d_i), kept count}
   uint2* kept;               // [B, K, topk] sparse draft: kept (id, logit bits), ascending id
   int B, K, V, C, CS, topk;
   int GA;                    // statistics work-groups per row: (2K+1) * C
-  int merge_sort;            // 1: the merge keeps its C * topk candidates in LDS
   int cache;                 // 1: finishing work-groups keep the row's words in dynamic LDS
 };
 
@@ -188,19 +188,6 @@ __device__ __forceinline__ float tile_max<float, NV_TILE>(const u32x4 (&r)[NV_TI
 // chunk's top k under the same order, so the union of the chunk lists holds
 // the global top k, which the merge kernel selects.
 // ============================================================================
-// Rank selection: entries x[0..n) are distinct composites in LDS; writes the
-// best kk of them to dst in descending order (an entry's rank is the number
-// of entries better than it), then zero padding up to k.
-__device__ void write_ranked(const uint64_t* x, int n, int kk, int k, uint64_t* dst) {
-  for (int i = threadIdx.x; i < n; i += WG) {
-    const uint64_t v = x[i];
-    int rank = 0;
-    for (int j = 0; j < n; ++j) rank += x[j] > v;
-    if (rank < kk) dst[rank] = v;
-  }
-  for (int i = kk + threadIdx.x; i < k; i += WG) dst[i] = 0;
-}
-
 // Exact selection by a 32-step binary search on order keys: the largest key
 // tau with at least kk logits >= tau is the kk-th largest; logits above tau
 // are all kept, ties at tau are kept in increasing id order.  The kk kept
@@ -260,63 +247,73 @@ __device__ void topk_chunk_exact(const u32x4 (&r)[NV_TILE], int lo, int len, int
   __syncthreads();
 }
 
-// Chunk candidates: exactly min(k, len) composites in descending order, then
-// zero padding to k.  Fast path (k <= 256): in each wave, the ceil(k/4)-th
-// largest of its 64 per-thread maxima is found by a ballot binary search;
-// the smallest of the four is a lower bound of the chunk's k-th largest logit
-// (each wave has ceil(k/4) logits at or above it), so every logit of the
-// chunk's top k passes it.  The few that do are compacted into LDS and
-// ranked exactly.
+// Chunk candidates, written to the chunk's candidate area as four lists (one
+// per wave) of at most WCAP composites each, with their lengths in cnts[4].
+// Fast path (k <= 256): in each wave, a lower bound of the ceil(k/4)-th
+// largest of its 64 per-thread maxima is found by a ballot binary search on
+// the upper 16 bits of their order keys; the smallest of the four bounds is
+// a lower bound of the chunk's k-th largest logit (each wave has ceil(k/4)
+// logits at or above it), so every logit of the chunk's top k passes it.
+// Each wave appends the logits that pass to its list with ballots.  The lists
+// are unsorted; the merge kernel selects exactly.  Exact path (k > 256, or a
+// list over WCAP): the chunk's exact top min(k, len) is stored contiguously
+// across the four list areas.
 template <typename ET>
-__device__ void topk_chunk(const u32x4 (&r)[NV_TILE], int lo, int len, int k, uint64_t* dst, float* red) {
+__device__ void topk_chunk(const u32x4 (&r)[NV_TILE], int lo, int len, int k, uint64_t* dst, int* cnts,
+                           float* red) {
   constexpr int VEC = Tr<ET>::VEC;
   __shared__ uint64_t cbuf[CAND_CAP];
   __shared__ uint32_t wkey[NWAVE];
+  __shared__ int s_over;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int kk = min(k, len);
   bool done = false;
   if (k <= TOPK_FAST_MAX) {
-    const uint32_t key = order_key(tile_max<ET, NV_TILE>(r));  // padding reads as -inf
+    const uint32_t key = order_key(tile_max<ET, NV_TILE>(r)) >> 16;  // padding reads as -inf
     const int m = (k + NWAVE - 1) / NWAVE;
-    uint32_t tau = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = tau | (1u << bit);
-      if (__popcll(__ballot(key >= cand)) >= m) tau = cand;
+    uint32_t pre = 0;
+    for (int bit = 15; bit >= 0; --bit) {
+      const uint32_t cand = pre | (1u << bit);
+      if (__popcll(__ballot(key >= cand)) >= m) pre = cand;
     }
-    if (lane == 0) wkey[wave] = tau;
+    if (lane == 0) wkey[wave] = pre << 16;
+    if (t == 0) s_over = 0;
     __syncthreads();
-    const float bound = key_value(min(min(wkey[0], wkey[1]), min(wkey[2], wkey[3])));
-    // Compaction without atomics: count, block scan, write.
-    int mine = 0;
+    // A negative prefix reads back as the lowest value of its bucket; the
+    // bucket of -inf reads back as a NaN pattern, which must become -inf.
+    float bound = key_value(min(min(wkey[0], wkey[1]), min(wkey[2], wkey[3])));
+    if (bound != bound) bound = NEG_INF;
+    uint64_t* wl = dst + wave * WCAP;
+    int n = 0;  // wave-uniform
 #pragma unroll
     for (int j = 0; j < NV_TILE; ++j)
 #pragma unroll
-      for (int e = 0; e < VEC; ++e)
-        mine += (j * WG + t) * VEC + e < len && Tr<ET>::at(r[j], e) >= bound;
-    float ex, tot;
-    block_scan((float)mine, red, ex, tot);
-    const int nc = (int)tot;
-    if (nc <= CAND_CAP) {
-      int pos = (int)ex;
-#pragma unroll
-      for (int j = 0; j < NV_TILE; ++j)
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          const float x = Tr<ET>::at(r[j], e);
-          const int off = (j * WG + t) * VEC + e;
-          if (off < len && x >= bound) cbuf[pos++] = composite(x, lo + off);
+      for (int e = 0; e < VEC; ++e) {
+        const float x = Tr<ET>::at(r[j], e);
+        const int off = (j * WG + t) * VEC + e;
+        const bool pass = off < len && x >= bound;
+        const unsigned long long mask = __ballot(pass);
+        if (mask) {
+          const int pos = n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+          if (pass && pos < WCAP) wl[pos] = composite(x, lo + off);
+          n += __popcll(mask);
         }
-      __syncthreads();
-      write_ranked(cbuf, nc, kk, k, dst);
-      done = true;
+      }
+    if (lane == 0) {
+      cnts[wave] = min(n, WCAP);
+      if (n > WCAP) s_over = 1;
     }
     __syncthreads();
+    done = s_over == 0;
   }
   if (!done) {
     topk_chunk_exact<ET>(r, lo, len, kk, cbuf, red);
-    write_ranked(cbuf, kk, kk, k, dst);
+    for (int i = t; i < kk; i += WG) dst[i] = cbuf[i];
+    if (t < NWAVE) cnts[t] = max(0, min(WCAP, kk - t * WCAP));
   }
 }
+
 // ============================================================================
 // Kernel A: statistics of one (row, position, chunk).
 // ============================================================================
@@ -370,7 +367,8 @@ void stats_kernel(Args a) {
   }
 
   if (is_draft && a.topk > 0) {
-    topk_chunk<ET>(r, lo, len, a.topk, a.cand + (((size_t)b * a.K + pos) * a.C + c) * a.topk, shf);
+    const size_t chunk = ((size_t)b * a.K + pos) * a.C + c;
+    topk_chunk<ET>(r, lo, len, a.topk, a.cand + chunk * NWAVE * WCAP, a.ccnt + chunk * NWAVE, shf);
     return;
   }
   const float m = block_max(tile_max<ET, NV_TILE>(r), shf);
@@ -750,106 +748,259 @@ __device__ void final_draw(const Args& a, int b, int n, float s, float MSt, floa
 
 // ============================================================================
 // Kernel M (sparse drafts only): one work-group per (row, draft position) of
-// a sampling row.  Selects the kk = min(k, V) best of the C * k chunk
-// candidates (ties to the lower id), which define the truncated draft
-// distribution q~ used at verification; writes the kept (id, logit) list in
-// increasing id order, the max kept logit, Z_q = sum over kept of
-// exp2(fma(l, s, -fl(max*s))) and q~(d_i).
+// a sampling row.  Selects the kk = min(k, V) best of the chunk candidates
+// (ties to the lower id), which define the truncated draft distribution q~
+// used at verification; writes the kept (id, logit) list in increasing id
+// order, the max kept logit, Z_q = sum over kept of exp2(fma(l, s, -fl(max*s)))
+// (summed in id order) and q~(d_i).
+//
+// The kk-th largest composite is found by a bitwise search over the bits in
+// which the candidates differ (block-wide counts, two bits per step).
+// Composites are distinct, so exactly kk candidates are at or above it.  The
+// candidates are held in registers when they fit, and read from their lists
+// in global memory at every step otherwise.
 // ============================================================================
+constexpr int MERGE_REG = 14;                   // candidates per thread held in registers
+constexpr int MERGE_REG_CAP = MERGE_REG * WG;   // up to 3584 candidates per (row, position)
+constexpr int MERGE_MAX_LISTS = 1024;           // lists whose offsets are scanned in LDS
+
+// Candidates of one (row, position) held in registers: thread t holds the
+// entries t, t + WG, ... of the concatenation of the lists.
+struct RegCands {
+  uint64_t v[MERGE_REG];
+  int N;
+  template <typename F>
+  __device__ __forceinline__ void each(F&& f) const {
+#pragma unroll
+    for (int r = 0; r < MERGE_REG; ++r)
+      if ((int)threadIdx.x + r * WG < N) f(v[r]);
+  }
+};
+// Candidates read from their lists in global memory (one wave per list).
+struct ListCands {
+  const uint64_t* g;
+  const int* gcnt;
+  int NL;
+  template <typename F>
+  __device__ __forceinline__ void each(F&& f) const {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int L = wave; L < NL; L += NWAVE) {
+      const int n = gcnt[L];
+      for (int j = lane; j < n; j += 64) f(g[(size_t)L * WCAP + j]);
+    }
+  }
+};
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m, 64);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Threshold composite: exactly kk candidates are >= it.  The kk-th largest
+// composite is built from the top, two bits per step: of the prefixes with
+// the step's bits set to 11, 10, 01 (and 00), the largest one with at least
+// kk candidates at or above it is kept.  Bits equal in every candidate are
+// taken as they are, and the search stops as soon as exactly kk candidates
+// are at or above the prefix.  One barrier per step: the wave partial counts
+// alternate between two LDS buffers.  Also returns the largest candidate
+// value (the largest kept logit) in *vmax.
+template <typename Src>
+__device__ uint64_t select_threshold(const Src& src, int kk, uint64_t* sh64, float* part /* 2 * 3 * NWAVE */,
+                                     float* vmax) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  uint64_t all_and = ~0ull, any_or = 0, best = 0;
+  src.each([&](uint64_t v) {
+    all_and &= v;
+    any_or |= v;
+    best = v > best ? v : best;
+  });
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    all_and &= shfl_xor_u64(all_and, m);
+    any_or |= shfl_xor_u64(any_or, m);
+    const uint64_t o = shfl_xor_u64(best, m);
+    best = o > best ? o : best;
+  }
+  if (lane == 0) {
+    sh64[wave] = all_and;
+    sh64[NWAVE + wave] = any_or;
+    sh64[2 * NWAVE + wave] = best;
+  }
+  __syncthreads();
+  all_and = sh64[0] & sh64[1] & sh64[2] & sh64[3];
+  any_or = sh64[NWAVE] | sh64[NWAVE + 1] | sh64[NWAVE + 2] | sh64[NWAVE + 3];
+  best = sh64[2 * NWAVE];
+#pragma unroll
+  for (int w = 1; w < NWAVE; ++w) best = sh64[2 * NWAVE + w] > best ? sh64[2 * NWAVE + w] : best;
+  *vmax = composite_value(best);
+  uint64_t var = all_and ^ any_or;  // bits that differ between candidates
+  uint64_t tau = all_and;           // constant bits; variable bits start at 0
+  int ph = 0;
+  while (var) {
+    const uint64_t hi = 1ull << (63 - __builtin_clzll(var));
+    var &= ~hi;
+    const uint64_t lo = var ? 1ull << (63 - __builtin_clzll(var)) : 0;
+    var &= ~lo;
+    const uint64_t c3 = tau | hi | lo, c2 = tau | hi, c1 = tau | lo;
+    float n3 = 0.f, n2 = 0.f, n1 = 0.f;
+    src.each([&](uint64_t v) {
+      n3 += v >= c3 ? 1.f : 0.f;
+      n2 += v >= c2 ? 1.f : 0.f;
+      n1 += v >= c1 ? 1.f : 0.f;
+    });
+    n3 = wave_sum(n3);
+    n2 = wave_sum(n2);
+    n1 = wave_sum(n1);
+    float* pp = part + ph * 3 * NWAVE;
+    if (lane == 0) {
+      pp[wave] = n3;
+      pp[NWAVE + wave] = n2;
+      pp[2 * NWAVE + wave] = n1;
+    }
+    __syncthreads();
+    ph ^= 1;
+    const int m3 = (int)(pp[0] + pp[1] + pp[2] + pp[3]);
+    const int m2 = (int)(pp[NWAVE] + pp[NWAVE + 1] + pp[NWAVE + 2] + pp[NWAVE + 3]);
+    const int m1 = lo ? (int)(pp[2 * NWAVE] + pp[2 * NWAVE + 1] + pp[2 * NWAVE + 2] + pp[2 * NWAVE + 3]) : 0;
+    int n = -1;
+    if (lo && m3 >= kk) {
+      tau = c3;
+      n = m3;
+    } else if (m2 >= kk) {
+      tau = c2;
+      n = m2;
+    } else if (lo && m1 >= kk) {
+      tau = c1;
+      n = m1;
+    }
+    if (n == kk) break;
+  }
+  __syncthreads();  // the partial buffers are reused by the caller
+  return tau;
+}
+
+// Kept set from the threshold: the kept composites go to sel[] (in
+// arbitrary order) and each thread sums exp2(fma(l, s, -ms)) over the kept
+// candidates it holds, in its own fixed order.  The logit of draft token d,
+// if kept, goes to *ld_bits.
+template <typename Src>
+__device__ __forceinline__ float take_kept(const Src& src, uint64_t thr, int d, float s, float ms, uint64_t* sel,
+                                           int* n_sel, uint32_t* ld_bits) {
+  float z = 0.f;
+  src.each([&](uint64_t v) {
+    if (v >= thr) {
+      const int at = atomicAdd(n_sel, 1);
+      if (at < SV_MAX_TOPK) sel[at] = v;
+      const float l = composite_value(v);
+      z += exp2_fast(fmaf(l, s, -ms));
+      if (composite_id(v) == d) *ld_bits = __float_as_uint(l);
+    }
+  });
+  return z;
+}
+
 template <typename ET>
 __global__ __launch_bounds__(WG) void merge_kernel(Args a) {
-  extern __shared__ uint64_t mbuf[];
+  extern __shared__ int loff[];  // list offsets in the concatenation (NL <= MERGE_MAX_LISTS)
   __shared__ uint64_t sel[SV_MAX_TOPK];
-  __shared__ float red[NWAVE];
-  __shared__ float s_q;
+  __shared__ uint64_t sh64[3 * NWAVE];
+  __shared__ float red[2 * 3 * NWAVE];
+  __shared__ int s_n;
+  __shared__ uint32_t s_ld;
   const int i = blockIdx.x % a.K, b = blockIdx.x / a.K;
   const float T = a.temp[b];
   if (!is_sampling_temperature(T)) return;
-  const int t = threadIdx.x, C = a.C, k = a.topk, N = C * k, kk = min(k, a.V);
-  const uint64_t* g = a.cand + ((size_t)b * a.K + i) * N;
-  if (a.merge_sort) {
-    // Pairwise merge tree of the C sorted chunk lists, each merge truncated
-    // to kk entries; output position o of a merge is found by a binary search
-    // on how many of its first o entries come from the first list (entries
-    // of the first list go first on ties, which only zero padding has).
-    uint64_t* src = mbuf;
-    uint64_t* dst = mbuf + N;
-    for (int j = t; j < N; j += WG) src[j] = g[j];
-    __syncthreads();
-    int nl = C, len = k;
-    while (nl > 1) {
-      const int nout = (nl + 1) / 2, lout = min(kk, 2 * len);
-      for (int idx = t; idx < nout * lout; idx += WG) {
-        const int q = idx / lout, o = idx % lout;
-        const uint64_t* A = src + (size_t)(2 * q) * len;
-        uint64_t v;
-        if (2 * q + 1 < nl) {
-          const uint64_t* Bl = A + len;
-          int ilo = max(0, o - len), ihi = min(o, len);
-          while (ilo < ihi) {
-            const int ii = (ilo + ihi + 1) >> 1;
-            if (o - ii >= len || A[ii - 1] >= Bl[o - ii]) ilo = ii; else ihi = ii - 1;
-          }
-          const int ia = ilo, jb = o - ilo;
-          v = (jb >= len || (ia < len && A[ia] >= Bl[jb])) ? A[ia] : Bl[jb];
-        } else {
-          v = o < len ? A[o] : 0;
-        }
-        dst[(size_t)q * lout + o] = v;
-      }
-      __syncthreads();
-      uint64_t* tmp = src; src = dst; dst = tmp;
-      nl = nout;
-      len = lout;
+  const int t = threadIdx.x;
+  const int NL = a.C * NWAVE, kk = min(a.topk, a.V);
+  const size_t slot = (size_t)b * a.K + i;
+  const uint64_t* g = a.cand + slot * NL * WCAP;
+  const int* gcnt = a.ccnt + slot * NL;
+  const int d = a.tok[slot];
+  const float s = LOG2E / T;
+
+  // Offsets of the lists in their concatenation (when the lists are few).
+  int N = INT_MAX;
+  if (NL <= MERGE_MAX_LISTS) {
+    constexpr int PER = MERGE_MAX_LISTS / WG;
+    int c4[PER], local = 0;
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      const int L = t * PER + r;
+      c4[r] = L < NL ? gcnt[L] : 0;
+      local += c4[r];
     }
-    for (int j = t; j < kk; j += WG) sel[j] = src[j];
-  } else {
-    // Candidates in global memory: global rank of each candidate = its
-    // position in its own sorted list plus, for every other list, the number
-    // of entries above it (binary search).  Composites are distinct.
-    for (int j = t; j < N; j += WG) {
-      const uint64_t v = g[j];
-      if (v == 0) continue;
-      const int c0 = j / k;
-      int rank = j - c0 * k;
-      for (int c = 0; c < C && rank < kk; ++c) {
-        if (c == c0) continue;
-        const uint64_t* L = g + (size_t)c * k;
-        int lo = 0, hi = k;  // first index with L[idx] < v
-        while (lo < hi) {
-          const int mid = (lo + hi) >> 1;
-          if (L[mid] > v) lo = mid + 1; else hi = mid;
-        }
-        rank += lo;
-      }
-      if (rank < kk) sel[rank] = v;
+    float ex, tot;
+    block_scan((float)local, red, ex, tot);
+    int o = (int)ex;
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      const int L = t * PER + r;
+      if (L < NL) loff[L] = o;
+      o += c4[r];
     }
+    N = (int)tot;
+  }
+  if (t == 0) {
+    s_n = 0;
+    s_ld = 0xFFFFFFFFu;
   }
   __syncthreads();
-  const float m = composite_value(sel[0]);  // the largest kept logit
-  const float s = LOG2E / T;
+  uint64_t thr;
+  float m, z;
+  if (N <= MERGE_REG_CAP) {
+    // Entry j = t + r * WG comes from the last list whose offset is <= j
+    // (binary lifting over the offsets, all of the thread's entries at once).
+    RegCands rc;
+    rc.N = N;
+    int Lr[MERGE_REG];
+#pragma unroll
+    for (int r = 0; r < MERGE_REG; ++r) Lr[r] = 0;
+    int step = 1;
+    while (2 * step < NL) step *= 2;
+    for (; step > 0; step >>= 1) {
+#pragma unroll
+      for (int r = 0; r < MERGE_REG; ++r) {
+        const int c = Lr[r] + step;
+        if (c < NL && loff[c] <= t + r * WG) Lr[r] = c;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < MERGE_REG; ++r) {
+      const int j = t + r * WG;
+      rc.v[r] = j < N ? g[(size_t)Lr[r] * WCAP + (j - loff[Lr[r]])] : 0;
+    }
+    thr = select_threshold(rc, kk, sh64, red, &m);
+    z = take_kept(rc, thr, d, s, mul_rn(m, s), sel, &s_n, &s_ld);
+  } else {
+    const ListCands lc{g, gcnt, NL};
+    thr = select_threshold(lc, kk, sh64, red, &m);
+    z = take_kept(lc, thr, d, s, mul_rn(m, s), sel, &s_n, &s_ld);
+  }
+  const float Z = block_sum(z, red);  // also orders sel[] and s_ld before their reads
   const float ms = mul_rn(m, s);
-  const int d = a.tok[(size_t)b * a.K + i];
-  if (t == 0) s_q = 0.f;
-  // Kept list in increasing id order (rank among the kept by id).
-  uint2* kept = a.kept + ((size_t)b * a.K + i) * k;
-  float z = 0.f;
+  // Place each kept composite by its rank in id order (~id is larger for
+  // lower ids); two entries per 16-byte LDS read.
+  uint2* kept = a.kept + slot * a.topk;
+  const uint4* s4 = reinterpret_cast<const uint4*>(sel);
   for (int j = t; j < kk; j += WG) {
     const uint64_t v = sel[j];
-    const int id = composite_id(v);
+    const uint32_t nid = (uint32_t)v;
     int pos = 0;
-    for (int q = 0; q < kk; ++q) pos += composite_id(sel[q]) < id;
-    const float l = composite_value(v);
-    kept[pos] = make_uint2((uint32_t)id, __float_as_uint(l));
+    const int pairs = kk >> 1;
+#pragma unroll 8
+    for (int q = 0; q < pairs; ++q) {
+      const uint4 w = s4[q];
+      pos += (w.x > nid) + (w.z > nid);
+    }
+    if (kk & 1) pos += (uint32_t)sel[kk - 1] > nid;
+    kept[pos] = make_uint2((uint32_t)composite_id(v), __float_as_uint(composite_value(v)));
   }
-  // Z_q in a fixed order: entries of sel[] (descending by value) strided by
-  // thread, then the block sum.
-  for (int j = t; j < kk; j += WG) z += exp2_fast(fmaf(composite_value(sel[j]), s, -ms));
-  const float Z = block_sum(z, red);
-  for (int j = t; j < kk; j += WG)
-    if (composite_id(sel[j]) == d) s_q = exp2_fast(fmaf(composite_value(sel[j]), s, -ms)) / Z;
-  __syncthreads();
-  if (t == 0) a.qstat[(size_t)b * a.K + i] = make_float4(m, Z, s_q, (float)kk);
+  if (t == 0) {
+    const uint32_t lb = s_ld;
+    const float qd = lb != 0xFFFFFFFFu ? exp2_fast(fmaf(__uint_as_float(lb), s, -ms)) / Z : 0.f;
+    a.qstat[slot] = make_float4(m, Z, qd, (float)kk);
+  }
 }
 
 // ============================================================================
@@ -1011,9 +1162,8 @@ __global__ __launch_bounds__(WG) void finish_kernel(Args a) {
 // ============================================================================
 struct Plan {
   int C = 0, CS = 0;
-  size_t off_cnt = 0, off_part = 0, off_subK = 0, off_subR = 0, off_cand = 0, off_qstat = 0, off_kept = 0,
+  size_t off_cnt = 0, off_part = 0, off_subK = 0, off_subR = 0, off_cand = 0, off_ccnt = 0, off_qstat = 0, off_kept = 0,
          total = 0;
-  bool merge_sort = false;  // sparse drafts: the merge sorts its candidates in LDS
   size_t merge_lds = 0;
   bool cache = false;       // finishing work-groups copy the row's words to LDS
   size_t lds_bytes = 0;     // dynamic LDS of the finishing work-groups
@@ -1049,13 +1199,15 @@ int make_plan(int B, int K, int V, int topk, int dtype, Plan& pl) {
   if (topk > 0) {
     const size_t slots = (size_t)B * K;
     pl.off_cand = off;
-    off = align256(off + sizeof(uint64_t) * slots * C * topk);
+    off = align256(off + sizeof(uint64_t) * slots * C * NWAVE * WCAP);
+    pl.off_ccnt = off;
+    off = align256(off + sizeof(int) * slots * C * NWAVE);
     pl.off_qstat = off;
     off = align256(off + sizeof(float4) * slots);
     pl.off_kept = off;
     off = align256(off + sizeof(uint2) * slots * topk);
-    pl.merge_sort = C * (long)topk <= MERGE_SORT_MAX;
-    pl.merge_lds = pl.merge_sort ? 2 * (size_t)C * topk * sizeof(uint64_t) : 0;
+    const size_t NL = (size_t)C * NWAVE;
+    pl.merge_lds = NL <= (size_t)MERGE_MAX_LISTS ? NL * sizeof(int) : 0;
   }
   pl.total = off;
   // Dynamic LDS of the finishing work-groups: 3 * C floats of chunk scratch,
@@ -1112,8 +1264,8 @@ int run(const void* tgt, const void* dft, const int32_t* tok, const float* uni, 
   a.B = B; a.K = K; a.V = V; a.C = pl.C; a.CS = pl.CS; a.topk = topk;
   a.GA = (2 * K + 1) * pl.C;
   a.cache = pl.cache ? 1 : 0;
-  a.merge_sort = pl.merge_sort ? 1 : 0;
   a.cand = topk > 0 ? reinterpret_cast<uint64_t*>(base + pl.off_cand) : nullptr;
+  a.ccnt = topk > 0 ? reinterpret_cast<int*>(base + pl.off_ccnt) : nullptr;
   a.qstat = topk > 0 ? reinterpret_cast<float4*>(base + pl.off_qstat) : nullptr;
   a.kept = topk > 0 ? reinterpret_cast<uint2*>(base + pl.off_kept) : nullptr;
   const size_t esz = dtype == SV_BF16 ? 2 : 4;
