@@ -422,15 +422,24 @@ void stats_kernel(Args a) {
 // fit, else global memory.  Partials and bonus sub-block sums were written by
 // the statistics kernel (plain words); residual sub-block sums are published
 // by this kernel's work-groups (complemented words, see pub_u32).
+// A row's published words, read from their LDS copy (CACHED) or from the
+// workspace.  Keeping CACHED a compile-time choice lets every access to the
+// copy compile to an LDS instruction.
+template <bool CACHED>
 struct RowView {
-  const uint32_t* pw;    // [(2K+1) * C * 4] partial words, or null
-  const uint32_t* sub;   // [C * NSUB] sub-block sums (plain), or null
+  const uint32_t* pw;    // CACHED: [(2K+1) * C * 4] partial words in LDS
+  const uint32_t* sub;   // CACHED: [C * NSUB] sub-block sums in LDS (plain)
+  bool sub_loaded;       // whether `sub` holds the sums (else they are read from the workspace)
 };
-__device__ __forceinline__ float view_part(const Args& a, const RowView& v, int b, int slot, int c, int w) {
-  return __uint_as_float(v.pw ? v.pw[((size_t)slot * a.C + c) * 4 + w] : part_words(a, b, slot, c)[w]);
+template <bool CACHED>
+__device__ __forceinline__ float view_part(const Args& a, const RowView<CACHED>& v, int b, int slot, int c, int w) {
+  if constexpr (CACHED) return __uint_as_float(v.pw[((size_t)slot * a.C + c) * 4 + w]);
+  else return __uint_as_float(part_words(a, b, slot, c)[w]);
 }
-__device__ __forceinline__ float view_sub(const RowView& v, const uint32_t* gsub, bool published, int c, int q) {
-  if (v.sub) return __uint_as_float(v.sub[c * NSUB + q]);
+template <bool CACHED>
+__device__ __forceinline__ float view_sub(const RowView<CACHED>& v, const uint32_t* gsub, bool published, int c,
+                                          int q) {
+  if (CACHED && v.sub_loaded) return __uint_as_float(v.sub[c * NSUB + q]);
   const uint32_t* p = gsub + (size_t)c * NSUB + q;
   return __uint_as_float(published ? got_u32(p) : *p);
 }
@@ -466,22 +475,41 @@ struct RowShared {
   float q[SV_MAX_K];     // q_i(d_i)
   int tok[SV_MAX_K];
   float red_f[NWAVE];
+  float uK;              // u_K: drives the final draw
   int n;                 // accepted drafts
   int greedy;
   float s;               // log2(e)/T
 };
 
-__device__ void decide_row(const Args& a, int b, RowShared& rs, const RowView& v) {
+// Per-row scalars, loaded by each thread t <= K at the start of a kernel so
+// that their latency overlaps the loads of the row's partials.
+struct RowIn {
+  float T;    // temperature of the row
+  int d;      // d_t (t < K)
+  float u;    // u_t (t <= K)
+  float qd;   // sparse draft: q~_t(d_t) (t < K)
+};
+__device__ __forceinline__ RowIn load_row_in(const Args& a, int b) {
+  const int K = a.K, t = threadIdx.x;
+  RowIn in{a.temp[b], -1, 0.f, 0.f};
+  if (t <= K) in.u = a.uni[(size_t)b * (K + 1) + t];
+  if (t < K) {
+    in.d = a.tok[(size_t)b * K + t];
+    if (a.topk > 0) in.qd = a.qstat[(size_t)b * K + t].z;
+  }
+  return in;
+}
+
+template <bool CACHED>
+__device__ __forceinline__ void decide_row(const Args& a, int b, RowShared& rs, const RowView<CACHED>& v,
+                                           const RowIn& in) {
   const int K = a.K, C = a.C, t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const float T = a.temp[b];
+  const float T = in.T;
   const bool greedy = !is_sampling_temperature(T);
   const float s = greedy ? 0.f : LOG2E / T;
-  int d = -1;
-  float u = 0.f;
-  if (t < K) {
-    d = a.tok[(size_t)b * K + t];
-    u = a.uni[(size_t)b * (K + 1) + t];
-  }
+  const int d = in.d;
+  const float u = in.u;
+  if (t == K) rs.uK = u;
   const int nmerge = (greedy || a.topk > 0) ? K + 1 : 2 * K + 1;
   for (int slot = wave; slot < nmerge; slot += NWAVE) {
     if (greedy) {
@@ -518,7 +546,7 @@ __device__ void decide_row(const Args& a, int b, RowShared& rs, const RowView& v
         const float lt = view_part(a, v, b, t, cd, 3);
         p = exp2_fast(fmaf(lt, s, -mul_rn(rs.M[t], s))) / rs.Z[t];
         if (a.topk > 0) {
-          q = a.qstat[(size_t)b * K + t].z;  // q~(d_t) of the truncated draft
+          q = in.qd;  // q~(d_t) of the truncated draft
         } else {
           const float lq = view_part(a, v, b, K + 1 + t, cd, 3);
           q = exp2_fast(fmaf(lq, s, -mul_rn(rs.M[K + 1 + t], s))) / rs.Z[K + 1 + t];
@@ -540,210 +568,236 @@ __device__ void decide_row(const Args& a, int b, RowShared& rs, const RowView& v
 }
 
 // ============================================================================
-// Inverse-CDF search inside an id range [start, start + len) of one row.
-// Weights: p(x) = exp2(fma(l_t, s, -MSt)) * rZt, or max(0, p(x) - q(x)) when
-// a draft row is given.  Returns the smallest id whose cumulative weight
-// (from start) exceeds tl; if none does (only through rounding), the last id
-// with positive weight, else start.  Segments of WG * VEC ids are scanned in
-// order with a block prefix sum.
+// Inverse-CDF search inside one segment [start, start + len) of a row,
+// len <= 64 * VEC, by one wave: lane l holds the ids start + l*VEC .. + VEC-1.
+// Weights: p(x) = exp2(fma(l_t, s, -MSt)) * rZt; with a draft row
+// max(0, p(x) - q(x)); with a kept list (sparse draft: ids ascending in kid,
+// q~ values in kq) max(0, p(x) - q~(x)).  The prefix is a wave scan in id
+// order.  Result, the same in every lane: the smallest id whose prefix
+// exceeds tl (-1 if none), the last id of positive weight (-1 if none) and
+// the segment's total weight.
 // ============================================================================
+struct SegResult {
+  int found;
+  int last_pos;
+  float total;
+};
+
 template <typename ET, bool ALIGNED>
-__device__ int range_search(const ET* __restrict__ trow, const ET* __restrict__ drow, int start, int len,
-                            float tl, float s, float MSt, float rZt, float MSq, float rZq, float* red,
-                            const uint2* kept = nullptr, int nkept = 0) {
+__device__ __forceinline__ SegResult segment_search(const ET* __restrict__ trow, const ET* __restrict__ drow,
+                                                    const int* kid, const float* kq, int nkept, int start,
+                                                    int len, float tl, float s, float MSt, float rZt, float MSq,
+                                                    float rZq) {
   constexpr int VEC = Tr<ET>::VEC;
-  __shared__ int sh_first, sh_last;
-  __shared__ float qloc[64 * VEC];
-  const int t = threadIdx.x;
-  if (t == 0) { sh_first = INT_MAX; sh_last = -1; }
-  if (kept) {
-    // Sparse draft: q~ is non-zero only at kept ids; place those of this
-    // range (at most 64 * VEC ids) into LDS.
-    for (int i = t; i < 64 * VEC; i += WG) qloc[i] = 0.f;
-    __syncthreads();
-    for (int j = t; j < nkept; j += WG) {
-      const int id = (int)kept[j].x;
-      if (id >= start && id < start + len)
-        qloc[id - start] = exp2_fast(fmaf(__uint_as_float(kept[j].y), s, -MSq)) * rZq;
+  const int l = threadIdx.x & 63, e = l * VEC;
+  const u32x4 vt = load_vec<ET, ALIGNED>(trow, start + e, len - e);
+  const u32x4 vq = drow ? load_vec<ET, ALIGNED>(drow, start + e, len - e) : vt;
+  int j = 0;  // first kept entry with id >= start + e
+  if (kid) {
+    int lo = 0, hi = nkept;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (kid[mid] < start + e) lo = mid + 1; else hi = mid;
     }
+    j = lo;
   }
-  __syncthreads();
-  float carry = 0.f;
-  int last_pos = -1;
-  for (int seg = 0; seg < len; seg += WG * VEC) {
-    const int e = seg + t * VEC;
-    const u32x4 vt = load_vec<ET, ALIGNED>(trow, start + e, len - e);
-    u32x4 vq = vt;
-    if (drow) vq = load_vec<ET, ALIGNED>(drow, start + e, len - e);
-    float w[VEC];
-    float local = 0.f;
+  float w[VEC];
+  float local = 0.f;
 #pragma unroll
-    for (int k = 0; k < VEC; ++k) {
-      const float p = exp2_fast(fmaf(Tr<ET>::at(vt, k), s, -MSt)) * rZt;
-      float wk = p;
-      if (drow) wk = fmaxf(0.f, p - exp2_fast(fmaf(Tr<ET>::at(vq, k), s, -MSq)) * rZq);
-      else if (kept) wk = (e + k < len && e + k < 64 * VEC) ? fmaxf(0.f, p - qloc[e + k]) : p;
-      w[k] = wk;
-      local += wk;
+  for (int k = 0; k < VEC; ++k) {
+    const float p = exp2_fast(fmaf(Tr<ET>::at(vt, k), s, -MSt)) * rZt;
+    float wk = p;
+    if (drow) {
+      wk = fmaxf(0.f, p - exp2_fast(fmaf(Tr<ET>::at(vq, k), s, -MSq)) * rZq);
+    } else if (kid) {
+      float qk = 0.f;
+      if (j < nkept && kid[j] == start + e + k) qk = kq[j++];
+      wk = fmaxf(0.f, p - qk);
     }
-    float excl, total;
-    block_scan(local, red, excl, total);
-    float cum = carry + excl;
-#pragma unroll
-    for (int k = 0; k < VEC; ++k) {
-      const bool in = e + k < len;
-      cum += w[k];
-      if (in && w[k] > 0.f) last_pos = start + e + k;
-      if (in && cum > tl) { atomicMin(&sh_first, start + e + k); break; }
-    }
-    __syncthreads();
-    if (sh_first != INT_MAX) break;
-    carry += total;
+    w[k] = e + k < len ? wk : 0.f;
+    local += w[k];
   }
-  if (last_pos >= 0) atomicMax(&sh_last, last_pos);
-  __syncthreads();
-  const int x = sh_first != INT_MAX ? sh_first : (sh_last >= 0 ? sh_last : start);
-  __syncthreads();
-  return x;
+  float inc = local;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float u = __shfl_up(inc, o, 64);
+    if (l >= o) inc += u;
+  }
+  float cum = __shfl_up(inc, 1, 64);
+  if (l == 0) cum = 0.f;
+  int found = -1, last_pos = -1;
+#pragma unroll
+  for (int k = 0; k < VEC; ++k) {
+    cum += w[k];
+    if (w[k] > 0.f) last_pos = start + e + k;
+    if (found < 0 && e + k < len && cum > tl) found = start + e + k;
+  }
+  SegResult r;
+  const unsigned long long hit = __ballot(found >= 0);
+  r.found = hit ? __shfl(found, (int)__builtin_ctzll(hit), 64) : -1;
+  const unsigned long long pos = __ballot(last_pos >= 0);
+  r.last_pos = pos ? __shfl(last_pos, 63 - (int)__builtin_clzll(pos), 64) : -1;
+  r.total = __shfl(inc, 63, 64);
+  return r;
 }
 
 // ============================================================================
-// Final draw for a sampling row ([RheoSampling] section 4 step 3).  The
-// weights are the residual max(0, p_n - q_n) after a rejection at n < K, or
-// the bonus position's p_K; their CDF is walked in three levels:
-//   1. chunk masses: one half-wave per chunk scans the chunk's 32 sub-block
-//      sums (residual sums published by kernel B, or bonus sums from the
-//      statistics kernel rescaled from the chunk max); the chunk mass is the
-//      scan's last element;
-//   2. a block scan over the chunk masses; the first chunk whose inclusive
-//      prefix exceeds t = u_K * S is selected;
-//   3. in that chunk, the same half-wave scan picks the sub-block, and a
-//      block prefix sum over its 64 * VEC ids picks the token.
+// Final draw for a sampling row ([RheoSampling] section 4 step 3), by wave 0
+// of the calling work-group alone (no block barriers).  The weights are the
+// residual max(0, p_n - q_n) after a rejection at n < K, or the bonus
+// position's p_K; their CDF is walked in three levels:
+//   1. chunk masses: lane c sums chunk c's 32 sub-block sums in order
+//      (residual sums published by the finishing work-groups, or bonus sums
+//      from the statistics kernel rescaled from the chunk max); a wave scan
+//      over the chunks gives S and the chunk c* whose inclusive prefix first
+//      exceeds t = u_K * S;
+//   2. in c*, lane q forms the prefix of sub-blocks 0..q in the same order
+//      (so the prefix of the last sub-block is the chunk mass bit for bit);
+//      the first sub-block whose prefix exceeds the remainder is selected;
+//   3. a wave prefix sum over its 64 * VEC ids picks the token.
 // A zero residual (reachable only through rounding) falls back to p_n with
-// chunk masses from the partials and a search over the whole chunk.
-// Scratch: `cf` holds 3 * C floats of LDS.  Writes out_tokens, num_accepted
-// and mass.
+// chunk masses from the partials and a walk over the whole chunk.  Writes
+// out_tokens, num_accepted and mass.  A sparse draft's kept list must be in
+// kid / kq (LDS, ascending id) before the call.
 // ============================================================================
-__device__ __forceinline__ float halfwave_incl_scan(float v) {
-  const int l = threadIdx.x & 31;
-#pragma unroll
-  for (int o = 1; o < 32; o <<= 1) {
-    const float u = __shfl_up(v, o, 32);
-    if (l >= o) v += u;
-  }
-  return v;
-}
-
-template <typename ET, bool ALIGNED>
-__device__ void final_draw(const Args& a, int b, int n, float s, float MSt, float rZt, float MSq,
-                           float rZq, float* red, const RowView& v, float* cf) {
+template <typename ET, bool ALIGNED, bool CACHED>
+__device__ __forceinline__ void final_draw(const Args& a, int b, int n, float s, float MSt, float rZt, float MSq,
+                                           float rZq, const RowShared& rs, const RowView<CACHED>& v,
+                                           const int* kid, const float* kq, int nkept) {
   constexpr int VEC = Tr<ET>::VEC;
-  static_assert(NSUB == 32, "one half-wave scans the sub-blocks of a chunk");
-  __shared__ int sh_i, sh_last, sh_q;
-  __shared__ float sh_tl, sh_tq;
-  const int K = a.K, C = a.C, t = threadIdx.x;
-  float* raw = cf;           // chunk masses
-  float* inc = cf + C;       // inclusive prefix of chunk masses
-  float* exc = cf + 2 * C;   // exclusive prefix of chunk masses
+  static_assert(NSUB == 32, "a chunk has 32 sub-blocks");
+  const int K = a.K, C = a.C, l = threadIdx.x;
+  if (l >= 64) return;
   const bool reject = n < K;
   const uint32_t* gsub = (reject ? a.subR : a.subK) + (size_t)b * C * NSUB;
   auto bonus_scale = [&](int c) {
     const float mc = view_part(a, v, b, K, c, 0);
     return mc == NEG_INF ? 0.f : exp2_fast(mul_rn(mc, s) - MSt) * rZt;
   };
-  // Sub-block weight q of chunk c (lane q of a half-wave).
-  auto sub_weight = [&](int c, int q) {
-    return reject ? view_sub(v, gsub, true, c, q) : view_sub(v, gsub, false, c, q) * bonus_scale(c);
+  // Sub-block weight q of chunk c; sc is the chunk's bonus scale.
+  auto sub_weight = [&](int c, int q, float sc) {
+    return reject ? view_sub(v, gsub, true, c, q) : view_sub(v, gsub, false, c, q) * sc;
   };
-  const int hw = t >> 5, l = t & 31;
-  for (int c = hw; c < C; c += WG / 32) {
-    const float m = halfwave_incl_scan(sub_weight(c, l));
-    if (l == 31) raw[c] = m;
-  }
-  __syncthreads();
-  auto scan_chunks = [&]() {
+  auto chunk_mass = [&](int c) {
+    const float sc = reject ? 1.f : bonus_scale(c);
+    float w[NSUB];
+#pragma unroll
+    for (int q = 0; q < NSUB; ++q) w[q] = sub_weight(c, q, sc);
+    float m = 0.f;
+#pragma unroll
+    for (int q = 0; q < NSUB; ++q) m += w[q];
+    return m;
+  };
+  auto p_mass = [&](int c) {  // fallback: mass of p_n in chunk c from the partials
+    const float mc = view_part(a, v, b, n, c, 0), zc = view_part(a, v, b, n, c, 1);
+    return mc == NEG_INF ? 0.f : zc * exp2_fast(mul_rn(mc, s) - MSt) * rZt;
+  };
+  // Scan of the chunk masses in groups of 64 chunks.  Pass 1 (tv < 0) gives
+  // S; pass 2 returns the selected chunk and its exclusive prefix.  Both
+  // passes compute the same values.
+  auto scan_select = [&](bool use_p, float tv, int& cs, float& exc_cs) -> float {
     float carry = 0.f;
-    for (int base = 0; base < C; base += WG) {
-      const int c = base + t;
-      float ex, tot;
-      const float in = block_scan(c < C ? raw[c] : 0.f, red, ex, tot);
-      if (c < C) { inc[c] = carry + in; exc[c] = carry + ex; }
-      carry += tot;
+    int last = -1;
+    cs = -1;
+    for (int base = 0; base < C; base += 64) {
+      const int c = base + l;
+      const float m = c < C ? (use_p ? p_mass(c) : chunk_mass(c)) : 0.f;
+      float in = m;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const float u = __shfl_up(in, o, 64);
+        if (l >= o) in += u;
+      }
+      float ex = __shfl_up(in, 1, 64);
+      if (l == 0) ex = 0.f;
+      if (tv >= 0.f) {
+        const unsigned long long hit = __ballot(c < C && carry + in > tv);
+        if (hit) {
+          const int q = (int)__builtin_ctzll(hit);
+          cs = base + q;
+          exc_cs = carry + __shfl(ex, q, 64);
+          return carry;
+        }
+        const unsigned long long pos = __ballot(c < C && m > 0.f);
+        if (pos) last = base + 63 - (int)__builtin_clzll(pos);
+      }
+      carry += __shfl(in, 63, 64);
     }
-    __syncthreads();
+    if (tv >= 0.f) {  // t reached the total only through rounding: last chunk of positive mass
+      cs = last >= 0 ? last : 0;
+      exc_cs = -__builtin_inff();
+    }
     return carry;
   };
-  float S = scan_chunks();
+  int cs;
+  float exc_cs = 0.f;
   bool fallback = false;
+  float S = scan_select(false, -1.f, cs, exc_cs);
   if (reject && S == 0.f) {
     fallback = true;
-    for (int c = t; c < C; c += WG) {
-      const float mc = view_part(a, v, b, n, c, 0), zc = view_part(a, v, b, n, c, 1);
-      raw[c] = mc == NEG_INF ? 0.f : zc * exp2_fast(mul_rn(mc, s) - MSt) * rZt;
-    }
-    __syncthreads();
-    S = scan_chunks();
+    S = scan_select(true, -1.f, cs, exc_cs);
   }
-  const float tv = a.uni[(size_t)b * (K + 1) + K] * S;
-  if (t == 0) { sh_i = INT_MAX; sh_last = 0; }
-  __syncthreads();
-  for (int c = t; c < C; c += WG) {
-    if (inc[c] > tv) atomicMin(&sh_i, c);
-    if (raw[c] > 0.f) atomicMax(&sh_last, c);
-  }
-  __syncthreads();
-  int cs = sh_i;
-  float t1 = cs != INT_MAX ? tv - exc[cs] : __builtin_inff();
-  if (cs == INT_MAX) cs = sh_last;  // t reached the total only through rounding
+  const float tv = rs.uK * S;
+  scan_select(fallback, tv, cs, exc_cs);
+  const float t1 = tv - exc_cs;  // +inf when t reached the total through rounding
   const int lo = cs * a.CS;
   const int len = min(a.CS, a.V - lo);
   const ET* trow = target_row<ET>(a, b, n);
-  const ET* drow = (reject && !fallback) ? draft_row<ET>(a, b, n) : nullptr;
-  int start = lo, slen = len;
-  float tl = t1;
-  if (!fallback) {
-    if (t < 32) {
-      // Same scan as for the chunk mass, so the sub-level prefix ends at it.
-      const float w = sub_weight(cs, l);
-      const float pin = halfwave_incl_scan(w);
-      const float pex = __shfl_up(pin, 1, 32);
-      const unsigned long long hit = __ballot(pin > t1) & 0xFFFFFFFFull;
-      const unsigned long long pos = __ballot(w > 0.f) & 0xFFFFFFFFull;
-      if (l == 0) {
-        if (hit) {
-          const int q = (int)__builtin_ctzll(hit);
-          sh_q = q;
-          sh_tq = t1;  // refined below by the lane that owns q
-        } else {
-          sh_q = pos ? 63 - (int)__builtin_clzll(pos) : 0;
-          sh_tq = __builtin_inff();
-        }
-      }
-      // The lane of the selected sub-block subtracts its exclusive prefix.
-      if (hit && l == (int)__builtin_ctzll(hit)) sh_tq = l ? t1 - pex : t1;
-    }
-    __syncthreads();
-    const int q = sh_q;
-    tl = sh_tq;
-    const int j = q / NWAVE, w = q % NWAVE;
-    start = lo + (j * WG + w * 64) * VEC;
-    slen = max(0, min(64 * VEC, lo + len - start));
-    __syncthreads();
-  }
-  int x = lo;
   const bool sparse = reject && !fallback && a.topk > 0;
-  const uint2* kept = sparse ? a.kept + ((size_t)b * K + n) * a.topk : nullptr;
-  const int nkept = sparse ? (int)a.qstat[(size_t)b * K + n].w : 0;
-  if (slen > 0)
-    x = range_search<ET, ALIGNED>(trow, sparse ? nullptr : drow, start, slen, tl, s, MSt, rZt, MSq, rZq, red,
-                                  kept, nkept);
+  const ET* drow = (reject && !fallback && !sparse) ? draft_row<ET>(a, b, n) : nullptr;
+  int x = lo;
+  if (fallback) {
+    // Walk the whole chunk in segments of 64 * VEC ids.
+    float carry = 0.f;
+    int last = -1;
+    x = -1;
+    for (int seg = 0; seg < len && x < 0; seg += 64 * VEC) {
+      const SegResult r = segment_search<ET, ALIGNED>(trow, nullptr, nullptr, nullptr, 0, lo + seg,
+                                                      min(64 * VEC, len - seg), t1 - carry, s, MSt, rZt, 0.f,
+                                                      0.f);
+      if (r.found >= 0) x = r.found;
+      if (r.last_pos >= 0) last = r.last_pos;
+      carry += r.total;
+    }
+    if (x < 0) x = last >= 0 ? last : lo;
+  } else {
+    // Sub-block of the chunk: lane q < 32 holds the prefix through q.
+    const float sc = reject ? 1.f : bonus_scale(cs);
+    float ws[NSUB];
+#pragma unroll
+    for (int q = 0; q < NSUB; ++q) ws[q] = sub_weight(cs, q, sc);
+    float pre = 0.f;
+#pragma unroll
+    for (int q = 0; q < NSUB; ++q)
+      if (q <= l) pre += ws[q];
+    const float wl = l < NSUB ? sub_weight(cs, l, sc) : 0.f;
+    const unsigned long long hit = __ballot(l < NSUB && pre > t1);
+    int q;
+    float tl;
+    if (hit) {
+      q = (int)__builtin_ctzll(hit);
+      const float pex = __shfl(pre, q > 0 ? q - 1 : 0, 64);
+      tl = q > 0 ? t1 - pex : t1;
+    } else {
+      const unsigned long long pos = __ballot(l < NSUB && wl > 0.f);
+      q = pos ? 63 - (int)__builtin_clzll(pos) : 0;
+      tl = __builtin_inff();
+    }
+    const int j = q / NWAVE, w = q % NWAVE;
+    const int start = lo + (j * WG + w * 64) * VEC;
+    const int slen = max(0, min(64 * VEC, lo + len - start));
+    if (slen > 0) {
+      const SegResult r = segment_search<ET, ALIGNED>(trow, drow, sparse ? kid : nullptr, kq, nkept, start, slen,
+                                                      tl, s, MSt, rZt, MSq, rZq);
+      x = r.found >= 0 ? r.found : (r.last_pos >= 0 ? r.last_pos : start);
+    }
+  }
   int32_t* out = a.out + (size_t)b * (K + 1);
-  for (int i = t; i <= K; i += WG) out[i] = i < n ? a.tok[(size_t)b * K + i] : (i == n ? x : -1);
-  if (t == 0) {
+  for (int i = l; i <= K; i += 64) out[i] = i < n ? rs.tok[i] : (i == n ? x : -1);
+  if (l == 0) {
     a.nacc[b] = n;
     if (a.mass) a.mass[b] = S;
   }
-  (void)sh_tl;
 }
 
 // ============================================================================
@@ -1017,7 +1071,7 @@ __device__ __forceinline__ void write_failed_row(const Args& a, int b) {
   if (threadIdx.x == 0) a.nacc[b] = -1;
 }
 
-template <typename ET, bool ALIGNED>
+template <typename ET, bool ALIGNED, bool CACHED>
 __global__ __launch_bounds__(WG) void finish_kernel(Args a) {
   constexpr int VEC = Tr<ET>::VEC;
   extern __shared__ uint32_t row_cache[];
@@ -1027,18 +1081,22 @@ __global__ __launch_bounds__(WG) void finish_kernel(Args a) {
   const int c = blockIdx.x % a.C;
   const int b = blockIdx.x / a.C;
   const int K = a.K, C = a.C, S = 2 * K + 1, t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  float* chunk_scratch = reinterpret_cast<float*>(row_cache);
-  uint32_t* cache_pw = a.cache ? row_cache + 3 * C : nullptr;
-  uint32_t* cache_sub = a.cache ? cache_pw + (size_t)S * C * 4 : nullptr;
-  if (cache_pw) {
+  // Sparse draft: the kept entries of the chunk (residual), then the row's
+  // kept list (final draw).
+  __shared__ float kq[SV_MAX_TOPK];
+  __shared__ int kid[SV_MAX_TOPK];
+  uint32_t* cache_pw = CACHED ? row_cache : nullptr;
+  uint32_t* cache_sub = CACHED ? cache_pw + (size_t)S * C * 4 : nullptr;
+  const RowIn in = load_row_in(a, b);
+  if (CACHED) {
     // All partials of the row in one round of loads (also the draft-token
     // logits, which the decision reads at a token-dependent chunk).
     const u32x4* src = reinterpret_cast<const u32x4*>(part_words(a, b, 0, 0));
     for (int i = t; i < S * C; i += WG) reinterpret_cast<u32x4*>(cache_pw)[i] = src[i];
     __syncthreads();
   }
-  RowView view{cache_pw, nullptr};
-  decide_row(a, b, rs, view);
+  RowView<CACHED> view{cache_pw, cache_sub, false};
+  decide_row(a, b, rs, view, in);
   const int n = rs.n;
   if (c == 0 && a.probs && t < K) {
     a.probs[((size_t)b * K + t) * 2 + 0] = rs.greedy ? 0.f : rs.p[t];
@@ -1058,7 +1116,7 @@ __global__ __launch_bounds__(WG) void finish_kernel(Args a) {
   const float s = rs.s;
   const float MSt = mul_rn(rs.M[n], s), rZt = 1.f / rs.Z[n];
   if (n == K) {
-    if (c == 0) final_draw<ET, ALIGNED>(a, b, n, s, MSt, rZt, 0.f, 0.f, rs.red_f, view, chunk_scratch);
+    if (c == 0) final_draw<ET, ALIGNED, CACHED>(a, b, n, s, MSt, rZt, 0.f, 0.f, rs, view, nullptr, nullptr, 0);
     return;
   }
   // Rejected at position n: residual max(0, p_n - q_n) over this chunk.
@@ -1079,8 +1137,8 @@ __global__ __launch_bounds__(WG) void finish_kernel(Args a) {
     load_tile<ET, ALIGNED, NV_TILE>(trow, lo, len, rt);
     // Correction of each kept id in this chunk, in id order, with its
     // sub-block (the entries of one sub-block are contiguous).
-    __shared__ float corr[SV_MAX_TOPK];
-    __shared__ int csub[SV_MAX_TOPK];
+    float* corr = kq;
+    int* csub = kid;
     for (int j = t; j < nkept; j += WG) {
       const int id = (int)kept[j].x;
       float cv = 0.f;
@@ -1148,9 +1206,23 @@ __global__ __launch_bounds__(WG) void finish_kernel(Args a) {
   __syncthreads();
   if (!sh_last) return;
   const bool ok = wait_words(subR_row, C * NSUB, cache_sub, nullptr, 0, nullptr, wall_clock64() + WAIT_TICKS);
-  view.sub = cache_sub;
-  final_draw<ET, ALIGNED>(a, b, n, s, MSt, rZt, MSq, rZq, rs.red_f, view, chunk_scratch);
-  __syncthreads();
+  view.sub_loaded = CACHED;
+  int nkept = 0;
+  if (a.topk > 0) {
+    // The row's kept list with its q~ values, for the search in wave 0.
+    nkept = (int)a.qstat[(size_t)b * K + n].w;
+    const uint2* kept = a.kept + ((size_t)b * K + n) * a.topk;
+    for (int j = t; j < nkept; j += WG) {
+      const uint2 e = kept[j];
+      kid[j] = (int)e.x;
+      kq[j] = exp2_fast(fmaf(__uint_as_float(e.y), s, -MSq)) * rZq;
+    }
+    __syncthreads();
+  }
+  final_draw<ET, ALIGNED, CACHED>(a, b, n, s, MSt, rZt, MSq, rZq, rs, view, kid, kq, nkept);
+  // With the sums in LDS the other waves clear the published words while
+  // wave 0 draws; otherwise the draw reads them, so the clear waits.
+  if (!CACHED || !ok) __syncthreads();
   if (!ok) write_failed_row(a, b);
   // Clear the row's published sums and counter for the next call.
   for (int i = t; i < C * NSUB; i += WG) clear_word(subR_row + i);
@@ -1210,11 +1282,11 @@ int make_plan(int B, int K, int V, int topk, int dtype, Plan& pl) {
     pl.merge_lds = NL <= (size_t)MERGE_MAX_LISTS ? NL * sizeof(int) : 0;
   }
   pl.total = off;
-  // Dynamic LDS of the finishing work-groups: 3 * C floats of chunk scratch,
-  // plus the row's partials and sub-block sums when they fit.
+  // Dynamic LDS of the finishing work-groups: the row's partials and
+  // sub-block sums when they fit.
   const size_t words = S * C * 4 + (size_t)C * NSUB;
   pl.cache = words <= (size_t)MAX_CACHE_WORDS;
-  pl.lds_bytes = (3 * (size_t)C + (pl.cache ? words : 0)) * sizeof(uint32_t);
+  pl.lds_bytes = (pl.cache ? words : 0) * sizeof(uint32_t);
   return SV_OK;
 }
 
@@ -1229,7 +1301,10 @@ int launch_typed(const Args& a, size_t lds, size_t merge_lds, hipStream_t st, hi
     if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
   }
   if (ev && hipEventRecord(ev[2], st) != hipSuccess) return SV_ERR_HIP;
-  hipLaunchKernelGGL((finish_kernel<ET, AL>), dim3(a.B * a.C), dim3(WG), lds, st, a);
+  if (a.cache)
+    hipLaunchKernelGGL((finish_kernel<ET, AL, true>), dim3(a.B * a.C), dim3(WG), lds, st, a);
+  else
+    hipLaunchKernelGGL((finish_kernel<ET, AL, false>), dim3(a.B * a.C), dim3(WG), lds, st, a);
   if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
   if (ev && hipEventRecord(ev[3], st) != hipSuccess) return SV_ERR_HIP;
   if (ev && hipEventRecord(ev[4], st) != hipSuccess) return SV_ERR_HIP;
