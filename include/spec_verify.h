@@ -32,8 +32,9 @@
  * All pointers are device pointers owned by the caller.  Inputs are read
  * only; outputs are fully overwritten.  The library allocates nothing, keeps
  * no mutable global state and never synchronises: every call only enqueues
- * two kernels on `stream`; outputs are valid once the caller has
- * synchronised that stream.  Calls on different workspaces are reentrant.
+ * two kernels on `stream` (three with a sparse draft); outputs are valid once
+ * the caller has synchronised that stream.  Calls on different workspaces
+ * are reentrant.
  */
 #ifndef SPEC_VERIFY_H
 #define SPEC_VERIFY_H
@@ -80,7 +81,11 @@ typedef enum {
  * dtype          sv_dtype of both logit tensors.
  * out_tokens     [B, K+1] int32 device: accepted drafts, the final token,
  *                then -1 padding.
- * num_accepted   [B] int32 device: number of accepted drafts, 0..K.
+ * num_accepted   [B] int32 device: number of accepted drafts, 0..K.  A row
+ *                whose internal hand-off between work-groups did not complete
+ *                within 100 ms (it completes in microseconds in any correct
+ *                launch; the bound only guarantees termination) gets -1 here
+ *                and -1 in every out_tokens slot.
  * workspace      device scratch of at least *workspace_bytes bytes, 256-byte
  *                aligned, zero-filled before its first use (e.g. hipMemset to
  *                0 once after allocating it).  Every call leaves it ready for
@@ -124,17 +129,16 @@ int spec_verify_probe(const void* target_logits, const void* draft_logits,
                       float* probs_out, float* mass_out);
 
 /*
- * spec_verify_timed - spec_verify that also records HIP events between its
- * kernel launches, for measuring each stage on the caller's stream.
+ * spec_verify_timed - spec_verify that also times each of its kernels on the
+ * caller's stream, for measurement.
  *
  * events     array of n_events events created by the caller (hipEventCreate).
- *            events[0] is recorded before the first launch, events[1] after
- *            the statistics kernel (which also completes greedy rows and rows
- *            that accepted every draft), events[2] after the sparse-draft
- *            merge (recorded right after events[1] when there is none),
- *            events[3] after the residual kernel (rejected rows: residual
- *            mass and correction draw) and events[4] at the end.  n_events
- *            must be 0 or 5.
+ *            events[0] / events[1] take the start / end timestamps of the
+ *            statistics kernel's dispatch, events[2] / events[3] those of the
+ *            sparse-draft merge kernel (both recorded after the statistics
+ *            kernel when there is none), events[4] / events[5] those of the
+ *            finishing kernel (decision, residual mass and final draw).
+ *            n_events must be 0 or 6.
  * Other arguments and return codes as spec_verify.
  */
 int spec_verify_timed(const void* target_logits, const void* draft_logits,

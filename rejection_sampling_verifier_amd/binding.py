@@ -170,20 +170,24 @@ def verify_probe(target, draft, draft_tokens, uniforms, temperature, topk_draft:
 
 
 class StageTimer:
-    """Five HIP events recorded by spec_verify_timed around its stages.
+    """Six HIP events taken by spec_verify_timed: the start and end of each of
+    its kernels (statistics, sparse-draft merge, finishing), from the
+    dispatches' own timestamps.
 
     ``run(...)`` enqueues one verification; ``stage_ms()`` (after the stream is
-    synchronised) returns the duration of each stage in milliseconds:
-    [statistics, top-k merge, residual mass, final draw].
+    synchronised) returns each kernel's duration in milliseconds:
+    [statistics, top-k merge (0 without a sparse draft), finishing].
     """
+
+    N = 6
 
     def __init__(self):
         self.hip = ctypes.CDLL("libamdhip64.so")
         self.hip.hipEventCreate.argtypes = [ctypes.POINTER(_vp)]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), _vp, _vp]
         self.hip.hipEventDestroy.argtypes = [_vp]
-        self.events = (_vp * 5)()
-        for i in range(5):
+        self.events = (_vp * self.N)()
+        for i in range(self.N):
             ev = _vp()
             if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
                 raise RuntimeError("hipEventCreate failed")
@@ -194,12 +198,12 @@ class StageTimer:
         args, out_tokens, num_accepted, _ = _prepare(target, draft, draft_tokens, uniforms, temperature,
                                                      topk_draft, out_tokens, num_accepted, workspace,
                                                      stream)
-        _check(load_library().spec_verify_timed(*args, self.events, 5))
+        _check(load_library().spec_verify_timed(*args, self.events, self.N))
         return out_tokens, num_accepted
 
     def stage_ms(self):
         out = []
-        for i in range(4):
+        for i in range(0, self.N, 2):
             ms = ctypes.c_float(0.0)
             if self.hip.hipEventElapsedTime(ctypes.byref(ms), self.events[i], self.events[i + 1]) != 0:
                 raise RuntimeError("hipEventElapsedTime failed")
@@ -207,7 +211,7 @@ class StageTimer:
         return out
 
     def close(self):
-        for i in range(5):
+        for i in range(self.N):
             if self.events[i]:
                 self.hip.hipEventDestroy(self.events[i])
                 self.events[i] = None

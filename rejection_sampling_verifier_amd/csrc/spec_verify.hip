@@ -51,6 +51,8 @@
 #include <cstddef>
 #include <cstdint>
 
+#include <hip/hip_ext.h>
+
 #include "spec_verify.h"
 #include "sv_device.h"
 
@@ -1290,25 +1292,30 @@ int make_plan(int B, int K, int V, int topk, int dtype, Plan& pl) {
   return SV_OK;
 }
 
+// Launches a kernel; with a start/stop event pair (timed calls) the events
+// take the dispatch's own start and end timestamps.
+template <typename F>
+int launch(F kernel, int grid, size_t lds, hipStream_t st, hipEvent_t* ev2, const Args& a) {
+  if (ev2)
+    hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(WG), (uint32_t)lds, st, ev2[0], ev2[1], 0, a);
+  else
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(WG), lds, st, a);
+  return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
 template <typename ET, bool AL>
 int launch_typed(const Args& a, size_t lds, size_t merge_lds, hipStream_t st, hipEvent_t* ev) {
-  if (ev && hipEventRecord(ev[0], st) != hipSuccess) return SV_ERR_HIP;
-  hipLaunchKernelGGL((stats_kernel<ET, AL>), dim3(a.B * a.GA), dim3(WG), 0, st, a);
-  if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
-  if (ev && hipEventRecord(ev[1], st) != hipSuccess) return SV_ERR_HIP;
+  int rc = launch(stats_kernel<ET, AL>, a.B * a.GA, 0, st, ev, a);
+  if (rc != SV_OK) return rc;
   if (a.topk > 0 && a.K > 0) {
-    hipLaunchKernelGGL((merge_kernel<ET>), dim3(a.B * a.K), dim3(WG), merge_lds, st, a);
-    if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
+    rc = launch(merge_kernel<ET>, a.B * a.K, merge_lds, st, ev ? ev + 2 : nullptr, a);
+    if (rc != SV_OK) return rc;
+  } else if (ev) {
+    if (hipEventRecord(ev[2], st) != hipSuccess || hipEventRecord(ev[3], st) != hipSuccess) return SV_ERR_HIP;
   }
-  if (ev && hipEventRecord(ev[2], st) != hipSuccess) return SV_ERR_HIP;
   if (a.cache)
-    hipLaunchKernelGGL((finish_kernel<ET, AL, true>), dim3(a.B * a.C), dim3(WG), lds, st, a);
-  else
-    hipLaunchKernelGGL((finish_kernel<ET, AL, false>), dim3(a.B * a.C), dim3(WG), lds, st, a);
-  if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
-  if (ev && hipEventRecord(ev[3], st) != hipSuccess) return SV_ERR_HIP;
-  if (ev && hipEventRecord(ev[4], st) != hipSuccess) return SV_ERR_HIP;
-  return SV_OK;
+    return launch(finish_kernel<ET, AL, true>, a.B * a.C, lds, st, ev ? ev + 4 : nullptr, a);
+  return launch(finish_kernel<ET, AL, false>, a.B * a.C, lds, st, ev ? ev + 4 : nullptr, a);
 }
 
 int run(const void* tgt, const void* dft, const int32_t* tok, const float* uni, const float* temp,
@@ -1327,7 +1334,7 @@ int run(const void* tgt, const void* dft, const int32_t* tok, const float* uni, 
   if (!tgt || !uni || !temp || !out || !nacc) return SV_ERR_ARG;
   if (K > 0 && (!dft || !tok)) return SV_ERR_ARG;
   if (reinterpret_cast<uintptr_t>(ws) & 255) return SV_ERR_ARG;
-  if (nev != 0 && (nev != 5 || !ev)) return SV_ERR_ARG;
+  if (nev != 0 && (nev != 6 || !ev)) return SV_ERR_ARG;
   Args a;
   a.tgt = tgt; a.dft = dft; a.tok = tok; a.uni = uni; a.temp = temp;
   a.out = out; a.nacc = nacc; a.probs = probs; a.mass = mass;
