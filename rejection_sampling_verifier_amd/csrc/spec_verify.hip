@@ -93,7 +93,7 @@ struct Args {
   uint32_t* subK;            // [B, C, NSUB] published bonus-position sub-block sums (vs chunk max)
   uint32_t* subR;            // [B, C, NSUB] published residual sub-block sums
   unsigned* cnt;             // [B] finishing work-groups that have arrived
-  uint64_t* cand;            // [B, K, C, NWAVE, WCAP] chunk candidate lists of sparse drafts
+  void* cand;                // [B, K, C, NWAVE, WCAP] chunk candidate lists of sparse drafts (Cand<ET>::T)
   int* ccnt;                 // [B, K, C, NWAVE] lengths of those lists
   float4* qstat;             // [B, K] sparse draft: {max kept logit, Z_q, q(d_i), kept count}
   uint2* kept;               // [B, K, topk] sparse draft: kept (id, logit bits), ascending id
@@ -190,6 +190,41 @@ __device__ __forceinline__ float tile_max<float, NV_TILE>(const u32x4 (&r)[NV_TI
 // chunk's top k under the same order, so the union of the chunk lists holds
 // the global top k, which the merge kernel selects.
 // ============================================================================
+// Chunk candidate as written by the statistics kernel: the composite of the
+// logit and its vocabulary id.
+template <typename ET>
+struct Cand {
+  using T = uint64_t;
+};
+template <typename ET>
+__device__ __forceinline__ uint64_t cand_composite(typename Cand<ET>::T c, int /*chunk_lo*/) {
+  return c;
+}
+// A passing logit staged in LDS by the statistics kernel: its bits and its
+// offset in the chunk, packed as cheaply as possible; turned into a
+// composite when the list is written out.  bf16: the widened value's low 16
+// bits are zero and chunk offsets are below 2^16, so both fit 32 bits.
+template <typename ET>
+struct Staged;
+template <>
+struct Staged<uint16_t> {
+  using T = uint32_t;
+  static __device__ __forceinline__ T pack(float x, int off) { return __float_as_uint(x) | (uint32_t)off; }
+  static __device__ __forceinline__ uint64_t composite_at(T v, int lo) {
+    return composite(__uint_as_float(v & 0xFFFF0000u), lo + (int)(v & 0xFFFFu));
+  }
+};
+template <>
+struct Staged<float> {
+  using T = uint64_t;
+  static __device__ __forceinline__ T pack(float x, int off) {
+    return ((uint64_t)__float_as_uint(x) << 32) | (uint32_t)off;
+  }
+  static __device__ __forceinline__ uint64_t composite_at(T v, int lo) {
+    return composite(__uint_as_float((uint32_t)(v >> 32)), lo + (int)(uint32_t)v);
+  }
+};
+
 // Exact selection by a 32-step binary search on order keys: the largest key
 // tau with at least kk logits >= tau is the kk-th largest; logits above tau
 // are all kept, ties at tau are kept in increasing id order.  The kk kept
@@ -261,10 +296,11 @@ __device__ void topk_chunk_exact(const u32x4 (&r)[NV_TILE], int lo, int len, int
 // list over WCAP): the chunk's exact top min(k, len) is stored contiguously
 // across the four list areas.
 template <typename ET>
-__device__ void topk_chunk(const u32x4 (&r)[NV_TILE], int lo, int len, int k, uint64_t* dst, int* cnts,
-                           float* red) {
+__device__ void topk_chunk(const u32x4 (&r)[NV_TILE], int lo, int len, int k, typename Cand<ET>::T* dst,
+                           int* cnts, float* red) {
   constexpr int VEC = Tr<ET>::VEC;
-  __shared__ uint64_t cbuf[CAND_CAP];
+  using CT = typename Cand<ET>::T;
+  __shared__ uint64_t cbuf[CAND_CAP];  // exact path: composites; fast path: the waves' staged lists
   __shared__ uint32_t wkey[NWAVE];
   __shared__ int s_over;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -285,21 +321,28 @@ __device__ void topk_chunk(const u32x4 (&r)[NV_TILE], int lo, int len, int k, ui
     // bucket of -inf reads back as a NaN pattern, which must become -inf.
     float bound = key_value(min(min(wkey[0], wkey[1]), min(wkey[2], wkey[3])));
     if (bound != bound) bound = NEG_INF;
-    uint64_t* wl = dst + wave * WCAP;
+    // Passing logits are staged in LDS (a wave's stores there cost little
+    // however sparse its lanes are) and written out as whole lists below.
+    // Two logits per ballot round; the order of a list does not matter.
+    using ST = typename Staged<ET>::T;
+    ST* stage = reinterpret_cast<ST*>(cbuf) + wave * WCAP;
     int n = 0;  // wave-uniform
+    auto below = [](unsigned long long m) {
+      return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    };
 #pragma unroll
     for (int j = 0; j < NV_TILE; ++j)
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        const float x = Tr<ET>::at(r[j], e);
+      for (int e = 0; e < VEC; e += 2) {
+        const float xa = Tr<ET>::at(r[j], e), xb = Tr<ET>::at(r[j], e + 1);
         const int off = (j * WG + t) * VEC + e;
-        const bool pass = off < len && x >= bound;
-        const unsigned long long mask = __ballot(pass);
-        if (mask) {
-          const int pos = n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-          if (pass && pos < WCAP) wl[pos] = composite(x, lo + off);
-          n += __popcll(mask);
+        const bool pa = off < len && xa >= bound, pb = off + 1 < len && xb >= bound;
+        const unsigned long long ma = __ballot(pa), mb = __ballot(pb);
+        if (ma | mb) {
+          const int pos = n + below(ma) + below(mb);
+          if (pa && pos < WCAP) stage[pos] = Staged<ET>::pack(xa, off);
+          if (pb && pos + pa < WCAP) stage[pos + pa] = Staged<ET>::pack(xb, off + 1);
+          n += __popcll(ma) + __popcll(mb);
         }
       }
     if (lane == 0) {
@@ -308,8 +351,13 @@ __device__ void topk_chunk(const u32x4 (&r)[NV_TILE], int lo, int len, int k, ui
     }
     __syncthreads();
     done = s_over == 0;
+    if (done) {
+      CT* wl = dst + wave * WCAP;
+      for (int i = lane; i < n; i += 64) wl[i] = Staged<ET>::composite_at(stage[i], lo);
+    }
   }
   if (!done) {
+    __syncthreads();  // the staged lists are no longer read
     topk_chunk_exact<ET>(r, lo, len, kk, cbuf, red);
     for (int i = t; i < kk; i += WG) dst[i] = cbuf[i];
     if (t < NWAVE) cnts[t] = max(0, min(WCAP, kk - t * WCAP));
@@ -370,7 +418,8 @@ void stats_kernel(Args a) {
 
   if (is_draft && a.topk > 0) {
     const size_t chunk = ((size_t)b * a.K + pos) * a.C + c;
-    topk_chunk<ET>(r, lo, len, a.topk, a.cand + chunk * NWAVE * WCAP, a.ccnt + chunk * NWAVE, shf);
+    topk_chunk<ET>(r, lo, len, a.topk, reinterpret_cast<typename Cand<ET>::T*>(a.cand) + chunk * NWAVE * WCAP,
+                   a.ccnt + chunk * NWAVE, shf);
     return;
   }
   const float m = block_max(tile_max<ET, NV_TILE>(r), shf);
@@ -810,129 +859,146 @@ __device__ __forceinline__ void final_draw(const Args& a, int b, int n, float s,
 // order, the max kept logit, Z_q = sum over kept of exp2(fma(l, s, -fl(max*s)))
 // (summed in id order) and q~(d_i).
 //
-// The kk-th largest composite is found by a bitwise search over the bits in
-// which the candidates differ (block-wide counts, two bits per step).
-// Composites are distinct, so exactly kk candidates are at or above it.  The
-// candidates are held in registers when they fit, and read from their lists
-// in global memory at every step otherwise.
+// The kk-th largest composite is found by a radix select with 11-bit
+// windows over the bits in which the candidates differ.  Composites are
+// distinct, so exactly kk candidates are at or above it.  The candidates are
+// held in registers (one per list and lane) when the lists are few enough,
+// and read from their lists in global memory at every pass otherwise.
 // ============================================================================
-constexpr int MERGE_REG = 14;                   // candidates per thread held in registers
-constexpr int MERGE_REG_CAP = MERGE_REG * WG;   // up to 3584 candidates per (row, position)
-constexpr int MERGE_MAX_LISTS = 1024;           // lists whose offsets are scanned in LDS
+constexpr int MERGE_REG = 12;     // lists per wave whose first 64 entries are held in registers
+constexpr int MERGE_OVF = 512;    // list entries past the 64th, gathered into LDS
 
-// Candidates of one (row, position) held in registers: thread t holds the
-// entries t, t + WG, ... of the concatenation of the lists.
+// Candidates of one (row, position) held by the work-group: wave w holds
+// lists w, w + NWAVE, ... (one register per list, lane l holding entry l, as
+// written: list r of a wave holds chunk r); entries past the 64th of a list
+// are in an LDS overflow buffer as composites.
+template <typename ET>
 struct RegCands {
-  uint64_t v[MERGE_REG];
-  int N;
+  typename Cand<ET>::T v[MERGE_REG];
+  uint32_t valid;          // bit r: v[r] is an entry
+  int CS;
+  const uint64_t* ovf;
+  int novf;
   template <typename F>
   __device__ __forceinline__ void each(F&& f) const {
 #pragma unroll
     for (int r = 0; r < MERGE_REG; ++r)
-      if ((int)threadIdx.x + r * WG < N) f(v[r]);
+      if (valid >> r & 1u) f(cand_composite<ET>(v[r], r * CS));
+    for (int j = threadIdx.x; j < novf; j += WG) f(ovf[j]);
   }
 };
-// Candidates read from their lists in global memory (one wave per list).
+// Candidates read from their lists in global memory (one wave per list;
+// list L holds chunk L / NWAVE).
+template <typename ET>
 struct ListCands {
-  const uint64_t* g;
+  const typename Cand<ET>::T* g;
   const int* gcnt;
-  int NL;
+  int NL, CS;
   template <typename F>
   __device__ __forceinline__ void each(F&& f) const {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     for (int L = wave; L < NL; L += NWAVE) {
       const int n = gcnt[L];
-      for (int j = lane; j < n; j += 64) f(g[(size_t)L * WCAP + j]);
+      for (int j = lane; j < n; j += 64) f(cand_composite<ET>(g[(size_t)L * WCAP + j], (L / NWAVE) * CS));
     }
   }
 };
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m, 64);
-  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m, 64);
-  return ((uint64_t)hi << 32) | lo;
-}
+// Threshold composite: exactly kk candidates are >= it.  A radix select over
+// the bits in which the candidates differ: the highest undecided differing
+// bit starts an 11-bit window, the window's digits of the candidates that
+// match the prefix decided so far are counted in an LDS histogram, and the
+// digit at which the count of larger candidates reaches kk is appended to
+// the prefix.  Bits equal in every candidate are taken as they are.  It stops
+// once every candidate with the chosen digit is needed (usually after the
+// first window; ties in value continue into the id bits).  Also returns the
+// largest candidate value (the largest kept logit) in *vmax.
+constexpr int RADIX_BITS = 11;
+constexpr int RADIX_BINS = 1 << RADIX_BITS;  // 2048 bins, 8 per thread
 
-// Threshold composite: exactly kk candidates are >= it.  The kk-th largest
-// composite is built from the top, two bits per step: of the prefixes with
-// the step's bits set to 11, 10, 01 (and 00), the largest one with at least
-// kk candidates at or above it is kept.  Bits equal in every candidate are
-// taken as they are, and the search stops as soon as exactly kk candidates
-// are at or above the prefix.  One barrier per step: the wave partial counts
-// alternate between two LDS buffers.  Also returns the largest candidate
-// value (the largest kept logit) in *vmax.
 template <typename Src>
-__device__ uint64_t select_threshold(const Src& src, int kk, uint64_t* sh64, float* part /* 2 * 3 * NWAVE */,
-                                     float* vmax) {
+__device__ uint64_t select_threshold(const Src& src, int kk, uint32_t* sh32, float* red, int* ired,
+                                     uint32_t* hist, float* vmax) {
+  __shared__ int s_digit, s_above, s_count;
+  constexpr int PER = RADIX_BINS / WG;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  uint64_t all_and = ~0ull, any_or = 0, best = 0;
+  uint32_t and_lo = ~0u, and_hi = ~0u, or_lo = 0u, or_hi = 0u;
+  float best = NEG_INF;
   src.each([&](uint64_t v) {
-    all_and &= v;
-    any_or |= v;
-    best = v > best ? v : best;
+    and_lo &= (uint32_t)v;
+    and_hi &= (uint32_t)(v >> 32);
+    or_lo |= (uint32_t)v;
+    or_hi |= (uint32_t)(v >> 32);
+    best = fmaxf(best, composite_value(v));
   });
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    all_and &= shfl_xor_u64(all_and, m);
-    any_or |= shfl_xor_u64(any_or, m);
-    const uint64_t o = shfl_xor_u64(best, m);
-    best = o > best ? o : best;
-  }
+  and_lo = wave_and(and_lo);
+  and_hi = wave_and(and_hi);
+  or_lo = wave_or(or_lo);
+  or_hi = wave_or(or_hi);
+  best = wave_max(best);
   if (lane == 0) {
-    sh64[wave] = all_and;
-    sh64[NWAVE + wave] = any_or;
-    sh64[2 * NWAVE + wave] = best;
+    sh32[wave] = and_lo;
+    sh32[NWAVE + wave] = and_hi;
+    sh32[2 * NWAVE + wave] = or_lo;
+    sh32[3 * NWAVE + wave] = or_hi;
+    red[wave] = best;
   }
-  __syncthreads();
-  all_and = sh64[0] & sh64[1] & sh64[2] & sh64[3];
-  any_or = sh64[NWAVE] | sh64[NWAVE + 1] | sh64[NWAVE + 2] | sh64[NWAVE + 3];
-  best = sh64[2 * NWAVE];
 #pragma unroll
-  for (int w = 1; w < NWAVE; ++w) best = sh64[2 * NWAVE + w] > best ? sh64[2 * NWAVE + w] : best;
-  *vmax = composite_value(best);
+  for (int i = 0; i < PER; ++i) hist[t * PER + i] = 0u;
+  __syncthreads();
+  uint64_t all_and = ~0ull, any_or = 0ull;
+  float mx = NEG_INF;
+#pragma unroll
+  for (int w = 0; w < NWAVE; ++w) {
+    all_and &= ((uint64_t)sh32[NWAVE + w] << 32) | sh32[w];
+    any_or |= ((uint64_t)sh32[3 * NWAVE + w] << 32) | sh32[2 * NWAVE + w];
+    mx = fmaxf(mx, red[w]);
+  }
+  *vmax = mx;
   uint64_t var = all_and ^ any_or;  // bits that differ between candidates
   uint64_t tau = all_and;           // constant bits; variable bits start at 0
-  int ph = 0;
+  int need = kk;
   while (var) {
-    const uint64_t hi = 1ull << (63 - __builtin_clzll(var));
-    var &= ~hi;
-    const uint64_t lo = var ? 1ull << (63 - __builtin_clzll(var)) : 0;
-    var &= ~lo;
-    const uint64_t c3 = tau | hi | lo, c2 = tau | hi, c1 = tau | lo;
-    float n3 = 0.f, n2 = 0.f, n1 = 0.f;
+    const int hb = 63 - __builtin_clzll(var);
+    const int lo = max(hb - (RADIX_BITS - 1), 0);
+    const uint64_t hi_mask = hb == 63 ? 0ull : ~((2ull << hb) - 1);  // bits above the window: all decided
+    const uint32_t dmask = (uint32_t)((2ull << (hb - lo)) - 1);
+    const uint64_t pre = tau & hi_mask;
     src.each([&](uint64_t v) {
-      n3 += v >= c3 ? 1.f : 0.f;
-      n2 += v >= c2 ? 1.f : 0.f;
-      n1 += v >= c1 ? 1.f : 0.f;
+      if ((v & hi_mask) == pre) atomicAdd(&hist[(uint32_t)(v >> lo) & dmask], 1u);
     });
-    n3 = wave_sum(n3);
-    n2 = wave_sum(n2);
-    n1 = wave_sum(n1);
-    float* pp = part + ph * 3 * NWAVE;
-    if (lane == 0) {
-      pp[wave] = n3;
-      pp[NWAVE + wave] = n2;
-      pp[2 * NWAVE + wave] = n1;
-    }
     __syncthreads();
-    ph ^= 1;
-    const int m3 = (int)(pp[0] + pp[1] + pp[2] + pp[3]);
-    const int m2 = (int)(pp[NWAVE] + pp[NWAVE + 1] + pp[NWAVE + 2] + pp[NWAVE + 3]);
-    const int m1 = lo ? (int)(pp[2 * NWAVE] + pp[2 * NWAVE + 1] + pp[2 * NWAVE + 2] + pp[2 * NWAVE + 3]) : 0;
-    int n = -1;
-    if (lo && m3 >= kk) {
-      tau = c3;
-      n = m3;
-    } else if (m2 >= kk) {
-      tau = c2;
-      n = m2;
-    } else if (lo && m1 >= kk) {
-      tau = c1;
-      n = m1;
+    // Thread t holds the bins of group 255 - t, so the exclusive scan counts
+    // the candidates in higher bins.
+    const int g = WG - 1 - t;
+    uint32_t h[PER];
+    int local = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      h[i] = hist[g * PER + i];
+      local += (int)h[i];
     }
-    if (n == kk) break;
+    int tot;
+    int above = block_count_scan(local, ired, tot);
+#pragma unroll
+    for (int i = PER - 1; i >= 0; --i) {
+      if (above < need && need <= above + (int)h[i]) {
+        s_digit = g * PER + i;
+        s_above = above;
+        s_count = (int)h[i];
+      }
+      above += (int)h[i];
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) hist[g * PER + i] = 0u;  // ready for the next window
+    __syncthreads();
+    need -= s_above;
+    tau |= (uint64_t)s_digit << lo;
+    var &= ~((uint64_t)dmask << lo);
+    const bool done = s_count == need;
+    __syncthreads();  // s_* are rewritten by the next window
+    if (done) break;
   }
-  __syncthreads();  // the partial buffers are reused by the caller
   return tau;
 }
 
@@ -958,105 +1024,128 @@ __device__ __forceinline__ float take_kept(const Src& src, uint64_t thr, int d, 
 
 template <typename ET>
 __global__ __launch_bounds__(WG) void merge_kernel(Args a) {
-  extern __shared__ int loff[];  // list offsets in the concatenation (NL <= MERGE_MAX_LISTS)
-  __shared__ uint64_t sel[SV_MAX_TOPK];
-  __shared__ uint64_t sh64[3 * NWAVE];
-  __shared__ float red[2 * 3 * NWAVE];
-  __shared__ int s_n;
+  __shared__ __align__(16) uint64_t sel[SV_MAX_TOPK + 2];  // kept composites (+ a zero pad entry)
+  __shared__ uint64_t ovf[MERGE_OVF];
+  __shared__ uint32_t hist[RADIX_BINS];  // radix histogram, then the ranks of the kept entries
+  static_assert(RADIX_BINS >= SV_MAX_TOPK, "ranks reuse the histogram");
+  int* rank = reinterpret_cast<int*>(hist);
+  __shared__ uint32_t sh32[4 * NWAVE];
+  __shared__ float red[NWAVE];
+  __shared__ int ired[NWAVE];
+  __shared__ int s_n, s_novf;
   __shared__ uint32_t s_ld;
   const int i = blockIdx.x % a.K, b = blockIdx.x / a.K;
   const float T = a.temp[b];
   if (!is_sampling_temperature(T)) return;
-  const int t = threadIdx.x;
-  const int NL = a.C * NWAVE, kk = min(a.topk, a.V);
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int C = a.C, NL = C * NWAVE, kk = min(a.topk, a.V);
   const size_t slot = (size_t)b * a.K + i;
-  const uint64_t* g = a.cand + slot * NL * WCAP;
+  using CT = typename Cand<ET>::T;
+  const CT* g = reinterpret_cast<const CT*>(a.cand) + slot * NL * WCAP;
   const int* gcnt = a.ccnt + slot * NL;
   const int d = a.tok[slot];
   const float s = LOG2E / T;
-
-  // Offsets of the lists in their concatenation (when the lists are few).
-  int N = INT_MAX;
-  if (NL <= MERGE_MAX_LISTS) {
-    constexpr int PER = MERGE_MAX_LISTS / WG;
-    int c4[PER], local = 0;
-#pragma unroll
-    for (int r = 0; r < PER; ++r) {
-      const int L = t * PER + r;
-      c4[r] = L < NL ? gcnt[L] : 0;
-      local += c4[r];
-    }
-    float ex, tot;
-    block_scan((float)local, red, ex, tot);
-    int o = (int)ex;
-#pragma unroll
-    for (int r = 0; r < PER; ++r) {
-      const int L = t * PER + r;
-      if (L < NL) loff[L] = o;
-      o += c4[r];
-    }
-    N = (int)tot;
-  }
   if (t == 0) {
     s_n = 0;
+    s_novf = 0;
     s_ld = 0xFFFFFFFFu;
   }
-  __syncthreads();
   uint64_t thr;
   float m, z;
-  if (N <= MERGE_REG_CAP) {
-    // Entry j = t + r * WG comes from the last list whose offset is <= j
-    // (binary lifting over the offsets, all of the thread's entries at once).
-    RegCands rc;
-    rc.N = N;
-    int Lr[MERGE_REG];
+  if (C <= MERGE_REG) {
+    // One round of loads: the lengths of the wave's lists (lane r holds list
+    // wave + NWAVE * r) and the first 64 entries of each (read whole: a list
+    // area holds WCAP entries).
+    RegCands<ET> rc;
+    rc.CS = a.CS;
+    const int my_cnt = lane < C ? gcnt[wave + NWAVE * lane] : 0;
 #pragma unroll
-    for (int r = 0; r < MERGE_REG; ++r) Lr[r] = 0;
-    int step = 1;
-    while (2 * step < NL) step *= 2;
-    for (; step > 0; step >>= 1) {
-#pragma unroll
-      for (int r = 0; r < MERGE_REG; ++r) {
-        const int c = Lr[r] + step;
-        if (c < NL && loff[c] <= t + r * WG) Lr[r] = c;
-      }
-    }
+    for (int r = 0; r < MERGE_REG; ++r) rc.v[r] = r < C ? g[(size_t)(wave + NWAVE * r) * WCAP + lane] : CT(0);
+    __syncthreads();  // s_n / s_novf / rank initialised
+    // Entries past the 64th go to the overflow buffer: one reservation per
+    // wave, then one round of loads for entries 64..127 (entries 128 and
+    // up, rarer still, one load at a time).
+    rc.valid = 0u;
+    int extra = 0;
 #pragma unroll
     for (int r = 0; r < MERGE_REG; ++r) {
-      const int j = t + r * WG;
-      rc.v[r] = j < N ? g[(size_t)Lr[r] * WCAP + (j - loff[Lr[r]])] : 0;
+      const int n = r < C ? __builtin_amdgcn_readlane(my_cnt, r) : 0;
+      if (lane < n) rc.valid |= 1u << r;
+      extra += max(0, n - 64);
     }
-    thr = select_threshold(rc, kk, sh64, red, &m);
-    z = take_kept(rc, thr, d, s, mul_rn(m, s), sel, &s_n, &s_ld);
+    int base = 0;
+    if (extra > 0) {  // wave-uniform
+      if (lane == 0) base = atomicAdd(&s_novf, extra);
+      base = __builtin_amdgcn_readfirstlane(base);
+      CT w2[MERGE_REG];
+#pragma unroll
+      for (int r = 0; r < MERGE_REG; ++r) {
+        const int n = r < C ? __builtin_amdgcn_readlane(my_cnt, r) : 0;
+        w2[r] = 64 + lane < n ? g[(size_t)(wave + NWAVE * r) * WCAP + 64 + lane] : CT(0);
+      }
+      int o = base;
+#pragma unroll
+      for (int r = 0; r < MERGE_REG; ++r) {
+        const int n = r < C ? __builtin_amdgcn_readlane(my_cnt, r) : 0;
+        if (64 + lane < n && o + lane < MERGE_OVF) ovf[o + lane] = cand_composite<ET>(w2[r], r * a.CS);
+        for (int j = 128 + lane; j < n; j += 64)
+          if (o + j - 64 < MERGE_OVF)
+            ovf[o + j - 64] = cand_composite<ET>(g[(size_t)(wave + NWAVE * r) * WCAP + j], r * a.CS);
+        o += max(0, n - 64);
+      }
+    }
+    __syncthreads();
+    rc.ovf = ovf;
+    rc.novf = s_novf;
+    if (rc.novf <= MERGE_OVF) {
+      thr = select_threshold(rc, kk, sh32, red, ired, hist, &m);
+      z = take_kept(rc, thr, d, s, mul_rn(m, s), sel, &s_n, &s_ld);
+    } else {
+      const ListCands<ET> lc{g, gcnt, NL, a.CS};
+      thr = select_threshold(lc, kk, sh32, red, ired, hist, &m);
+      z = take_kept(lc, thr, d, s, mul_rn(m, s), sel, &s_n, &s_ld);
+    }
   } else {
-    const ListCands lc{g, gcnt, NL};
-    thr = select_threshold(lc, kk, sh64, red, &m);
+    __syncthreads();
+    const ListCands<ET> lc{g, gcnt, NL, a.CS};
+    thr = select_threshold(lc, kk, sh32, red, ired, hist, &m);
     z = take_kept(lc, thr, d, s, mul_rn(m, s), sel, &s_n, &s_ld);
   }
   const float Z = block_sum(z, red);  // also orders sel[] and s_ld before their reads
   const float ms = mul_rn(m, s);
-  // Place each kept composite by its rank in id order (~id is larger for
-  // lower ids); two entries per 16-byte LDS read.
-  uint2* kept = a.kept + slot * a.topk;
+  for (int j = t; j < kk; j += WG) rank[j] = 0;
+  __syncthreads();
+  // Rank of each kept composite in id order (~id is larger for lower ids):
+  // work items (entry j, block of 64 others) add their counts to rank[j].
+  // Entries are read two at a time (16-byte LDS reads); sel[kk] is zeroed
+  // first so that an odd kk reads a zero (never larger) in its last pair.
+  const int nblk = (kk + 63) / 64;
+  if (t == 0) sel[kk] = 0ull;  // kk < SV_MAX_TOPK + 1 entries: see the declaration
+  __syncthreads();
   const uint4* s4 = reinterpret_cast<const uint4*>(sel);
+  for (int w = t; w < kk * nblk; w += WG) {
+    const int j = w % kk, p0 = (w / kk) * 32, p1 = min(p0 + 32, (kk + 1) / 2);
+    const uint32_t nid = (uint32_t)sel[j];
+    int c = 0;
+#pragma unroll 8
+    for (int q = p0; q < p1; ++q) {
+      const uint4 e = s4[q];
+      c += (e.x > nid) + (e.z > nid);
+    }
+    atomicAdd(&rank[j], c);
+  }
+  __syncthreads();
+  uint2* kept = a.kept + slot * a.topk;
   for (int j = t; j < kk; j += WG) {
     const uint64_t v = sel[j];
-    const uint32_t nid = (uint32_t)v;
-    int pos = 0;
-    const int pairs = kk >> 1;
-#pragma unroll 8
-    for (int q = 0; q < pairs; ++q) {
-      const uint4 w = s4[q];
-      pos += (w.x > nid) + (w.z > nid);
-    }
-    if (kk & 1) pos += (uint32_t)sel[kk - 1] > nid;
-    kept[pos] = make_uint2((uint32_t)composite_id(v), __float_as_uint(composite_value(v)));
+    kept[rank[j]] = make_uint2((uint32_t)composite_id(v), __float_as_uint(composite_value(v)));
   }
   if (t == 0) {
     const uint32_t lb = s_ld;
     const float qd = lb != 0xFFFFFFFFu ? exp2_fast(fmaf(__uint_as_float(lb), s, -ms)) / Z : 0.f;
     a.qstat[slot] = make_float4(m, Z, qd, (float)kk);
   }
+  (void)lane;
 }
 
 // ============================================================================
@@ -1280,8 +1369,7 @@ int make_plan(int B, int K, int V, int topk, int dtype, Plan& pl) {
     off = align256(off + sizeof(float4) * slots);
     pl.off_kept = off;
     off = align256(off + sizeof(uint2) * slots * topk);
-    const size_t NL = (size_t)C * NWAVE;
-    pl.merge_lds = NL <= (size_t)MERGE_MAX_LISTS ? NL * sizeof(int) : 0;
+    pl.merge_lds = 0;
   }
   pl.total = off;
   // Dynamic LDS of the finishing work-groups: the row's partials and
@@ -1346,7 +1434,7 @@ int run(const void* tgt, const void* dft, const int32_t* tok, const float* uni, 
   a.B = B; a.K = K; a.V = V; a.C = pl.C; a.CS = pl.CS; a.topk = topk;
   a.GA = (2 * K + 1) * pl.C;
   a.cache = pl.cache ? 1 : 0;
-  a.cand = topk > 0 ? reinterpret_cast<uint64_t*>(base + pl.off_cand) : nullptr;
+  a.cand = topk > 0 ? static_cast<void*>(base + pl.off_cand) : nullptr;
   a.ccnt = topk > 0 ? reinterpret_cast<int*>(base + pl.off_ccnt) : nullptr;
   a.qstat = topk > 0 ? reinterpret_cast<float4*>(base + pl.off_qstat) : nullptr;
   a.kept = topk > 0 ? reinterpret_cast<uint2*>(base + pl.off_kept) : nullptr;

@@ -115,6 +115,10 @@ constexpr int ROW_HALF_MIRROR = 0x141;
 constexpr int ROW_MIRROR = 0x140;
 constexpr int ROW_BCAST15 = 0x142;
 constexpr int ROW_BCAST31 = 0x143;
+constexpr int ROW_SHR1 = 0x111;
+constexpr int ROW_SHR2 = 0x112;
+constexpr int ROW_SHR4 = 0x114;
+constexpr int ROW_SHR8 = 0x118;
 }  // namespace dpp
 
 template <int CTRL, int ROW_MASK = 0xF>
@@ -147,6 +151,36 @@ __device__ __forceinline__ float wave_sum(float v) {
   v += dpp_f<dpp::ROW_BCAST15, 0xA>(0.f, v);
   v += dpp_f<dpp::ROW_BCAST31, 0xC>(0.f, v);
   return lane63(v);
+}
+// Inclusive scan over the 64 lanes in lane order: shifts by 1, 2, 4, 8 inside
+// each row of 16 lanes, then lane 15 of a row is added to the next row and
+// lane 31 to the upper half.  Exact for integer-valued floats below 2^24.
+__device__ __forceinline__ float wave_incl_scan(float v) {
+  v += dpp_f<dpp::ROW_SHR1>(0.f, v);
+  v += dpp_f<dpp::ROW_SHR2>(0.f, v);
+  v += dpp_f<dpp::ROW_SHR4>(0.f, v);
+  v += dpp_f<dpp::ROW_SHR8>(0.f, v);
+  v += dpp_f<dpp::ROW_BCAST15, 0xA>(0.f, v);
+  v += dpp_f<dpp::ROW_BCAST31, 0xC>(0.f, v);
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_and(uint32_t v) {
+  v &= (uint32_t)dpp_i<dpp::QUAD_1032>(-1, (int)v);
+  v &= (uint32_t)dpp_i<dpp::QUAD_2301>(-1, (int)v);
+  v &= (uint32_t)dpp_i<dpp::ROW_HALF_MIRROR>(-1, (int)v);
+  v &= (uint32_t)dpp_i<dpp::ROW_MIRROR>(-1, (int)v);
+  v &= (uint32_t)dpp_i<dpp::ROW_BCAST15, 0xA>(-1, (int)v);
+  v &= (uint32_t)dpp_i<dpp::ROW_BCAST31, 0xC>(-1, (int)v);
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
+  v |= (uint32_t)dpp_i<dpp::QUAD_1032>(0, (int)v);
+  v |= (uint32_t)dpp_i<dpp::QUAD_2301>(0, (int)v);
+  v |= (uint32_t)dpp_i<dpp::ROW_HALF_MIRROR>(0, (int)v);
+  v |= (uint32_t)dpp_i<dpp::ROW_MIRROR>(0, (int)v);
+  v |= (uint32_t)dpp_i<dpp::ROW_BCAST15, 0xA>(0, (int)v);
+  v |= (uint32_t)dpp_i<dpp::ROW_BCAST31, 0xC>(0, (int)v);
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 // (value, index) argmax: larger value wins, equal values go to the lower index.
 __device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2) {
@@ -235,6 +269,25 @@ __device__ __forceinline__ float block_scan(float v, float* sh, float& excl, flo
   total = tot;
   excl = base + prev;
   return base + inc;
+}
+
+// Scan of integer counts over the block in thread order (DPP inside waves,
+// one barrier pair across them): returns the exclusive prefix, sets the total.
+// `sh` needs NWAVE ints.
+__device__ __forceinline__ int block_count_scan(int v, int* sh, int& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int inc = (int)wave_incl_scan((float)v);
+  if (lane == 63) sh[w] = inc;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int k = 0; k < NWAVE; ++k) {
+    if (k < w) base += sh[k];
+    tot += sh[k];
+  }
+  __syncthreads();
+  total = tot;
+  return base + inc - v;
 }
 
 }  // namespace sv
