@@ -50,6 +50,7 @@
 #include <climits>
 #include <cstddef>
 #include <cstdint>
+#include <type_traits>
 
 #include <hip/hip_ext.h>
 
@@ -324,27 +325,42 @@ __device__ void topk_chunk(const u32x4 (&r)[NV_TILE], int lo, int len, int k, ty
     // Passing logits are staged in LDS (a wave's stores there cost little
     // however sparse its lanes are) and written out as whole lists below.
     // Two logits per ballot round; the order of a list does not matter.
+    // Positions wrap inside the wave's staging area: a list that overflows
+    // it is discarded below, so its clobbered entries are never read.
+    // Padding past the chunk reads as -inf, so it can only pass a bound of
+    // -inf, the one case that needs the explicit range check.
     using ST = typename Staged<ET>::T;
     ST* stage = reinterpret_cast<ST*>(cbuf) + wave * WCAP;
     int n = 0;  // wave-uniform
     auto below = [](unsigned long long m) {
       return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
     };
+    auto compact = [&](auto check) {
 #pragma unroll
-    for (int j = 0; j < NV_TILE; ++j)
+      for (int j = 0; j < NV_TILE; ++j)
 #pragma unroll
-      for (int e = 0; e < VEC; e += 2) {
-        const float xa = Tr<ET>::at(r[j], e), xb = Tr<ET>::at(r[j], e + 1);
-        const int off = (j * WG + t) * VEC + e;
-        const bool pa = off < len && xa >= bound, pb = off + 1 < len && xb >= bound;
-        const unsigned long long ma = __ballot(pa), mb = __ballot(pb);
-        if (ma | mb) {
-          const int pos = n + below(ma) + below(mb);
-          if (pa && pos < WCAP) stage[pos] = Staged<ET>::pack(xa, off);
-          if (pb && pos + pa < WCAP) stage[pos + pa] = Staged<ET>::pack(xb, off + 1);
-          n += __popcll(ma) + __popcll(mb);
+        for (int e = 0; e < VEC; e += 2) {
+          const float xa = Tr<ET>::at(r[j], e), xb = Tr<ET>::at(r[j], e + 1);
+          const int off = (j * WG + t) * VEC + e;
+          bool pa = xa >= bound, pb = xb >= bound;
+          if (decltype(check)::value) {
+            pa = pa && off < len;
+            pb = pb && off + 1 < len;
+          }
+          const unsigned long long ma = __ballot(pa), mb = __ballot(pb);
+          if (ma | mb) {
+            const int na = __popcll(ma);
+            if (pa) stage[(n + below(ma)) & (WCAP - 1)] = Staged<ET>::pack(xa, off);
+            if (pb) stage[(n + na + below(mb)) & (WCAP - 1)] = Staged<ET>::pack(xb, off + 1);
+            n += na + __popcll(mb);
+          }
         }
-      }
+    };
+    static_assert((WCAP & (WCAP - 1)) == 0, "wrap-around staging");
+    if (bound > NEG_INF)
+      compact(std::false_type{});
+    else
+      compact(std::true_type{});
     if (lane == 0) {
       cnts[wave] = min(n, WCAP);
       if (n > WCAP) s_over = 1;
