@@ -1234,31 +1234,31 @@ __global__ __launch_bounds__(WG) void finish_kernel(Args a) {
     // Sparse draft: q~ is non-zero only at the kept ids, so the residual of
     // a sub-block is sum(p) - sum over its kept ids of min(p, q~).  Only the
     // target row is re-read.
-    const float4 qs = a.qstat[(size_t)b * K + n];
-    MSq = mul_rn(qs.x, s);
-    rZq = 1.f / qs.y;
-    const int nkept = (int)qs.w;
+    // The kept list, its statistics and the tile are loaded in one round.
     const uint2* kept = a.kept + ((size_t)b * K + n) * a.topk;
+    const float4 qs = a.qstat[(size_t)b * K + n];
+    uint2 e0 = make_uint2(0xFFFFFFFFu, 0u);
+    if (t < a.topk) e0 = kept[t];
     const ET* trow = target_row<ET>(a, b, n);
     u32x4 rt[NV_TILE];
     load_tile<ET, ALIGNED, NV_TILE>(trow, lo, len, rt);
-    // Correction of each kept id in this chunk, in id order, with its
-    // sub-block (the entries of one sub-block are contiguous).
+    MSq = mul_rn(qs.x, s);
+    rZq = 1.f / qs.y;
+    const int nkept = (int)qs.w;
+    // Correction min(p, q~) of each kept id in this chunk (0 elsewhere); the
+    // ids go to kid[] in their (ascending) order.
     float* corr = kq;
-    int* csub = kid;
     for (int j = t; j < nkept; j += WG) {
-      const int id = (int)kept[j].x;
+      const uint2 e = j == t ? e0 : kept[j];
+      const int id = (int)e.x;
       float cv = 0.f;
-      int sb = -1;
       if (id >= lo && id < lo + len) {
         const float pv = exp2_fast(fmaf(Tr<ET>::load1(trow + id), s, -MSt)) * rZt;
-        const float qv = exp2_fast(fmaf(__uint_as_float(kept[j].y), s, -MSq)) * rZq;
+        const float qv = exp2_fast(fmaf(__uint_as_float(e.y), s, -MSq)) * rZq;
         cv = fminf(pv, qv);
-        const int vi = (id - lo) / VEC;            // vector index in the chunk
-        sb = (vi / WG) * NWAVE + (vi % WG) / 64;   // sub-block (j, wave)
       }
       corr[j] = cv;
-      csub[j] = sb;
+      kid[j] = id;
     }
 #pragma unroll
     for (int j = 0; j < NV_TILE; ++j) {
@@ -1273,9 +1273,19 @@ __global__ __launch_bounds__(WG) void finish_kernel(Args a) {
     }
     __syncthreads();
     if (t < NSUB) {
+      // Sub-block t holds the ids lo + [t, t+1) * 64 * VEC: a contiguous run
+      // of the sorted kept list, summed in list order.
+      auto lower = [&](int x) {
+        int l0 = 0, h0 = nkept;
+        while (l0 < h0) {
+          const int mid = (l0 + h0) >> 1;
+          if (kid[mid] < x) l0 = mid + 1; else h0 = mid;
+        }
+        return l0;
+      };
+      const int j0 = lower(lo + t * 64 * VEC), j1 = lower(lo + (t + 1) * 64 * VEC);
       float cs = 0.f;
-      for (int j = 0; j < nkept; ++j)
-        if (csub[j] == t) cs += corr[j];
+      for (int j = j0; j < j1; ++j) cs += corr[j];
       shsub[t] = fmaxf(0.f, shsub[t] - cs);
     }
     __syncthreads();
