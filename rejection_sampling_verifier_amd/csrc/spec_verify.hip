@@ -759,53 +759,56 @@ __device__ __forceinline__ void final_draw(const Args& a, int b, int n, float s,
     const float mc = view_part(a, v, b, n, c, 0), zc = view_part(a, v, b, n, c, 1);
     return mc == NEG_INF ? 0.f : zc * exp2_fast(mul_rn(mc, s) - MSt) * rZt;
   };
-  // Scan of the chunk masses in groups of 64 chunks.  Pass 1 (tv < 0) gives
-  // S; pass 2 returns the selected chunk and its exclusive prefix.  Both
-  // passes compute the same values.
-  auto scan_select = [&](bool use_p, float tv, int& cs, float& exc_cs) -> float {
-    float carry = 0.f;
-    int last = -1;
-    cs = -1;
-    for (int base = 0; base < C; base += 64) {
-      const int c = base + l;
-      const float m = c < C ? (use_p ? p_mass(c) : chunk_mass(c)) : 0.f;
-      float in = m;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const float u = __shfl_up(in, o, 64);
-        if (l >= o) in += u;
-      }
-      float ex = __shfl_up(in, 1, 64);
-      if (l == 0) ex = 0.f;
-      if (tv >= 0.f) {
-        const unsigned long long hit = __ballot(c < C && carry + in > tv);
-        if (hit) {
-          const int q = (int)__builtin_ctzll(hit);
-          cs = base + q;
-          exc_cs = carry + __shfl(ex, q, 64);
-          return carry;
-        }
-        const unsigned long long pos = __ballot(c < C && m > 0.f);
-        if (pos) last = base + 63 - (int)__builtin_clzll(pos);
-      }
-      carry += __shfl(in, 63, 64);
-    }
-    if (tv >= 0.f) {  // t reached the total only through rounding: last chunk of positive mass
-      cs = last >= 0 ? last : 0;
-      exc_cs = -__builtin_inff();
+  // Chunk masses in groups of 64 chunks (lane l holds chunk base + l) and
+  // their wave scan (DPP); the exclusive prefix is the previous lane's.
+  auto group = [&](bool use_p, int base, float& m, float& in, float& ex) {
+    const int c = base + l;
+    m = c < C ? (use_p ? p_mass(c) : chunk_mass(c)) : 0.f;
+    in = wave_incl_scan(m);
+    ex = __shfl_up(in, 1, 64);
+    if (l == 0) ex = 0.f;
+  };
+  // Pass 1: the total S.  The first group's values are kept for pass 2.
+  bool fallback = false;
+  float m0, in0, ex0;
+  auto total = [&](bool use_p) {
+    group(use_p, 0, m0, in0, ex0);
+    float carry = lane63(in0);
+    for (int base = 64; base < C; base += 64) {
+      float m, in, ex;
+      group(use_p, base, m, in, ex);
+      carry += lane63(in);
     }
     return carry;
   };
-  int cs;
-  float exc_cs = 0.f;
-  bool fallback = false;
-  float S = scan_select(false, -1.f, cs, exc_cs);
+  float S = total(false);
   if (reject && S == 0.f) {
     fallback = true;
-    S = scan_select(true, -1.f, cs, exc_cs);
+    S = total(true);
   }
   const float tv = rs.uK * S;
-  scan_select(fallback, tv, cs, exc_cs);
+  // Pass 2: the first chunk whose inclusive prefix exceeds tv.
+  int cs = -1, last = -1;
+  float exc_cs = 0.f, carry = 0.f;
+  for (int base = 0; base < C; base += 64) {
+    float m = m0, in = in0, ex = ex0;
+    if (base > 0) group(fallback, base, m, in, ex);
+    const int c = base + l;
+    const unsigned long long hit = __ballot(c < C && carry + in > tv);
+    if (hit) {
+      const int q = (int)__builtin_ctzll(hit);
+      cs = base + q;
+      exc_cs = carry + __shfl(ex, q, 64);
+      break;
+    }
+    const unsigned long long pos = __ballot(c < C && m > 0.f);
+    if (pos) last = base + 63 - (int)__builtin_clzll(pos);
+    carry += lane63(in);
+  }
+  if (cs < 0) {  // t reached the total only through rounding: last chunk of positive mass
+    cs = last >= 0 ? last : 0;
+    exc_cs = -__builtin_inff();
+  }
   const float t1 = tv - exc_cs;  // +inf when t reached the total through rounding
   const int lo = cs * a.CS;
   const int len = min(a.CS, a.V - lo);
@@ -1188,9 +1191,11 @@ __global__ __launch_bounds__(WG) void finish_kernel(Args a) {
   const int c = blockIdx.x % a.C;
   const int b = blockIdx.x / a.C;
   const int K = a.K, C = a.C, S = 2 * K + 1, t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  // Sparse draft: the kept entries of the chunk (residual), then the row's
-  // kept list (final draw).
+  // Sparse draft: the row's kept list at the rejected position (ids and q~
+  // values, for the residual and the final draw) and the corrections
+  // min(p, q~) of the ids in this chunk.
   __shared__ float kq[SV_MAX_TOPK];
+  __shared__ float kcorr[SV_MAX_TOPK];
   __shared__ int kid[SV_MAX_TOPK];
   uint32_t* cache_pw = CACHED ? row_cache : nullptr;
   uint32_t* cache_sub = CACHED ? cache_pw + (size_t)S * C * 4 : nullptr;
@@ -1230,6 +1235,7 @@ __global__ __launch_bounds__(WG) void finish_kernel(Args a) {
   const int lo = c * a.CS;
   const int len = min(a.CS, a.V - lo);
   float MSq, rZq;
+  int nkept = 0;
   if (a.topk > 0) {
     // Sparse draft: q~ is non-zero only at the kept ids, so the residual of
     // a sub-block is sum(p) - sum over its kept ids of min(p, q~).  Only the
@@ -1244,21 +1250,22 @@ __global__ __launch_bounds__(WG) void finish_kernel(Args a) {
     load_tile<ET, ALIGNED, NV_TILE>(trow, lo, len, rt);
     MSq = mul_rn(qs.x, s);
     rZq = 1.f / qs.y;
-    const int nkept = (int)qs.w;
+    nkept = (int)qs.w;
     // Correction min(p, q~) of each kept id in this chunk (0 elsewhere); the
     // ids go to kid[] in their (ascending) order.
-    float* corr = kq;
+    float* corr = kcorr;
     for (int j = t; j < nkept; j += WG) {
       const uint2 e = j == t ? e0 : kept[j];
       const int id = (int)e.x;
+      const float qv = exp2_fast(fmaf(__uint_as_float(e.y), s, -MSq)) * rZq;
       float cv = 0.f;
       if (id >= lo && id < lo + len) {
         const float pv = exp2_fast(fmaf(Tr<ET>::load1(trow + id), s, -MSt)) * rZt;
-        const float qv = exp2_fast(fmaf(__uint_as_float(e.y), s, -MSq)) * rZq;
         cv = fminf(pv, qv);
       }
       corr[j] = cv;
       kid[j] = id;
+      kq[j] = qv;
     }
 #pragma unroll
     for (int j = 0; j < NV_TILE; ++j) {
@@ -1324,18 +1331,8 @@ __global__ __launch_bounds__(WG) void finish_kernel(Args a) {
   if (!sh_last) return;
   const bool ok = wait_words(subR_row, C * NSUB, cache_sub, nullptr, 0, nullptr, wall_clock64() + WAIT_TICKS);
   view.sub_loaded = CACHED;
-  int nkept = 0;
-  if (a.topk > 0) {
-    // The row's kept list with its q~ values, for the search in wave 0.
-    nkept = (int)a.qstat[(size_t)b * K + n].w;
-    const uint2* kept = a.kept + ((size_t)b * K + n) * a.topk;
-    for (int j = t; j < nkept; j += WG) {
-      const uint2 e = kept[j];
-      kid[j] = (int)e.x;
-      kq[j] = exp2_fast(fmaf(__uint_as_float(e.y), s, -MSq)) * rZq;
-    }
-    __syncthreads();
-  }
+  // A sparse draft's kept list (ids and q~ values) is still in LDS from the
+  // residual pass.
   final_draw<ET, ALIGNED, CACHED>(a, b, n, s, MSt, rZt, MSq, rZq, rs, view, kid, kq, nkept);
   // With the sums in LDS the other waves clear the published words while
   // wave 0 draws; otherwise the draw reads them, so the clear waits.
