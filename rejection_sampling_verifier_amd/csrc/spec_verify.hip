@@ -395,19 +395,26 @@ void stats_kernel(Args a) {
   const int rest = blockIdx.x / a.C;
   const int slot = rest % S;
   const int b = rest / S;
-  const float T = a.temp[b];
-  const bool greedy = !is_sampling_temperature(T);
   const bool is_draft = slot > a.K;
-  // Greedy rows never read the draft.
-  if (is_draft && greedy) return;
   const int pos = is_draft ? slot - a.K - 1 : slot;
   const ET* row = is_draft ? draft_row<ET>(a, b, pos) : target_row<ET>(a, b, pos);
   const int lo = c * a.CS;
   const int len = min(a.CS, a.V - lo);
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
 
+  // A target slot issues its loads before it needs the temperature; a draft
+  // slot first checks it, since greedy rows never read the draft.
   u32x4 r[NV_TILE];
-  load_tile<ET, ALIGNED, NV_TILE>(row, lo, len, r);
+  float T;
+  if (!is_draft) {
+    load_tile<ET, ALIGNED, NV_TILE>(row, lo, len, r);
+    T = a.temp[b];
+  } else {
+    T = a.temp[b];
+    if (!is_sampling_temperature(T)) return;
+    load_tile<ET, ALIGNED, NV_TILE>(row, lo, len, r);
+  }
+  const bool greedy = !is_sampling_temperature(T);
 
   __shared__ float shf[NWAVE];
   __shared__ int shi[NWAVE];
@@ -558,11 +565,21 @@ struct RowIn {
 };
 __device__ __forceinline__ RowIn load_row_in(const Args& a, int b) {
   const int K = a.K, t = threadIdx.x;
-  RowIn in{a.temp[b], -1, 0.f, 0.f};
-  if (t <= K) in.u = a.uni[(size_t)b * (K + 1) + t];
-  if (t < K) {
-    in.d = a.tok[(size_t)b * K + t];
-    if (a.topk > 0) in.qd = a.qstat[(size_t)b * K + t].z;
+  // Loaded per lane, without branches, so that nothing waits for these
+  // loads before their first use (lanes past K read a valid entry and drop it).
+  int bv = b;
+  asm volatile("" : "+v"(bv));
+  RowIn in{a.temp[bv], -1, 0.f, 0.f};
+  in.u = a.uni[(size_t)b * (K + 1) + min(t, K)];
+  if (K > 0) {
+    const size_t i = (size_t)b * K + min(t, K - 1);
+    in.d = a.tok[i];
+    if (a.topk > 0) in.qd = a.qstat[i].z;
+  }
+  if (t > K) in.u = 0.f;
+  if (t >= K) {
+    in.d = -1;
+    in.qd = 0.f;
   }
   return in;
 }
@@ -571,33 +588,70 @@ template <bool CACHED>
 __device__ __forceinline__ void decide_row(const Args& a, int b, RowShared& rs, const RowView<CACHED>& v,
                                            const RowIn& in) {
   const int K = a.K, C = a.C, t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const float T = in.T;
+  const float T = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(in.T)));
   const bool greedy = !is_sampling_temperature(T);
   const float s = greedy ? 0.f : LOG2E / T;
   const int d = in.d;
   const float u = in.u;
   if (t == K) rs.uK = u;
   const int nmerge = (greedy || a.topk > 0) ? K + 1 : 2 * K + 1;
-  for (int slot = wave; slot < nmerge; slot += NWAVE) {
+  // Each wave merges three slots at a time, so that their reduction chains
+  // overlap.
+  constexpr int U = 3;
+  for (int base = wave; base < nmerge; base += U * NWAVE) {
     if (greedy) {
-      float bv = NEG_INF;
-      int bi = INT_MAX;
-      for (int c = lane; c < C; c += 64)
-        argmax_merge(bv, bi, view_part(a, v, b, slot, c, 0), __float_as_int(view_part(a, v, b, slot, c, 2)));
-      wave_argmax(bv, bi);
-      if (lane == 0) { rs.M[slot] = bv; rs.Z[slot] = 0.f; rs.idx[slot] = bi; }
-    } else {
-      float m = NEG_INF;
-      for (int c = lane; c < C; c += 64) m = fmaxf(m, view_part(a, v, b, slot, c, 0));
-      m = wave_max(m);
-      const float MS = mul_rn(m, s);
-      float z = 0.f;
-      for (int c = lane; c < C; c += 64) {
-        const float mc = view_part(a, v, b, slot, c, 0), zc = view_part(a, v, b, slot, c, 1);
-        if (mc != NEG_INF) z += zc * exp2_fast(mul_rn(mc, s) - MS);
+      float bv[U];
+      int bi[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int slot = base + u * NWAVE;
+        bv[u] = NEG_INF;
+        bi[u] = INT_MAX;
+        if (slot < nmerge)
+          for (int c = lane; c < C; c += 64)
+            argmax_merge(bv[u], bi[u], view_part(a, v, b, slot, c, 0),
+                         __float_as_int(view_part(a, v, b, slot, c, 2)));
       }
-      z = wave_sum(z);
-      if (lane == 0) { rs.M[slot] = m; rs.Z[slot] = z; rs.idx[slot] = 0; }
+#pragma unroll
+      for (int u = 0; u < U; ++u) wave_argmax(bv[u], bi[u]);
+      if (lane == 0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int slot = base + u * NWAVE;
+          if (slot < nmerge) { rs.M[slot] = bv[u]; rs.Z[slot] = 0.f; rs.idx[slot] = bi[u]; }
+        }
+      }
+    } else {
+      float m[U], z[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int slot = base + u * NWAVE;
+        m[u] = NEG_INF;
+        if (slot < nmerge)
+          for (int c = lane; c < C; c += 64) m[u] = fmaxf(m[u], view_part(a, v, b, slot, c, 0));
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) m[u] = wave_max(m[u]);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int slot = base + u * NWAVE;
+        const float MS = mul_rn(m[u], s);
+        z[u] = 0.f;
+        if (slot < nmerge)
+          for (int c = lane; c < C; c += 64) {
+            const float mc = view_part(a, v, b, slot, c, 0), zc = view_part(a, v, b, slot, c, 1);
+            if (mc != NEG_INF) z[u] += zc * exp2_fast(mul_rn(mc, s) - MS);
+          }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) z[u] = wave_sum(z[u]);
+      if (lane == 0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int slot = base + u * NWAVE;
+          if (slot < nmerge) { rs.M[slot] = m[u]; rs.Z[slot] = z[u]; rs.idx[slot] = 0; }
+        }
+      }
     }
   }
   __syncthreads();
