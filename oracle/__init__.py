@@ -14,8 +14,11 @@ forms, brute force, a worked example).  See ``oracle/verifier.py``.
 from .verifier import (  # noqa: F401
     BF16,
     F32,
+    Relaxed,
     RowResult,
     decode_logits,
+    relaxed_gamma,
+    target_rank,
     tempered_softmax,
     topk_keep_mask,
     verify_row,

@@ -102,6 +102,43 @@ def topk_keep_mask(logits: np.ndarray, k: int) -> np.ndarray:
     return keep
 
 
+@dataclass(frozen=True)
+class Relaxed:
+    """Parameters of the lossy relaxed acceptance rule.
+
+    [Acceptance Is Not Speed] section 1 describes relaxed verification that
+    tolerates q > p within a divergence budget; its section 6 harness and
+    section 7 recommendations add a support filter.  The rule, restated:
+
+    * support guard: reject d if its target rank exceeds ``max_rank`` (rank 1
+      is the most likely token; ``max_rank <= 0`` disables the check) or if
+      p(d) < ``min_prob``;
+    * strict branch: accept if q(d) <= p(d) (and p(d) > 0);
+    * otherwise accept iff u * q(d) < gamma with
+      gamma = min(p + sqrt(2 * alpha * p * (1 - p)), 1).
+
+    With alpha = 0 and no guard this is the lossless rule.
+    """
+
+    alpha: float = 0.0
+    max_rank: int = 0
+    min_prob: float = 0.0
+
+
+def relaxed_gamma(p: float, alpha: float) -> float:
+    """gamma(p) = min(p + sqrt(2 alpha p (1 - p)), 1) ([Acceptance Is Not
+    Speed] section 6: the reverse-KL budget expanded to second order)."""
+    return min(p + float(np.sqrt(2.0 * alpha * p * (1.0 - p))), 1.0)
+
+
+def target_rank(logits: np.ndarray, tok: int) -> int:
+    """1 + the number of ids whose logit is strictly larger than tok's (equal
+    logits share the better rank).  Order on logits equals order on p for
+    T > 0."""
+    logits = np.asarray(logits, dtype=np.float64)
+    return 1 + int(np.count_nonzero(logits > logits[tok]))
+
+
 @dataclass
 class RowResult:
     """Outcome of verifying one row, with the diagnostics the parity tests use.
@@ -118,6 +155,8 @@ class RowResult:
     gap         distance from t = u_K*S to the nearer edge of the sampled
                 token's CDF interval (probability units); inf for greedy.
     fallback    True when a zero residual fell back to the target row.
+    ranks       int64 [K]: target rank of each draft token under the relaxed
+                rule (0 when not computed or the token is out of range).
     """
 
     tokens: np.ndarray
@@ -129,6 +168,7 @@ class RowResult:
     S: float
     gap: float
     fallback: bool
+    ranks: np.ndarray = None
 
     def min_margin(self) -> float:
         """Smallest margin over the decisions this row actually took.
@@ -145,7 +185,7 @@ class RowResult:
         return min(m, self.gap)
 
 
-def verify_row(tl, dl, d, u, T: float, k: int = 0) -> RowResult:
+def verify_row(tl, dl, d, u, T: float, k: int = 0, relaxed: Relaxed | None = None) -> RowResult:
     """Verify one row of K draft tokens against K+1 target positions.
 
     tl  float64 [K+1, V] target logits; row i is the target's next-token
@@ -158,6 +198,10 @@ def verify_row(tl, dl, d, u, T: float, k: int = 0) -> RowResult:
     u   float [K+1] uniforms in [0, 1).
     T   temperature of this row; T <= 0 selects greedy verification.
     k   sparse draft truncation (0 = none).
+    relaxed  optional lossy acceptance rule (see Relaxed); greedy rows and the
+        final draw are unchanged by it (reading: a relaxed rejection is
+        corrected from the same residual norm(max(0, p - q)), which the pages
+        leave open).
     """
     tl = np.asarray(tl, dtype=np.float64)
     Kp1, V = tl.shape
@@ -199,15 +243,43 @@ def verify_row(tl, dl, d, u, T: float, k: int = 0) -> RowResult:
     p_d = np.zeros(K)
     q_d = np.zeros(K)
     margins = np.zeros(K)
-    n = K
+    ranks = np.zeros(K, dtype=np.int64)
+    accept = np.zeros(K, dtype=bool)
     for i in range(K):
         tok = int(d[i])
         if 0 <= tok < V:
             p_d[i] = P[i][tok]
             q_d[i] = Q[i][tok]
-        margins[i] = abs(u[i] * q_d[i] - p_d[i])
+        if relaxed is None:
+            accept[i] = u[i] * q_d[i] < p_d[i]
+            margins[i] = abs(u[i] * q_d[i] - p_d[i])
+            continue
+        # Relaxed rule: the margin is the smallest distance of any comparison
+        # the rule evaluates to its threshold.
+        p, q = p_d[i], q_d[i]
+        m = float("inf")
+        ok = True
+        if not (0 <= tok < V):
+            ok = False  # p = q = 0: rejected, as under the lossless rule
+        else:
+            ranks[i] = target_rank(tl[i], tok)
+            if relaxed.max_rank > 0 and ranks[i] > relaxed.max_rank:
+                ok = False
+        if ok and relaxed.min_prob > 0:
+            m = min(m, abs(p - relaxed.min_prob))
+            ok = p >= relaxed.min_prob
+        if ok:
+            m = min(m, abs(q - p))
+            if p > 0 and q <= p:
+                accept[i] = True
+            else:
+                g = relaxed_gamma(p, relaxed.alpha)
+                m = min(m, abs(u[i] * q - g))
+                accept[i] = u[i] * q < g
+        margins[i] = m
+    n = K
     for i in range(K):
-        if not (u[i] * q_d[i] < p_d[i]):
+        if not accept[i]:
             n = i
             break
 
@@ -240,17 +312,18 @@ def verify_row(tl, dl, d, u, T: float, k: int = 0) -> RowResult:
 
     tokens[:n] = d[:n]
     tokens[n] = x
-    return RowResult(tokens, n, False, p_d, q_d, margins, S, gap, fallback)
+    return RowResult(tokens, n, False, p_d, q_d, margins, S, gap, fallback, ranks)
 
 
 def verify(target_raw, draft_raw, draft_tokens, uniforms, temperature,
-           topk: int, dtype: str, rows=None) -> list[RowResult]:
+           topk: int, dtype: str, rows=None, relaxed: Relaxed | None = None) -> list[RowResult]:
     """Verify a batch row by row.
 
     target_raw  [B, K+1, V] stored logits (uint16 bf16 patterns or float32)
     draft_raw   [B, K, V] stored logits (may be None if K == 0)
     draft_tokens int [B, K]; uniforms float [B, K+1]; temperature float [B]
     rows        optional iterable of row indices (default: all rows)
+    relaxed     optional lossy acceptance rule (see Relaxed)
     """
     B = target_raw.shape[0]
     K = target_raw.shape[1] - 1
@@ -261,5 +334,5 @@ def verify(target_raw, draft_raw, draft_tokens, uniforms, temperature,
         dl = None
         if K > 0 and T > 0:
             dl = decode_logits(draft_raw[b], dtype)
-        out.append(verify_row(tl, dl, draft_tokens[b], uniforms[b], T, topk))
+        out.append(verify_row(tl, dl, draft_tokens[b], uniforms[b], T, topk, relaxed))
     return out

@@ -5,7 +5,9 @@ CPU; the real oracle is untouched), rebinds the pin tests to the mutant and
 requires at least one pin to fail.  This shows the pins are not satisfied by
 a wrong oracle: a flipped residual sign, a reused uniform, a shifted slot
 index, a transposed acceptance ratio, a dropped temperature, an off-by-one
-top-k, a non-strict inverse CDF or a wrong greedy replacement.
+top-k, a non-strict inverse CDF, a wrong greedy replacement, or in the relaxed
+rule a dropped factor in gamma, a rank that counts ties or an off-by-one
+rank guard.
 """
 
 from __future__ import annotations
@@ -24,7 +26,7 @@ MUTANTS = {
     "residual_sign": ("w = np.maximum(0.0, P[n] - Q[n])", "w = np.maximum(0.0, Q[n] - P[n])"),
     "reuse_u_n": ("    t = u[K] * S\n    C = np.cumsum(w)", "    t = u[n] * S\n    C = np.cumsum(w)"),
     "shifted_target_slot": ("p_d[i] = P[i][tok]", "p_d[i] = P[min(i + 1, K)][tok]"),
-    "transposed_ratio": ("if not (u[i] * q_d[i] < p_d[i]):", "if not (u[i] * p_d[i] < q_d[i]):"),
+    "transposed_ratio": ("accept[i] = u[i] * q_d[i] < p_d[i]", "accept[i] = u[i] * p_d[i] < q_d[i]"),
     "draft_without_temperature": ("Q.append(tempered_softmax(np.where(keep, dl[i], -np.inf), T))",
                                   "Q.append(tempered_softmax(np.where(keep, dl[i], -np.inf), 1.0))"),
     "bonus_wrong_slot": ("        w = P[K]\n", "        w = P[max(K - 1, 0)]\n"),
@@ -38,6 +40,11 @@ MUTANTS = {
     "greedy_tie_highest_id": ("a = [int(np.argmax(tl[i])) for i in range(K + 1)]",
                               "a = [int(V - 1 - np.argmax(tl[i][::-1])) for i in range(K + 1)]"),
     "residual_unclipped": ("w = np.maximum(0.0, P[n] - Q[n])", "w = np.abs(P[n] - Q[n])"),
+    "gamma_without_factor_two": ("np.sqrt(2.0 * alpha * p * (1.0 - p))", "np.sqrt(alpha * p * (1.0 - p))"),
+    "rank_counts_ties": ("1 + int(np.count_nonzero(logits > logits[tok]))",
+                         "1 + int(np.count_nonzero(logits >= logits[tok]))"),
+    "guard_ignores_rank": ("if relaxed.max_rank > 0 and ranks[i] > relaxed.max_rank:",
+                           "if relaxed.max_rank > 0 and ranks[i] > relaxed.max_rank + 1:"),
 }
 
 
@@ -69,6 +76,10 @@ def _run_pins():
         pins.test_zero_weight_token_never_emitted_at_u_zero,
         pins.test_k0_is_textbook_inverse_cdf,
         pins.test_residual_never_picks_token_where_p_le_q,
+        lambda: pins.test_relaxed_acceptance_probability(0.5, 0.2, 0.8, 0.75),
+        lambda: pins.test_relaxed_acceptance_probability(2.0, 0.5, 0.6, 1.0),
+        pins.test_target_rank_brute_force,
+        pins.test_support_guard,
     ]
     failed = 0
     for c in cases:
@@ -88,4 +99,7 @@ def test_pins_catch_mutant(name, monkeypatch):
     mod = _mutant_module(name)
     for attr in ("verify_row", "tempered_softmax", "topk_keep_mask", "decode_logits"):
         monkeypatch.setattr(pins, attr, getattr(mod, attr))
+    # The relaxed-rule pins reach these through the oracle package.
+    for attr in ("Relaxed", "target_rank", "relaxed_gamma"):
+        monkeypatch.setattr(pins.oracle, attr, getattr(mod, attr))
     assert _run_pins() > 0, f"no pin caught the planted mistake {name!r}"

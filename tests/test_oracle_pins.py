@@ -454,3 +454,109 @@ def test_margins_and_gap_reported():
     assert r.n == 1 and abs(r.margins[0] - 0.25) < 1e-15
     assert abs(r.gap - 0.0) < 1e-15                  # t = 0.5 sits on the edge between 0 and 1
     assert r.tokens[1] == 1
+
+
+# ------------------------------------------------ relaxed (lossy) acceptance
+# [Acceptance Is Not Speed] sections 1, 6 and 7: relaxed verification accepts
+# d with probability min(1, gamma(p)/q), gamma = min(p + sqrt(2 alpha p (1-p)), 1),
+# behind a support guard on the target rank and probability of d.
+def _two_token_logits(p0, T):
+    """Logits of two tokens whose tempered softmax gives token 0 probability p0."""
+    return np.array([0.0, T * math.log((1.0 - p0) / p0)])
+
+
+def _accept_threshold(tl, dl, tok, T, relaxed, lo=0.0, hi=1.0, iters=60):
+    """sup{u : the oracle accepts d at u}, by bisection (acceptance is an
+    interval [0, u*) in u)."""
+    if verify_row(tl, dl, [tok], [hi * (1 - 1e-15), 0.5], T, 0, relaxed).n == 1:
+        return 1.0
+    for _ in range(iters):
+        mid = 0.5 * (lo + hi)
+        if verify_row(tl, dl, [tok], [mid, 0.5], T, 0, relaxed).n == 1:
+            lo = mid
+        else:
+            hi = mid
+    return 0.5 * (lo + hi)
+
+
+@pytest.mark.parametrize("alpha,p,q,expected", [
+    (0.5, 0.2, 0.8, 0.75),     # gamma = 0.2 + sqrt(2*0.5*0.2*0.8) = 0.6; 0.6/0.8
+    (0.125, 0.5, 0.9, 0.75 / 0.9),  # gamma = 0.5 + sqrt(0.0625) = 0.75
+    (0.0, 0.2, 0.8, 0.25),     # alpha = 0: the lossless ratio p/q
+    (2.0, 0.5, 0.6, 1.0),      # gamma clipped at 1 > q: always accepted
+])
+def test_relaxed_acceptance_probability(alpha, p, q, expected):
+    T = 0.7
+    tl = np.stack([_two_token_logits(p, T), np.zeros(2)])
+    dl = _two_token_logits(q, T)[None, :]
+    thr = _accept_threshold(tl, dl, 0, T, oracle.Relaxed(alpha=alpha))
+    assert abs(thr - expected) < 1e-9, (thr, expected)
+
+
+def test_relaxed_zero_alpha_without_guard_is_lossless():
+    rng = np.random.default_rng(5)
+    for trial in range(40):
+        V, K = 9, 3
+        tl = rng.normal(0, 2, (K + 1, V))
+        dl = tl[:K] + rng.normal(0, 1, (K, V))
+        d = rng.integers(0, V, K)
+        u = rng.random(K + 1)
+        k = [0, 4][trial % 2]
+        a = verify_row(tl, dl, d, u, 0.9, k)
+        b = verify_row(tl, dl, d, u, 0.9, k, oracle.Relaxed())
+        assert a.n == b.n and list(a.tokens) == list(b.tokens)
+
+
+def test_relaxed_never_accepts_less_than_lossless():
+    rng = np.random.default_rng(6)
+    for _ in range(60):
+        V, K = 7, 4
+        tl = rng.normal(0, 2, (K + 1, V))
+        dl = tl[:K] + rng.normal(0, 1.5, (K, V))
+        d = rng.integers(0, V, K)
+        u = rng.random(K + 1)
+        a = verify_row(tl, dl, d, u, 1.0)
+        b = verify_row(tl, dl, d, u, 1.0, 0, oracle.Relaxed(alpha=0.3))
+        assert b.n >= a.n
+
+
+def test_target_rank_brute_force():
+    rng = np.random.default_rng(7)
+    for _ in range(50):
+        l = np.round(rng.normal(0, 1, 40), 1)   # many ties
+        tok = int(rng.integers(0, 40))
+        better = sum(1 for x in range(40) if l[x] > l[tok])
+        assert oracle.target_rank(l, tok) == better + 1
+    # through the verifier's diagnostics
+    tl = np.array([[3.0, 2.0, 2.0, 1.0, 0.0], [0.0] * 5])
+    dl = np.array([[3.0, 2.0, 2.0, 1.0, 0.0]])
+    r = verify_row(tl, dl, [3], [0.0, 0.5], 1.0, 0, oracle.Relaxed(max_rank=10))
+    assert r.ranks[0] == 4
+
+
+def test_support_guard():
+    T = 1.0
+    tl = np.array([[3.0, 2.0, 1.0, 0.0, -1.0], [0.0] * 5])
+    dl = np.array([[0.0, 0.0, -4.0, 0.0, 0.0]])   # q(2) < p(2): the strict branch would accept
+    p2 = softmax_T(tl[0], T)[2]
+    assert verify_row(tl, dl, [2], [0.0, 0.5], T).n == 1
+    assert verify_row(tl, dl, [2], [0.0, 0.5], T, 0, oracle.Relaxed(max_rank=2)).n == 0
+    assert verify_row(tl, dl, [2], [0.0, 0.5], T, 0, oracle.Relaxed(max_rank=3)).n == 1
+    assert verify_row(tl, dl, [2], [0.0, 0.5], T, 0, oracle.Relaxed(min_prob=p2 * 1.01)).n == 0
+    assert verify_row(tl, dl, [2], [0.0, 0.5], T, 0, oracle.Relaxed(min_prob=p2 * 0.99)).n == 1
+    # a token outside [0, V) is rejected whatever the budget
+    assert verify_row(tl, dl, [7], [0.0, 0.5], T, 0, oracle.Relaxed(alpha=5.0)).n == 0
+
+
+def test_relaxed_rejection_draws_the_lossless_residual():
+    rng = np.random.default_rng(8)
+    for _ in range(30):
+        V, K = 8, 2
+        tl = rng.normal(0, 2, (K + 1, V))
+        dl = tl[:K] + rng.normal(0, 2, (K, V))
+        d = [int(np.argmax(dl[0])), 0]
+        u = np.array([0.999999, 0.5, rng.random()])
+        a = verify_row(tl, dl, d, u, 1.0)
+        b = verify_row(tl, dl, d, u, 1.0, 0, oracle.Relaxed(alpha=0.05))
+        if a.n == 0 and b.n == 0:
+            assert a.tokens[0] == b.tokens[0] and abs(a.S - b.S) < 1e-15
