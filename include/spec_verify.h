@@ -129,6 +129,44 @@ int spec_verify_probe(const void* target_logits, const void* draft_logits,
                       float* probs_out, float* mass_out);
 
 /*
+ * spec_verify_relaxed - spec_verify with a lossy relaxed acceptance rule in
+ * place of u*q < p ("Acceptance Is Not Speed (arXiv:2610.23818): ...",
+ * newsaint.id: section 1 describes verification that tolerates q > p within
+ * a divergence budget, section 6 gives the budget's rule and a support guard,
+ * section 7 recommends a strict support filter).  For each draft d_i of a
+ * sampling row, in order:
+ *   1. support guard: reject if d_i is outside [0, V), if its target rank
+ *      1 + #{x : l_i(x) > l_i(d_i)} exceeds max_rank (max_rank = 0 disables
+ *      the rank check), or if p_i(d_i) < min_prob;
+ *   2. strict branch: accept if p_i(d_i) > 0 and q_i(d_i) <= p_i(d_i);
+ *   3. otherwise accept iff u_i * q < gamma, gamma = min(p + sqrt(2 alpha p
+ *      (1 - p)), 1) with p = p_i(d_i), q = q_i(d_i).
+ * The first rejection ends the prefix as in spec_verify, and the correction
+ * is drawn from the same residual norm(max(0, p_n - q_n)) (the pages leave
+ * the correction under relaxed rules open; this is the plain reading).
+ * Greedy rows (T <= 0) and the bonus draw are unchanged.  The output
+ * distribution is no longer the target's: the rule is lossy by design.
+ *
+ * alpha     >= 0 divergence budget (0 with max_rank = 0 and min_prob = 0
+ *           gives exactly spec_verify's decisions).
+ * max_rank  >= 0 largest accepted target rank (0 = no rank check).  With a
+ *           rank check the statistics pass also counts, per target position,
+ *           the logits above l(d_i) (one compare per target logit).
+ * min_prob  in [0, 1]: smallest accepted p_i(d_i).
+ * probs_out, mass_out as spec_verify_probe (may be NULL).
+ * Other arguments as spec_verify.  SV_ERR_ARG also for a negative or NaN
+ * alpha, a negative max_rank or min_prob outside [0, 1].
+ */
+int spec_verify_relaxed(const void* target_logits, const void* draft_logits,
+                        const int32_t* draft_tokens, const float* uniforms,
+                        const float* temperature, int B, int K, int V,
+                        int topk_draft, int dtype, float alpha, int max_rank,
+                        float min_prob, int32_t* out_tokens,
+                        int32_t* num_accepted, void* workspace,
+                        size_t* workspace_bytes, hipStream_t stream,
+                        float* probs_out, float* mass_out);
+
+/*
  * spec_verify_timed - spec_verify that also times each of its kernels on the
  * caller's stream, for measurement.
  *

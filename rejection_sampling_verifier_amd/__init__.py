@@ -18,5 +18,6 @@ from .binding import (  # noqa: F401
     plan,
     verify,
     verify_probe,
+    verify_relaxed,
     workspace_bytes,
 )

@@ -58,6 +58,10 @@ def load_library(path: str | None = None):
     lib.spec_verify.restype = _i32
     lib.spec_verify_probe.argtypes = _COMMON + [_vp, _vp]
     lib.spec_verify_probe.restype = _i32
+    lib.spec_verify_relaxed.argtypes = ([_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                          ctypes.c_float, _i32, ctypes.c_float, _vp, _vp, _vp, _sz, _vp,
+                                          _vp, _vp])
+    lib.spec_verify_relaxed.restype = _i32
     lib.spec_verify_timed.argtypes = _COMMON + [ctypes.POINTER(_vp), _i32]
     lib.spec_verify_timed.restype = _i32
     lib.spec_verify_plan.argtypes = [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32)]
@@ -167,6 +171,29 @@ def verify_probe(target, draft, draft_tokens, uniforms, temperature, topk_draft:
     mass = torch.empty((B,), dtype=torch.float32, device=target.device)
     _check(load_library().spec_verify_probe(*args, _ptr(probs), _ptr(mass)))
     return out_tokens, num_accepted, probs, mass
+
+
+def verify_relaxed(target, draft, draft_tokens, uniforms, temperature, topk_draft: int = 0, *,
+                   alpha: float = 0.0, max_rank: int = 0, min_prob: float = 0.0, probes: bool = False,
+                   out_tokens=None, num_accepted=None, workspace=None, stream=None):
+    """spec_verify_relaxed: the lossy relaxed acceptance rule (see the header).
+
+    Returns (out_tokens, num_accepted), plus (probs [B, K, 2], mass [B]) when
+    ``probes`` is set.
+    """
+    args, out_tokens, num_accepted, _ = _prepare(target, draft, draft_tokens, uniforms, temperature,
+                                                 topk_draft, out_tokens, num_accepted, workspace, stream)
+    probs = mass = None
+    if probes:
+        B, Kp1 = out_tokens.shape
+        probs = torch.empty((B, Kp1 - 1, 2), dtype=torch.float32, device=target.device)
+        mass = torch.empty((B,), dtype=torch.float32, device=target.device)
+    a = args[:10] + [ctypes.c_float(alpha), int(max_rank), ctypes.c_float(min_prob)] + args[10:] + \
+        [_ptr(probs), _ptr(mass)]
+    _check(load_library().spec_verify_relaxed(*a))
+    if probes:
+        return out_tokens, num_accepted, probs, mass
+    return out_tokens, num_accepted
 
 
 class StageTimer:

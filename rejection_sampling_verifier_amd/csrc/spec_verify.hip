@@ -99,6 +99,10 @@ struct Args {
   float4* qstat;             // [B, K] sparse draft: {max kept logit, Z_q, q(d_i), kept count}
   uint2* kept;               // [B, K, topk] sparse draft: kept (id, logit bits), ascending id
   int B, K, V, C, CS, topk;
+  // Relaxed (lossy) acceptance: 0 = the lossless rule.  With max_rank > 0 the
+  // statistics kernel also counts, per target chunk, the logits above l(d_i).
+  int relaxed, max_rank;
+  float alpha, min_prob;
   int GA;                    // statistics work-groups per row: (2K+1) * C
   int cache;                 // 1: finishing work-groups keep the row's words in dynamic LDS
 };
@@ -406,9 +410,17 @@ void stats_kernel(Args a) {
   // slot first checks it, since greedy rows never read the draft.
   u32x4 r[NV_TILE];
   float T;
+  // Relaxed rule with a rank guard: a target position counts its logits
+  // above the draft token's logit (a token outside [0, V) counts nothing).
+  const bool count_rank = a.relaxed && a.max_rank > 0 && !is_draft && pos < a.K;
+  float lref = __builtin_inff();
   if (!is_draft) {
     load_tile<ET, ALIGNED, NV_TILE>(row, lo, len, r);
     T = a.temp[b];
+    if (count_rank) {
+      const int d = a.tok[(size_t)b * a.K + pos];
+      if (d >= 0 && d < a.V) lref = Tr<ET>::load1(row + d);
+    }
   } else {
     T = a.temp[b];
     if (!is_sampling_temperature(T)) return;
@@ -466,6 +478,15 @@ void stats_kernel(Args a) {
 #pragma unroll
   for (int j = 1; j < NV_TILE; ++j) zl += zj[j];
   const float z = block_sum(zl, shf);
+  uint32_t above = 0u;
+  if (count_rank) {
+    int na = 0;
+#pragma unroll
+    for (int j = 0; j < NV_TILE; ++j)
+#pragma unroll
+      for (int k = 0; k < VEC; ++k) na += Tr<ET>::at(r[j], k) > lref;  // padding reads as -inf
+    above = (uint32_t)block_sum((float)na, shf);  // exact: counts are below 2^24
+  }
   if (slot == a.K) {
     // Sub-block sums of the bonus position: sub-block (j, wave) holds the
     // 64 * VEC consecutive ids of vector row j owned by that wave.
@@ -484,7 +505,7 @@ void stats_kernel(Args a) {
       const int d = a.tok[(size_t)b * a.K + pos];
       if (d >= lo && d < lo + len) ld = __float_as_uint(Tr<ET>::load1(row + d));
     }
-    *reinterpret_cast<u32x4*>(dst) = u32x4{__float_as_uint(m), __float_as_uint(z), 0u, ld};
+    *reinterpret_cast<u32x4*>(dst) = u32x4{__float_as_uint(m), __float_as_uint(z), above, ld};
   }
   (void)S;
 }
@@ -676,7 +697,30 @@ __device__ __forceinline__ void decide_row(const Args& a, int b, RowShared& rs, 
       rs.p[t] = p;
       rs.q[t] = q;
       rs.tok[t] = d;
-      acc = greedy ? (d == rs.idx[t]) : (u * q < p);
+      if (greedy) {
+        acc = d == rs.idx[t];
+      } else if (!a.relaxed) {
+        acc = u * q < p;
+      } else {
+        // Relaxed rule ([Acceptance Is Not Speed] sections 1, 6, 7): a
+        // support guard on the rank and probability of d, the strict branch
+        // q <= p, else acceptance against gamma = min(p + sqrt(2 a p (1-p)), 1).
+        bool ok = d >= 0 && d < a.V;
+        if (ok && a.max_rank > 0) {
+          uint32_t above = 0u;
+          for (int c = 0; c < C; ++c) above += __float_as_uint(view_part(a, v, b, t, c, 2));
+          ok = above + 1u <= (uint32_t)a.max_rank;
+        }
+        if (ok && a.min_prob > 0.f) ok = p >= a.min_prob;
+        if (!ok) {
+          acc = false;
+        } else if (p > 0.f && q <= p) {
+          acc = true;
+        } else {
+          const float g = fminf(p + __fsqrt_rn(2.f * a.alpha * p * (1.f - p)), 1.f);
+          acc = u * q < g;
+        }
+      }
     }
     const unsigned long long rej = __ballot(!acc);
     if (t == 0) {
@@ -1483,10 +1527,20 @@ int launch_typed(const Args& a, size_t lds, size_t merge_lds, hipStream_t st, hi
   return launch(finish_kernel<ET, AL, false>, a.B * a.C, lds, st, ev ? ev + 4 : nullptr, a);
 }
 
+struct RelaxedRule {
+  float alpha;
+  int max_rank;
+  float min_prob;
+};
+
 int run(const void* tgt, const void* dft, const int32_t* tok, const float* uni, const float* temp,
         int B, int K, int V, int topk, int dtype, int32_t* out, int32_t* nacc, void* ws,
-        size_t* ws_bytes, hipStream_t st, float* probs, float* mass, hipEvent_t* ev, int nev) {
+        size_t* ws_bytes, hipStream_t st, float* probs, float* mass, hipEvent_t* ev, int nev,
+        const RelaxedRule* rule = nullptr) {
   if (!ws_bytes) return SV_ERR_ARG;
+  if (rule && !(rule->alpha >= 0.f && rule->alpha <= 1e30f && rule->min_prob >= 0.f &&
+                rule->min_prob <= 1.f && rule->max_rank >= 0))
+    return SV_ERR_ARG;
   if (topk >= V) topk = 0;
   Plan pl;
   const int rc = make_plan(B, K, V, topk, dtype, pl);
@@ -1511,6 +1565,10 @@ int run(const void* tgt, const void* dft, const int32_t* tok, const float* uni, 
   a.B = B; a.K = K; a.V = V; a.C = pl.C; a.CS = pl.CS; a.topk = topk;
   a.GA = (2 * K + 1) * pl.C;
   a.cache = pl.cache ? 1 : 0;
+  a.relaxed = rule ? 1 : 0;
+  a.alpha = rule ? rule->alpha : 0.f;
+  a.max_rank = rule ? rule->max_rank : 0;
+  a.min_prob = rule ? rule->min_prob : 0.f;
   a.cand = topk > 0 ? static_cast<void*>(base + pl.off_cand) : nullptr;
   a.ccnt = topk > 0 ? reinterpret_cast<int*>(base + pl.off_ccnt) : nullptr;
   a.qstat = topk > 0 ? reinterpret_cast<float4*>(base + pl.off_qstat) : nullptr;
@@ -1559,6 +1617,17 @@ int spec_verify_timed(const void* target_logits, const void* draft_logits, const
   return run(target_logits, draft_logits, draft_tokens, uniforms, temperature, B, K, V, topk_draft,
              dtype, out_tokens, num_accepted, workspace, workspace_bytes, stream, nullptr, nullptr,
              events, n_events);
+}
+
+int spec_verify_relaxed(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                        const float* uniforms, const float* temperature, int B, int K, int V,
+                        int topk_draft, int dtype, float alpha, int max_rank, float min_prob,
+                        int32_t* out_tokens, int32_t* num_accepted, void* workspace,
+                        size_t* workspace_bytes, hipStream_t stream, float* probs_out, float* mass_out) {
+  const RelaxedRule rule{alpha, max_rank, min_prob};
+  return run(target_logits, draft_logits, draft_tokens, uniforms, temperature, B, K, V, topk_draft,
+             dtype, out_tokens, num_accepted, workspace, workspace_bytes, stream, probs_out, mass_out,
+             nullptr, 0, &rule);
 }
 
 int spec_verify_plan(int B, int K, int V, int topk_draft, int dtype, int* chunks, int* chunk_len) {

@@ -20,7 +20,7 @@ import numpy as np
 import torch
 
 import oracle
-from rejection_sampling_verifier_amd import verify_probe
+from rejection_sampling_verifier_amd import verify_probe, verify_relaxed
 
 ABS_MARGIN = 1e-5
 REL_MARGIN = 1e-4
@@ -41,10 +41,16 @@ def to_device(d, dev="cuda"):
     )
 
 
-def run_gpu(d, dev_inputs=None):
+def run_gpu(d, dev_inputs=None, relaxed: oracle.Relaxed | None = None):
     x = dev_inputs if dev_inputs is not None else to_device(d)
-    out, nacc, probs, mass = verify_probe(x["target"], x["draft"], x["tokens"], x["uniforms"],
-                                          x["temperature"], d["topk"])
+    if relaxed is None:
+        out, nacc, probs, mass = verify_probe(x["target"], x["draft"], x["tokens"], x["uniforms"],
+                                              x["temperature"], d["topk"])
+    else:
+        out, nacc, probs, mass = verify_relaxed(x["target"], x["draft"], x["tokens"], x["uniforms"],
+                                                x["temperature"], d["topk"], alpha=relaxed.alpha,
+                                                max_rank=relaxed.max_rank, min_prob=relaxed.min_prob,
+                                                probes=True)
     torch.cuda.synchronize()
     return out.cpu().numpy(), nacc.cpu().numpy(), probs.cpu().numpy(), mass.cpu().numpy()
 
@@ -73,8 +79,9 @@ def check_well_formed(d, out, nacc, rows=None):
         assert all(out[b, n + 1:] == -1), (b, out[b])
 
 
-def check_rows(d, gpu, rows=None, stats=None):
-    """Compare GPU results with the oracle on `rows`; return the near-boundary count.
+def check_rows(d, gpu, rows=None, stats=None, relaxed: oracle.Relaxed | None = None):
+    """Compare GPU results with the oracle on `rows` (under the relaxed rule
+    when given); return the near-boundary count.
 
     If `stats` is a dict it receives 'near' and 'near_equal' (near-boundary
     rows whose tokens match the oracle anyway)."""
@@ -82,7 +89,7 @@ def check_rows(d, gpu, rows=None, stats=None):
     B = out.shape[0]
     rows = list(range(B)) if rows is None else list(rows)
     ref = oracle.verify(d["target"], d["draft"], d["tokens"], d["uniforms"], d["temperature"],
-                        d["topk"], d["dtype"], rows=rows)
+                        d["topk"], d["dtype"], rows=rows, relaxed=relaxed)
     near = near_equal = 0
     for b, r in zip(rows, ref):
         if not r.greedy:

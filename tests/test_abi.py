@@ -93,3 +93,37 @@ def test_topk_at_or_above_vocab_is_dense():
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(RuntimeError, match="no fallback"):
         B.load_library(str(tmp_path / "absent.so"))
+
+
+def test_relaxed_rule_argument_errors_without_launch():
+    lib = B.load_library()
+    p = ctypes.c_void_p(0x100000)
+    need = B.workspace_bytes(4, 3, 1000, 0, B.SV_BF16)
+    ws = ctypes.c_void_p(0x200000)
+
+    def call(alpha, max_rank, min_prob):
+        n = ctypes.c_size_t(need)
+        return lib.spec_verify_relaxed(p, p, p, p, p, 4, 3, 1000, 0, B.SV_BF16, ctypes.c_float(alpha),
+                                       max_rank, ctypes.c_float(min_prob), p, p, ws, ctypes.byref(n),
+                                       None, None, None)
+
+    assert call(-0.5, 0, 0.0) == B.SV_ERR_ARG
+    assert call(float("nan"), 0, 0.0) == B.SV_ERR_ARG
+    assert call(0.5, -1, 0.0) == B.SV_ERR_ARG
+    assert call(0.5, 10, 1.5) == B.SV_ERR_ARG
+    assert call(0.5, 10, -0.1) == B.SV_ERR_ARG
+    # a valid rule still runs the usual checks first: a short workspace
+    n = ctypes.c_size_t(need - 1)
+    assert lib.spec_verify_relaxed(p, p, p, p, p, 4, 3, 1000, 0, B.SV_BF16, ctypes.c_float(0.5), 10,
+                                   ctypes.c_float(0.1), p, p, ws, ctypes.byref(n), None, None,
+                                   None) == B.SV_ERR_WORKSPACE
+
+
+def test_timed_call_needs_six_events():
+    lib = B.load_library()
+    p = ctypes.c_void_p(0x100000)
+    need = B.workspace_bytes(4, 3, 1000, 0, B.SV_BF16)
+    evs = (ctypes.c_void_p * 6)()
+    n = ctypes.c_size_t(need)
+    assert lib.spec_verify_timed(p, p, p, p, p, 4, 3, 1000, 0, B.SV_BF16, p, p, ctypes.c_void_p(0x200000),
+                                 ctypes.byref(n), None, evs, 5) == B.SV_ERR_ARG
