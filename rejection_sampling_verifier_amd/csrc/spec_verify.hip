@@ -477,15 +477,33 @@ void stats_kernel(Args a) {
   float zl = zj[0];
 #pragma unroll
   for (int j = 1; j < NV_TILE; ++j) zl += zj[j];
-  const float z = block_sum(zl, shf);
+  float z;
   uint32_t above = 0u;
   if (count_rank) {
+    // The count of logits above l(d) shares the sum's block reduction.
+    __shared__ float shn[NWAVE];
     int na = 0;
 #pragma unroll
     for (int j = 0; j < NV_TILE; ++j)
 #pragma unroll
       for (int k = 0; k < VEC; ++k) na += Tr<ET>::at(r[j], k) > lref;  // padding reads as -inf
-    above = (uint32_t)block_sum((float)na, shf);  // exact: counts are below 2^24
+    const float zw = wave_sum(zl), nw = wave_sum((float)na);  // exact: counts are below 2^24
+    if (lane == 0) {
+      shf[wave] = zw;
+      shn[wave] = nw;
+    }
+    __syncthreads();
+    z = shf[0];
+    float nt = shn[0];
+#pragma unroll
+    for (int w = 1; w < NWAVE; ++w) {
+      z += shf[w];
+      nt += shn[w];
+    }
+    __syncthreads();
+    above = (uint32_t)nt;
+  } else {
+    z = block_sum(zl, shf);
   }
   if (slot == a.K) {
     // Sub-block sums of the bonus position: sub-block (j, wave) holds the
