@@ -17,6 +17,8 @@ from .verifier import (  # noqa: F401
     Relaxed,
     RowResult,
     decode_logits,
+    kl_divergence,
+    kl_rows,
     relaxed_gamma,
     target_rank,
     tempered_softmax,

@@ -336,3 +336,39 @@ def verify(target_raw, draft_raw, draft_tokens, uniforms, temperature,
             dl = decode_logits(draft_raw[b], dtype)
         out.append(verify_row(tl, dl, draft_tokens[b], uniforms[b], T, topk, relaxed))
     return out
+
+
+def kl_divergence(target_logits, draft_logits, T: float) -> float:
+    """KL(p || q) = sum_x p(x) log(p(x) / q(x)) of the tempered softmaxes, in
+    nats, in float64.
+
+    The test-time speculation summary on gist.science (paper 2605.09329,
+    section 2) distils the drafter with KL(p || q) between the target's and
+    the drafter's distributions over the verified positions; this is that
+    value, exactly, at one position.  Terms with p(x) = 0 contribute 0; a
+    token with p(x) > 0 and q(x) = 0 makes it +inf.
+    """
+    P = tempered_softmax(target_logits, T)
+    Q = tempered_softmax(draft_logits, T)
+    m = P > 0
+    if np.any(Q[m] == 0):
+        return float("inf")
+    return float(np.sum(P[m] * (np.log(P[m]) - np.log(Q[m]))))
+
+
+def kl_rows(target_raw, draft_raw, temperature, dtype: str, rows=None) -> np.ndarray:
+    """KL(p_i || q_i) for every draft position i of each row: float64 [n, K].
+    Greedy rows (T <= 0) have no sampling distribution: NaN."""
+    B = target_raw.shape[0]
+    K = target_raw.shape[1] - 1
+    rows = range(B) if rows is None else rows
+    out = []
+    for b in rows:
+        T = float(temperature[b])
+        if not (T > 0):
+            out.append(np.full(K, np.nan))
+            continue
+        tl = decode_logits(target_raw[b], dtype)
+        dl = decode_logits(draft_raw[b], dtype)
+        out.append(np.array([kl_divergence(tl[i], dl[i], T) for i in range(K)]))
+    return np.array(out).reshape(len(out), K)

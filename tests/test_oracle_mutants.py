@@ -43,6 +43,10 @@ MUTANTS = {
     "gamma_without_factor_two": ("np.sqrt(2.0 * alpha * p * (1.0 - p))", "np.sqrt(alpha * p * (1.0 - p))"),
     "rank_counts_ties": ("1 + int(np.count_nonzero(logits > logits[tok]))",
                          "1 + int(np.count_nonzero(logits >= logits[tok]))"),
+    "kl_reversed": ("return float(np.sum(P[m] * (np.log(P[m]) - np.log(Q[m]))))",
+                    "return float(np.sum(Q[m] * (np.log(Q[m]) - np.log(P[m]))))"),
+    "kl_without_temperature": ("    P = tempered_softmax(target_logits, T)\n    Q = tempered_softmax(draft_logits, T)",
+                               "    P = tempered_softmax(target_logits, 1.0)\n    Q = tempered_softmax(draft_logits, 1.0)"),
     "guard_ignores_rank": ("if relaxed.max_rank > 0 and ranks[i] > relaxed.max_rank:",
                            "if relaxed.max_rank > 0 and ranks[i] > relaxed.max_rank + 1:"),
 }
@@ -80,6 +84,8 @@ def _run_pins():
         lambda: pins.test_relaxed_acceptance_probability(2.0, 0.5, 0.6, 1.0),
         pins.test_target_rank_brute_force,
         pins.test_support_guard,
+        pins.test_kl_two_token_closed_form,
+        pins.test_kl_properties,
     ]
     failed = 0
     for c in cases:
@@ -100,6 +106,6 @@ def test_pins_catch_mutant(name, monkeypatch):
     for attr in ("verify_row", "tempered_softmax", "topk_keep_mask", "decode_logits"):
         monkeypatch.setattr(pins, attr, getattr(mod, attr))
     # The relaxed-rule pins reach these through the oracle package.
-    for attr in ("Relaxed", "target_rank", "relaxed_gamma"):
+    for attr in ("Relaxed", "target_rank", "relaxed_gamma", "kl_divergence"):
         monkeypatch.setattr(pins.oracle, attr, getattr(mod, attr))
     assert _run_pins() > 0, f"no pin caught the planted mistake {name!r}"

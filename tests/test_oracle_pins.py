@@ -560,3 +560,44 @@ def test_relaxed_rejection_draws_the_lossless_residual():
         b = verify_row(tl, dl, d, u, 1.0, 0, oracle.Relaxed(alpha=0.05))
         if a.n == 0 and b.n == 0:
             assert a.tokens[0] == b.tokens[0] and abs(a.S - b.S) < 1e-15
+
+
+# ---------------------------------------------- KL(p || q) per position
+# gist.science summary of 2605.09329, section 2: the distillation signal is
+# KL(p || q) over the verified positions.
+def test_kl_two_token_closed_form():
+    # p = (1/2, 1/2), q = (1/4, 3/4): KL = 1/2 ln 2 + 1/2 ln(2/3) = 1/2 ln(4/3)
+    T = 1.3
+    tl = _two_token_logits(0.5, T)
+    dl = _two_token_logits(0.25, T)
+    assert abs(oracle.kl_divergence(tl, dl, T) - 0.5 * math.log(4.0 / 3.0)) < 1e-14
+    # p = (0.2, 0.8), q = (0.5, 0.5): 0.2 ln 0.4 + 0.8 ln 1.6
+    tl = _two_token_logits(0.2, T)
+    dl = _two_token_logits(0.5, T)
+    assert abs(oracle.kl_divergence(tl, dl, T) - (0.2 * math.log(0.4) + 0.8 * math.log(1.6))) < 1e-14
+
+
+def test_kl_properties():
+    rng = np.random.default_rng(9)
+    for _ in range(30):
+        l = rng.normal(0, 2, 50)
+        m = l + rng.normal(0, 1, 50)
+        T = float(rng.uniform(0.3, 2.0))
+        assert oracle.kl_divergence(l, l, T) == 0.0
+        kl = oracle.kl_divergence(l, m, T)
+        assert kl > 0
+        # invariant to shifting either set of logits
+        assert abs(oracle.kl_divergence(l + 3.0, m - 2.0, T) - kl) < 1e-12
+        # temperature T on l equals temperature 1 on l / T
+        assert abs(oracle.kl_divergence(l / T, m / T, 1.0) - kl) < 1e-12
+    # a token the draft cannot produce while the target can: +inf
+    assert oracle.kl_divergence([0.0, 0.0], [0.0, -np.inf], 1.0) == float("inf")
+    # the target's zero-probability tokens contribute nothing
+    assert abs(oracle.kl_divergence([0.0, -np.inf], [0.0, 0.0], 1.0) - math.log(2.0)) < 1e-15
+
+
+def test_kl_rows_greedy_rows_are_nan():
+    tr = np.zeros((2, 3, 4), dtype=np.float32)
+    dr = np.zeros((2, 2, 4), dtype=np.float32)
+    out = oracle.kl_rows(tr, dr, np.array([1.0, 0.0]), "f32")
+    assert out.shape == (2, 2) and (out[0] == 0).all() and np.isnan(out[1]).all()
