@@ -119,6 +119,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="also run plain copies of this many MiB (counter calibration)")
+    ap.add_argument("--kl", action="store_true",
+                    help="time spec_verify_kl (verification plus KL(p||q) per position; whole-call "
+                         "rate only)")
     ap.add_argument("--relaxed", default="",
                     help="ALPHA,MAX_RANK,MIN_PROB: time the lossy relaxed acceptance rule instead "
                          "(whole-call rate only; per-kernel times come from a rocprofv3 trace)")
@@ -166,8 +169,14 @@ def main():
         a_, r_, p_ = args.relaxed.split(",")
         rule = dict(alpha=float(a_), max_rank=int(r_), min_prob=float(p_))
 
+    kl_buf = torch.empty((B, K), dtype=torch.float32, device=dev) if args.kl else None
+
     def step(i, timer=None):
         x = sets[i % copies]
+        if args.kl and timer is None:
+            rsv.verify_kl(x["target"], x["draft"], x["tokens"], x["uniforms"], x["temperature"], d["topk"],
+                          out_tokens=out, num_accepted=nacc, kl=kl_buf, workspace=ws, stream=stream.cuda_stream)
+            return
         if rule is not None and timer is None:
             rsv.verify_relaxed(x["target"], x["draft"], x["tokens"], x["uniforms"], x["temperature"],
                                d["topk"], **rule, out_tokens=out, num_accepted=nacc, workspace=ws,
@@ -229,7 +238,8 @@ def main():
         "config": {"workload": case.name, "B": B, "K": K, "V": V, "logits": d["dtype"],
                    "temperature": float(case.temperature), "greedy_rows": case.greedy_rows,
                    "topk_draft": case.topk, "input_copies": copies,
-                   "acceptance": "lossless" if rule is None else f"relaxed {rule}"},
+                   "acceptance": "lossless" if rule is None else f"relaxed {rule}",
+                   "kl_per_position": bool(args.kl)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "kernel": "stats_kernel",

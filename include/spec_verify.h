@@ -167,6 +167,33 @@ int spec_verify_relaxed(const void* target_logits, const void* draft_logits,
                         float* probs_out, float* mass_out);
 
 /*
+ * spec_verify_kl - spec_verify that also returns KL(p_i || q_i), in nats, for
+ * every draft position of each sampling row: the distillation signal that
+ * test-time speculation takes from the verification step (gist.science
+ * summary of paper 2605.09329, section 2: KL between the target's and the
+ * drafter's distributions over the verified positions, with position weights
+ * applied by the caller).  The value is exact up to fp32 rounding:
+ *   KL = E_p[l_t - l_q] / T - ln 2 (fl(M_t s) - fl(M_q s)) - ln Z_t + ln Z_q
+ * with the chunk statistics of the verification pass (s = log2(e) / T).
+ * The statistics pass pairs each draft position with its target position so
+ * that both are read once; tokens and num_accepted equal spec_verify's up to
+ * the rounding of p and q (their decisions use the same partial sums).
+ *
+ * kl_out  [B, K] float32 device: KL(p_i || q_i); NaN for greedy rows (no
+ *         sampling distribution); +inf where the draft gives zero mass to a
+ *         token the target can produce.  Required when K > 0.
+ * A sparse draft (0 < topk_draft < V) is not supported (KL against a
+ * truncated draft is +inf): SV_ERR_UNSUPPORTED.  Other arguments and return
+ * codes as spec_verify.
+ */
+int spec_verify_kl(const void* target_logits, const void* draft_logits,
+                   const int32_t* draft_tokens, const float* uniforms,
+                   const float* temperature, int B, int K, int V,
+                   int topk_draft, int dtype, int32_t* out_tokens,
+                   int32_t* num_accepted, void* workspace,
+                   size_t* workspace_bytes, hipStream_t stream, float* kl_out);
+
+/*
  * spec_verify_timed - spec_verify that also times each of its kernels on the
  * caller's stream, for measurement.
  *

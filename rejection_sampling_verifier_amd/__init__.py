@@ -17,6 +17,7 @@ from .binding import (  # noqa: F401
     new_workspace,
     plan,
     verify,
+    verify_kl,
     verify_probe,
     verify_relaxed,
     workspace_bytes,

@@ -62,6 +62,8 @@ def load_library(path: str | None = None):
                                           ctypes.c_float, _i32, ctypes.c_float, _vp, _vp, _vp, _sz, _vp,
                                           _vp, _vp])
     lib.spec_verify_relaxed.restype = _i32
+    lib.spec_verify_kl.argtypes = _COMMON + [_vp]
+    lib.spec_verify_kl.restype = _i32
     lib.spec_verify_timed.argtypes = _COMMON + [ctypes.POINTER(_vp), _i32]
     lib.spec_verify_timed.restype = _i32
     lib.spec_verify_plan.argtypes = [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32)]
@@ -194,6 +196,20 @@ def verify_relaxed(target, draft, draft_tokens, uniforms, temperature, topk_draf
     if probes:
         return out_tokens, num_accepted, probs, mass
     return out_tokens, num_accepted
+
+
+def verify_kl(target, draft, draft_tokens, uniforms, temperature, topk_draft: int = 0, *,
+              out_tokens=None, num_accepted=None, kl=None, workspace=None, stream=None):
+    """spec_verify_kl: verification plus KL(p_i || q_i) per draft position.
+
+    Returns (out_tokens [B, K+1], num_accepted [B], kl [B, K] float32)."""
+    args, out_tokens, num_accepted, _ = _prepare(target, draft, draft_tokens, uniforms, temperature,
+                                                 topk_draft, out_tokens, num_accepted, workspace, stream)
+    B, Kp1 = out_tokens.shape
+    if kl is None:
+        kl = torch.empty((B, Kp1 - 1), dtype=torch.float32, device=target.device)
+    _check(load_library().spec_verify_kl(*args, _ptr(kl)))
+    return out_tokens, num_accepted, kl
 
 
 class StageTimer:

@@ -103,6 +103,7 @@ struct Args {
   // statistics kernel also counts, per target chunk, the logits above l(d_i).
   int relaxed, max_rank;
   float alpha, min_prob;
+  float* kl;                 // [B, K] KL(p_i || q_i) out (spec_verify_kl: paired statistics), or null
   int GA;                    // statistics work-groups per row: (2K+1) * C
   int cache;                 // 1: finishing work-groups keep the row's words in dynamic LDS
 };
@@ -388,11 +389,7 @@ __device__ void topk_chunk(const u32x4 (&r)[NV_TILE], int lo, int len, int k, ty
 // Kernel A: statistics of one (row, position, chunk).
 // ============================================================================
 template <typename ET, bool ALIGNED>
-__global__ __launch_bounds__(WG)
-#if SV_MAX_WAVES > 0
-__attribute__((amdgpu_waves_per_eu(SV_MAX_WAVES, SV_MAX_WAVES)))
-#endif
-void stats_kernel(Args a) {
+__device__ __forceinline__ void stats_body(const Args& a) {
   constexpr int VEC = Tr<ET>::VEC;
   const int S = 2 * a.K + 1;
   const int c = blockIdx.x % a.C;
@@ -526,6 +523,115 @@ void stats_kernel(Args a) {
     *reinterpret_cast<u32x4*>(dst) = u32x4{__float_as_uint(m), __float_as_uint(z), above, ld};
   }
   (void)S;
+}
+
+template <typename ET, bool ALIGNED>
+__global__ __launch_bounds__(WG)
+#if SV_MAX_WAVES > 0
+__attribute__((amdgpu_waves_per_eu(SV_MAX_WAVES, SV_MAX_WAVES)))
+#endif
+void stats_kernel(Args a) {
+  stats_body<ET, ALIGNED>(a);
+}
+
+// ============================================================================
+// Kernel A' (spec_verify_kl): the statistics pass with the draft position
+// paired to its target position.  The work-group of target position i < K of
+// a sampling row holds both chunks (target and draft) and writes both
+// partials; the draft slot's third word carries
+//   A_c = sum over the chunk of exp2(fma(l_t, s, -fl(m_t,c * s))) * (l_t - l_q),
+// from which the finishing kernel forms KL(p_i || q_i).  Draft work-groups
+// have nothing to do; every other slot runs the usual statistics.
+// ============================================================================
+template <typename ET, bool ALIGNED>
+__global__ __launch_bounds__(WG) void paired_kernel(Args a) {
+  constexpr int VEC = Tr<ET>::VEC;
+  const int S = 2 * a.K + 1;
+  const int c = blockIdx.x % a.C;
+  const int rest = blockIdx.x / a.C;
+  const int slot = rest % S;
+  const int b = rest / S;
+  if (slot > a.K) return;
+  const float T = a.temp[b];
+  if (slot == a.K || !is_sampling_temperature(T)) {
+    stats_body<ET, ALIGNED>(a);
+    return;
+  }
+  const int pos = slot;
+  const int lo = c * a.CS;
+  const int len = min(a.CS, a.V - lo);
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const ET* trow = target_row<ET>(a, b, pos);
+  const ET* drow = draft_row<ET>(a, b, pos);
+  u32x4 rt[NV_TILE], rq[NV_TILE];
+  load_tile<ET, ALIGNED, NV_TILE>(trow, lo, len, rt);
+  load_tile<ET, ALIGNED, NV_TILE>(drow, lo, len, rq);
+  __shared__ float sh[3 * NWAVE];
+  float mt = wave_max(tile_max<ET, NV_TILE>(rt)), mq = wave_max(tile_max<ET, NV_TILE>(rq));
+  if (lane == 0) {
+    sh[wave] = mt;
+    sh[NWAVE + wave] = mq;
+  }
+  __syncthreads();
+  mt = sh[0];
+  mq = sh[NWAVE];
+#pragma unroll
+  for (int w = 1; w < NWAVE; ++w) {
+    mt = fmaxf(mt, sh[w]);
+    mq = fmaxf(mq, sh[NWAVE + w]);
+  }
+  __syncthreads();
+  const float s = LOG2E / T;
+  const float mst = mt == NEG_INF ? 0.f : mul_rn(mt, s);
+  const float msq = mq == NEG_INF ? 0.f : mul_rn(mq, s);
+  // Sums in the same order as the unpaired pass (pairs of elements per
+  // vector, vectors in order, then the block).
+  float zt = 0.f, zq = 0.f, ac = 0.f;
+#pragma unroll
+  for (int j = 0; j < NV_TILE; ++j) {
+    float t0 = 0.f, t1 = 0.f, q0 = 0.f, q1 = 0.f;
+#pragma unroll
+    for (int k = 0; k < VEC; k += 2) {
+      const float la = Tr<ET>::at(rt[j], k), lb = Tr<ET>::at(rt[j], k + 1);
+      const float ea = exp2_fast(fmaf(la, s, -mst)), eb = exp2_fast(fmaf(lb, s, -mst));
+      t0 += ea;
+      t1 += eb;
+      q0 += exp2_fast(fmaf(Tr<ET>::at(rq[j], k), s, -msq));
+      q1 += exp2_fast(fmaf(Tr<ET>::at(rq[j], k + 1), s, -msq));
+      // A token the target cannot produce adds nothing (also when both are -inf).
+      if (ea > 0.f) ac += ea * (la - Tr<ET>::at(rq[j], k));
+      if (eb > 0.f) ac += eb * (lb - Tr<ET>::at(rq[j], k + 1));
+    }
+    zt = j ? zt + (t0 + t1) : t0 + t1;
+    zq = j ? zq + (q0 + q1) : q0 + q1;
+  }
+  zt = wave_sum(zt);
+  zq = wave_sum(zq);
+  ac = wave_sum(ac);
+  if (lane == 0) {
+    sh[wave] = zt;
+    sh[NWAVE + wave] = zq;
+    sh[2 * NWAVE + wave] = ac;
+  }
+  __syncthreads();
+  if (t == 0) {
+    float Zt = sh[0], Zq = sh[NWAVE], A = sh[2 * NWAVE];
+#pragma unroll
+    for (int w = 1; w < NWAVE; ++w) {
+      Zt += sh[w];
+      Zq += sh[NWAVE + w];
+      A += sh[2 * NWAVE + w];
+    }
+    uint32_t ldt = 0u, ldq = 0u;
+    const int d = a.tok[(size_t)b * a.K + pos];
+    if (d >= lo && d < lo + len) {
+      ldt = __float_as_uint(Tr<ET>::load1(trow + d));
+      ldq = __float_as_uint(Tr<ET>::load1(drow + d));
+    }
+    *reinterpret_cast<u32x4*>(part_words(a, b, pos, c)) = u32x4{__float_as_uint(mt), __float_as_uint(Zt), 0u, ldt};
+    *reinterpret_cast<u32x4*>(part_words(a, b, a.K + 1 + pos, c)) =
+        u32x4{__float_as_uint(mq), __float_as_uint(Zq), __float_as_uint(A), ldq};
+  }
 }
 
 // ============================================================================
@@ -1326,6 +1432,26 @@ __global__ __launch_bounds__(WG) void finish_kernel(Args a) {
   RowView<CACHED> view{cache_pw, cache_sub, false};
   decide_row(a, b, rs, view, in);
   const int n = rs.n;
+  if (c == 0 && a.kl && t < K) {
+    // KL(p_t || q_t) = E_p[l_t - l_q] / T - ln2 (fl(M_t s) - fl(M_q s)) - ln Z_t + ln Z_q,
+    // with E_p[l_t - l_q] = sum_c A_c exp2(fl(m_c s) - fl(M_t s)) / Z_t; the
+    // combination is done in double.
+    float kl = __builtin_nanf("");
+    if (!rs.greedy) {
+      const float s = rs.s;
+      const float MSt = mul_rn(rs.M[t], s), MSq = mul_rn(rs.M[K + 1 + t], s);
+      double sa = 0.0;
+      for (int cc = 0; cc < C; ++cc) {
+        const float mc = view_part(a, view, b, t, cc, 0);
+        if (mc != NEG_INF)
+          sa += (double)view_part(a, view, b, K + 1 + t, cc, 2) * (double)exp2_fast(mul_rn(mc, s) - MSt);
+      }
+      const double ln2 = 0.69314718055994530942;
+      const double Zt = rs.Z[t], Zq = rs.Z[K + 1 + t];
+      kl = (float)(sa / Zt * ((double)s * ln2) - ln2 * ((double)MSt - (double)MSq) - log(Zt) + log(Zq));
+    }
+    a.kl[(size_t)b * K + t] = kl;
+  }
   if (c == 0 && a.probs && t < K) {
     a.probs[((size_t)b * K + t) * 2 + 0] = rs.greedy ? 0.f : rs.p[t];
     a.probs[((size_t)b * K + t) * 2 + 1] = rs.greedy ? 0.f : rs.q[t];
@@ -1532,7 +1658,8 @@ int launch(F kernel, int grid, size_t lds, hipStream_t st, hipEvent_t* ev2, cons
 
 template <typename ET, bool AL>
 int launch_typed(const Args& a, size_t lds, size_t merge_lds, hipStream_t st, hipEvent_t* ev) {
-  int rc = launch(stats_kernel<ET, AL>, a.B * a.GA, 0, st, ev, a);
+  int rc = a.kl ? launch(paired_kernel<ET, AL>, a.B * a.GA, 0, st, ev, a)
+                : launch(stats_kernel<ET, AL>, a.B * a.GA, 0, st, ev, a);
   if (rc != SV_OK) return rc;
   if (a.topk > 0 && a.K > 0) {
     rc = launch(merge_kernel<ET>, a.B * a.K, merge_lds, st, ev ? ev + 2 : nullptr, a);
@@ -1554,7 +1681,7 @@ struct RelaxedRule {
 int run(const void* tgt, const void* dft, const int32_t* tok, const float* uni, const float* temp,
         int B, int K, int V, int topk, int dtype, int32_t* out, int32_t* nacc, void* ws,
         size_t* ws_bytes, hipStream_t st, float* probs, float* mass, hipEvent_t* ev, int nev,
-        const RelaxedRule* rule = nullptr) {
+        const RelaxedRule* rule = nullptr, float* kl = nullptr) {
   if (!ws_bytes) return SV_ERR_ARG;
   if (rule && !(rule->alpha >= 0.f && rule->alpha <= 1e30f && rule->min_prob >= 0.f &&
                 rule->min_prob <= 1.f && rule->max_rank >= 0))
@@ -1583,6 +1710,7 @@ int run(const void* tgt, const void* dft, const int32_t* tok, const float* uni, 
   a.B = B; a.K = K; a.V = V; a.C = pl.C; a.CS = pl.CS; a.topk = topk;
   a.GA = (2 * K + 1) * pl.C;
   a.cache = pl.cache ? 1 : 0;
+  a.kl = kl;
   a.relaxed = rule ? 1 : 0;
   a.alpha = rule ? rule->alpha : 0.f;
   a.max_rank = rule ? rule->max_rank : 0;
@@ -1646,6 +1774,17 @@ int spec_verify_relaxed(const void* target_logits, const void* draft_logits, con
   return run(target_logits, draft_logits, draft_tokens, uniforms, temperature, B, K, V, topk_draft,
              dtype, out_tokens, num_accepted, workspace, workspace_bytes, stream, probs_out, mass_out,
              nullptr, 0, &rule);
+}
+
+int spec_verify_kl(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                   const float* uniforms, const float* temperature, int B, int K, int V, int topk_draft,
+                   int dtype, int32_t* out_tokens, int32_t* num_accepted, void* workspace,
+                   size_t* workspace_bytes, hipStream_t stream, float* kl_out) {
+  if (topk_draft > 0 && topk_draft < V) return SV_ERR_UNSUPPORTED;
+  if (workspace && K > 0 && !kl_out) return SV_ERR_ARG;
+  return run(target_logits, draft_logits, draft_tokens, uniforms, temperature, B, K, V, topk_draft,
+             dtype, out_tokens, num_accepted, workspace, workspace_bytes, stream, nullptr, nullptr,
+             nullptr, 0, nullptr, K > 0 ? kl_out : nullptr);
 }
 
 int spec_verify_plan(int B, int K, int V, int topk_draft, int dtype, int* chunks, int* chunk_len) {

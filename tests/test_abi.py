@@ -127,3 +127,17 @@ def test_timed_call_needs_six_events():
     n = ctypes.c_size_t(need)
     assert lib.spec_verify_timed(p, p, p, p, p, 4, 3, 1000, 0, B.SV_BF16, p, p, ctypes.c_void_p(0x200000),
                                  ctypes.byref(n), None, evs, 5) == B.SV_ERR_ARG
+
+
+def test_kl_argument_errors_without_launch():
+    lib = B.load_library()
+    p = ctypes.c_void_p(0x100000)
+    need = B.workspace_bytes(4, 3, 1000, 0, B.SV_BF16)
+
+    def call(topk, kl):
+        n = ctypes.c_size_t(need)
+        return lib.spec_verify_kl(p, p, p, p, p, 4, 3, 1000, topk, B.SV_BF16, p, p, ctypes.c_void_p(0x200000),
+                                  ctypes.byref(n), None, kl)
+
+    assert call(128, p) == B.SV_ERR_UNSUPPORTED      # KL against a truncated draft
+    assert call(0, None) == B.SV_ERR_ARG             # no output for the KL values
