@@ -389,13 +389,9 @@ __device__ void topk_chunk(const u32x4 (&r)[NV_TILE], int lo, int len, int k, ty
 // Kernel A: statistics of one (row, position, chunk).
 // ============================================================================
 template <typename ET, bool ALIGNED>
-__device__ __forceinline__ void stats_body(const Args& a) {
+__device__ __forceinline__ void stats_body(const Args& a, int b, int slot, int c) {
   constexpr int VEC = Tr<ET>::VEC;
   const int S = 2 * a.K + 1;
-  const int c = blockIdx.x % a.C;
-  const int rest = blockIdx.x / a.C;
-  const int slot = rest % S;
-  const int b = rest / S;
   const bool is_draft = slot > a.K;
   const int pos = is_draft ? slot - a.K - 1 : slot;
   const ET* row = is_draft ? draft_row<ET>(a, b, pos) : target_row<ET>(a, b, pos);
@@ -531,7 +527,9 @@ __global__ __launch_bounds__(WG)
 __attribute__((amdgpu_waves_per_eu(SV_MAX_WAVES, SV_MAX_WAVES)))
 #endif
 void stats_kernel(Args a) {
-  stats_body<ET, ALIGNED>(a);
+  const int S = 2 * a.K + 1;
+  const int rest = blockIdx.x / a.C;
+  stats_body<ET, ALIGNED>(a, rest / S, rest % S, blockIdx.x % a.C);
 }
 
 // ============================================================================
@@ -540,21 +538,20 @@ void stats_kernel(Args a) {
 // a sampling row holds both chunks (target and draft) and writes both
 // partials; the draft slot's third word carries
 //   A_c = sum over the chunk of exp2(fma(l_t, s, -fl(m_t,c * s))) * (l_t - l_q),
-// from which the finishing kernel forms KL(p_i || q_i).  Draft work-groups
-// have nothing to do; every other slot runs the usual statistics.
+// from which the finishing kernel forms KL(p_i || q_i).  The grid covers the
+// K+1 target slots only; the bonus slot and greedy rows run the usual
+// statistics (greedy rows never read the draft).
 // ============================================================================
 template <typename ET, bool ALIGNED>
 __global__ __launch_bounds__(WG) void paired_kernel(Args a) {
   constexpr int VEC = Tr<ET>::VEC;
-  const int S = 2 * a.K + 1;
   const int c = blockIdx.x % a.C;
   const int rest = blockIdx.x / a.C;
-  const int slot = rest % S;
-  const int b = rest / S;
-  if (slot > a.K) return;
+  const int slot = rest % (a.K + 1);
+  const int b = rest / (a.K + 1);
   const float T = a.temp[b];
   if (slot == a.K || !is_sampling_temperature(T)) {
-    stats_body<ET, ALIGNED>(a);
+    stats_body<ET, ALIGNED>(a, b, slot, c);
     return;
   }
   const int pos = slot;
@@ -1658,7 +1655,7 @@ int launch(F kernel, int grid, size_t lds, hipStream_t st, hipEvent_t* ev2, cons
 
 template <typename ET, bool AL>
 int launch_typed(const Args& a, size_t lds, size_t merge_lds, hipStream_t st, hipEvent_t* ev) {
-  int rc = a.kl ? launch(paired_kernel<ET, AL>, a.B * a.GA, 0, st, ev, a)
+  int rc = a.kl ? launch(paired_kernel<ET, AL>, a.B * (a.K + 1) * a.C, 0, st, ev, a)
                 : launch(stats_kernel<ET, AL>, a.B * a.GA, 0, st, ev, a);
   if (rc != SV_OK) return rc;
   if (a.topk > 0 && a.K > 0) {
