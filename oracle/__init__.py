@@ -16,6 +16,7 @@ from .verifier import (  # noqa: F401
     F32,
     Relaxed,
     RowResult,
+    TreeResult,
     decode_logits,
     kl_divergence,
     kl_rows,
@@ -25,4 +26,7 @@ from .verifier import (  # noqa: F401
     topk_keep_mask,
     verify_row,
     verify,
+    tree_children,
+    verify_tree,
+    verify_tree_row,
 )

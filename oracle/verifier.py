@@ -372,3 +372,161 @@ def kl_rows(target_raw, draft_raw, temperature, dtype: str, rows=None) -> np.nda
         dl = decode_logits(draft_raw[b], dtype)
         out.append(np.array([kl_divergence(tl[i], dl[i], T) for i in range(K)]))
     return np.array(out).reshape(len(out), K)
+
+
+# ---------------------------------------------------------------------------
+# Tree verification ([RheoSampling] section 4, RheoVerification).
+# ---------------------------------------------------------------------------
+@dataclass
+class TreeResult:
+    """Outcome of verifying one row's draft tree.
+
+    path        accepted node ids, root-to-leaf order (node 0, the root, is
+                not listed).
+    tokens      int64 [N]: the accepted nodes' tokens, then the final token,
+                then -1.
+    n           len(path).
+    greedy      True for a greedy row (T <= 0).
+    final_w     float64 [V]: the normalised distribution the final token was
+                drawn from (None for greedy rows).
+    S           its mass before normalisation (1 for a bonus draw at a leaf).
+    gap         distance of t = u_0 * S to the nearer edge of the drawn
+                token's CDF interval (inf for greedy rows).
+    fallback    True when a residual of mass 0 fell back to the node's target.
+    tested      [(node, p(d), q(d), r(d), threshold)] for every sibling
+                tested, in order; threshold = r(d) / q(d) (inf when q(d) = 0).
+    margins     |u_node * q(d) - r(d)| for each tested node, in order.
+    """
+
+    path: list
+    tokens: np.ndarray
+    n: int
+    greedy: bool
+    final_w: np.ndarray
+    S: float
+    gap: float
+    fallback: bool
+    tested: list
+    margins: list
+
+    def min_margin(self) -> float:
+        if self.greedy:
+            return float("inf")
+        return min(min(self.margins, default=float("inf")), self.gap)
+
+
+def tree_children(parent, N: int) -> list:
+    """children[v]: nodes c in 1..N-1 with parent[c] == v, ascending (the
+    order in which siblings are tested).  A parent outside [0, c) makes c
+    unreachable."""
+    ch = [[] for _ in range(N)]
+    for c in range(1, N):
+        p = int(parent[c])
+        if 0 <= p < c:
+            ch[p].append(c)
+    return ch
+
+
+def verify_tree_row(tl, dl, tok, parent, u, T: float, k: int = 0) -> TreeResult:
+    """Verify one row's draft tree against the target.
+
+    tl      float64 [N, V]: target logits at each node (the next-token
+            distribution after the path to that node; node 0 is the root).
+    dl      float64 [N, V]: draft logits at each node (the distribution the
+            node's children were drawn from); read for nodes with children.
+    tok     int [N]: token of each node (entry 0 unused).
+    parent  int [N]: parent of each node (< the node; entry 0 unused).
+    u       float [N]: u[c] drives the test of node c; u[0] the final draw.
+    T       temperature; T <= 0 selects greedy verification.
+    k       sparse draft truncation at every node (0 = none).
+
+    Reading (the pages leave the sibling draw open): siblings are independent
+    draws from the drafter's distribution at their parent, tested in id order.
+    The first sibling is accepted with probability min(1, p/q) at its token;
+    after a rejection the target is replaced by the residual r = norm(max(0,
+    r - q)) and the next sibling is tested against r with min(1, r/q); an
+    accepted node is descended into.  With r_0 = p, every residual is
+    r_j = max(0, p - c_j q) / W_j with c_0 = 0, W_0 = 1, c_{j+1} = c_j + W_j
+    and W_j = sum_x max(0, p - c_j q).  When every child is rejected the final
+    token is drawn from the last residual; at a leaf it is drawn from the
+    leaf's target (the bonus token).
+    """
+    tl = np.asarray(tl, dtype=np.float64)
+    N, V = tl.shape
+    tok = np.asarray(tok, dtype=np.int64).reshape(N)
+    u = np.asarray(u, dtype=np.float64).reshape(N)
+    ch = tree_children(parent, N)
+    tokens = np.full(N, -1, dtype=np.int64)
+    path = []
+    if not (T > 0):
+        # Greedy: descend into the first child (in id order) equal to the
+        # node's target argmax; when none is, emit the argmax.
+        v = 0
+        while True:
+            a = int(np.argmax(tl[v]))
+            nxt = next((c for c in ch[v] if int(tok[c]) == a), None)
+            if nxt is None:
+                break
+            path.append(nxt)
+            v = nxt
+        tokens[: len(path)] = [int(tok[c]) for c in path]
+        tokens[len(path)] = int(np.argmax(tl[v]))
+        return TreeResult(path, tokens, len(path), True, None, float("nan"), float("inf"), False, [], [])
+    dl = np.asarray(dl, dtype=np.float64).reshape(N, V)
+    tested, margins = [], []
+    fallback = False
+    v = 0
+    while True:
+        P = tempered_softmax(tl[v], T)
+        if not ch[v]:
+            w, S = P, 1.0      # leaf: bonus token from the target
+            break
+        keep = topk_keep_mask(dl[v], k)
+        Q = tempered_softmax(np.where(keep, dl[v], -np.inf), T)
+        c, W = 0.0, 1.0
+        accepted = None
+        for child in ch[v]:
+            d = int(tok[child])
+            pd, qd = (P[d], Q[d]) if 0 <= d < V else (0.0, 0.0)
+            rd = max(0.0, pd - c * qd) / W
+            tested.append((child, pd, qd, rd, rd / qd if qd > 0 else float("inf")))
+            margins.append(abs(u[child] * qd - rd))
+            if u[child] * qd < rd:
+                accepted = child
+                break
+            c = c + W
+            W = float(np.sum(np.maximum(0.0, P - c * Q)))
+            if W == 0.0:          # only through rounding (c4)
+                break
+        if accepted is not None:
+            path.append(accepted)
+            v = accepted
+            continue
+        if W == 0.0:
+            w, S, fallback = P, 1.0, True
+        else:
+            w, S = np.maximum(0.0, P - c * Q), W
+        break
+    t = u[0] * S
+    C = np.cumsum(w)
+    hits = np.flatnonzero(C > t)      # first token whose cumulative weight exceeds t (c3)
+    x = int(hits[0]) if hits.size else int(np.flatnonzero(w > 0)[-1])
+    lo = C[x - 1] if x > 0 else 0.0
+    gap = float(min(t - lo, C[x] - t))
+    tokens[: len(path)] = [int(tok[c]) for c in path]
+    tokens[len(path)] = x
+    return TreeResult(path, tokens, len(path), False, w / np.sum(w), float(S), gap, fallback, tested, margins)
+
+
+def verify_tree(target_raw, draft_raw, tokens, parents, uniforms, temperature, topk: int, dtype: str,
+                rows=None) -> list:
+    """verify_tree_row over a batch: target_raw / draft_raw [B, N, V] stored
+    logits, tokens / parents int [B, N], uniforms [B, N], temperature [B]."""
+    B = target_raw.shape[0]
+    out = []
+    for b in (range(B) if rows is None else rows):
+        T = float(temperature[b])
+        tl = decode_logits(target_raw[b], dtype)
+        dl = decode_logits(draft_raw[b], dtype) if T > 0 else None
+        out.append(verify_tree_row(tl, dl, tokens[b], parents[b], uniforms[b], T, topk))
+    return out

@@ -7,7 +7,9 @@ a wrong oracle: a flipped residual sign, a reused uniform, a shifted slot
 index, a transposed acceptance ratio, a dropped temperature, an off-by-one
 top-k, a non-strict inverse CDF, a wrong greedy replacement, or in the relaxed
 rule a dropped factor in gamma, a rank that counts ties or an off-by-one
-rank guard.
+rank guard, and in the tree walk a reset residual scale, siblings tested
+against the target instead of the residual, a final draw from the target or a
+greedy walk that ignores the argmax.
 """
 
 from __future__ import annotations
@@ -47,6 +49,11 @@ MUTANTS = {
                     "return float(np.sum(Q[m] * (np.log(Q[m]) - np.log(P[m]))))"),
     "kl_without_temperature": ("    P = tempered_softmax(target_logits, T)\n    Q = tempered_softmax(draft_logits, T)",
                                "    P = tempered_softmax(target_logits, 1.0)\n    Q = tempered_softmax(draft_logits, 1.0)"),
+    "tree_scale_reset": ("            c = c + W\n", "            c = W\n"),
+    "tree_siblings_against_target": ("            rd = max(0.0, pd - c * qd) / W\n", "            rd = pd\n"),
+    "tree_final_from_target": ("            w, S = np.maximum(0.0, P - c * Q), W\n", "            w, S = P, 1.0\n"),
+    "tree_descends_first_child": ("            nxt = next((c for c in ch[v] if int(tok[c]) == a), None)",
+                                  "            nxt = ch[v][0] if ch[v] else None"),
     "guard_ignores_rank": ("if relaxed.max_rank > 0 and ranks[i] > relaxed.max_rank:",
                            "if relaxed.max_rank > 0 and ranks[i] > relaxed.max_rank + 1:"),
 }
@@ -86,6 +93,9 @@ def _run_pins():
         pins.test_support_guard,
         pins.test_kl_two_token_closed_form,
         pins.test_kl_properties,
+        lambda: pins.test_tree_lossless_enumeration("fan2", 4, 1.0, 0, 41),
+        lambda: pins.test_tree_lossless_enumeration("binary2", 4, 1.2, 0, 43),
+        pins.test_tree_greedy_is_greedy_decode,
     ]
     failed = 0
     for c in cases:
@@ -106,6 +116,7 @@ def test_pins_catch_mutant(name, monkeypatch):
     for attr in ("verify_row", "tempered_softmax", "topk_keep_mask", "decode_logits"):
         monkeypatch.setattr(pins, attr, getattr(mod, attr))
     # The relaxed-rule pins reach these through the oracle package.
-    for attr in ("Relaxed", "target_rank", "relaxed_gamma", "kl_divergence"):
+    for attr in ("Relaxed", "target_rank", "relaxed_gamma", "kl_divergence", "verify_tree_row",
+                 "tree_children"):
         monkeypatch.setattr(pins.oracle, attr, getattr(mod, attr))
     assert _run_pins() > 0, f"no pin caught the planted mistake {name!r}"

@@ -601,3 +601,149 @@ def test_kl_rows_greedy_rows_are_nan():
     dr = np.zeros((2, 2, 4), dtype=np.float32)
     out = oracle.kl_rows(tr, dr, np.array([1.0, 0.0]), "f32")
     assert out.shape == (2, 2) and (out[0] == 0).all() and np.isnan(out[1]).all()
+
+
+# ------------------------------------------------------ tree verification
+# [RheoSampling] section 4 (RheoVerification): siblings tested in turn, each
+# rejection replacing the target by the residual norm(max(0, r - q)); an
+# accepted node is descended into.  Section 6 (Theorem 1): lossless.
+TREES = {
+    "fan2": [-1, 0, 0],                      # root with two children
+    "fan3-deep": [-1, 0, 0, 0, 1, 3],        # three children; two of them have a child
+    "binary2": [-1, 0, 0, 1, 1],             # root -> 2 children, the first has 2 children
+    "chain3": [-1, 0, 1, 2],                 # a chain: the linear verifier
+}
+
+
+def _depths(parent):
+    dep = [0] * len(parent)
+    for c in range(1, len(parent)):
+        dep[c] = dep[parent[c]] + 1
+    return dep
+
+
+def _prefix(parent, tok, v):
+    out = []
+    while v > 0:
+        out.append(int(tok[v]))
+        v = parent[v]
+    return tuple(reversed(out))
+
+
+def enumerate_tree_verifier(model, parent):
+    """Exact output distribution of the tree oracle over draft trees (each
+    node's token drawn independently from the draft at its parent) and the
+    uniforms (a depth-first split of each tested node's uniform at its
+    acceptance threshold; the final draw is credited with final_w)."""
+    N, V = len(parent), model.V
+    dist = defaultdict(float)
+    for toks in itertools.product(range(V), repeat=N - 1):
+        tok = (0,) + toks
+        wt = 1.0
+        for c in range(1, N):
+            wt *= model.q(_prefix(parent, tok, parent[c]))[tok[c]]
+        if wt == 0.0:
+            continue
+        tl = np.stack([model.lp[_prefix(parent, tok, v)] for v in range(N)])
+        dl = np.stack([model.lq[_prefix(parent, tok, v)] for v in range(N)])
+
+        def explore(fixed, meas):
+            u = np.full(N, 0.5)
+            for node, val in fixed.items():
+                u[node] = val
+            r = oracle.verify_tree_row(tl, dl, tok, parent, u, model.T, model.k)
+            nxt = next(((node, thr) for node, _, _, _, thr in r.tested if node not in fixed), None)
+            if nxt is None:
+                for x in range(V):
+                    if r.final_w[x] > 0:
+                        out = tuple(int(t) for t in r.tokens[: r.n]) + (x,)
+                        dist[out] += wt * meas * r.final_w[x]
+                return
+            node, thr = nxt
+            a = min(1.0, thr)
+            if a > 0:
+                explore({**fixed, node: a / 2.0}, meas * a)
+            if a < 1:
+                explore({**fixed, node: (1.0 + a) / 2.0}, meas * (1.0 - a))
+
+        explore({}, 1.0)
+    return dist
+
+
+@pytest.mark.parametrize("tree,V,T,k,seed", [
+    ("fan2", 4, 1.0, 0, 41),
+    ("fan3-deep", 4, 0.8, 0, 42),
+    ("binary2", 4, 1.2, 0, 43),
+    ("binary2", 5, 1.0, 3, 44),     # sparse draft at every node
+    ("chain3", 3, 0.9, 0, 45),
+])
+def test_tree_lossless_enumeration(tree, V, T, k, seed):
+    parent = TREES[tree]
+    model = ToyModel(V, max(_depths(parent)), T, k, seed)
+    dist = enumerate_tree_verifier(model, parent)
+    assert abs(sum(dist.values()) - 1.0) < 1e-12
+    check_lossless(model, dist)
+
+
+def test_tree_chain_equals_linear_verifier():
+    rng = np.random.default_rng(46)
+    for trial in range(40):
+        K, V = 4, 12
+        tl = rng.normal(0, 2, (K + 1, V))
+        dl = tl + rng.normal(0, 1, (K + 1, V))
+        d = rng.integers(0, V, K)
+        u_lin = rng.random(K + 1)
+        parent = [-1] + list(range(K))
+        tok = np.concatenate([[0], d])
+        u_tree = np.concatenate([[u_lin[K]], u_lin[:K]])
+        T = [0.8, 0.0][trial % 2]
+        a = oracle.verify_row(tl, dl[:K], d, u_lin, T)
+        b = oracle.verify_tree_row(tl, dl, tok, parent, u_tree, T)
+        assert a.n == b.n and list(a.tokens) == list(b.tokens)
+        if T > 0:
+            assert abs(a.S - b.S) < 1e-15
+
+
+def test_tree_greedy_is_greedy_decode():
+    model = ToyModel(4, 2, 1.0, 0, 47)
+    parent = TREES["binary2"]
+    for toks in itertools.product(range(4), repeat=4):
+        tok = (0,) + toks
+        tl = np.stack([model.lp[_prefix(parent, tok, v)] for v in range(5)])
+        r = oracle.verify_tree_row(tl, None, tok, parent, np.full(5, 0.5), 0.0)
+        # brute force: the greedy decode of the toy target, and the longest
+        # prefix of it that is a path of the tree (first matching child)
+        s = ()
+        for _ in range(3):
+            s = s + (int(np.argmax(model.lp[s])),)
+        v, n = 0, 0
+        for depth in range(2):
+            nxt = [c for c in range(1, 5) if parent[c] == v and tok[c] == s[depth]]
+            if not nxt:
+                break
+            v, n = nxt[0], n + 1
+        assert r.n == n and list(r.tokens[: n + 1]) == list(s[: n + 1])
+
+
+def test_tree_residual_recursion_closed_form():
+    """r_{j+1} = norm(max(0, r_j - q)) equals max(0, p - c_{j+1} q) / W_{j+1}
+    with c_{j+1} = c_j + W_j: the tree oracle's second-sibling test uses it."""
+    rng = np.random.default_rng(48)
+    p = softmax_T(rng.normal(0, 2, 9), 1.0)
+    q = softmax_T(rng.normal(0, 2, 9), 1.0)
+    r, c, W = p.copy(), 0.0, 1.0
+    for _ in range(4):
+        nxt = np.maximum(0.0, r - q)
+        if nxt.sum() == 0:
+            break
+        r = nxt / nxt.sum()
+        c = c + W
+        W = np.maximum(0.0, p - c * q).sum()
+        assert np.allclose(r, np.maximum(0.0, p - c * q) / W, atol=1e-14)
+    # and the oracle tests the second sibling against r_1 = norm(max(0, p - q))
+    tl = np.stack([np.log(p), np.zeros(9), np.zeros(9)])
+    dl = np.stack([np.log(q), np.zeros(9), np.zeros(9)])
+    x = int(np.argmax(np.maximum(0.0, p - q)))
+    res = oracle.verify_tree_row(tl, dl, [0, int(np.argmax(q - p)), x], [-1, 0, 0], [0.5, 0.999999, 0.3], 1.0)
+    r1 = np.maximum(0.0, p - q) / np.maximum(0.0, p - q).sum()
+    assert res.tested[1][0] == 2 and abs(res.tested[1][3] - r1[x]) < 1e-14
