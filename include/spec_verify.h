@@ -32,9 +32,9 @@
  * All pointers are device pointers owned by the caller.  Inputs are read
  * only; outputs are fully overwritten.  The library allocates nothing, keeps
  * no mutable global state and never synchronises: every call only enqueues
- * two kernels on `stream` (three with a sparse draft); outputs are valid once
- * the caller has synchronised that stream.  Calls on different workspaces
- * are reentrant.
+ * kernels on `stream` (two, three with a sparse draft; 1 + rounds for
+ * spec_verify_tree); outputs are valid once the caller has synchronised that
+ * stream.  Calls on different workspaces are reentrant.
  */
 #ifndef SPEC_VERIFY_H
 #define SPEC_VERIFY_H
@@ -62,6 +62,7 @@ typedef enum {
 
 #define SV_MAX_TOPK 1024
 #define SV_MAX_K 64
+#define SV_MAX_NODES 64
 
 /*
  * spec_verify - verify B rows; see the description at the top of this file.
@@ -192,6 +193,91 @@ int spec_verify_kl(const void* target_logits, const void* draft_logits,
                    int topk_draft, int dtype, int32_t* out_tokens,
                    int32_t* num_accepted, void* workspace,
                    size_t* workspace_bytes, hipStream_t stream, float* kl_out);
+
+/*
+ * spec_verify_tree - verify B rows of draft trees against one target pass
+ * (RheoSampling 2026, section 4, RheoVerification: sibling candidates are
+ * tested one after the other; an accepted candidate is descended into; after
+ * a rejection the next sibling is tested against the residual
+ * norm(max(0, r - q~)); when every candidate is rejected the final token is
+ * drawn from the last residual).
+ *
+ * A row's tree has N nodes; node 0 is the root (the committed prefix) and
+ * every other node c is a candidate token tok[c] drawn, independently of its
+ * siblings, from the drafter's distribution at its parent par[c] < c.
+ * Children are tested in increasing node index.  With r_0 = p_v at node v,
+ * the j-th tested child (0-based) is accepted when u[c] * q_v(d) < r_j(d),
+ * where r_j = max(0, p_v - c_j q_v) / W_j, c_0 = 0, W_0 = 1,
+ * c_{j+1} = c_j + W_j, W_j = sum_x max(0, p_v(x) - c_j q_v(x)).  A rejection
+ * therefore costs one pass over node v's target and draft logits (for the
+ * next W).  A leaf reached by acceptance emits a bonus token drawn from its
+ * target p_leaf.  Greedy rows (T <= 0) descend into the first child whose
+ * token equals the node's target argmax and emit the argmax where none does.
+ * Every draw is the inverse CDF of spec_verify with uniform u[b][0].  A chain
+ * (par[c] = c - 1) gives exactly spec_verify's result with K = N - 1,
+ * draft_tokens[i] = tok[i+1] and uniforms (u[1..N-1], u[0]).
+ *
+ * target_logits  [B, N, V] device, dtype: the target's next-token logits at
+ *                each node (after the path root..node).
+ * draft_logits   [B, N, V] device, dtype: the drafter's logits at each node;
+ *                read only for nodes with children (other rows may hold any
+ *                values) and never for greedy rows.
+ * node_tokens    [B, N] int32 device; entry 0 is not read.  A token outside
+ *                [0, V) has p = q = 0 and is rejected.
+ * parents        [B, N] int32 device; entry 0 is not read.  par[c] must be
+ *                < c; a node whose parent is not an earlier node is never
+ *                reached.
+ * uniforms       [B, N] float32 device in [0, 1): u[c] tests node c, u[0]
+ *                drives the final draw.
+ * temperature    [B] float32 device; T <= 0 (or NaN) selects greedy.
+ * B >= 1, N in [1, SV_MAX_NODES], V >= 1.
+ * topk_draft     0 or >= V (dense draft); a sparse draft is SV_ERR_UNSUPPORTED.
+ * rounds         >= 1: launches of the walking kernel.  Each launch performs
+ *                at most one residual pass per row with all of the row's
+ *                vocabulary chunks in parallel; a row that needs more passes
+ *                than `rounds` completes the rest in the last launch with
+ *                one work-group (same result, slower).
+ * out_tokens     [B, N] int32 device: the tokens of the accepted nodes in
+ *                path order, then the final token, then -1.
+ * out_nodes      [B, N] int32 device: the accepted node indices in path
+ *                order, then -1.
+ * num_accepted   [B] int32 device: accepted nodes (-1 if a wait for another
+ *                work-group's results timed out, which a correct launch
+ *                never does).
+ * workspace, workspace_bytes, stream as spec_verify (the size depends on
+ *                B, N, V and dtype).
+ * probs_out      [B, N, 3] float32 device or NULL: (p_v(d), q_v(d), r_j(d))
+ *                of every tested node, NaN for nodes not tested.
+ * mass_out       [B] float32 device or NULL: total weight of the final
+ *                draw's distribution (W for a residual, ~1 for a target), 0
+ *                for greedy rows.
+ * Every call enqueues 1 + rounds kernels.  SV_ERR_UNSUPPORTED also when the
+ * row's chunk statistics (2 N C 16 bytes) do not fit the walking kernel's
+ * LDS.
+ */
+int spec_verify_tree(const void* target_logits, const void* draft_logits,
+                     const int32_t* node_tokens, const int32_t* parents,
+                     const float* uniforms, const float* temperature, int B,
+                     int N, int V, int topk_draft, int dtype, int rounds,
+                     int32_t* out_tokens, int32_t* out_nodes,
+                     int32_t* num_accepted, void* workspace,
+                     size_t* workspace_bytes, hipStream_t stream,
+                     float* probs_out, float* mass_out);
+
+/*
+ * spec_verify_tree_timed - spec_verify_tree (without probes) that also times
+ * its kernels: events[0] / events[1] take the start / end of the statistics
+ * kernel's dispatch, events[2] / events[3] the start of the first and the end
+ * of the last walking kernel.  n_events must be 4.
+ */
+int spec_verify_tree_timed(const void* target_logits, const void* draft_logits,
+                           const int32_t* node_tokens, const int32_t* parents,
+                           const float* uniforms, const float* temperature,
+                           int B, int N, int V, int topk_draft, int dtype,
+                           int rounds, int32_t* out_tokens, int32_t* out_nodes,
+                           int32_t* num_accepted, void* workspace,
+                           size_t* workspace_bytes, hipStream_t stream,
+                           hipEvent_t* events, int n_events);
 
 /*
  * spec_verify_timed - spec_verify that also times each of its kernels on the

@@ -10,15 +10,20 @@ from .binding import (  # noqa: F401
     SV_BF16,
     SV_F32,
     SV_MAX_K,
+    SV_MAX_NODES,
     SV_MAX_TOPK,
     SpecVerifyError,
     StageTimer,
+    TreeTimer,
     load_library,
+    new_tree_workspace,
     new_workspace,
     plan,
+    tree_workspace_bytes,
     verify,
     verify_kl,
     verify_probe,
     verify_relaxed,
+    verify_tree,
     workspace_bytes,
 )

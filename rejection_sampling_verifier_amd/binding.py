@@ -30,6 +30,7 @@ def _header_define(name: str) -> int:
 
 SV_MAX_TOPK = _header_define("SV_MAX_TOPK")
 SV_MAX_K = _header_define("SV_MAX_K")
+SV_MAX_NODES = _header_define("SV_MAX_NODES")
 
 
 class SpecVerifyError(RuntimeError):
@@ -66,6 +67,11 @@ def load_library(path: str | None = None):
     lib.spec_verify_kl.restype = _i32
     lib.spec_verify_timed.argtypes = _COMMON + [ctypes.POINTER(_vp), _i32]
     lib.spec_verify_timed.restype = _i32
+    _tree = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]
+    lib.spec_verify_tree.argtypes = _tree + [_vp, _vp]
+    lib.spec_verify_tree.restype = _i32
+    lib.spec_verify_tree_timed.argtypes = _tree + [ctypes.POINTER(_vp), _i32]
+    lib.spec_verify_tree_timed.restype = _i32
     lib.spec_verify_plan.argtypes = [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32)]
     lib.spec_verify_plan.restype = _i32
     lib.spec_verify_status_string.argtypes = [_i32]
@@ -212,37 +218,96 @@ def verify_kl(target, draft, draft_tokens, uniforms, temperature, topk_draft: in
     return out_tokens, num_accepted, kl
 
 
-class StageTimer:
-    """Six HIP events taken by spec_verify_timed: the start and end of each of
-    its kernels (statistics, sparse-draft merge, finishing), from the
-    dispatches' own timestamps.
+def tree_workspace_bytes(B: int, N: int, V: int, dtype: int = SV_BF16, rounds: int = 1) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().spec_verify_tree(None, None, None, None, None, None, B, N, V, 0, dtype, rounds,
+                                           None, None, None, None, ctypes.byref(n), None, None, None))
+    return n.value
 
-    ``run(...)`` enqueues one verification; ``stage_ms()`` (after the stream is
-    synchronised) returns each kernel's duration in milliseconds:
-    [statistics, top-k merge (0 without a sparse draft), finishing].
+
+def new_tree_workspace(B: int, N: int, V: int, dtype: int = SV_BF16, device="cuda"):
+    """A zero-filled workspace for spec_verify_tree at this shape."""
+    n = tree_workspace_bytes(B, N, V, dtype)
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def _prepare_tree(target, draft, node_tokens, parents, uniforms, temperature, topk_draft, rounds,
+                  out_tokens, out_nodes, num_accepted, workspace, stream):
+    if target.dim() != 3:
+        raise ValueError("target_logits must be [B, N, V]")
+    B, N, V = target.shape
+    dev = target.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    dt = _dtype_code(target)
+    tensors = [("target_logits", target, (B, N, V), target.dtype),
+               ("uniforms", uniforms, (B, N), torch.float32),
+               ("temperature", temperature, (B,), torch.float32)]
+    if N > 1:
+        tensors += [("draft_logits", draft, (B, N, V), target.dtype),
+                    ("node_tokens", node_tokens, (B, N), torch.int32),
+                    ("parents", parents, (B, N), torch.int32)]
+    for name, t, shape, dtype in tensors:
+        if t is None or tuple(t.shape) != shape or t.dtype != dtype or t.device != dev or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {shape} on {dev}")
+    if out_tokens is None:
+        out_tokens = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if out_nodes is None:
+        out_nodes = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if num_accepted is None:
+        num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = new_tree_workspace(B, N, V, dt, dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    ws_n = ctypes.c_size_t(workspace.numel() * workspace.element_size())
+    many = N > 1
+    args = [_ptr(target), _ptr(draft) if many else None, _ptr(node_tokens) if many else None,
+            _ptr(parents) if many else None, _ptr(uniforms), _ptr(temperature), B, N, V, topk_draft, dt,
+            int(rounds), _ptr(out_tokens), _ptr(out_nodes), _ptr(num_accepted), _ptr(workspace),
+            ctypes.byref(ws_n), ctypes.c_void_p(stream)]
+    # The caller holds `keep` until the call has been enqueued: a workspace
+    # created here must not return to torch's allocator before that.
+    keep = (target, draft, node_tokens, parents, uniforms, temperature, workspace)
+    return args, out_tokens, out_nodes, num_accepted, keep
+
+
+def verify_tree(target, draft, node_tokens, parents, uniforms, temperature, topk_draft: int = 0, *,
+                rounds: int = 4, probes: bool = False, out_tokens=None, out_nodes=None, num_accepted=None,
+                workspace=None, stream=None):
+    """spec_verify_tree: verify one draft tree per row (see the header).
+
+    Returns (out_tokens [B, N], out_nodes [B, N], num_accepted [B]), plus
+    (probs [B, N, 3], mass [B]) when ``probes`` is set.
     """
+    args, out_tokens, out_nodes, num_accepted, keep = _prepare_tree(
+        target, draft, node_tokens, parents, uniforms, temperature, topk_draft, rounds, out_tokens, out_nodes,
+        num_accepted, workspace, stream)
+    probs = mass = None
+    if probes:
+        B, N = out_tokens.shape
+        probs = torch.empty((B, N, 3), dtype=torch.float32, device=target.device)
+        mass = torch.empty((B,), dtype=torch.float32, device=target.device)
+    _check(load_library().spec_verify_tree(*args, _ptr(probs), _ptr(mass)))
+    del keep
+    if probes:
+        return out_tokens, out_nodes, num_accepted, probs, mass
+    return out_tokens, out_nodes, num_accepted
 
-    N = 6
 
-    def __init__(self):
+class _Events:
+    def __init__(self, n: int):
+        self.N = n
         self.hip = ctypes.CDLL("libamdhip64.so")
         self.hip.hipEventCreate.argtypes = [ctypes.POINTER(_vp)]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), _vp, _vp]
         self.hip.hipEventDestroy.argtypes = [_vp]
-        self.events = (_vp * self.N)()
-        for i in range(self.N):
+        self.events = (_vp * n)()
+        for i in range(n):
             ev = _vp()
             if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
                 raise RuntimeError("hipEventCreate failed")
             self.events[i] = ev
-
-    def run(self, target, draft, draft_tokens, uniforms, temperature, topk_draft=0, *,
-            out_tokens=None, num_accepted=None, workspace=None, stream=None):
-        args, out_tokens, num_accepted, _ = _prepare(target, draft, draft_tokens, uniforms, temperature,
-                                                     topk_draft, out_tokens, num_accepted, workspace,
-                                                     stream)
-        _check(load_library().spec_verify_timed(*args, self.events, self.N))
-        return out_tokens, num_accepted
 
     def stage_ms(self):
         out = []
@@ -258,3 +323,42 @@ class StageTimer:
             if self.events[i]:
                 self.hip.hipEventDestroy(self.events[i])
                 self.events[i] = None
+
+
+class TreeTimer(_Events):
+    """Four HIP events taken by spec_verify_tree_timed: ``stage_ms()`` returns
+    [statistics kernel, all walking kernels (first start to last end)] in ms."""
+
+    def __init__(self):
+        super().__init__(4)
+
+    def run(self, target, draft, node_tokens, parents, uniforms, temperature, topk_draft=0, *, rounds=4,
+            out_tokens=None, out_nodes=None, num_accepted=None, workspace=None, stream=None):
+        args, out_tokens, out_nodes, num_accepted, keep = _prepare_tree(
+            target, draft, node_tokens, parents, uniforms, temperature, topk_draft, rounds, out_tokens,
+            out_nodes, num_accepted, workspace, stream)
+        _check(load_library().spec_verify_tree_timed(*args, self.events, self.N))
+        del keep
+        return out_tokens, out_nodes, num_accepted
+
+
+class StageTimer(_Events):
+    """Six HIP events taken by spec_verify_timed: the start and end of each of
+    its kernels (statistics, sparse-draft merge, finishing), from the
+    dispatches' own timestamps.
+
+    ``run(...)`` enqueues one verification; ``stage_ms()`` (after the stream is
+    synchronised) returns each kernel's duration in milliseconds:
+    [statistics, top-k merge (0 without a sparse draft), finishing].
+    """
+
+    def __init__(self):
+        super().__init__(6)
+
+    def run(self, target, draft, draft_tokens, uniforms, temperature, topk_draft=0, *,
+            out_tokens=None, num_accepted=None, workspace=None, stream=None):
+        args, out_tokens, num_accepted, _ = _prepare(target, draft, draft_tokens, uniforms, temperature,
+                                                     topk_draft, out_tokens, num_accepted, workspace,
+                                                     stream)
+        _check(load_library().spec_verify_timed(*args, self.events, self.N))
+        return out_tokens, num_accepted

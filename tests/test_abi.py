@@ -141,3 +141,50 @@ def test_kl_argument_errors_without_launch():
 
     assert call(128, p) == B.SV_ERR_UNSUPPORTED      # KL against a truncated draft
     assert call(0, None) == B.SV_ERR_ARG             # no output for the KL values
+
+
+def _tree_call(lib, B_=4, N=7, V=1000, topk=0, dtype=B.SV_BF16, rounds=2, ptrs=True, ws=None, ws_n=None,
+               events=None, n_events=0):
+    p = ctypes.c_void_p(0x100000) if ptrs else None
+    n = None if ws_n is None else ctypes.byref(ctypes.c_size_t(ws_n))
+    if events is not None:
+        return lib.spec_verify_tree_timed(p, p, p, p, p, p, B_, N, V, topk, dtype, rounds, p, p, p, ws, n, None,
+                                          events, n_events)
+    return lib.spec_verify_tree(p, p, p, p, p, p, B_, N, V, topk, dtype, rounds, p, p, p, ws, n, None, None, None)
+
+
+def test_tree_argument_errors_without_launch():
+    lib = B.load_library()
+    need = B.tree_workspace_bytes(4, 7, 1000, B.SV_BF16)
+    assert need % 256 == 0 and need > 0
+    assert B.tree_workspace_bytes(64, 61, 151936, B.SV_BF16) > need
+    ws = ctypes.c_void_p(0x200000)
+    assert _tree_call(lib, B_=0, ws=ws, ws_n=need) == B.SV_ERR_ARG
+    assert _tree_call(lib, N=0, ws=ws, ws_n=need) == B.SV_ERR_ARG
+    assert _tree_call(lib, V=0, ws=ws, ws_n=need) == B.SV_ERR_ARG
+    assert _tree_call(lib, dtype=9, ws=ws, ws_n=need) == B.SV_ERR_ARG
+    assert _tree_call(lib, rounds=0, ws=ws, ws_n=need) == B.SV_ERR_ARG
+    assert _tree_call(lib, rounds=B.SV_MAX_NODES + 1, ws=ws, ws_n=need) == B.SV_ERR_ARG
+    assert _tree_call(lib, topk=-1, ws=ws, ws_n=need) == B.SV_ERR_ARG
+    assert _tree_call(lib, ws=ws, ws_n=None) == B.SV_ERR_ARG
+    assert _tree_call(lib, ws=ws, ws_n=need - 1) == B.SV_ERR_WORKSPACE
+    assert _tree_call(lib, ptrs=False, ws=ws, ws_n=need) == B.SV_ERR_ARG
+    assert _tree_call(lib, ws=ctypes.c_void_p(0x200040), ws_n=need) == B.SV_ERR_ARG
+    assert _tree_call(lib, topk=128, ws=ws, ws_n=need) == B.SV_ERR_UNSUPPORTED   # sparse draft
+    assert _tree_call(lib, N=B.SV_MAX_NODES + 1, ws=ws, ws_n=1 << 40) == B.SV_ERR_UNSUPPORTED
+    # the row's chunk statistics must fit the walking kernel's LDS
+    assert _tree_call(lib, N=64, V=1 << 20, dtype=B.SV_F32, ws=ws, ws_n=1 << 40) == B.SV_ERR_UNSUPPORTED
+    # topk at or above V is a dense draft
+    assert _tree_call(lib, topk=1000, ws=None, ws_n=0) == B.SV_OK
+    evs = (ctypes.c_void_p * 4)()
+    assert _tree_call(lib, ws=ws, ws_n=need, events=evs, n_events=3) == B.SV_ERR_ARG
+
+
+def test_tree_single_node_needs_no_tree_inputs():
+    lib = B.load_library()
+    need = B.tree_workspace_bytes(2, 1, 500, B.SV_F32)
+    p = ctypes.c_void_p(0x100000)
+    n = ctypes.c_size_t(need - 1)
+    # N == 1: draft logits, tokens and parents may be NULL (only the size check fails here)
+    assert lib.spec_verify_tree(p, None, None, None, p, p, 2, 1, 500, 0, B.SV_F32, 1, p, p, p,
+                                ctypes.c_void_p(0x200000), ctypes.byref(n), None, None, None) == B.SV_ERR_WORKSPACE

@@ -173,4 +173,166 @@ def make(case: Case | int, threads: int | None = None) -> dict:
                 temperature=T, topk=case.topk, dtype=case.dtype, case=case)
 
 
-__all__ = ["BF16", "F32", "Case", "CONFIGS", "make", "bf16_bits", "bf16_to_f32", "replace"]
+# ---------------------------------------------------------------- draft trees
+
+
+def level_tree(widths, seed: int = 0) -> tuple:
+    """Parents of a tree with widths[l] nodes at depth l + 1, in breadth-first
+    order (node 0 is the root, every parent precedes its children).  Each node
+    of a level picks its parent among the previous level's nodes with
+    probability proportional to 1 / (rank + 1): like a dynamic draft tree,
+    the best-ranked nodes are expanded most."""
+    rng = np.random.default_rng(seed)
+    parents = [-1]
+    prev = [0]
+    for w in widths:
+        wts = 1.0 / np.arange(1, len(prev) + 1)
+        pick = rng.choice(len(prev), size=w, p=wts / wts.sum())
+        level = []
+        for j in sorted(pick.tolist()):
+            parents.append(prev[j])
+            level.append(len(parents) - 1)
+        prev = level
+    return tuple(parents)
+
+
+def random_tree(N: int, rng: np.random.Generator) -> np.ndarray:
+    """A uniformly drawn recursive tree: node c's parent is uniform on [0, c)."""
+    par = np.full(N, -1, dtype=np.int32)
+    for c in range(1, N):
+        par[c] = rng.integers(0, c)
+    return par
+
+
+# A 60-node draft tree of depth 8 (plus the root), the tree size and depth
+# of the pages' dynamic-tree experiments.
+TREE_60_DEPTH8 = level_tree((4, 8, 12, 12, 10, 7, 4, 3), seed=7)
+
+
+@dataclass(frozen=True)
+class TreeCase:
+    """Recipe of one synthetic batch of draft trees.  Logits follow Case's
+    recipe at every node (the target at a node is the distribution after the
+    path to it; the draft there is target + noise); node c's token is drawn
+    from the tempered draft at its parent, independently of its siblings
+    (greedy rows: the parent's draft ids in decreasing logit order)."""
+
+    B: int
+    V: int
+    parents: tuple | None = TREE_60_DEPTH8   # shared topology; None: a random tree per row
+    nodes: int = 0                           # node count of the random trees
+    dtype: str = BF16
+    target_sigma: float = 3.0
+    peaks: int = 20
+    peak_height: float = 8.0
+    draft_sigma: float = 1.0
+    temperature: float = 1.0
+    greedy_rows: int = 0
+    seed: int = 0
+    name: str = ""
+
+    @property
+    def N(self) -> int:
+        return len(self.parents) if self.parents is not None else self.nodes
+
+
+# The tree workload: B = 32 rows of the 61-node tree over the 151,936-id
+# vocabulary, bf16, T = 1.0 (the pages' temperature for the tree experiments).
+TREE_CONFIGS = [
+    TreeCase(B=32, V=151936, draft_sigma=1.0, temperature=1.0, seed=2001,
+             name="B32-N61-depth8-V151936-bf16-T1.0"),
+]
+
+
+def _make_tree_row(case: TreeCase, seq: np.random.SeedSequence, T: float):
+    rng = np.random.default_rng(seq)
+    N, V = case.N, case.V
+    par = np.asarray(case.parents, dtype=np.int32) if case.parents is not None else random_tree(N, rng)
+    has_kids = np.zeros(N, dtype=bool)
+    has_kids[par[1:]] = True
+    tgt = rng.standard_normal((N, V), dtype=np.float32)
+    tgt *= np.float32(case.target_sigma)
+    for i in range(N):
+        if case.peaks:
+            ids = rng.choice(V, size=case.peaks, replace=False)
+            tgt[i, ids] += np.float32(case.peak_height)
+    if case.dtype == BF16:
+        tgt_store = bf16_bits(tgt)
+        tgt_val = bf16_to_f32(tgt_store)
+    else:
+        tgt_store = tgt
+        tgt_val = tgt
+    # Drafts at leaves are never read: they hold the target.
+    dft_store = tgt_store.copy()
+    dft_val = tgt_val.copy()
+    for i in np.flatnonzero(has_kids):
+        noise = rng.standard_normal(V, dtype=np.float32)
+        noise *= np.float32(case.draft_sigma)
+        d = tgt_val[i] + noise
+        if case.dtype == BF16:
+            dft_store[i] = bf16_bits(d)
+            dft_val[i] = bf16_to_f32(dft_store[i])
+        else:
+            dft_store[i] = d
+            dft_val[i] = d
+    toks = np.full(N, -1, dtype=np.int32)
+    for v in np.flatnonzero(has_kids):
+        kids = np.flatnonzero(par == v)
+        kids = kids[kids > v]
+        if T > 0:
+            # Gumbel-max, one independent draw per child
+            for c in kids:
+                with np.errstate(divide="ignore"):
+                    score = dft_val[v] / np.float32(T) - np.log(rng.standard_exponential(V, dtype=np.float32))
+                toks[c] = int(np.argmax(score))
+        else:
+            order = np.argsort(-dft_val[v], kind="stable")
+            toks[kids] = order[: kids.size]
+    uni = rng.random(N, dtype=np.float32)
+    return tgt_store, dft_store, toks, par, uni
+
+
+def make_tree(case: TreeCase | int, threads: int | None = None) -> dict:
+    """Generate one batch of draft trees.  Returns host arrays:
+
+    target, draft [B, N, V] uint16 (bf16 bits) or float32
+    tokens, parents [B, N] int32 (entry 0: -1), uniforms [B, N] float32 in
+    [0, 1), temperature [B] float32, plus 'dtype' and 'case'.
+    """
+    if isinstance(case, int):
+        case = TREE_CONFIGS[case]
+    B, N, V = case.B, case.N, case.V
+    seqs = np.random.SeedSequence(case.seed).spawn(B + 1)
+    T = np.full(B, case.temperature, dtype=np.float32)
+    if case.greedy_rows:
+        perm = np.random.default_rng(seqs[B]).permutation(B)
+        T[perm[: case.greedy_rows]] = 0.0
+    st = np.uint16 if case.dtype == BF16 else np.float32
+    target = np.empty((B, N, V), dtype=st)
+    draft = np.empty((B, N, V), dtype=st)
+    tokens = np.empty((B, N), dtype=np.int32)
+    parents = np.empty((B, N), dtype=np.int32)
+    uniforms = np.empty((B, N), dtype=np.float32)
+
+    def work(b):
+        t, d, tk, par, u = _make_tree_row(case, seqs[b], float(T[b]))
+        target[b] = t
+        draft[b] = d
+        tokens[b] = tk
+        parents[b] = par
+        uniforms[b] = u
+
+    if threads is None:
+        threads = min(16, os.cpu_count() or 1)
+    if threads <= 1 or B == 1:
+        for b in range(B):
+            work(b)
+    else:
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(work, range(B)))
+    return dict(target=target, draft=draft, tokens=tokens, parents=parents, uniforms=uniforms,
+                temperature=T, dtype=case.dtype, case=case)
+
+
+__all__ = ["BF16", "F32", "Case", "CONFIGS", "make", "bf16_bits", "bf16_to_f32", "replace",
+           "TreeCase", "TREE_CONFIGS", "TREE_60_DEPTH8", "level_tree", "random_tree", "make_tree"]
