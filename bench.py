@@ -122,6 +122,8 @@ def main():
     ap.add_argument("--kl", action="store_true",
                     help="time spec_verify_kl (verification plus KL(p||q) per position; whole-call "
                          "rate only)")
+    ap.add_argument("--tree", type=int, default=-1,
+                    help="time spec_verify_tree on this draft-tree workload instead (0 = 61-node tree)")
     ap.add_argument("--relaxed", default="",
                     help="ALPHA,MAX_RANK,MIN_PROB: time the lossy relaxed acceptance rule instead "
                          "(whole-call rate only; per-kernel times come from a rocprofv3 trace)")
@@ -137,6 +139,10 @@ def main():
 
     import workloads as W
     import rejection_sampling_verifier_amd as rsv
+
+    if args.tree >= 0:
+        tree_main(args, W, rsv, np, torch)
+        return
 
     case = W.CONFIGS[args.config]
     t0 = time.perf_counter()
@@ -259,6 +265,155 @@ def main():
     if not args.no_cpu:
         print("[bench] timing the CPU oracle ...", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(d, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+def tree_algorithmic_bytes(d) -> dict:
+    """Every target logit once, and the draft logits of every node with
+    children of a sampling row once, plus tokens, parents, uniforms,
+    temperatures and outputs."""
+    import numpy as np
+
+    B, N, V = d["target"].shape
+    esz = d["target"].itemsize
+    internal = 0
+    for b in range(B):
+        if d["temperature"][b] > 0:
+            internal += np.unique(d["parents"][b, 1:][d["parents"][b, 1:] >= 0]).size
+    logits = B * N * V * esz + internal * V * esz
+    small = 3 * B * N * 4 + B * 4 + 2 * B * N * 4 + B * 4
+    return {"stats_kernel": logits, "m_min": logits + small, "internal_nodes": internal}
+
+
+def tree_cpu_baseline(d, budget_s: float):
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+
+    B, N, _ = d["target"].shape
+    threads = min(16, os.cpu_count() or 1)
+
+    def one(b):
+        return oracle.verify_tree(d["target"], d["draft"], d["tokens"], d["parents"], d["uniforms"],
+                                  d["temperature"], 0, d["dtype"], rows=[b])
+
+    rows_done = 0
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        while True:
+            list(ex.map(one, range(B)))
+            rows_done += B
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    dt = time.perf_counter() - t0
+    return {"value": rows_done * (N - 1) / dt, "unit": "nodes/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows_done // B} full passes over the {B}-row batch ({rows_done} trees, "
+                      f"{rows_done * (N - 1)} draft nodes) in {dt:.1f} s, rows spread over {threads} threads"}
+
+
+def tree_main(args, W, rsv, np, torch):
+    """One step = one spec_verify_tree call over a batch of draft trees."""
+    case = W.TREE_CONFIGS[args.tree]
+    t0 = time.perf_counter()
+    d = W.make_tree(case)
+    print(f"[bench] generated {case.name} in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    by = tree_algorithmic_bytes(d)
+    copies = min(8, max(1, -(-(2 * MALL_BYTES) // by["m_min"]) + (1 if by["m_min"] < 2 * MALL_BYTES else 0)))
+
+    def upload(a):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        if a.dtype == np.uint16:
+            t = t.view(torch.bfloat16)
+        return t.to(dev)
+
+    keys = ("target", "draft", "tokens", "parents", "uniforms", "temperature")
+    base = {k: upload(d[k]) for k in keys}
+    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(copies - 1)]
+    B, N, V = base["target"].shape
+    dt_code = rsv.SV_BF16 if d["dtype"] == "bf16" else rsv.SV_F32
+    ws = rsv.new_tree_workspace(B, N, V, dt_code, dev)
+    out = torch.empty((B, N), dtype=torch.int32, device=dev)
+    nodes = torch.empty((B, N), dtype=torch.int32, device=dev)
+    nacc = torch.empty((B,), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, timer=None):
+        x = sets[i % copies]
+        fn = timer.run if timer is not None else rsv.verify_tree
+        fn(x["target"], x["draft"], x["tokens"], x["parents"], x["uniforms"], x["temperature"], 0,
+           out_tokens=out, out_nodes=nodes, num_accepted=nacc, workspace=ws,
+           stream=stream.cuda_stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - w0) * 1e3
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    accepted = float(nacc.float().mean().item())
+
+    timers = [rsv.TreeTimer() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, timers[i])
+    torch.cuda.synchronize()
+    stages = np.array([t.stage_ms() for t in timers])
+    for t in timers:
+        t.close()
+    stats_ms, walk_ms = (float(v) for v in stages.mean(axis=0))
+
+    # Residual passes per row (rejected siblings), from one probed call.
+    x = sets[0]
+    _, _, na, probs, _ = rsv.verify_tree(x["target"], x["draft"], x["tokens"], x["parents"], x["uniforms"],
+                                         x["temperature"], 0, probes=True, workspace=ws)
+    torch.cuda.synchronize()
+    tested = (~torch.isnan(probs[:, :, 0])).sum(dim=1).cpu().numpy()
+    passes = tested - na.cpu().numpy()
+
+    value = B * (N - 1) / (ms_per_step * 1e-3)
+    achieved = by["stats_kernel"] / (stats_ms * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "nodes/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": case.name, "B": B, "nodes": N, "V": V, "logits": d["dtype"],
+                   "temperature": float(case.temperature), "internal_nodes_read": by["internal_nodes"],
+                   "input_copies": copies},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "tree_stats_kernel", "bytes_per_launch": by["stats_kernel"],
+                     "avg_launch_ms": round(stats_ms, 5)},
+        "effective_GBps_whole_call": round(by["m_min"] / (ms_per_step * 1e-3) / 1e9, 1),
+        "m_min_bytes": by["m_min"],
+        "kernel_ms": {"tree_stats_kernel": round(stats_ms, 5), "tree_finish_kernel": round(walk_ms, 5)},
+        "wall_ms_per_step": round(wall_ms / args.steps, 5),
+        "mean_accepted": round(accepted, 4),
+        "mean_residual_passes": round(float(passes.mean()), 3),
+        "max_residual_passes": int(passes.max()),
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if not args.no_cpu:
+        print("[bench] timing the CPU oracle ...", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = tree_cpu_baseline(d, args.cpu_seconds)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

@@ -32,9 +32,9 @@
  * All pointers are device pointers owned by the caller.  Inputs are read
  * only; outputs are fully overwritten.  The library allocates nothing, keeps
  * no mutable global state and never synchronises: every call only enqueues
- * kernels on `stream` (two, three with a sparse draft; 1 + rounds for
- * spec_verify_tree); outputs are valid once the caller has synchronised that
- * stream.  Calls on different workspaces are reentrant.
+ * two kernels on `stream` (three with a sparse draft); outputs are valid
+ * once the caller has synchronised that stream.  Calls on different
+ * workspaces are reentrant.
  */
 #ifndef SPEC_VERIFY_H
 #define SPEC_VERIFY_H
@@ -232,11 +232,6 @@ int spec_verify_kl(const void* target_logits, const void* draft_logits,
  * temperature    [B] float32 device; T <= 0 (or NaN) selects greedy.
  * B >= 1, N in [1, SV_MAX_NODES], V >= 1.
  * topk_draft     0 or >= V (dense draft); a sparse draft is SV_ERR_UNSUPPORTED.
- * rounds         >= 1: launches of the walking kernel.  Each launch performs
- *                at most one residual pass per row with all of the row's
- *                vocabulary chunks in parallel; a row that needs more passes
- *                than `rounds` completes the rest in the last launch with
- *                one work-group (same result, slower).
  * out_tokens     [B, N] int32 device: the tokens of the accepted nodes in
  *                path order, then the final token, then -1.
  * out_nodes      [B, N] int32 device: the accepted node indices in path
@@ -251,14 +246,13 @@ int spec_verify_kl(const void* target_logits, const void* draft_logits,
  * mass_out       [B] float32 device or NULL: total weight of the final
  *                draw's distribution (W for a residual, ~1 for a target), 0
  *                for greedy rows.
- * Every call enqueues 1 + rounds kernels.  SV_ERR_UNSUPPORTED also when the
- * row's chunk statistics (2 N C 16 bytes) do not fit the walking kernel's
- * LDS.
+ * Every call enqueues two kernels.  SV_ERR_UNSUPPORTED also when the row's
+ * chunk statistics (2 N C 16 bytes) do not fit the walking kernel's LDS.
  */
 int spec_verify_tree(const void* target_logits, const void* draft_logits,
                      const int32_t* node_tokens, const int32_t* parents,
                      const float* uniforms, const float* temperature, int B,
-                     int N, int V, int topk_draft, int dtype, int rounds,
+                     int N, int V, int topk_draft, int dtype,
                      int32_t* out_tokens, int32_t* out_nodes,
                      int32_t* num_accepted, void* workspace,
                      size_t* workspace_bytes, hipStream_t stream,
@@ -267,14 +261,14 @@ int spec_verify_tree(const void* target_logits, const void* draft_logits,
 /*
  * spec_verify_tree_timed - spec_verify_tree (without probes) that also times
  * its kernels: events[0] / events[1] take the start / end of the statistics
- * kernel's dispatch, events[2] / events[3] the start of the first and the end
- * of the last walking kernel.  n_events must be 4.
+ * kernel's dispatch, events[2] / events[3] those of the walking kernel.
+ * n_events must be 4.
  */
 int spec_verify_tree_timed(const void* target_logits, const void* draft_logits,
                            const int32_t* node_tokens, const int32_t* parents,
                            const float* uniforms, const float* temperature,
                            int B, int N, int V, int topk_draft, int dtype,
-                           int rounds, int32_t* out_tokens, int32_t* out_nodes,
+                           int32_t* out_tokens, int32_t* out_nodes,
                            int32_t* num_accepted, void* workspace,
                            size_t* workspace_bytes, hipStream_t stream,
                            hipEvent_t* events, int n_events);

@@ -67,7 +67,7 @@ def load_library(path: str | None = None):
     lib.spec_verify_kl.restype = _i32
     lib.spec_verify_timed.argtypes = _COMMON + [ctypes.POINTER(_vp), _i32]
     lib.spec_verify_timed.restype = _i32
-    _tree = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]
+    _tree = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]
     lib.spec_verify_tree.argtypes = _tree + [_vp, _vp]
     lib.spec_verify_tree.restype = _i32
     lib.spec_verify_tree_timed.argtypes = _tree + [ctypes.POINTER(_vp), _i32]
@@ -218,9 +218,9 @@ def verify_kl(target, draft, draft_tokens, uniforms, temperature, topk_draft: in
     return out_tokens, num_accepted, kl
 
 
-def tree_workspace_bytes(B: int, N: int, V: int, dtype: int = SV_BF16, rounds: int = 1) -> int:
+def tree_workspace_bytes(B: int, N: int, V: int, dtype: int = SV_BF16) -> int:
     n = ctypes.c_size_t(0)
-    _check(load_library().spec_verify_tree(None, None, None, None, None, None, B, N, V, 0, dtype, rounds,
+    _check(load_library().spec_verify_tree(None, None, None, None, None, None, B, N, V, 0, dtype,
                                            None, None, None, None, ctypes.byref(n), None, None, None))
     return n.value
 
@@ -231,7 +231,7 @@ def new_tree_workspace(B: int, N: int, V: int, dtype: int = SV_BF16, device="cud
     return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
 
 
-def _prepare_tree(target, draft, node_tokens, parents, uniforms, temperature, topk_draft, rounds,
+def _prepare_tree(target, draft, node_tokens, parents, uniforms, temperature, topk_draft,
                   out_tokens, out_nodes, num_accepted, workspace, stream):
     if target.dim() != 3:
         raise ValueError("target_logits must be [B, N, V]")
@@ -264,8 +264,8 @@ def _prepare_tree(target, draft, node_tokens, parents, uniforms, temperature, to
     many = N > 1
     args = [_ptr(target), _ptr(draft) if many else None, _ptr(node_tokens) if many else None,
             _ptr(parents) if many else None, _ptr(uniforms), _ptr(temperature), B, N, V, topk_draft, dt,
-            int(rounds), _ptr(out_tokens), _ptr(out_nodes), _ptr(num_accepted), _ptr(workspace),
-            ctypes.byref(ws_n), ctypes.c_void_p(stream)]
+            _ptr(out_tokens), _ptr(out_nodes), _ptr(num_accepted), _ptr(workspace), ctypes.byref(ws_n),
+            ctypes.c_void_p(stream)]
     # The caller holds `keep` until the call has been enqueued: a workspace
     # created here must not return to torch's allocator before that.
     keep = (target, draft, node_tokens, parents, uniforms, temperature, workspace)
@@ -273,15 +273,15 @@ def _prepare_tree(target, draft, node_tokens, parents, uniforms, temperature, to
 
 
 def verify_tree(target, draft, node_tokens, parents, uniforms, temperature, topk_draft: int = 0, *,
-                rounds: int = 4, probes: bool = False, out_tokens=None, out_nodes=None, num_accepted=None,
-                workspace=None, stream=None):
+                probes: bool = False, out_tokens=None, out_nodes=None, num_accepted=None, workspace=None,
+                stream=None):
     """spec_verify_tree: verify one draft tree per row (see the header).
 
     Returns (out_tokens [B, N], out_nodes [B, N], num_accepted [B]), plus
     (probs [B, N, 3], mass [B]) when ``probes`` is set.
     """
     args, out_tokens, out_nodes, num_accepted, keep = _prepare_tree(
-        target, draft, node_tokens, parents, uniforms, temperature, topk_draft, rounds, out_tokens, out_nodes,
+        target, draft, node_tokens, parents, uniforms, temperature, topk_draft, out_tokens, out_nodes,
         num_accepted, workspace, stream)
     probs = mass = None
     if probes:
@@ -327,15 +327,15 @@ class _Events:
 
 class TreeTimer(_Events):
     """Four HIP events taken by spec_verify_tree_timed: ``stage_ms()`` returns
-    [statistics kernel, all walking kernels (first start to last end)] in ms."""
+    [statistics kernel, walking kernel] in ms."""
 
     def __init__(self):
         super().__init__(4)
 
-    def run(self, target, draft, node_tokens, parents, uniforms, temperature, topk_draft=0, *, rounds=4,
+    def run(self, target, draft, node_tokens, parents, uniforms, temperature, topk_draft=0, *,
             out_tokens=None, out_nodes=None, num_accepted=None, workspace=None, stream=None):
         args, out_tokens, out_nodes, num_accepted, keep = _prepare_tree(
-            target, draft, node_tokens, parents, uniforms, temperature, topk_draft, rounds, out_tokens,
+            target, draft, node_tokens, parents, uniforms, temperature, topk_draft, out_tokens,
             out_nodes, num_accepted, workspace, stream)
         _check(load_library().spec_verify_tree_timed(*args, self.events, self.N))
         del keep

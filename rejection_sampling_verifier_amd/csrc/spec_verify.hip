@@ -1746,7 +1746,7 @@ constexpr int TREE_MAX_LDS_WORDS = 14336;  // the walking kernel's dynamic LDS (
 
 struct TreePlan {
   int C = 0, CS = 0;
-  size_t off_cnt = 0, off_part = 0, off_subK = 0, off_subR = 0, off_gath = 0, off_state = 0, total = 0;
+  size_t off_cnt = 0, off_part = 0, off_subK = 0, off_subR = 0, off_gath = 0, total = 0;
   size_t lds_bytes = 0;
 };
 
@@ -1760,21 +1760,19 @@ int make_tree_plan(int B, int N, int V, int dtype, TreePlan& pl) {
   if (words > (size_t)TREE_MAX_LDS_WORDS) return SV_ERR_UNSUPPORTED;
   pl.C = C;
   pl.CS = CS;
-  // subR and cnt are zero between calls; the other regions are written
-  // before they are read.
+  // The counters and subR are zero between calls; the other regions are
+  // written before they are read.
   size_t off = 0;
-  pl.off_cnt = off;
-  off = align256(off + sizeof(unsigned) * (size_t)B);
+  pl.off_cnt = off;  // claim [B], then leave [B]
+  off = align256(off + 2 * sizeof(unsigned) * (size_t)B);
   pl.off_part = off;
   off = align256(off + 4 * sizeof(uint32_t) * (size_t)B * 2 * N * C);
   pl.off_subK = off;
   off = align256(off + sizeof(uint32_t) * (size_t)B * N * C * NSUB);
   pl.off_subR = off;
-  off = align256(off + sizeof(uint32_t) * (size_t)B * C * NSUB);
+  off = align256(off + sizeof(uint32_t) * (size_t)B * N * C * NSUB);
   pl.off_gath = off;
   off = align256(off + 2 * sizeof(float) * (size_t)B * N);
-  pl.off_state = off;
-  off = align256(off + sizeof(TreeState) * (size_t)B);
   pl.total = off;
   pl.lds_bytes = words * sizeof(uint32_t);
   return SV_OK;
@@ -1791,23 +1789,19 @@ int launch_tree_kernel(F kernel, int grid, size_t lds, hipStream_t st, hipEvent_
 }
 
 template <typename ET, bool AL>
-int launch_tree(TreeArgs a, size_t lds, int rounds, hipStream_t st, hipEvent_t* ev) {
-  int rc = launch_tree_kernel(tree_stats_kernel<ET, AL>, a.B * 2 * a.N * a.C, 0, st, ev ? ev[0] : nullptr,
-                              ev ? ev[1] : nullptr, a);
-  a.last_round = rounds - 1;
-  for (int r = 0; r < rounds && rc == SV_OK; ++r) {
-    a.round = r;
-    rc = launch_tree_kernel(tree_finish_kernel<ET, AL>, a.B * a.C, lds, st, (ev && r == 0) ? ev[2] : nullptr,
-                            (ev && r == rounds - 1) ? ev[3] : nullptr, a);
-  }
-  return rc;
+int launch_tree(const TreeArgs& a, size_t lds, hipStream_t st, hipEvent_t* ev) {
+  const int rc = launch_tree_kernel(tree_stats_kernel<ET, AL>, a.B * 2 * a.N * a.C, 0, st, ev ? ev[0] : nullptr,
+                                    ev ? ev[1] : nullptr, a);
+  if (rc != SV_OK) return rc;
+  return launch_tree_kernel(tree_finish_kernel<ET, AL>, a.B * a.C, lds, st, ev ? ev[2] : nullptr,
+                            ev ? ev[3] : nullptr, a);
 }
 
 int run_tree(const void* tgt, const void* dft, const int32_t* tok, const int32_t* par, const float* uni,
-             const float* temp, int B, int N, int V, int topk, int dtype, int rounds, int32_t* out,
-             int32_t* onodes, int32_t* nacc, void* ws, size_t* ws_bytes, hipStream_t st, float* probs,
-             float* mass, hipEvent_t* ev, int nev) {
-  if (!ws_bytes || topk < 0 || rounds < 1 || rounds > SV_MAX_NODES) return SV_ERR_ARG;
+             const float* temp, int B, int N, int V, int topk, int dtype, int32_t* out, int32_t* onodes,
+             int32_t* nacc, void* ws, size_t* ws_bytes, hipStream_t st, float* probs, float* mass,
+             hipEvent_t* ev, int nev) {
+  if (!ws_bytes || topk < 0) return SV_ERR_ARG;
   if (topk >= V) topk = 0;
   if (topk > 0) return SV_ERR_UNSUPPORTED;
   TreePlan pl;
@@ -1826,24 +1820,23 @@ int run_tree(const void* tgt, const void* dft, const int32_t* tok, const int32_t
   a.tgt = tgt; a.dft = dft; a.tok = tok; a.par = par; a.uni = uni; a.temp = temp;
   a.out = out; a.onodes = onodes; a.nacc = nacc; a.probes = probs; a.mass = mass;
   char* base = static_cast<char*>(ws);
-  a.cnt = reinterpret_cast<unsigned*>(base + pl.off_cnt);
+  a.claim = reinterpret_cast<unsigned*>(base + pl.off_cnt);
+  a.leave = a.claim + B;
   a.part = reinterpret_cast<uint32_t*>(base + pl.off_part);
   a.subK = reinterpret_cast<uint32_t*>(base + pl.off_subK);
   a.subR = reinterpret_cast<uint32_t*>(base + pl.off_subR);
   a.gath = reinterpret_cast<float*>(base + pl.off_gath);
-  a.state = reinterpret_cast<TreeState*>(base + pl.off_state);
   a.B = B; a.N = N; a.V = V; a.C = pl.C; a.CS = pl.CS;
-  a.round = 0; a.last_round = rounds - 1;
   const size_t esz = dtype == SV_BF16 ? 2 : 4;
   const bool aligned = (reinterpret_cast<uintptr_t>(tgt) % 16 == 0) &&
                        (N == 1 || reinterpret_cast<uintptr_t>(dft) % 16 == 0) && ((size_t)V * esz) % 16 == 0;
   (void)hipGetLastError();
   hipEvent_t* e = nev ? ev : nullptr;
   if (dtype == SV_BF16)
-    return aligned ? launch_tree<uint16_t, true>(a, pl.lds_bytes, rounds, st, e)
-                   : launch_tree<uint16_t, false>(a, pl.lds_bytes, rounds, st, e);
-  return aligned ? launch_tree<float, true>(a, pl.lds_bytes, rounds, st, e)
-                 : launch_tree<float, false>(a, pl.lds_bytes, rounds, st, e);
+    return aligned ? launch_tree<uint16_t, true>(a, pl.lds_bytes, st, e)
+                   : launch_tree<uint16_t, false>(a, pl.lds_bytes, st, e);
+  return aligned ? launch_tree<float, true>(a, pl.lds_bytes, st, e)
+                 : launch_tree<float, false>(a, pl.lds_bytes, st, e);
 }
 
 }  // namespace
@@ -1903,23 +1896,23 @@ int spec_verify_kl(const void* target_logits, const void* draft_logits, const in
 
 int spec_verify_tree(const void* target_logits, const void* draft_logits, const int32_t* node_tokens,
                      const int32_t* parents, const float* uniforms, const float* temperature, int B, int N,
-                     int V, int topk_draft, int dtype, int rounds, int32_t* out_tokens, int32_t* out_nodes,
+                     int V, int topk_draft, int dtype, int32_t* out_tokens, int32_t* out_nodes,
                      int32_t* num_accepted, void* workspace, size_t* workspace_bytes, hipStream_t stream,
                      float* probs_out, float* mass_out) {
   return run_tree(target_logits, draft_logits, node_tokens, parents, uniforms, temperature, B, N, V, topk_draft,
-                  dtype, rounds, out_tokens, out_nodes, num_accepted, workspace, workspace_bytes, stream,
-                  probs_out, mass_out, nullptr, 0);
+                  dtype, out_tokens, out_nodes, num_accepted, workspace, workspace_bytes, stream, probs_out,
+                  mass_out, nullptr, 0);
 }
 
 int spec_verify_tree_timed(const void* target_logits, const void* draft_logits, const int32_t* node_tokens,
                            const int32_t* parents, const float* uniforms, const float* temperature, int B,
-                           int N, int V, int topk_draft, int dtype, int rounds, int32_t* out_tokens,
-                           int32_t* out_nodes, int32_t* num_accepted, void* workspace,
-                           size_t* workspace_bytes, hipStream_t stream, hipEvent_t* events, int n_events) {
+                           int N, int V, int topk_draft, int dtype, int32_t* out_tokens, int32_t* out_nodes,
+                           int32_t* num_accepted, void* workspace, size_t* workspace_bytes,
+                           hipStream_t stream, hipEvent_t* events, int n_events) {
   if (workspace && n_events != 4) return SV_ERR_ARG;
   return run_tree(target_logits, draft_logits, node_tokens, parents, uniforms, temperature, B, N, V, topk_draft,
-                  dtype, rounds, out_tokens, out_nodes, num_accepted, workspace, workspace_bytes, stream,
-                  nullptr, nullptr, events, n_events);
+                  dtype, out_tokens, out_nodes, num_accepted, workspace, workspace_bytes, stream, nullptr,
+                  nullptr, events, n_events);
 }
 
 int spec_verify_plan(int B, int K, int V, int topk_draft, int dtype, int* chunks, int* chunk_len) {

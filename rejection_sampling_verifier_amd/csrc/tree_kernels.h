@@ -1,5 +1,5 @@
 // Draft-tree verification: the statistics pass over every node of each row's
-// tree and the residual-pass rounds of the tree walk.  Included by
+// tree and the tree walk with its residual passes.  Included by
 // spec_verify.hip inside its anonymous namespace; it uses that file's
 // helpers (tiles, reductions, published words, segment_search).
 //
@@ -19,24 +19,11 @@
 // node slots 0..N-1 the targets and N..2N-1 the drafts (a draft slot only for
 // a node with children); it writes the chunk partials, the logits of each
 // child's token at its parent (target and draft), and for a leaf the 32
-// sub-block sums of its target.  tree_finish_kernel, launched `rounds` times:
-// one work-group per (row, chunk).  Every work-group of a row repeats the
-// walk up to the next rejection, the row's work-groups run that rejection's
-// residual pass together (published sums, last arriver as in finish_kernel),
-// and the last arriver continues the walk.  A row that needs another pass
-// leaves its walk state for the next round; in the last round the last
-// arriver runs the remaining passes over all chunks alone.
+// sub-block sums of its target.  tree_finish_kernel: one work-group per
+// (row, chunk) walks the row's tree; the residual passes are shared out among
+// the row's work-groups chunk by chunk (see the kernel).
 
 constexpr int MAX_NODES = SV_MAX_NODES;
-
-struct TreeState {
-  int phase;                 // 0: a residual pass at (v, c) is pending; 1: done
-  int v;                     // node of the pending pass
-  int j;                     // the child rejected last at v
-  float c;                   // residual scale of the pending pass
-  int n;                     // accepted nodes so far
-  int path[MAX_NODES];       // accepted nodes, root to leaf
-};
 
 struct TreeArgs {
   const void* tgt;           // [B, N, V]
@@ -50,14 +37,13 @@ struct TreeArgs {
   int32_t* nacc;             // [B]
   uint32_t* part;            // [B, 2N, C, 4] chunk partials {max | argmax value, sum, argmax id, 0}
   uint32_t* subK;            // [B, N, C, NSUB] leaf target sub-block sums (vs chunk max)
-  uint32_t* subR;            // [B, C, NSUB] published residual sub-block sums
-  unsigned* cnt;             // [B]
+  uint32_t* subR;            // [B, N, C, NSUB] published residual sub-block sums, one set per pass
+  unsigned* claim;           // [B] residual-pass tickets handed out
+  unsigned* leave;           // [B] work-groups of the row that have finished
   float* gath;               // [B, N, 2] l_t, l_q of each node's token at its parent
-  TreeState* state;          // [B]
   float* probes;             // [B, N, 3] (p(d), q(d), r(d)) of each tested node, NaN elsewhere; or null
   float* mass;               // [B] total weight of the final draw's distribution; or null
   int B, N, V, C, CS;
-  int round, last_round;
 };
 
 template <typename ET>
@@ -68,13 +54,6 @@ __device__ __forceinline__ uint32_t* tree_part(const TreeArgs& a, int b, int slo
   return a.part + (((size_t)b * 2 * a.N + slot) * (size_t)a.C + c) * 4;
 }
 
-// Bit mask of the children of `node` (parents must precede their children).
-__device__ __forceinline__ unsigned long long tree_kids(const int* par, int N, int node) {
-  unsigned long long m = 0;
-  for (int x = node + 1; x < N; ++x)
-    if (par[x] == node) m |= 1ull << x;
-  return m;
-}
 
 // ============================================================================
 // Statistics of one (row, node slot, chunk).
@@ -168,13 +147,56 @@ void tree_stats_kernel(TreeArgs a) {
 }
 
 // ============================================================================
+// Reductions over groups of G = 16, 32 or 64 lanes of a wave, G a compile-time
+// constant.  They take the steps of wave_sum / wave_max / wave_argmax that
+// stay inside the group, so a group whose lanes past the data hold the
+// identity gives bit for bit what those reductions give over the wave.  The
+// group's result is in its last lane.
+// ============================================================================
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+  v += dpp_f<dpp::QUAD_1032>(0.f, v);
+  v += dpp_f<dpp::QUAD_2301>(0.f, v);
+  v += dpp_f<dpp::ROW_HALF_MIRROR>(0.f, v);
+  v += dpp_f<dpp::ROW_MIRROR>(0.f, v);
+  if (G >= 32) v += dpp_f<dpp::ROW_BCAST15, 0xA>(0.f, v);
+  if (G >= 64) v += dpp_f<dpp::ROW_BCAST31, 0xC>(0.f, v);
+  return v;
+}
+template <int G>
+__device__ __forceinline__ float group_max(float v) {
+  v = fmaxf(v, dpp_f<dpp::QUAD_1032>(NEG_INF, v));
+  v = fmaxf(v, dpp_f<dpp::QUAD_2301>(NEG_INF, v));
+  v = fmaxf(v, dpp_f<dpp::ROW_HALF_MIRROR>(NEG_INF, v));
+  v = fmaxf(v, dpp_f<dpp::ROW_MIRROR>(NEG_INF, v));
+  if (G >= 32) v = fmaxf(v, dpp_f<dpp::ROW_BCAST15, 0xA>(NEG_INF, v));
+  if (G >= 64) v = fmaxf(v, dpp_f<dpp::ROW_BCAST31, 0xC>(NEG_INF, v));
+  return v;
+}
+template <int G>
+__device__ __forceinline__ void group_argmax(float& v, int& i) {
+  argmax_step<dpp::QUAD_1032>(v, i);
+  argmax_step<dpp::QUAD_2301>(v, i);
+  argmax_step<dpp::ROW_HALF_MIRROR>(v, i);
+  argmax_step<dpp::ROW_MIRROR>(v, i);
+  if (G >= 32) argmax_step<dpp::ROW_BCAST15, 0xA>(v, i);
+  if (G >= 64) argmax_step<dpp::ROW_BCAST31, 0xC>(v, i);
+}
+// Broadcast of the group's last lane to the whole group.
+template <int G>
+__device__ __forceinline__ float group_last(float v) {
+  const int lane = threadIdx.x & 63;
+  return __shfl(v, (lane & ~(G - 1)) + G - 1, 64);
+}
+
+// ============================================================================
 // The walk, on the row's merged statistics in LDS.
 // ============================================================================
 struct TreeRow {
   float M[2 * MAX_NODES];    // target (0..N-1) and draft (N..2N-1) max, or argmax value (greedy)
   float Z[2 * MAX_NODES];
+  unsigned long long kids[MAX_NODES];  // bit x: node x is a child of the node
   int idx[MAX_NODES];        // target argmax (greedy)
-  int par[MAX_NODES];
   int tok[MAX_NODES];
   float u[MAX_NODES];
   float gt[MAX_NODES], gq[MAX_NODES];
@@ -188,6 +210,54 @@ struct TreeRow {
 };
 enum { W_PASS = 0, W_LEAF = 1, W_RESID = 2, W_GREEDY = 3, W_FALLBACK = 4 };
 
+// Merges the chunk statistics of every node (and of the draft of every node
+// with children) into tr.M / tr.Z / tr.idx: one group of G lanes per slot,
+// lane g of the group holding chunks g, g + G, ... (G = 64 when C > 32), so
+// that the results equal the wave reductions of the linear verifier bit for
+// bit.
+template <int G>
+__device__ __forceinline__ void tree_merge(TreeRow& tr, const uint32_t* pw, int N, int C, bool greedy, float s) {
+  constexpr int PER = 64 / G;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int gl = lane % G;
+  const int nslots = greedy ? N : 2 * N;
+  for (int base = wave * PER; base < nslots; base += NWAVE * PER) {
+    const int slot = base + lane / G;
+    const int node = slot < N ? slot : slot - N;
+    const bool need = slot < nslots && (slot < N || tr.kids[node] != 0ull);
+    auto word = [&](int cc, int w) { return __uint_as_float(pw[((size_t)slot * C + cc) * 4 + w]); };
+    if (greedy) {
+      float bv = NEG_INF;
+      int bi = INT_MAX;
+      if (need)
+        for (int cc = gl; cc < C; cc += G) argmax_merge(bv, bi, word(cc, 0), __float_as_int(word(cc, 2)));
+      group_argmax<G>(bv, bi);
+      if (need && gl == G - 1) {
+        tr.M[slot] = bv;
+        tr.Z[slot] = 0.f;
+        tr.idx[node] = bi;
+      }
+    } else {
+      float m = NEG_INF;
+      if (need)
+        for (int cc = gl; cc < C; cc += G) m = fmaxf(m, word(cc, 0));
+      m = group_last<G>(group_max<G>(m));
+      const float MS = mul_rn(m, s);
+      float z = 0.f;
+      if (need)
+        for (int cc = gl; cc < C; cc += G) {
+          const float mc = word(cc, 0), zc = word(cc, 1);
+          if (mc != NEG_INF) z += zc * exp2_fast(mul_rn(mc, s) - MS);
+        }
+      z = group_sum<G>(z);
+      if (need && gl == G - 1) {
+        tr.M[slot] = m;
+        tr.Z[slot] = z;
+      }
+    }
+  }
+}
+
 // Continues the walk at node v, testing the children after child `after`
 // against the residual (c, W).  Thread 0 only.  With `probe` (the row's
 // [N, 3] diagnostics) each tested node's p(d), q(d), r(d) are recorded.
@@ -195,11 +265,13 @@ __device__ __forceinline__ void tree_walk(TreeRow& tr, int N, int V, int v, int 
   const float s = tr.s;
   int n = tr.n;
   for (;;) {
-    const unsigned long long kids = tree_kids(tr.par, N, v);
+    const unsigned long long kids = tr.kids[v];
     if (tr.greedy) {
       int nxt = -1;
-      for (int x = 1; x < N; ++x)
-        if ((kids >> x & 1ull) && tr.tok[x] == tr.idx[v]) { nxt = x; break; }
+      for (unsigned long long m = kids; m; m &= m - 1) {
+        const int x = (int)__builtin_ctzll(m);
+        if (tr.tok[x] == tr.idx[v]) { nxt = x; break; }
+      }
       if (nxt < 0) { tr.status = W_GREEDY; tr.v = v; tr.x = tr.idx[v]; break; }
       tr.path[n++] = nxt;
       v = nxt;
@@ -208,8 +280,10 @@ __device__ __forceinline__ void tree_walk(TreeRow& tr, int N, int V, int v, int 
     if (kids == 0) { tr.status = W_LEAF; tr.v = v; break; }
     const float MSt = mul_rn(tr.M[v], s), MSq = mul_rn(tr.M[N + v], s);
     int acc = -1, rej = -1;
-    for (int x = after + 1; x < N; ++x) {
-      if (!(kids >> x & 1ull)) continue;
+    // The next child after `after` (children are tested in node order).
+    const unsigned long long rest = after >= 63 ? 0ull : kids & ~((2ull << after) - 1ull);
+    if (rest) {
+      const int x = (int)__builtin_ctzll(rest);
       const int d = tr.tok[x];
       float pd = 0.f, qd = 0.f;
       if (d >= 0 && d < V) {
@@ -222,9 +296,8 @@ __device__ __forceinline__ void tree_walk(TreeRow& tr, int N, int V, int v, int 
         probe[x * 3 + 1] = qd;
         probe[x * 3 + 2] = rd;
       }
-      if (tr.u[x] * qd < rd) { acc = x; break; }
-      rej = x;
-      break;  // a rejection needs the next residual's mass first
+      if (tr.u[x] * qd < rd) acc = x;
+      else rej = x;  // a rejection needs the next residual's mass first
     }
     if (acc >= 0) {
       tr.path[n++] = acc;
@@ -405,81 +478,63 @@ __device__ __forceinline__ void tree_chunk_residual(const TreeArgs& a, const Tre
 }
 
 // ============================================================================
-// One round of the tree walk: one work-group per (row, chunk).
+// The tree walk: one work-group per (row, chunk), one launch.
+//
+// Every work-group of a row merges the row's statistics and walks the tree
+// up to the first rejection.  The residual passes that follow are split into
+// tickets, pass = ticket / C and chunk = ticket % C, handed out by an atomic
+// counter to the row's work-groups in the order they ask.  A work-group
+// computes the chunk of a ticket of the current pass and publishes its 32
+// sums; holding a ticket of a later pass, it waits for the current pass's
+// sums, which it may do because every chunk of that pass has been handed out
+// to a running work-group, and continues the walk with them.  All of a row's
+// work-groups thus walk the same way.  The holder of the first ticket past
+// the last pass draws the final token; the last work-group of the row to
+// finish clears the row's tickets and published sums for the next call.
 // ============================================================================
 template <typename ET, bool ALIGNED>
 __global__ __launch_bounds__(WG) void tree_finish_kernel(TreeArgs a) {
   extern __shared__ __align__(16) uint32_t tcache[];  // [2N * C * 4] partial words, then [C * NSUB] residual sums
   __shared__ TreeRow tr;
   __shared__ float shsub[NSUB];
-  __shared__ int sh_last;
-  __shared__ int s_phase;
+  __shared__ unsigned s_ticket;
+  __shared__ float s_W;
   const int N = a.N, C = a.C;
   const int c = blockIdx.x % C, b = blockIdx.x / C;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   uint32_t* pw = tcache;
   float* csub = reinterpret_cast<float*>(tcache + (size_t)2 * N * C * 4);
-  TreeState* st = a.state + b;
-  if (a.round > 0) {
-    if (t == 0) s_phase = st->phase;
-    __syncthreads();
-    if (s_phase != 0) return;
-  }
+  float* probe = (c == 0 && a.probes) ? a.probes + (size_t)b * 3 * N : nullptr;
   // The row's partials and scalars in one round of loads.
   const u32x4* src = reinterpret_cast<const u32x4*>(tree_part(a, b, 0, 0));
   for (int i = t; i < 2 * N * C; i += WG) reinterpret_cast<u32x4*>(pw)[i] = src[i];
+  int p = -1;
   if (t < N) {
     const size_t i = (size_t)b * N + t;
-    tr.par[t] = t == 0 ? -1 : a.par[i];
     tr.tok[t] = t == 0 ? -1 : a.tok[i];
     tr.u[t] = a.uni[i];
     tr.gt[t] = a.gath[i * 2];
     tr.gq[t] = a.gath[i * 2 + 1];
+    if (t > 0) p = a.par[i];
   }
+  if (t < MAX_NODES) tr.kids[t] = 0ull;
   const float T = a.temp[b];
   const bool greedy = !is_sampling_temperature(T);
   __syncthreads();
+  // Children masks: node t sets its bit in its parent's mask.
+  if (p >= 0 && p < t) atomicOr(&tr.kids[p], 1ull << t);
+  __syncthreads();
   // Merge each node's chunk statistics (draft slots only where they exist).
   const float s = greedy ? 0.f : LOG2E / T;
-  for (int slot = wave; slot < 2 * N; slot += NWAVE) {
-    const int node = slot % N;
-    const bool need = slot < N || (!greedy && tree_kids(tr.par, N, node) != 0);
-    if (!need) continue;  // wave-uniform
-    auto word = [&](int cc, int w) { return __uint_as_float(pw[((size_t)slot * C + cc) * 4 + w]); };
-    if (greedy) {
-      float bv = NEG_INF;
-      int bi = INT_MAX;
-      for (int cc = lane; cc < C; cc += 64) argmax_merge(bv, bi, word(cc, 0), __float_as_int(word(cc, 2)));
-      wave_argmax(bv, bi);
-      if (lane == 0) { tr.M[slot] = bv; tr.Z[slot] = 0.f; tr.idx[node] = bi; }
-    } else {
-      float m = NEG_INF;
-      for (int cc = lane; cc < C; cc += 64) m = fmaxf(m, word(cc, 0));
-      m = wave_max(m);
-      const float MS = mul_rn(m, s);
-      float z = 0.f;
-      for (int cc = lane; cc < C; cc += 64) {
-        const float mc = word(cc, 0), zc = word(cc, 1);
-        if (mc != NEG_INF) z += zc * exp2_fast(mul_rn(mc, s) - MS);
-      }
-      z = wave_sum(z);
-      if (lane == 0) { tr.M[slot] = m; tr.Z[slot] = z; }
-    }
-  }
+  if (C <= 16) tree_merge<16>(tr, pw, N, C, greedy, s);
+  else if (C <= 32) tree_merge<32>(tr, pw, N, C, greedy, s);
+  else tree_merge<64>(tr, pw, N, C, greedy, s);
+  __syncthreads();
   if (t == 0) {
     tr.s = s;
     tr.greedy = greedy ? 1 : 0;
-    if (a.round == 0) {
-      tr.n = 0;
-      tree_walk(tr, N, a.V, 0, 0, 0.f, 1.f, (c == 0 && a.probes) ? a.probes + (size_t)b * 3 * N : nullptr);
-    } else {
-      tr.n = st->n;
-      for (int i = 0; i < tr.n; ++i) tr.path[i] = st->path[i];
-      tr.status = W_PASS;
-      tr.v = st->v;
-      tr.j = st->j;
-      tr.c = st->c;
-    }
+    tr.n = 0;
+    tree_walk(tr, N, a.V, 0, 0, 0.f, 1.f, probe);
   }
   __syncthreads();
   auto emit = [&](int x, float S) {  // wave 0
@@ -492,7 +547,6 @@ __global__ __launch_bounds__(WG) void tree_finish_kernel(TreeArgs a) {
     if (lane == 0) {
       a.nacc[b] = tr.n;
       if (a.mass) a.mass[b] = S;
-      st->phase = 1;
     }
   };
   if (tr.status != W_PASS) {
@@ -505,34 +559,31 @@ __global__ __launch_bounds__(WG) void tree_finish_kernel(TreeArgs a) {
     emit(x, S);
     return;
   }
-  // The pending residual pass, split over the row's work-groups.
-  tree_chunk_residual<ET, ALIGNED>(a, tr, b, tr.v, tr.c, c, shsub);
-  uint32_t* subR_row = a.subR + (size_t)b * C * NSUB;
-  if (t < NSUB) pub_f32(subR_row + (size_t)c * NSUB + t, shsub[t]);
-  if (t == 0)
-    sh_last = __hip_atomic_fetch_add(a.cnt + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)C - 1u;
-  __syncthreads();
-  if (!sh_last) return;
-  const bool ok = wait_words(subR_row, C * NSUB, reinterpret_cast<uint32_t*>(csub), nullptr, 0, nullptr,
-                             wall_clock64() + WAIT_TICKS);
-  for (int i = t; i < C * NSUB; i += WG) clear_word(subR_row + i);
-  if (t == 0) __hip_atomic_store(a.cnt + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (!ok) {
-    if (t <= N) {
-      if (t < N) {
-        a.out[(size_t)b * N + t] = -1;
-        a.onodes[(size_t)b * N + t] = -1;
-      }
-      if (t == 0) {
-        a.nacc[b] = -1;
-        st->phase = 1;
-      }
-    }
-    return;
-  }
-  __shared__ float s_W;
+  // Residual passes.
+  uint32_t* subR_row = a.subR + (size_t)b * N * C * NSUB;
+  constexpr unsigned NONE = 0xFFFFFFFFu;
+  int pass = 0;            // passes applied to the walk so far
+  unsigned ticket = NONE;  // held ticket
+  bool ok = true;
   for (;;) {
-    // csub holds the sums of the pass at (tr.v, tr.c): its total is W.
+    if (ticket == NONE) {
+      if (t == 0) s_ticket = __hip_atomic_fetch_add(a.claim + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      ticket = s_ticket;
+    }
+    const int tp = (int)(ticket / (unsigned)C);
+    if (tp == pass) {
+      // A chunk of the current pass: its sums of max(0, p_v - c q_v).
+      const int tc = (int)(ticket % (unsigned)C);
+      tree_chunk_residual<ET, ALIGNED>(a, tr, b, tr.v, tr.c, tc, shsub);
+      if (t < NSUB) pub_f32(subR_row + ((size_t)pass * C + tc) * NSUB + t, shsub[t]);
+      ticket = NONE;
+      continue;
+    }
+    // Every chunk of the current pass has been handed out: collect its sums.
+    ok = wait_words(subR_row + (size_t)pass * C * NSUB, C * NSUB, reinterpret_cast<uint32_t*>(csub), nullptr, 0,
+                    nullptr, wall_clock64() + WAIT_TICKS);
+    if (!ok) break;
     if (wave == 0) {
       float S;
       tree_draw<ET, ALIGNED>(a, tr, pw, csub, b, tr.v, W_RESID, tr.c, -1.f, &S);
@@ -540,32 +591,37 @@ __global__ __launch_bounds__(WG) void tree_finish_kernel(TreeArgs a) {
     }
     __syncthreads();
     if (t == 0) {
-      const float W = s_W;
-      if (W == 0.f) {  // only through rounding: draw from the node's target
+      if (s_W == 0.f)  // only through rounding: draw from the node's target
         tr.status = W_FALLBACK;
-      } else {
-        tree_walk(tr, N, a.V, tr.v, tr.j, tr.c, W, a.probes ? a.probes + (size_t)b * 3 * N : nullptr);
-      }
+      else
+        tree_walk(tr, N, a.V, tr.v, tr.j, tr.c, s_W, probe);
     }
     __syncthreads();
+    ++pass;
     if (tr.status != W_PASS) break;
-    if (a.round < a.last_round) {
-      // Leave the next pass to the next round.
-      if (t == 0) {
-        st->phase = 0;
-        st->v = tr.v;
-        st->j = tr.j;
-        st->c = tr.c;
-        st->n = tr.n;
-      }
-      for (int i = t; i < tr.n; i += WG) st->path[i] = tr.path[i];
-      return;
-    }
-    // Last round: this work-group runs the pass over every chunk alone.
-    for (int cc = 0; cc < C; ++cc) tree_chunk_residual<ET, ALIGNED>(a, tr, b, tr.v, tr.c, cc, csub + cc * NSUB);
   }
-  if (wave != 0) return;
-  float S;
-  const int x = tree_draw<ET, ALIGNED>(a, tr, pw, csub, b, tr.v, tr.status, tr.c, tr.u[0], &S);
-  emit(x, S);
+  if (!ok) {
+    // Reached only if a wait ran past its deadline: num_accepted = -1 marks it.
+    for (int i = t; i < N; i += WG) {
+      a.out[(size_t)b * N + i] = -1;
+      a.onodes[(size_t)b * N + i] = -1;
+    }
+    if (t == 0) a.nacc[b] = -1;
+  } else if (ticket == (unsigned)pass * (unsigned)C && wave == 0) {
+    float S;
+    const int x = tree_draw<ET, ALIGNED>(a, tr, pw, csub, b, tr.v, tr.status, tr.c, tr.u[0], &S);
+    emit(x, S);
+  }
+  // The last work-group of the row to finish clears its tickets and sums.
+  __syncthreads();
+  if (t == 0)
+    s_ticket = __hip_atomic_fetch_add(a.leave + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)C - 1u;
+  __syncthreads();
+  if (!s_ticket) return;
+  const int used = ok ? pass : N;
+  for (int i = t; i < used * C * NSUB; i += WG) clear_word(subR_row + i);
+  if (t == 0) {
+    __hip_atomic_store(a.claim + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.leave + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }

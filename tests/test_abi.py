@@ -143,14 +143,14 @@ def test_kl_argument_errors_without_launch():
     assert call(0, None) == B.SV_ERR_ARG             # no output for the KL values
 
 
-def _tree_call(lib, B_=4, N=7, V=1000, topk=0, dtype=B.SV_BF16, rounds=2, ptrs=True, ws=None, ws_n=None,
+def _tree_call(lib, B_=4, N=7, V=1000, topk=0, dtype=B.SV_BF16, ptrs=True, ws=None, ws_n=None,
                events=None, n_events=0):
     p = ctypes.c_void_p(0x100000) if ptrs else None
     n = None if ws_n is None else ctypes.byref(ctypes.c_size_t(ws_n))
     if events is not None:
-        return lib.spec_verify_tree_timed(p, p, p, p, p, p, B_, N, V, topk, dtype, rounds, p, p, p, ws, n, None,
+        return lib.spec_verify_tree_timed(p, p, p, p, p, p, B_, N, V, topk, dtype, p, p, p, ws, n, None,
                                           events, n_events)
-    return lib.spec_verify_tree(p, p, p, p, p, p, B_, N, V, topk, dtype, rounds, p, p, p, ws, n, None, None, None)
+    return lib.spec_verify_tree(p, p, p, p, p, p, B_, N, V, topk, dtype, p, p, p, ws, n, None, None, None)
 
 
 def test_tree_argument_errors_without_launch():
@@ -163,8 +163,6 @@ def test_tree_argument_errors_without_launch():
     assert _tree_call(lib, N=0, ws=ws, ws_n=need) == B.SV_ERR_ARG
     assert _tree_call(lib, V=0, ws=ws, ws_n=need) == B.SV_ERR_ARG
     assert _tree_call(lib, dtype=9, ws=ws, ws_n=need) == B.SV_ERR_ARG
-    assert _tree_call(lib, rounds=0, ws=ws, ws_n=need) == B.SV_ERR_ARG
-    assert _tree_call(lib, rounds=B.SV_MAX_NODES + 1, ws=ws, ws_n=need) == B.SV_ERR_ARG
     assert _tree_call(lib, topk=-1, ws=ws, ws_n=need) == B.SV_ERR_ARG
     assert _tree_call(lib, ws=ws, ws_n=None) == B.SV_ERR_ARG
     assert _tree_call(lib, ws=ws, ws_n=need - 1) == B.SV_ERR_WORKSPACE
@@ -186,5 +184,5 @@ def test_tree_single_node_needs_no_tree_inputs():
     p = ctypes.c_void_p(0x100000)
     n = ctypes.c_size_t(need - 1)
     # N == 1: draft logits, tokens and parents may be NULL (only the size check fails here)
-    assert lib.spec_verify_tree(p, None, None, None, p, p, 2, 1, 500, 0, B.SV_F32, 1, p, p, p,
+    assert lib.spec_verify_tree(p, None, None, None, p, p, 2, 1, 500, 0, B.SV_F32, p, p, p,
                                 ctypes.c_void_p(0x200000), ctypes.byref(n), None, None, None) == B.SV_ERR_WORKSPACE
