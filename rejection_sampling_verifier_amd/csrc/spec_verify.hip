@@ -73,7 +73,6 @@ constexpr int MAX_C = 2048;                // vocabulary chunks per position
 constexpr int MAX_SLOTS = 2 * SV_MAX_K + 1;
 constexpr int MAX_CACHE_WORDS = 8192;       // dynamic LDS for a row's published words (32 KiB)
 constexpr int TOPK_FAST_MAX = WG;          // sparse drafts: fast chunk selection for k <= 256
-constexpr int CAND_CAP = SV_MAX_TOPK;      // LDS buffer of the exact chunk selection
 constexpr int WCAP = 256;                  // candidate list length per wave of a chunk
 // Longest wait for another work-group's results: 100 ms of the 100 MHz
 // constant clock.  Every wait ends well before that in a correct launch; the
@@ -234,9 +233,9 @@ struct Staged<float> {
 // Exact selection by a 32-step binary search on order keys: the largest key
 // tau with at least kk logits >= tau is the kk-th largest; logits above tau
 // are all kept, ties at tau are kept in increasing id order.  The kk kept
-// composites are left in buf[0..kk).
+// composites are written to dst[0..kk).
 template <typename ET>
-__device__ void topk_chunk_exact(const u32x4 (&r)[NV_TILE], int lo, int len, int kk, uint64_t* buf,
+__device__ void topk_chunk_exact(const u32x4 (&r)[NV_TILE], int lo, int len, int kk, uint64_t* dst,
                                  float* red) {
   constexpr int VEC = Tr<ET>::VEC;
   __shared__ int s_pos;
@@ -265,7 +264,7 @@ __device__ void topk_chunk_exact(const u32x4 (&r)[NV_TILE], int lo, int len, int
     for (int e = 0; e < VEC; ++e) {
       const float x = Tr<ET>::at(r[j], e);
       const int off = (j * WG + t) * VEC + e;
-      if (off < len && order_key(x) > tau) buf[atomicAdd(&s_pos, 1)] = composite(x, lo + off);
+      if (off < len && order_key(x) > tau) dst[atomicAdd(&s_pos, 1)] = composite(x, lo + off);
     }
   const int need = kk - above;
   float carry = 0.f;
@@ -281,7 +280,7 @@ __device__ void topk_chunk_exact(const u32x4 (&r)[NV_TILE], int lo, int len, int
       const float x = Tr<ET>::at(r[j], e);
       const int off = (j * WG + t) * VEC + e;
       if (off < len && order_key(x) == tau) {
-        if (rank < need) buf[above + rank] = composite(x, lo + off);
+        if (rank < need) dst[above + rank] = composite(x, lo + off);
         ++rank;
       }
     }
@@ -297,16 +296,19 @@ __device__ void topk_chunk_exact(const u32x4 (&r)[NV_TILE], int lo, int len, int
 // the upper 16 bits of their order keys; the smallest of the four bounds is
 // a lower bound of the chunk's k-th largest logit (each wave has ceil(k/4)
 // logits at or above it), so every logit of the chunk's top k passes it.
-// Each wave appends the logits that pass to its list with ballots.  The lists
-// are unsorted; the merge kernel selects exactly.  Exact path (k > 256, or a
-// list over WCAP): the chunk's exact top min(k, len) is stored contiguously
-// across the four list areas.
+// Each wave lists the logits that pass.  The lists are unsorted; the merge
+// kernel selects exactly.  Exact path (k > 256, or a list over WCAP): the
+// chunk's exact top min(k, len) is stored contiguously across the four list
+// areas.
 template <typename ET>
 __device__ void topk_chunk(const u32x4 (&r)[NV_TILE], int lo, int len, int k, typename Cand<ET>::T* dst,
                            int* cnts, float* red) {
   constexpr int VEC = Tr<ET>::VEC;
+  constexpr int NE = NV_TILE * VEC;  // logits per thread: 64 (bf16) or 32 (fp32)
   using CT = typename Cand<ET>::T;
-  __shared__ uint64_t cbuf[CAND_CAP];  // exact path: composites; fast path: the waves' staged lists
+  using ST = typename Staged<ET>::T;
+  // Fast path: each wave's list of passing logits, staged as (bits, offset).
+  __shared__ uint64_t sbuf[NWAVE * WCAP];
   __shared__ uint32_t wkey[NWAVE];
   __shared__ int s_over;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -327,45 +329,61 @@ __device__ void topk_chunk(const u32x4 (&r)[NV_TILE], int lo, int len, int k, ty
     // bucket of -inf reads back as a NaN pattern, which must become -inf.
     float bound = key_value(min(min(wkey[0], wkey[1]), min(wkey[2], wkey[3])));
     if (bound != bound) bound = NEG_INF;
-    // Passing logits are staged in LDS (a wave's stores there cost little
-    // however sparse its lanes are) and written out as whole lists below.
-    // Two logits per ballot round; the order of a list does not matter.
-    // Positions wrap inside the wave's staging area: a list that overflows
-    // it is discarded below, so its clobbered entries are never read.
-    // Padding past the chunk reads as -inf, so it can only pass a bound of
-    // -inf, the one case that needs the explicit range check.
-    using ST = typename Staged<ET>::T;
-    ST* stage = reinterpret_cast<ST*>(cbuf) + wave * WCAP;
-    int n = 0;  // wave-uniform
-    auto below = [](unsigned long long m) {
-      return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-    };
-    auto compact = [&](auto check) {
+    // Each thread marks its passing logits in bit masks, logit i of the
+    // thread at bit 31 - (i % 32) of mask i / 32; padding past the chunk
+    // reads as -inf, so it can pass only a bound of -inf, the one case that
+    // needs the range check.
+    uint32_t mask[NE / 32];
+    auto mark = [&](auto check) {
+#pragma unroll
+      for (int h = 0; h < NE / 32; ++h) mask[h] = 0u;
 #pragma unroll
       for (int j = 0; j < NV_TILE; ++j)
 #pragma unroll
-        for (int e = 0; e < VEC; e += 2) {
-          const float xa = Tr<ET>::at(r[j], e), xb = Tr<ET>::at(r[j], e + 1);
-          const int off = (j * WG + t) * VEC + e;
-          bool pa = xa >= bound, pb = xb >= bound;
-          if (decltype(check)::value) {
-            pa = pa && off < len;
-            pb = pb && off + 1 < len;
-          }
-          const unsigned long long ma = __ballot(pa), mb = __ballot(pb);
-          if (ma | mb) {
-            const int na = __popcll(ma);
-            if (pa) stage[(n + below(ma)) & (WCAP - 1)] = Staged<ET>::pack(xa, off);
-            if (pb) stage[(n + na + below(mb)) & (WCAP - 1)] = Staged<ET>::pack(xb, off + 1);
-            n += na + __popcll(mb);
-          }
+        for (int e = 0; e < VEC; ++e) {
+          const int i = j * VEC + e;
+          bool pass = Tr<ET>::at(r[j], e) >= bound;
+          if (decltype(check)::value) pass = pass && (j * WG + t) * VEC + e < len;
+          mask[i / 32] = mask[i / 32] + mask[i / 32] + (pass ? 1u : 0u);
         }
     };
-    static_assert((WCAP & (WCAP - 1)) == 0, "wrap-around staging");
     if (bound > NEG_INF)
-      compact(std::false_type{});
+      mark(std::false_type{});
     else
-      compact(std::true_type{});
+      mark(std::true_type{});
+    int cnt = 0;
+#pragma unroll
+    for (int h = 0; h < NE / 32; ++h) cnt += __popc(mask[h]);
+    // The wave's list: thread order, then logit order within a thread.
+    // Positions wrap inside the wave's staging area: a list that overflows
+    // it is discarded below, so its clobbered entries are never read.
+    const float incl = wave_incl_scan((float)cnt);  // exact: at most 4096
+    const int n = (int)lane63(incl);
+    int pos = (int)incl - cnt;
+    ST* wl_stage = reinterpret_cast<ST*>(sbuf) + wave * WCAP;
+#pragma unroll
+    for (int j = 0; j < NV_TILE; ++j) {
+      // Vector j's logits e = 0..VEC-1 sit at bits VEC-1-e of mj.
+      constexpr unsigned VMASK = (1u << VEC) - 1u;
+      uint32_t mj = (mask[(j * VEC) / 32] >> (32 - VEC - (j * VEC) % 32)) & VMASK;
+      while (mj) {
+        const int bp = 31 - __builtin_clz(mj);
+        mj &= ~(1u << bp);
+        const int e = VEC - 1 - bp;
+        const int wi = e / (VEC / 4);
+        uint32_t word = r[j][0];
+        word = wi == 1 ? r[j][1] : word;
+        word = wi == 2 ? r[j][2] : word;
+        word = wi == 3 ? r[j][3] : word;
+        float x;
+        if constexpr (VEC == 8)
+          x = __uint_as_float((e & 1) ? (word & 0xFFFF0000u) : (word << 16));
+        else
+          x = __uint_as_float(word);
+        wl_stage[pos & (WCAP - 1)] = Staged<ET>::pack(x, (j * WG + t) * VEC + e);
+        ++pos;
+      }
+    }
     if (lane == 0) {
       cnts[wave] = min(n, WCAP);
       if (n > WCAP) s_over = 1;
@@ -374,13 +392,12 @@ __device__ void topk_chunk(const u32x4 (&r)[NV_TILE], int lo, int len, int k, ty
     done = s_over == 0;
     if (done) {
       CT* wl = dst + wave * WCAP;
-      for (int i = lane; i < n; i += 64) wl[i] = Staged<ET>::composite_at(stage[i], lo);
+      for (int q = lane; q < n; q += 64) wl[q] = Staged<ET>::composite_at(wl_stage[q], lo);
     }
   }
   if (!done) {
-    __syncthreads();  // the staged lists are no longer read
-    topk_chunk_exact<ET>(r, lo, len, kk, cbuf, red);
-    for (int i = t; i < kk; i += WG) dst[i] = cbuf[i];
+    __syncthreads();  // the fast path's lists are no longer read
+    topk_chunk_exact<ET>(r, lo, len, kk, dst, red);
     if (t < NWAVE) cnts[t] = max(0, min(WCAP, kk - t * WCAP));
   }
 }

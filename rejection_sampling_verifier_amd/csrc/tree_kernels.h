@@ -77,6 +77,13 @@ void tree_stats_kernel(TreeArgs a) {
   __shared__ float shf[NWAVE];
   __shared__ int shi[NWAVE];
   __shared__ float shsub[NSUB];
+  const ET* row = tree_row<ET>(a, is_draft, b, node);
+  const int lo = c * a.CS;
+  const int len = min(a.CS, a.V - lo);
+  // A target slot issues its loads before it needs the tree; a draft slot
+  // first checks that its node has children (and that the row samples).
+  u32x4 r[NV_TILE];
+  if (!is_draft) load_tile<ET, ALIGNED, NV_TILE>(row, lo, len, r);
   if (wave == 0) {
     const int p = (lane > 0 && lane < N) ? a.par[(size_t)b * N + lane] : -1;
     const unsigned long long m = __ballot(lane > node && lane < N && p == node);
@@ -88,12 +95,10 @@ void tree_stats_kernel(TreeArgs a) {
   __syncthreads();
   const unsigned long long kids = s_kids;
   const bool greedy = !is_sampling_temperature(T);
-  if (is_draft && (greedy || kids == 0)) return;  // no children drawn from this draft (or greedy)
-  const ET* row = tree_row<ET>(a, is_draft, b, node);
-  const int lo = c * a.CS;
-  const int len = min(a.CS, a.V - lo);
-  u32x4 r[NV_TILE];
-  load_tile<ET, ALIGNED, NV_TILE>(row, lo, len, r);
+  if (is_draft) {
+    if (greedy || kids == 0) return;  // no children drawn from this draft (or a greedy row)
+    load_tile<ET, ALIGNED, NV_TILE>(row, lo, len, r);
+  }
   uint32_t* dst = tree_part(a, b, slot, c);
   if (greedy) {
     float bv = Tr<ET>::at(r[0], 0);
