@@ -122,6 +122,8 @@ def main():
     ap.add_argument("--kl", action="store_true",
                     help="time spec_verify_kl (verification plus KL(p||q) per position; whole-call "
                          "rate only)")
+    ap.add_argument("--early-exit", action="store_true",
+                    help="time spec_verify_early_exit (reads each row's logits up to its first rejection)")
     ap.add_argument("--tree", type=int, default=-1,
                     help="time spec_verify_tree on this draft-tree workload instead (0 = 61-node tree)")
     ap.add_argument("--relaxed", default="",
@@ -176,9 +178,15 @@ def main():
         rule = dict(alpha=float(a_), max_rank=int(r_), min_prob=float(p_))
 
     kl_buf = torch.empty((B, K), dtype=torch.float32, device=dev) if args.kl else None
+    ee_ws = rsv.new_early_exit_workspace(B, K, V, dt_code, dev) if args.early_exit else None
 
     def step(i, timer=None):
         x = sets[i % copies]
+        if args.early_exit and timer is None:
+            rsv.verify_early_exit(x["target"], x["draft"], x["tokens"], x["uniforms"], x["temperature"],
+                                  d["topk"], out_tokens=out, num_accepted=nacc, workspace=ee_ws,
+                                  stream=stream.cuda_stream)
+            return
         if args.kl and timer is None:
             rsv.verify_kl(x["target"], x["draft"], x["tokens"], x["uniforms"], x["temperature"], d["topk"],
                           out_tokens=out, num_accepted=nacc, kl=kl_buf, workspace=ws, stream=stream.cuda_stream)
@@ -227,6 +235,17 @@ def main():
     positions = B * K
     value = positions / (ms_per_step * 1e-3)
     achieved = by["stats_kernel"] / (stats_ms * 1e-3) / 1e9
+    roof_kernel, roof_bytes, roof_ms = "stats_kernel", by["stats_kernel"], stats_ms
+    if args.early_exit:
+        # One kernel per call: its algorithmic bytes are the logits of the
+        # positions each row reaches (targets 0..n, drafts 0..min(n, K-1) of
+        # sampling rows); the residual re-read is extra traffic.
+        n_acc = nacc.cpu().numpy().astype(np.int64)
+        esz = d["target"].itemsize
+        samp = d["temperature"] > 0
+        rows = np.minimum(n_acc + 1, K + 1) + np.where(samp, np.minimum(n_acc + 1, K), 0)
+        roof_kernel, roof_bytes, roof_ms = "early_exit_kernel", int(rows.sum()) * V * esz, ms_per_step
+        achieved = roof_bytes / (roof_ms * 1e-3) / 1e9
     traffic = traffic_from_profiles(case.name.split("-T")[0] if False else f"B{B}K{K}V{V}")
     line = {
         "metric": METRIC,
@@ -245,11 +264,11 @@ def main():
                    "temperature": float(case.temperature), "greedy_rows": case.greedy_rows,
                    "topk_draft": case.topk, "input_copies": copies,
                    "acceptance": "lossless" if rule is None else f"relaxed {rule}",
-                   "kl_per_position": bool(args.kl)},
+                   "kl_per_position": bool(args.kl), "early_exit": bool(args.early_exit)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "kernel": "stats_kernel",
-                     "bytes_per_launch": by["stats_kernel"], "avg_launch_ms": round(stats_ms, 5)},
+                     "traffic": None if args.early_exit else traffic, "kernel": roof_kernel,
+                     "bytes_per_launch": roof_bytes, "avg_launch_ms": round(roof_ms, 5)},
         "effective_GBps_whole_call": round(by["m_min"] / (ms_per_step * 1e-3) / 1e9, 1),
         "m_min_bytes": by["m_min"],
         "kernel_ms": {"stats_kernel": round(float(stage_ms[0]), 5),

@@ -32,8 +32,8 @@
  * All pointers are device pointers owned by the caller.  Inputs are read
  * only; outputs are fully overwritten.  The library allocates nothing, keeps
  * no mutable global state and never synchronises: every call only enqueues
- * two kernels on `stream` (three with a sparse draft); outputs are valid
- * once the caller has synchronised that stream.  Calls on different
+ * at most three kernels on `stream`; outputs are valid once the caller has
+ * synchronised that stream.  Calls on different
  * workspaces are reentrant.
  */
 #ifndef SPEC_VERIFY_H
@@ -193,6 +193,38 @@ int spec_verify_kl(const void* target_logits, const void* draft_logits,
                    int topk_draft, int dtype, int32_t* out_tokens,
                    int32_t* num_accepted, void* workspace,
                    size_t* workspace_bytes, hipStream_t stream, float* kl_out);
+
+/*
+ * spec_verify_early_exit - spec_verify that verifies the positions of a row
+ * one after the other and stops reading its logits at the first rejection:
+ * no later draft can be committed ("Speculative decoding: memverifikasi
+ * token draft sebelum diterima", subsection "Penolakan memendekkan pekerjaan
+ * speculative yang berguna").  A row that rejects at position n reads the
+ * target and draft logits of positions 0..n only (plus the residual pass of
+ * position n), instead of all 2K+1 positions; in exchange its positions are
+ * verified in sequence rather than in parallel.  Tokens, counts, the
+ * probabilities p_i(d_i), q_i(d_i) and the final mass equal spec_verify's
+ * bit for bit.
+ *
+ * One kernel per call.  A dense draft only: 0 < topk_draft < V is
+ * SV_ERR_UNSUPPORTED, and so is a shape whose row statistics
+ * ((2K+1) C 16 + C 128 bytes) do not fit the kernel's LDS.
+ * The workspace has its own size (query with workspace == NULL) and must
+ * not be shared with the other entry points: this call keeps it zero between
+ * calls and relies on that.
+ * probs_out  [B, K, 2] float32 device or NULL: (p_i(d_i), q_i(d_i)) of every
+ *            position the row tested, NaN past its first rejection (and for
+ *            greedy rows).
+ * mass_out   [B] float32 device or NULL: as spec_verify_probe.
+ * Other arguments and return codes as spec_verify.
+ */
+int spec_verify_early_exit(const void* target_logits, const void* draft_logits,
+                           const int32_t* draft_tokens, const float* uniforms,
+                           const float* temperature, int B, int K, int V,
+                           int topk_draft, int dtype, int32_t* out_tokens,
+                           int32_t* num_accepted, void* workspace,
+                           size_t* workspace_bytes, hipStream_t stream,
+                           float* probs_out, float* mass_out);
 
 /*
  * spec_verify_tree - verify B rows of draft trees against one target pass

@@ -15,12 +15,15 @@ from .binding import (  # noqa: F401
     SpecVerifyError,
     StageTimer,
     TreeTimer,
+    early_exit_workspace_bytes,
     load_library,
+    new_early_exit_workspace,
     new_tree_workspace,
     new_workspace,
     plan,
     tree_workspace_bytes,
     verify,
+    verify_early_exit,
     verify_kl,
     verify_probe,
     verify_relaxed,

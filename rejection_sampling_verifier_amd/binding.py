@@ -67,6 +67,8 @@ def load_library(path: str | None = None):
     lib.spec_verify_kl.restype = _i32
     lib.spec_verify_timed.argtypes = _COMMON + [ctypes.POINTER(_vp), _i32]
     lib.spec_verify_timed.restype = _i32
+    lib.spec_verify_early_exit.argtypes = _COMMON + [_vp, _vp]
+    lib.spec_verify_early_exit.restype = _i32
     _tree = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]
     lib.spec_verify_tree.argtypes = _tree + [_vp, _vp]
     lib.spec_verify_tree.restype = _i32
@@ -142,7 +144,6 @@ def _prepare(target, draft, draft_tokens, uniforms, temperature, topk_draft, out
         out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
     if num_accepted is None:
         num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
-    nbytes = workspace_bytes(B, K, V, topk_draft, dt)
     if workspace is None:
         workspace = new_workspace(B, K, V, topk_draft, dt, dev)
     if stream is None:
@@ -216,6 +217,44 @@ def verify_kl(target, draft, draft_tokens, uniforms, temperature, topk_draft: in
         kl = torch.empty((B, Kp1 - 1), dtype=torch.float32, device=target.device)
     _check(load_library().spec_verify_kl(*args, _ptr(kl)))
     return out_tokens, num_accepted, kl
+
+
+def early_exit_workspace_bytes(B: int, K: int, V: int, dtype: int = SV_BF16) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().spec_verify_early_exit(None, None, None, None, None, B, K, V, 0, dtype, None, None,
+                                                 None, ctypes.byref(n), None, None, None))
+    return n.value
+
+
+def new_early_exit_workspace(B: int, K: int, V: int, dtype: int = SV_BF16, device="cuda"):
+    """A zero-filled workspace for spec_verify_early_exit at this shape (its
+    own: not to be shared with the other calls)."""
+    n = early_exit_workspace_bytes(B, K, V, dtype)
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def verify_early_exit(target, draft, draft_tokens, uniforms, temperature, topk_draft: int = 0, *,
+                      probes: bool = False, out_tokens=None, num_accepted=None, workspace=None, stream=None):
+    """spec_verify_early_exit: the same results as ``verify``, reading each
+    row's logits only up to its first rejection.
+
+    Returns (out_tokens, num_accepted), plus (probs [B, K, 2], mass [B]) when
+    ``probes`` is set (probabilities past a row's first rejection are NaN).
+    """
+    if workspace is None and target.dim() == 3:
+        B, Kp1, V = target.shape
+        workspace = new_early_exit_workspace(B, Kp1 - 1, V, _dtype_code(target), target.device)
+    args, out_tokens, num_accepted, _ = _prepare(target, draft, draft_tokens, uniforms, temperature,
+                                                 topk_draft, out_tokens, num_accepted, workspace, stream)
+    probs = mass = None
+    if probes:
+        B, Kp1 = out_tokens.shape
+        probs = torch.empty((B, Kp1 - 1, 2), dtype=torch.float32, device=target.device)
+        mass = torch.empty((B,), dtype=torch.float32, device=target.device)
+    _check(load_library().spec_verify_early_exit(*args, _ptr(probs), _ptr(mass)))
+    if probes:
+        return out_tokens, num_accepted, probs, mass
+    return out_tokens, num_accepted
 
 
 def tree_workspace_bytes(B: int, N: int, V: int, dtype: int = SV_BF16) -> int:

@@ -103,6 +103,8 @@ struct Args {
   int relaxed, max_rank;
   float alpha, min_prob;
   float* kl;                 // [B, K] KL(p_i || q_i) out (spec_verify_kl: paired statistics), or null
+  unsigned* claim;           // [B] early exit: stage tickets handed out
+  unsigned* leave;           // [B] early exit: work-groups of the row that have finished
   int GA;                    // statistics work-groups per row: (2K+1) * C
   int cache;                 // 1: finishing work-groups keep the row's words in dynamic LDS
 };
@@ -1599,6 +1601,8 @@ __global__ __launch_bounds__(WG) void finish_kernel(Args a) {
   if (t == 0) __hip_atomic_store(a.cnt + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+#include "early_exit.h"
+
 // ============================================================================
 // Host side.
 // ============================================================================
@@ -1756,6 +1760,80 @@ int run(const void* tgt, const void* dft, const int32_t* tok, const float* uni, 
                  : launch_typed<float, false>(a, pl.lds_bytes, pl.merge_lds, st, e);
 }
 
+// ---- early exit ---------------------------------------------------------------
+constexpr int EE_MAX_LDS_WORDS = 14336;  // the early-exit kernel's dynamic LDS (56 KiB)
+
+struct EEPlan {
+  int C = 0, CS = 0;
+  size_t off_cnt = 0, off_part = 0, off_subK = 0, off_subR = 0, total = 0;
+  size_t lds_bytes = 0;
+};
+
+int make_ee_plan(int B, int K, int V, int dtype, EEPlan& pl) {
+  if (B < 1 || K < 0 || V < 1 || (dtype != SV_BF16 && dtype != SV_F32)) return SV_ERR_ARG;
+  if (K > SV_MAX_K) return SV_ERR_UNSUPPORTED;
+  int C, CS;
+  if (!vocab_split(V, dtype, C, CS)) return SV_ERR_UNSUPPORTED;
+  if ((long long)B * C > INT_MAX) return SV_ERR_UNSUPPORTED;
+  const size_t S = 2 * (size_t)K + 1;
+  const size_t words = S * C * 4 + (size_t)C * NSUB;
+  if (words > (size_t)EE_MAX_LDS_WORDS) return SV_ERR_UNSUPPORTED;
+  pl.C = C;
+  pl.CS = CS;
+  // Every region is zero between calls: the kernel publishes into them and
+  // clears what it used.
+  size_t off = 0;
+  pl.off_cnt = off;  // claim [B], then leave [B]
+  off = align256(off + 2 * sizeof(unsigned) * (size_t)B);
+  pl.off_part = off;
+  off = align256(off + 4 * sizeof(uint32_t) * (size_t)B * S * C);
+  pl.off_subK = off;
+  off = align256(off + sizeof(uint32_t) * (size_t)B * C * NSUB);
+  pl.off_subR = off;
+  off = align256(off + sizeof(uint32_t) * (size_t)B * C * NSUB);
+  pl.total = off;
+  pl.lds_bytes = words * sizeof(uint32_t);
+  return SV_OK;
+}
+
+int run_early_exit(const void* tgt, const void* dft, const int32_t* tok, const float* uni, const float* temp,
+                   int B, int K, int V, int topk, int dtype, int32_t* out, int32_t* nacc, void* ws,
+                   size_t* ws_bytes, hipStream_t st, float* probs, float* mass) {
+  if (!ws_bytes || topk < 0) return SV_ERR_ARG;
+  if (topk >= V) topk = 0;
+  if (topk > 0) return SV_ERR_UNSUPPORTED;
+  EEPlan pl;
+  const int rc = make_ee_plan(B, K, V, dtype, pl);
+  if (rc != SV_OK) return rc;
+  if (!ws) {
+    *ws_bytes = pl.total;
+    return SV_OK;
+  }
+  if (*ws_bytes < pl.total) return SV_ERR_WORKSPACE;
+  if (!tgt || !uni || !temp || !out || !nacc) return SV_ERR_ARG;
+  if (K > 0 && (!dft || !tok)) return SV_ERR_ARG;
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return SV_ERR_ARG;
+  Args a{};
+  a.tgt = tgt; a.dft = dft; a.tok = tok; a.uni = uni; a.temp = temp;
+  a.out = out; a.nacc = nacc; a.probs = probs; a.mass = mass;
+  char* base = static_cast<char*>(ws);
+  a.claim = reinterpret_cast<unsigned*>(base + pl.off_cnt);
+  a.leave = a.claim + B;
+  a.part = reinterpret_cast<uint32_t*>(base + pl.off_part);
+  a.subK = reinterpret_cast<uint32_t*>(base + pl.off_subK);
+  a.subR = reinterpret_cast<uint32_t*>(base + pl.off_subR);
+  a.B = B; a.K = K; a.V = V; a.C = pl.C; a.CS = pl.CS; a.topk = 0;
+  const size_t esz = dtype == SV_BF16 ? 2 : 4;
+  const bool aligned = (reinterpret_cast<uintptr_t>(tgt) % 16 == 0) &&
+                       (K == 0 || reinterpret_cast<uintptr_t>(dft) % 16 == 0) && ((size_t)V * esz) % 16 == 0;
+  (void)hipGetLastError();
+  if (dtype == SV_BF16)
+    return aligned ? launch(early_exit_kernel<uint16_t, true>, B * pl.C, pl.lds_bytes, st, nullptr, a)
+                   : launch(early_exit_kernel<uint16_t, false>, B * pl.C, pl.lds_bytes, st, nullptr, a);
+  return aligned ? launch(early_exit_kernel<float, true>, B * pl.C, pl.lds_bytes, st, nullptr, a)
+                 : launch(early_exit_kernel<float, false>, B * pl.C, pl.lds_bytes, st, nullptr, a);
+}
+
 // ---- draft trees ------------------------------------------------------------
 #include "tree_kernels.h"
 
@@ -1909,6 +1987,14 @@ int spec_verify_kl(const void* target_logits, const void* draft_logits, const in
   return run(target_logits, draft_logits, draft_tokens, uniforms, temperature, B, K, V, topk_draft,
              dtype, out_tokens, num_accepted, workspace, workspace_bytes, stream, nullptr, nullptr,
              nullptr, 0, nullptr, K > 0 ? kl_out : nullptr);
+}
+
+int spec_verify_early_exit(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                           const float* uniforms, const float* temperature, int B, int K, int V, int topk_draft,
+                           int dtype, int32_t* out_tokens, int32_t* num_accepted, void* workspace,
+                           size_t* workspace_bytes, hipStream_t stream, float* probs_out, float* mass_out) {
+  return run_early_exit(target_logits, draft_logits, draft_tokens, uniforms, temperature, B, K, V, topk_draft,
+                        dtype, out_tokens, num_accepted, workspace, workspace_bytes, stream, probs_out, mass_out);
 }
 
 int spec_verify_tree(const void* target_logits, const void* draft_logits, const int32_t* node_tokens,

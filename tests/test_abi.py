@@ -186,3 +186,30 @@ def test_tree_single_node_needs_no_tree_inputs():
     # N == 1: draft logits, tokens and parents may be NULL (only the size check fails here)
     assert lib.spec_verify_tree(p, None, None, None, p, p, 2, 1, 500, 0, B.SV_F32, p, p, p,
                                 ctypes.c_void_p(0x200000), ctypes.byref(n), None, None, None) == B.SV_ERR_WORKSPACE
+
+
+def test_early_exit_argument_errors_without_launch():
+    lib = B.load_library()
+    p = ctypes.c_void_p(0x100000)
+    need = B.early_exit_workspace_bytes(4, 3, 1000, B.SV_BF16)
+    assert need > 0 and need % 256 == 0
+
+    def call(B_=4, K=3, V=1000, topk=0, dtype=B.SV_BF16, ws=0x200000, n=None, ptrs=True):
+        q = p if ptrs else None
+        size = ctypes.c_size_t(need if n is None else n)
+        return lib.spec_verify_early_exit(q, q, q, q, q, B_, K, V, topk, dtype, q, q,
+                                          ctypes.c_void_p(ws) if ws else None, ctypes.byref(size), None, None, None)
+
+    assert call(B_=0) == B.SV_ERR_ARG
+    assert call(K=-1) == B.SV_ERR_ARG
+    assert call(V=0) == B.SV_ERR_ARG
+    assert call(dtype=5) == B.SV_ERR_ARG
+    assert call(topk=-2) == B.SV_ERR_ARG
+    assert call(topk=10) == B.SV_ERR_UNSUPPORTED          # sparse drafts
+    assert call(topk=1000, ws=0) == B.SV_OK               # topk >= V is dense (size query only)
+    assert call(n=need - 1) == B.SV_ERR_WORKSPACE
+    assert call(ptrs=False) == B.SV_ERR_ARG
+    assert call(ws=0x200080) == B.SV_ERR_ARG              # misaligned
+    assert call(K=B.SV_MAX_K + 1, n=1 << 40) == B.SV_ERR_UNSUPPORTED
+    # the row's statistics must fit the kernel's LDS
+    assert call(K=64, V=1 << 22, dtype=B.SV_F32, n=1 << 40) == B.SV_ERR_UNSUPPORTED

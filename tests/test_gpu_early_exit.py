@@ -1,0 +1,153 @@
+"""GPU tests of early-exit verification (spec_verify_early_exit).
+
+The call verifies a row's positions one after the other and stops reading
+its logits at the first rejection ("Speculative decoding: memverifikasi token
+draft sebelum diterima", subsection "Penolakan memendekkan pekerjaan
+speculative yang berguna").  Every sum is formed as in spec_verify, so its
+tokens, counts, tested probabilities and final mass must equal spec_verify's
+bit for bit; spec_verify itself is held to the oracle in test_gpu_parity.py.
+The oracle is also checked directly on a few cases.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from rejection_sampling_verifier_amd import (SpecVerifyError, new_early_exit_workspace, verify_early_exit,
+                                             verify_probe, SV_BF16, SV_F32)
+from tests.parity import PROB_TOL, check_well_formed, decisions_firm, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(**kw):
+    base = dict(B=6, K=3, V=40000, dtype=W.BF16, draft_sigma=0.8, temperature=0.9, seed=7)
+    base.update(kw)
+    return W.Case(**base)
+
+
+CASES = {
+    "bf16-3chunks": _case(),
+    "bf16-ragged-unaligned": _case(V=40001, seed=8),
+    "f32-3chunks-ragged": _case(dtype=W.F32, V=20001, seed=10),
+    "tiny-V": _case(V=100, peaks=3, seed=12),
+    "V1": _case(V=1, peaks=0, seed=13),
+    "K0": _case(K=0, seed=15),
+    "B1-K1": _case(B=1, K=1, seed=16),
+    "K12": _case(K=12, V=5000, seed=17),
+    "mixed-greedy": _case(B=12, greedy_rows=6, seed=18),
+    "all-greedy": _case(B=5, greedy_rows=5, seed=19),
+    "hot-T": _case(B=32, temperature=4.0, seed=20),
+    "cold-T": _case(temperature=0.05, seed=21),
+    "low-agreement": _case(B=16, draft_sigma=3.0, seed=22),
+    "high-agreement": _case(B=16, K=8, draft_sigma=0.05, seed=33),
+}
+
+
+def _both(d, x=None, ws=None):
+    x = x if x is not None else to_device(d)
+    a = verify_probe(x["target"], x["draft"], x["tokens"], x["uniforms"], x["temperature"], 0)
+    e = verify_early_exit(x["target"], x["draft"], x["tokens"], x["uniforms"], x["temperature"], 0, probes=True,
+                          workspace=ws)
+    torch.cuda.synchronize()
+    return [t.cpu().numpy() for t in a], [t.cpu().numpy() for t in e]
+
+
+def _assert_equal(d, lin, ee):
+    l_out, l_n, l_probs, l_mass = lin
+    e_out, e_n, e_probs, e_mass = ee
+    np.testing.assert_array_equal(e_n, l_n)
+    np.testing.assert_array_equal(e_out, l_out)
+    K = d["tokens"].shape[1]
+    for b in range(e_out.shape[0]):
+        if d["temperature"][b] > 0:
+            n = int(l_n[b])
+            tested = min(n + 1, K)
+            np.testing.assert_array_equal(e_probs[b, :tested], l_probs[b, :tested])
+            assert np.isnan(e_probs[b, tested:]).all(), (b, e_probs[b])
+            assert e_mass[b] == l_mass[b], (b, e_mass[b], l_mass[b])
+        else:
+            assert np.isnan(e_probs[b]).all()
+            assert e_mass[b] == 0.0
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_equals_spec_verify_bitwise(name):
+    d = W.make(CASES[name])
+    lin, ee = _both(d)
+    _assert_equal(d, lin, ee)
+    check_well_formed(d, ee[0], ee[1])
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3])
+def test_equals_spec_verify_on_the_workloads(cfg):
+    d = W.make(cfg)
+    lin, ee = _both(d)
+    _assert_equal(d, lin, ee)
+    print(f"[early-exit] config {cfg}: mean accepted {ee[1].mean():.3f} of {d['tokens'].shape[1]}", flush=True)
+
+
+def test_matches_oracle_directly():
+    d = W.make(_case(B=10, K=5, V=30000, draft_sigma=1.2, greedy_rows=3, seed=34))
+    _, ee = _both(d)
+    out, nacc, probs, mass = ee
+    ref = oracle.verify(d["target"], d["draft"], d["tokens"], d["uniforms"], d["temperature"], 0, d["dtype"])
+    near = 0
+    for b, r in enumerate(ref):
+        if not r.greedy:
+            n = min(r.n + 1, d["tokens"].shape[1])
+            np.testing.assert_allclose(probs[b, :n, 0], r.p_d[:n], rtol=0, atol=PROB_TOL)
+            np.testing.assert_allclose(probs[b, :n, 1], r.q_d[:n], rtol=0, atol=PROB_TOL)
+            assert abs(float(mass[b]) - r.S) <= PROB_TOL
+        if decisions_firm(r, d["uniforms"][b]):
+            assert int(nacc[b]) == r.n and list(out[b]) == list(r.tokens), (b, out[b], r.tokens)
+        else:
+            near += 1
+    assert near <= 3
+
+
+def test_workspace_is_left_clean_between_calls():
+    a = W.make(_case(B=8, K=4, draft_sigma=2.0, seed=35))
+    b = W.make(_case(B=8, K=4, draft_sigma=0.3, seed=36))
+    ws = new_early_exit_workspace(8, 4, 40000, SV_BF16)
+    xa, xb = to_device(a), to_device(b)
+    la, ea = _both(a, xa, ws)
+    lb, eb = _both(b, xb, ws)
+    la2, ea2 = _both(a, xa, ws)
+    _assert_equal(a, la, ea)
+    _assert_equal(b, lb, eb)
+    _assert_equal(a, la2, ea2)
+    # the workspace must be all zero again
+    torch.cuda.synchronize()
+    assert int(ws.count_nonzero().item()) == 0
+
+
+def test_out_of_range_draft_tokens_are_rejected():
+    d = W.make(_case(B=6, K=3, seed=37))
+    tok = d["tokens"].copy()
+    tok[0, 0] = -1
+    tok[1, 1] = 40000
+    tok[2, 2] = 2 ** 31 - 1
+    d["tokens"] = tok
+    lin, ee = _both(d)
+    _assert_equal(d, lin, ee)
+    assert ee[1][0] == 0 and ee[1][1] <= 1 and ee[1][2] <= 2
+
+
+def test_sparse_draft_is_unsupported():
+    d = W.make(_case(B=2, K=2, topk=16, seed=38))
+    x = to_device(d)
+    with pytest.raises(SpecVerifyError):
+        verify_early_exit(x["target"], x["draft"], x["tokens"], x["uniforms"], x["temperature"], 16)
+
+
+def test_f32_workspace_query_and_reuse_across_shapes():
+    ws = new_early_exit_workspace(8, 6, 20001, SV_F32)
+    for K, V, seed in [(6, 20001, 39), (2, 5000, 40), (6, 20001, 41)]:
+        d = W.make(_case(B=8, K=K, V=V, dtype=W.F32, seed=seed))
+        lin, ee = _both(d, ws=ws)
+        _assert_equal(d, lin, ee)
