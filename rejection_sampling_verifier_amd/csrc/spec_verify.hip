@@ -390,12 +390,17 @@ __device__ void topk_chunk(const u32x4 (&r)[NV_TILE], int lo, int len, int k, ty
       cnts[wave] = min(n, WCAP);
       if (n > WCAP) s_over = 1;
     }
+    if (n <= WCAP) {
+      // The wave's list is complete: written at once, without waiting for
+      // the other waves (a chunk with an overflowing list is rewritten by
+      // the exact path below).  The merge kernel reads it once: streaming
+      // stores.
+      CT* wl = dst + wave * WCAP;
+      for (int q = lane; q < n; q += 64)
+        __builtin_nontemporal_store(Staged<ET>::composite_at(wl_stage[q], lo), wl + q);
+    }
     __syncthreads();
     done = s_over == 0;
-    if (done) {
-      CT* wl = dst + wave * WCAP;
-      for (int q = lane; q < n; q += 64) wl[q] = Staged<ET>::composite_at(wl_stage[q], lo);
-    }
   }
   if (!done) {
     __syncthreads();  // the fast path's lists are no longer read
