@@ -354,7 +354,7 @@ def tree_main(args, W, rsv, np, torch):
     sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(copies - 1)]
     B, N, V = base["target"].shape
     dt_code = rsv.SV_BF16 if d["dtype"] == "bf16" else rsv.SV_F32
-    ws = rsv.new_tree_workspace(B, N, V, dt_code, dev)
+    ws = rsv.new_tree_workspace(B, N, V, dt_code, dev, case.topk)
     out = torch.empty((B, N), dtype=torch.int32, device=dev)
     nodes = torch.empty((B, N), dtype=torch.int32, device=dev)
     nacc = torch.empty((B,), dtype=torch.int32, device=dev)
@@ -363,7 +363,7 @@ def tree_main(args, W, rsv, np, torch):
     def step(i, timer=None):
         x = sets[i % copies]
         fn = timer.run if timer is not None else rsv.verify_tree
-        fn(x["target"], x["draft"], x["tokens"], x["parents"], x["uniforms"], x["temperature"], 0,
+        fn(x["target"], x["draft"], x["tokens"], x["parents"], x["uniforms"], x["temperature"], case.topk,
            out_tokens=out, out_nodes=nodes, num_accepted=nacc, workspace=ws,
            stream=stream.cuda_stream)
 
@@ -394,7 +394,7 @@ def tree_main(args, W, rsv, np, torch):
     # Residual passes per row (rejected siblings), from one probed call.
     x = sets[0]
     _, _, na, probs, _ = rsv.verify_tree(x["target"], x["draft"], x["tokens"], x["parents"], x["uniforms"],
-                                         x["temperature"], 0, probes=True, workspace=ws)
+                                         x["temperature"], case.topk, probes=True, workspace=ws)
     torch.cuda.synchronize()
     tested = (~torch.isnan(probs[:, :, 0])).sum(dim=1).cpu().numpy()
     passes = tested - na.cpu().numpy()
@@ -416,6 +416,7 @@ def tree_main(args, W, rsv, np, torch):
         "data": "synthetic",
         "config": {"workload": case.name, "B": B, "nodes": N, "V": V, "logits": d["dtype"],
                    "temperature": float(case.temperature), "internal_nodes_read": by["internal_nodes"],
+                   "topk_draft": case.topk,
                    "input_copies": copies},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,

@@ -263,7 +263,9 @@ int spec_verify_early_exit(const void* target_logits, const void* draft_logits,
  *                drives the final draw.
  * temperature    [B] float32 device; T <= 0 (or NaN) selects greedy.
  * B >= 1, N in [1, SV_MAX_NODES], V >= 1.
- * topk_draft     0 or >= V (dense draft); a sparse draft is SV_ERR_UNSUPPORTED.
+ * topk_draft     0 or >= V: dense drafts; otherwise every node's draft is cut
+ *                to its topk_draft largest logits (at most SV_MAX_TOPK), as in
+ *                spec_verify, and a third kernel selects each node's kept set.
  * out_tokens     [B, N] int32 device: the tokens of the accepted nodes in
  *                path order, then the final token, then -1.
  * out_nodes      [B, N] int32 device: the accepted node indices in path
@@ -278,8 +280,9 @@ int spec_verify_early_exit(const void* target_logits, const void* draft_logits,
  * mass_out       [B] float32 device or NULL: total weight of the final
  *                draw's distribution (W for a residual, ~1 for a target), 0
  *                for greedy rows.
- * Every call enqueues two kernels.  SV_ERR_UNSUPPORTED also when the row's
- * chunk statistics (2 N C 16 bytes) do not fit the walking kernel's LDS.
+ * Every call enqueues two kernels (three with a sparse draft).
+ * SV_ERR_UNSUPPORTED also when the row's chunk statistics (2 N C 16 bytes,
+ * plus 12 topk_draft bytes) do not fit the walking kernel's LDS.
  */
 int spec_verify_tree(const void* target_logits, const void* draft_logits,
                      const int32_t* node_tokens, const int32_t* parents,
@@ -293,7 +296,8 @@ int spec_verify_tree(const void* target_logits, const void* draft_logits,
 /*
  * spec_verify_tree_timed - spec_verify_tree (without probes) that also times
  * its kernels: events[0] / events[1] take the start / end of the statistics
- * kernel's dispatch, events[2] / events[3] those of the walking kernel.
+ * kernel's dispatch, events[2] / events[3] those of the walking kernel (a
+ * sparse draft's selection kernel runs between them, untimed).
  * n_events must be 4.
  */
 int spec_verify_tree_timed(const void* target_logits, const void* draft_logits,

@@ -257,16 +257,16 @@ def verify_early_exit(target, draft, draft_tokens, uniforms, temperature, topk_d
     return out_tokens, num_accepted
 
 
-def tree_workspace_bytes(B: int, N: int, V: int, dtype: int = SV_BF16) -> int:
+def tree_workspace_bytes(B: int, N: int, V: int, dtype: int = SV_BF16, topk_draft: int = 0) -> int:
     n = ctypes.c_size_t(0)
-    _check(load_library().spec_verify_tree(None, None, None, None, None, None, B, N, V, 0, dtype,
+    _check(load_library().spec_verify_tree(None, None, None, None, None, None, B, N, V, topk_draft, dtype,
                                            None, None, None, None, ctypes.byref(n), None, None, None))
     return n.value
 
 
-def new_tree_workspace(B: int, N: int, V: int, dtype: int = SV_BF16, device="cuda"):
+def new_tree_workspace(B: int, N: int, V: int, dtype: int = SV_BF16, device="cuda", topk_draft: int = 0):
     """A zero-filled workspace for spec_verify_tree at this shape."""
-    n = tree_workspace_bytes(B, N, V, dtype)
+    n = tree_workspace_bytes(B, N, V, dtype, topk_draft)
     return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
 
 
@@ -296,7 +296,7 @@ def _prepare_tree(target, draft, node_tokens, parents, uniforms, temperature, to
     if num_accepted is None:
         num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
     if workspace is None:
-        workspace = new_tree_workspace(B, N, V, dt, dev)
+        workspace = new_tree_workspace(B, N, V, dt, dev, topk_draft)
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
     ws_n = ctypes.c_size_t(workspace.numel() * workspace.element_size())

@@ -1284,8 +1284,10 @@ __device__ __forceinline__ float take_kept(const Src& src, uint64_t thr, int d, 
   return z;
 }
 
+// The merge of slot (row b, position i): `d` is the token whose q~ is
+// recorded (-1 for none).  Returns kk, the number of kept ids.
 template <typename ET>
-__global__ __launch_bounds__(WG) void merge_kernel(Args a) {
+__device__ __forceinline__ int merge_body(const Args& a, int b, int i, int d) {
   __shared__ __align__(16) uint64_t sel[SV_MAX_TOPK + 2];  // kept composites (+ a zero pad entry)
   __shared__ uint64_t ovf[MERGE_OVF];
   __shared__ uint32_t hist[RADIX_BINS];  // radix histogram, then the ranks of the kept entries
@@ -1295,17 +1297,15 @@ __global__ __launch_bounds__(WG) void merge_kernel(Args a) {
   __shared__ float red[NWAVE];
   __shared__ int ired[NWAVE];
   __shared__ int s_n, s_novf;
+  __shared__ int s_wext[NWAVE];
   __shared__ uint32_t s_ld;
-  const int i = blockIdx.x % a.K, b = blockIdx.x / a.K;
   const float T = a.temp[b];
-  if (!is_sampling_temperature(T)) return;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int C = a.C, NL = C * NWAVE, kk = min(a.topk, a.V);
   const size_t slot = (size_t)b * a.K + i;
   using CT = typename Cand<ET>::T;
   const CT* g = reinterpret_cast<const CT*>(a.cand) + slot * NL * WCAP;
   const int* gcnt = a.ccnt + slot * NL;
-  const int d = a.tok[slot];
   const float s = LOG2E / T;
   if (t == 0) {
     s_n = 0;
@@ -1335,10 +1335,19 @@ __global__ __launch_bounds__(WG) void merge_kernel(Args a) {
       if (lane < n) rc.valid |= 1u << r;
       extra += max(0, n - 64);
     }
-    int base = 0;
+    // Each wave's overflow entries go to a fixed place in the buffer (waves
+    // in order), so that the order of the candidates -- and with it every
+    // sum over them -- does not depend on timing.
+    if (lane == 0) s_wext[wave] = extra;
+    __syncthreads();
+    int base = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < NWAVE; ++w) {
+      if (w < wave) base += s_wext[w];
+      total += s_wext[w];
+    }
+    if (t == 0) s_novf = total;
     if (extra > 0) {  // wave-uniform
-      if (lane == 0) base = atomicAdd(&s_novf, extra);
-      base = __builtin_amdgcn_readfirstlane(base);
       CT w2[MERGE_REG];
 #pragma unroll
       for (int r = 0; r < MERGE_REG; ++r) {
@@ -1408,6 +1417,14 @@ __global__ __launch_bounds__(WG) void merge_kernel(Args a) {
     a.qstat[slot] = make_float4(m, Z, qd, (float)kk);
   }
   (void)lane;
+  return kk;
+}
+
+template <typename ET>
+__global__ __launch_bounds__(WG) void merge_kernel(Args a) {
+  const int i = blockIdx.x % a.K, b = blockIdx.x / a.K;
+  if (!is_sampling_temperature(a.temp[b])) return;
+  merge_body<ET>(a, b, i, a.tok[(size_t)b * a.K + i]);
 }
 
 // ============================================================================
@@ -1847,16 +1864,17 @@ constexpr int TREE_MAX_LDS_WORDS = 14336;  // the walking kernel's dynamic LDS (
 struct TreePlan {
   int C = 0, CS = 0;
   size_t off_cnt = 0, off_part = 0, off_subK = 0, off_subR = 0, off_gath = 0, total = 0;
+  size_t off_cand = 0, off_ccnt = 0, off_qstat = 0, off_kept = 0;
   size_t lds_bytes = 0;
 };
 
-int make_tree_plan(int B, int N, int V, int dtype, TreePlan& pl) {
+int make_tree_plan(int B, int N, int V, int dtype, int topk, TreePlan& pl) {
   if (B < 1 || N < 1 || V < 1 || (dtype != SV_BF16 && dtype != SV_F32)) return SV_ERR_ARG;
-  if (N > SV_MAX_NODES) return SV_ERR_UNSUPPORTED;
+  if (N > SV_MAX_NODES || topk > SV_MAX_TOPK) return SV_ERR_UNSUPPORTED;
   int C, CS;
   if (!vocab_split(V, dtype, C, CS)) return SV_ERR_UNSUPPORTED;
   if ((long long)B * 2 * N * C > INT_MAX) return SV_ERR_UNSUPPORTED;
-  const size_t words = (size_t)2 * N * C * 4 + (size_t)C * NSUB;
+  const size_t words = (size_t)2 * N * C * 4 + (size_t)C * NSUB + 3 * (size_t)topk;
   if (words > (size_t)TREE_MAX_LDS_WORDS) return SV_ERR_UNSUPPORTED;
   pl.C = C;
   pl.CS = CS;
@@ -1873,6 +1891,17 @@ int make_tree_plan(int B, int N, int V, int dtype, TreePlan& pl) {
   off = align256(off + sizeof(uint32_t) * (size_t)B * N * C * NSUB);
   pl.off_gath = off;
   off = align256(off + 2 * sizeof(float) * (size_t)B * N);
+  if (topk > 0) {
+    const size_t nodes = (size_t)B * N;
+    pl.off_cand = off;
+    off = align256(off + sizeof(uint64_t) * nodes * C * NWAVE * WCAP);
+    pl.off_ccnt = off;
+    off = align256(off + sizeof(int) * nodes * C * NWAVE);
+    pl.off_qstat = off;
+    off = align256(off + sizeof(float4) * nodes);
+    pl.off_kept = off;
+    off = align256(off + sizeof(uint2) * nodes * topk);
+  }
   pl.total = off;
   pl.lds_bytes = words * sizeof(uint32_t);
   return SV_OK;
@@ -1890,9 +1919,19 @@ int launch_tree_kernel(F kernel, int grid, size_t lds, hipStream_t st, hipEvent_
 
 template <typename ET, bool AL>
 int launch_tree(const TreeArgs& a, size_t lds, hipStream_t st, hipEvent_t* ev) {
-  const int rc = launch_tree_kernel(tree_stats_kernel<ET, AL>, a.B * 2 * a.N * a.C, 0, st, ev ? ev[0] : nullptr,
-                                    ev ? ev[1] : nullptr, a);
+  int rc = launch_tree_kernel(tree_stats_kernel<ET, AL>, a.B * 2 * a.N * a.C, 0, st, ev ? ev[0] : nullptr,
+                              ev ? ev[1] : nullptr, a);
   if (rc != SV_OK) return rc;
+  if (a.topk > 0) {
+    // The exact top-k of each node's draft, through the merge of the sparse
+    // linear path (positions read as nodes).
+    Args m{};
+    m.temp = a.temp;
+    m.cand = a.cand; m.ccnt = a.ccnt; m.qstat = a.qstat; m.kept = a.kept;
+    m.B = a.B; m.K = a.N; m.V = a.V; m.C = a.C; m.CS = a.CS; m.topk = a.topk;
+    hipLaunchKernelGGL(tree_merge_kernel<ET>, dim3(a.B * a.N), dim3(WG), 0, st, a, m);
+    if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
+  }
   return launch_tree_kernel(tree_finish_kernel<ET, AL>, a.B * a.C, lds, st, ev ? ev[2] : nullptr,
                             ev ? ev[3] : nullptr, a);
 }
@@ -1903,9 +1942,8 @@ int run_tree(const void* tgt, const void* dft, const int32_t* tok, const int32_t
              hipEvent_t* ev, int nev) {
   if (!ws_bytes || topk < 0) return SV_ERR_ARG;
   if (topk >= V) topk = 0;
-  if (topk > 0) return SV_ERR_UNSUPPORTED;
   TreePlan pl;
-  const int rc = make_tree_plan(B, N, V, dtype, pl);
+  const int rc = make_tree_plan(B, N, V, dtype, topk, pl);
   if (rc != SV_OK) return rc;
   if (!ws) {
     *ws_bytes = pl.total;
@@ -1926,7 +1964,11 @@ int run_tree(const void* tgt, const void* dft, const int32_t* tok, const int32_t
   a.subK = reinterpret_cast<uint32_t*>(base + pl.off_subK);
   a.subR = reinterpret_cast<uint32_t*>(base + pl.off_subR);
   a.gath = reinterpret_cast<float*>(base + pl.off_gath);
-  a.B = B; a.N = N; a.V = V; a.C = pl.C; a.CS = pl.CS;
+  a.cand = topk > 0 ? static_cast<void*>(base + pl.off_cand) : nullptr;
+  a.ccnt = topk > 0 ? reinterpret_cast<int*>(base + pl.off_ccnt) : nullptr;
+  a.qstat = topk > 0 ? reinterpret_cast<float4*>(base + pl.off_qstat) : nullptr;
+  a.kept = topk > 0 ? reinterpret_cast<uint2*>(base + pl.off_kept) : nullptr;
+  a.B = B; a.N = N; a.V = V; a.C = pl.C; a.CS = pl.CS; a.topk = topk;
   const size_t esz = dtype == SV_BF16 ? 2 : 4;
   const bool aligned = (reinterpret_cast<uintptr_t>(tgt) % 16 == 0) &&
                        (N == 1 || reinterpret_cast<uintptr_t>(dft) % 16 == 0) && ((size_t)V * esz) % 16 == 0;

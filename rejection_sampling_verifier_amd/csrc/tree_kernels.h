@@ -43,7 +43,13 @@ struct TreeArgs {
   float* gath;               // [B, N, 2] l_t, l_q of each node's token at its parent
   float* probes;             // [B, N, 3] (p(d), q(d), r(d)) of each tested node, NaN elsewhere; or null
   float* mass;               // [B] total weight of the final draw's distribution; or null
-  int B, N, V, C, CS;
+  // Sparse drafts (topk > 0): chunk candidate lists, then per node the kept
+  // set (ascending id) and {max kept logit, Z_q, -, kept count}.
+  void* cand;                // [B, N, C, NWAVE, WCAP]
+  int* ccnt;                 // [B, N, C, NWAVE]
+  float4* qstat;             // [B, N]
+  uint2* kept;               // [B, N, topk]
+  int B, N, V, C, CS, topk;
 };
 
 template <typename ET>
@@ -98,6 +104,13 @@ void tree_stats_kernel(TreeArgs a) {
   if (is_draft) {
     if (greedy || kids == 0) return;  // no children drawn from this draft (or a greedy row)
     load_tile<ET, ALIGNED, NV_TILE>(row, lo, len, r);
+    if (a.topk > 0) {
+      // A truncated draft: the chunk's candidates for the node's top k.
+      const size_t chunk = ((size_t)b * N + node) * a.C + c;
+      topk_chunk<ET>(r, lo, len, a.topk, reinterpret_cast<typename Cand<ET>::T*>(a.cand) + chunk * NWAVE * WCAP,
+                     a.ccnt + chunk * NWAVE, shf);
+      return;
+    }
   }
   uint32_t* dst = tree_part(a, b, slot, c);
   if (greedy) {
@@ -149,6 +162,41 @@ void tree_stats_kernel(TreeArgs a) {
     if (d >= lo && d < lo + len) a.gath[((size_t)b * N + t) * 2 + (is_draft ? 1 : 0)] = Tr<ET>::load1(row + d);
   }
   if (t == 0) *reinterpret_cast<u32x4*>(dst) = u32x4{__float_as_uint(m), __float_as_uint(z), 0u, 0u};
+}
+
+// ============================================================================
+// Sparse drafts: the exact top-k selection of each node with children (the
+// merge of spec_verify's sparse path, one work-group per (row, node)), then
+// each child's token logit in the kept set (-inf when not kept), for the
+// node's q~ at the child's token.
+// ============================================================================
+template <typename ET>
+__global__ __launch_bounds__(WG) void tree_merge_kernel(TreeArgs ta, Args ma) {
+  const int N = ta.N;
+  const int node = blockIdx.x % N, b = blockIdx.x / N;
+  const int t = threadIdx.x;
+  __shared__ int s_has;
+  if (!is_sampling_temperature(ta.temp[b])) return;
+  int p = -1;
+  if (t > node && t < N) p = ta.par[(size_t)b * N + t];
+  if (t == 0) s_has = 0;
+  __syncthreads();
+  if (p == node) s_has = 1;
+  __syncthreads();
+  if (!s_has) return;
+  const int kk = merge_body<ET>(ma, b, node, -1);
+  __syncthreads();  // the kept list is written
+  if (p == node) {
+    const int d = ta.tok[(size_t)b * N + t];
+    const uint2* kept = ta.kept + ((size_t)b * N + node) * ta.topk;
+    int lo = 0, hi = kk;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if ((int)kept[mid].x < d) lo = mid + 1; else hi = mid;
+    }
+    ta.gath[((size_t)b * N + t) * 2 + 1] =
+        (lo < kk && (int)kept[lo].x == d) ? __uint_as_float(kept[lo].y) : NEG_INF;
+  }
 }
 
 // ============================================================================
@@ -221,7 +269,8 @@ enum { W_PASS = 0, W_LEAF = 1, W_RESID = 2, W_GREEDY = 3, W_FALLBACK = 4 };
 // that the results equal the wave reductions of the linear verifier bit for
 // bit.
 template <int G>
-__device__ __forceinline__ void tree_merge(TreeRow& tr, const uint32_t* pw, int N, int C, bool greedy, float s) {
+__device__ __forceinline__ void tree_merge(TreeRow& tr, const uint32_t* pw, int N, int C, bool greedy, bool sparse,
+                                           float s) {
   constexpr int PER = 64 / G;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int gl = lane % G;
@@ -229,7 +278,7 @@ __device__ __forceinline__ void tree_merge(TreeRow& tr, const uint32_t* pw, int 
   for (int base = wave * PER; base < nslots; base += NWAVE * PER) {
     const int slot = base + lane / G;
     const int node = slot < N ? slot : slot - N;
-    const bool need = slot < nslots && (slot < N || tr.kids[node] != 0ull);
+    const bool need = slot < nslots && (slot < N || (!sparse && tr.kids[node] != 0ull));
     auto word = [&](int cc, int w) { return __uint_as_float(pw[((size_t)slot * C + cc) * 4 + w]); };
     if (greedy) {
       float bv = NEG_INF;
@@ -333,7 +382,8 @@ __device__ __forceinline__ void tree_walk(TreeRow& tr, int N, int V, int v, int 
 // ============================================================================
 template <typename ET, bool ALIGNED>
 __device__ __forceinline__ int tree_draw(const TreeArgs& a, const TreeRow& tr, const uint32_t* pw, const float* csub, int b,
-                         int v, int mode, float cscale, float uK, float* S_out) {
+                         int v, int mode, float cscale, float uK, float* S_out, const int* kid = nullptr,
+                         const float* kq = nullptr, int nkept = 0) {
   constexpr int VEC = Tr<ET>::VEC;
   const int N = a.N, C = a.C, l = threadIdx.x & 63;
   const float s = tr.s;
@@ -404,7 +454,7 @@ __device__ __forceinline__ int tree_draw(const TreeArgs& a, const TreeRow& tr, c
   const int lo = cs * a.CS;
   const int len = min(a.CS, a.V - lo);
   const ET* trow = tree_row<ET>(a, false, b, v);
-  const ET* drow = mode == W_RESID ? tree_row<ET>(a, true, b, v) : nullptr;
+  const ET* drow = (mode == W_RESID && !kid) ? tree_row<ET>(a, true, b, v) : nullptr;
   const float MSq = mode == W_RESID ? mul_rn(tr.M[N + v], s) : 0.f;
   const float rZq = mode == W_RESID ? cscale / tr.Z[N + v] : 0.f;
   if (mode == W_FALLBACK) {
@@ -444,9 +494,83 @@ __device__ __forceinline__ int tree_draw(const TreeArgs& a, const TreeRow& tr, c
   const int start = lo + (jj * WG + w * 64) * VEC;
   const int slen = max(0, min(64 * VEC, lo + len - start));
   if (slen <= 0) return lo;
-  const SegResult r = segment_search<ET, ALIGNED>(trow, drow, nullptr, nullptr, 0, start, slen, tl, s, MSt, rZt,
-                                                  MSq, rZq);
+  const SegResult r = segment_search<ET, ALIGNED>(trow, drow, mode == W_RESID ? kid : nullptr, kq, nkept, start,
+                                                  slen, tl, s, MSt, rZt, MSq, rZq);
   return r.found >= 0 ? r.found : (r.last_pos >= 0 ? r.last_pos : start);
+}
+
+// Sparse drafts: node v's kept list into LDS (all threads): ids ascending in
+// kid, c q~ values in kq.  Returns the kept count.
+__device__ __forceinline__ int tree_load_kept(const TreeArgs& a, const TreeRow& tr, int b, int v, float cscale,
+                                              int* kid, float* kq) {
+  const int N = a.N;
+  const float s = tr.s;
+  const float MSq = mul_rn(tr.M[N + v], s), rZq = cscale / tr.Z[N + v];
+  const int nkept = (int)a.qstat[(size_t)b * N + v].w;
+  const uint2* kept = a.kept + ((size_t)b * N + v) * a.topk;
+  for (int j = threadIdx.x; j < nkept; j += WG) {
+    const uint2 e = kept[j];
+    kid[j] = (int)e.x;
+    kq[j] = exp2_fast(fmaf(__uint_as_float(e.y), s, -MSq)) * rZq;
+  }
+  __syncthreads();
+  return nkept;
+}
+
+// Sparse drafts: sub-block sums of max(0, p_v - c q~_v) over one chunk (all
+// threads), as spec_verify's sparse residual: the sum of p over the
+// sub-block less, at its kept ids, min(p, c q~).  Only the target is read.
+template <typename ET, bool ALIGNED>
+__device__ __forceinline__ void tree_chunk_residual_sparse(const TreeArgs& a, const TreeRow& tr, int b, int v,
+                                                           int chunk, float* dst, const int* kid, const float* kq,
+                                                           float* kcorr, int nkept) {
+  constexpr int VEC = Tr<ET>::VEC;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const float s = tr.s;
+  const float MSt = mul_rn(tr.M[v], s), rZt = 1.f / tr.Z[v];
+  const int lo = chunk * a.CS;
+  const int len = min(a.CS, a.V - lo);
+  const ET* trow = tree_row<ET>(a, false, b, v);
+  u32x4 rt[NV_TILE];
+  load_tile<ET, ALIGNED, NV_TILE>(trow, lo, len, rt);
+  for (int j = t; j < nkept; j += WG) {
+    const int id = kid[j];
+    float cv = 0.f;
+    if (id >= lo && id < lo + len) {
+      const float pv = exp2_fast(fmaf(Tr<ET>::load1(trow + id), s, -MSt)) * rZt;
+      cv = fminf(pv, kq[j]);
+    }
+    kcorr[j] = cv;
+  }
+#pragma unroll
+  for (int j = 0; j < NV_TILE; ++j) {
+    float w0 = 0.f, w1 = 0.f;
+#pragma unroll
+    for (int k = 0; k < VEC; k += 2) {
+      w0 += exp2_fast(fmaf(Tr<ET>::at(rt[j], k), s, -MSt)) * rZt;
+      w1 += exp2_fast(fmaf(Tr<ET>::at(rt[j], k + 1), s, -MSt)) * rZt;
+    }
+    const float sum = wave_sum(w0 + w1);
+    if (lane == 0) dst[j * NWAVE + wave] = sum;
+  }
+  __syncthreads();
+  if (t < NSUB) {
+    // Sub-block t holds the ids lo + [t, t+1) * 64 * VEC: a contiguous run of
+    // the sorted kept list, summed in list order.
+    auto lower = [&](int x) {
+      int l0 = 0, h0 = nkept;
+      while (l0 < h0) {
+        const int mid = (l0 + h0) >> 1;
+        if (kid[mid] < x) l0 = mid + 1; else h0 = mid;
+      }
+      return l0;
+    };
+    const int j0 = lower(lo + t * 64 * VEC), j1 = lower(lo + (t + 1) * 64 * VEC);
+    float cs = 0.f;
+    for (int j = j0; j < j1; ++j) cs += kcorr[j];
+    dst[t] = fmaxf(0.f, dst[t] - cs);
+  }
+  __syncthreads();
 }
 
 // Sub-block sums of max(0, p_v - c q_v) over one chunk (all threads); the 32
@@ -499,7 +623,9 @@ __device__ __forceinline__ void tree_chunk_residual(const TreeArgs& a, const Tre
 // ============================================================================
 template <typename ET, bool ALIGNED>
 __global__ __launch_bounds__(WG) void tree_finish_kernel(TreeArgs a) {
-  extern __shared__ __align__(16) uint32_t tcache[];  // [2N * C * 4] partial words, then [C * NSUB] residual sums
+  // Dynamic LDS: [2N * C * 4] partial words, [C * NSUB] residual sums, then
+  // for a sparse draft [topk] kept ids, [topk] c q~ values, [topk] corrections.
+  extern __shared__ __align__(16) uint32_t tcache[];
   __shared__ TreeRow tr;
   __shared__ float shsub[NSUB];
   __shared__ unsigned s_ticket;
@@ -509,6 +635,9 @@ __global__ __launch_bounds__(WG) void tree_finish_kernel(TreeArgs a) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   uint32_t* pw = tcache;
   float* csub = reinterpret_cast<float*>(tcache + (size_t)2 * N * C * 4);
+  int* kid = reinterpret_cast<int*>(csub + (size_t)C * NSUB);
+  float* kq = reinterpret_cast<float*>(kid + a.topk);
+  float* kcorr = kq + a.topk;
   float* probe = (c == 0 && a.probes) ? a.probes + (size_t)b * 3 * N : nullptr;
   // The row's partials and scalars in one round of loads.
   const u32x4* src = reinterpret_cast<const u32x4*>(tree_part(a, b, 0, 0));
@@ -531,9 +660,16 @@ __global__ __launch_bounds__(WG) void tree_finish_kernel(TreeArgs a) {
   __syncthreads();
   // Merge each node's chunk statistics (draft slots only where they exist).
   const float s = greedy ? 0.f : LOG2E / T;
-  if (C <= 16) tree_merge<16>(tr, pw, N, C, greedy, s);
-  else if (C <= 32) tree_merge<32>(tr, pw, N, C, greedy, s);
-  else tree_merge<64>(tr, pw, N, C, greedy, s);
+  const bool sparse = a.topk > 0 && !greedy;
+  if (C <= 16) tree_merge<16>(tr, pw, N, C, greedy, sparse, s);
+  else if (C <= 32) tree_merge<32>(tr, pw, N, C, greedy, sparse, s);
+  else tree_merge<64>(tr, pw, N, C, greedy, sparse, s);
+  if (sparse && t < N && tr.kids[t] != 0ull) {
+    // The truncated draft's statistics come from the merge kernel.
+    const float4 q = a.qstat[(size_t)b * N + t];
+    tr.M[N + t] = q.x;
+    tr.Z[N + t] = q.y;
+  }
   __syncthreads();
   if (t == 0) {
     tr.s = s;
@@ -580,7 +716,12 @@ __global__ __launch_bounds__(WG) void tree_finish_kernel(TreeArgs a) {
     if (tp == pass) {
       // A chunk of the current pass: its sums of max(0, p_v - c q_v).
       const int tc = (int)(ticket % (unsigned)C);
-      tree_chunk_residual<ET, ALIGNED>(a, tr, b, tr.v, tr.c, tc, shsub);
+      if (sparse) {
+        const int nk = tree_load_kept(a, tr, b, tr.v, tr.c, kid, kq);
+        tree_chunk_residual_sparse<ET, ALIGNED>(a, tr, b, tr.v, tc, shsub, kid, kq, kcorr, nk);
+      } else {
+        tree_chunk_residual<ET, ALIGNED>(a, tr, b, tr.v, tr.c, tc, shsub);
+      }
       if (t < NSUB) pub_f32(subR_row + ((size_t)pass * C + tc) * NSUB + t, shsub[t]);
       ticket = NONE;
       continue;
@@ -612,10 +753,15 @@ __global__ __launch_bounds__(WG) void tree_finish_kernel(TreeArgs a) {
       a.onodes[(size_t)b * N + i] = -1;
     }
     if (t == 0) a.nacc[b] = -1;
-  } else if (ticket == (unsigned)pass * (unsigned)C && wave == 0) {
-    float S;
-    const int x = tree_draw<ET, ALIGNED>(a, tr, pw, csub, b, tr.v, tr.status, tr.c, tr.u[0], &S);
-    emit(x, S);
+  } else if (ticket == (unsigned)pass * (unsigned)C) {
+    // A sparse residual draw needs the node's kept list (scaled by c).
+    const int nk = (sparse && tr.status == W_RESID) ? tree_load_kept(a, tr, b, tr.v, tr.c, kid, kq) : 0;
+    if (wave == 0) {
+      float S;
+      const int x = tree_draw<ET, ALIGNED>(a, tr, pw, csub, b, tr.v, tr.status, tr.c, tr.u[0], &S,
+                                           nk ? kid : nullptr, kq, nk);
+      emit(x, S);
+    }
   }
   // The last work-group of the row to finish clears its tickets and sums.
   __syncthreads();

@@ -168,7 +168,12 @@ def test_tree_argument_errors_without_launch():
     assert _tree_call(lib, ws=ws, ws_n=need - 1) == B.SV_ERR_WORKSPACE
     assert _tree_call(lib, ptrs=False, ws=ws, ws_n=need) == B.SV_ERR_ARG
     assert _tree_call(lib, ws=ctypes.c_void_p(0x200040), ws_n=need) == B.SV_ERR_ARG
-    assert _tree_call(lib, topk=128, ws=ws, ws_n=need) == B.SV_ERR_UNSUPPORTED   # sparse draft
+    assert _tree_call(lib, V=5000, topk=B.SV_MAX_TOPK + 1, ws=ws, ws_n=1 << 40) == B.SV_ERR_UNSUPPORTED
+    assert B.tree_workspace_bytes(4, 7, 1000, B.SV_BF16) == need                    # dense
+    n = ctypes.c_size_t(0)
+    assert lib.spec_verify_tree(None, None, None, None, None, None, 4, 7, 1000, 128, B.SV_BF16, None, None, None,
+                                None, ctypes.byref(n), None, None, None) == B.SV_OK
+    assert n.value > need                                                           # sparse: candidate areas
     assert _tree_call(lib, N=B.SV_MAX_NODES + 1, ws=ws, ws_n=1 << 40) == B.SV_ERR_UNSUPPORTED
     # the row's chunk statistics must fit the walking kernel's LDS
     assert _tree_call(lib, N=64, V=1 << 20, dtype=B.SV_F32, ws=ws, ws_n=1 << 40) == B.SV_ERR_UNSUPPORTED

@@ -54,7 +54,8 @@ def tree_to_device(d, dev="cuda"):
 def run_tree_gpu(d, x=None, workspace=None):
     x = x if x is not None else tree_to_device(d)
     out, nodes, nacc, probs, mass = verify_tree(x["target"], x["draft"], x["tokens"], x["parents"], x["uniforms"],
-                                                x["temperature"], 0, probes=True, workspace=workspace)
+                                                x["temperature"], d.get("topk", 0), probes=True,
+                                                workspace=workspace)
     torch.cuda.synchronize()
     return tuple(t.cpu().numpy() for t in (out, nodes, nacc, probs, mass))
 
@@ -93,7 +94,7 @@ def check_tree_rows(d, gpu, rows=None, stats=None):
     B, N = out.shape
     rows = list(range(B)) if rows is None else list(rows)
     ref = oracle.verify_tree(d["target"], d["draft"], d["tokens"], d["parents"], d["uniforms"],
-                             d["temperature"], 0, d["dtype"], rows=rows)
+                             d["temperature"], d.get("topk", 0), d["dtype"], rows=rows)
     near = 0
     worst = 0.0
     for b, r in zip(rows, ref):
@@ -138,6 +139,14 @@ CASES = {
     "61-node-tree": _case(B=4, V=17000, parents=W.TREE_60_DEPTH8, temperature=0.7, seed=96),
     "fp32-T0.3-chain-and-fan": _case(V=5000, dtype=W.F32, parents=(-1, 0, 1, 1, 2, 0, 5), temperature=0.3,
                                      seed=97),
+    # sparse (top-k truncated) drafts at every node
+    "top128-bf16-3chunks-level": _case(parents=W.level_tree((3, 4, 4, 3), seed=1), topk=128, seed=102),
+    "top3-f32-V1024-fan": _case(V=1024, dtype=W.F32, target_sigma=2.0, peaks=0, draft_sigma=0.5,
+                                parents=FAN_4x2, topk=3, seed=103),
+    "top128-61-node-tree": _case(B=4, V=17000, parents=W.TREE_60_DEPTH8, temperature=0.7, topk=128, seed=104),
+    "top128-wide-low-agreement": _case(V=9000, draft_sigma=3.0, parents=WIDE_8, topk=128, seed=105),
+    "top300-exact-path-random": _case(V=20001, parents=None, nodes=10, topk=300, seed=106),
+    "top128-mixed-greedy": _case(B=10, V=30000, parents=None, nodes=16, greedy_rows=4, topk=128, seed=107),
 }
 
 
@@ -176,16 +185,16 @@ def _chain_from_linear(d):
     par = np.broadcast_to(np.arange(-1, K, dtype=np.int32), (B, K + 1)).copy()
     u = np.concatenate([d["uniforms"][:, K:], d["uniforms"][:, :K]], axis=1)
     return dict(target=tgt, draft=dft, tokens=tok, parents=par, uniforms=u, temperature=d["temperature"],
-                dtype=d["dtype"])
+                topk=d["topk"], dtype=d["dtype"])
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 3])
+@pytest.mark.parametrize("cfg", [0, 1, 3, 4])
 def test_chain_tree_equals_linear_verifier_bitwise(cfg):
     d = W.make(cfg)
     B, K = d["tokens"].shape
     x = to_device(d)
     l_out, l_n, l_probs, l_mass = verify_probe(x["target"], x["draft"], x["tokens"], x["uniforms"],
-                                               x["temperature"], 0)
+                                               x["temperature"], d["topk"])
     torch.cuda.synchronize()
     l_out, l_n, l_probs, l_mass = (t.cpu().numpy() for t in (l_out, l_n, l_probs, l_mass))
     del x
@@ -248,16 +257,17 @@ def test_workspace_is_left_clean_between_calls():
     check_tree_rows(b, rb)
 
 
-def test_full_size_tree_workload_sampled_rows():
-    """The 61-node, depth-8 tree over 151,936 ids (B = 32): every row well
-    formed, sampled rows against the oracle."""
-    d = W.make_tree(0)
+@pytest.mark.parametrize("cfg", [0, 1])
+def test_full_size_tree_workload_sampled_rows(cfg):
+    """The 61-node, depth-8 tree over 151,936 ids (B = 32; dense and top-128
+    drafts): every row well formed, sampled rows against the oracle."""
+    d = W.make_tree(cfg)
     gpu = run_tree_gpu(d)
     B = d["tokens"].shape[0]
     check_tree_well_formed(d, gpu, range(B))
     rows = [0, 7, 13, 22, 31]
     st = {}
     near = check_tree_rows(d, gpu, rows=rows, stats=st)
-    print(f"[tree] full size: near-boundary {near}/{len(rows)}, mean accepted {gpu[2].mean():.2f}, "
+    print(f"[tree] full size {cfg}: near-boundary {near}/{len(rows)}, mean accepted {gpu[2].mean():.2f}, "
           f"worst prob error {st['worst']:.2e}", flush=True)
     assert near <= 2

@@ -228,6 +228,7 @@ class TreeCase:
     draft_sigma: float = 1.0
     temperature: float = 1.0
     greedy_rows: int = 0
+    topk: int = 0                            # sparse draft truncation at every node (0 = dense)
     seed: int = 0
     name: str = ""
 
@@ -236,11 +237,15 @@ class TreeCase:
         return len(self.parents) if self.parents is not None else self.nodes
 
 
-# The tree workload: B = 32 rows of the 61-node tree over the 151,936-id
-# vocabulary, bf16, T = 1.0 (the pages' temperature for the tree experiments).
+# The tree workloads: B = 32 rows of the 61-node tree over the 151,936-id
+# vocabulary, bf16, T = 1.0 (the pages' temperature for the tree experiments),
+# with dense drafts and with drafts truncated to their top 128.
 TREE_CONFIGS = [
     TreeCase(B=32, V=151936, draft_sigma=1.0, temperature=1.0, seed=2001,
              name="B32-N61-depth8-V151936-bf16-T1.0"),
+    # The same trees with every node's draft cut to its top 128 logits.
+    TreeCase(B=32, V=151936, draft_sigma=1.0, temperature=1.0, topk=128, seed=2002,
+             name="B32-N61-depth8-V151936-bf16-T1.0-top128"),
 ]
 
 
@@ -280,11 +285,13 @@ def _make_tree_row(case: TreeCase, seq: np.random.SeedSequence, T: float):
         kids = np.flatnonzero(par == v)
         kids = kids[kids > v]
         if T > 0:
-            # Gumbel-max, one independent draw per child
+            # Gumbel-max over the (truncated) draft, one independent draw per child
+            ids = _top_ids(dft_val[v], case.topk)
             for c in kids:
                 with np.errstate(divide="ignore"):
-                    score = dft_val[v] / np.float32(T) - np.log(rng.standard_exponential(V, dtype=np.float32))
-                toks[c] = int(np.argmax(score))
+                    score = dft_val[v, ids] / np.float32(T) - np.log(rng.standard_exponential(ids.size,
+                                                                                          dtype=np.float32))
+                toks[c] = int(ids[int(np.argmax(score))])
         else:
             order = np.argsort(-dft_val[v], kind="stable")
             toks[kids] = order[: kids.size]
@@ -331,7 +338,7 @@ def make_tree(case: TreeCase | int, threads: int | None = None) -> dict:
         with ThreadPoolExecutor(max_workers=threads) as ex:
             list(ex.map(work, range(B)))
     return dict(target=target, draft=draft, tokens=tokens, parents=parents, uniforms=uniforms,
-                temperature=T, dtype=case.dtype, case=case)
+                temperature=T, topk=case.topk, dtype=case.dtype, case=case)
 
 
 __all__ = ["BF16", "F32", "Case", "CONFIGS", "make", "bf16_bits", "bf16_to_f32", "replace",
