@@ -178,7 +178,7 @@ def main():
         rule = dict(alpha=float(a_), max_rank=int(r_), min_prob=float(p_))
 
     kl_buf = torch.empty((B, K), dtype=torch.float32, device=dev) if args.kl else None
-    ee_ws = rsv.new_early_exit_workspace(B, K, V, dt_code, dev) if args.early_exit else None
+    ee_ws = rsv.new_early_exit_workspace(B, K, V, dt_code, dev, d["topk"]) if args.early_exit else None
 
     def step(i, timer=None):
         x = sets[i % copies]

@@ -206,9 +206,10 @@ int spec_verify_kl(const void* target_logits, const void* draft_logits,
  * probabilities p_i(d_i), q_i(d_i) and the final mass equal spec_verify's
  * bit for bit.
  *
- * One kernel per call.  A dense draft only: 0 < topk_draft < V is
- * SV_ERR_UNSUPPORTED, and so is a shape whose row statistics
- * ((2K+1) C 16 + C 128 bytes) do not fit the kernel's LDS.
+ * One kernel per call.  topk_draft as spec_verify: a truncated draft's
+ * selection is made for a position only once the row reaches it.  A shape
+ * whose row statistics ((2K+1) C 16 + C 128 bytes, plus C 16 + 16 topk_draft
+ * for a truncated draft) do not fit the kernel's LDS is SV_ERR_UNSUPPORTED.
  * The workspace has its own size (query with workspace == NULL) and must
  * not be shared with the other entry points: this call keeps it zero between
  * calls and relies on that.

@@ -219,17 +219,17 @@ def verify_kl(target, draft, draft_tokens, uniforms, temperature, topk_draft: in
     return out_tokens, num_accepted, kl
 
 
-def early_exit_workspace_bytes(B: int, K: int, V: int, dtype: int = SV_BF16) -> int:
+def early_exit_workspace_bytes(B: int, K: int, V: int, dtype: int = SV_BF16, topk_draft: int = 0) -> int:
     n = ctypes.c_size_t(0)
-    _check(load_library().spec_verify_early_exit(None, None, None, None, None, B, K, V, 0, dtype, None, None,
-                                                 None, ctypes.byref(n), None, None, None))
+    _check(load_library().spec_verify_early_exit(None, None, None, None, None, B, K, V, topk_draft, dtype, None,
+                                                 None, None, ctypes.byref(n), None, None, None))
     return n.value
 
 
-def new_early_exit_workspace(B: int, K: int, V: int, dtype: int = SV_BF16, device="cuda"):
+def new_early_exit_workspace(B: int, K: int, V: int, dtype: int = SV_BF16, device="cuda", topk_draft: int = 0):
     """A zero-filled workspace for spec_verify_early_exit at this shape (its
     own: not to be shared with the other calls)."""
-    n = early_exit_workspace_bytes(B, K, V, dtype)
+    n = early_exit_workspace_bytes(B, K, V, dtype, topk_draft)
     return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
 
 
@@ -243,7 +243,7 @@ def verify_early_exit(target, draft, draft_tokens, uniforms, temperature, topk_d
     """
     if workspace is None and target.dim() == 3:
         B, Kp1, V = target.shape
-        workspace = new_early_exit_workspace(B, Kp1 - 1, V, _dtype_code(target), target.device)
+        workspace = new_early_exit_workspace(B, Kp1 - 1, V, _dtype_code(target), target.device, topk_draft)
     args, out_tokens, num_accepted, _ = _prepare(target, draft, draft_tokens, uniforms, temperature,
                                                  topk_draft, out_tokens, num_accepted, workspace, stream)
     probs = mass = None

@@ -10,7 +10,9 @@
 // section 4).  The result equals spec_verify's bit for bit: every sum is
 // formed in the same order.
 //
-// One launch, one work-group per (row, chunk).  A row's work is cut into
+// One launch, one work-group per (row, chunk) for a dense draft; for a
+// truncated draft fewer per row, as many as the device holds at once with
+// every row in flight.  A row's work is cut into
 // stages: stage i <= n computes the chunk statistics of position i (target,
 // and the draft of a sampling row); after a rejection at n one more stage
 // computes the residual sums of position n.  Each stage is cut into tickets,
@@ -29,7 +31,7 @@
 // of position `pos` when `draft`), published as the words spec_verify's
 // statistics kernel writes; the bonus position also publishes its 32
 // sub-block sums.
-template <typename ET, bool ALIGNED>
+template <typename ET, bool ALIGNED, bool SPARSE>
 __device__ __forceinline__ void ee_stats_chunk(const Args& a, int b, int pos, int c, bool greedy, bool draft,
                                                float s, float* shf, int* shi, float* shsub) {
   constexpr int VEC = Tr<ET>::VEC;
@@ -39,6 +41,14 @@ __device__ __forceinline__ void ee_stats_chunk(const Args& a, int b, int pos, in
   const ET* row = draft ? draft_row<ET>(a, b, pos) : target_row<ET>(a, b, pos);
   u32x4 r[NV_TILE];
   load_tile<ET, ALIGNED, NV_TILE>(row, lo, len, r);
+  if (SPARSE && draft) {
+    // A truncated draft: the chunk's candidates, published for the row's
+    // other work-groups.
+    const size_t chunk = ((size_t)b * K + pos) * a.C + c;
+    topk_chunk<ET, true>(r, lo, len, a.topk, reinterpret_cast<typename Cand<ET>::T*>(a.cand) + chunk * NWAVE * WCAP,
+                         a.ccnt + chunk * NWAVE, shf);
+    return;
+  }
   const int d = pos < K ? a.tok[(size_t)b * K + pos] : -1;
   uint32_t* dst = part_words(a, b, draft ? K + 1 + pos : pos, c);
   if (greedy) {
@@ -140,6 +150,109 @@ __device__ __forceinline__ void ee_residual_chunk(const Args& a, int b, int n, i
   if (t < NSUB) pub_f32(a.subR + ((size_t)b * a.C + c) * NSUB + t, shsub[t]);
 }
 
+// Sparse drafts: waits until every candidate list of position `pos` is
+// published (its count, then its entries).  Counts are left in cnt (LDS).
+__device__ __forceinline__ bool ee_wait_cands(const Args& a, int b, int pos, uint64_t deadline, int* cnt) {
+  const int NL = a.C * NWAVE;
+  const size_t slot = (size_t)b * a.K + pos;
+  if (!wait_words(reinterpret_cast<const uint32_t*>(a.ccnt + slot * NL), NL, reinterpret_cast<uint32_t*>(cnt),
+                  nullptr, 0, nullptr, deadline))
+    return false;
+  const uint64_t* g = reinterpret_cast<const uint64_t*>(a.cand) + slot * NL * WCAP;
+  for (;;) {
+    bool ok = true;
+    for (int i = threadIdx.x; i < NL * WCAP; i += WG) {
+      const int L = i / WCAP, j = i % WCAP;
+      if (j < cnt[L]) ok &= cand_ld<true>(g + (size_t)L * WCAP + j) != 0ull;
+    }
+    if (__syncthreads_and(ok)) return true;
+    if (__syncthreads_or(wall_clock64() > deadline)) return false;
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+// Sparse drafts: the exact top-k selection of position `pos`'s draft, made
+// by the first work-group of the row to get here (from the published
+// candidate lists) and published for the others, which wait for it: the
+// first one is running, so the wait ends.  Leaves {max kept logit, Z_q,
+// q~(d), kept count} in *qs and the kept ids and logits (ascending id) in
+// kid[0..topk) and kid[topk..2 topk) (LDS).  The published words: the four
+// of *qs, then the ids, then the logits.
+template <typename ET>
+__device__ __forceinline__ bool ee_select(const Args& a, int b, int pos, int d, int* lcnt, int* kid, float4* qs) {
+  __shared__ unsigned s_first;
+  const int t = threadIdx.x, kk = a.topk;  // topk < V: kk ids are kept
+  const size_t slot = (size_t)b * a.K + pos;
+  uint32_t* res = a.mres + slot * (4 + 2 * (size_t)kk);
+  if (t == 0) s_first = __hip_atomic_fetch_add(a.mclaim + slot, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u;
+  __syncthreads();
+  const uint64_t deadline = wall_clock64() + WAIT_TICKS;
+  if (!s_first)
+    return wait_words(res, 4, reinterpret_cast<uint32_t*>(qs), res + 4, 2 * kk, reinterpret_cast<uint32_t*>(kid),
+                      deadline);
+  if (!ee_wait_cands(a, b, pos, deadline, lcnt)) return false;
+  float* kl = reinterpret_cast<float*>(kid + kk);
+  merge_body<ET, true>(a, b, pos, d, qs, kid, kl);
+  __syncthreads();
+  for (int i = t; i < kk; i += WG) {
+    pub_u32(res + 4 + i, (uint32_t)kid[i]);
+    pub_f32(res + 4 + kk + i, kl[i]);
+  }
+  if (t < 4) pub_u32(res + t, reinterpret_cast<const uint32_t*>(qs)[t]);
+  return true;
+}
+
+// Sparse drafts: the residual sums of one chunk, as finish_kernel's sparse
+// branch (the sum of p over a sub-block less min(p, q~) at its kept ids);
+// the kept ids and q~ values are in kid / kq (LDS, ascending id).
+template <typename ET, bool ALIGNED>
+__device__ __forceinline__ void ee_residual_chunk_sparse(const Args& a, int b, int n, int c, float s, float MSt,
+                                                         float rZt, const int* kid, const float* kq, float* corr,
+                                                         int nkept, float* shsub) {
+  constexpr int VEC = Tr<ET>::VEC;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int lo = c * a.CS;
+  const int len = min(a.CS, a.V - lo);
+  const ET* trow = target_row<ET>(a, b, n);
+  u32x4 rt[NV_TILE];
+  load_tile<ET, ALIGNED, NV_TILE>(trow, lo, len, rt);
+  for (int j = t; j < nkept; j += WG) {
+    const int id = kid[j];
+    float cv = 0.f;
+    if (id >= lo && id < lo + len) {
+      const float pv = exp2_fast(fmaf(Tr<ET>::load1(trow + id), s, -MSt)) * rZt;
+      cv = fminf(pv, kq[j]);
+    }
+    corr[j] = cv;
+  }
+#pragma unroll
+  for (int j = 0; j < NV_TILE; ++j) {
+    float w0 = 0.f, w1 = 0.f;
+#pragma unroll
+    for (int k = 0; k < VEC; k += 2) {
+      w0 += exp2_fast(fmaf(Tr<ET>::at(rt[j], k), s, -MSt)) * rZt;
+      w1 += exp2_fast(fmaf(Tr<ET>::at(rt[j], k + 1), s, -MSt)) * rZt;
+    }
+    const float v = wave_sum(w0 + w1);
+    if (lane == 0) shsub[j * NWAVE + wave] = v;
+  }
+  __syncthreads();
+  if (t < NSUB) {
+    auto lower = [&](int x) {
+      int l0 = 0, h0 = nkept;
+      while (l0 < h0) {
+        const int mid = (l0 + h0) >> 1;
+        if (kid[mid] < x) l0 = mid + 1; else h0 = mid;
+      }
+      return l0;
+    };
+    const int j0 = lower(lo + t * 64 * VEC), j1 = lower(lo + (t + 1) * 64 * VEC);
+    float cs = 0.f;
+    for (int j = j0; j < j1; ++j) cs += corr[j];
+    pub_f32(a.subR + ((size_t)b * a.C + c) * NSUB + t, fmaxf(0.f, shsub[t] - cs));
+  }
+}
+
 // Merge of one slot's decoded chunk words (LDS) by one wave, in the order of
 // decide_row.
 __device__ __forceinline__ void ee_merge_slot(const Args& a, RowShared& rs, const uint32_t* pw, int slot,
@@ -167,9 +280,15 @@ __device__ __forceinline__ void ee_merge_slot(const Args& a, RowShared& rs, cons
   }
 }
 
-template <typename ET, bool ALIGNED>
-__global__ __launch_bounds__(WG) void early_exit_kernel(Args a) {
-  extern __shared__ __align__(16) uint32_t ee_cache[];  // [(2K+1) * C * 4] decoded words, then [C * NSUB] sums
+// SPARSE: the instantiation for truncated drafts.  Their selection is heavy
+// in registers: the compiler is held to four waves per SIMD (a few spills)
+// rather than two, which measured faster; dense calls keep the lighter code.
+template <typename ET, bool ALIGNED, bool SPARSE>
+__global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(SPARSE ? 4 : 1))) void early_exit_kernel(Args a) {
+  // Dynamic LDS: [(2K+1) * C * 4] decoded words, [C * NSUB] sums, then for a
+  // sparse draft [C * NWAVE] list counts and [topk] kept ids, logits, q~
+  // values and corrections.
+  extern __shared__ __align__(16) uint32_t ee_cache[];
   __shared__ RowShared rs;
   __shared__ float shf[NWAVE];
   __shared__ int shi[NWAVE];
@@ -177,12 +296,19 @@ __global__ __launch_bounds__(WG) void early_exit_kernel(Args a) {
   __shared__ unsigned s_ticket;
   __shared__ int s_acc;
   const int K = a.K, C = a.C, S = 2 * K + 1;
-  const int c = blockIdx.x % C, b = blockIdx.x / C;
+  const int c = blockIdx.x % a.G, b = blockIdx.x / a.G;
   const int t = threadIdx.x, wave = t >> 6;
   uint32_t* pw = ee_cache;
   uint32_t* sub = ee_cache + (size_t)S * C * 4;
+  int* lcnt = reinterpret_cast<int*>(sub + (size_t)C * NSUB);
+  int* kid = lcnt + C * NWAVE;
+  float* kl = reinterpret_cast<float*>(kid + a.topk);
+  float* kq = kl + a.topk;
+  float* kcorr = kq + a.topk;
+  __shared__ float4 s_qs;  // sparse draft: {max kept logit, Z_q, q~(d), kept count} of the current position
   const float T = a.temp[b];
   const bool greedy = !is_sampling_temperature(T);
+  const bool sparse = SPARSE && !greedy;
   const float s = greedy ? 0.f : LOG2E / T;
   if (t < K) rs.tok[t] = a.tok[(size_t)b * K + t];
   if (t == 0) {
@@ -213,7 +339,10 @@ __global__ __launch_bounds__(WG) void early_exit_kernel(Args a) {
     if (ticket - base < size) {
       const int k = (int)(ticket - base);
       if (phase == STATS) {
-        ee_stats_chunk<ET, ALIGNED>(a, b, pos, k % C, greedy, k >= C, s, shf, shi, shsub);
+        ee_stats_chunk<ET, ALIGNED, SPARSE>(a, b, pos, k % C, greedy, k >= C, s, shf, shi, shsub);
+      } else if (sparse) {
+        const float MSt = mul_rn(rs.M[pos], s), rZt = 1.f / rs.Z[pos];
+        ee_residual_chunk_sparse<ET, ALIGNED>(a, b, pos, k, s, MSt, rZt, kid, kq, kcorr, (int)s_qs.w, shsub);
       } else {
         const float MSt = mul_rn(rs.M[pos], s), rZt = 1.f / rs.Z[pos];
         const float MSq = mul_rn(rs.M[K + 1 + pos], s), rZq = 1.f / rs.Z[K + 1 + pos];
@@ -225,14 +354,25 @@ __global__ __launch_bounds__(WG) void early_exit_kernel(Args a) {
     }
     // Every chunk of the current stage has been handed out: collect it.
     if (phase == STATS) {
-      const bool draft = !greedy && pos < K;
+      const bool draft = !greedy && pos < K && !sparse;
       const bool bonus = !greedy && pos == K;
       ok = wait_words(part_words(a, b, pos, 0), C * 4, pw + (size_t)pos * C * 4,
                       draft ? part_words(a, b, K + 1 + pos, 0) : (bonus ? a.subK + (size_t)b * C * NSUB : nullptr),
                       draft ? C * 4 : (bonus ? C * NSUB : 0),
                       draft ? pw + (size_t)(K + 1 + pos) * C * 4 : (bonus ? sub : nullptr),
                       wall_clock64() + WAIT_TICKS);
+      if constexpr (SPARSE)
+        if (ok && sparse && pos < K) ok = ee_select<ET>(a, b, pos, rs.tok[pos], lcnt, kid, &s_qs);
       if (!ok) break;
+      if constexpr (SPARSE) if (sparse && pos < K) {
+        const float4 qs = s_qs;
+        const float MSq = mul_rn(qs.x, s), rZq = 1.f / qs.y;
+        for (int j = t; j < (int)qs.w; j += WG) kq[j] = exp2_fast(fmaf(kl[j], s, -MSq)) * rZq;
+        if (t == 0) {
+          rs.M[K + 1 + pos] = qs.x;
+          rs.Z[K + 1 + pos] = qs.y;
+        }
+      }
       if (wave == 0) ee_merge_slot(a, rs, pw, pos, greedy, s);
       if (wave == 1 && draft) ee_merge_slot(a, rs, pw, K + 1 + pos, greedy, s);
       __syncthreads();
@@ -248,9 +388,13 @@ __global__ __launch_bounds__(WG) void early_exit_kernel(Args a) {
             if (d >= 0 && d < a.V) {
               const int cd = d / a.CS;
               const float lt = __uint_as_float(pw[((size_t)pos * C + cd) * 4 + 3]);
-              const float lq = __uint_as_float(pw[((size_t)(K + 1 + pos) * C + cd) * 4 + 3]);
               p = exp2_fast(fmaf(lt, s, -mul_rn(rs.M[pos], s))) / rs.Z[pos];
-              q = exp2_fast(fmaf(lq, s, -mul_rn(rs.M[K + 1 + pos], s))) / rs.Z[K + 1 + pos];
+              if (sparse) {
+                q = s_qs.z;  // q~(d) of the truncated draft
+              } else {
+                const float lq = __uint_as_float(pw[((size_t)(K + 1 + pos) * C + cd) * 4 + 3]);
+                q = exp2_fast(fmaf(lq, s, -mul_rn(rs.M[K + 1 + pos], s))) / rs.Z[K + 1 + pos];
+              }
             }
             const float u = a.uni[(size_t)b * (K + 1) + pos];
             acc = u * q < p;
@@ -296,13 +440,17 @@ __global__ __launch_bounds__(WG) void early_exit_kernel(Args a) {
       const float MSq = n < K ? mul_rn(rs.M[K + 1 + n], s) : 0.f;
       const float rZq = n < K ? 1.f / rs.Z[K + 1 + n] : 0.f;
       const RowView<true> view{pw, sub, true};
-      final_draw<ET, ALIGNED, true>(a, b, n, s, MSt, rZt, MSq, rZq, rs, view, nullptr, nullptr, 0);
+      if constexpr (SPARSE)
+        final_draw<ET, ALIGNED, true>(a, b, n, s, MSt, rZt, MSq, rZq, rs, view, sparse ? kid : nullptr, kq,
+                                      sparse && n < K ? (int)s_qs.w : 0);
+      else
+        final_draw<ET, ALIGNED, true>(a, b, n, s, MSt, rZt, MSq, rZq, rs, view, nullptr, nullptr, 0);
     }
   }
   // The last work-group of the row to finish clears its published words.
   __syncthreads();
   if (t == 0)
-    s_ticket = __hip_atomic_fetch_add(a.leave + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)C - 1u;
+    s_ticket = __hip_atomic_fetch_add(a.leave + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)a.G - 1u;
   __syncthreads();
   if (!s_ticket) return;
   const int last = ok ? pos : K;  // positions whose words may have been published
@@ -313,6 +461,26 @@ __global__ __launch_bounds__(WG) void early_exit_kernel(Args a) {
     for (int i = t; i < C * NSUB; i += WG) clear_word(a.subK + (size_t)b * C * NSUB + i);
   if (!ok || (!greedy && pos < K))
     for (int i = t; i < C * NSUB; i += WG) clear_word(a.subR + (size_t)b * C * NSUB + i);
+  if (SPARSE && (sparse || !ok)) {
+    // Published candidate lists and counts of the positions computed.
+    const int NL = C * NWAVE;
+    for (int p = 0; p < min(last + 1, K); ++p) {
+      const size_t slot = (size_t)b * K + p;
+      uint32_t* cw = reinterpret_cast<uint32_t*>(a.ccnt + slot * NL);
+      uint64_t* g = reinterpret_cast<uint64_t*>(a.cand) + slot * NL * WCAP;
+      for (int i = t; i < NL * WCAP; i += WG) {
+        const int L = i / WCAP, j = i % WCAP;
+        const uint32_t w = peek(cw + L);
+        const int n = w ? min((int)~w, WCAP) : (ok ? 0 : WCAP);
+        if (j < n) __hip_atomic_store(g + (size_t)L * WCAP + j, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __syncthreads();  // the counts are read before they are cleared
+      for (int i = t; i < NL; i += WG) clear_word(cw + i);
+      uint32_t* res = a.mres + slot * (4 + 2 * (size_t)a.topk);
+      for (int i = t; i < 4 + 2 * a.topk; i += WG) clear_word(res + i);
+      if (t == 0) __hip_atomic_store(a.mclaim + slot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
   if (t == 0) {
     __hip_atomic_store(a.claim + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(a.leave + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

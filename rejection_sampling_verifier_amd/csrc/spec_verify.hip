@@ -105,8 +105,11 @@ struct Args {
   float* kl;                 // [B, K] KL(p_i || q_i) out (spec_verify_kl: paired statistics), or null
   unsigned* claim;           // [B] early exit: stage tickets handed out
   unsigned* leave;           // [B] early exit: work-groups of the row that have finished
+  unsigned* mclaim;          // [B, K] early exit, sparse draft: work-groups that reached a position's selection
+  uint32_t* mres;            // [B, K, 4 + 2 topk] early exit, sparse draft: published selection results
   int GA;                    // statistics work-groups per row: (2K+1) * C
   int cache;                 // 1: finishing work-groups keep the row's words in dynamic LDS
+  int G;                     // early exit: work-groups per row
 };
 
 // ---- published words -------------------------------------------------------
@@ -129,6 +132,31 @@ __device__ __forceinline__ uint32_t got_u32(const uint32_t* p) { return ~peek(p)
 __device__ __forceinline__ float got_f32(const uint32_t* p) { return __uint_as_float(~peek(p)); }
 __device__ __forceinline__ void clear_word(uint32_t* p) {
   __hip_atomic_store(p, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Candidate lists read by another work-group (early exit): composites are
+// never zero, so each entry is published as itself with a write-through
+// agent-scope atomic store and read with agent-scope atomic loads; counts
+// are published words.  PUB = false: plain stores and loads (the next
+// kernel reads them).
+template <bool PUB>
+__device__ __forceinline__ void cand_st(uint64_t* p, uint64_t v) {
+  if constexpr (PUB) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else __builtin_nontemporal_store(v, p);
+}
+template <bool PUB>
+__device__ __forceinline__ uint64_t cand_ld(const uint64_t* p) {
+  if constexpr (PUB) return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else return *p;
+}
+template <bool PUB>
+__device__ __forceinline__ void cnt_st(int* p, int v) {
+  if constexpr (PUB) pub_u32(reinterpret_cast<uint32_t*>(p), (uint32_t)v);
+  else *p = v;
+}
+template <bool PUB>
+__device__ __forceinline__ int cnt_ld(const int* p) {
+  if constexpr (PUB) return (int)got_u32(reinterpret_cast<const uint32_t*>(p));
+  else return *p;
 }
 
 __device__ __forceinline__ uint32_t* part_words(const Args& a, int b, int slot, int c) {
@@ -236,11 +264,10 @@ struct Staged<float> {
 // tau with at least kk logits >= tau is the kk-th largest; logits above tau
 // are all kept, ties at tau are kept in increasing id order.  The kk kept
 // composites are written to dst[0..kk).
-template <typename ET>
+template <typename ET, bool PUB>
 __device__ void topk_chunk_exact(const u32x4 (&r)[NV_TILE], int lo, int len, int kk, uint64_t* dst,
                                  float* red) {
   constexpr int VEC = Tr<ET>::VEC;
-  __shared__ int s_pos;
   const int t = threadIdx.x;
   auto count_keys = [&](uint32_t thr, bool strict) {
     int n = 0;
@@ -258,18 +285,28 @@ __device__ void topk_chunk_exact(const u32x4 (&r)[NV_TILE], int lo, int len, int
     const uint32_t cand = tau | (1u << bit);
     if (count_keys(cand, false) >= kk) tau = cand;
   }
-  const int above = count_keys(tau, true);
-  if (t == 0) s_pos = 0;
-  __syncthreads();
+  // Logits above tau, then the first ties, each in id order (places by
+  // block scans, so that the lists -- and every sum over them -- do not
+  // depend on timing).
+  float carry = 0.f;
 #pragma unroll 1
-  for (int j = 0; j < NV_TILE; ++j)
+  for (int j = 0; j < NV_TILE; ++j) {
+    int mine = 0;
+    for (int e = 0; e < VEC; ++e)
+      mine += (j * WG + t) * VEC + e < len && order_key(Tr<ET>::at(r[j], e)) > tau;
+    float ex, tot;
+    block_scan((float)mine, red, ex, tot);
+    int at = (int)(carry + ex);
     for (int e = 0; e < VEC; ++e) {
       const float x = Tr<ET>::at(r[j], e);
       const int off = (j * WG + t) * VEC + e;
-      if (off < len && order_key(x) > tau) dst[atomicAdd(&s_pos, 1)] = composite(x, lo + off);
+      if (off < len && order_key(x) > tau) cand_st<PUB>(dst + at++, composite(x, lo + off));
     }
+    carry += tot;
+  }
+  const int above = (int)carry;
   const int need = kk - above;
-  float carry = 0.f;
+  carry = 0.f;
 #pragma unroll 1
   for (int j = 0; j < NV_TILE; ++j) {
     int mine = 0;
@@ -282,7 +319,7 @@ __device__ void topk_chunk_exact(const u32x4 (&r)[NV_TILE], int lo, int len, int
       const float x = Tr<ET>::at(r[j], e);
       const int off = (j * WG + t) * VEC + e;
       if (off < len && order_key(x) == tau) {
-        if (rank < need) dst[above + rank] = composite(x, lo + off);
+        if (rank < need) cand_st<PUB>(dst + above + rank, composite(x, lo + off));
         ++rank;
       }
     }
@@ -302,7 +339,7 @@ __device__ void topk_chunk_exact(const u32x4 (&r)[NV_TILE], int lo, int len, int
 // kernel selects exactly.  Exact path (k > 256, or a list over WCAP): the
 // chunk's exact top min(k, len) is stored contiguously across the four list
 // areas.
-template <typename ET>
+template <typename ET, bool PUB = false>
 __device__ void topk_chunk(const u32x4 (&r)[NV_TILE], int lo, int len, int k, typename Cand<ET>::T* dst,
                            int* cnts, float* red) {
   constexpr int VEC = Tr<ET>::VEC;
@@ -387,25 +424,31 @@ __device__ void topk_chunk(const u32x4 (&r)[NV_TILE], int lo, int len, int k, ty
       }
     }
     if (lane == 0) {
-      cnts[wave] = min(n, WCAP);
+      if (!PUB) cnts[wave] = min(n, WCAP);
       if (n > WCAP) s_over = 1;
     }
-    if (n <= WCAP) {
+    if (!PUB && n <= WCAP) {
       // The wave's list is complete: written at once, without waiting for
       // the other waves (a chunk with an overflowing list is rewritten by
       // the exact path below).  The merge kernel reads it once: streaming
       // stores.
       CT* wl = dst + wave * WCAP;
-      for (int q = lane; q < n; q += 64)
-        __builtin_nontemporal_store(Staged<ET>::composite_at(wl_stage[q], lo), wl + q);
+      for (int q = lane; q < n; q += 64) cand_st<PUB>(wl + q, Staged<ET>::composite_at(wl_stage[q], lo));
     }
     __syncthreads();
     done = s_over == 0;
+    if (PUB && done) {
+      // Published lists are written only once final, so that no entry is
+      // left past the counts (the reader and the clearing go by them).
+      CT* wl = dst + wave * WCAP;
+      for (int q = lane; q < n; q += 64) cand_st<PUB>(wl + q, Staged<ET>::composite_at(wl_stage[q], lo));
+      if (lane == 0) cnt_st<PUB>(cnts + wave, n);
+    }
   }
   if (!done) {
     __syncthreads();  // the fast path's lists are no longer read
-    topk_chunk_exact<ET>(r, lo, len, kk, dst, red);
-    if (t < NWAVE) cnts[t] = max(0, min(WCAP, kk - t * WCAP));
+    topk_chunk_exact<ET, PUB>(r, lo, len, kk, dst, red);
+    if (t < NWAVE) cnt_st<PUB>(cnts + t, max(0, min(WCAP, kk - t * WCAP)));
   }
 }
 
@@ -687,7 +730,7 @@ __device__ __forceinline__ float view_sub(const RowView<CACHED>& v, const uint32
 // Block-wide wait until the words p0[0..n0) and p1[0..n1) are published.
 // Decoded values are left in d0 / d1 (LDS) when those are given.  Returns
 // false (uniformly) if the deadline passed first.
-__device__ bool wait_words(const uint32_t* p0, int n0, uint32_t* d0, const uint32_t* p1, int n1, uint32_t* d1,
+__device__ __forceinline__ bool wait_words(const uint32_t* p0, int n0, uint32_t* d0, const uint32_t* p1, int n1, uint32_t* d1,
                            uint64_t deadline) {
   for (;;) {
     bool ok = true;
@@ -1151,7 +1194,7 @@ struct RegCands {
 };
 // Candidates read from their lists in global memory (one wave per list;
 // list L holds chunk L / NWAVE).
-template <typename ET>
+template <typename ET, bool PUB = false>
 struct ListCands {
   const typename Cand<ET>::T* g;
   const int* gcnt;
@@ -1160,8 +1203,8 @@ struct ListCands {
   __device__ __forceinline__ void each(F&& f) const {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     for (int L = wave; L < NL; L += NWAVE) {
-      const int n = gcnt[L];
-      for (int j = lane; j < n; j += 64) f(cand_composite<ET>(g[(size_t)L * WCAP + j], (L / NWAVE) * CS));
+      const int n = cnt_ld<PUB>(gcnt + L);
+      for (int j = lane; j < n; j += 64) f(cand_composite<ET>(cand_ld<PUB>(g + (size_t)L * WCAP + j), (L / NWAVE) * CS));
     }
   }
 };
@@ -1285,9 +1328,13 @@ __device__ __forceinline__ float take_kept(const Src& src, uint64_t thr, int d, 
 }
 
 // The merge of slot (row b, position i): `d` is the token whose q~ is
-// recorded (-1 for none).  Returns kk, the number of kept ids.
-template <typename ET>
-__device__ __forceinline__ int merge_body(const Args& a, int b, int i, int d) {
+// recorded (-1 for none).  Returns kk, the number of kept ids.  With PUB the
+// candidate lists are published ones (early exit), and the results go to
+// LDS instead of the workspace: {max kept logit, Z_q, q~(d), kk} to
+// *qs_out, the kept ids and logits in ascending id order to kid_out / kl_out.
+template <typename ET, bool PUB = false>
+__device__ __forceinline__ int merge_body(const Args& a, int b, int i, int d, float4* qs_out = nullptr,
+                                          int* kid_out = nullptr, float* kl_out = nullptr) {
   __shared__ __align__(16) uint64_t sel[SV_MAX_TOPK + 2];  // kept composites (+ a zero pad entry)
   __shared__ uint64_t ovf[MERGE_OVF];
   __shared__ uint32_t hist[RADIX_BINS];  // radix histogram, then the ranks of the kept entries
@@ -1320,9 +1367,10 @@ __device__ __forceinline__ int merge_body(const Args& a, int b, int i, int d) {
     // area holds WCAP entries).
     RegCands<ET> rc;
     rc.CS = a.CS;
-    const int my_cnt = lane < C ? gcnt[wave + NWAVE * lane] : 0;
+    const int my_cnt = lane < C ? cnt_ld<PUB>(gcnt + wave + NWAVE * lane) : 0;
 #pragma unroll
-    for (int r = 0; r < MERGE_REG; ++r) rc.v[r] = r < C ? g[(size_t)(wave + NWAVE * r) * WCAP + lane] : CT(0);
+    for (int r = 0; r < MERGE_REG; ++r)
+      rc.v[r] = r < C ? cand_ld<PUB>(g + (size_t)(wave + NWAVE * r) * WCAP + lane) : CT(0);
     __syncthreads();  // s_n / s_novf / rank initialised
     // Entries past the 64th go to the overflow buffer: one reservation per
     // wave, then one round of loads for entries 64..127 (entries 128 and
@@ -1352,7 +1400,7 @@ __device__ __forceinline__ int merge_body(const Args& a, int b, int i, int d) {
 #pragma unroll
       for (int r = 0; r < MERGE_REG; ++r) {
         const int n = r < C ? __builtin_amdgcn_readlane(my_cnt, r) : 0;
-        w2[r] = 64 + lane < n ? g[(size_t)(wave + NWAVE * r) * WCAP + 64 + lane] : CT(0);
+        w2[r] = 64 + lane < n ? cand_ld<PUB>(g + (size_t)(wave + NWAVE * r) * WCAP + 64 + lane) : CT(0);
       }
       int o = base;
 #pragma unroll
@@ -1361,7 +1409,7 @@ __device__ __forceinline__ int merge_body(const Args& a, int b, int i, int d) {
         if (64 + lane < n && o + lane < MERGE_OVF) ovf[o + lane] = cand_composite<ET>(w2[r], r * a.CS);
         for (int j = 128 + lane; j < n; j += 64)
           if (o + j - 64 < MERGE_OVF)
-            ovf[o + j - 64] = cand_composite<ET>(g[(size_t)(wave + NWAVE * r) * WCAP + j], r * a.CS);
+            ovf[o + j - 64] = cand_composite<ET>(cand_ld<PUB>(g + (size_t)(wave + NWAVE * r) * WCAP + j), r * a.CS);
         o += max(0, n - 64);
       }
     }
@@ -1372,13 +1420,13 @@ __device__ __forceinline__ int merge_body(const Args& a, int b, int i, int d) {
       thr = select_threshold(rc, kk, sh32, red, ired, hist, &m);
       z = take_kept(rc, thr, d, s, mul_rn(m, s), sel, &s_n, &s_ld);
     } else {
-      const ListCands<ET> lc{g, gcnt, NL, a.CS};
+      const ListCands<ET, PUB> lc{g, gcnt, NL, a.CS};
       thr = select_threshold(lc, kk, sh32, red, ired, hist, &m);
       z = take_kept(lc, thr, d, s, mul_rn(m, s), sel, &s_n, &s_ld);
     }
   } else {
     __syncthreads();
-    const ListCands<ET> lc{g, gcnt, NL, a.CS};
+    const ListCands<ET, PUB> lc{g, gcnt, NL, a.CS};
     thr = select_threshold(lc, kk, sh32, red, ired, hist, &m);
     z = take_kept(lc, thr, d, s, mul_rn(m, s), sel, &s_n, &s_ld);
   }
@@ -1406,15 +1454,20 @@ __device__ __forceinline__ int merge_body(const Args& a, int b, int i, int d) {
     atomicAdd(&rank[j], c);
   }
   __syncthreads();
-  uint2* kept = a.kept + slot * a.topk;
   for (int j = t; j < kk; j += WG) {
     const uint64_t v = sel[j];
-    kept[rank[j]] = make_uint2((uint32_t)composite_id(v), __float_as_uint(composite_value(v)));
+    if constexpr (PUB) {
+      kid_out[rank[j]] = composite_id(v);
+      kl_out[rank[j]] = composite_value(v);
+    } else {
+      a.kept[slot * a.topk + rank[j]] = make_uint2((uint32_t)composite_id(v), __float_as_uint(composite_value(v)));
+    }
   }
   if (t == 0) {
     const uint32_t lb = s_ld;
     const float qd = lb != 0xFFFFFFFFu ? exp2_fast(fmaf(__uint_as_float(lb), s, -ms)) / Z : 0.f;
-    a.qstat[slot] = make_float4(m, Z, qd, (float)kk);
+    if constexpr (PUB) *qs_out = make_float4(m, Z, qd, (float)kk);
+    else a.qstat[slot] = make_float4(m, Z, qd, (float)kk);
   }
   (void)lane;
   return kk;
@@ -1788,17 +1841,18 @@ constexpr int EE_MAX_LDS_WORDS = 14336;  // the early-exit kernel's dynamic LDS 
 struct EEPlan {
   int C = 0, CS = 0;
   size_t off_cnt = 0, off_part = 0, off_subK = 0, off_subR = 0, total = 0;
+  size_t off_cand = 0, off_ccnt = 0, off_mclaim = 0, off_mres = 0;
   size_t lds_bytes = 0;
 };
 
-int make_ee_plan(int B, int K, int V, int dtype, EEPlan& pl) {
+int make_ee_plan(int B, int K, int V, int dtype, int topk, EEPlan& pl) {
   if (B < 1 || K < 0 || V < 1 || (dtype != SV_BF16 && dtype != SV_F32)) return SV_ERR_ARG;
-  if (K > SV_MAX_K) return SV_ERR_UNSUPPORTED;
+  if (K > SV_MAX_K || topk > SV_MAX_TOPK) return SV_ERR_UNSUPPORTED;
   int C, CS;
   if (!vocab_split(V, dtype, C, CS)) return SV_ERR_UNSUPPORTED;
   if ((long long)B * C > INT_MAX) return SV_ERR_UNSUPPORTED;
   const size_t S = 2 * (size_t)K + 1;
-  const size_t words = S * C * 4 + (size_t)C * NSUB;
+  const size_t words = S * C * 4 + (size_t)C * NSUB + (topk > 0 ? (size_t)C * NWAVE + 4 * (size_t)topk : 0);
   if (words > (size_t)EE_MAX_LDS_WORDS) return SV_ERR_UNSUPPORTED;
   pl.C = C;
   pl.CS = CS;
@@ -1813,9 +1867,39 @@ int make_ee_plan(int B, int K, int V, int dtype, EEPlan& pl) {
   off = align256(off + sizeof(uint32_t) * (size_t)B * C * NSUB);
   pl.off_subR = off;
   off = align256(off + sizeof(uint32_t) * (size_t)B * C * NSUB);
+  if (topk > 0) {
+    // Published candidate lists and counts (zero between calls).
+    const size_t slots = (size_t)B * K;
+    pl.off_cand = off;
+    off = align256(off + sizeof(uint64_t) * slots * C * NWAVE * WCAP);
+    pl.off_ccnt = off;
+    off = align256(off + sizeof(int) * slots * C * NWAVE);
+    // The selection of each position: made by the first work-group of the
+    // row to reach it and published for the others.
+    pl.off_mclaim = off;
+    off = align256(off + sizeof(unsigned) * slots);
+    pl.off_mres = off;
+    off = align256(off + sizeof(uint32_t) * slots * (4 + 2 * (size_t)topk));
+  }
   pl.total = off;
   pl.lds_bytes = words * sizeof(uint32_t);
   return SV_OK;
+}
+
+// Work-groups per row of a truncated draft: as many as the device holds at
+// once with every row in flight, at most one per chunk.  A row's tickets go
+// to whichever of its work-groups ask, so any number of them computes the
+// row; with fewer, a work-group takes more tickets per stage and fewer sit
+// waiting at a stage's end (its selection) while other rows' work-groups
+// wait for a free slot.  Dense drafts keep one per chunk, which measured
+// faster for them.
+int ee_groups(const void* kernel, size_t lds, int B, int C) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return C;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, WG, lds) != hipSuccess || per_cu < 1) return C;
+  const long cap = (long)per_cu * cus;
+  return (int)std::max(1L, std::min((long)C, cap / B));
 }
 
 int run_early_exit(const void* tgt, const void* dft, const int32_t* tok, const float* uni, const float* temp,
@@ -1823,9 +1907,8 @@ int run_early_exit(const void* tgt, const void* dft, const int32_t* tok, const f
                    size_t* ws_bytes, hipStream_t st, float* probs, float* mass) {
   if (!ws_bytes || topk < 0) return SV_ERR_ARG;
   if (topk >= V) topk = 0;
-  if (topk > 0) return SV_ERR_UNSUPPORTED;
   EEPlan pl;
-  const int rc = make_ee_plan(B, K, V, dtype, pl);
+  const int rc = make_ee_plan(B, K, V, dtype, topk, pl);
   if (rc != SV_OK) return rc;
   if (!ws) {
     *ws_bytes = pl.total;
@@ -1844,16 +1927,25 @@ int run_early_exit(const void* tgt, const void* dft, const int32_t* tok, const f
   a.part = reinterpret_cast<uint32_t*>(base + pl.off_part);
   a.subK = reinterpret_cast<uint32_t*>(base + pl.off_subK);
   a.subR = reinterpret_cast<uint32_t*>(base + pl.off_subR);
-  a.B = B; a.K = K; a.V = V; a.C = pl.C; a.CS = pl.CS; a.topk = 0;
+  a.cand = topk > 0 ? static_cast<void*>(base + pl.off_cand) : nullptr;
+  a.ccnt = topk > 0 ? reinterpret_cast<int*>(base + pl.off_ccnt) : nullptr;
+  a.mclaim = topk > 0 ? reinterpret_cast<unsigned*>(base + pl.off_mclaim) : nullptr;
+  a.mres = topk > 0 ? reinterpret_cast<uint32_t*>(base + pl.off_mres) : nullptr;
+  a.B = B; a.K = K; a.V = V; a.C = pl.C; a.CS = pl.CS; a.topk = topk;
   const size_t esz = dtype == SV_BF16 ? 2 : 4;
   const bool aligned = (reinterpret_cast<uintptr_t>(tgt) % 16 == 0) &&
                        (K == 0 || reinterpret_cast<uintptr_t>(dft) % 16 == 0) && ((size_t)V * esz) % 16 == 0;
   (void)hipGetLastError();
-  if (dtype == SV_BF16)
-    return aligned ? launch(early_exit_kernel<uint16_t, true>, B * pl.C, pl.lds_bytes, st, nullptr, a)
-                   : launch(early_exit_kernel<uint16_t, false>, B * pl.C, pl.lds_bytes, st, nullptr, a);
-  return aligned ? launch(early_exit_kernel<float, true>, B * pl.C, pl.lds_bytes, st, nullptr, a)
-                 : launch(early_exit_kernel<float, false>, B * pl.C, pl.lds_bytes, st, nullptr, a);
+  void (*kernel)(Args);
+  if (topk > 0) {
+    if (dtype == SV_BF16) kernel = aligned ? early_exit_kernel<uint16_t, true, true> : early_exit_kernel<uint16_t, false, true>;
+    else kernel = aligned ? early_exit_kernel<float, true, true> : early_exit_kernel<float, false, true>;
+  } else {
+    if (dtype == SV_BF16) kernel = aligned ? early_exit_kernel<uint16_t, true, false> : early_exit_kernel<uint16_t, false, false>;
+    else kernel = aligned ? early_exit_kernel<float, true, false> : early_exit_kernel<float, false, false>;
+  }
+  a.G = topk > 0 ? ee_groups(reinterpret_cast<const void*>(kernel), pl.lds_bytes, B, pl.C) : pl.C;
+  return launch(kernel, B * a.G, pl.lds_bytes, st, nullptr, a);
 }
 
 // ---- draft trees ------------------------------------------------------------

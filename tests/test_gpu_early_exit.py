@@ -17,7 +17,7 @@ import torch
 
 import oracle
 import workloads as W
-from rejection_sampling_verifier_amd import (SpecVerifyError, new_early_exit_workspace, verify_early_exit,
+from rejection_sampling_verifier_amd import (new_early_exit_workspace, verify_early_exit,
                                              verify_probe, SV_BF16, SV_F32)
 from tests.parity import PROB_TOL, check_well_formed, decisions_firm, to_device
 
@@ -50,8 +50,9 @@ CASES = {
 
 def _both(d, x=None, ws=None):
     x = x if x is not None else to_device(d)
-    a = verify_probe(x["target"], x["draft"], x["tokens"], x["uniforms"], x["temperature"], 0)
-    e = verify_early_exit(x["target"], x["draft"], x["tokens"], x["uniforms"], x["temperature"], 0, probes=True,
+    k = int(d["topk"])
+    a = verify_probe(x["target"], x["draft"], x["tokens"], x["uniforms"], x["temperature"], k)
+    e = verify_early_exit(x["target"], x["draft"], x["tokens"], x["uniforms"], x["temperature"], k, probes=True,
                           workspace=ws)
     torch.cuda.synchronize()
     return [t.cpu().numpy() for t in a], [t.cpu().numpy() for t in e]
@@ -138,11 +139,73 @@ def test_out_of_range_draft_tokens_are_rejected():
     assert ee[1][0] == 0 and ee[1][1] <= 1 and ee[1][2] <= 2
 
 
-def test_sparse_draft_is_unsupported():
-    d = W.make(_case(B=2, K=2, topk=16, seed=38))
-    x = to_device(d)
-    with pytest.raises(SpecVerifyError):
-        verify_early_exit(x["target"], x["draft"], x["tokens"], x["uniforms"], x["temperature"], 16)
+SPARSE = {
+    "top128": _case(B=8, topk=128, seed=50),
+    "top1": _case(topk=1, seed=51),
+    "top3-ragged": _case(V=40001, topk=3, seed=52),
+    "top300-exact-path": _case(topk=300, seed=53),
+    "top1024-exact-path": _case(B=3, topk=1024, seed=54),
+    "f32-top64": _case(dtype=W.F32, V=20001, topk=64, seed=55),
+    "mixed-greedy-top128": _case(B=10, greedy_rows=4, topk=128, seed=56),
+    "small-V-top128": _case(V=200, peaks=3, topk=128, seed=57),
+    "K0-top16": _case(K=0, topk=16, seed=58),
+    "high-agreement-top32": _case(B=16, K=8, draft_sigma=0.05, topk=32, seed=59),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SPARSE))
+def test_sparse_draft_equals_spec_verify_bitwise(name):
+    """A truncated draft: each reached position's selection is made inside
+    the call, from the same candidate lists and in the same order as
+    spec_verify's, so the results are the same bits."""
+    d = W.make(SPARSE[name])
+    lin, ee = _both(d)
+    _assert_equal(d, lin, ee)
+    check_well_formed(d, ee[0], ee[1])
+
+
+def test_sparse_draft_on_the_top128_workload():
+    d = W.make(4)
+    lin, ee = _both(d)
+    _assert_equal(d, lin, ee)
+    print(f"[early-exit] config 4: mean accepted {ee[1].mean():.3f} of {d['tokens'].shape[1]}", flush=True)
+
+
+def test_sparse_draft_matches_oracle_directly():
+    d = W.make(_case(B=8, K=4, V=30000, draft_sigma=1.2, greedy_rows=2, topk=64, seed=60))
+    _, ee = _both(d)
+    out, nacc, probs, mass = ee
+    ref = oracle.verify(d["target"], d["draft"], d["tokens"], d["uniforms"], d["temperature"], 64, d["dtype"])
+    near = 0
+    for b, r in enumerate(ref):
+        if not r.greedy:
+            n = min(r.n + 1, d["tokens"].shape[1])
+            np.testing.assert_allclose(probs[b, :n, 0], r.p_d[:n], rtol=0, atol=PROB_TOL)
+            np.testing.assert_allclose(probs[b, :n, 1], r.q_d[:n], rtol=0, atol=PROB_TOL)
+            assert abs(float(mass[b]) - r.S) <= PROB_TOL
+        if decisions_firm(r, d["uniforms"][b]):
+            assert int(nacc[b]) == r.n and list(out[b]) == list(r.tokens), (b, out[b], r.tokens)
+        else:
+            near += 1
+    assert near <= 3
+
+
+def test_sparse_workspace_is_left_clean_between_calls():
+    """Published candidate lists are cleared by the row's last work-group,
+    also where a chunk's fast selection overflowed into the exact path."""
+    ws = new_early_exit_workspace(8, 4, 40000, SV_BF16, topk_draft=300)
+    cases = [_case(B=8, K=4, draft_sigma=2.0, topk=300, seed=61),
+             _case(B=8, K=4, draft_sigma=0.3, topk=300, seed=62),
+             _case(B=5, K=2, V=30000, topk=8, seed=63)]
+    for case in cases + cases[:1]:
+        d = W.make(case)
+        x = to_device(d)
+        a = verify_probe(x["target"], x["draft"], x["tokens"], x["uniforms"], x["temperature"], case.topk)
+        e = verify_early_exit(x["target"], x["draft"], x["tokens"], x["uniforms"], x["temperature"], case.topk,
+                              probes=True, workspace=ws)
+        torch.cuda.synchronize()
+        _assert_equal(d, [t.cpu().numpy() for t in a], [t.cpu().numpy() for t in e])
+        assert int(ws.count_nonzero().item()) == 0
 
 
 def test_f32_workspace_query_and_reuse_across_shapes():

@@ -121,15 +121,18 @@ def test_greedy_rows_ignore_uniforms_and_drafts():
     check_rows(d, gpu1)
 
 
-@pytest.mark.parametrize("case", ["dense", "top128"])
+@pytest.mark.parametrize("case", ["dense", "top128", "top1024"])
 def test_deterministic_bitwise(case):
     """Fixed-order reductions everywhere: repeated calls give the same bits,
     including the sparse draft's selection, whose candidate lists spill past
-    64 entries into a shared buffer (config-4 sizes)."""
+    64 entries into a shared buffer (config-4 sizes), and the exact chunk
+    selection (top-1024), whose lists are placed by block scans."""
     if case == "dense":
         d = W.make(_case(B=16, V=70000, seed=33))
-    else:
+    elif case == "top128":
         d = W.make(W.replace(W.CONFIGS[4], B=32))
+    else:
+        d = W.make(_case(B=8, K=3, V=40000, topk=1024, seed=35))
     x = to_device(d)
     a = run_gpu(d, x)
     for _ in range(3):
