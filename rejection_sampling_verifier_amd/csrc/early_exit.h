@@ -10,9 +10,7 @@
 // section 4).  The result equals spec_verify's bit for bit: every sum is
 // formed in the same order.
 //
-// One launch, one work-group per (row, chunk) for a dense draft; for a
-// truncated draft fewer per row, as many as the device holds at once with
-// every row in flight.  A row's work is cut into
+// One launch, one work-group per (row, chunk).  A row's work is cut into
 // stages: stage i <= n computes the chunk statistics of position i (target,
 // and the draft of a sampling row); after a rejection at n one more stage
 // computes the residual sums of position n.  Each stage is cut into tickets,
@@ -296,7 +294,10 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(SPARSE ? 4 :
   __shared__ unsigned s_ticket;
   __shared__ int s_acc;
   const int K = a.K, C = a.C, S = 2 * K + 1;
-  const int c = blockIdx.x % a.G, b = blockIdx.x / a.G;
+  // Chunk-major numbering: the first work-groups to start are a few per row
+  // for every row; later ones join their rows as slots free up (a row still
+  // running by then gets the help, one already done is walked through).
+  const int b = blockIdx.x % a.B, c = blockIdx.x / a.B;
   const int t = threadIdx.x, wave = t >> 6;
   uint32_t* pw = ee_cache;
   uint32_t* sub = ee_cache + (size_t)S * C * 4;
@@ -450,7 +451,7 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(SPARSE ? 4 :
   // The last work-group of the row to finish clears its published words.
   __syncthreads();
   if (t == 0)
-    s_ticket = __hip_atomic_fetch_add(a.leave + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)a.G - 1u;
+    s_ticket = __hip_atomic_fetch_add(a.leave + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)C - 1u;
   __syncthreads();
   if (!s_ticket) return;
   const int last = ok ? pos : K;  // positions whose words may have been published

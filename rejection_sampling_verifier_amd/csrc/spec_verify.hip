@@ -109,7 +109,6 @@ struct Args {
   uint32_t* mres;            // [B, K, 4 + 2 topk] early exit, sparse draft: published selection results
   int GA;                    // statistics work-groups per row: (2K+1) * C
   int cache;                 // 1: finishing work-groups keep the row's words in dynamic LDS
-  int G;                     // early exit: work-groups per row
 };
 
 // ---- published words -------------------------------------------------------
@@ -1886,22 +1885,6 @@ int make_ee_plan(int B, int K, int V, int dtype, int topk, EEPlan& pl) {
   return SV_OK;
 }
 
-// Work-groups per row of a truncated draft: as many as the device holds at
-// once with every row in flight, at most one per chunk.  A row's tickets go
-// to whichever of its work-groups ask, so any number of them computes the
-// row; with fewer, a work-group takes more tickets per stage and fewer sit
-// waiting at a stage's end (its selection) while other rows' work-groups
-// wait for a free slot.  Dense drafts keep one per chunk, which measured
-// faster for them.
-int ee_groups(const void* kernel, size_t lds, int B, int C) {
-  int dev = 0, cus = 0, per_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return C;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, WG, lds) != hipSuccess || per_cu < 1) return C;
-  const long cap = (long)per_cu * cus;
-  return (int)std::max(1L, std::min((long)C, cap / B));
-}
-
 int run_early_exit(const void* tgt, const void* dft, const int32_t* tok, const float* uni, const float* temp,
                    int B, int K, int V, int topk, int dtype, int32_t* out, int32_t* nacc, void* ws,
                    size_t* ws_bytes, hipStream_t st, float* probs, float* mass) {
@@ -1944,8 +1927,7 @@ int run_early_exit(const void* tgt, const void* dft, const int32_t* tok, const f
     if (dtype == SV_BF16) kernel = aligned ? early_exit_kernel<uint16_t, true, false> : early_exit_kernel<uint16_t, false, false>;
     else kernel = aligned ? early_exit_kernel<float, true, false> : early_exit_kernel<float, false, false>;
   }
-  a.G = topk > 0 ? ee_groups(reinterpret_cast<const void*>(kernel), pl.lds_bytes, B, pl.C) : pl.C;
-  return launch(kernel, B * a.G, pl.lds_bytes, st, nullptr, a);
+  return launch(kernel, B * pl.C, pl.lds_bytes, st, nullptr, a);
 }
 
 // ---- draft trees ------------------------------------------------------------
