@@ -340,7 +340,10 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(SPARSE ? 4 :
     if (ticket - base < size) {
       const int k = (int)(ticket - base);
       if (phase == STATS) {
-        ee_stats_chunk<ET, ALIGNED, SPARSE>(a, b, pos, k % C, greedy, k >= C, s, shf, shi, shsub);
+        // A truncated draft's chunks come first in their stage: its selection
+        // then overlaps the target chunks.
+        const bool dslot = (SPARSE && sparse && pos < K) ? k < C : k >= C;
+        ee_stats_chunk<ET, ALIGNED, SPARSE>(a, b, pos, k % C, greedy, dslot, s, shf, shi, shsub);
       } else if (sparse) {
         const float MSt = mul_rn(rs.M[pos], s), rZt = 1.f / rs.Z[pos];
         ee_residual_chunk_sparse<ET, ALIGNED>(a, b, pos, k, s, MSt, rZt, kid, kq, kcorr, (int)s_qs.w, shsub);
@@ -357,13 +360,15 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(SPARSE ? 4 :
     if (phase == STATS) {
       const bool draft = !greedy && pos < K && !sparse;
       const bool bonus = !greedy && pos == K;
-      ok = wait_words(part_words(a, b, pos, 0), C * 4, pw + (size_t)pos * C * 4,
-                      draft ? part_words(a, b, K + 1 + pos, 0) : (bonus ? a.subK + (size_t)b * C * NSUB : nullptr),
-                      draft ? C * 4 : (bonus ? C * NSUB : 0),
-                      draft ? pw + (size_t)(K + 1 + pos) * C * 4 : (bonus ? sub : nullptr),
-                      wall_clock64() + WAIT_TICKS);
+      // A truncated draft's selection first (its chunks were handed out first).
       if constexpr (SPARSE)
-        if (ok && sparse && pos < K) ok = ee_select<ET>(a, b, pos, rs.tok[pos], lcnt, kid, &s_qs);
+        if (sparse && pos < K) ok = ee_select<ET>(a, b, pos, rs.tok[pos], lcnt, kid, &s_qs);
+      if (ok)
+        ok = wait_words(part_words(a, b, pos, 0), C * 4, pw + (size_t)pos * C * 4,
+                        draft ? part_words(a, b, K + 1 + pos, 0) : (bonus ? a.subK + (size_t)b * C * NSUB : nullptr),
+                        draft ? C * 4 : (bonus ? C * NSUB : 0),
+                        draft ? pw + (size_t)(K + 1 + pos) * C * 4 : (bonus ? sub : nullptr),
+                        wall_clock64() + WAIT_TICKS);
       if (!ok) break;
       if constexpr (SPARSE) if (sparse && pos < K) {
         const float4 qs = s_qs;
