@@ -92,7 +92,7 @@ __device__ __forceinline__ void load_tile(const ET* __restrict__ row, int lo, in
     if (ALIGNED) {
       // Aligned rows hold a multiple of VEC logits and chunks start on VEC
       // boundaries, so a vector is either wholly inside the chunk or past it.
-      if (e < len) r[j] = *reinterpret_cast<const u32x4*>(row + lo + e);
+      if (e < len) r[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + lo + e));
       else r[j] = u32x4{f, f, f, f};
     } else {
       u32x4 v = {f, f, f, f};
