@@ -79,7 +79,6 @@ void tree_stats_kernel(TreeArgs a) {
   const int node = slot % N;
   const bool is_draft = slot >= N;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  __shared__ unsigned long long s_kids;
   __shared__ float shf[NWAVE];
   __shared__ int shi[NWAVE];
   __shared__ float shsub[NSUB];
@@ -90,16 +89,13 @@ void tree_stats_kernel(TreeArgs a) {
   // first checks that its node has children (and that the row samples).
   u32x4 r[NV_TILE];
   if (!is_draft) load_tile<ET, ALIGNED, NV_TILE>(row, lo, len, r);
-  if (wave == 0) {
-    const int p = (lane > 0 && lane < N) ? a.par[(size_t)b * N + lane] : -1;
-    const unsigned long long m = __ballot(lane > node && lane < N && p == node);
-    if (lane == 0) s_kids = m;
-  }
+  // Every wave forms the node's children mask itself (no barrier before a
+  // leaf's draft work-group can leave).
   const float T = a.temp[b];
+  const int p = (lane > 0 && lane < N) ? a.par[(size_t)b * N + lane] : -1;
+  const unsigned long long kids = __ballot(lane > node && lane < N && p == node);
   if (a.probes && slot == 0 && c == 0)
     for (int i = t; i < 3 * N; i += WG) a.probes[(size_t)b * 3 * N + i] = __builtin_nanf("");
-  __syncthreads();
-  const unsigned long long kids = s_kids;
   const bool greedy = !is_sampling_temperature(T);
   if (is_draft) {
     if (greedy || kids == 0) return;  // no children drawn from this draft (or a greedy row)
