@@ -10,20 +10,23 @@
 // section 4).  The result equals spec_verify's bit for bit: every sum is
 // formed in the same order.
 //
-// One launch, one work-group per (row, chunk).  A row's work is cut into
-// stages: stage i <= n computes the chunk statistics of position i (target,
-// and the draft of a sampling row); after a rejection at n one more stage
-// computes the residual sums of position n.  Each stage is cut into tickets,
-// one per chunk and slot, numbered consecutively across the stages and
-// handed out by an agent-scope counter to the row's work-groups in the order
-// they ask.  A work-group holding a ticket of the current stage computes
-// that chunk and publishes it; holding a ticket of a later stage, it waits
-// for the current stage's words -- every ticket of which has been handed out
-// to a running work-group -- and takes the row's next decision with them.  So a stage is computed
-// only once the decision before it has accepted, and no work-group waits for
-// one that may not have started.  The holder of the first ticket past the
-// last stage draws the final token; the last work-group of the row to finish
-// clears the row's published words and counters for the next call.
+// One launch, one work-group per (row, chunk), numbered chunk-major.  A
+// row's work is cut into stages: stage i <= n computes the chunk statistics
+// of position i (target, and the draft of a sampling row; a truncated draft
+// publishes candidate lists instead, and the first work-group to collect the
+// stage makes the position's selection for all); after a rejection at n one
+// more stage computes the residual sums of position n.  Each stage is cut
+// into tickets, one per chunk and slot, numbered consecutively across the
+// stages and handed out by an agent-scope counter to the row's work-groups
+// in the order they ask.  A work-group holding a ticket of the current stage
+// computes that chunk and publishes it; holding a ticket of a later stage,
+// it waits for the current stage's words -- every ticket of which has been
+// handed out to a running work-group -- and takes the row's next decision
+// with them.  So a stage is computed only once the decision before it has
+// accepted, and no work-group waits for one that may not have started.  The
+// holder of the first ticket past the last stage draws the final token; the
+// last work-group of the row to finish clears the row's published words and
+// counters for the next call.
 
 // Statistics of one chunk of one slot (target position `pos`, or the draft
 // of position `pos` when `draft`), published as the words spec_verify's

@@ -729,8 +729,8 @@ __device__ __forceinline__ float view_sub(const RowView<CACHED>& v, const uint32
 // Block-wide wait until the words p0[0..n0) and p1[0..n1) are published.
 // Decoded values are left in d0 / d1 (LDS) when those are given.  Returns
 // false (uniformly) if the deadline passed first.
-__device__ __forceinline__ bool wait_words(const uint32_t* p0, int n0, uint32_t* d0, const uint32_t* p1, int n1, uint32_t* d1,
-                           uint64_t deadline) {
+__device__ __forceinline__ bool wait_words(const uint32_t* p0, int n0, uint32_t* d0, const uint32_t* p1, int n1,
+                                           uint32_t* d1, uint64_t deadline) {
   for (;;) {
     bool ok = true;
     for (int i = threadIdx.x; i < n0; i += WG) {
@@ -1203,7 +1203,8 @@ struct ListCands {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     for (int L = wave; L < NL; L += NWAVE) {
       const int n = cnt_ld<PUB>(gcnt + L);
-      for (int j = lane; j < n; j += 64) f(cand_composite<ET>(cand_ld<PUB>(g + (size_t)L * WCAP + j), (L / NWAVE) * CS));
+      for (int j = lane; j < n; j += 64)
+        f(cand_composite<ET>(cand_ld<PUB>(g + (size_t)L * WCAP + j), (L / NWAVE) * CS));
     }
   }
 };
@@ -1919,15 +1920,13 @@ int run_early_exit(const void* tgt, const void* dft, const int32_t* tok, const f
   const bool aligned = (reinterpret_cast<uintptr_t>(tgt) % 16 == 0) &&
                        (K == 0 || reinterpret_cast<uintptr_t>(dft) % 16 == 0) && ((size_t)V * esz) % 16 == 0;
   (void)hipGetLastError();
-  void (*kernel)(Args);
-  if (topk > 0) {
-    if (dtype == SV_BF16) kernel = aligned ? early_exit_kernel<uint16_t, true, true> : early_exit_kernel<uint16_t, false, true>;
-    else kernel = aligned ? early_exit_kernel<float, true, true> : early_exit_kernel<float, false, true>;
-  } else {
-    if (dtype == SV_BF16) kernel = aligned ? early_exit_kernel<uint16_t, true, false> : early_exit_kernel<uint16_t, false, false>;
-    else kernel = aligned ? early_exit_kernel<float, true, false> : early_exit_kernel<float, false, false>;
-  }
-  return launch(kernel, B * pl.C, pl.lds_bytes, st, nullptr, a);
+  // Indexed by [bf16][aligned][truncated draft].
+  void (*const kernels[2][2][2])(Args) = {
+      {{early_exit_kernel<float, false, false>, early_exit_kernel<float, false, true>},
+       {early_exit_kernel<float, true, false>, early_exit_kernel<float, true, true>}},
+      {{early_exit_kernel<uint16_t, false, false>, early_exit_kernel<uint16_t, false, true>},
+       {early_exit_kernel<uint16_t, true, false>, early_exit_kernel<uint16_t, true, true>}}};
+  return launch(kernels[dtype == SV_BF16][aligned][topk > 0], B * pl.C, pl.lds_bytes, st, nullptr, a);
 }
 
 // ---- draft trees ------------------------------------------------------------

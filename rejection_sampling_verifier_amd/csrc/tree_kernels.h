@@ -377,9 +377,9 @@ __device__ __forceinline__ void tree_walk(TreeRow& tr, int N, int V, int v, int 
 // (the residual's W when `want_total`).
 // ============================================================================
 template <typename ET, bool ALIGNED>
-__device__ __forceinline__ int tree_draw(const TreeArgs& a, const TreeRow& tr, const uint32_t* pw, const float* csub, int b,
-                         int v, int mode, float cscale, float uK, float* S_out, const int* kid = nullptr,
-                         const float* kq = nullptr, int nkept = 0) {
+__device__ __forceinline__ int tree_draw(const TreeArgs& a, const TreeRow& tr, const uint32_t* pw, const float* csub,
+                                         int b, int v, int mode, float cscale, float uK, float* S_out,
+                                         const int* kid = nullptr, const float* kq = nullptr, int nkept = 0) {
   constexpr int VEC = Tr<ET>::VEC;
   const int N = a.N, C = a.C, l = threadIdx.x & 63;
   const float s = tr.s;
@@ -572,8 +572,8 @@ __device__ __forceinline__ void tree_chunk_residual_sparse(const TreeArgs& a, co
 // Sub-block sums of max(0, p_v - c q_v) over one chunk (all threads); the 32
 // sums go to dst[0..NSUB).
 template <typename ET, bool ALIGNED>
-__device__ __forceinline__ void tree_chunk_residual(const TreeArgs& a, const TreeRow& tr, int b, int v, float cscale, int chunk,
-                                    float* dst) {
+__device__ __forceinline__ void tree_chunk_residual(const TreeArgs& a, const TreeRow& tr, int b, int v, float cscale,
+                                                    int chunk, float* dst) {
   constexpr int VEC = Tr<ET>::VEC;
   const int N = a.N, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const float s = tr.s;
