@@ -45,6 +45,8 @@ CASES = {
     "cold-T": _case(temperature=0.05, seed=21),
     "low-agreement": _case(B=16, draft_sigma=3.0, seed=22),
     "high-agreement": _case(B=16, K=8, draft_sigma=0.05, seed=33),
+    "K64-high-agreement": _case(B=4, K=64, V=3000, draft_sigma=0.02, seed=76),
+    "V1M-ragged-unaligned": _case(B=2, K=2, V=(1 << 20) + 3, seed=78),
 }
 
 
@@ -150,6 +152,7 @@ SPARSE = {
     "small-V-top128": _case(V=200, peaks=3, topk=128, seed=57),
     "K0-top16": _case(K=0, topk=16, seed=58),
     "high-agreement-top32": _case(B=16, K=8, draft_sigma=0.05, topk=32, seed=59),
+    "K64-top16-high-agreement": _case(B=3, K=64, V=5000, draft_sigma=0.02, topk=16, seed=77),
 }
 
 

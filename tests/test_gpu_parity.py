@@ -56,6 +56,13 @@ SMALL = {
     "topk-ge-V": _case(V=3000, topk=3000, seed=30),
     "topk-small-V": _case(V=200, peaks=3, topk=128, seed=31),
     "topk-K0": _case(K=0, topk=16, seed=32),
+    # the largest K (SV_MAX_K = 64), and a vocabulary of a million ids
+    "K64": _case(B=4, K=64, V=5000, seed=70),
+    "K64-high-agreement": _case(B=4, K=64, V=3000, draft_sigma=0.02, seed=71),
+    "K64-top16": _case(B=3, K=64, V=5000, topk=16, draft_sigma=0.02, seed=73),
+    "K64-mixed-greedy": _case(B=4, K=64, V=4000, greedy_rows=2, draft_sigma=0.02, seed=74),
+    "V1M-ragged-unaligned": _case(B=2, K=2, V=(1 << 20) + 3, seed=72),
+    "V1M-top128": _case(B=2, K=2, V=1 << 20, topk=128, seed=75),
 }
 
 

@@ -147,6 +147,11 @@ CASES = {
     "top128-wide-low-agreement": _case(V=9000, draft_sigma=3.0, parents=WIDE_8, topk=128, seed=105),
     "top300-exact-path-random": _case(V=20001, parents=None, nodes=10, topk=300, seed=106),
     "top128-mixed-greedy": _case(B=10, V=30000, parents=None, nodes=16, greedy_rows=4, topk=128, seed=107),
+    # the largest trees (SV_MAX_NODES = 64)
+    "64-node-random": _case(B=4, V=5000, parents=None, nodes=64, seed=108),
+    "64-node-chain-high-agreement": _case(B=3, V=3000, parents=tuple([-1] + list(range(63))), draft_sigma=0.02,
+                                          seed=109),
+    "top16-64-node-random": _case(B=3, V=5000, parents=None, nodes=64, topk=16, seed=110),
 }
 
 
