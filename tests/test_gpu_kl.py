@@ -40,6 +40,7 @@ CASES = {
     "cold-T": _case(temperature=0.2, seed=84),
     "low-agreement": _case(draft_sigma=3.0, seed=85),
     "K12": _case(K=12, V=5000, seed=86),
+    "K64-high-agreement": _case(B=4, K=64, V=3000, draft_sigma=0.02, seed=88),
 }
 
 

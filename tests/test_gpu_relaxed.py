@@ -41,6 +41,7 @@ CASES = {
     "topk128": _case(topk=128, seed=72),
     "mixed-greedy": _case(B=12, greedy_rows=5, seed=73),
     "K12": _case(K=12, V=5000, seed=74),
+    "K64-top16": _case(B=4, K=64, V=5000, draft_sigma=0.3, topk=16, seed=77),
 }
 
 
