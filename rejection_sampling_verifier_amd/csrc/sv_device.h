@@ -80,8 +80,10 @@ template <> struct Tr<float> {
 // (row, position) in registers.  Thread t owns vector j at element offset
 // (j * WG + t) * VEC of the chunk, so each load instruction of the wave covers
 // 64 consecutive 16-byte vectors (1 KiB).  Elements past the chunk end read
-// as -inf.  ALIGNED requires row + lo to be 16-byte aligned.
-template <typename ET, bool ALIGNED, int NV>
+// as -inf.  ALIGNED requires row + lo to be 16-byte aligned.  Logits read
+// once use nontemporal loads (NT); rows read again soon (a tree node's
+// residual passes) keep the cache.
+template <typename ET, bool ALIGNED, int NV, bool NT = true>
 __device__ __forceinline__ void load_tile(const ET* __restrict__ row, int lo, int len, u32x4 (&r)[NV]) {
   constexpr int VEC = Tr<ET>::VEC;
   const int t = threadIdx.x;
@@ -92,7 +94,10 @@ __device__ __forceinline__ void load_tile(const ET* __restrict__ row, int lo, in
     if (ALIGNED) {
       // Aligned rows hold a multiple of VEC logits and chunks start on VEC
       // boundaries, so a vector is either wholly inside the chunk or past it.
-      if (e < len) r[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + lo + e));
+      if (e < len) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(row + lo + e);
+        r[j] = NT ? __builtin_nontemporal_load(src) : *src;
+      }
       else r[j] = u32x4{f, f, f, f};
     } else {
       u32x4 v = {f, f, f, f};

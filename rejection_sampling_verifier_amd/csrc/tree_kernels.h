@@ -528,7 +528,7 @@ __device__ __forceinline__ void tree_chunk_residual_sparse(const TreeArgs& a, co
   const int len = min(a.CS, a.V - lo);
   const ET* trow = tree_row<ET>(a, false, b, v);
   u32x4 rt[NV_TILE];
-  load_tile<ET, ALIGNED, NV_TILE>(trow, lo, len, rt);
+  load_tile<ET, ALIGNED, NV_TILE, false>(trow, lo, len, rt);
   for (int j = t; j < nkept; j += WG) {
     const int id = kid[j];
     float cv = 0.f;
@@ -582,8 +582,8 @@ __device__ __forceinline__ void tree_chunk_residual(const TreeArgs& a, const Tre
   const int lo = chunk * a.CS;
   const int len = min(a.CS, a.V - lo);
   u32x4 rt[NV_TILE], rq[NV_TILE];
-  load_tile<ET, ALIGNED, NV_TILE>(tree_row<ET>(a, false, b, v), lo, len, rt);
-  load_tile<ET, ALIGNED, NV_TILE>(tree_row<ET>(a, true, b, v), lo, len, rq);
+  load_tile<ET, ALIGNED, NV_TILE, false>(tree_row<ET>(a, false, b, v), lo, len, rt);
+  load_tile<ET, ALIGNED, NV_TILE, false>(tree_row<ET>(a, true, b, v), lo, len, rq);
 #pragma unroll
   for (int j = 0; j < NV_TILE; ++j) {
     float w0 = 0.f, w1 = 0.f;
