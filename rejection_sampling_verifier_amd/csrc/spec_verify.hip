@@ -64,9 +64,12 @@ namespace {
 #ifndef SV_NV_TILE
 #define SV_NV_TILE 8
 #endif
-#ifndef SV_MAX_WAVES
-#define SV_MAX_WAVES 4                      // cap on waves per SIMD (0: none)
-#endif
+// Waves per SIMD of the statistics kernels (a cap: more in flight measured
+// slower), for dense drafts and for truncated ones, whose draft work-groups
+// hold their slots longer (candidate filter and list stores).  The tree's
+// statistics kernel keeps STATS_WAVES: at five it spills.
+constexpr int STATS_WAVES = 4;
+constexpr int STATS_WAVES_TOPK = 5;
 constexpr int NV_TILE = SV_NV_TILE;        // 16-byte vectors per thread per chunk
 constexpr int NSUB = NV_TILE * NWAVE;      // sub-blocks per chunk (one wave x one vector row)
 constexpr int MAX_C = 2048;                // vocabulary chunks per position
@@ -587,12 +590,8 @@ __device__ __forceinline__ void stats_body(const Args& a, int b, int slot, int c
   (void)S;
 }
 
-template <typename ET, bool ALIGNED>
-__global__ __launch_bounds__(WG)
-#if SV_MAX_WAVES > 0
-__attribute__((amdgpu_waves_per_eu(SV_MAX_WAVES, SV_MAX_WAVES)))
-#endif
-void stats_kernel(Args a) {
+template <typename ET, bool ALIGNED, int WAVES>
+__global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(WAVES, WAVES))) void stats_kernel(Args a) {
   const int S = 2 * a.K + 1;
   const int rest = blockIdx.x / a.C;
   stats_body<ET, ALIGNED>(a, rest / S, rest % S, blockIdx.x % a.C);
@@ -1762,7 +1761,8 @@ int launch(F kernel, int grid, size_t lds, hipStream_t st, hipEvent_t* ev2, cons
 template <typename ET, bool AL>
 int launch_typed(const Args& a, size_t lds, size_t merge_lds, hipStream_t st, hipEvent_t* ev) {
   int rc = a.kl ? launch(paired_kernel<ET, AL>, a.B * (a.K + 1) * a.C, 0, st, ev, a)
-                : launch(stats_kernel<ET, AL>, a.B * a.GA, 0, st, ev, a);
+                : launch(a.topk > 0 ? stats_kernel<ET, AL, STATS_WAVES_TOPK> : stats_kernel<ET, AL, STATS_WAVES>,
+                         a.B * a.GA, 0, st, ev, a);
   if (rc != SV_OK) return rc;
   if (a.topk > 0 && a.K > 0) {
     rc = launch(merge_kernel<ET>, a.B * a.K, merge_lds, st, ev ? ev + 2 : nullptr, a);

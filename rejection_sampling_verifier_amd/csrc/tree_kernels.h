@@ -65,10 +65,7 @@ __device__ __forceinline__ uint32_t* tree_part(const TreeArgs& a, int b, int slo
 // Statistics of one (row, node slot, chunk).
 // ============================================================================
 template <typename ET, bool ALIGNED>
-__global__ __launch_bounds__(WG)
-#if SV_MAX_WAVES > 0
-__attribute__((amdgpu_waves_per_eu(SV_MAX_WAVES, SV_MAX_WAVES)))
-#endif
+__global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(STATS_WAVES, STATS_WAVES)))
 void tree_stats_kernel(TreeArgs a) {
   constexpr int VEC = Tr<ET>::VEC;
   const int N = a.N;
