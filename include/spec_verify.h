@@ -32,9 +32,10 @@
  * All pointers are device pointers owned by the caller.  Inputs are read
  * only; outputs are fully overwritten.  The library allocates nothing, keeps
  * no mutable global state and never synchronises: every call only enqueues
- * at most three kernels on `stream`; outputs are valid once the caller has
- * synchronised that stream.  Calls on different
- * workspaces are reentrant.
+ * at most three kernels on `stream` (no memory set or copy), so a call can
+ * be captured in a HIP graph and replayed; outputs are valid once the caller
+ * has synchronised that stream.  Calls on different workspaces are
+ * reentrant.
  */
 #ifndef SPEC_VERIFY_H
 #define SPEC_VERIFY_H
