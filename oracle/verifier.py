@@ -27,7 +27,7 @@ used, every step is restated from the mathematics):
   (lossless speculative decoding keeps the target distribution) and the
   strict branch of the section 6 harness (q <= p always accepts).
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
 
 * uniforms ``u[K+1]``: ``u[i]`` (i < K) drives the acceptance test at
   position i, ``u[K]`` drives the final (correction or bonus) sample;
