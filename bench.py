@@ -131,7 +131,7 @@ def main():
                          "(whole-call rate only; per-kernel times come from a rocprofv3 trace)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(rows shard across GPUs without communication; see the design notes)",
               file=sys.stderr)
         sys.exit(2)
