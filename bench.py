@@ -126,6 +126,9 @@ def main():
                     help="time spec_verify_early_exit (reads each row's logits up to its first rejection)")
     ap.add_argument("--tree", type=int, default=-1,
                     help="time spec_verify_tree on this draft-tree workload instead (0 = 61-node tree)")
+    ap.add_argument("--streams", type=int, default=1,
+                    help="independent batches in flight: consecutive calls alternate over this many streams, "
+                         "each with its own workspace and outputs (1: one call after the other)")
     ap.add_argument("--relaxed", default="",
                     help="ALPHA,MAX_RANK,MIN_PROB: time the lossy relaxed acceptance rule instead "
                          "(whole-call rate only; per-kernel times come from a rocprofv3 trace)")
@@ -167,21 +170,32 @@ def main():
     B, Kp1, V = base["target"].shape
     K = Kp1 - 1
     dt_code = rsv.SV_BF16 if d["dtype"] == "bf16" else rsv.SV_F32
-    ws = rsv.new_workspace(B, K, V, d["topk"], dt_code, dev)
-    out = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
-    nacc = torch.empty((B,), dtype=torch.int32, device=dev)
-    stream = torch.cuda.current_stream(dev)
+    # One stream, workspace and output set per batch in flight.
+    ns = max(1, args.streams)
+    main_stream = torch.cuda.current_stream(dev)
+    streams = [main_stream] + [torch.cuda.Stream(dev) for _ in range(ns - 1)]
+
+    def buffers():
+        return {"ws": rsv.new_workspace(B, K, V, d["topk"], dt_code, dev),
+                "out": torch.empty((B, K + 1), dtype=torch.int32, device=dev),
+                "nacc": torch.empty((B,), dtype=torch.int32, device=dev),
+                "kl": torch.empty((B, K), dtype=torch.float32, device=dev) if args.kl else None,
+                "ee_ws": (rsv.new_early_exit_workspace(B, K, V, dt_code, dev, d["topk"])
+                          if args.early_exit else None)}
+
+    bufs = [buffers() for _ in range(ns)]
+    nacc = bufs[0]["nacc"]
 
     rule = None
     if args.relaxed:
         a_, r_, p_ = args.relaxed.split(",")
         rule = dict(alpha=float(a_), max_rank=int(r_), min_prob=float(p_))
 
-    kl_buf = torch.empty((B, K), dtype=torch.float32, device=dev) if args.kl else None
-    ee_ws = rsv.new_early_exit_workspace(B, K, V, dt_code, dev, d["topk"]) if args.early_exit else None
-
     def step(i, timer=None):
         x = sets[i % copies]
+        k = 0 if timer is not None else i % ns  # per-kernel timing runs on one stream
+        stream, bf = streams[k], bufs[k]
+        out, nacc, ws, ee_ws, kl_buf = bf["out"], bf["nacc"], bf["ws"], bf["ee_ws"], bf["kl"]
         if args.early_exit and timer is None:
             rsv.verify_early_exit(x["target"], x["draft"], x["tokens"], x["uniforms"], x["temperature"],
                                   d["topk"], out_tokens=out, num_accepted=nacc, workspace=ee_ws,
@@ -208,10 +222,14 @@ def main():
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
-    ev0.record(stream)
+    ev0.record(main_stream)
+    for s_ in streams[1:]:
+        s_.wait_event(ev0)
     for i in range(args.steps):
         step(i)
-    ev1.record(stream)
+    for s_ in streams[1:]:
+        main_stream.wait_stream(s_)
+    ev1.record(main_stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - w0) * 1e3
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
@@ -268,7 +286,8 @@ def main():
                    "temperature": float(case.temperature), "greedy_rows": case.greedy_rows,
                    "topk_draft": case.topk, "input_copies": copies,
                    "acceptance": "lossless" if rule is None else f"relaxed {rule}",
-                   "kl_per_position": bool(args.kl), "early_exit": bool(args.early_exit)},
+                   "kl_per_position": bool(args.kl), "early_exit": bool(args.early_exit),
+                   "streams": ns},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": None if args.early_exit else traffic, "kernel": roof_kernel,
