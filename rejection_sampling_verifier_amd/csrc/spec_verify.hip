@@ -1169,7 +1169,8 @@ __device__ __forceinline__ void final_draw(const Args& a, int b, int n, float s,
 // and read from their lists in global memory at every pass otherwise.
 // ============================================================================
 constexpr int MERGE_REG = 12;     // lists per wave whose first 64 entries are held in registers
-constexpr int MERGE_OVF = 512;    // list entries past the 64th, gathered into LDS
+constexpr int MERGE_OVF = 480;    // list entries past the 64th, gathered into LDS (sized so that
+                                  // eight merge work-groups fit a CU's LDS)
 
 // Candidates of one (row, position) held by the work-group: wave w holds
 // lists w, w + NWAVE, ... (one register per list, lane l holding entry l, as
@@ -1472,8 +1473,10 @@ __device__ __forceinline__ int merge_body(const Args& a, int b, int i, int d, fl
   return kk;
 }
 
+// Eight waves per SIMD (64 VGPRs, a few spills): the 2048 work-groups of a
+// 256-row, 8-draft batch are resident at once.
 template <typename ET>
-__global__ __launch_bounds__(WG) void merge_kernel(Args a) {
+__global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(8, 8))) void merge_kernel(Args a) {
   const int i = blockIdx.x % a.K, b = blockIdx.x / a.K;
   if (!is_sampling_temperature(a.temp[b])) return;
   merge_body<ET>(a, b, i, a.tok[(size_t)b * a.K + i]);
