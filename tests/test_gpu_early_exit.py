@@ -153,6 +153,8 @@ SPARSE = {
     "K0-top16": _case(K=0, topk=16, seed=58),
     "high-agreement-top32": _case(B=16, K=8, draft_sigma=0.05, topk=32, seed=59),
     "K64-top16-high-agreement": _case(B=3, K=64, V=5000, draft_sigma=0.02, topk=16, seed=77),
+    "topk-ge-V-is-dense": _case(V=3000, topk=3000, seed=79),
+    "top1023-of-1024": _case(B=4, K=3, V=1024, topk=1023, seed=80),
 }
 
 
