@@ -1,5 +1,6 @@
 """A seeded sweep of small random shapes: the GPU against the fp64 oracle
-(spec_verify) and early exit against spec_verify bit for bit.
+(spec_verify and spec_verify_tree) and early exit against spec_verify bit
+for bit.
 
 Shapes mix B, K (0 to 9), V (1 to 9,000, aligned and ragged), bf16 and
 fp32, dense and top-k drafts (k from 1 to 1,024, and past V), greedy and
@@ -56,3 +57,32 @@ def test_sweep_case(i):
     np.testing.assert_array_equal(e_n, lin[1])
     np.testing.assert_array_equal(e_out, lin[0])
     check_well_formed(d, e_out, e_n)
+
+
+N_TREE_CASES = 60
+
+
+def _draw_tree_case(i: int) -> W.TreeCase:
+    rng = np.random.default_rng(7000 + i)
+    B = int(rng.integers(1, 9))
+    V = int(rng.choice([1, 8, 100, 1024, 4097, 9000]))
+    topk = int(rng.choice([0, 0, 1, 16, 128, max(1, min(V - 1, 1024)), V])) if rng.random() < 0.5 else 0
+    return W.TreeCase(B=B, V=V, parents=None, nodes=int(rng.integers(1, 65)),
+                      dtype=W.BF16 if rng.random() < 0.6 else W.F32,
+                      target_sigma=float(rng.choice([0.5, 2.0, 3.0])),
+                      peaks=int(rng.integers(0, 4)) if V >= 100 else 0,
+                      draft_sigma=float(rng.choice([0.05, 0.8, 3.0])),
+                      temperature=float(rng.choice([0.05, 0.3, 1.0, 2.5])),
+                      greedy_rows=int(rng.integers(0, B + 1)), topk=topk, seed=8000 + i, name=f"tree-sweep-{i}")
+
+
+@pytest.mark.parametrize("i", range(N_TREE_CASES))
+def test_tree_sweep_case(i):
+    """Random trees of 1 to 64 nodes (one per row) against the fp64 tree walk."""
+    from tests.test_gpu_tree import check_tree_rows, run_tree_gpu
+
+    case = _draw_tree_case(i)
+    print(f"[tree-sweep] {i}: B={case.B} nodes={case.nodes} V={case.V} {case.dtype} topk={case.topk} "
+          f"T={case.temperature} greedy={case.greedy_rows} sigma={case.draft_sigma}", flush=True)
+    d = W.make_tree(case)
+    check_tree_rows(d, run_tree_gpu(d))
