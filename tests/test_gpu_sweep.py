@@ -86,3 +86,26 @@ def test_tree_sweep_case(i):
           f"T={case.temperature} greedy={case.greedy_rows} sigma={case.draft_sigma}", flush=True)
     d = W.make_tree(case)
     check_tree_rows(d, run_tree_gpu(d))
+
+
+@pytest.mark.parametrize("i", range(0, N_CASES, 3))
+def test_sweep_relaxed_and_kl(i):
+    """The same shapes under a random relaxed rule (against the oracle's
+    relaxed walk) and, for dense drafts, the per-position KL."""
+    import oracle
+    from tests.parity import run_gpu
+    from tests.test_gpu_kl import _check_kl
+    from rejection_sampling_verifier_amd import verify_kl
+
+    case = _draw_case(i)
+    rng = np.random.default_rng(9000 + i)
+    rule = oracle.Relaxed(alpha=float(rng.choice([0.0, 0.2, 0.5, 1.0])),
+                          max_rank=int(rng.choice([0, 1, 3, 10])), min_prob=float(rng.choice([0.0, 0.01, 0.1])))
+    print(f"[sweep-relaxed] {i}: B={case.B} K={case.K} V={case.V} {case.dtype} topk={case.topk} {rule}", flush=True)
+    d = W.make(case)
+    check_rows(d, run_gpu(d, relaxed=rule), relaxed=rule)
+    if case.topk == 0 or case.topk >= case.V:
+        x = to_device(d)
+        _, _, kl = verify_kl(x["target"], x["draft"], x["tokens"], x["uniforms"], x["temperature"])
+        torch.cuda.synchronize()
+        _check_kl(d, kl.cpu().numpy(), list(range(case.B)))
