@@ -157,6 +157,14 @@ class RowResult:
     fallback    True when a zero residual fell back to the target row.
     ranks       int64 [K]: target rank of each draft token under the relaxed
                 rule (0 when not computed or the token is out of range).
+    accept      bool [K]: the rule's outcome at every position (also those
+                after the first rejection); False for greedy rows.  A forced
+                outcome (see verify_row) does not change it.
+    t           u_K * S, the point of the final distribution's CDF that was
+                sampled (NaN for greedy rows).
+    near_ids    ids of positive weight whose CDF interval [C(x-1), C(x)]
+                meets [t - draw_eps, t + draw_eps]: the draws a computation
+                rounding differently could return (empty for greedy rows).
     """
 
     tokens: np.ndarray
@@ -169,6 +177,9 @@ class RowResult:
     gap: float
     fallback: bool
     ranks: np.ndarray = None
+    accept: np.ndarray = None
+    t: float = float("nan")
+    near_ids: tuple = ()
 
     def min_margin(self) -> float:
         """Smallest margin over the decisions this row actually took.
@@ -185,7 +196,32 @@ class RowResult:
         return min(m, self.gap)
 
 
-def verify_row(tl, dl, d, u, T: float, k: int = 0, relaxed: Relaxed | None = None) -> RowResult:
+def inverse_cdf(w: np.ndarray, t: float, draw_eps: float):
+    """Inverse-CDF draw from the non-negative weights w at the point t.
+
+    Ascending token id; the drawn token is the smallest x whose cumulative
+    weight C(x) exceeds t (strict, so a zero-weight token is never drawn).
+    If no C(x) exceeds t, which happens only when rounding lets t reach the
+    total, the last id of positive weight is drawn.  Returns (x, gap,
+    near_ids): gap is the distance from t to the nearer edge of x's interval
+    [C(x-1), C(x)]; near_ids lists every id of positive weight whose interval
+    meets [t - draw_eps, t + draw_eps].
+    """
+    C = np.cumsum(w)
+    above = np.flatnonzero(C > t)
+    if above.size:
+        x = int(above[0])
+    else:  # t reached the top only through rounding
+        x = int(np.flatnonzero(w > 0)[-1])
+    lo = C[x - 1] if x > 0 else 0.0
+    gap = float(min(t - lo, C[x] - t))
+    starts = np.concatenate(([0.0], C[:-1]))
+    near = np.flatnonzero((w > 0) & (starts <= t + draw_eps) & (C >= t - draw_eps))
+    return x, gap, tuple(int(i) for i in near)
+
+
+def verify_row(tl, dl, d, u, T: float, k: int = 0, relaxed: Relaxed | None = None,
+               force: dict | None = None, draw_eps: float = 1e-5) -> RowResult:
     """Verify one row of K draft tokens against K+1 target positions.
 
     tl  float64 [K+1, V] target logits; row i is the target's next-token
@@ -202,6 +238,12 @@ def verify_row(tl, dl, d, u, T: float, k: int = 0, relaxed: Relaxed | None = Non
         final draw are unchanged by it (reading: a relaxed rejection is
         corrected from the same residual norm(max(0, p - q)), which the pages
         leave open).
+    force   optional {position: accepted} overriding the rule's outcome at
+        those positions of a sampling row.  The verifier itself never uses
+        it; a test uses it to follow the other outcome of a decision that
+        lies within rounding distance of its threshold, which a computation
+        in another precision may take.
+    draw_eps  half-width of the window around t that defines near_ids.
     """
     tl = np.asarray(tl, dtype=np.float64)
     Kp1, V = tl.shape
@@ -226,7 +268,8 @@ def verify_row(tl, dl, d, u, T: float, k: int = 0, relaxed: Relaxed | None = Non
         tokens[:n] = d[:n]
         tokens[n] = a[n]
         return RowResult(tokens, n, True, nanK, nanK.copy(), nanK.copy(),
-                         float("nan"), float("inf"), False)
+                         float("nan"), float("inf"), False, np.zeros(K, dtype=np.int64),
+                         np.zeros(K, dtype=bool))
 
     dl = np.zeros((0, V)) if K == 0 else np.asarray(dl, dtype=np.float64).reshape(K, V)
     P =[tempered_softmax(tl[i], T) for i in range(K + 1)]
@@ -277,9 +320,12 @@ def verify_row(tl, dl, d, u, T: float, k: int = 0, relaxed: Relaxed | None = Non
                 m = min(m, abs(u[i] * q - g))
                 accept[i] = u[i] * q < g
         margins[i] = m
+    taken = accept.copy()
+    for i, outcome in (force or {}).items():
+        taken[int(i)] = bool(outcome)
     n = K
     for i in range(K):
-        if not accept[i]:
+        if not taken[i]:
             n = i
             break
 
@@ -301,18 +347,11 @@ def verify_row(tl, dl, d, u, T: float, k: int = 0, relaxed: Relaxed | None = Non
     # Inverse-CDF sample with u_K: ascending token id, first x whose
     # cumulative weight exceeds t = u_K * S.
     t = u[K] * S
-    C = np.cumsum(w)
-    above = np.flatnonzero(C > t)
-    if above.size:
-        x = int(above[0])
-    else:  # t reached the top only through rounding
-        x = int(np.flatnonzero(w > 0)[-1])
-    lo = C[x - 1] if x > 0 else 0.0
-    gap = float(min(t - lo, C[x] - t))
+    x, gap, near_ids = inverse_cdf(w, t, draw_eps)
 
     tokens[:n] = d[:n]
     tokens[n] = x
-    return RowResult(tokens, n, False, p_d, q_d, margins, S, gap, fallback, ranks)
+    return RowResult(tokens, n, False, p_d, q_d, margins, S, gap, fallback, ranks, accept, float(t), near_ids)
 
 
 def verify(target_raw, draft_raw, draft_tokens, uniforms, temperature,
@@ -389,13 +428,21 @@ class TreeResult:
     greedy      True for a greedy row (T <= 0).
     final_w     float64 [V]: the normalised distribution the final token was
                 drawn from (None for greedy rows).
-    S           its mass before normalisation (1 for a bonus draw at a leaf).
-    gap         distance of t = u_0 * S to the nearer edge of the drawn
-                token's CDF interval (inf for greedy rows).
+    S           mass of that distribution in units of the node's target p:
+                1 for a bonus draw at a leaf, else the product of the masses
+                removed by normalisation at each rejection (the mass of
+                max(0, p - c q) with c the accumulated draft weight).
+    gap         distance of t = u_0 * sum(final_w) to the nearer edge of the
+                drawn token's CDF interval (inf for greedy rows).
     fallback    True when a residual of mass 0 fell back to the node's target.
     tested      [(node, p(d), q(d), r(d), threshold)] for every sibling
                 tested, in order; threshold = r(d) / q(d) (inf when q(d) = 0).
     margins     |u_node * q(d) - r(d)| for each tested node, in order.
+    accepts     the rule's outcome for each tested node, in order (a forced
+                outcome does not change it).
+    t           the point of the final distribution's CDF that was sampled.
+    near_ids    ids of positive weight whose CDF interval meets
+                [t - draw_eps, t + draw_eps].
     """
 
     path: list
@@ -408,8 +455,13 @@ class TreeResult:
     fallback: bool
     tested: list
     margins: list
+    accepts: list = None
+    t: float = float("nan")
+    near_ids: tuple = ()
 
     def min_margin(self) -> float:
+        """Smallest margin over the decisions the walk took: every tested
+        sibling and the final draw.  Greedy decisions compare exact values."""
         if self.greedy:
             return float("inf")
         return min(min(self.margins, default=float("inf")), self.gap)
@@ -427,8 +479,10 @@ def tree_children(parent, N: int) -> list:
     return ch
 
 
-def verify_tree_row(tl, dl, tok, parent, u, T: float, k: int = 0) -> TreeResult:
-    """Verify one row's draft tree against the target.
+def verify_tree_row(tl, dl, tok, parent, u, T: float, k: int = 0, force: dict | None = None,
+                    draw_eps: float = 1e-5) -> TreeResult:
+    """Verify one row's draft tree against the target ([RheoSampling]
+    section 4, RheoVerification).
 
     tl      float64 [N, V]: target logits at each node (the next-token
             distribution after the path to that node; node 0 is the root).
@@ -439,17 +493,23 @@ def verify_tree_row(tl, dl, tok, parent, u, T: float, k: int = 0) -> TreeResult:
     u       float [N]: u[c] drives the test of node c; u[0] the final draw.
     T       temperature; T <= 0 selects greedy verification.
     k       sparse draft truncation at every node (0 = none).
+    force   optional {node: accepted} overriding the rule's outcome for those
+            nodes (tests only: following the other outcome of a decision
+            within rounding distance of its threshold).
+    draw_eps  half-width of the window around t that defines near_ids.
+
+    The walk, as the page states it: at node v the distribution the next
+    candidate is tested against starts as v's target p.  A candidate with
+    token d is accepted with probability min(1, r(d)/q(d)), i.e. iff
+    u * q(d) < r(d), and the walk descends into it.  After a rejection r is
+    replaced by norm(max(0, r - q)) and the next sibling is tested against
+    it.  When every child is rejected the final token is drawn from the last
+    r; at a leaf it is drawn from the leaf's target (the bonus token).
 
     Reading (the pages leave the sibling draw open): siblings are independent
-    draws from the drafter's distribution at their parent, tested in id order.
-    The first sibling is accepted with probability min(1, p/q) at its token;
-    after a rejection the target is replaced by the residual r = norm(max(0,
-    r - q)) and the next sibling is tested against r with min(1, r/q); an
-    accepted node is descended into.  With r_0 = p, every residual is
-    r_j = max(0, p - c_j q) / W_j with c_0 = 0, W_0 = 1, c_{j+1} = c_j + W_j
-    and W_j = sum_x max(0, p - c_j q).  When every child is rejected the final
-    token is drawn from the last residual; at a leaf it is drawn from the
-    leaf's target (the bonus token).
+    draws from the drafter's distribution at their parent, tested in id
+    order.  A residual of mass 0 (reachable only through rounding) ends the
+    walk with a draw from the node's target.
     """
     tl = np.asarray(tl, dtype=np.float64)
     N, V = tl.shape
@@ -458,6 +518,7 @@ def verify_tree_row(tl, dl, tok, parent, u, T: float, k: int = 0) -> TreeResult:
     ch = tree_children(parent, N)
     tokens = np.full(N, -1, dtype=np.int64)
     path = []
+    force = force or {}
     if not (T > 0):
         # Greedy: descend into the first child (in id order) equal to the
         # node's target argmax; when none is, emit the argmax.
@@ -471,9 +532,9 @@ def verify_tree_row(tl, dl, tok, parent, u, T: float, k: int = 0) -> TreeResult:
             v = nxt
         tokens[: len(path)] = [int(tok[c]) for c in path]
         tokens[len(path)] = int(np.argmax(tl[v]))
-        return TreeResult(path, tokens, len(path), True, None, float("nan"), float("inf"), False, [], [])
+        return TreeResult(path, tokens, len(path), True, None, float("nan"), float("inf"), False, [], [], [])
     dl = np.asarray(dl, dtype=np.float64).reshape(N, V)
-    tested, margins = [], []
+    tested, margins, accepts = [], [], []
     fallback = False
     v = 0
     while True:
@@ -483,39 +544,41 @@ def verify_tree_row(tl, dl, tok, parent, u, T: float, k: int = 0) -> TreeResult:
             break
         keep = topk_keep_mask(dl[v], k)
         Q = tempered_softmax(np.where(keep, dl[v], -np.inf), T)
-        c, W = 0.0, 1.0
+        r = P                  # the distribution the next sibling is tested against
+        S = 1.0                # mass of r in units of p
         accepted = None
         for child in ch[v]:
             d = int(tok[child])
-            pd, qd = (P[d], Q[d]) if 0 <= d < V else (0.0, 0.0)
-            rd = max(0.0, pd - c * qd) / W
+            pd, qd, rd = (P[d], Q[d], r[d]) if 0 <= d < V else (0.0, 0.0, 0.0)
+            ok = u[child] * qd < rd
             tested.append((child, pd, qd, rd, rd / qd if qd > 0 else float("inf")))
             margins.append(abs(u[child] * qd - rd))
-            if u[child] * qd < rd:
+            accepts.append(bool(ok))
+            if force.get(child, ok):
                 accepted = child
                 break
-            c = c + W
-            W = float(np.sum(np.maximum(0.0, P - c * Q)))
-            if W == 0.0:          # only through rounding (c4)
+            res = np.maximum(0.0, r - Q)   # rejected: r <- norm(max(0, r - q))
+            m = float(np.sum(res))
+            if m == 0.0:                   # only through rounding (c4)
+                fallback = True
                 break
+            r = res / m
+            S = S * m
         if accepted is not None:
             path.append(accepted)
             v = accepted
             continue
-        if W == 0.0:
-            w, S, fallback = P, 1.0, True
+        if fallback:
+            w, S = P, 1.0
         else:
-            w, S = np.maximum(0.0, P - c * Q), W
+            w = r
         break
-    t = u[0] * S
-    C = np.cumsum(w)
-    hits = np.flatnonzero(C > t)      # first token whose cumulative weight exceeds t (c3)
-    x = int(hits[0]) if hits.size else int(np.flatnonzero(w > 0)[-1])
-    lo = C[x - 1] if x > 0 else 0.0
-    gap = float(min(t - lo, C[x] - t))
+    t = u[0] * float(np.sum(w))
+    x, gap, near_ids = inverse_cdf(w, t, draw_eps)
     tokens[: len(path)] = [int(tok[c]) for c in path]
     tokens[len(path)] = x
-    return TreeResult(path, tokens, len(path), False, w / np.sum(w), float(S), gap, fallback, tested, margins)
+    return TreeResult(path, tokens, len(path), False, w / np.sum(w), float(S), gap, fallback, tested, margins,
+                      accepts, float(t), near_ids)
 
 
 def verify_tree(target_raw, draft_raw, tokens, parents, uniforms, temperature, topk: int, dtype: str,

@@ -7,9 +7,14 @@ a wrong oracle: a flipped residual sign, a reused uniform, a shifted slot
 index, a transposed acceptance ratio, a dropped temperature, an off-by-one
 top-k, a non-strict inverse CDF, a wrong greedy replacement, or in the relaxed
 rule a dropped factor in gamma, a rank that counts ties or an off-by-one
-rank guard, and in the tree walk a reset residual scale, siblings tested
-against the target instead of the residual, a final draw from the target or a
-greedy walk that ignores the argmax.
+rank guard, and in the tree walk a residual taken from the target instead of
+the last residual, a residual left unnormalised, siblings tested against the
+target instead of the residual, a final draw from the target or a greedy walk
+that ignores the argmax.  The batch wrappers are covered too (a shifted row
+index, a greedy row whose draft is read), as are the margins (a margin taken
+over positions the scan never reached, or without the final draw), the forced
+outcomes tests use to follow the other side of a near decision, and the set
+of draws near the sampled point.
 """
 
 from __future__ import annotations
@@ -26,7 +31,7 @@ SRC = open(ov.__file__).read()
 
 MUTANTS = {
     "residual_sign": ("w = np.maximum(0.0, P[n] - Q[n])", "w = np.maximum(0.0, Q[n] - P[n])"),
-    "reuse_u_n": ("    t = u[K] * S\n    C = np.cumsum(w)", "    t = u[n] * S\n    C = np.cumsum(w)"),
+    "reuse_u_n": ("    t = u[K] * S\n    x, gap", "    t = u[n] * S\n    x, gap"),
     "shifted_target_slot": ("p_d[i] = P[i][tok]", "p_d[i] = P[min(i + 1, K)][tok]"),
     "transposed_ratio": ("accept[i] = u[i] * q_d[i] < p_d[i]", "accept[i] = u[i] * p_d[i] < q_d[i]"),
     "draft_without_temperature": ("Q.append(tempered_softmax(np.where(keep, dl[i], -np.inf), T))",
@@ -49,11 +54,27 @@ MUTANTS = {
                     "return float(np.sum(Q[m] * (np.log(Q[m]) - np.log(P[m]))))"),
     "kl_without_temperature": ("    P = tempered_softmax(target_logits, T)\n    Q = tempered_softmax(draft_logits, T)",
                                "    P = tempered_softmax(target_logits, 1.0)\n    Q = tempered_softmax(draft_logits, 1.0)"),
-    "tree_scale_reset": ("            c = c + W\n", "            c = W\n"),
-    "tree_siblings_against_target": ("            rd = max(0.0, pd - c * qd) / W\n", "            rd = pd\n"),
-    "tree_final_from_target": ("            w, S = np.maximum(0.0, P - c * Q), W\n", "            w, S = P, 1.0\n"),
+    "tree_residual_from_target": ("            res = np.maximum(0.0, r - Q)",
+                                  "            res = np.maximum(0.0, P - Q)"),
+    "tree_residual_not_normalised": ("            r = res / m\n", "            r = res\n"),
+    "tree_siblings_against_target": ("pd, qd, rd = (P[d], Q[d], r[d])", "pd, qd, rd = (P[d], Q[d], P[d])"),
+    "tree_final_from_target": ("        else:\n            w = r\n        break", "        else:\n            w = P\n        break"),
     "tree_descends_first_child": ("            nxt = next((c for c in ch[v] if int(tok[c]) == a), None)",
                                   "            nxt = ch[v][0] if ch[v] else None"),
+    "verify_shifted_row": ("        tl = decode_logits(target_raw[b], dtype)\n        T = float(temperature[b])",
+                           "        tl = decode_logits(target_raw[(b + 1) % B], dtype)\n        T = float(temperature[b])"),
+    "verify_greedy_reads_draft": ("        if K > 0 and T > 0:\n            dl = decode_logits(draft_raw[b], dtype)",
+                                  "        if K > 0:\n            dl = decode_logits(draft_raw[b], dtype)"),
+    "verify_tree_shifted_row": ("        tl = decode_logits(target_raw[b], dtype)\n        dl = decode_logits(draft_raw[b], dtype) if T",
+                                "        tl = decode_logits(target_raw[(b + 1) % B], dtype)\n        dl = decode_logits(draft_raw[b], dtype) if T"),
+    "verify_tree_greedy_reads_draft": ("dl = decode_logits(draft_raw[b], dtype) if T > 0 else None",
+                                       "dl = decode_logits(draft_raw[b], dtype)"),
+    "margin_over_unreached": ("reached = self.margins[: min(self.n + 1, K)]", "reached = self.margins"),
+    "margin_without_draw": ("        return min(m, self.gap)", "        return m"),
+    "tree_margin_without_draw": ("return min(min(self.margins, default=float(\"inf\")), self.gap)",
+                                 "return min(self.margins, default=float(\"inf\"))"),
+    "force_ignored": ("        taken[int(i)] = bool(outcome)", "        pass"),
+    "near_ids_only_the_draw": ("(starts <= t + draw_eps) & (C >= t - draw_eps)", "(starts <= t) & (C > t)"),
     "guard_ignores_rank": ("if relaxed.max_rank > 0 and ranks[i] > relaxed.max_rank:",
                            "if relaxed.max_rank > 0 and ranks[i] > relaxed.max_rank + 1:"),
 }
@@ -96,6 +117,12 @@ def _run_pins():
         lambda: pins.test_tree_lossless_enumeration("fan2", 4, 1.0, 0, 41),
         lambda: pins.test_tree_lossless_enumeration("binary2", 4, 1.2, 0, 43),
         pins.test_tree_greedy_is_greedy_decode,
+        lambda: pins.test_verify_batch_equals_rows_and_skips_greedy_drafts(0),
+        pins.test_verify_tree_batch_equals_rows_and_skips_greedy_drafts,
+        pins.test_min_margin_takes_reached_decisions_and_the_draw,
+        pins.test_tree_min_margin_takes_tested_nodes_and_the_draw,
+        pins.test_forced_outcome_follows_the_other_path,
+        pins.test_near_ids_are_the_neighbours_of_t,
     ]
     failed = 0
     for c in cases:
@@ -117,6 +144,6 @@ def test_pins_catch_mutant(name, monkeypatch):
         monkeypatch.setattr(pins, attr, getattr(mod, attr))
     # The relaxed-rule pins reach these through the oracle package.
     for attr in ("Relaxed", "target_rank", "relaxed_gamma", "kl_divergence", "verify_tree_row",
-                 "tree_children"):
+                 "tree_children", "verify", "verify_tree", "verify_row"):
         monkeypatch.setattr(pins.oracle, attr, getattr(mod, attr))
     assert _run_pins() > 0, f"no pin caught the planted mistake {name!r}"

@@ -726,20 +726,25 @@ def test_tree_greedy_is_greedy_decode():
 
 
 def test_tree_residual_recursion_closed_form():
-    """r_{j+1} = norm(max(0, r_j - q)) equals max(0, p - c_{j+1} q) / W_{j+1}
-    with c_{j+1} = c_j + W_j: the tree oracle's second-sibling test uses it."""
+    """The closed form the GPU walk evaluates -- r_j = max(0, p - c_j q) / W_j
+    with c_0 = 0, W_0 = 1, c_{j+1} = c_j + W_j, W_j = sum max(0, p - c_j q) --
+    equals the page's recursion r_{j+1} = norm(max(0, r_j - q)), which the
+    oracle takes ([RheoSampling] section 4), and W_j equals the product of the
+    recursion's normalisers (the oracle's S, the mass the GPU reports)."""
     rng = np.random.default_rng(48)
     p = softmax_T(rng.normal(0, 2, 9), 1.0)
     q = softmax_T(rng.normal(0, 2, 9), 1.0)
-    r, c, W = p.copy(), 0.0, 1.0
+    r, c, W, prod = p.copy(), 0.0, 1.0, 1.0
     for _ in range(4):
         nxt = np.maximum(0.0, r - q)
         if nxt.sum() == 0:
             break
+        prod *= nxt.sum()
         r = nxt / nxt.sum()
         c = c + W
         W = np.maximum(0.0, p - c * q).sum()
         assert np.allclose(r, np.maximum(0.0, p - c * q) / W, atol=1e-14)
+        assert abs(prod - W) < 1e-14
     # and the oracle tests the second sibling against r_1 = norm(max(0, p - q))
     tl = np.stack([np.log(p), np.zeros(9), np.zeros(9)])
     dl = np.stack([np.log(q), np.zeros(9), np.zeros(9)])
@@ -747,3 +752,170 @@ def test_tree_residual_recursion_closed_form():
     res = oracle.verify_tree_row(tl, dl, [0, int(np.argmax(q - p)), x], [-1, 0, 0], [0.5, 0.999999, 0.3], 1.0)
     r1 = np.maximum(0.0, p - q) / np.maximum(0.0, p - q).sum()
     assert res.tested[1][0] == 2 and abs(res.tested[1][3] - r1[x]) < 1e-14
+
+
+# ------------------------------------------- batch wrappers and margins
+# verify() and verify_tree() decode each row's stored logits (bf16 bit
+# patterns widen exactly), read a row's draft only when it samples (greedy
+# verification needs the target's argmax alone, [nalar] "Semantik penerimaan
+# ..."), and return one result per requested row, in the requested order.
+class _RowReads:
+    """Stored logits that record which rows are read."""
+
+    def __init__(self, a):
+        self.a, self.read = a, []
+
+    @property
+    def shape(self):
+        return self.a.shape
+
+    def __getitem__(self, b):
+        self.read.append(int(b))
+        return self.a[b]
+
+
+def _bf16(x):
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    return ((b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
+
+
+def _batch(seed=50, B=3, K=3, V=37):
+    rng = np.random.default_rng(seed)
+    tgt = _bf16(rng.normal(0, 2, (B, K + 1, V)))
+    dft = _bf16(decode_logits(tgt[:, :K], "bf16") + rng.normal(0, 0.7, (B, K, V)))
+    dft[1] = 0x7FC0                       # the greedy row's draft: NaN bits, never to be read
+    tok = rng.integers(0, V, (B, K)).astype(np.int32)
+    uni = rng.random((B, K + 1)).astype(np.float32)
+    temp = np.array([0.7, 0.0, 1.3], dtype=np.float32)[:B]
+    return tgt, dft, tok, uni, temp
+
+
+def _same_row(a, b):
+    assert a.n == b.n and list(a.tokens) == list(b.tokens) and a.greedy == b.greedy
+    if not a.greedy:
+        assert np.array_equal(a.p_d, b.p_d) and np.array_equal(a.q_d, b.q_d) and a.S == b.S
+
+
+@pytest.mark.parametrize("topk", [0, 5])
+def test_verify_batch_equals_rows_and_skips_greedy_drafts(topk):
+    tgt, dft, tok, uni, temp = _batch()
+    reads = _RowReads(dft)
+    got = oracle.verify(tgt, reads, tok, uni, temp, topk, "bf16")
+    assert 1 not in reads.read, "a greedy row's draft was read"
+    assert len(got) == 3
+    for b in range(3):
+        dl = decode_logits(dft[b], "bf16") if temp[b] > 0 else None
+        _same_row(got[b], oracle.verify_row(decode_logits(tgt[b], "bf16"), dl, tok[b], uni[b], float(temp[b]),
+                                            topk))
+    sub = oracle.verify(tgt, dft, tok, uni, temp, topk, "bf16", rows=[2, 0])
+    _same_row(sub[0], got[2])
+    _same_row(sub[1], got[0])
+
+
+def test_verify_tree_batch_equals_rows_and_skips_greedy_drafts():
+    rng = np.random.default_rng(51)
+    B, N, V = 3, 5, 23
+    tgt = _bf16(rng.normal(0, 2, (B, N, V)))
+    dft = _bf16(decode_logits(tgt, "bf16") + rng.normal(0, 0.8, (B, N, V)))
+    dft[1] = 0x7FC0
+    par = np.array([[-1, 0, 0, 1, 1]] * B, dtype=np.int32)
+    tok = rng.integers(0, V, (B, N)).astype(np.int32)
+    uni = rng.random((B, N)).astype(np.float32)
+    temp = np.array([0.9, 0.0, 1.4], dtype=np.float32)
+    reads = _RowReads(dft)
+    got = oracle.verify_tree(tgt, reads, tok, par, uni, temp, 0, "bf16")
+    assert 1 not in reads.read, "a greedy row's draft was read"
+    for b, rows in ((0, None), (1, None), (2, None)):
+        dl = decode_logits(dft[b], "bf16") if temp[b] > 0 else None
+        want = oracle.verify_tree_row(decode_logits(tgt[b], "bf16"), dl, tok[b], par[b], uni[b], float(temp[b]))
+        assert got[b].path == want.path and list(got[b].tokens) == list(want.tokens)
+        assert got[b].greedy == want.greedy and (want.greedy or got[b].S == want.S)
+    sub = oracle.verify_tree(tgt, dft, tok, par, uni, temp, 0, "bf16", rows=[2, 1])
+    assert list(sub[0].tokens) == list(got[2].tokens) and list(sub[1].tokens) == list(got[1].tokens)
+
+
+def _two_token_row(p, q):
+    """Target / draft logits over two ids with softmax (p, 1-p) and (q, 1-q) at T = 1."""
+    return np.log([p, 1.0 - p]), np.log([q, 1.0 - q])
+
+
+def test_min_margin_takes_reached_decisions_and_the_draw():
+    # Position 0: p(0) = 0.3, q(0) = 0.6, u = 0.9 -> 0.54 >= 0.3, rejected
+    # with margin 0.24.  Position 1 is never reached; its test sits exactly on
+    # the threshold (u q = p, margin 0).  The residual max(0, p - q) = (0, 0.3)
+    # has S = 0.3; u_K = 0.5 gives t = 0.15 inside id 1's interval [0, 0.3],
+    # gap 0.15.  So the smallest margin of the decisions taken is 0.15.
+    lp, lq = _two_token_row(0.3, 0.6)
+    tl = np.stack([lp, lp, lp])
+    dl = np.stack([lq, lq])
+    r = verify_row(tl, dl, [0, 0], [0.9, 0.5, 0.5], 1.0)
+    assert r.n == 0 and list(r.tokens) == [1, -1, -1]
+    assert abs(r.margins[0] - 0.24) < 1e-12 and abs(r.margins[1]) < 1e-12
+    assert abs(r.gap - 0.15) < 1e-12 and abs(r.min_margin() - 0.15) < 1e-12
+    # Both accepted (u q < p at each position: 0.1*0.6 < 0.3), bonus draw from
+    # p = (0.3, 0.7) at t = 0.31: id 1, gap 0.01; the margins are 0.24 each.
+    r = verify_row(tl, dl, [0, 0], [0.1, 0.1, 0.31], 1.0)
+    assert r.n == 2 and abs(r.min_margin() - 0.01) < 1e-12
+    # A draw far from every edge: the smallest acceptance margin decides.
+    r = verify_row(tl, dl, [0, 0], [0.1, 0.45, 0.65], 1.0)   # margins 0.24, 0.03; gap 0.35
+    assert r.n == 2 and abs(r.min_margin() - 0.03) < 1e-12
+    g = verify_row(tl, dl, [0, 0], [0.9, 0.5, 0.5], 0.0)
+    assert g.min_margin() == float("inf")
+
+
+def test_tree_min_margin_takes_tested_nodes_and_the_draw():
+    # Root with two children, both with token 0: p = (0.3, 0.7), q = (0.6, 0.4).
+    # Child 1: u = 0.9 -> 0.54 >= 0.3, rejected, margin 0.24.  The residual
+    # norm(max(0, p - q)) = (0, 1), so child 2 (token 0, r = 0) is rejected with
+    # margin |0.2 * 0.6 - 0| = 0.12; its residual max(0, (0, 1) - q) = (0, 0.6)
+    # normalises to (0, 1) again, so S = 0.3 * 0.6 = 0.18 (in units of p:
+    # max(0, p - 1.3 q) = (0, 0.18)).  The final draw from (0, 1) at
+    # t = u_0 = 0.995 has gap 0.005.
+    lp, lq = _two_token_row(0.3, 0.6)
+    z = np.zeros(2)
+    tl = np.stack([lp, z, z])
+    dl = np.stack([lq, z, z])
+    r = oracle.verify_tree_row(tl, dl, [0, 0, 0], [-1, 0, 0], [0.995, 0.9, 0.2], 1.0)
+    assert r.n == 0 and [c for c, *_ in r.tested] == [1, 2] and r.tokens[0] == 1
+    assert abs(r.margins[0] - 0.24) < 1e-12 and abs(r.margins[1] - 0.12) < 1e-12
+    assert abs(r.S - 0.18) < 1e-12 and abs(r.gap - 0.005) < 1e-12
+    assert abs(r.min_margin() - 0.005) < 1e-12
+    r = oracle.verify_tree_row(tl, dl, [0, 0, 0], [-1, 0, 0], [0.5, 0.9, 0.2], 1.0)
+    assert abs(r.min_margin() - 0.12) < 1e-12
+
+
+def test_forced_outcome_follows_the_other_path():
+    # The same two-token row: position 0 rejects (0.54 >= 0.3).  Forcing it to
+    # accept continues at position 1 under the rule, without changing the
+    # recorded outcome; forcing position 1 to reject ends the scan there.
+    lp, lq = _two_token_row(0.3, 0.6)
+    tl = np.stack([lp, lp, lp])
+    dl = np.stack([lq, lq])
+    u = [0.9, 0.1, 0.5]
+    r = verify_row(tl, dl, [0, 0], u, 1.0)
+    assert r.n == 0 and list(r.accept) == [False, True]
+    f = verify_row(tl, dl, [0, 0], u, 1.0, force={0: True})
+    assert f.n == 2 and list(f.accept) == [False, True] and list(f.tokens[:2]) == [0, 0]
+    f = verify_row(tl, dl, [0, 0], u, 1.0, force={0: True, 1: False})
+    assert f.n == 1 and f.tokens[1] == 1 and abs(f.S - 0.3) < 1e-12
+    # Tree: forcing the first child to be accepted descends into it (a leaf:
+    # bonus draw from its target, uniform over 2 ids at t = 0.995 -> id 1).
+    z = np.zeros(2)
+    t = oracle.verify_tree_row(np.stack([lp, z, z]), np.stack([lq, z, z]), [0, 0, 0], [-1, 0, 0],
+                               [0.995, 0.9, 0.2], 1.0, force={1: True})
+    assert t.path == [1] and list(t.tokens[:2]) == [0, 1] and t.accepts == [False] and t.S == 1.0
+
+
+def test_near_ids_are_the_neighbours_of_t():
+    # K = 0, four equally likely ids: the intervals are [0, .25], [.25, .5],
+    # [.5, .75], [.75, 1].  t just above 0.5 draws id 2 and is within 1e-5 of
+    # id 1's interval too; t = 0.6 is near id 2 only.  A zero-weight id (a
+    # -inf logit) is never a neighbour, even when its empty interval sits at t.
+    tl = np.zeros((1, 4))
+    r = verify_row(tl, None, [], [0.5 + 1e-6], 1.0)
+    assert r.tokens[0] == 2 and r.near_ids == (1, 2) and abs(r.t - (0.5 + 1e-6)) < 1e-15
+    r = verify_row(tl, None, [], [0.6], 1.0)
+    assert r.near_ids == (2,)
+    tl = np.array([[0.0, -np.inf, 0.0, 0.0]])          # thirds; id 1 has weight 0
+    r = verify_row(tl, None, [], [1.0 / 3.0 + 1e-7], 1.0)
+    assert r.tokens[0] == 2 and r.near_ids == (0, 2)
