@@ -4,6 +4,13 @@ Argument marshalling only.  Every step of the verifier runs in the library's
 HIP kernels; torch provides the device memory and the current HIP stream.
 If the library has not been built the calls raise instead of computing
 anything another way.
+
+Workspaces.  A call given no ``workspace`` uses one cached per (call kind,
+device, stream): allocated and zero-filled on that stream the first time,
+or when a larger shape needs more, and reused afterwards (the library leaves
+a workspace zeroed after every call).  Calls on one stream run in order, so
+they can share it; calls on different streams get different workspaces.
+Outputs the binding allocates are allocated on the stream the call runs on.
 """
 
 from __future__ import annotations
@@ -121,8 +128,55 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+_WS_CACHE: dict = {}
+
+
+def _stream_handle(dev, stream) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream if stream is None else int(stream)
+
+
+class _OnStream:
+    """Allocations inside belong to the stream with this handle (torch's
+    caching allocator then reuses their blocks only in that stream's order)."""
+
+    def __init__(self, dev, handle):
+        self.ctx = None
+        if handle != torch.cuda.current_stream(dev).cuda_stream:
+            self.ctx = torch.cuda.stream(torch.cuda.ExternalStream(handle, device=dev))
+
+    def __enter__(self):
+        if self.ctx is not None:
+            self.ctx.__enter__()
+
+    def __exit__(self, *exc):
+        if self.ctx is not None:
+            self.ctx.__exit__(*exc)
+
+
+def _empty_on(args, shape, dtype, dev):
+    """torch.empty on the stream of the prepared call `args` (its last entry)."""
+    with _OnStream(dev, args[-1].value or 0):
+        return torch.empty(shape, dtype=dtype, device=dev)
+
+
+def _cached_workspace(kind: str, nbytes: int, dev, handle: int):
+    key = (kind, dev.index if dev.index is not None else torch.cuda.current_device(), handle)
+    ws = _WS_CACHE.get(key)
+    if ws is None or ws.numel() < nbytes:
+        with _OnStream(dev, handle):
+            ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        _WS_CACHE[key] = ws
+    return ws
+
+
+def release_workspaces():
+    """Drop the cached workspaces (their memory returns to torch's allocator
+    in the order of the streams they were used on)."""
+    _WS_CACHE.clear()
+
+
 def _prepare(target, draft, draft_tokens, uniforms, temperature, topk_draft, out_tokens,
-             num_accepted, workspace, stream):
+             num_accepted, workspace, stream, ws_kind="linear"):
     if target.dim() != 3:
         raise ValueError("target_logits must be [B, K+1, V]")
     B, Kp1, V = target.shape
@@ -140,14 +194,16 @@ def _prepare(target, draft, draft_tokens, uniforms, temperature, topk_draft, out
     for name, t, shape, dtype in tensors:
         if t is None or tuple(t.shape) != shape or t.dtype != dtype or t.device != dev or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {shape} on {dev}")
-    if out_tokens is None:
-        out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
-    if num_accepted is None:
-        num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    stream = _stream_handle(dev, stream)
+    with _OnStream(dev, stream):
+        if out_tokens is None:
+            out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+        if num_accepted is None:
+            num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
     if workspace is None:
-        workspace = new_workspace(B, K, V, topk_draft, dt, dev)
-    if stream is None:
-        stream = torch.cuda.current_stream(dev).cuda_stream
+        n = (early_exit_workspace_bytes(B, K, V, dt, topk_draft) if ws_kind == "early_exit"
+             else workspace_bytes(B, K, V, topk_draft, dt))
+        workspace = _cached_workspace(ws_kind, n, dev, stream)
     ws_n = ctypes.c_size_t(workspace.numel() * workspace.element_size())
     args = [_ptr(target), _ptr(draft) if K > 0 else None, _ptr(draft_tokens) if K > 0 else None,
             _ptr(uniforms), _ptr(temperature), B, K, V, topk_draft, dt, _ptr(out_tokens),
@@ -176,8 +232,8 @@ def verify_probe(target, draft, draft_tokens, uniforms, temperature, topk_draft:
     args, out_tokens, num_accepted, _ = _prepare(target, draft, draft_tokens, uniforms, temperature,
                                                  topk_draft, None, None, workspace, stream)
     B, Kp1 = out_tokens.shape
-    probs = torch.empty((B, Kp1 - 1, 2), dtype=torch.float32, device=target.device)
-    mass = torch.empty((B,), dtype=torch.float32, device=target.device)
+    probs = _empty_on(args, (B, Kp1 - 1, 2), torch.float32, target.device)
+    mass = _empty_on(args, (B,), torch.float32, target.device)
     _check(load_library().spec_verify_probe(*args, _ptr(probs), _ptr(mass)))
     return out_tokens, num_accepted, probs, mass
 
@@ -195,8 +251,8 @@ def verify_relaxed(target, draft, draft_tokens, uniforms, temperature, topk_draf
     probs = mass = None
     if probes:
         B, Kp1 = out_tokens.shape
-        probs = torch.empty((B, Kp1 - 1, 2), dtype=torch.float32, device=target.device)
-        mass = torch.empty((B,), dtype=torch.float32, device=target.device)
+        probs = _empty_on(args, (B, Kp1 - 1, 2), torch.float32, target.device)
+        mass = _empty_on(args, (B,), torch.float32, target.device)
     a = args[:10] + [ctypes.c_float(alpha), int(max_rank), ctypes.c_float(min_prob)] + args[10:] + \
         [_ptr(probs), _ptr(mass)]
     _check(load_library().spec_verify_relaxed(*a))
@@ -214,7 +270,7 @@ def verify_kl(target, draft, draft_tokens, uniforms, temperature, topk_draft: in
                                                  topk_draft, out_tokens, num_accepted, workspace, stream)
     B, Kp1 = out_tokens.shape
     if kl is None:
-        kl = torch.empty((B, Kp1 - 1), dtype=torch.float32, device=target.device)
+        kl = _empty_on(args, (B, Kp1 - 1), torch.float32, target.device)
     _check(load_library().spec_verify_kl(*args, _ptr(kl)))
     return out_tokens, num_accepted, kl
 
@@ -241,16 +297,14 @@ def verify_early_exit(target, draft, draft_tokens, uniforms, temperature, topk_d
     Returns (out_tokens, num_accepted), plus (probs [B, K, 2], mass [B]) when
     ``probes`` is set (probabilities past a row's first rejection are NaN).
     """
-    if workspace is None and target.dim() == 3:
-        B, Kp1, V = target.shape
-        workspace = new_early_exit_workspace(B, Kp1 - 1, V, _dtype_code(target), target.device, topk_draft)
     args, out_tokens, num_accepted, _ = _prepare(target, draft, draft_tokens, uniforms, temperature,
-                                                 topk_draft, out_tokens, num_accepted, workspace, stream)
+                                                 topk_draft, out_tokens, num_accepted, workspace, stream,
+                                                 ws_kind="early_exit")
     probs = mass = None
     if probes:
         B, Kp1 = out_tokens.shape
-        probs = torch.empty((B, Kp1 - 1, 2), dtype=torch.float32, device=target.device)
-        mass = torch.empty((B,), dtype=torch.float32, device=target.device)
+        probs = _empty_on(args, (B, Kp1 - 1, 2), torch.float32, target.device)
+        mass = _empty_on(args, (B,), torch.float32, target.device)
     _check(load_library().spec_verify_early_exit(*args, _ptr(probs), _ptr(mass)))
     if probes:
         return out_tokens, num_accepted, probs, mass
@@ -289,24 +343,22 @@ def _prepare_tree(target, draft, node_tokens, parents, uniforms, temperature, to
     for name, t, shape, dtype in tensors:
         if t is None or tuple(t.shape) != shape or t.dtype != dtype or t.device != dev or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {shape} on {dev}")
-    if out_tokens is None:
-        out_tokens = torch.empty((B, N), dtype=torch.int32, device=dev)
-    if out_nodes is None:
-        out_nodes = torch.empty((B, N), dtype=torch.int32, device=dev)
-    if num_accepted is None:
-        num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    stream = _stream_handle(dev, stream)
+    with _OnStream(dev, stream):
+        if out_tokens is None:
+            out_tokens = torch.empty((B, N), dtype=torch.int32, device=dev)
+        if out_nodes is None:
+            out_nodes = torch.empty((B, N), dtype=torch.int32, device=dev)
+        if num_accepted is None:
+            num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
     if workspace is None:
-        workspace = new_tree_workspace(B, N, V, dt, dev, topk_draft)
-    if stream is None:
-        stream = torch.cuda.current_stream(dev).cuda_stream
+        workspace = _cached_workspace("tree", tree_workspace_bytes(B, N, V, dt, topk_draft), dev, stream)
     ws_n = ctypes.c_size_t(workspace.numel() * workspace.element_size())
     many = N > 1
     args = [_ptr(target), _ptr(draft) if many else None, _ptr(node_tokens) if many else None,
             _ptr(parents) if many else None, _ptr(uniforms), _ptr(temperature), B, N, V, topk_draft, dt,
             _ptr(out_tokens), _ptr(out_nodes), _ptr(num_accepted), _ptr(workspace), ctypes.byref(ws_n),
             ctypes.c_void_p(stream)]
-    # The caller holds `keep` until the call has been enqueued: a workspace
-    # created here must not return to torch's allocator before that.
     keep = (target, draft, node_tokens, parents, uniforms, temperature, workspace)
     return args, out_tokens, out_nodes, num_accepted, keep
 
@@ -325,8 +377,8 @@ def verify_tree(target, draft, node_tokens, parents, uniforms, temperature, topk
     probs = mass = None
     if probes:
         B, N = out_tokens.shape
-        probs = torch.empty((B, N, 3), dtype=torch.float32, device=target.device)
-        mass = torch.empty((B,), dtype=torch.float32, device=target.device)
+        probs = _empty_on(args, (B, N, 3), torch.float32, target.device)
+        mass = _empty_on(args, (B,), torch.float32, target.device)
     _check(load_library().spec_verify_tree(*args, _ptr(probs), _ptr(mass)))
     del keep
     if probes:

@@ -76,3 +76,26 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_cpu_baseline_median_of_three_and_host_facts():
+    d = W.make(0)
+    cb, ref = bench.cpu_baseline(d, 0.3)
+    assert cb["kind"] == "oracle" and cb["unit"] == "positions/s" and len(cb["runs"]) == 3
+    assert cb["value"] == sorted(cb["runs"])[1] or abs(cb["value"] - sorted(cb["runs"])[1]) < 0.1
+    assert 1 <= cb["cores"] <= bench.CPU_THREADS
+    assert cb["host"]["logical_cpus"] == os.cpu_count()
+    assert len(ref) == d["target"].shape[0]
+
+
+def test_oracle_comparison_counts_equal_and_differing_rows():
+    d = W.make(0)
+    _, ref = bench.cpu_baseline(d, 0.05)
+    out = np.stack([r.tokens for r in ref]).astype(np.int32)
+    nacc = np.array([r.n for r in ref], dtype=np.int32)
+    c = bench.oracle_comparison(out, nacc, ref, d["uniforms"])
+    assert c["rows"] == 4 and c["rows_equal"] == 4 and c["firm_rows_differing"] == 0
+    b = next(k for k, r in enumerate(ref) if r.gap > 1e-3)
+    out[b, ref[b].n] = (out[b, ref[b].n] + 1) % d["target"].shape[2]
+    c = bench.oracle_comparison(out, nacc, ref, d["uniforms"])
+    assert c["rows_equal"] == 3 and c["firm_rows_differing"] == 1

@@ -73,15 +73,16 @@ def test_small_cases_match_oracle(name):
     C, L = plan(case.B, case.K, case.V, case.topk, SV_BF16 if case.dtype == W.BF16 else SV_F32)
     _log(f"[parity] {name}: B={case.B} K={case.K} V={case.V} {case.dtype} chunks={C}x{L}")
     st = {}
-    near = check_rows(d, run_gpu(d), stats=st)
-    _log(f"[parity] {name}: near-boundary rows {near}/{case.B} ({st['near_equal']} equal anyway)")
-    assert near < case.B, "no row was compared exactly"
+    check_rows(d, run_gpu(d), stats=st)
+    _log(f"[parity] {name}: near acceptance {st['near_accept']}, near draws {st['near_draw']} "
+         f"({st['near_draw_equal']} drew the oracle's token) of {case.B} rows")
 
 
 def test_config0_full():
     d = W.make(0)
-    near = check_rows(d, run_gpu(d))
-    _log(f"[parity] config0: near-boundary rows {near}/4")
+    st = {}
+    check_rows(d, run_gpu(d), stats=st)
+    _log(f"[parity] config0: near acceptance {st['near_accept']}, near draws {st['near_draw']} of 4 rows")
 
 
 def _edge_inputs(V=3000, K=3, B=4, dtype=W.BF16, seed=30):
@@ -177,22 +178,19 @@ def _full(c):
 
 
 @pytest.mark.parametrize("c", [1, 2, 3, 4])
-def test_full_config_sampled_rows(c):
+def test_full_config_every_row(c):
+    """Every row of the full-size workload, in the launch configuration the
+    bench times, against the oracle decision by decision."""
     d = _full(c)
     B = d["target"].shape[0]
     _log(f"[parity] config {c}: running GPU on all {B} rows")
     gpu = run_gpu(d)
-    check_well_formed(d, gpu[0], gpu[1])
-    rng = np.random.default_rng(c)
-    T = d["temperature"]
-    rows = sorted(set(rng.choice(B, size=min(B, 40), replace=False).tolist()) | {0, B - 1})
-    if (T <= 0).any():
-        rows = sorted(set(rows) | set(np.flatnonzero(T <= 0)[:64].tolist()))
+    _log(f"[parity] config {c}: oracle on all {B} rows")
     st = {}
-    near = check_rows(d, gpu, rows, stats=st)
-    _log(f"[parity] config {c}: oracle rows {len(rows)}, near-boundary {near} "
-         f"({st['near_equal']} equal anyway), mean accepted {gpu[1].mean():.3f}")
-    assert near <= len(rows) // 2, "too few rows compared exactly"
+    check_rows(d, gpu, stats=st)
+    _log(f"[parity] config {c}: {B} rows; near acceptance decisions {st['near_accept']}, near draws "
+         f"{st['near_draw']} ({st['near_draw_equal']} drew the oracle's token, the rest a neighbour); "
+         f"mean accepted {gpu[1].mean():.3f}")
 
 
 def test_workspace_reused_across_calls_and_shapes():
@@ -266,3 +264,29 @@ def test_topk_draft_token_outside_kept_set():
     gpu = run_gpu(d)
     assert (gpu[2][:, 0, 1] == 0).all()
     check_rows(d, gpu)
+
+
+def test_side_stream_without_workspace_equals_current_stream():
+    """stream= a side stream and no workspace: the binding's cached workspace
+    and outputs belong to that stream; results equal the current-stream call
+    bit for bit, across repeated calls and a larger shape that grows the
+    cached workspace."""
+    import rejection_sampling_verifier_amd as rsv
+    side = torch.cuda.Stream()
+    for i, case in enumerate([_case(B=6, seed=60), _case(B=6, seed=61), _case(B=12, V=70000, topk=128, seed=62)]):
+        d = W.make(case)
+        x = to_device(d)
+        ref = run_gpu(d, x)
+        torch.cuda.synchronize()
+        got = rsv.verify_probe(x["target"], x["draft"], x["tokens"], x["uniforms"], x["temperature"], d["topk"],
+                               stream=side.cuda_stream)
+        side.synchronize()
+        for a, b in zip(ref, got):
+            b = b.cpu().numpy()
+            assert np.array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
+                                  b.view(np.uint32) if b.dtype == np.float32 else b)
+        e_out, e_n = rsv.verify_early_exit(x["target"], x["draft"], x["tokens"], x["uniforms"], x["temperature"],
+                                           d["topk"], stream=side.cuda_stream)
+        side.synchronize()
+        assert np.array_equal(e_out.cpu().numpy(), ref[0]) and np.array_equal(e_n.cpu().numpy(), ref[1])
+        _log(f"[parity] side stream call {i}: equal")

@@ -9,10 +9,12 @@ is drawn from the last residual (or, at a leaf, from the leaf's target).
 Comparison rules (as for the linear verifier):
 * p(d), q(d) and r(d) of every tested node, and the mass of the final draw's
   distribution: within 1e-6 absolute of the oracle;
-* accepted nodes, output tokens and num_accepted bit-exact on every row whose
-  decisions are firm (margin |u q(d) - r(d)| and CDF gap above 1e-5, the
-  acceptance margin also above 1e-4 of max(r, u q));
-* near-boundary rows are counted and must still be well formed.
+* every sibling test the GPU took equals the oracle's outcome unless its
+  margin |u q(d) - r(d)| is at most 1e-5 and at most 1e-4 of max(r, u q);
+  where such a near test went the other way the oracle follows the GPU's
+  outcome and the rest of the row is compared with that walk;
+* the final token bit-exact when its CDF gap exceeds 1e-5, else one of the
+  ids whose CDF interval lies within 1e-5 of the sampled point.
 A chain tree must reproduce spec_verify bit for bit, and repeated calls must
 give the same bits.
 """
@@ -26,7 +28,7 @@ import torch
 import oracle
 import workloads as W
 from rejection_sampling_verifier_amd import verify_probe, verify_tree
-from tests.parity import ABS_MARGIN, PROB_TOL, REL_MARGIN, to_device
+from tests.parity import check_tree_rows, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -58,69 +60,6 @@ def run_tree_gpu(d, x=None, workspace=None):
                                                 workspace=workspace)
     torch.cuda.synchronize()
     return tuple(t.cpu().numpy() for t in (out, nodes, nacc, probs, mass))
-
-
-def tree_firm(r: oracle.TreeResult, u) -> bool:
-    if r.greedy:
-        return True
-    for (node, pd, qd, rd, _), m in zip(r.tested, r.margins):
-        if m <= ABS_MARGIN and m <= REL_MARGIN * max(rd, float(u[node]) * qd):
-            return False
-    return r.gap > ABS_MARGIN
-
-
-def check_tree_well_formed(d, gpu, rows):
-    out, nodes, nacc = gpu[:3]
-    V = d["target"].shape[2]
-    for b in rows:
-        n = int(nacc[b])
-        par, tok = d["parents"][b], d["tokens"][b]
-        N = par.shape[0]
-        assert 0 <= n < N, (b, n)
-        v = 0
-        for i in range(n):
-            c = int(nodes[b, i])
-            assert 0 < c < N and int(par[c]) == v, (b, nodes[b])
-            assert int(out[b, i]) == int(tok[c]), (b, out[b], nodes[b])
-            v = c
-        assert 0 <= int(out[b, n]) < V, (b, out[b])
-        assert (out[b, n + 1:] == -1).all() and (nodes[b, n:] == -1).all(), (b, out[b], nodes[b])
-
-
-def check_tree_rows(d, gpu, rows=None, stats=None):
-    """Compare GPU results with the oracle on `rows`; return the
-    near-boundary count."""
-    out, nodes, nacc, probs, mass = gpu
-    B, N = out.shape
-    rows = list(range(B)) if rows is None else list(rows)
-    ref = oracle.verify_tree(d["target"], d["draft"], d["tokens"], d["parents"], d["uniforms"],
-                             d["temperature"], d.get("topk", 0), d["dtype"], rows=rows)
-    near = 0
-    worst = 0.0
-    for b, r in zip(rows, ref):
-        firm = tree_firm(r, d["uniforms"][b])
-        if not firm:
-            near += 1
-            continue
-        assert int(nacc[b]) == r.n, (b, int(nacc[b]), r.n, out[b], r.tokens)
-        assert list(out[b]) == list(r.tokens), (b, out[b], r.tokens)
-        assert list(nodes[b, : r.n]) == list(r.path), (b, nodes[b], r.path)
-        if r.greedy:
-            assert float(mass[b]) == 0.0
-            continue
-        tested = {node: (pd, qd, rd) for node, pd, qd, rd, _ in r.tested}
-        for c in range(N):
-            if c in tested:
-                err = np.abs(probs[b, c].astype(np.float64) - np.array(tested[c]))
-                worst = max(worst, float(err.max()))
-                assert (err <= PROB_TOL).all(), (b, c, probs[b, c], tested[c])
-            else:
-                assert np.isnan(probs[b, c]).all(), (b, c, probs[b, c])
-        assert abs(float(mass[b]) - r.S) <= PROB_TOL, (b, float(mass[b]), r.S)
-    check_tree_well_formed(d, gpu, rows)
-    if stats is not None:
-        stats.update(near=near, rows=len(rows), worst=worst)
-    return near
 
 
 def _case(**kw):
@@ -159,10 +98,9 @@ CASES = {
 def test_tree_matches_oracle(name):
     d = W.make_tree(CASES[name])
     st = {}
-    near = check_tree_rows(d, run_tree_gpu(d), stats=st)
-    print(f"[tree] {name}: near-boundary rows {near}/{st['rows']}, worst prob error {st['worst']:.2e}",
-          flush=True)
-    assert near <= st["rows"] // 2
+    check_tree_rows(d, run_tree_gpu(d), stats=st)
+    print(f"[tree] {name}: near acceptance {st['near_accept']}, near draws {st['near_draw']} of {st['rows']} "
+          f"rows, worst prob error {st['worst']:.2e}", flush=True)
 
 
 @pytest.mark.parametrize("name", ["wide-low-agreement", "mixed-greedy", "61-node-tree"])
@@ -263,16 +201,12 @@ def test_workspace_is_left_clean_between_calls():
 
 
 @pytest.mark.parametrize("cfg", [0, 1])
-def test_full_size_tree_workload_sampled_rows(cfg):
+def test_full_size_tree_workload_every_row(cfg):
     """The 61-node, depth-8 tree over 151,936 ids (B = 32; dense and top-128
-    drafts): every row well formed, sampled rows against the oracle."""
+    drafts): every row against the oracle, decision by decision."""
     d = W.make_tree(cfg)
     gpu = run_tree_gpu(d)
-    B = d["tokens"].shape[0]
-    check_tree_well_formed(d, gpu, range(B))
-    rows = [0, 7, 13, 22, 31]
     st = {}
-    near = check_tree_rows(d, gpu, rows=rows, stats=st)
-    print(f"[tree] full size {cfg}: near-boundary {near}/{len(rows)}, mean accepted {gpu[2].mean():.2f}, "
-          f"worst prob error {st['worst']:.2e}", flush=True)
-    assert near <= 2
+    check_tree_rows(d, gpu, stats=st)
+    print(f"[tree] full size {cfg}: near acceptance {st['near_accept']}, near draws {st['near_draw']} of "
+          f"{st['rows']} rows, mean accepted {gpu[2].mean():.2f}, worst prob error {st['worst']:.2e}", flush=True)
