@@ -89,10 +89,13 @@ typedef enum {
  *                launch; the bound only guarantees termination) gets -1 here
  *                and -1 in every out_tokens slot.
  * workspace      device scratch of at least *workspace_bytes bytes, 256-byte
- *                aligned, zero-filled before its first use (e.g. hipMemset to
- *                0 once after allocating it).  Every call leaves it ready for
- *                the next one (its counters return to zero), so it can be
- *                reused without clearing.  Calls that overlap in time must use
+ *                aligned, zero-filled before its first use with a given
+ *                shape (B, K, V, topk_draft, dtype), e.g. by hipMemset to 0.
+ *                Every call leaves the regions its shape's layout needs
+ *                zeroed again (its counters return to zero), so calls of the
+ *                same shape can reuse it without clearing; a call of another
+ *                shape lays the regions out differently and needs it
+ *                zero-filled first.  Calls that overlap in time must use
  *                different workspaces.  NULL requests the size only:
  *                *workspace_bytes is set to the size required and nothing is
  *                launched.
@@ -213,7 +216,8 @@ int spec_verify_kl(const void* target_logits, const void* draft_logits,
  * for a truncated draft) do not fit the kernel's LDS is SV_ERR_UNSUPPORTED.
  * The workspace has its own size (query with workspace == NULL) and must
  * not be shared with the other entry points: this call keeps it zero between
- * calls and relies on that.
+ * calls of one shape and relies on that (zero-fill it before a call of
+ * another shape).
  * probs_out  [B, K, 2] float32 device or NULL: (p_i(d_i), q_i(d_i)) of every
  *            position the row tested, NaN past its first rejection (and for
  *            greedy rows).

@@ -6,11 +6,13 @@ If the library has not been built the calls raise instead of computing
 anything another way.
 
 Workspaces.  A call given no ``workspace`` uses one cached per (call kind,
-device, stream): allocated and zero-filled on that stream the first time,
-or when a larger shape needs more, and reused afterwards (the library leaves
-a workspace zeroed after every call).  Calls on one stream run in order, so
-they can share it; calls on different streams get different workspaces.
-Outputs the binding allocates are allocated on the stream the call runs on.
+device, stream, shape): allocated and zero-filled on that stream the first
+time and reused afterwards (the library leaves a workspace zeroed, for the
+layout of the shape it ran, after every call).  Calls on one stream run in
+order, so they can share it; calls on different streams get different
+workspaces.  Each (kind, device, stream) keeps its most recently used
+shapes only (WS_CACHE_SHAPES).  Outputs the binding allocates are allocated
+on the stream the call runs on.
 """
 
 from __future__ import annotations
@@ -119,7 +121,8 @@ def workspace_bytes(B: int, K: int, V: int, topk_draft: int = 0, dtype: int = SV
 
 
 def new_workspace(B: int, K: int, V: int, topk_draft: int = 0, dtype: int = SV_BF16, device="cuda"):
-    """A zero-filled workspace for this shape (reusable across calls on one stream)."""
+    """A zero-filled workspace for this shape (reusable, without clearing,
+    across calls of this shape on one stream)."""
     n = workspace_bytes(B, K, V, topk_draft, dtype)
     return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
 
@@ -129,6 +132,7 @@ def _ptr(t):
 
 
 _WS_CACHE: dict = {}
+WS_CACHE_SHAPES = 4
 
 
 def _stream_handle(dev, stream) -> int:
@@ -159,13 +163,20 @@ def _empty_on(args, shape, dtype, dev):
         return torch.empty(shape, dtype=dtype, device=dev)
 
 
-def _cached_workspace(kind: str, nbytes: int, dev, handle: int):
+def _cached_workspace(kind: str, shape: tuple, nbytes: int, dev, handle: int):
+    """The zeroed workspace of this (kind, device, stream) for `shape`.  A
+    workspace is reused only for the shape it was used with: the library
+    keeps a shape's counter regions zero between calls, and another shape's
+    layout puts other regions there."""
     key = (kind, dev.index if dev.index is not None else torch.cuda.current_device(), handle)
-    ws = _WS_CACHE.get(key)
-    if ws is None or ws.numel() < nbytes:
+    per = _WS_CACHE.setdefault(key, {})
+    ws = per.pop(shape, None)
+    if ws is None:
+        while len(per) >= WS_CACHE_SHAPES:
+            per.pop(next(iter(per)))       # least recently used; freed in this stream's order
         with _OnStream(dev, handle):
             ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
-        _WS_CACHE[key] = ws
+    per[shape] = ws                         # most recently used last
     return ws
 
 
@@ -203,7 +214,7 @@ def _prepare(target, draft, draft_tokens, uniforms, temperature, topk_draft, out
     if workspace is None:
         n = (early_exit_workspace_bytes(B, K, V, dt, topk_draft) if ws_kind == "early_exit"
              else workspace_bytes(B, K, V, topk_draft, dt))
-        workspace = _cached_workspace(ws_kind, n, dev, stream)
+        workspace = _cached_workspace(ws_kind, (B, K, V, topk_draft, dt), n, dev, stream)
     ws_n = ctypes.c_size_t(workspace.numel() * workspace.element_size())
     args = [_ptr(target), _ptr(draft) if K > 0 else None, _ptr(draft_tokens) if K > 0 else None,
             _ptr(uniforms), _ptr(temperature), B, K, V, topk_draft, dt, _ptr(out_tokens),
@@ -352,7 +363,8 @@ def _prepare_tree(target, draft, node_tokens, parents, uniforms, temperature, to
         if num_accepted is None:
             num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
     if workspace is None:
-        workspace = _cached_workspace("tree", tree_workspace_bytes(B, N, V, dt, topk_draft), dev, stream)
+        workspace = _cached_workspace("tree", (B, N, V, topk_draft, dt), tree_workspace_bytes(B, N, V, dt, topk_draft),
+                                      dev, stream)
     ws_n = ctypes.c_size_t(workspace.numel() * workspace.element_size())
     many = N > 1
     args = [_ptr(target), _ptr(draft) if many else None, _ptr(node_tokens) if many else None,

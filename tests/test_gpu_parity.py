@@ -193,14 +193,21 @@ def test_full_config_every_row(c):
          f"mean accepted {gpu[1].mean():.3f}")
 
 
-def test_workspace_reused_across_calls_and_shapes():
-    """Counters in the workspace return to zero after every call."""
+def test_workspace_reused_across_calls_of_one_shape():
+    """Counters in the workspace return to zero after every call, so calls of
+    one shape reuse it without clearing; another shape needs it zeroed first
+    (its layout puts other regions where the first shape's counters were)."""
     import rejection_sampling_verifier_amd as rsv
     big = rsv.new_workspace(16, 5, 70000, 0, SV_BF16, "cuda")
     for i, case in enumerate([_case(B=16, K=5, V=70000, seed=40),
-                              _case(B=9, K=2, V=30000, seed=41),
                               _case(B=16, K=5, V=70000, greedy_rows=5, seed=42),
-                              _case(B=3, K=4, V=50000, temperature=2.0, seed=43)]):
+                              _case(B=16, K=5, V=70000, temperature=2.0, seed=43),
+                              _case(B=16, K=5, V=70000, seed=40),
+                              _case(B=9, K=2, V=30000, seed=41),
+                              _case(B=9, K=2, V=30000, seed=44),
+                              _case(B=80, K=1, V=5000, seed=45)]):
+        if i in (4, 6):
+            big.zero_()                       # a new shape
         d = W.make(case)
         x = to_device(d)
         out, nacc, probs, mass = rsv.verify_probe(x["target"], x["draft"], x["tokens"], x["uniforms"],
@@ -209,6 +216,27 @@ def test_workspace_reused_across_calls_and_shapes():
         gpu = (out.cpu().numpy(), nacc.cpu().numpy(), probs.cpu().numpy(), mass.cpu().numpy())
         check_rows(d, gpu)
         _log(f"[parity] workspace reuse call {i}: ok")
+
+
+def test_binding_cache_switches_shapes_on_one_stream():
+    """The binding's cached workspaces: alternating shapes (B 512 after B 256,
+    whose layout differs) on the current stream, each equal to a call with a
+    fresh workspace."""
+    import rejection_sampling_verifier_amd as rsv
+    rsv.binding.release_workspaces()
+    cases = [_case(B=256, K=7, V=9000, seed=46), _case(B=512, K=4, V=8000, greedy_rows=100, seed=47)]
+    data = [W.make(c) for c in cases]
+    for rep in range(3):
+        for c, d in zip(cases, data):
+            x = to_device(d)
+            ws = rsv.new_workspace(c.B, c.K, c.V, 0, SV_BF16, "cuda")
+            ref = rsv.verify_probe(x["target"], x["draft"], x["tokens"], x["uniforms"], x["temperature"], 0,
+                                   workspace=ws)
+            got = rsv.verify_probe(x["target"], x["draft"], x["tokens"], x["uniforms"], x["temperature"], 0)
+            torch.cuda.synchronize()
+            for a, b in zip(ref, got):
+                assert torch.equal(a, b)
+    _log("[parity] cached workspaces across shapes: ok")
 
 
 def test_zero_residual_falls_back_to_target():
