@@ -31,7 +31,8 @@
  *
  * All pointers are device pointers owned by the caller.  Inputs are read
  * only; outputs are fully overwritten.  The library allocates nothing, keeps
- * no mutable global state and never synchronises: every call only enqueues
+ * no mutable global state other than spec_verify_noalloc's static scratch,
+ * and never synchronises: every call only enqueues
  * at most three kernels on `stream` (no memory set or copy), so a call can
  * be captured in a HIP graph and replayed; outputs are valid once the caller
  * has synchronised that stream.  Calls on different workspaces are
@@ -58,12 +59,16 @@ typedef enum {
   SV_ERR_WORKSPACE = 2,    /* *workspace_bytes smaller than the size required    */
   SV_ERR_UNSUPPORTED = 3,  /* 0 < topk_draft < V with topk_draft > SV_MAX_TOPK, or */
                            /* K > SV_MAX_K                                        */
-  SV_ERR_HIP = 4           /* a kernel launch failed (hipGetLastError)           */
+  SV_ERR_HIP = 4,          /* a kernel launch failed (hipGetLastError)           */
+  SV_ERR_SCRATCH = 5       /* spec_verify_noalloc: the shape needs more scratch  */
+                           /* than SV_SCRATCH_BYTES                              */
 } sv_status;
 
 #define SV_MAX_TOPK 1024
 #define SV_MAX_K 64
 #define SV_MAX_NODES 64
+/* Size of spec_verify_noalloc's static device scratch (per GPU). */
+#define SV_SCRATCH_BYTES (32u << 20)
 
 /*
  * spec_verify - verify B rows; see the description at the top of this file.
@@ -335,6 +340,34 @@ int spec_verify_timed(const void* target_logits, const void* draft_logits,
                       int32_t* num_accepted, void* workspace,
                       size_t* workspace_bytes, hipStream_t stream,
                       hipEvent_t* events, int n_events);
+
+/*
+ * spec_verify_noalloc - spec_verify for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, semantics and results as spec_verify
+ * (bit for bit), without the workspace: the scratch is a static device array
+ * of SV_SCRATCH_BYTES inside the library, one per GPU, held until the
+ * process ends.  Its device address is looked up once per device, on the
+ * first call made with that device current.  Each call clears the part of
+ * the scratch its shape uses with a small fill kernel on `stream` (no
+ * memory set, so it can be captured) and then enqueues spec_verify's kernels.
+ * The call allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine).
+ *
+ * Every call on a GPU shares that GPU's scratch: calls that overlap in time
+ * on one GPU (different streams, or graphs replayed concurrently) race and
+ * must not be issued; calls serialised on one stream are fine.
+ * Returns SV_ERR_SCRATCH, before enqueuing anything, when the shape's
+ * workspace (spec_verify's size query) exceeds SV_SCRATCH_BYTES -- a dense
+ * draft of 256 rows, K = 7, V = 201,088 needs about 1.7 MB; truncated drafts
+ * need about 8 KB per (row, position, vocabulary chunk) more.  SV_ERR_HIP if
+ * the scratch's address cannot be obtained.  Other codes as spec_verify.
+ */
+int spec_verify_noalloc(const void* target_logits, const void* draft_logits,
+                        const int32_t* draft_tokens, const float* uniforms,
+                        const float* temperature, int B, int K, int V,
+                        int topk_draft, int dtype, int32_t* out_tokens,
+                        int32_t* num_accepted, hipStream_t stream);
 
 /*
  * spec_verify_plan - the vocabulary split the library would use for a shape:

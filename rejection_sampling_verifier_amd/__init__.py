@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     SV_MAX_K,
     SV_MAX_NODES,
     SV_MAX_TOPK,
+    SV_SCRATCH_BYTES,
     SpecVerifyError,
     StageTimer,
     TreeTimer,
@@ -25,6 +26,7 @@ from .binding import (  # noqa: F401
     verify,
     verify_early_exit,
     verify_kl,
+    verify_noalloc,
     verify_probe,
     verify_relaxed,
     verify_tree,

@@ -28,7 +28,7 @@ LIB_PATH = os.path.join(PKG, "libspecverify.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "spec_verify.h")
 
 SV_BF16, SV_F32 = 0, 1
-SV_OK, SV_ERR_ARG, SV_ERR_WORKSPACE, SV_ERR_UNSUPPORTED, SV_ERR_HIP = 0, 1, 2, 3, 4
+SV_OK, SV_ERR_ARG, SV_ERR_WORKSPACE, SV_ERR_UNSUPPORTED, SV_ERR_HIP, SV_ERR_SCRATCH = 0, 1, 2, 3, 4, 5
 
 
 def _header_define(name: str) -> int:
@@ -40,6 +40,7 @@ def _header_define(name: str) -> int:
 SV_MAX_TOPK = _header_define("SV_MAX_TOPK")
 SV_MAX_K = _header_define("SV_MAX_K")
 SV_MAX_NODES = _header_define("SV_MAX_NODES")
+SV_SCRATCH_BYTES = 32 << 20  # spec_verify.h: (32u << 20)
 
 
 class SpecVerifyError(RuntimeError):
@@ -66,6 +67,8 @@ def load_library(path: str | None = None):
     lib = ctypes.CDLL(p)
     lib.spec_verify.argtypes = _COMMON
     lib.spec_verify.restype = _i32
+    lib.spec_verify_noalloc.argtypes = _COMMON[:12] + [_vp]
+    lib.spec_verify_noalloc.restype = _i32
     lib.spec_verify_probe.argtypes = _COMMON + [_vp, _vp]
     lib.spec_verify_probe.restype = _i32
     lib.spec_verify_relaxed.argtypes = ([_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
@@ -132,6 +135,7 @@ def _ptr(t):
 
 
 _WS_CACHE: dict = {}
+_NO_WORKSPACE = torch.empty(0, dtype=torch.uint8)  # marks a call that takes no workspace
 WS_CACHE_SHAPES = 4
 
 
@@ -211,7 +215,9 @@ def _prepare(target, draft, draft_tokens, uniforms, temperature, topk_draft, out
             out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
         if num_accepted is None:
             num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
-    if workspace is None:
+    if workspace is _NO_WORKSPACE:
+        pass
+    elif workspace is None:
         n = (early_exit_workspace_bytes(B, K, V, dt, topk_draft) if ws_kind == "early_exit"
              else workspace_bytes(B, K, V, topk_draft, dt))
         workspace = _cached_workspace(ws_kind, (B, K, V, topk_draft, dt), n, dev, stream)
@@ -233,6 +239,17 @@ def verify(target, draft, draft_tokens, uniforms, temperature, topk_draft: int =
     args, out_tokens, num_accepted, _ = _prepare(target, draft, draft_tokens, uniforms, temperature,
                                                  topk_draft, out_tokens, num_accepted, workspace, stream)
     _check(load_library().spec_verify(*args))
+    return out_tokens, num_accepted
+
+
+def verify_noalloc(target, draft, draft_tokens, uniforms, temperature, topk_draft: int = 0, *,
+                   out_tokens=None, num_accepted=None, stream=None):
+    """spec_verify_noalloc: spec_verify without a workspace (the library's
+    static per-GPU scratch; see the header).  Calls that overlap in time on
+    one GPU race.  Returns (out_tokens, num_accepted)."""
+    args, out_tokens, num_accepted, _ = _prepare(target, draft, draft_tokens, uniforms, temperature,
+                                                 topk_draft, out_tokens, num_accepted, _NO_WORKSPACE, stream)
+    _check(load_library().spec_verify_noalloc(*(args[:12] + [args[-1]])))
     return out_tokens, num_accepted
 
 

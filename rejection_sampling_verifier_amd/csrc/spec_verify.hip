@@ -50,6 +50,7 @@
 #include <climits>
 #include <cstddef>
 #include <cstdint>
+#include <mutex>
 #include <type_traits>
 
 #include <hip/hip_ext.h>
@@ -1687,6 +1688,7 @@ struct Plan {
   int C = 0, CS = 0;
   size_t off_cnt = 0, off_part = 0, off_subK = 0, off_subR = 0, off_cand = 0, off_ccnt = 0, off_qstat = 0, off_kept = 0,
          total = 0;
+  size_t zero_bytes = 0;    // leading bytes holding every region that must be zero before a call
   size_t merge_lds = 0;
   bool cache = false;       // finishing work-groups copy the row's words to LDS
   size_t lds_bytes = 0;     // dynamic LDS of the finishing work-groups
@@ -1742,6 +1744,7 @@ int make_plan(int B, int K, int V, int topk, int dtype, Plan& pl) {
     pl.merge_lds = 0;
   }
   pl.total = off;
+  pl.zero_bytes = topk > 0 ? pl.off_cand : off;  // the candidate area is written before it is read
   // Dynamic LDS of the finishing work-groups: the row's partials and
   // sub-block sums when they fit.
   const size_t words = S * C * 4 + (size_t)C * NSUB;
@@ -2057,6 +2060,40 @@ int run_tree(const void* tgt, const void* dft, const int32_t* tok, const int32_t
                  : launch_tree<float, false>(a, pl.lds_bytes, st, e);
 }
 
+// Zeroes n 16-byte words (the no-allocation entry point's scratch, before a
+// call): an ordinary kernel, so a call stays capturable in a HIP graph.
+__global__ __launch_bounds__(WG) void zero_fill_kernel(u32x4* __restrict__ p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * WG + threadIdx.x; i < n; i += (size_t)gridDim.x * WG)
+    p[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+}  // namespace
+
+// ---- static scratch of spec_verify_noalloc ----------------------------------
+// One copy per GPU, zero at module load, held until the process ends.  In
+// host code `scratch` names a host-side stand-in, not the device array: its
+// device address comes from hipGetSymbolAddress, once per device, and only
+// that address is passed to kernels.
+static __device__ __align__(256) unsigned char scratch[SV_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::once_flag g_scratch_once[SCRATCH_MAX_DEVICES];
+void* g_scratch_ptr[SCRATCH_MAX_DEVICES];
+
+// The scratch's device address on the current device (nullptr on failure).
+void* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= SCRATCH_MAX_DEVICES) return nullptr;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) p = nullptr;
+    g_scratch_ptr[dev] = p;
+  });
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -2068,6 +2105,31 @@ int spec_verify(const void* target_logits, const void* draft_logits, const int32
   return run(target_logits, draft_logits, draft_tokens, uniforms, temperature, B, K, V, topk_draft,
              dtype, out_tokens, num_accepted, workspace, workspace_bytes, stream, nullptr, nullptr,
              nullptr, 0);
+}
+
+int spec_verify_noalloc(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                        const float* uniforms, const float* temperature, int B, int K, int V, int topk_draft,
+                        int dtype, int32_t* out_tokens, int32_t* num_accepted, hipStream_t stream) {
+  Plan pl;
+  const int rc = make_plan(B, K, V, topk_draft >= V ? 0 : topk_draft, dtype, pl);
+  if (rc != SV_OK) return rc;
+  if (pl.total > (size_t)SV_SCRATCH_BYTES) return SV_ERR_SCRATCH;
+  if (!target_logits || !uniforms || !temperature || !out_tokens || !num_accepted) return SV_ERR_ARG;
+  if (K > 0 && (!draft_logits || !draft_tokens)) return SV_ERR_ARG;
+  void* ws = scratch_address();
+  if (!ws) return SV_ERR_HIP;
+  // The regions that must start at zero: the previous call may have had
+  // another shape, whose layout left other words there.
+  (void)hipGetLastError();
+  const size_t n16 = pl.zero_bytes / 16;
+  if (n16 > 0) {
+    const int grid = (int)std::min<size_t>(1024, (n16 + WG - 1) / WG);
+    hipLaunchKernelGGL(zero_fill_kernel, dim3(grid), dim3(WG), 0, stream, static_cast<u32x4*>(ws), n16);
+    if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
+  }
+  size_t ws_bytes = SV_SCRATCH_BYTES;
+  return run(target_logits, draft_logits, draft_tokens, uniforms, temperature, B, K, V, topk_draft, dtype,
+             out_tokens, num_accepted, ws, &ws_bytes, stream, nullptr, nullptr, nullptr, 0);
 }
 
 int spec_verify_probe(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
@@ -2159,6 +2221,7 @@ const char* spec_verify_status_string(int status) {
     case SV_ERR_WORKSPACE: return "workspace too small";
     case SV_ERR_UNSUPPORTED: return "unsupported shape or top-k";
     case SV_ERR_HIP: return "HIP kernel launch failed";
+    case SV_ERR_SCRATCH: return "shape needs more than the static scratch of spec_verify_noalloc (SV_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

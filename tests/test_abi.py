@@ -223,3 +223,24 @@ def test_early_exit_argument_errors_without_launch():
     assert call(K=B.SV_MAX_K + 1, n=1 << 40) == B.SV_ERR_UNSUPPORTED
     # the row's statistics must fit the kernel's LDS
     assert call(K=64, V=1 << 22, dtype=B.SV_F32, n=1 << 40) == B.SV_ERR_UNSUPPORTED
+
+
+def test_noalloc_errors_before_any_launch():
+    """spec_verify_noalloc rejects a shape whose workspace exceeds the static
+    scratch (SV_ERR_SCRATCH) and bad arguments before touching the GPU."""
+    lib = B.load_library()
+    src = open(HEADER).read()
+    m = re.search(r"#define\s+SV_SCRATCH_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == B.SV_SCRATCH_BYTES
+    p = ctypes.c_void_p(0x100000)
+    # a top-128 draft batch of 256 rows x 8 positions needs ~170 MB of candidate lists
+    assert B.workspace_bytes(256, 8, 151936, 128, B.SV_BF16) > B.SV_SCRATCH_BYTES
+    assert lib.spec_verify_noalloc(p, p, p, p, p, 256, 8, 151936, 128, B.SV_BF16, p, p, None) == B.SV_ERR_SCRATCH
+    # the dense 201,088-id batch fits
+    assert B.workspace_bytes(256, 7, 201088, 0, B.SV_BF16) <= B.SV_SCRATCH_BYTES
+    assert lib.spec_verify_noalloc(None, p, p, p, p, 4, 3, 1000, 0, B.SV_BF16, p, p, None) == B.SV_ERR_ARG
+    assert lib.spec_verify_noalloc(p, None, p, p, p, 4, 3, 1000, 0, B.SV_BF16, p, p, None) == B.SV_ERR_ARG
+    assert lib.spec_verify_noalloc(p, p, p, p, p, 0, 3, 1000, 0, B.SV_BF16, p, p, None) == B.SV_ERR_ARG
+    assert lib.spec_verify_noalloc(p, p, p, p, p, 4, 3, 1000, -1, B.SV_BF16, p, p, None) == B.SV_ERR_ARG
+    assert lib.spec_verify_noalloc(p, p, p, p, p, 4, 3, 1000, 0, 9, p, p, None) == B.SV_ERR_ARG
+    assert lib.spec_verify_status_string(B.SV_ERR_SCRATCH).startswith(b"shape needs more")
