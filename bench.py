@@ -57,10 +57,10 @@ def algorithmic_bytes(d) -> dict:
     return {"stats_kernel": logits, "m_min": logits + small}
 
 
-def traffic_from_profiles(workload: str):
-    """HBM bytes per launch of the statistics kernel from the committed
-    rocprofv3 counter summary, if it was taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", f"stats_kernel_{workload}_pmc.txt")
+def traffic_from_profiles(workload: str, kernel: str = "stats_kernel"):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.txt")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -319,14 +319,15 @@ def main():
     for t in timers:
         t.close()
     stage_ms = stages.mean(axis=0)
-    if not case.topk:
+    n_launch = rsv.launches(B, K, V, d["topk"], dt_code)
+    if n_launch < 3:
         stage_ms[1] = 0.0  # no merge kernel: its two events are recorded back to back
     stats_ms = float(stage_ms[0])
 
     positions = B * K
     value = positions / (ms_per_step * 1e-3)
-    achieved = by["stats_kernel"] / (stats_ms * 1e-3) / 1e9
     roof_kernel, roof_bytes, roof_ms = "stats_kernel", by["stats_kernel"], stats_ms
+    achieved = roof_bytes / (roof_ms * 1e-3) / 1e9
     if args.early_exit:
         # One kernel per call: its algorithmic bytes are the logits of the
         # positions each row reaches (targets 0..n, drafts 0..min(n, K-1) of
@@ -337,7 +338,7 @@ def main():
         rows = np.minimum(n_acc + 1, K + 1) + np.where(samp, np.minimum(n_acc + 1, K), 0)
         roof_kernel, roof_bytes, roof_ms = "early_exit_kernel", int(rows.sum()) * V * esz, ms_per_step
         achieved = roof_bytes / (roof_ms * 1e-3) / 1e9
-    traffic = traffic_from_profiles(case.name.split("-T")[0] if False else f"B{B}K{K}V{V}")
+    traffic = traffic_from_profiles(f"B{B}K{K}V{V}", roof_kernel)
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -371,6 +372,7 @@ def main():
         "kernel_ms": {"stats_kernel": round(float(stage_ms[0]), 5),
                       "merge_kernel": round(float(stage_ms[1]), 5),
                       "finish_kernel": round(float(stage_ms[2]), 5)},
+        "launches_per_call": n_launch,
         "wall_ms_per_step": round(wall_ms / args.steps, 5),
         "mean_accepted": round(accepted, 4),
         "kernel_ms_rule": "lossless",

@@ -370,6 +370,15 @@ int spec_verify_noalloc(const void* target_logits, const void* draft_logits,
                         int32_t* num_accepted, hipStream_t stream);
 
 /*
+ * spec_verify_launches - how many kernels a spec_verify (or _probe, _relaxed,
+ * _timed) call of this shape enqueues: 2 for a dense draft (statistics,
+ * finishing), 3 with a truncated draft (statistics, selection, finishing);
+ * spec_verify_noalloc enqueues one more (the fill of its scratch).  A
+ * negative value is minus an sv_status for a shape spec_verify refuses.
+ */
+int spec_verify_launches(int B, int K, int V, int topk_draft, int dtype);
+
+/*
  * spec_verify_plan - the vocabulary split the library would use for a shape:
  * *chunks vocabulary chunks per (row, position), each *chunk_len ids long
  * (the last one may be shorter).  For tests that need inputs spanning several

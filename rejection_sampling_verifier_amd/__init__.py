@@ -17,6 +17,7 @@ from .binding import (  # noqa: F401
     StageTimer,
     TreeTimer,
     early_exit_workspace_bytes,
+    launches,
     load_library,
     new_early_exit_workspace,
     new_tree_workspace,

@@ -86,6 +86,8 @@ def load_library(path: str | None = None):
     lib.spec_verify_tree.restype = _i32
     lib.spec_verify_tree_timed.argtypes = _tree + [ctypes.POINTER(_vp), _i32]
     lib.spec_verify_tree_timed.restype = _i32
+    lib.spec_verify_launches.argtypes = [_i32, _i32, _i32, _i32, _i32]
+    lib.spec_verify_launches.restype = _i32
     lib.spec_verify_plan.argtypes = [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32)]
     lib.spec_verify_plan.restype = _i32
     lib.spec_verify_status_string.argtypes = [_i32]
@@ -114,6 +116,14 @@ def plan(B: int, K: int, V: int, topk_draft: int = 0, dtype: int = SV_BF16):
     c, L = ctypes.c_int(0), ctypes.c_int(0)
     _check(load_library().spec_verify_plan(B, K, V, topk_draft, dtype, ctypes.byref(c), ctypes.byref(L)))
     return c.value, L.value
+
+
+def launches(B: int, K: int, V: int, topk_draft: int = 0, dtype: int = SV_BF16) -> int:
+    """Kernels a spec_verify call of this shape enqueues (1: the fused kernel)."""
+    n = load_library().spec_verify_launches(B, K, V, topk_draft, dtype)
+    if n < 0:
+        _check(-n)
+    return n
 
 
 def workspace_bytes(B: int, K: int, V: int, topk_draft: int = 0, dtype: int = SV_BF16) -> int:

@@ -2203,6 +2203,14 @@ int spec_verify_tree_timed(const void* target_logits, const void* draft_logits, 
                   nullptr, events, n_events);
 }
 
+int spec_verify_launches(int B, int K, int V, int topk_draft, int dtype) {
+  if (topk_draft >= V) topk_draft = 0;
+  Plan pl;
+  const int rc = make_plan(B, K, V, topk_draft, dtype, pl);
+  if (rc != SV_OK) return -rc;
+  return topk_draft > 0 && K > 0 ? 3 : 2;
+}
+
 int spec_verify_plan(int B, int K, int V, int topk_draft, int dtype, int* chunks, int* chunk_len) {
   if (!chunks || !chunk_len) return SV_ERR_ARG;
   if (topk_draft >= V) topk_draft = 0;

@@ -244,3 +244,13 @@ def test_noalloc_errors_before_any_launch():
     assert lib.spec_verify_noalloc(p, p, p, p, p, 4, 3, 1000, -1, B.SV_BF16, p, p, None) == B.SV_ERR_ARG
     assert lib.spec_verify_noalloc(p, p, p, p, p, 4, 3, 1000, 0, 9, p, p, None) == B.SV_ERR_ARG
     assert lib.spec_verify_status_string(B.SV_ERR_SCRATCH).startswith(b"shape needs more")
+
+
+def test_launch_count_query():
+    assert B.launches(256, 7, 201088, 0, B.SV_BF16) == 2
+    assert B.launches(256, 8, 151936, 128, B.SV_BF16) == 3
+    assert B.launches(4, 0, 1000, 16, B.SV_BF16) == 2          # no draft positions: no selection
+    assert B.launches(4, 3, 500, 500, B.SV_BF16) == 2           # top-k >= V is dense
+    lib = B.load_library()
+    assert lib.spec_verify_launches(0, 3, 1000, 0, B.SV_BF16) == -B.SV_ERR_ARG
+    assert lib.spec_verify_launches(4, B.SV_MAX_K + 1, 1000, 0, B.SV_BF16) == -B.SV_ERR_UNSUPPORTED
