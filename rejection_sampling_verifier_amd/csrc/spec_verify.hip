@@ -1998,7 +1998,7 @@ int launch_tree_kernel(F kernel, int grid, size_t lds, hipStream_t st, hipEvent_
 
 template <typename ET, bool AL>
 int launch_tree(const TreeArgs& a, size_t lds, hipStream_t st, hipEvent_t* ev) {
-  int rc = launch_tree_kernel(tree_stats_kernel<ET, AL>, a.B * 2 * a.N * a.C, 0, st, ev ? ev[0] : nullptr,
+  int rc = launch_tree_kernel(tree_stats_kernel<ET, AL>, a.B * a.N * a.C, 0, st, ev ? ev[0] : nullptr,
                               ev ? ev[1] : nullptr, a);
   if (rc != SV_OK) return rc;
   if (a.topk > 0) {

@@ -15,11 +15,11 @@
 // at a leaf it is the bonus token drawn from the leaf's target.  Greedy rows
 // (T <= 0) descend into the first child equal to the node's target argmax.
 //
-// Kernels.  tree_stats_kernel: one work-group per (row, node slot, chunk),
-// node slots 0..N-1 the targets and N..2N-1 the drafts (a draft slot only for
-// a node with children); it writes the chunk partials, the logits of each
-// child's token at its parent (target and draft), and for a leaf the 32
-// sub-block sums of its target.  tree_finish_kernel: one work-group per
+// Kernels.  tree_stats_kernel: one work-group per (row, node, chunk), for
+// the node's target and, if the node has children, its draft (partial slots
+// 0..N-1 the targets, N..2N-1 the drafts); it writes the chunk partials, the
+// logits of each child's token at its parent (target and draft), and for a
+// leaf the 32 sub-block sums of its target.  tree_finish_kernel: one work-group per
 // (row, chunk) walks the row's tree; the residual passes are shared out among
 // the row's work-groups chunk by chunk (see the kernel).
 
@@ -62,50 +62,24 @@ __device__ __forceinline__ uint32_t* tree_part(const TreeArgs& a, int b, int slo
 
 
 // ============================================================================
-// Statistics of one (row, node slot, chunk).
+// Statistics of one slot's chunk, from its tile r (target slot: slot = node;
+// draft slot: slot = N + node).  kids: the node's children mask.
 // ============================================================================
 template <typename ET, bool ALIGNED>
-__global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(STATS_WAVES, STATS_WAVES)))
-void tree_stats_kernel(TreeArgs a) {
+__device__ __forceinline__ void tree_slot_stats(const TreeArgs& a, int b, int node, bool is_draft, int c, int lo,
+                                                int len, const u32x4 (&r)[NV_TILE], float T, bool greedy,
+                                                unsigned long long kids, float* shf, int* shi, float* shsub) {
   constexpr int VEC = Tr<ET>::VEC;
-  const int N = a.N;
-  const int c = blockIdx.x % a.C;
-  const int rest = blockIdx.x / a.C;
-  const int slot = rest % (2 * N);
-  const int b = rest / (2 * N);
-  const int node = slot % N;
-  const bool is_draft = slot >= N;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  __shared__ float shf[NWAVE];
-  __shared__ int shi[NWAVE];
-  __shared__ float shsub[NSUB];
+  const int N = a.N, t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const ET* row = tree_row<ET>(a, is_draft, b, node);
-  const int lo = c * a.CS;
-  const int len = min(a.CS, a.V - lo);
-  // A target slot issues its loads before it needs the tree; a draft slot
-  // first checks that its node has children (and that the row samples).
-  u32x4 r[NV_TILE];
-  if (!is_draft) load_tile<ET, ALIGNED, NV_TILE>(row, lo, len, r);
-  // Every wave forms the node's children mask itself (no barrier before a
-  // leaf's draft work-group can leave).
-  const float T = a.temp[b];
-  const int p = (lane > 0 && lane < N) ? a.par[(size_t)b * N + lane] : -1;
-  const unsigned long long kids = __ballot(lane > node && lane < N && p == node);
-  if (a.probes && slot == 0 && c == 0)
-    for (int i = t; i < 3 * N; i += WG) a.probes[(size_t)b * 3 * N + i] = __builtin_nanf("");
-  const bool greedy = !is_sampling_temperature(T);
-  if (is_draft) {
-    if (greedy || kids == 0) return;  // no children drawn from this draft (or a greedy row)
-    load_tile<ET, ALIGNED, NV_TILE>(row, lo, len, r);
-    if (a.topk > 0) {
-      // A truncated draft: the chunk's candidates for the node's top k.
-      const size_t chunk = ((size_t)b * N + node) * a.C + c;
-      topk_chunk<ET>(r, lo, len, a.topk, reinterpret_cast<typename Cand<ET>::T*>(a.cand) + chunk * NWAVE * WCAP,
-                     a.ccnt + chunk * NWAVE, shf);
-      return;
-    }
+  if (is_draft && a.topk > 0) {
+    // A truncated draft: the chunk's candidates for the node's top k.
+    const size_t chunk = ((size_t)b * N + node) * a.C + c;
+    topk_chunk<ET>(r, lo, len, a.topk, reinterpret_cast<typename Cand<ET>::T*>(a.cand) + chunk * NWAVE * WCAP,
+                   a.ccnt + chunk * NWAVE, shf);
+    return;
   }
-  uint32_t* dst = tree_part(a, b, slot, c);
+  uint32_t* dst = tree_part(a, b, is_draft ? N + node : node, c);
   if (greedy) {
     float bv = Tr<ET>::at(r[0], 0);
     int bi = lo + t * VEC;
@@ -155,6 +129,45 @@ void tree_stats_kernel(TreeArgs a) {
     if (d >= lo && d < lo + len) a.gath[((size_t)b * N + t) * 2 + (is_draft ? 1 : 0)] = Tr<ET>::load1(row + d);
   }
   if (t == 0) *reinterpret_cast<u32x4*>(dst) = u32x4{__float_as_uint(m), __float_as_uint(z), 0u, 0u};
+}
+
+// ============================================================================
+// Statistics of one (row, node, chunk): the node's target and, for a node
+// with children in a sampling row, its draft (the distribution the children
+// were drawn from).  The target's tile, the temperature and the parents are
+// loaded at once; the draft's loads are issued as soon as the children mask
+// is known and overlap the target's statistics.  Leaves and greedy rows read
+// no draft.
+// ============================================================================
+template <typename ET, bool ALIGNED>
+__global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(STATS_WAVES, STATS_WAVES)))
+void tree_stats_kernel(TreeArgs a) {
+  const int N = a.N;
+  const int c = blockIdx.x % a.C;
+  const int rest = blockIdx.x / a.C;
+  const int node = rest % N;
+  const int b = rest / N;
+  const int t = threadIdx.x, lane = t & 63;
+  __shared__ float shf[NWAVE];
+  __shared__ int shi[NWAVE];
+  __shared__ float shsub[NSUB];
+  const int lo = c * a.CS;
+  const int len = min(a.CS, a.V - lo);
+  u32x4 rt[NV_TILE], rq[NV_TILE];
+  load_tile<ET, ALIGNED, NV_TILE>(tree_row<ET>(a, false, b, node), lo, len, rt);
+  // Every wave forms the node's children mask itself.
+  const float T = a.temp[b];
+  const int p = (lane > 0 && lane < N) ? a.par[(size_t)b * N + lane] : -1;
+  const unsigned long long kids = __ballot(lane > node && lane < N && p == node);
+  if (a.probes && node == 0 && c == 0)
+    for (int i = t; i < 3 * N; i += WG) a.probes[(size_t)b * 3 * N + i] = __builtin_nanf("");
+  const bool greedy = !is_sampling_temperature(T);
+  const bool with_draft = !greedy && kids != 0;  // uniform
+  if (with_draft) load_tile<ET, ALIGNED, NV_TILE>(tree_row<ET>(a, true, b, node), lo, len, rq);
+  tree_slot_stats<ET, ALIGNED>(a, b, node, false, c, lo, len, rt, T, greedy, kids, shf, shi, shsub);
+  if (!with_draft) return;
+  __syncthreads();  // the shared scratch is reused
+  tree_slot_stats<ET, ALIGNED>(a, b, node, true, c, lo, len, rq, T, greedy, kids, shf, shi, shsub);
 }
 
 // ============================================================================
