@@ -329,13 +329,15 @@ def main():
     roof_kernel, roof_bytes, roof_ms = "stats_kernel", by["stats_kernel"], stats_ms
     achieved = roof_bytes / (roof_ms * 1e-3) / 1e9
     if args.early_exit:
-        # One kernel per call: its algorithmic bytes are the logits of the
-        # positions each row reaches (targets 0..n, drafts 0..min(n, K-1) of
-        # sampling rows); the residual re-read is extra traffic.
+        # Algorithmic bytes: the logits of the positions each row reaches
+        # (targets 0..n, drafts 0..min(n, K-1) of sampling rows); a truncated
+        # draft is selected before the walk, so all K drafts of a sampling
+        # row are read.  The residual re-read is extra traffic.
         n_acc = nacc.cpu().numpy().astype(np.int64)
         esz = d["target"].itemsize
         samp = d["temperature"] > 0
-        rows = np.minimum(n_acc + 1, K + 1) + np.where(samp, np.minimum(n_acc + 1, K), 0)
+        drafts = np.full_like(n_acc, K) if int(d["topk"]) > 0 else np.minimum(n_acc + 1, K)
+        rows = np.minimum(n_acc + 1, K + 1) + np.where(samp, drafts, 0)
         roof_kernel, roof_bytes, roof_ms = "early_exit_kernel", int(rows.sum()) * V * esz, ms_per_step
         achieved = roof_bytes / (roof_ms * 1e-3) / 1e9
     traffic = traffic_from_profiles(f"B{B}K{K}V{V}", roof_kernel)

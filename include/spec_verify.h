@@ -215,14 +215,18 @@ int spec_verify_kl(const void* target_logits, const void* draft_logits,
  * probabilities p_i(d_i), q_i(d_i) and the final mass equal spec_verify's
  * bit for bit.
  *
- * One kernel per call.  topk_draft as spec_verify: a truncated draft's
- * selection is made for a position only once the row reaches it.  A shape
- * whose row statistics ((2K+1) C 16 + C 128 bytes, plus C 16 + 16 topk_draft
- * for a truncated draft) do not fit the kernel's LDS is SV_ERR_UNSUPPORTED.
- * The workspace has its own size (query with workspace == NULL) and must
- * not be shared with the other entry points: this call keeps it zero between
- * calls of one shape and relies on that (zero-fill it before a call of
- * another shape).
+ * One kernel per call for a dense draft.  topk_draft as spec_verify: a
+ * truncated draft's selection does not depend on any decision, so such a
+ * call makes every position's selection before the walk (three kernels:
+ * position 0's statistics and the drafts' candidate lists, the selections,
+ * the walk); it reads all K drafts of a sampling row, and the targets up to
+ * the first rejection.  A shape whose row statistics ((2K+1) C 16 + C 128
+ * bytes, plus 16 topk_draft for a truncated draft) do not fit the walking
+ * kernel's LDS is SV_ERR_UNSUPPORTED.  The workspace has its own size (query
+ * with workspace == NULL) and must not be shared with the other entry
+ * points: each call leaves it ready for the next call of the same shape (a
+ * dense draft leaves it all zero); zero-fill it before a call of another
+ * shape.
  * probs_out  [B, K, 2] float32 device or NULL: (p_i(d_i), q_i(d_i)) of every
  *            position the row tested, NaN past its first rejection (and for
  *            greedy rows).

@@ -330,7 +330,8 @@ def new_early_exit_workspace(B: int, K: int, V: int, dtype: int = SV_BF16, devic
 def verify_early_exit(target, draft, draft_tokens, uniforms, temperature, topk_draft: int = 0, *,
                       probes: bool = False, out_tokens=None, num_accepted=None, workspace=None, stream=None):
     """spec_verify_early_exit: the same results as ``verify``, reading each
-    row's logits only up to its first rejection.
+    row's target logits (and a dense draft's) only up to its first rejection;
+    a truncated draft is selected in full first.
 
     Returns (out_tokens, num_accepted), plus (probs [B, K, 2], mass [B]) when
     ``probes`` is set (probabilities past a row's first rejection are NaN).

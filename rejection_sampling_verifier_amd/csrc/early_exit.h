@@ -12,27 +12,43 @@
 //
 // One launch, one work-group per (row, chunk), numbered chunk-major.  A
 // row's work is cut into stages: stage i <= n computes the chunk statistics
-// of position i (target, and the draft of a sampling row; a truncated draft
-// publishes candidate lists instead, and the first work-group to collect the
-// stage makes the position's selection for all); after a rejection at n one
-// more stage computes the residual sums of position n.  Each stage is cut
-// into tickets, one per chunk and slot, numbered consecutively across the
-// stages and handed out by an agent-scope counter to the row's work-groups
-// in the order they ask.  A work-group holding a ticket of the current stage
-// computes that chunk and publishes it; holding a ticket of a later stage,
-// it waits for the current stage's words -- every ticket of which has been
-// handed out to a running work-group -- and takes the row's next decision
-// with them.  So a stage is computed only once the decision before it has
-// accepted, and no work-group waits for one that may not have started.  The
-// holder of the first ticket past the last stage draws the final token; the
-// last work-group of the row to finish clears the row's published words and
-// counters for the next call.
+// of position i (target, and the draft of a sampling row); after a rejection
+// at n one more stage computes the residual sums of position n.  Each stage
+// is cut into tickets, one per chunk and slot, numbered consecutively across
+// the stages and handed out by an agent-scope counter to the row's
+// work-groups in the order they ask.  A work-group holding a ticket of the
+// current stage computes that chunk and publishes it; holding a ticket of a
+// later stage, it waits for the current stage's words -- every ticket of
+// which has been handed out to a running work-group -- and takes the row's
+// next decision with them.  So a stage is computed only once the decision
+// before it has accepted, and no work-group waits for one that may not have
+// started.  The holder of the first ticket past the last stage draws the
+// final token; the last work-group of the row to finish clears the row's
+// published words and counters for the next call.
+//
+// A truncated draft's exact selection does not depend on any decision, and
+// made inside the walk it sat on every stage's critical path.  Such calls
+// therefore run two launches first: the statistics kernel's body over
+// position 0's target and every draft slot (candidate lists), then the merge
+// kernel (every position's selection).  The walk then starts at its first
+// decision, and each later stage holds the target's chunks only.
+
+// Truncated drafts, the first of the call's three launches: one work-group
+// per (row, slot, chunk) over position 0's target (slot 0) and the K draft
+// slots (slots 1..K), with the statistics kernel's body: plain partial words
+// for position 0, candidate lists for the drafts of sampling rows.
+template <typename ET, bool ALIGNED, int WAVES>
+__global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(WAVES, WAVES))) void ee_first_kernel(Args a) {
+  const int rest = blockIdx.x / a.C;
+  const int j = rest % (a.K + 1);
+  stats_body<ET, ALIGNED>(a, rest / (a.K + 1), j == 0 ? 0 : a.K + j, blockIdx.x % a.C);
+}
 
 // Statistics of one chunk of one slot (target position `pos`, or the draft
 // of position `pos` when `draft`), published as the words spec_verify's
 // statistics kernel writes; the bonus position also publishes its 32
 // sub-block sums.
-template <typename ET, bool ALIGNED, bool SPARSE>
+template <typename ET, bool ALIGNED>
 __device__ __forceinline__ void ee_stats_chunk(const Args& a, int b, int pos, int c, bool greedy, bool draft,
                                                float s, float* shf, int* shi, float* shsub) {
   constexpr int VEC = Tr<ET>::VEC;
@@ -42,14 +58,6 @@ __device__ __forceinline__ void ee_stats_chunk(const Args& a, int b, int pos, in
   const ET* row = draft ? draft_row<ET>(a, b, pos) : target_row<ET>(a, b, pos);
   u32x4 r[NV_TILE];
   load_tile<ET, ALIGNED, NV_TILE>(row, lo, len, r);
-  if (SPARSE && draft) {
-    // A truncated draft: the chunk's candidates, published for the row's
-    // other work-groups.
-    const size_t chunk = ((size_t)b * K + pos) * a.C + c;
-    topk_chunk<ET, true>(r, lo, len, a.topk, reinterpret_cast<typename Cand<ET>::T*>(a.cand) + chunk * NWAVE * WCAP,
-                         a.ccnt + chunk * NWAVE, shf);
-    return;
-  }
   const int d = pos < K ? a.tok[(size_t)b * K + pos] : -1;
   uint32_t* dst = part_words(a, b, draft ? K + 1 + pos : pos, c);
   if (greedy) {
@@ -151,58 +159,6 @@ __device__ __forceinline__ void ee_residual_chunk(const Args& a, int b, int n, i
   if (t < NSUB) pub_f32(a.subR + ((size_t)b * a.C + c) * NSUB + t, shsub[t]);
 }
 
-// Sparse drafts: waits until every candidate list of position `pos` is
-// published (its count, then its entries).  Counts are left in cnt (LDS).
-__device__ __forceinline__ bool ee_wait_cands(const Args& a, int b, int pos, uint64_t deadline, int* cnt) {
-  const int NL = a.C * NWAVE;
-  const size_t slot = (size_t)b * a.K + pos;
-  if (!wait_words(reinterpret_cast<const uint32_t*>(a.ccnt + slot * NL), NL, reinterpret_cast<uint32_t*>(cnt),
-                  nullptr, 0, nullptr, deadline))
-    return false;
-  const uint64_t* g = reinterpret_cast<const uint64_t*>(a.cand) + slot * NL * WCAP;
-  for (;;) {
-    bool ok = true;
-    for (int i = threadIdx.x; i < NL * WCAP; i += WG) {
-      const int L = i / WCAP, j = i % WCAP;
-      if (j < cnt[L]) ok &= cand_ld<true>(g + (size_t)L * WCAP + j) != 0ull;
-    }
-    if (__syncthreads_and(ok)) return true;
-    if (__syncthreads_or(wall_clock64() > deadline)) return false;
-    __builtin_amdgcn_s_sleep(2);
-  }
-}
-
-// Sparse drafts: the exact top-k selection of position `pos`'s draft, made
-// by the first work-group of the row to get here (from the published
-// candidate lists) and published for the others, which wait for it: the
-// first one is running, so the wait ends.  Leaves {max kept logit, Z_q,
-// q~(d), kept count} in *qs and the kept ids and logits (ascending id) in
-// kid[0..topk) and kid[topk..2 topk) (LDS).  The published words: the four
-// of *qs, then the ids, then the logits.
-template <typename ET>
-__device__ __forceinline__ bool ee_select(const Args& a, int b, int pos, int d, int* lcnt, int* kid, float4* qs) {
-  __shared__ unsigned s_first;
-  const int t = threadIdx.x, kk = a.topk;  // topk < V: kk ids are kept
-  const size_t slot = (size_t)b * a.K + pos;
-  uint32_t* res = a.mres + slot * (4 + 2 * (size_t)kk);
-  if (t == 0) s_first = __hip_atomic_fetch_add(a.mclaim + slot, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u;
-  __syncthreads();
-  const uint64_t deadline = wall_clock64() + WAIT_TICKS;
-  if (!s_first)
-    return wait_words(res, 4, reinterpret_cast<uint32_t*>(qs), res + 4, 2 * kk, reinterpret_cast<uint32_t*>(kid),
-                      deadline);
-  if (!ee_wait_cands(a, b, pos, deadline, lcnt)) return false;
-  float* kl = reinterpret_cast<float*>(kid + kk);
-  merge_body<ET, true>(a, b, pos, d, qs, kid, kl);
-  __syncthreads();
-  for (int i = t; i < kk; i += WG) {
-    pub_u32(res + 4 + i, (uint32_t)kid[i]);
-    pub_f32(res + 4 + kk + i, kl[i]);
-  }
-  if (t < 4) pub_u32(res + t, reinterpret_cast<const uint32_t*>(qs)[t]);
-  return true;
-}
-
 // Sparse drafts: the residual sums of one chunk, as finish_kernel's sparse
 // branch (the sum of p over a sub-block less min(p, q~) at its kept ids);
 // the kept ids and q~ values are in kid / kq (LDS, ascending id).
@@ -281,14 +237,13 @@ __device__ __forceinline__ void ee_merge_slot(const Args& a, RowShared& rs, cons
   }
 }
 
-// SPARSE: the instantiation for truncated drafts.  Their selection is heavy
-// in registers: the compiler is held to four waves per SIMD (a few spills)
-// rather than two, which measured faster; dense calls keep the lighter code.
+// SPARSE: the instantiation for truncated drafts, whose position-0
+// statistics (plain words) and selections (qstat, kept) were written by the
+// two launches before it.
 template <typename ET, bool ALIGNED, bool SPARSE>
-__global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(SPARSE ? 4 : 1))) void early_exit_kernel(Args a) {
+__global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4))) void early_exit_kernel(Args a) {
   // Dynamic LDS: [(2K+1) * C * 4] decoded words, [C * NSUB] sums, then for a
-  // sparse draft [C * NWAVE] list counts and [topk] kept ids, logits, q~
-  // values and corrections.
+  // sparse draft [topk] kept ids, logits, q~ values and corrections.
   extern __shared__ __align__(16) uint32_t ee_cache[];
   __shared__ RowShared rs;
   __shared__ float shf[NWAVE];
@@ -304,8 +259,7 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(SPARSE ? 4 :
   const int t = threadIdx.x, wave = t >> 6;
   uint32_t* pw = ee_cache;
   uint32_t* sub = ee_cache + (size_t)S * C * 4;
-  int* lcnt = reinterpret_cast<int*>(sub + (size_t)C * NSUB);
-  int* kid = lcnt + C * NWAVE;
+  int* kid = reinterpret_cast<int*>(sub + (size_t)C * NSUB);
   float* kl = reinterpret_cast<float*>(kid + a.topk);
   float* kq = kl + a.topk;
   float* kcorr = kq + a.topk;
@@ -331,8 +285,12 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(SPARSE ? 4 :
   unsigned ticket = NONE;  // held ticket
   bool ok = true;
   // Tickets of the current stage: one per chunk and slot (a sampling
-  // position below K has a target and a draft slot).
-  auto stage_size = [&]() { return (unsigned)((phase == STATS && !greedy && pos < K) ? 2 * C : C); };
+  // position below K has a target and a draft slot; with a truncated draft
+  // position 0 is computed already and later positions hold the target only).
+  auto stage_size = [&]() -> unsigned {
+    if (SPARSE && phase == STATS && pos == 0) return 0u;
+    return (phase == STATS && !SPARSE && !greedy && pos < K) ? 2u * C : (unsigned)C;
+  };
   unsigned size = stage_size();
   for (;;) {
     if (ticket == NONE) {
@@ -343,10 +301,7 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(SPARSE ? 4 :
     if (ticket - base < size) {
       const int k = (int)(ticket - base);
       if (phase == STATS) {
-        // A truncated draft's chunks come first in their stage: its selection
-        // then overlaps the target chunks.
-        const bool dslot = (SPARSE && sparse && pos < K) ? k < C : k >= C;
-        ee_stats_chunk<ET, ALIGNED, SPARSE>(a, b, pos, k % C, greedy, dslot, s, shf, shi, shsub);
+        ee_stats_chunk<ET, ALIGNED>(a, b, pos, k % C, greedy, !SPARSE && k >= C, s, shf, shi, shsub);
       } else if (sparse) {
         const float MSt = mul_rn(rs.M[pos], s), rZt = 1.f / rs.Z[pos];
         ee_residual_chunk_sparse<ET, ALIGNED>(a, b, pos, k, s, MSt, rZt, kid, kq, kcorr, (int)s_qs.w, shsub);
@@ -363,17 +318,27 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(SPARSE ? 4 :
     if (phase == STATS) {
       const bool draft = !greedy && pos < K && !sparse;
       const bool bonus = !greedy && pos == K;
-      // A truncated draft's selection first (its chunks were handed out first).
-      if constexpr (SPARSE)
-        if (sparse && pos < K) ok = ee_select<ET>(a, b, pos, rs.tok[pos], lcnt, kid, &s_qs);
-      if (ok)
+      if (SPARSE && pos == 0) {
+        // Written by the statistics launch before this one: plain words.
+        for (int i = t; i < C * 4; i += WG) pw[i] = part_words(a, b, 0, 0)[i];
+      } else {
         ok = wait_words(part_words(a, b, pos, 0), C * 4, pw + (size_t)pos * C * 4,
                         draft ? part_words(a, b, K + 1 + pos, 0) : (bonus ? a.subK + (size_t)b * C * NSUB : nullptr),
                         draft ? C * 4 : (bonus ? C * NSUB : 0),
                         draft ? pw + (size_t)(K + 1 + pos) * C * 4 : (bonus ? sub : nullptr),
                         wall_clock64() + WAIT_TICKS);
+      }
       if (!ok) break;
       if constexpr (SPARSE) if (sparse && pos < K) {
+        // The position's selection, made by the merge kernel.
+        const size_t slot = (size_t)b * K + pos;
+        if (t == 0) s_qs = a.qstat[slot];
+        for (int j = t; j < a.topk; j += WG) {
+          const uint2 e = a.kept[slot * a.topk + j];
+          kid[j] = (int)e.x;
+          kl[j] = __uint_as_float(e.y);
+        }
+        __syncthreads();
         const float4 qs = s_qs;
         const float MSq = mul_rn(qs.x, s), rZq = 1.f / qs.y;
         for (int j = t; j < (int)qs.w; j += WG) kq[j] = exp2_fast(fmaf(kl[j], s, -MSq)) * rZq;
@@ -470,26 +435,6 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(SPARSE ? 4 :
     for (int i = t; i < C * NSUB; i += WG) clear_word(a.subK + (size_t)b * C * NSUB + i);
   if (!ok || (!greedy && pos < K))
     for (int i = t; i < C * NSUB; i += WG) clear_word(a.subR + (size_t)b * C * NSUB + i);
-  if (SPARSE && (sparse || !ok)) {
-    // Published candidate lists and counts of the positions computed.
-    const int NL = C * NWAVE;
-    for (int p = 0; p < min(last + 1, K); ++p) {
-      const size_t slot = (size_t)b * K + p;
-      uint32_t* cw = reinterpret_cast<uint32_t*>(a.ccnt + slot * NL);
-      uint64_t* g = reinterpret_cast<uint64_t*>(a.cand) + slot * NL * WCAP;
-      for (int i = t; i < NL * WCAP; i += WG) {
-        const int L = i / WCAP, j = i % WCAP;
-        const uint32_t w = peek(cw + L);
-        const int n = w ? min((int)~w, WCAP) : (ok ? 0 : WCAP);
-        if (j < n) __hip_atomic_store(g + (size_t)L * WCAP + j, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      __syncthreads();  // the counts are read before they are cleared
-      for (int i = t; i < NL; i += WG) clear_word(cw + i);
-      uint32_t* res = a.mres + slot * (4 + 2 * (size_t)a.topk);
-      for (int i = t; i < 4 + 2 * a.topk; i += WG) clear_word(res + i);
-      if (t == 0) __hip_atomic_store(a.mclaim + slot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
   if (t == 0) {
     __hip_atomic_store(a.claim + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(a.leave + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -109,9 +109,8 @@ struct Args {
   float* kl;                 // [B, K] KL(p_i || q_i) out (spec_verify_kl: paired statistics), or null
   unsigned* claim;           // [B] early exit: stage tickets handed out
   unsigned* leave;           // [B] early exit: work-groups of the row that have finished
-  unsigned* mclaim;          // [B, K] early exit, sparse draft: work-groups that reached a position's selection
-  uint32_t* mres;            // [B, K, 4 + 2 topk] early exit, sparse draft: published selection results
   int GA;                    // statistics work-groups per row: (2K+1) * C
+  int resident;              // finishing work-groups the device holds at once (0: unknown)
   int cache;                 // 1: finishing work-groups keep the row's words in dynamic LDS
 };
 
@@ -136,31 +135,9 @@ __device__ __forceinline__ float got_f32(const uint32_t* p) { return __uint_as_f
 __device__ __forceinline__ void clear_word(uint32_t* p) {
   __hip_atomic_store(p, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// Candidate lists read by another work-group (early exit): composites are
-// never zero, so each entry is published as itself with a write-through
-// agent-scope atomic store and read with agent-scope atomic loads; counts
-// are published words.  PUB = false: plain stores and loads (the next
-// kernel reads them).
-template <bool PUB>
-__device__ __forceinline__ void cand_st(uint64_t* p, uint64_t v) {
-  if constexpr (PUB) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  else __builtin_nontemporal_store(v, p);
-}
-template <bool PUB>
-__device__ __forceinline__ uint64_t cand_ld(const uint64_t* p) {
-  if constexpr (PUB) return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  else return *p;
-}
-template <bool PUB>
-__device__ __forceinline__ void cnt_st(int* p, int v) {
-  if constexpr (PUB) pub_u32(reinterpret_cast<uint32_t*>(p), (uint32_t)v);
-  else *p = v;
-}
-template <bool PUB>
-__device__ __forceinline__ int cnt_ld(const int* p) {
-  if constexpr (PUB) return (int)got_u32(reinterpret_cast<const uint32_t*>(p));
-  else return *p;
-}
+// Candidate lists: written once by the statistics pass and read once by the
+// merge kernel, a later launch (streaming stores, plain loads).
+__device__ __forceinline__ void cand_st(uint64_t* p, uint64_t v) { __builtin_nontemporal_store(v, p); }
 
 __device__ __forceinline__ uint32_t* part_words(const Args& a, int b, int slot, int c) {
   return a.part + (((size_t)b * (2 * a.K + 1) + slot) * (size_t)a.C + c) * 4;
@@ -267,7 +244,7 @@ struct Staged<float> {
 // tau with at least kk logits >= tau is the kk-th largest; logits above tau
 // are all kept, ties at tau are kept in increasing id order.  The kk kept
 // composites are written to dst[0..kk).
-template <typename ET, bool PUB>
+template <typename ET>
 __device__ void topk_chunk_exact(const u32x4 (&r)[NV_TILE], int lo, int len, int kk, uint64_t* dst,
                                  float* red) {
   constexpr int VEC = Tr<ET>::VEC;
@@ -303,7 +280,7 @@ __device__ void topk_chunk_exact(const u32x4 (&r)[NV_TILE], int lo, int len, int
     for (int e = 0; e < VEC; ++e) {
       const float x = Tr<ET>::at(r[j], e);
       const int off = (j * WG + t) * VEC + e;
-      if (off < len && order_key(x) > tau) cand_st<PUB>(dst + at++, composite(x, lo + off));
+      if (off < len && order_key(x) > tau) cand_st(dst + at++, composite(x, lo + off));
     }
     carry += tot;
   }
@@ -322,7 +299,7 @@ __device__ void topk_chunk_exact(const u32x4 (&r)[NV_TILE], int lo, int len, int
       const float x = Tr<ET>::at(r[j], e);
       const int off = (j * WG + t) * VEC + e;
       if (off < len && order_key(x) == tau) {
-        if (rank < need) cand_st<PUB>(dst + above + rank, composite(x, lo + off));
+        if (rank < need) cand_st(dst + above + rank, composite(x, lo + off));
         ++rank;
       }
     }
@@ -338,11 +315,43 @@ __device__ void topk_chunk_exact(const u32x4 (&r)[NV_TILE], int lo, int len, int
 // the upper 16 bits of their order keys; the smallest of the four bounds is
 // a lower bound of the chunk's k-th largest logit (each wave has ceil(k/4)
 // logits at or above it), so every logit of the chunk's top k passes it.
-// Each wave lists the logits that pass.  The lists are unsorted; the merge
-// kernel selects exactly.  Exact path (k > 256, or a list over WCAP): the
-// chunk's exact top min(k, len) is stored contiguously across the four list
-// areas.
-template <typename ET, bool PUB = false>
+// Each wave lists the logits that pass: the vectors whose maximum passes
+// (few: about one in ten) are compacted into LDS in vector order, then each
+// lane tests the eight logits of one of them, so the per-logit work is spent
+// on those vectors only; a wave with more than VCAP such vectors marks its
+// logits one by one instead.  The lists are unsorted; the merge kernel
+// selects exactly.  Exact path (k > 256, or a list over WCAP): the chunk's
+// exact top min(k, len) is stored contiguously across the four list areas.
+constexpr int VCAP = 128;  // passing vectors a wave compacts
+
+// The 32-bit word of a vector that holds element e (e < VEC), selected
+// without dynamic register indexing.
+template <typename ET>
+__device__ __forceinline__ float vec_elem(const u32x4& v, int e) {
+  constexpr int VEC = Tr<ET>::VEC;
+  const int wi = e / (VEC / 4);
+  uint32_t word = v[0];
+  word = wi == 1 ? v[1] : word;
+  word = wi == 2 ? v[2] : word;
+  word = wi == 3 ? v[3] : word;
+  if constexpr (VEC == 8)
+    return __uint_as_float((e & 1) ? (word & 0xFFFF0000u) : (word << 16));
+  else
+    return __uint_as_float(word);
+}
+
+template <typename ET>
+__device__ __forceinline__ float vec_max(const u32x4& v) {
+  if constexpr (Tr<ET>::VEC == 8)
+    return max3_raw(max3_raw(Tr<ET>::at(v, 0), Tr<ET>::at(v, 1), Tr<ET>::at(v, 2)),
+                    max3_raw(Tr<ET>::at(v, 3), Tr<ET>::at(v, 4), Tr<ET>::at(v, 5)),
+                    max3_raw(Tr<ET>::at(v, 6), Tr<ET>::at(v, 7), Tr<ET>::at(v, 7)));
+  else
+    return max3_raw(max3_raw(Tr<ET>::at(v, 0), Tr<ET>::at(v, 1), Tr<ET>::at(v, 2)), Tr<ET>::at(v, 3),
+                    Tr<ET>::at(v, 3));
+}
+
+template <typename ET>
 __device__ void topk_chunk(const u32x4 (&r)[NV_TILE], int lo, int len, int k, typename Cand<ET>::T* dst,
                            int* cnts, float* red) {
   constexpr int VEC = Tr<ET>::VEC;
@@ -351,13 +360,21 @@ __device__ void topk_chunk(const u32x4 (&r)[NV_TILE], int lo, int len, int k, ty
   using ST = typename Staged<ET>::T;
   // Fast path: each wave's list of passing logits, staged as (bits, offset).
   __shared__ uint64_t sbuf[NWAVE * WCAP];
+  __shared__ u32x4 vbuf[NWAVE * VCAP];      // the wave's passing vectors
+  __shared__ uint16_t voff[NWAVE * VCAP];   // and their offsets in the chunk
   __shared__ uint32_t wkey[NWAVE];
   __shared__ int s_over;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int kk = min(k, len);
   bool done = false;
   if (k <= TOPK_FAST_MAX) {
-    const uint32_t key = order_key(tile_max<ET, NV_TILE>(r)) >> 16;  // padding reads as -inf
+    float vm[NV_TILE];  // the thread's vector maxima (padding reads as -inf)
+#pragma unroll
+    for (int j = 0; j < NV_TILE; ++j) vm[j] = vec_max<ET>(r[j]);
+    float tm = max3_raw(vm[0], vm[1], vm[2]);
+#pragma unroll
+    for (int j = 3; j < NV_TILE; j += 2) tm = max3_raw(tm, vm[j], vm[j + 1 < NV_TILE ? j + 1 : j]);
+    const uint32_t key = order_key(tm) >> 16;
     const int m = (k + NWAVE - 1) / NWAVE;
     uint32_t pre = 0;
     for (int bit = 15; bit >= 0; --bit) {
@@ -371,87 +388,120 @@ __device__ void topk_chunk(const u32x4 (&r)[NV_TILE], int lo, int len, int k, ty
     // bucket of -inf reads back as a NaN pattern, which must become -inf.
     float bound = key_value(min(min(wkey[0], wkey[1]), min(wkey[2], wkey[3])));
     if (bound != bound) bound = NEG_INF;
-    // Each thread marks its passing logits in bit masks, logit i of the
-    // thread at bit 31 - (i % 32) of mask i / 32; padding past the chunk
-    // reads as -inf, so it can pass only a bound of -inf, the one case that
-    // needs the range check.
-    uint32_t mask[NE / 32];
-    auto mark = [&](auto check) {
-#pragma unroll
-      for (int h = 0; h < NE / 32; ++h) mask[h] = 0u;
-#pragma unroll
-      for (int j = 0; j < NV_TILE; ++j)
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          const int i = j * VEC + e;
-          bool pass = Tr<ET>::at(r[j], e) >= bound;
-          if (decltype(check)::value) pass = pass && (j * WG + t) * VEC + e < len;
-          mask[i / 32] = mask[i / 32] + mask[i / 32] + (pass ? 1u : 0u);
-        }
-    };
-    if (bound > NEG_INF)
-      mark(std::false_type{});
-    else
-      mark(std::true_type{});
-    int cnt = 0;
-#pragma unroll
-    for (int h = 0; h < NE / 32; ++h) cnt += __popc(mask[h]);
-    // The wave's list: thread order, then logit order within a thread.
-    // Positions wrap inside the wave's staging area: a list that overflows
-    // it is discarded below, so its clobbered entries are never read.
-    const float incl = wave_incl_scan((float)cnt);  // exact: at most 4096
-    const int n = (int)lane63(incl);
-    int pos = (int)incl - cnt;
+    // The wave's list is staged as (bits, offset).  Positions wrap inside the
+    // wave's staging area: a list that overflows it is discarded below, so
+    // its clobbered entries are never read.
     ST* wl_stage = reinterpret_cast<ST*>(sbuf) + wave * WCAP;
+    // Vectors whose maximum passes, compacted in the wave's area (only for a
+    // finite bound: with a bound of -inf every logit passes).  List order:
+    // vector j, then thread, then logit.
+    int nv = 0;  // wave-uniform
+    if (bound > NEG_INF) {
 #pragma unroll
-    for (int j = 0; j < NV_TILE; ++j) {
-      // Vector j's logits e = 0..VEC-1 sit at bits VEC-1-e of mj.
-      constexpr unsigned VMASK = (1u << VEC) - 1u;
-      uint32_t mj = (mask[(j * VEC) / 32] >> (32 - VEC - (j * VEC) % 32)) & VMASK;
-      while (mj) {
-        const int bp = 31 - __builtin_clz(mj);
-        mj &= ~(1u << bp);
-        const int e = VEC - 1 - bp;
-        const int wi = e / (VEC / 4);
-        uint32_t word = r[j][0];
-        word = wi == 1 ? r[j][1] : word;
-        word = wi == 2 ? r[j][2] : word;
-        word = wi == 3 ? r[j][3] : word;
-        float x;
-        if constexpr (VEC == 8)
-          x = __uint_as_float((e & 1) ? (word & 0xFFFF0000u) : (word << 16));
-        else
-          x = __uint_as_float(word);
-        wl_stage[pos & (WCAP - 1)] = Staged<ET>::pack(x, (j * WG + t) * VEC + e);
-        ++pos;
+      for (int j = 0; j < NV_TILE; ++j) {
+        const bool p = vm[j] >= bound;
+        const uint64_t bal = __ballot(p);
+        if (bal) {
+          const int idx = nv + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+          if (p && idx < VCAP) {
+            vbuf[wave * VCAP + idx] = r[j];
+            voff[wave * VCAP + idx] = (uint16_t)((j * WG + t) * VEC);
+          }
+          nv += __popcll(bal);
+        }
+      }
+    }
+    int n;
+    if (bound > NEG_INF && nv <= VCAP) {
+      __builtin_amdgcn_wave_barrier();  // the compacted vectors are read by other lanes
+      int pos0 = 0;
+      for (int q0 = 0; q0 < nv; q0 += 64) {
+        const int q = q0 + lane;
+        u32x4 v = u32x4{0u, 0u, 0u, 0u};
+        int off = 0;
+        uint32_t m8 = 0u;  // logit e of the vector at bit VEC-1-e
+        if (q < nv) {
+          v = vbuf[wave * VCAP + q];
+          off = voff[wave * VCAP + q];
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) m8 = m8 + m8 + (Tr<ET>::at(v, e) >= bound ? 1u : 0u);
+        }
+        const int c = __popc(m8);
+        const float incl = wave_incl_scan((float)c);  // exact: at most 512
+        int pos = pos0 + (int)incl - c;
+        while (m8) {
+          const int bp = 31 - __builtin_clz(m8);
+          m8 &= ~(1u << bp);
+          const int e = VEC - 1 - bp;
+          wl_stage[pos & (WCAP - 1)] = Staged<ET>::pack(vec_elem<ET>(v, e), off + e);
+          ++pos;
+        }
+        pos0 += (int)lane63(incl);
+      }
+      n = pos0;
+    } else {
+      // Each thread marks its passing logits in bit masks, logit i of the
+      // thread at bit 31 - (i % 32) of mask i / 32; padding past the chunk
+      // reads as -inf, so it can pass only a bound of -inf, the one case that
+      // needs the range check.  List order: thread, then logit.
+      uint32_t mask[NE / 32];
+      auto mark = [&](auto check) {
+#pragma unroll
+        for (int h = 0; h < NE / 32; ++h) mask[h] = 0u;
+#pragma unroll
+        for (int j = 0; j < NV_TILE; ++j)
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) {
+            const int i = j * VEC + e;
+            bool pass = Tr<ET>::at(r[j], e) >= bound;
+            if (decltype(check)::value) pass = pass && (j * WG + t) * VEC + e < len;
+            mask[i / 32] = mask[i / 32] + mask[i / 32] + (pass ? 1u : 0u);
+          }
+      };
+      if (bound > NEG_INF)
+        mark(std::false_type{});
+      else
+        mark(std::true_type{});
+      int cnt = 0;
+#pragma unroll
+      for (int h = 0; h < NE / 32; ++h) cnt += __popc(mask[h]);
+      const float incl = wave_incl_scan((float)cnt);  // exact: at most 4096
+      n = (int)lane63(incl);
+      int pos = (int)incl - cnt;
+#pragma unroll
+      for (int j = 0; j < NV_TILE; ++j) {
+        // Vector j's logits e = 0..VEC-1 sit at bits VEC-1-e of mj.
+        constexpr unsigned VMASK = (1u << VEC) - 1u;
+        uint32_t mj = (mask[(j * VEC) / 32] >> (32 - VEC - (j * VEC) % 32)) & VMASK;
+        while (mj) {
+          const int bp = 31 - __builtin_clz(mj);
+          mj &= ~(1u << bp);
+          const int e = VEC - 1 - bp;
+          wl_stage[pos & (WCAP - 1)] = Staged<ET>::pack(vec_elem<ET>(r[j], e), (j * WG + t) * VEC + e);
+          ++pos;
+        }
       }
     }
     if (lane == 0) {
-      if (!PUB) cnts[wave] = min(n, WCAP);
+      cnts[wave] = min(n, WCAP);
       if (n > WCAP) s_over = 1;
     }
-    if (!PUB && n <= WCAP) {
+    if (n <= WCAP) {
       // The wave's list is complete: written at once, without waiting for
       // the other waves (a chunk with an overflowing list is rewritten by
       // the exact path below).  The merge kernel reads it once: streaming
       // stores.
       CT* wl = dst + wave * WCAP;
-      for (int q = lane; q < n; q += 64) cand_st<PUB>(wl + q, Staged<ET>::composite_at(wl_stage[q], lo));
+      for (int q = lane; q < n; q += 64) cand_st(wl + q, Staged<ET>::composite_at(wl_stage[q], lo));
     }
     __syncthreads();
     done = s_over == 0;
-    if (PUB && done) {
-      // Published lists are written only once final, so that no entry is
-      // left past the counts (the reader and the clearing go by them).
-      CT* wl = dst + wave * WCAP;
-      for (int q = lane; q < n; q += 64) cand_st<PUB>(wl + q, Staged<ET>::composite_at(wl_stage[q], lo));
-      if (lane == 0) cnt_st<PUB>(cnts + wave, n);
-    }
   }
   if (!done) {
     __syncthreads();  // the fast path's lists are no longer read
-    topk_chunk_exact<ET, PUB>(r, lo, len, kk, dst, red);
-    if (t < NWAVE) cnt_st<PUB>(cnts + t, max(0, min(WCAP, kk - t * WCAP)));
+    topk_chunk_exact<ET>(r, lo, len, kk, dst, red);
+    if (t < NWAVE) cnts[t] = max(0, min(WCAP, kk - t * WCAP));
   }
 }
 
@@ -1194,7 +1244,7 @@ struct RegCands {
 };
 // Candidates read from their lists in global memory (one wave per list;
 // list L holds chunk L / NWAVE).
-template <typename ET, bool PUB = false>
+template <typename ET>
 struct ListCands {
   const typename Cand<ET>::T* g;
   const int* gcnt;
@@ -1203,9 +1253,9 @@ struct ListCands {
   __device__ __forceinline__ void each(F&& f) const {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     for (int L = wave; L < NL; L += NWAVE) {
-      const int n = cnt_ld<PUB>(gcnt + L);
+      const int n = *(gcnt + L);
       for (int j = lane; j < n; j += 64)
-        f(cand_composite<ET>(cand_ld<PUB>(g + (size_t)L * WCAP + j), (L / NWAVE) * CS));
+        f(cand_composite<ET>(*(g + (size_t)L * WCAP + j), (L / NWAVE) * CS));
     }
   }
 };
@@ -1329,13 +1379,11 @@ __device__ __forceinline__ float take_kept(const Src& src, uint64_t thr, int d, 
 }
 
 // The merge of slot (row b, position i): `d` is the token whose q~ is
-// recorded (-1 for none).  Returns kk, the number of kept ids.  With PUB the
-// candidate lists are published ones (early exit), and the results go to
-// LDS instead of the workspace: {max kept logit, Z_q, q~(d), kk} to
-// *qs_out, the kept ids and logits in ascending id order to kid_out / kl_out.
-template <typename ET, bool PUB = false>
-__device__ __forceinline__ int merge_body(const Args& a, int b, int i, int d, float4* qs_out = nullptr,
-                                          int* kid_out = nullptr, float* kl_out = nullptr) {
+// recorded (-1 for none).  Writes {max kept logit, Z_q, q~(d), kk} to qstat
+// and the kept ids and logits in ascending id order to kept; returns kk,
+// the number of kept ids.
+template <typename ET>
+__device__ __forceinline__ int merge_body(const Args& a, int b, int i, int d) {
   __shared__ __align__(16) uint64_t sel[SV_MAX_TOPK + 2];  // kept composites (+ a zero pad entry)
   __shared__ uint64_t ovf[MERGE_OVF];
   __shared__ uint32_t hist[RADIX_BINS];  // radix histogram, then the ranks of the kept entries
@@ -1368,10 +1416,10 @@ __device__ __forceinline__ int merge_body(const Args& a, int b, int i, int d, fl
     // area holds WCAP entries).
     RegCands<ET> rc;
     rc.CS = a.CS;
-    const int my_cnt = lane < C ? cnt_ld<PUB>(gcnt + wave + NWAVE * lane) : 0;
+    const int my_cnt = lane < C ? *(gcnt + wave + NWAVE * lane) : 0;
 #pragma unroll
     for (int r = 0; r < MERGE_REG; ++r)
-      rc.v[r] = r < C ? cand_ld<PUB>(g + (size_t)(wave + NWAVE * r) * WCAP + lane) : CT(0);
+      rc.v[r] = r < C ? *(g + (size_t)(wave + NWAVE * r) * WCAP + lane) : CT(0);
     __syncthreads();  // s_n / s_novf / rank initialised
     // Entries past the 64th go to the overflow buffer: one reservation per
     // wave, then one round of loads for entries 64..127 (entries 128 and
@@ -1401,7 +1449,7 @@ __device__ __forceinline__ int merge_body(const Args& a, int b, int i, int d, fl
 #pragma unroll
       for (int r = 0; r < MERGE_REG; ++r) {
         const int n = r < C ? __builtin_amdgcn_readlane(my_cnt, r) : 0;
-        w2[r] = 64 + lane < n ? cand_ld<PUB>(g + (size_t)(wave + NWAVE * r) * WCAP + 64 + lane) : CT(0);
+        w2[r] = 64 + lane < n ? *(g + (size_t)(wave + NWAVE * r) * WCAP + 64 + lane) : CT(0);
       }
       int o = base;
 #pragma unroll
@@ -1410,7 +1458,7 @@ __device__ __forceinline__ int merge_body(const Args& a, int b, int i, int d, fl
         if (64 + lane < n && o + lane < MERGE_OVF) ovf[o + lane] = cand_composite<ET>(w2[r], r * a.CS);
         for (int j = 128 + lane; j < n; j += 64)
           if (o + j - 64 < MERGE_OVF)
-            ovf[o + j - 64] = cand_composite<ET>(cand_ld<PUB>(g + (size_t)(wave + NWAVE * r) * WCAP + j), r * a.CS);
+            ovf[o + j - 64] = cand_composite<ET>(*(g + (size_t)(wave + NWAVE * r) * WCAP + j), r * a.CS);
         o += max(0, n - 64);
       }
     }
@@ -1421,13 +1469,13 @@ __device__ __forceinline__ int merge_body(const Args& a, int b, int i, int d, fl
       thr = select_threshold(rc, kk, sh32, red, ired, hist, &m);
       z = take_kept(rc, thr, d, s, mul_rn(m, s), sel, &s_n, &s_ld);
     } else {
-      const ListCands<ET, PUB> lc{g, gcnt, NL, a.CS};
+      const ListCands<ET> lc{g, gcnt, NL, a.CS};
       thr = select_threshold(lc, kk, sh32, red, ired, hist, &m);
       z = take_kept(lc, thr, d, s, mul_rn(m, s), sel, &s_n, &s_ld);
     }
   } else {
     __syncthreads();
-    const ListCands<ET, PUB> lc{g, gcnt, NL, a.CS};
+    const ListCands<ET> lc{g, gcnt, NL, a.CS};
     thr = select_threshold(lc, kk, sh32, red, ired, hist, &m);
     z = take_kept(lc, thr, d, s, mul_rn(m, s), sel, &s_n, &s_ld);
   }
@@ -1457,18 +1505,12 @@ __device__ __forceinline__ int merge_body(const Args& a, int b, int i, int d, fl
   __syncthreads();
   for (int j = t; j < kk; j += WG) {
     const uint64_t v = sel[j];
-    if constexpr (PUB) {
-      kid_out[rank[j]] = composite_id(v);
-      kl_out[rank[j]] = composite_value(v);
-    } else {
-      a.kept[slot * a.topk + rank[j]] = make_uint2((uint32_t)composite_id(v), __float_as_uint(composite_value(v)));
-    }
+    a.kept[slot * a.topk + rank[j]] = make_uint2((uint32_t)composite_id(v), __float_as_uint(composite_value(v)));
   }
   if (t == 0) {
     const uint32_t lb = s_ld;
     const float qd = lb != 0xFFFFFFFFu ? exp2_fast(fmaf(__uint_as_float(lb), s, -ms)) / Z : 0.f;
-    if constexpr (PUB) *qs_out = make_float4(m, Z, qd, (float)kk);
-    else a.qstat[slot] = make_float4(m, Z, qd, (float)kk);
+    a.qstat[slot] = make_float4(m, Z, qd, (float)kk);
   }
   (void)lane;
   return kk;
@@ -1483,13 +1525,29 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(8, 8))) void
   merge_body<ET>(a, b, i, a.tok[(size_t)b * a.K + i]);
 }
 
+// Finishing work-groups that take part per row, G <= C: each takes m chunks,
+// with m the smallest count for which the sampling rows' work-groups are
+// all resident at once (greedy rows need one work-group each, briefly).
+constexpr int FINISH_COUNT_MAX = 4096;  // rows whose temperatures a work-group counts
+__device__ __forceinline__ int finish_groups(int nsamp, int C, int resident) {
+  if (resident <= 0 || nsamp <= 0) return C;
+  const long long m = max(1LL, ((long long)nsamp * C + resident - 1) / resident);
+  return (int)((C + m - 1) / m);
+}
+
 // ============================================================================
-// Kernel B: finishing work-group (row b, chunk c).  Decides the row from the
+// Kernel B: finishing work-group j of row b.  Decides the row from the
 // statistics partials, then: greedy rows and rows that accepted every draft
-// are completed by the row's chunk-0 work-group; for a rejected row each
+// are completed by the row's work-group 0; for a rejected row each
 // work-group publishes the 32 sub-block sums of max(0, p_n - q_n) over its
-// chunk, and the last of the row's C work-groups to arrive (atomic counter)
-// draws the correction token and clears the row's published words.
+// chunks j, j + G, j + 2G, ..., and the last of the row's G work-groups to
+// arrive (atomic counter) draws the correction token and clears the row's
+// published words.  The grid has C work-groups per row; G of them take part
+// (the others leave at once), with G chosen from the number of sampling rows
+// so that the working grid is about what the chip holds at once: every
+// work-group decides once and then streams, and no late generation of
+// work-groups drains after the others.  Greedy rows need their work-group 0
+// only; the others leave before deciding.
 // ============================================================================
 __device__ __forceinline__ void write_failed_row(const Args& a, int b) {
   // Reached only if a wait ran past its deadline: num_accepted = -1 marks it.
@@ -1504,8 +1562,11 @@ __global__ __launch_bounds__(WG) void finish_kernel(Args a) {
   __shared__ RowShared rs;
   __shared__ float shsub[NSUB];
   __shared__ int sh_last;
-  const int c = blockIdx.x % a.C;
-  const int b = blockIdx.x / a.C;
+  __shared__ int sh_ns[NWAVE];
+  // Numbered j-major: the work-groups that take part (j < G) come first, and
+  // those past G, which leave at once, last.
+  const int j0 = blockIdx.x / a.B;
+  const int b = blockIdx.x % a.B;
   const int K = a.K, C = a.C, S = 2 * K + 1, t = threadIdx.x, lane = t & 63, wave = t >> 6;
   // Sparse draft: the row's kept list at the rejected position (ids and q~
   // values, for the residual and the final draw) and the corrections
@@ -1516,17 +1577,33 @@ __global__ __launch_bounds__(WG) void finish_kernel(Args a) {
   uint32_t* cache_pw = CACHED ? row_cache : nullptr;
   uint32_t* cache_sub = CACHED ? cache_pw + (size_t)S * C * 4 : nullptr;
   const RowIn in = load_row_in(a, b);
+  // The sampling rows of the batch, counted in the round of loads that
+  // brings the row's partials.
+  int ns = 0;
+  if (a.B <= FINISH_COUNT_MAX)
+    for (int i = t; i < a.B; i += WG) ns += is_sampling_temperature(a.temp[i]) ? 1 : 0;
   if (CACHED) {
     // All partials of the row in one round of loads (also the draft-token
     // logits, which the decision reads at a token-dependent chunk).
     const u32x4* src = reinterpret_cast<const u32x4*>(part_words(a, b, 0, 0));
     for (int i = t; i < S * C; i += WG) reinterpret_cast<u32x4*>(cache_pw)[i] = src[i];
-    __syncthreads();
   }
+  ns = (int)wave_sum((float)ns);  // exact: at most FINISH_COUNT_MAX
+  if (lane == 0) sh_ns[wave] = ns;
+  __syncthreads();
+  ns = a.B;
+  if (a.B <= FINISH_COUNT_MAX) {
+    ns = 0;
+#pragma unroll
+    for (int w = 0; w < NWAVE; ++w) ns += sh_ns[w];
+  }
+  const int G = finish_groups(ns, C, a.resident);
+  // Work-groups past G, and a greedy row's past the first, have nothing to do.
+  if (j0 >= G || (j0 != 0 && !is_sampling_temperature(in.T))) return;
   RowView<CACHED> view{cache_pw, cache_sub, false};
   decide_row(a, b, rs, view, in);
   const int n = rs.n;
-  if (c == 0 && a.kl && t < K) {
+  if (j0 == 0 && a.kl && t < K) {
     // KL(p_t || q_t) = E_p[l_t - l_q] / T - ln2 (fl(M_t s) - fl(M_q s)) - ln Z_t + ln Z_q,
     // with E_p[l_t - l_q] = sum_c A_c exp2(fl(m_c s) - fl(M_t s)) / Z_t; the
     // combination is done in double.
@@ -1546,12 +1623,12 @@ __global__ __launch_bounds__(WG) void finish_kernel(Args a) {
     }
     a.kl[(size_t)b * K + t] = kl;
   }
-  if (c == 0 && a.probs && t < K) {
+  if (j0 == 0 && a.probs && t < K) {
     a.probs[((size_t)b * K + t) * 2 + 0] = rs.greedy ? 0.f : rs.p[t];
     a.probs[((size_t)b * K + t) * 2 + 1] = rs.greedy ? 0.f : rs.q[t];
   }
   if (rs.greedy) {
-    if (c != 0) return;
+    if (j0 != 0) return;
     // The target's argmax replaces the first mismatch or fills the bonus slot.
     int32_t* out = a.out + (size_t)b * (K + 1);
     for (int i = t; i <= K; i += WG) out[i] = i < n ? rs.tok[i] : (i == n ? rs.idx[n] : -1);
@@ -1564,105 +1641,116 @@ __global__ __launch_bounds__(WG) void finish_kernel(Args a) {
   const float s = rs.s;
   const float MSt = mul_rn(rs.M[n], s), rZt = 1.f / rs.Z[n];
   if (n == K) {
-    if (c == 0) final_draw<ET, ALIGNED, CACHED>(a, b, n, s, MSt, rZt, 0.f, 0.f, rs, view, nullptr, nullptr, 0);
+    if (j0 == 0) final_draw<ET, ALIGNED, CACHED>(a, b, n, s, MSt, rZt, 0.f, 0.f, rs, view, nullptr, nullptr, 0);
     return;
   }
-  // Rejected at position n: residual max(0, p_n - q_n) over this chunk.
-  const int lo = c * a.CS;
-  const int len = min(a.CS, a.V - lo);
+  // Rejected at position n: residual max(0, p_n - q_n) over the
+  // work-group's chunks, each published as 32 sub-block sums.
+  uint32_t* subR_row = a.subR + (size_t)b * C * NSUB;
   float MSq, rZq;
   int nkept = 0;
   if (a.topk > 0) {
     // Sparse draft: q~ is non-zero only at the kept ids, so the residual of
     // a sub-block is sum(p) - sum over its kept ids of min(p, q~).  Only the
-    // target row is re-read.
-    // The kept list, its statistics and the tile are loaded in one round.
+    // target row is re-read.  The kept list (ids and q~ values, ascending
+    // id) goes to LDS once; its first entries, its statistics and the first
+    // chunk's tile are loaded in one round.
     const uint2* kept = a.kept + ((size_t)b * K + n) * a.topk;
     const float4 qs = a.qstat[(size_t)b * K + n];
     uint2 e0 = make_uint2(0xFFFFFFFFu, 0u);
     if (t < a.topk) e0 = kept[t];
     const ET* trow = target_row<ET>(a, b, n);
-    u32x4 rt[NV_TILE];
-    load_tile<ET, ALIGNED, NV_TILE>(trow, lo, len, rt);
     MSq = mul_rn(qs.x, s);
     rZq = 1.f / qs.y;
     nkept = (int)qs.w;
-    // Correction min(p, q~) of each kept id in this chunk (0 elsewhere); the
-    // ids go to kid[] in their (ascending) order.
-    float* corr = kcorr;
-    for (int j = t; j < nkept; j += WG) {
-      const uint2 e = j == t ? e0 : kept[j];
-      const int id = (int)e.x;
-      const float qv = exp2_fast(fmaf(__uint_as_float(e.y), s, -MSq)) * rZq;
-      float cv = 0.f;
-      if (id >= lo && id < lo + len) {
-        const float pv = exp2_fast(fmaf(Tr<ET>::load1(trow + id), s, -MSt)) * rZt;
-        cv = fminf(pv, qv);
-      }
-      corr[j] = cv;
-      kid[j] = id;
-      kq[j] = qv;
-    }
-#pragma unroll
-    for (int j = 0; j < NV_TILE; ++j) {
-      float w0 = 0.f, w1 = 0.f;
-#pragma unroll
-      for (int k = 0; k < VEC; k += 2) {
-        w0 += exp2_fast(fmaf(Tr<ET>::at(rt[j], k), s, -MSt)) * rZt;
-        w1 += exp2_fast(fmaf(Tr<ET>::at(rt[j], k + 1), s, -MSt)) * rZt;
-      }
-      const float v = wave_sum(w0 + w1);
-      if (lane == 0) shsub[j * NWAVE + wave] = v;
-    }
-    __syncthreads();
-    if (t < NSUB) {
-      // Sub-block t holds the ids lo + [t, t+1) * 64 * VEC: a contiguous run
-      // of the sorted kept list, summed in list order.
-      auto lower = [&](int x) {
-        int l0 = 0, h0 = nkept;
-        while (l0 < h0) {
-          const int mid = (l0 + h0) >> 1;
-          if (kid[mid] < x) l0 = mid + 1; else h0 = mid;
+    for (int c = j0; c < C; c += G) {
+      const int lo = c * a.CS;
+      const int len = min(a.CS, a.V - lo);
+      u32x4 rt[NV_TILE];
+      load_tile<ET, ALIGNED, NV_TILE>(trow, lo, len, rt);
+      if (c == j0) {
+        for (int jj = t; jj < nkept; jj += WG) {
+          const uint2 e = jj == t ? e0 : kept[jj];
+          kid[jj] = (int)e.x;
+          kq[jj] = exp2_fast(fmaf(__uint_as_float(e.y), s, -MSq)) * rZq;
         }
-        return l0;
-      };
-      const int j0 = lower(lo + t * 64 * VEC), j1 = lower(lo + (t + 1) * 64 * VEC);
-      float cs = 0.f;
-      for (int j = j0; j < j1; ++j) cs += corr[j];
-      shsub[t] = fmaxf(0.f, shsub[t] - cs);
+        __syncthreads();
+      }
+      // Correction min(p, q~) of each kept id in this chunk (0 elsewhere).
+      for (int jj = t; jj < nkept; jj += WG) {
+        const int id = kid[jj];
+        float cv = 0.f;
+        if (id >= lo && id < lo + len) {
+          const float pv = exp2_fast(fmaf(Tr<ET>::load1(trow + id), s, -MSt)) * rZt;
+          cv = fminf(pv, kq[jj]);
+        }
+        kcorr[jj] = cv;
+      }
+#pragma unroll
+      for (int jv = 0; jv < NV_TILE; ++jv) {
+        float w0 = 0.f, w1 = 0.f;
+#pragma unroll
+        for (int k = 0; k < VEC; k += 2) {
+          w0 += exp2_fast(fmaf(Tr<ET>::at(rt[jv], k), s, -MSt)) * rZt;
+          w1 += exp2_fast(fmaf(Tr<ET>::at(rt[jv], k + 1), s, -MSt)) * rZt;
+        }
+        const float v = wave_sum(w0 + w1);
+        if (lane == 0) shsub[jv * NWAVE + wave] = v;
+      }
+      __syncthreads();
+      if (t < NSUB) {
+        // Sub-block t holds the ids lo + [t, t+1) * 64 * VEC: a contiguous
+        // run of the sorted kept list, summed in list order.
+        auto lower = [&](int x) {
+          int l0 = 0, h0 = nkept;
+          while (l0 < h0) {
+            const int mid = (l0 + h0) >> 1;
+            if (kid[mid] < x) l0 = mid + 1; else h0 = mid;
+          }
+          return l0;
+        };
+        const int i0 = lower(lo + t * 64 * VEC), i1 = lower(lo + (t + 1) * 64 * VEC);
+        float cs = 0.f;
+        for (int i = i0; i < i1; ++i) cs += kcorr[i];
+        pub_f32(subR_row + (size_t)c * NSUB + t, fmaxf(0.f, shsub[t] - cs));
+      }
+      __syncthreads();  // shsub and kcorr are reused by the next chunk
     }
-    __syncthreads();
   } else {
     MSq = mul_rn(rs.M[K + 1 + n], s);
     rZq = 1.f / rs.Z[K + 1 + n];
-    u32x4 rt[NV_TILE], rq[NV_TILE];
-    load_tile<ET, ALIGNED, NV_TILE>(target_row<ET>(a, b, n), lo, len, rt);
-    load_tile<ET, ALIGNED, NV_TILE>(draft_row<ET>(a, b, n), lo, len, rq);
+    for (int c = j0; c < C; c += G) {
+      const int lo = c * a.CS;
+      const int len = min(a.CS, a.V - lo);
+      u32x4 rt[NV_TILE], rq[NV_TILE];
+      load_tile<ET, ALIGNED, NV_TILE>(target_row<ET>(a, b, n), lo, len, rt);
+      load_tile<ET, ALIGNED, NV_TILE>(draft_row<ET>(a, b, n), lo, len, rq);
 #pragma unroll
-    for (int j = 0; j < NV_TILE; ++j) {
-      float w0 = 0.f, w1 = 0.f;
+      for (int jv = 0; jv < NV_TILE; ++jv) {
+        float w0 = 0.f, w1 = 0.f;
 #pragma unroll
-      for (int k = 0; k < VEC; k += 2) {
-        const float p0 = exp2_fast(fmaf(Tr<ET>::at(rt[j], k), s, -MSt)) * rZt;
-        const float q0 = exp2_fast(fmaf(Tr<ET>::at(rq[j], k), s, -MSq)) * rZq;
-        const float p1 = exp2_fast(fmaf(Tr<ET>::at(rt[j], k + 1), s, -MSt)) * rZt;
-        const float q1 = exp2_fast(fmaf(Tr<ET>::at(rq[j], k + 1), s, -MSq)) * rZq;
-        w0 += fmaxf(0.f, p0 - q0);
-        w1 += fmaxf(0.f, p1 - q1);
+        for (int k = 0; k < VEC; k += 2) {
+          const float p0 = exp2_fast(fmaf(Tr<ET>::at(rt[jv], k), s, -MSt)) * rZt;
+          const float q0 = exp2_fast(fmaf(Tr<ET>::at(rq[jv], k), s, -MSq)) * rZq;
+          const float p1 = exp2_fast(fmaf(Tr<ET>::at(rt[jv], k + 1), s, -MSt)) * rZt;
+          const float q1 = exp2_fast(fmaf(Tr<ET>::at(rq[jv], k + 1), s, -MSq)) * rZq;
+          w0 += fmaxf(0.f, p0 - q0);
+          w1 += fmaxf(0.f, p1 - q1);
+        }
+        const float v = wave_sum(w0 + w1);
+        if (lane == 0) shsub[jv * NWAVE + wave] = v;
       }
-      const float v = wave_sum(w0 + w1);
-      if (lane == 0) shsub[j * NWAVE + wave] = v;
+      __syncthreads();
+      if (t < NSUB) pub_f32(subR_row + (size_t)c * NSUB + t, shsub[t]);
+      __syncthreads();  // shsub is reused by the next chunk
     }
-    __syncthreads();
   }
-  uint32_t* subR_row = a.subR + (size_t)b * C * NSUB;
-  if (t < NSUB) pub_f32(subR_row + (size_t)c * NSUB + t, shsub[t]);
   // Count this work-group.  Its sums need no ordering with the count: the
   // last work-group polls them until they are published (each of its peers
   // has already issued its stores, so the wait ends).
   if (t == 0)
     sh_last = __hip_atomic_fetch_add(a.cnt + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-              (unsigned)C - 1u;
+              (unsigned)G - 1u;
   __syncthreads();
   if (!sh_last) return;
   const bool ok = wait_words(subR_row, C * NSUB, cache_sub, nullptr, 0, nullptr, wall_clock64() + WAIT_TICKS);
@@ -1764,6 +1852,36 @@ int launch(F kernel, int grid, size_t lds, hipStream_t st, hipEvent_t* ev2, cons
   return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
+// Work-groups of `kernel` (WG threads, `lds` bytes of dynamic LDS) that the
+// current device holds at once, or 0 if unknown; remembered per device,
+// kernel and LDS size.
+int resident_groups(const void* kernel, size_t lds) {
+  struct Entry {
+    int dev;
+    const void* kernel;
+    size_t lds;
+    int groups;
+  };
+  constexpr int N = 64;
+  static Entry seen[N];
+  static int used = 0;
+  static std::mutex mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  for (int i = 0; i < used; ++i)
+    if (seen[i].dev == dev && seen[i].kernel == kernel && seen[i].lds == lds) return seen[i].groups;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, WG, lds) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  const int groups = cus * per_cu;
+  if (used < N) seen[used++] = Entry{dev, kernel, lds, groups};
+  return groups;
+}
+
 template <typename ET, bool AL>
 int launch_typed(const Args& a, size_t lds, size_t merge_lds, hipStream_t st, hipEvent_t* ev) {
   int rc = a.kl ? launch(paired_kernel<ET, AL>, a.B * (a.K + 1) * a.C, 0, st, ev, a)
@@ -1776,9 +1894,10 @@ int launch_typed(const Args& a, size_t lds, size_t merge_lds, hipStream_t st, hi
   } else if (ev) {
     if (hipEventRecord(ev[2], st) != hipSuccess || hipEventRecord(ev[3], st) != hipSuccess) return SV_ERR_HIP;
   }
-  if (a.cache)
-    return launch(finish_kernel<ET, AL, true>, a.B * a.C, lds, st, ev ? ev + 4 : nullptr, a);
-  return launch(finish_kernel<ET, AL, false>, a.B * a.C, lds, st, ev ? ev + 4 : nullptr, a);
+  void (*const fk)(Args) = a.cache ? finish_kernel<ET, AL, true> : finish_kernel<ET, AL, false>;
+  Args af = a;
+  af.resident = resident_groups(reinterpret_cast<const void*>(fk), lds);
+  return launch(fk, a.B * a.C, lds, st, ev ? ev + 4 : nullptr, af);
 }
 
 struct RelaxedRule {
@@ -1818,6 +1937,7 @@ int run(const void* tgt, const void* dft, const int32_t* tok, const float* uni, 
   a.subR = reinterpret_cast<uint32_t*>(base + pl.off_subR);
   a.B = B; a.K = K; a.V = V; a.C = pl.C; a.CS = pl.CS; a.topk = topk;
   a.GA = (2 * K + 1) * pl.C;
+  a.resident = 0;
   a.cache = pl.cache ? 1 : 0;
   a.kl = kl;
   a.relaxed = rule ? 1 : 0;
@@ -1847,7 +1967,7 @@ constexpr int EE_MAX_LDS_WORDS = 14336;  // the early-exit kernel's dynamic LDS 
 struct EEPlan {
   int C = 0, CS = 0;
   size_t off_cnt = 0, off_part = 0, off_subK = 0, off_subR = 0, total = 0;
-  size_t off_cand = 0, off_ccnt = 0, off_mclaim = 0, off_mres = 0;
+  size_t off_cand = 0, off_ccnt = 0, off_qstat = 0, off_kept = 0;
   size_t lds_bytes = 0;
 };
 
@@ -1856,14 +1976,15 @@ int make_ee_plan(int B, int K, int V, int dtype, int topk, EEPlan& pl) {
   if (K > SV_MAX_K || topk > SV_MAX_TOPK) return SV_ERR_UNSUPPORTED;
   int C, CS;
   if (!vocab_split(V, dtype, C, CS)) return SV_ERR_UNSUPPORTED;
-  if ((long long)B * C > INT_MAX) return SV_ERR_UNSUPPORTED;
+  if ((long long)B * (K + 1) * C > INT_MAX) return SV_ERR_UNSUPPORTED;
   const size_t S = 2 * (size_t)K + 1;
-  const size_t words = S * C * 4 + (size_t)C * NSUB + (topk > 0 ? (size_t)C * NWAVE + 4 * (size_t)topk : 0);
+  const size_t words = S * C * 4 + (size_t)C * NSUB + 4 * (size_t)topk;
   if (words > (size_t)EE_MAX_LDS_WORDS) return SV_ERR_UNSUPPORTED;
   pl.C = C;
   pl.CS = CS;
-  // Every region is zero between calls: the kernel publishes into them and
-  // clears what it used.
+  // The counters, partial words and sums are zero between calls: the kernel
+  // publishes into them and clears what it used.  The candidate lists and
+  // selections of a truncated draft are plain, written before they are read.
   size_t off = 0;
   pl.off_cnt = off;  // claim [B], then leave [B]
   off = align256(off + 2 * sizeof(unsigned) * (size_t)B);
@@ -1874,29 +1995,39 @@ int make_ee_plan(int B, int K, int V, int dtype, int topk, EEPlan& pl) {
   pl.off_subR = off;
   off = align256(off + sizeof(uint32_t) * (size_t)B * C * NSUB);
   if (topk > 0) {
-    // Published candidate lists and counts (zero between calls).
     const size_t slots = (size_t)B * K;
     pl.off_cand = off;
     off = align256(off + sizeof(uint64_t) * slots * C * NWAVE * WCAP);
     pl.off_ccnt = off;
     off = align256(off + sizeof(int) * slots * C * NWAVE);
-    // The selection of each position: made by the first work-group of the
-    // row to reach it and published for the others.
-    pl.off_mclaim = off;
-    off = align256(off + sizeof(unsigned) * slots);
-    pl.off_mres = off;
-    off = align256(off + sizeof(uint32_t) * slots * (4 + 2 * (size_t)topk));
+    pl.off_qstat = off;
+    off = align256(off + sizeof(float4) * slots);
+    pl.off_kept = off;
+    off = align256(off + sizeof(uint2) * slots * topk);
   }
   pl.total = off;
   pl.lds_bytes = words * sizeof(uint32_t);
   return SV_OK;
 }
 
+// A truncated draft: position 0's statistics and the drafts' candidate
+// lists, the selections, then the walk.  A dense draft: the walk alone.
+template <typename ET, bool AL>
+int launch_early_exit(const Args& a, size_t lds, hipStream_t st) {
+  if (a.topk > 0) {
+    int rc = launch(ee_first_kernel<ET, AL, STATS_WAVES_TOPK>, a.B * (a.K + 1) * a.C, 0, st, nullptr, a);
+    if (rc == SV_OK) rc = launch(merge_kernel<ET>, a.B * a.K, 0, st, nullptr, a);
+    if (rc != SV_OK) return rc;
+    return launch(early_exit_kernel<ET, AL, true>, a.B * a.C, lds, st, nullptr, a);
+  }
+  return launch(early_exit_kernel<ET, AL, false>, a.B * a.C, lds, st, nullptr, a);
+}
+
 int run_early_exit(const void* tgt, const void* dft, const int32_t* tok, const float* uni, const float* temp,
                    int B, int K, int V, int topk, int dtype, int32_t* out, int32_t* nacc, void* ws,
                    size_t* ws_bytes, hipStream_t st, float* probs, float* mass) {
   if (!ws_bytes || topk < 0) return SV_ERR_ARG;
-  if (topk >= V) topk = 0;
+  if (topk >= V || K == 0) topk = 0;  // no draft to truncate
   EEPlan pl;
   const int rc = make_ee_plan(B, K, V, dtype, topk, pl);
   if (rc != SV_OK) return rc;
@@ -1919,20 +2050,18 @@ int run_early_exit(const void* tgt, const void* dft, const int32_t* tok, const f
   a.subR = reinterpret_cast<uint32_t*>(base + pl.off_subR);
   a.cand = topk > 0 ? static_cast<void*>(base + pl.off_cand) : nullptr;
   a.ccnt = topk > 0 ? reinterpret_cast<int*>(base + pl.off_ccnt) : nullptr;
-  a.mclaim = topk > 0 ? reinterpret_cast<unsigned*>(base + pl.off_mclaim) : nullptr;
-  a.mres = topk > 0 ? reinterpret_cast<uint32_t*>(base + pl.off_mres) : nullptr;
+  a.qstat = topk > 0 ? reinterpret_cast<float4*>(base + pl.off_qstat) : nullptr;
+  a.kept = topk > 0 ? reinterpret_cast<uint2*>(base + pl.off_kept) : nullptr;
   a.B = B; a.K = K; a.V = V; a.C = pl.C; a.CS = pl.CS; a.topk = topk;
   const size_t esz = dtype == SV_BF16 ? 2 : 4;
   const bool aligned = (reinterpret_cast<uintptr_t>(tgt) % 16 == 0) &&
                        (K == 0 || reinterpret_cast<uintptr_t>(dft) % 16 == 0) && ((size_t)V * esz) % 16 == 0;
   (void)hipGetLastError();
-  // Indexed by [bf16][aligned][truncated draft].
-  void (*const kernels[2][2][2])(Args) = {
-      {{early_exit_kernel<float, false, false>, early_exit_kernel<float, false, true>},
-       {early_exit_kernel<float, true, false>, early_exit_kernel<float, true, true>}},
-      {{early_exit_kernel<uint16_t, false, false>, early_exit_kernel<uint16_t, false, true>},
-       {early_exit_kernel<uint16_t, true, false>, early_exit_kernel<uint16_t, true, true>}}};
-  return launch(kernels[dtype == SV_BF16][aligned][topk > 0], B * pl.C, pl.lds_bytes, st, nullptr, a);
+  if (dtype == SV_BF16)
+    return aligned ? launch_early_exit<uint16_t, true>(a, pl.lds_bytes, st)
+                   : launch_early_exit<uint16_t, false>(a, pl.lds_bytes, st);
+  return aligned ? launch_early_exit<float, true>(a, pl.lds_bytes, st)
+                 : launch_early_exit<float, false>(a, pl.lds_bytes, st);
 }
 
 // ---- draft trees ------------------------------------------------------------

@@ -211,9 +211,11 @@ def test_early_exit_argument_errors_without_launch():
     assert call(dtype=5) == B.SV_ERR_ARG
     assert call(topk=-2) == B.SV_ERR_ARG
     assert call(topk=B.SV_MAX_TOPK + 1, V=5000, n=1 << 40) == B.SV_ERR_UNSUPPORTED
-    # a truncated draft needs room for its published candidate lists
+    # a truncated draft needs room for its candidate lists and selections;
+    # without drafts (K = 0) there is nothing to truncate
     sparse = B.early_exit_workspace_bytes(4, 3, 5000, B.SV_BF16, 10)
     assert sparse > B.early_exit_workspace_bytes(4, 3, 5000, B.SV_BF16) and sparse % 256 == 0
+    assert B.early_exit_workspace_bytes(4, 0, 5000, B.SV_BF16, 10) == B.early_exit_workspace_bytes(4, 0, 5000, B.SV_BF16)
     assert call(topk=10, V=5000, n=sparse - 1) == B.SV_ERR_WORKSPACE
     assert call(topk=1000, ws=0) == B.SV_OK               # topk >= V is dense (size query only)
     assert B.early_exit_workspace_bytes(4, 3, 1000, B.SV_BF16, 1000) == need

@@ -113,5 +113,5 @@ def test_graph_replays_equal_eager_calls(name):
         want = [t.cpu().numpy() for t in e_outs]
         for a, b in zip(got, want):
             np.testing.assert_array_equal(a, b, err_msg=f"{name}: replay over input set {i}")
-        if kind == "early":  # its workspace is all zero between calls (the others keep plain data)
+        if kind == "early" and topk == 0:  # all zero between calls (the others keep plain data)
             assert int(g_ws.count_nonzero().item()) == 0, "graph workspace left dirty"
