@@ -76,7 +76,7 @@ constexpr int NSUB = NV_TILE * NWAVE;      // sub-blocks per chunk (one wave x o
 constexpr int MAX_C = 2048;                // vocabulary chunks per position
 constexpr int MAX_SLOTS = 2 * SV_MAX_K + 1;
 constexpr int MAX_CACHE_WORDS = 8192;       // dynamic LDS for a row's published words (32 KiB)
-constexpr int TOPK_FAST_MAX = WG;          // sparse drafts: fast chunk selection for k <= 256
+constexpr int TOPK_FAST_MAX = 512;         // sparse drafts: fast chunk selection for k <= 512
 constexpr int WCAP = 256;                  // candidate list length per wave of a chunk
 // Longest wait for another work-group's results: 100 ms of the 100 MHz
 // constant clock.  Every wait ends well before that in a correct launch; the
@@ -260,11 +260,16 @@ __device__ void topk_chunk_exact(const u32x4 (&r)[NV_TILE], int lo, int len, int
       }
     return (int)block_sum((float)n, red);  // exact: counts are below 2^24
   };
+  // The largest key tau with at least kk logits at or above it: the kk-th
+  // largest key.  A bf16 logit's key has the low 16 bits all zero (positive)
+  // or all one (negative), so only the upper 16 bits are searched.
+  constexpr int LOW = Tr<ET>::VEC == 8 ? 16 : 0;
   uint32_t tau = 0;
-  for (int bit = 31; bit >= 0; --bit) {
+  for (int bit = 31; bit >= LOW; --bit) {
     const uint32_t cand = tau | (1u << bit);
     if (count_keys(cand, false) >= kk) tau = cand;
   }
+  if (LOW) tau |= (tau & 0x80000000u) ? 0u : 0xFFFFu;
   // Logits above tau, then the first ties, each in id order (places by
   // block scans, so that the lists -- and every sum over them -- do not
   // depend on timing).
@@ -310,17 +315,18 @@ __device__ void topk_chunk_exact(const u32x4 (&r)[NV_TILE], int lo, int len, int
 
 // Chunk candidates, written to the chunk's candidate area as four lists (one
 // per wave) of at most WCAP composites each, with their lengths in cnts[4].
-// Fast path (k <= 256): in each wave, a lower bound of the ceil(k/4)-th
-// largest of its 64 per-thread maxima is found by a ballot binary search on
-// the upper 16 bits of their order keys; the smallest of the four bounds is
-// a lower bound of the chunk's k-th largest logit (each wave has ceil(k/4)
-// logits at or above it), so every logit of the chunk's top k passes it.
+// Fast path (k <= 512): in each wave, a lower bound of the ceil(k/4)-th
+// largest of its 512 vector maxima (VEC logits each) is found by a ballot
+// binary search on the upper 16 bits of their order keys; each of those
+// vectors holds a distinct logit at or above it, so the smallest of the four
+// bounds is a lower bound of the chunk's k-th largest logit, and every logit
+// of the chunk's top k passes it.
 // Each wave lists the logits that pass: the vectors whose maximum passes
 // (few: about one in ten) are compacted into LDS in vector order, then each
 // lane tests the eight logits of one of them, so the per-logit work is spent
 // on those vectors only; a wave with more than VCAP such vectors marks its
 // logits one by one instead.  The lists are unsorted; the merge kernel
-// selects exactly.  Exact path (k > 256, or a list over WCAP): the chunk's
+// selects exactly.  Exact path (k > 512, or a list over WCAP): the chunk's
 // exact top min(k, len) is stored contiguously across the four list areas.
 constexpr int VCAP = 128;  // passing vectors a wave compacts
 
@@ -369,17 +375,20 @@ __device__ void topk_chunk(const u32x4 (&r)[NV_TILE], int lo, int len, int k, ty
   bool done = false;
   if (k <= TOPK_FAST_MAX) {
     float vm[NV_TILE];  // the thread's vector maxima (padding reads as -inf)
+    uint32_t vk[NV_TILE];  // and the upper 16 bits of their order keys
 #pragma unroll
-    for (int j = 0; j < NV_TILE; ++j) vm[j] = vec_max<ET>(r[j]);
-    float tm = max3_raw(vm[0], vm[1], vm[2]);
-#pragma unroll
-    for (int j = 3; j < NV_TILE; j += 2) tm = max3_raw(tm, vm[j], vm[j + 1 < NV_TILE ? j + 1 : j]);
-    const uint32_t key = order_key(tm) >> 16;
-    const int m = (k + NWAVE - 1) / NWAVE;
+    for (int j = 0; j < NV_TILE; ++j) {
+      vm[j] = vec_max<ET>(r[j]);
+      vk[j] = order_key(vm[j]) >> 16;
+    }
+    const int m = (k + NWAVE - 1) / NWAVE;  // at most 128 of the wave's 512 vectors
     uint32_t pre = 0;
     for (int bit = 15; bit >= 0; --bit) {
       const uint32_t cand = pre | (1u << bit);
-      if (__popcll(__ballot(key >= cand)) >= m) pre = cand;
+      int cnt = 0;
+#pragma unroll
+      for (int j = 0; j < NV_TILE; ++j) cnt += __popcll(__ballot(vk[j] >= cand));
+      if (cnt >= m) pre = cand;
     }
     if (lane == 0) wkey[wave] = pre << 16;
     if (t == 0) s_over = 0;

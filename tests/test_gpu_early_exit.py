@@ -132,7 +132,8 @@ SPARSE = {
     "top128": _case(B=8, topk=128, seed=50),
     "top1": _case(topk=1, seed=51),
     "top3-ragged": _case(V=40001, topk=3, seed=52),
-    "top300-exact-path": _case(topk=300, seed=53),
+    "top300-wide-fast-path": _case(topk=300, seed=53),
+    "top600-exact-path": _case(B=4, topk=600, seed=81),
     "top1024-exact-path": _case(B=3, topk=1024, seed=54),
     "f32-top64": _case(dtype=W.F32, V=20001, topk=64, seed=55),
     "mixed-greedy-top128": _case(B=10, greedy_rows=4, topk=128, seed=56),
@@ -175,11 +176,11 @@ def test_sparse_workspace_is_reused_within_a_shape():
     selection overflowed into the exact path), and the candidate lists and
     selections are rewritten by every call.  Another shape starts from a
     zero-filled workspace, as the header asks."""
-    groups = [[_case(B=8, K=4, draft_sigma=2.0, topk=300, seed=61),
-               _case(B=8, K=4, draft_sigma=0.3, topk=300, seed=62)],
+    groups = [[_case(B=8, K=4, draft_sigma=2.0, topk=600, seed=61),
+               _case(B=8, K=4, draft_sigma=0.3, topk=600, seed=62)],
               [_case(B=5, K=2, V=30000, topk=8, seed=63),
                _case(B=5, K=2, V=30000, draft_sigma=0.2, topk=8, seed=64)]]
-    ws = new_early_exit_workspace(8, 4, 40000, SV_BF16, topk_draft=300)
+    ws = new_early_exit_workspace(8, 4, 40000, SV_BF16, topk_draft=600)
     for group in groups:
         ws.zero_()
         for case in group + group[:1]:

@@ -84,7 +84,8 @@ CASES = {
                                 parents=FAN_4x2, topk=3, seed=103),
     "top128-61-node-tree": _case(B=4, V=17000, parents=W.TREE_60_DEPTH8, temperature=0.7, topk=128, seed=104),
     "top128-wide-low-agreement": _case(V=9000, draft_sigma=3.0, parents=WIDE_8, topk=128, seed=105),
-    "top300-exact-path-random": _case(V=20001, parents=None, nodes=10, topk=300, seed=106),
+    "top300-random": _case(V=20001, parents=None, nodes=10, topk=300, seed=106),
+    "top600-exact-path-random": _case(V=20001, parents=None, nodes=10, topk=600, seed=111),
     "top128-mixed-greedy": _case(B=10, V=30000, parents=None, nodes=16, greedy_rows=4, topk=128, seed=107),
     # the largest trees (SV_MAX_NODES = 64)
     "64-node-random": _case(B=4, V=5000, parents=None, nodes=64, seed=108),
