@@ -64,6 +64,9 @@ SMALL = {
     "K64-mixed-greedy": _case(B=4, K=64, V=4000, greedy_rows=2, draft_sigma=0.02, seed=74),
     "V1M-ragged-unaligned": _case(B=2, K=2, V=(1 << 20) + 3, seed=72),
     "V1M-top128": _case(B=2, K=2, V=1 << 20, topk=128, seed=75),
+    # a row whose partials do not fit the finishing kernel's LDS (129 slots x
+    # 17 chunks): the finishing work-groups read them from global memory
+    "K64-uncached-row": _case(B=3, K=64, V=262149, greedy_rows=1, draft_sigma=0.02, seed=76),
 }
 
 
