@@ -1,6 +1,6 @@
 """The GPU parity checkers themselves, exercised on the CPU.
 
-The checkers in tests/parity.py and tests/test_gpu_tree.py decide what
+The checkers in tests/parity.py decide what
 "matches the oracle" means.  Here they are fed outputs built from the oracle
 (no GPU): correct outputs must pass, outputs that take the other side of a
 decision within rounding distance of its threshold must pass, and outputs
