@@ -10,8 +10,9 @@
 //     diterima" (nalar.dev): batched verification of all draft positions from
 //     one target pass, greedy vs sampling semantics, first-rejection cut.
 //
-// Two launches per call, both on the caller's stream; no work-group ever
-// waits for another one that may not have started.
+// Two launches per call (three with a truncated draft), all on the caller's
+// stream; no work-group ever waits for another one that may not have
+// started.
 //
 //   A. stats_kernel, one work-group per (row, position, vocabulary chunk).
 //      Streams its chunk of target or draft logits once from HBM (16-byte
@@ -19,19 +20,20 @@
 //      exp2((l - max) * log2(e)/T) -- or, for greedy rows, the chunk argmax.
 //      The chunk holding a position's draft token records that token's
 //      logit; the bonus position also writes 32 sub-block sums for the final
-//      draw.
-//   B. finish_kernel, one work-group per (row, chunk).  Each work-group
-//      loads its row's partials into LDS in one round of loads, merges them
-//      and runs the first-rejection scan.  Greedy rows and rows that accepted
-//      every draft are completed by the row's work-group 0.  For a rejected
-//      row every work-group re-reads target and draft logits of the rejected
-//      position in its chunk and publishes 32 sub-block sums of
-//      max(0, p_n - q_n); the last work-group of the row to arrive (atomic
-//      counter) draws the correction token.
+//      draw.  A truncated draft's chunks write candidate lists instead, and
+//      merge_kernel (one work-group per (row, position)) selects exactly.
+//   B. finish_kernel, up to C work-groups per row.  Each loads its row's
+//      partials into LDS in one round of loads, merges them and runs the
+//      first-rejection scan.  Greedy rows and rows that accepted every draft
+//      are completed by the row's work-group 0.  For a rejected row, the
+//      row's first G work-groups re-read target and draft logits of the
+//      rejected position, chunk j, j + G, ... each, and publish 32 sub-block
+//      sums of max(0, p_n - q_n) per chunk; the last of them to arrive
+//      (atomic counter) draws the correction token.
 //
 // The final draw is an inverse CDF over a three-level hierarchy: chunk
-// masses (block scan), the 32 sub-block sums of the selected chunk, and a
-// block prefix sum over the 512 (bf16) or 256 (fp32) ids of the selected
+// masses (a wave scan), the 32 sub-block sums of the selected chunk, and a
+// wave prefix sum over the 512 (bf16) or 256 (fp32) ids of the selected
 // sub-block.
 //
 // Numerical conventions.  With s = log2(e)/T and MS = fl(M*s) for a max M,
