@@ -99,8 +99,8 @@ struct Args {
   uint32_t* subK;            // [B, C, NSUB] published bonus-position sub-block sums (vs chunk max)
   uint32_t* subR;            // [B, C, NSUB] published residual sub-block sums
   unsigned* cnt;             // [B] finishing work-groups that have arrived
-  void* cand;                // [B, K, C, NWAVE, WCAP] chunk candidate lists of sparse drafts (Cand<ET>::T)
-  int* ccnt;                 // [B, K, C, NWAVE] lengths of those lists
+  void* cand;                // [B, K, C, NWAVE * WCAP] chunk candidate lists of sparse drafts (Cand<ET>::T)
+  int* ccnt;                 // [B, K, C] lengths of those lists
   float4* qstat;             // [B, K] sparse draft: {max kept logit, Z_q, q(d_i), kept count}
   uint2* kept;               // [B, K, topk] sparse draft: kept (id, logit bits), ascending id
   int B, K, V, C, CS, topk;
@@ -315,20 +315,22 @@ __device__ void topk_chunk_exact(const u32x4 (&r)[NV_TILE], int lo, int len, int
   __syncthreads();
 }
 
-// Chunk candidates, written to the chunk's candidate area as four lists (one
-// per wave) of at most WCAP composites each, with their lengths in cnts[4].
+// Chunk candidates, written to the chunk's candidate area as one list of
+// composites, its length in *cnt.
 // Fast path (k <= 512): in each wave, a lower bound of the ceil(k/4)-th
 // largest of its 512 vector maxima (VEC logits each) is found by a ballot
 // binary search on the upper 16 bits of their order keys; each of those
 // vectors holds a distinct logit at or above it, so the smallest of the four
 // bounds is a lower bound of the chunk's k-th largest logit, and every logit
 // of the chunk's top k passes it.
-// Each wave lists the logits that pass: the vectors whose maximum passes
-// (few: about one in ten) are compacted into LDS in vector order, then each
-// lane tests the eight logits of one of them, so the per-logit work is spent
-// on those vectors only; a wave with more than VCAP such vectors marks its
-// logits one by one instead.  The lists are unsorted; the merge kernel
-// selects exactly.  Exact path (k > 512, or a list over WCAP): the chunk's
+// Each wave lists the logits that pass (at most WCAP): the vectors whose
+// maximum passes (a few percent) are compacted into LDS in vector order,
+// then each lane tests the logits of one of them, so the per-logit work is
+// spent on those vectors only; a wave with more than VCAP such vectors marks
+// its logits one by one instead.  The four waves' lists are written back to
+// back by the whole block, one contiguous run per chunk (four short runs
+// apart in memory cost the statistics pass about 10 us on a 256-row,
+// 8-draft batch).  The list is unsorted; the merge kernel selects exactly.  Exact path (k > 512, or a list over WCAP): the chunk's
 // exact top min(k, len) is stored contiguously across the four list areas.
 constexpr int VCAP = 128;  // passing vectors a wave compacts
 
@@ -361,7 +363,7 @@ __device__ __forceinline__ float vec_max(const u32x4& v) {
 
 template <typename ET>
 __device__ void topk_chunk(const u32x4 (&r)[NV_TILE], int lo, int len, int k, typename Cand<ET>::T* dst,
-                           int* cnts, float* red) {
+                           int* cnt, float* red) {
   constexpr int VEC = Tr<ET>::VEC;
   constexpr int NE = NV_TILE * VEC;  // logits per thread: 64 (bf16) or 32 (fp32)
   using CT = typename Cand<ET>::T;
@@ -371,6 +373,7 @@ __device__ void topk_chunk(const u32x4 (&r)[NV_TILE], int lo, int len, int k, ty
   __shared__ u32x4 vbuf[NWAVE * VCAP];      // the wave's passing vectors
   __shared__ uint16_t voff[NWAVE * VCAP];   // and their offsets in the chunk
   __shared__ uint32_t wkey[NWAVE];
+  __shared__ int s_wn[NWAVE];
   __shared__ int s_over;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int kk = min(k, len);
@@ -495,24 +498,28 @@ __device__ void topk_chunk(const u32x4 (&r)[NV_TILE], int lo, int len, int k, ty
       }
     }
     if (lane == 0) {
-      cnts[wave] = min(n, WCAP);
+      s_wn[wave] = n;
       if (n > WCAP) s_over = 1;
-    }
-    if (n <= WCAP) {
-      // The wave's list is complete: written at once, without waiting for
-      // the other waves (a chunk with an overflowing list is rewritten by
-      // the exact path below).  The merge kernel reads it once: streaming
-      // stores.
-      CT* wl = dst + wave * WCAP;
-      for (int q = lane; q < n; q += 64) cand_st(wl + q, Staged<ET>::composite_at(wl_stage[q], lo));
     }
     __syncthreads();
     done = s_over == 0;
+    if (done) {
+      // The chunk's list: the waves' lists back to back, written by the
+      // whole block (the merge kernel reads it once: streaming stores).
+      const int o1 = s_wn[0], o2 = o1 + s_wn[1], o3 = o2 + s_wn[2], tot = o3 + s_wn[3];
+      for (int q = t; q < tot; q += WG) {
+        const int w = (q >= o1) + (q >= o2) + (q >= o3);
+        const int from = w == 0 ? 0 : (w == 1 ? o1 : (w == 2 ? o2 : o3));
+        const ST* ws = reinterpret_cast<const ST*>(sbuf) + w * WCAP;
+        cand_st(dst + q, Staged<ET>::composite_at(ws[q - from], lo));
+      }
+      if (t == 0) *cnt = tot;
+    }
   }
   if (!done) {
-    __syncthreads();  // the fast path's lists are no longer read
+    __syncthreads();  // the fast path's staging is no longer read
     topk_chunk_exact<ET>(r, lo, len, kk, dst, red);
-    if (t < NWAVE) cnts[t] = max(0, min(WCAP, kk - t * WCAP));
+    if (t == 0) *cnt = kk;
   }
 }
 
@@ -578,7 +585,7 @@ __device__ __forceinline__ void stats_body(const Args& a, int b, int slot, int c
   if (is_draft && a.topk > 0) {
     const size_t chunk = ((size_t)b * a.K + pos) * a.C + c;
     topk_chunk<ET>(r, lo, len, a.topk, reinterpret_cast<typename Cand<ET>::T*>(a.cand) + chunk * NWAVE * WCAP,
-                   a.ccnt + chunk * NWAVE, shf);
+                   a.ccnt + chunk, shf);
     return;
   }
   const float m = block_max(tile_max<ET, NV_TILE>(r), shf);
@@ -1234,10 +1241,10 @@ constexpr int MERGE_REG = 12;     // lists per wave whose first 64 entries are h
 constexpr int MERGE_OVF = 480;    // list entries past the 64th, gathered into LDS (sized so that
                                   // eight merge work-groups fit a CU's LDS)
 
-// Candidates of one (row, position) held by the work-group: wave w holds
-// lists w, w + NWAVE, ... (one register per list, lane l holding entry l, as
-// written: list r of a wave holds chunk r); entries past the 64th of a list
-// are in an LDS overflow buffer as composites.
+// Candidates of one (row, position) held by the work-group: register r of
+// wave w holds entries [64 w, 64 w + 64) of chunk r's list (lane l holding
+// entry 64 w + l); entries past the 256th of a list are in an LDS overflow
+// buffer as composites.
 template <typename ET>
 struct RegCands {
   typename Cand<ET>::T v[MERGE_REG];
@@ -1253,20 +1260,20 @@ struct RegCands {
     for (int j = threadIdx.x; j < novf; j += WG) f(ovf[j]);
   }
 };
-// Candidates read from their lists in global memory (one wave per list;
-// list L holds chunk L / NWAVE).
+// Candidates read from their lists in global memory (wave w reads the lists
+// of chunks w, w + NWAVE, ...).
 template <typename ET>
 struct ListCands {
   const typename Cand<ET>::T* g;
   const int* gcnt;
-  int NL, CS;
+  int C, CS;
   template <typename F>
   __device__ __forceinline__ void each(F&& f) const {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int L = wave; L < NL; L += NWAVE) {
+    for (int L = wave; L < C; L += NWAVE) {
       const int n = *(gcnt + L);
       for (int j = lane; j < n; j += 64)
-        f(cand_composite<ET>(*(g + (size_t)L * WCAP + j), (L / NWAVE) * CS));
+        f(cand_composite<ET>(*(g + (size_t)L * NWAVE * WCAP + j), L * CS));
     }
   }
 };
@@ -1408,11 +1415,11 @@ __device__ __forceinline__ int merge_body(const Args& a, int b, int i, int d) {
   __shared__ uint32_t s_ld;
   const float T = a.temp[b];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int C = a.C, NL = C * NWAVE, kk = min(a.topk, a.V);
+  const int C = a.C, kk = min(a.topk, a.V);
   const size_t slot = (size_t)b * a.K + i;
   using CT = typename Cand<ET>::T;
-  const CT* g = reinterpret_cast<const CT*>(a.cand) + slot * NL * WCAP;
-  const int* gcnt = a.ccnt + slot * NL;
+  const CT* g = reinterpret_cast<const CT*>(a.cand) + slot * C * NWAVE * WCAP;  // chunk r's list at r * NWAVE * WCAP
+  const int* gcnt = a.ccnt + slot * C;
   const float s = LOG2E / T;
   if (t == 0) {
     s_n = 0;
@@ -1422,26 +1429,26 @@ __device__ __forceinline__ int merge_body(const Args& a, int b, int i, int d) {
   uint64_t thr;
   float m, z;
   if (C <= MERGE_REG) {
-    // One round of loads: the lengths of the wave's lists (lane r holds list
-    // wave + NWAVE * r) and the first 64 entries of each (read whole: a list
-    // area holds WCAP entries).
+    // One round of loads: the list lengths (lane r holds chunk r's) and a
+    // window of 64 entries of each list (wave w: entries [64 w, 64 w + 64),
+    // read whole: a list area holds NWAVE * WCAP entries).
+    constexpr int HELD = NWAVE * 64;  // entries of a list held in registers
     RegCands<ET> rc;
     rc.CS = a.CS;
-    const int my_cnt = lane < C ? *(gcnt + wave + NWAVE * lane) : 0;
+    const int my_cnt = lane < C ? *(gcnt + lane) : 0;
 #pragma unroll
     for (int r = 0; r < MERGE_REG; ++r)
-      rc.v[r] = r < C ? *(g + (size_t)(wave + NWAVE * r) * WCAP + lane) : CT(0);
+      rc.v[r] = r < C ? *(g + (size_t)r * NWAVE * WCAP + wave * 64 + lane) : CT(0);
     __syncthreads();  // s_n / s_novf / rank initialised
-    // Entries past the 64th go to the overflow buffer: one reservation per
-    // wave, then one round of loads for entries 64..127 (entries 128 and
-    // up, rarer still, one load at a time).
+    // Entries past the first HELD of a list go to the overflow buffer: wave
+    // w takes those of chunks w, w + NWAVE, ... (rare).
     rc.valid = 0u;
     int extra = 0;
 #pragma unroll
     for (int r = 0; r < MERGE_REG; ++r) {
       const int n = r < C ? __builtin_amdgcn_readlane(my_cnt, r) : 0;
-      if (lane < n) rc.valid |= 1u << r;
-      extra += max(0, n - 64);
+      if (wave * 64 + lane < n) rc.valid |= 1u << r;
+      if (r % NWAVE == wave) extra += max(0, n - HELD);
     }
     // Each wave's overflow entries go to a fixed place in the buffer (waves
     // in order), so that the order of the candidates -- and with it every
@@ -1456,21 +1463,13 @@ __device__ __forceinline__ int merge_body(const Args& a, int b, int i, int d) {
     }
     if (t == 0) s_novf = total;
     if (extra > 0) {  // wave-uniform
-      CT w2[MERGE_REG];
-#pragma unroll
-      for (int r = 0; r < MERGE_REG; ++r) {
-        const int n = r < C ? __builtin_amdgcn_readlane(my_cnt, r) : 0;
-        w2[r] = 64 + lane < n ? *(g + (size_t)(wave + NWAVE * r) * WCAP + 64 + lane) : CT(0);
-      }
       int o = base;
-#pragma unroll
-      for (int r = 0; r < MERGE_REG; ++r) {
-        const int n = r < C ? __builtin_amdgcn_readlane(my_cnt, r) : 0;
-        if (64 + lane < n && o + lane < MERGE_OVF) ovf[o + lane] = cand_composite<ET>(w2[r], r * a.CS);
-        for (int j = 128 + lane; j < n; j += 64)
-          if (o + j - 64 < MERGE_OVF)
-            ovf[o + j - 64] = cand_composite<ET>(*(g + (size_t)(wave + NWAVE * r) * WCAP + j), r * a.CS);
-        o += max(0, n - 64);
+      for (int r = __builtin_amdgcn_readfirstlane(wave); r < C; r += NWAVE) {
+        const int n = __builtin_amdgcn_readlane(my_cnt, r);
+        for (int j = HELD + lane; j < n; j += 64)
+          if (o + j - HELD < MERGE_OVF)
+            ovf[o + j - HELD] = cand_composite<ET>(*(g + (size_t)r * NWAVE * WCAP + j), r * a.CS);
+        o += max(0, n - HELD);
       }
     }
     __syncthreads();
@@ -1480,13 +1479,13 @@ __device__ __forceinline__ int merge_body(const Args& a, int b, int i, int d) {
       thr = select_threshold(rc, kk, sh32, red, ired, hist, &m);
       z = take_kept(rc, thr, d, s, mul_rn(m, s), sel, &s_n, &s_ld);
     } else {
-      const ListCands<ET> lc{g, gcnt, NL, a.CS};
+      const ListCands<ET> lc{g, gcnt, C, a.CS};
       thr = select_threshold(lc, kk, sh32, red, ired, hist, &m);
       z = take_kept(lc, thr, d, s, mul_rn(m, s), sel, &s_n, &s_ld);
     }
   } else {
     __syncthreads();
-    const ListCands<ET> lc{g, gcnt, NL, a.CS};
+    const ListCands<ET> lc{g, gcnt, C, a.CS};
     thr = select_threshold(lc, kk, sh32, red, ired, hist, &m);
     z = take_kept(lc, thr, d, s, mul_rn(m, s), sel, &s_n, &s_ld);
   }
@@ -1835,7 +1834,7 @@ int make_plan(int B, int K, int V, int topk, int dtype, Plan& pl) {
     pl.off_cand = off;
     off = align256(off + sizeof(uint64_t) * slots * C * NWAVE * WCAP);
     pl.off_ccnt = off;
-    off = align256(off + sizeof(int) * slots * C * NWAVE);
+    off = align256(off + sizeof(int) * slots * C);
     pl.off_qstat = off;
     off = align256(off + sizeof(float4) * slots);
     pl.off_kept = off;
@@ -2010,7 +2009,7 @@ int make_ee_plan(int B, int K, int V, int dtype, int topk, EEPlan& pl) {
     pl.off_cand = off;
     off = align256(off + sizeof(uint64_t) * slots * C * NWAVE * WCAP);
     pl.off_ccnt = off;
-    off = align256(off + sizeof(int) * slots * C * NWAVE);
+    off = align256(off + sizeof(int) * slots * C);
     pl.off_qstat = off;
     off = align256(off + sizeof(float4) * slots);
     pl.off_kept = off;
@@ -2115,7 +2114,7 @@ int make_tree_plan(int B, int N, int V, int dtype, int topk, TreePlan& pl) {
     pl.off_cand = off;
     off = align256(off + sizeof(uint64_t) * nodes * C * NWAVE * WCAP);
     pl.off_ccnt = off;
-    off = align256(off + sizeof(int) * nodes * C * NWAVE);
+    off = align256(off + sizeof(int) * nodes * C);
     pl.off_qstat = off;
     off = align256(off + sizeof(float4) * nodes);
     pl.off_kept = off;

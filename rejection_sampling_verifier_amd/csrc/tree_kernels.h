@@ -46,7 +46,7 @@ struct TreeArgs {
   // Sparse drafts (topk > 0): chunk candidate lists, then per node the kept
   // set (ascending id) and {max kept logit, Z_q, -, kept count}.
   void* cand;                // [B, N, C, NWAVE, WCAP]
-  int* ccnt;                 // [B, N, C, NWAVE]
+  int* ccnt;                 // [B, N, C]
   float4* qstat;             // [B, N]
   uint2* kept;               // [B, N, topk]
   int B, N, V, C, CS, topk;
@@ -76,7 +76,7 @@ __device__ __forceinline__ void tree_slot_stats(const TreeArgs& a, int b, int no
     // A truncated draft: the chunk's candidates for the node's top k.
     const size_t chunk = ((size_t)b * N + node) * a.C + c;
     topk_chunk<ET>(r, lo, len, a.topk, reinterpret_cast<typename Cand<ET>::T*>(a.cand) + chunk * NWAVE * WCAP,
-                   a.ccnt + chunk * NWAVE, shf);
+                   a.ccnt + chunk, shf);
     return;
   }
   uint32_t* dst = tree_part(a, b, is_draft ? N + node : node, c);
