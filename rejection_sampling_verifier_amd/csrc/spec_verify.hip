@@ -860,6 +860,54 @@ __device__ __forceinline__ RowIn load_row_in(const Args& a, int b) {
   return in;
 }
 
+// Merge of slots 0..nmerge of a row's chunk statistics: the row's max and
+// sum against it (the argmax for greedy rows) per slot, into rs.  One group of
+// G lanes per slot, lane g of the group holding chunks g, g + G, ... (G is
+// the smallest of 16, 32, 64 that holds C, else 64), so every result equals
+// the wave-wide merge of the slot's chunks bit for bit: the same operations
+// per lane, and the reduction steps that stay inside the group.
+template <int G, bool CACHED>
+__device__ __forceinline__ void merge_slots(const Args& a, int b, RowShared& rs, const RowView<CACHED>& v,
+                                            int nmerge, bool greedy, float s) {
+  constexpr int PER = 64 / G;
+  const int C = a.C, lane = threadIdx.x & 63, wave = threadIdx.x >> 6, gl = lane % G;
+  for (int base = wave * PER; base < nmerge; base += NWAVE * PER) {
+    const int slot = base + lane / G;
+    const bool need = slot < nmerge;
+    if (greedy) {
+      float bv = NEG_INF;
+      int bi = INT_MAX;
+      if (need)
+        for (int c = gl; c < C; c += G)
+          argmax_merge(bv, bi, view_part(a, v, b, slot, c, 0), __float_as_int(view_part(a, v, b, slot, c, 2)));
+      group_argmax<G>(bv, bi);
+      if (need && gl == G - 1) {
+        rs.M[slot] = bv;
+        rs.Z[slot] = 0.f;
+        rs.idx[slot] = bi;
+      }
+    } else {
+      float m = NEG_INF;
+      if (need)
+        for (int c = gl; c < C; c += G) m = fmaxf(m, view_part(a, v, b, slot, c, 0));
+      m = group_last<G>(group_max<G>(m));
+      const float MS = mul_rn(m, s);
+      float z = 0.f;
+      if (need)
+        for (int c = gl; c < C; c += G) {
+          const float mc = view_part(a, v, b, slot, c, 0), zc = view_part(a, v, b, slot, c, 1);
+          if (mc != NEG_INF) z += zc * exp2_fast(mul_rn(mc, s) - MS);
+        }
+      z = group_sum<G>(z);
+      if (need && gl == G - 1) {
+        rs.M[slot] = m;
+        rs.Z[slot] = z;
+        rs.idx[slot] = 0;
+      }
+    }
+  }
+}
+
 template <bool CACHED>
 __device__ __forceinline__ void decide_row(const Args& a, int b, RowShared& rs, const RowView<CACHED>& v,
                                            const RowIn& in) {
@@ -871,65 +919,11 @@ __device__ __forceinline__ void decide_row(const Args& a, int b, RowShared& rs, 
   const float u = in.u;
   if (t == K) rs.uK = u;
   const int nmerge = (greedy || a.topk > 0) ? K + 1 : 2 * K + 1;
-  // Each wave merges three slots at a time, so that their reduction chains
-  // overlap.
-  constexpr int U = 3;
-  for (int base = wave; base < nmerge; base += U * NWAVE) {
-    if (greedy) {
-      float bv[U];
-      int bi[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int slot = base + u * NWAVE;
-        bv[u] = NEG_INF;
-        bi[u] = INT_MAX;
-        if (slot < nmerge)
-          for (int c = lane; c < C; c += 64)
-            argmax_merge(bv[u], bi[u], view_part(a, v, b, slot, c, 0),
-                         __float_as_int(view_part(a, v, b, slot, c, 2)));
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) wave_argmax(bv[u], bi[u]);
-      if (lane == 0) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int slot = base + u * NWAVE;
-          if (slot < nmerge) { rs.M[slot] = bv[u]; rs.Z[slot] = 0.f; rs.idx[slot] = bi[u]; }
-        }
-      }
-    } else {
-      float m[U], z[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int slot = base + u * NWAVE;
-        m[u] = NEG_INF;
-        if (slot < nmerge)
-          for (int c = lane; c < C; c += 64) m[u] = fmaxf(m[u], view_part(a, v, b, slot, c, 0));
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) m[u] = wave_max(m[u]);
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int slot = base + u * NWAVE;
-        const float MS = mul_rn(m[u], s);
-        z[u] = 0.f;
-        if (slot < nmerge)
-          for (int c = lane; c < C; c += 64) {
-            const float mc = view_part(a, v, b, slot, c, 0), zc = view_part(a, v, b, slot, c, 1);
-            if (mc != NEG_INF) z[u] += zc * exp2_fast(mul_rn(mc, s) - MS);
-          }
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) z[u] = wave_sum(z[u]);
-      if (lane == 0) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int slot = base + u * NWAVE;
-          if (slot < nmerge) { rs.M[slot] = m[u]; rs.Z[slot] = z[u]; rs.idx[slot] = 0; }
-        }
-      }
-    }
-  }
+  // Groups of G lanes (the smallest of 16, 32, 64 that holds C) merge one
+  // slot each, so a wave merges 64 / G slots at once.
+  if (C <= 16) merge_slots<16>(a, b, rs, v, nmerge, greedy, s);
+  else if (C <= 32) merge_slots<32>(a, b, rs, v, nmerge, greedy, s);
+  else merge_slots<64>(a, b, rs, v, nmerge, greedy, s);
   __syncthreads();
   if (wave == 0) {
     // Acceptance test of every position at once ([RheoSampling] section 4

@@ -208,6 +208,47 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
   i = __builtin_amdgcn_readlane(i, 63);
 }
 
+// Reductions over groups of G = 16, 32 or 64 lanes of a wave, G a compile-time
+// constant.  They take the steps of wave_sum / wave_max / wave_argmax that
+// stay inside the group, so a group whose lanes past the data hold the
+// identity gives bit for bit what those reductions give over the wave.  The
+// group's result is in its last lane.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+  v += dpp_f<dpp::QUAD_1032>(0.f, v);
+  v += dpp_f<dpp::QUAD_2301>(0.f, v);
+  v += dpp_f<dpp::ROW_HALF_MIRROR>(0.f, v);
+  v += dpp_f<dpp::ROW_MIRROR>(0.f, v);
+  if (G >= 32) v += dpp_f<dpp::ROW_BCAST15, 0xA>(0.f, v);
+  if (G >= 64) v += dpp_f<dpp::ROW_BCAST31, 0xC>(0.f, v);
+  return v;
+}
+template <int G>
+__device__ __forceinline__ float group_max(float v) {
+  v = fmaxf(v, dpp_f<dpp::QUAD_1032>(NEG_INF, v));
+  v = fmaxf(v, dpp_f<dpp::QUAD_2301>(NEG_INF, v));
+  v = fmaxf(v, dpp_f<dpp::ROW_HALF_MIRROR>(NEG_INF, v));
+  v = fmaxf(v, dpp_f<dpp::ROW_MIRROR>(NEG_INF, v));
+  if (G >= 32) v = fmaxf(v, dpp_f<dpp::ROW_BCAST15, 0xA>(NEG_INF, v));
+  if (G >= 64) v = fmaxf(v, dpp_f<dpp::ROW_BCAST31, 0xC>(NEG_INF, v));
+  return v;
+}
+template <int G>
+__device__ __forceinline__ void group_argmax(float& v, int& i) {
+  argmax_step<dpp::QUAD_1032>(v, i);
+  argmax_step<dpp::QUAD_2301>(v, i);
+  argmax_step<dpp::ROW_HALF_MIRROR>(v, i);
+  argmax_step<dpp::ROW_MIRROR>(v, i);
+  if (G >= 32) argmax_step<dpp::ROW_BCAST15, 0xA>(v, i);
+  if (G >= 64) argmax_step<dpp::ROW_BCAST31, 0xC>(v, i);
+}
+// Broadcast of the group's last lane to the whole group.
+template <int G>
+__device__ __forceinline__ float group_last(float v) {
+  const int lane = threadIdx.x & 63;
+  return __shfl(v, (lane & ~(G - 1)) + G - 1, 64);
+}
+
 // max(a, b, c) issued directly.  The compiler's fmaxf first quiets possible
 // signaling NaNs in operands it cannot prove canonical (such as logits
 // widened from loaded bits); here only a NaN logit could be one, and a NaN
