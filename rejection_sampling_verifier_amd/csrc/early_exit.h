@@ -10,8 +10,8 @@
 // section 4).  The result equals spec_verify's bit for bit: every sum is
 // formed in the same order.
 //
-// One launch, one work-group per (row, chunk), numbered chunk-major.  A
-// row's work is cut into stages: stage i <= n computes the chunk statistics
+// The walk: one launch, one work-group per (row, chunk), numbered
+// chunk-major.  A row's work is cut into stages: stage i <= n computes the chunk statistics
 // of position i (target, and the draft of a sampling row); after a rejection
 // at n one more stage computes the residual sums of position n.  Each stage
 // is cut into tickets, one per chunk and slot, numbered consecutively across

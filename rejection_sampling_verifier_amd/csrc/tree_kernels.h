@@ -5,7 +5,8 @@
 //
 // Source: [RheoSampling] section 4 (RheoVerification).  A node's children are
 // candidate tokens drawn from the drafter's distribution q~ at the node; they
-// are tested in id order, the first with min(1, p/q~) at its token.  An
+// are tested in increasing node index, the first with min(1, p/q~) at its
+// token.  An
 // accepted child is descended into; after a rejection the target is replaced
 // by the residual norm(max(0, r - q~)) and the next child is tested against
 // it.  Every residual is r_j = max(0, p - c_j q) / W_j with c_0 = 0, W_0 = 1,
