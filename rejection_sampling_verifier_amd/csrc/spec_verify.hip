@@ -99,11 +99,13 @@ struct Args {
   uint32_t* subK;            // [B, C, NSUB] published bonus-position sub-block sums (vs chunk max)
   uint32_t* subR;            // [B, C, NSUB] published residual sub-block sums
   unsigned* cnt;             // [B] finishing work-groups that have arrived
-  void* cand;                // [B, K, C, NWAVE * WCAP] chunk candidate lists of sparse drafts (Cand<ET>::T)
-  int* ccnt;                 // [B, K, C] lengths of those lists
+  void* cand;                // [B, K, C, cstride] chunk candidate lists of sparse drafts (Cand<ET>::T)
+  int* ccnt;                 // [B, K, C, 2] their lengths and the order keys of their bounds (0: none)
   float4* qstat;             // [B, K] sparse draft: {max kept logit, Z_q, q(d_i), kept count}
   uint2* kept;               // [B, K, topk] sparse draft: kept (id, logit bits), ascending id
   int B, K, V, C, CS, topk;
+  int cstride;               // sparse drafts: candidate entries per chunk
+  int ckeep;                 // sparse drafts: logits a chunk lists at least
   // Relaxed (lossy) acceptance: 0 = the lossless rule.  With max_rank > 0 the
   // statistics kernel also counts, per target chunk, the logits above l(d_i).
   int relaxed, max_rank;
@@ -201,11 +203,16 @@ __device__ __forceinline__ float tile_max<float, NV_TILE>(const u32x4 (&r)[NV_TI
 }
 
 // ============================================================================
-// Sparse draft truncation ([RheoSampling] section 3): each chunk of a draft
-// position contributes its own min(k, len) best logits (larger value first,
-// then lower id); any logit of the position's global top k is among its
-// chunk's top k under the same order, so the union of the chunk lists holds
-// the global top k, which the merge kernel selects.
+// Sparse draft truncation ([RheoSampling] section 3).  The global top k of a
+// draft position takes about k / C logits from each of its C chunks, so a
+// chunk lists only its best logits down to a bound: every logit at or above
+// the bound, at least `keep` of them (keep = min(k, ceil(2k/C) + 16)).  With
+// the list goes the bound's order key, or 0 when the list holds the chunk's
+// whole top k (keep = k, the bound is -inf, or the exact path ran).  The
+// merge kernel selects the k-th largest of the union and checks that it is
+// at or above every chunk's bound: then every logit of the global top k is
+// listed.  Otherwise it selects again with the logits of the chunks whose
+// bound is higher read from the draft row itself.
 // ============================================================================
 // Chunk candidate as written by the statistics kernel: the composite of the
 // logit and its vocabulary id.
@@ -315,14 +322,15 @@ __device__ void topk_chunk_exact(const u32x4 (&r)[NV_TILE], int lo, int len, int
   __syncthreads();
 }
 
-// Chunk candidates, written to the chunk's candidate area as one list of
-// composites, its length in *cnt.
-// Fast path (k <= 512): in each wave, a lower bound of the ceil(k/4)-th
+// Chunk candidates, written to the chunk's candidate area (cap entries) as
+// one list of composites; cnt[0] gets its length and cnt[1] the order key of
+// the bound above which it is complete (0: it holds the chunk's top k).
+// Fast path (k <= 512): in each wave, a lower bound of the ceil(keep/4)-th
 // largest of its 512 vector maxima (VEC logits each) is found by a ballot
 // binary search on the upper 16 bits of their order keys; each of those
 // vectors holds a distinct logit at or above it, so the smallest of the four
-// bounds is a lower bound of the chunk's k-th largest logit, and every logit
-// of the chunk's top k passes it.
+// bounds is a lower bound of the chunk's keep-th largest logit: at least
+// keep logits pass it.
 // Each wave lists the logits that pass (at most WCAP): the vectors whose
 // maximum passes (a few percent) are compacted into LDS in vector order,
 // then each lane tests the logits of one of them, so the per-logit work is
@@ -330,8 +338,9 @@ __device__ void topk_chunk_exact(const u32x4 (&r)[NV_TILE], int lo, int len, int
 // its logits one by one instead.  The four waves' lists are written back to
 // back by the whole block, one contiguous run per chunk (four short runs
 // apart in memory cost the statistics pass about 10 us on a 256-row,
-// 8-draft batch).  The list is unsorted; the merge kernel selects exactly.  Exact path (k > 512, or a list over WCAP): the chunk's
-// exact top min(k, len) is stored contiguously across the four list areas.
+// 8-draft batch).  The list is unsorted; the merge kernel selects exactly.
+// Exact path (k > 512, a wave's list over WCAP or the chunk's over cap): the
+// chunk's exact top min(k, len).
 constexpr int VCAP = 128;  // passing vectors a wave compacts
 
 // The 32-bit word of a vector that holds element e (e < VEC), selected
@@ -362,8 +371,8 @@ __device__ __forceinline__ float vec_max(const u32x4& v) {
 }
 
 template <typename ET>
-__device__ void topk_chunk(const u32x4 (&r)[NV_TILE], int lo, int len, int k, typename Cand<ET>::T* dst,
-                           int* cnt, float* red) {
+__device__ void topk_chunk(const u32x4 (&r)[NV_TILE], int lo, int len, int k, int keep, int cap,
+                           typename Cand<ET>::T* dst, int* cnt, float* red) {
   constexpr int VEC = Tr<ET>::VEC;
   constexpr int NE = NV_TILE * VEC;  // logits per thread: 64 (bf16) or 32 (fp32)
   using CT = typename Cand<ET>::T;
@@ -386,7 +395,7 @@ __device__ void topk_chunk(const u32x4 (&r)[NV_TILE], int lo, int len, int k, ty
       vm[j] = vec_max<ET>(r[j]);
       vk[j] = order_key(vm[j]) >> 16;
     }
-    const int m = (k + NWAVE - 1) / NWAVE;  // at most 128 of the wave's 512 vectors
+    const int m = (keep + NWAVE - 1) / NWAVE;  // at most 128 of the wave's 512 vectors
     uint32_t pre = 0;
     for (int bit = 15; bit >= 0; --bit) {
       const uint32_t cand = pre | (1u << bit);
@@ -502,24 +511,32 @@ __device__ void topk_chunk(const u32x4 (&r)[NV_TILE], int lo, int len, int k, ty
       if (n > WCAP) s_over = 1;
     }
     __syncthreads();
-    done = s_over == 0;
+    const int o1 = s_wn[0], o2 = o1 + s_wn[1], o3 = o2 + s_wn[2], tot = o3 + s_wn[3];
+    done = s_over == 0 && tot <= cap;
     if (done) {
       // The chunk's list: the waves' lists back to back, written by the
       // whole block (the merge kernel reads it once: streaming stores).
-      const int o1 = s_wn[0], o2 = o1 + s_wn[1], o3 = o2 + s_wn[2], tot = o3 + s_wn[3];
       for (int q = t; q < tot; q += WG) {
         const int w = (q >= o1) + (q >= o2) + (q >= o3);
         const int from = w == 0 ? 0 : (w == 1 ? o1 : (w == 2 ? o2 : o3));
         const ST* ws = reinterpret_cast<const ST*>(sbuf) + w * WCAP;
         cand_st(dst + q, Staged<ET>::composite_at(ws[q - from], lo));
       }
-      if (t == 0) *cnt = tot;
+      if (t == 0) {
+        // The list holds every logit at or above the bound: all of the
+        // chunk's top k unless fewer than k were asked for.
+        cnt[0] = tot;
+        cnt[1] = keep < kk && bound > NEG_INF ? (int)order_key(bound) : 0;
+      }
     }
   }
   if (!done) {
     __syncthreads();  // the fast path's staging is no longer read
     topk_chunk_exact<ET>(r, lo, len, kk, dst, red);
-    if (t == 0) *cnt = kk;
+    if (t == 0) {
+      cnt[0] = kk;
+      cnt[1] = 0;
+    }
   }
 }
 
@@ -584,8 +601,8 @@ __device__ __forceinline__ void stats_body(const Args& a, int b, int slot, int c
 
   if (is_draft && a.topk > 0) {
     const size_t chunk = ((size_t)b * a.K + pos) * a.C + c;
-    topk_chunk<ET>(r, lo, len, a.topk, reinterpret_cast<typename Cand<ET>::T*>(a.cand) + chunk * NWAVE * WCAP,
-                   a.ccnt + chunk, shf);
+    topk_chunk<ET>(r, lo, len, a.topk, a.ckeep, a.cstride,
+                   reinterpret_cast<typename Cand<ET>::T*>(a.cand) + chunk * a.cstride, a.ccnt + 2 * chunk, shf);
     return;
   }
   const float m = block_max(tile_max<ET, NV_TILE>(r), shf);
@@ -1260,14 +1277,41 @@ template <typename ET>
 struct ListCands {
   const typename Cand<ET>::T* g;
   const int* gcnt;
-  int C, CS;
+  int C, CS, stride;
   template <typename F>
   __device__ __forceinline__ void each(F&& f) const {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     for (int L = wave; L < C; L += NWAVE) {
-      const int n = *(gcnt + L);
-      for (int j = lane; j < n; j += 64)
-        f(cand_composite<ET>(*(g + (size_t)L * NWAVE * WCAP + j), L * CS));
+      const int n = *(gcnt + 2 * L);
+      for (int j = lane; j < n; j += 64) f(cand_composite<ET>(*(g + (size_t)L * stride + j), L * CS));
+    }
+  }
+};
+// The fallback's candidates: the lists of the chunks whose bound key is at
+// or below `key`, and the logits of the other chunks read from the draft row
+// (those whose key is at least `key`; no other can reach the top k).
+template <typename ET>
+struct MixedCands {
+  const typename Cand<ET>::T* g;
+  const int* gcnt;
+  const ET* row;
+  int C, CS, V, stride;
+  uint32_t key;
+  template <typename F>
+  __device__ __forceinline__ void each(F&& f) const {
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    for (int L = wave; L < C; L += NWAVE) {
+      if ((uint32_t)*(gcnt + 2 * L + 1) > key) continue;
+      const int n = *(gcnt + 2 * L);
+      for (int j = lane; j < n; j += 64) f(cand_composite<ET>(*(g + (size_t)L * stride + j), L * CS));
+    }
+    for (int L = 0; L < C; ++L) {
+      if ((uint32_t)*(gcnt + 2 * L + 1) <= key) continue;
+      const int lo = L * CS, hi = min(lo + CS, V);
+      for (int x = lo + t; x < hi; x += WG) {
+        const float v = Tr<ET>::load1(row + x);
+        if (order_key(v) >= key) f(composite(v, x));
+      }
     }
   }
 };
@@ -1390,6 +1434,24 @@ __device__ __forceinline__ float take_kept(const Src& src, uint64_t thr, int d, 
   return z;
 }
 
+// Whether every chunk's list reaches down to the union's kk-th largest
+// composite thr: each chunk's bound key (0 for a list holding the chunk's
+// top k) is at most thr's value key.  Uniform over the block; the vote goes
+// through vote[NWAVE] (LDS), which is free again on return.
+__device__ __forceinline__ bool lists_hold_top(const int* gcnt, int C, uint64_t thr, int* vote) {
+  const uint32_t key = (uint32_t)(thr >> 32);
+  bool ok = true;
+  for (int c = threadIdx.x; c < C; c += WG) ok &= (uint32_t)*(gcnt + 2 * c + 1) <= key;
+  const bool wave_ok = __ballot(!ok) == 0ull;
+  if ((threadIdx.x & 63) == 0) vote[threadIdx.x >> 6] = wave_ok;
+  __syncthreads();
+  bool all = true;
+#pragma unroll
+  for (int w = 0; w < NWAVE; ++w) all &= vote[w] != 0;
+  __syncthreads();
+  return all;
+}
+
 // The merge of slot (row b, position i): `d` is the token whose q~ is
 // recorded (-1 for none).  Writes {max kept logit, Z_q, q~(d), kk} to qstat
 // and the kept ids and logits in ascending id order to kept; returns kk,
@@ -1412,8 +1474,8 @@ __device__ __forceinline__ int merge_body(const Args& a, int b, int i, int d) {
   const int C = a.C, kk = min(a.topk, a.V);
   const size_t slot = (size_t)b * a.K + i;
   using CT = typename Cand<ET>::T;
-  const CT* g = reinterpret_cast<const CT*>(a.cand) + slot * C * NWAVE * WCAP;  // chunk r's list at r * NWAVE * WCAP
-  const int* gcnt = a.ccnt + slot * C;
+  const CT* g = reinterpret_cast<const CT*>(a.cand) + slot * C * a.cstride;  // chunk r's list at r * cstride
+  const int* gcnt = a.ccnt + slot * C * 2;  // chunk r: {length, bound key}
   const float s = LOG2E / T;
   if (t == 0) {
     s_n = 0;
@@ -1421,18 +1483,19 @@ __device__ __forceinline__ int merge_body(const Args& a, int b, int i, int d) {
     s_ld = 0xFFFFFFFFu;
   }
   uint64_t thr;
-  float m, z;
+  float m, z = 0.f;
+  bool held;
   if (C <= MERGE_REG) {
     // One round of loads: the list lengths (lane r holds chunk r's) and a
     // window of 64 entries of each list (wave w: entries [64 w, 64 w + 64),
-    // read whole: a list area holds NWAVE * WCAP entries).
+    // read whole: a list area holds at least NWAVE * 64 entries).
     constexpr int HELD = NWAVE * 64;  // entries of a list held in registers
     RegCands<ET> rc;
     rc.CS = a.CS;
-    const int my_cnt = lane < C ? *(gcnt + lane) : 0;
+    const int my_cnt = lane < C ? *(gcnt + 2 * lane) : 0;
 #pragma unroll
     for (int r = 0; r < MERGE_REG; ++r)
-      rc.v[r] = r < C ? *(g + (size_t)r * NWAVE * WCAP + wave * 64 + lane) : CT(0);
+      rc.v[r] = r < C ? *(g + (size_t)r * a.cstride + wave * 64 + lane) : CT(0);
     __syncthreads();  // s_n / s_novf / rank initialised
     // Entries past the first HELD of a list go to the overflow buffer: wave
     // w takes those of chunks w, w + NWAVE, ... (rare).
@@ -1462,7 +1525,7 @@ __device__ __forceinline__ int merge_body(const Args& a, int b, int i, int d) {
         const int n = __builtin_amdgcn_readlane(my_cnt, r);
         for (int j = HELD + lane; j < n; j += 64)
           if (o + j - HELD < MERGE_OVF)
-            ovf[o + j - HELD] = cand_composite<ET>(*(g + (size_t)r * NWAVE * WCAP + j), r * a.CS);
+            ovf[o + j - HELD] = cand_composite<ET>(*(g + (size_t)r * a.cstride + j), r * a.CS);
         o += max(0, n - HELD);
       }
     }
@@ -1471,17 +1534,31 @@ __device__ __forceinline__ int merge_body(const Args& a, int b, int i, int d) {
     rc.novf = s_novf;
     if (rc.novf <= MERGE_OVF) {
       thr = select_threshold(rc, kk, sh32, red, ired, hist, &m);
-      z = take_kept(rc, thr, d, s, mul_rn(m, s), sel, &s_n, &s_ld);
+      held = lists_hold_top(gcnt, C, thr, ired);
+      if (held) z = take_kept(rc, thr, d, s, mul_rn(m, s), sel, &s_n, &s_ld);
     } else {
-      const ListCands<ET> lc{g, gcnt, C, a.CS};
+      const ListCands<ET> lc{g, gcnt, C, a.CS, a.cstride};
       thr = select_threshold(lc, kk, sh32, red, ired, hist, &m);
-      z = take_kept(lc, thr, d, s, mul_rn(m, s), sel, &s_n, &s_ld);
+      held = lists_hold_top(gcnt, C, thr, ired);
+      if (held) z = take_kept(lc, thr, d, s, mul_rn(m, s), sel, &s_n, &s_ld);
     }
   } else {
     __syncthreads();
-    const ListCands<ET> lc{g, gcnt, C, a.CS};
+    const ListCands<ET> lc{g, gcnt, C, a.CS, a.cstride};
     thr = select_threshold(lc, kk, sh32, red, ired, hist, &m);
-    z = take_kept(lc, thr, d, s, mul_rn(m, s), sel, &s_n, &s_ld);
+    held = lists_hold_top(gcnt, C, thr, ired);
+    if (held) z = take_kept(lc, thr, d, s, mul_rn(m, s), sel, &s_n, &s_ld);
+  }
+  if (!held) {
+    // A chunk's list stops above the k-th largest of the union, so some of
+    // its unlisted logits may belong to the top k: select again, with those
+    // chunks' logits read from the draft row.  Only logits whose key is at
+    // least the union's k-th largest can (it is a lower bound of the
+    // global one).  The largest logit is always listed, so m stands.
+    const MixedCands<ET> mc{g, gcnt, draft_row<ET>(a, b, i), C, a.CS, a.V, a.cstride, (uint32_t)(thr >> 32)};
+    float m2;
+    thr = select_threshold(mc, kk, sh32, red, ired, hist, &m2);
+    z = take_kept(mc, thr, d, s, mul_rn(m, s), sel, &s_n, &s_ld);
   }
   const float Z = block_sum(z, red);  // also orders sel[] and s_ld before their reads
   const float ms = mul_rn(m, s);
@@ -1778,6 +1855,7 @@ __global__ __launch_bounds__(WG) void finish_kernel(Args a) {
 // ============================================================================
 struct Plan {
   int C = 0, CS = 0;
+  int ckeep = 0, cstride = 0;  // sparse drafts: see cand_layout
   size_t off_cnt = 0, off_part = 0, off_subK = 0, off_subR = 0, off_cand = 0, off_ccnt = 0, off_qstat = 0, off_kept = 0,
          total = 0;
   size_t zero_bytes = 0;    // leading bytes holding every region that must be zero before a call
@@ -1800,6 +1878,19 @@ bool vocab_split(int V, int dtype, int& C, int& CS) {
   C = (int)((V + cs - 1) / cs);
   CS = (int)cs;
   return true;
+}
+
+// Sparse drafts: the logits each chunk lists at least, about twice a chunk's
+// share of the top k plus a margin (a chunk holding more of the top k than
+// that is read again by the merge kernel), and the entries of a chunk's
+// candidate area: room for three times that (a fast-path list over it takes
+// the exact path), for the exact path's min(k, len) and for the merge
+// kernel's fixed windows of NWAVE * 64 entries.
+void cand_layout(int topk, int V, int C, int& keep, int& stride) {
+  const int kk = std::min(topk, V);
+  keep = std::min(kk, (2 * kk + C - 1) / C + 16);
+  const int st = std::max(std::max(NWAVE * 64, kk), 3 * keep);
+  stride = (st + 63) / 64 * 64;
 }
 
 int make_plan(int B, int K, int V, int topk, int dtype, Plan& pl) {
@@ -1825,10 +1916,11 @@ int make_plan(int B, int K, int V, int topk, int dtype, Plan& pl) {
   off = align256(off + sizeof(uint32_t) * (size_t)B * C * NSUB);
   if (topk > 0) {
     const size_t slots = (size_t)B * K;
+    cand_layout(topk, V, C, pl.ckeep, pl.cstride);
     pl.off_cand = off;
-    off = align256(off + sizeof(uint64_t) * slots * C * NWAVE * WCAP);
+    off = align256(off + sizeof(uint64_t) * slots * C * pl.cstride);
     pl.off_ccnt = off;
-    off = align256(off + sizeof(int) * slots * C);
+    off = align256(off + 2 * sizeof(int) * slots * C);
     pl.off_qstat = off;
     off = align256(off + sizeof(float4) * slots);
     pl.off_kept = off;
@@ -1940,6 +2032,7 @@ int run(const void* tgt, const void* dft, const int32_t* tok, const float* uni, 
   a.subK = reinterpret_cast<uint32_t*>(base + pl.off_subK);
   a.subR = reinterpret_cast<uint32_t*>(base + pl.off_subR);
   a.B = B; a.K = K; a.V = V; a.C = pl.C; a.CS = pl.CS; a.topk = topk;
+  a.ckeep = pl.ckeep; a.cstride = pl.cstride;
   a.GA = (2 * K + 1) * pl.C;
   a.resident = 0;
   a.cache = pl.cache ? 1 : 0;
@@ -1970,6 +2063,7 @@ constexpr int EE_MAX_LDS_WORDS = 14336;  // the early-exit kernel's dynamic LDS 
 
 struct EEPlan {
   int C = 0, CS = 0;
+  int ckeep = 0, cstride = 0;
   size_t off_cnt = 0, off_part = 0, off_subK = 0, off_subR = 0, total = 0;
   size_t off_cand = 0, off_ccnt = 0, off_qstat = 0, off_kept = 0;
   size_t lds_bytes = 0;
@@ -2000,10 +2094,11 @@ int make_ee_plan(int B, int K, int V, int dtype, int topk, EEPlan& pl) {
   off = align256(off + sizeof(uint32_t) * (size_t)B * C * NSUB);
   if (topk > 0) {
     const size_t slots = (size_t)B * K;
+    cand_layout(topk, V, C, pl.ckeep, pl.cstride);
     pl.off_cand = off;
-    off = align256(off + sizeof(uint64_t) * slots * C * NWAVE * WCAP);
+    off = align256(off + sizeof(uint64_t) * slots * C * pl.cstride);
     pl.off_ccnt = off;
-    off = align256(off + sizeof(int) * slots * C);
+    off = align256(off + 2 * sizeof(int) * slots * C);
     pl.off_qstat = off;
     off = align256(off + sizeof(float4) * slots);
     pl.off_kept = off;
@@ -2057,6 +2152,7 @@ int run_early_exit(const void* tgt, const void* dft, const int32_t* tok, const f
   a.qstat = topk > 0 ? reinterpret_cast<float4*>(base + pl.off_qstat) : nullptr;
   a.kept = topk > 0 ? reinterpret_cast<uint2*>(base + pl.off_kept) : nullptr;
   a.B = B; a.K = K; a.V = V; a.C = pl.C; a.CS = pl.CS; a.topk = topk;
+  a.ckeep = pl.ckeep; a.cstride = pl.cstride;
   const size_t esz = dtype == SV_BF16 ? 2 : 4;
   const bool aligned = (reinterpret_cast<uintptr_t>(tgt) % 16 == 0) &&
                        (K == 0 || reinterpret_cast<uintptr_t>(dft) % 16 == 0) && ((size_t)V * esz) % 16 == 0;
@@ -2075,6 +2171,7 @@ constexpr int TREE_MAX_LDS_WORDS = 14336;  // the walking kernel's dynamic LDS (
 
 struct TreePlan {
   int C = 0, CS = 0;
+  int ckeep = 0, cstride = 0;
   size_t off_cnt = 0, off_part = 0, off_subK = 0, off_subR = 0, off_gath = 0, total = 0;
   size_t off_cand = 0, off_ccnt = 0, off_qstat = 0, off_kept = 0;
   size_t lds_bytes = 0;
@@ -2105,10 +2202,11 @@ int make_tree_plan(int B, int N, int V, int dtype, int topk, TreePlan& pl) {
   off = align256(off + 2 * sizeof(float) * (size_t)B * N);
   if (topk > 0) {
     const size_t nodes = (size_t)B * N;
+    cand_layout(topk, V, C, pl.ckeep, pl.cstride);
     pl.off_cand = off;
-    off = align256(off + sizeof(uint64_t) * nodes * C * NWAVE * WCAP);
+    off = align256(off + sizeof(uint64_t) * nodes * C * pl.cstride);
     pl.off_ccnt = off;
-    off = align256(off + sizeof(int) * nodes * C);
+    off = align256(off + 2 * sizeof(int) * nodes * C);
     pl.off_qstat = off;
     off = align256(off + sizeof(float4) * nodes);
     pl.off_kept = off;
@@ -2139,8 +2237,10 @@ int launch_tree(const TreeArgs& a, size_t lds, hipStream_t st, hipEvent_t* ev) {
     // linear path (positions read as nodes).
     Args m{};
     m.temp = a.temp;
+    m.dft = a.dft;  // node v's draft row is row (b, v) of [B, N, V]: the fallback reads it
     m.cand = a.cand; m.ccnt = a.ccnt; m.qstat = a.qstat; m.kept = a.kept;
     m.B = a.B; m.K = a.N; m.V = a.V; m.C = a.C; m.CS = a.CS; m.topk = a.topk;
+    m.ckeep = a.ckeep; m.cstride = a.cstride;
     hipLaunchKernelGGL(tree_merge_kernel<ET>, dim3(a.B * a.N), dim3(WG), 0, st, a, m);
     if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
   }
@@ -2181,6 +2281,7 @@ int run_tree(const void* tgt, const void* dft, const int32_t* tok, const int32_t
   a.qstat = topk > 0 ? reinterpret_cast<float4*>(base + pl.off_qstat) : nullptr;
   a.kept = topk > 0 ? reinterpret_cast<uint2*>(base + pl.off_kept) : nullptr;
   a.B = B; a.N = N; a.V = V; a.C = pl.C; a.CS = pl.CS; a.topk = topk;
+  a.ckeep = pl.ckeep; a.cstride = pl.cstride;
   const size_t esz = dtype == SV_BF16 ? 2 : 4;
   const bool aligned = (reinterpret_cast<uintptr_t>(tgt) % 16 == 0) &&
                        (N == 1 || reinterpret_cast<uintptr_t>(dft) % 16 == 0) && ((size_t)V * esz) % 16 == 0;

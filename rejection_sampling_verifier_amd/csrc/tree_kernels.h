@@ -46,11 +46,12 @@ struct TreeArgs {
   float* mass;               // [B] total weight of the final draw's distribution; or null
   // Sparse drafts (topk > 0): chunk candidate lists, then per node the kept
   // set (ascending id) and {max kept logit, Z_q, -, kept count}.
-  void* cand;                // [B, N, C, NWAVE, WCAP]
-  int* ccnt;                 // [B, N, C]
+  void* cand;                // [B, N, C, cstride]
+  int* ccnt;                 // [B, N, C, 2] list lengths and bound keys
   float4* qstat;             // [B, N]
   uint2* kept;               // [B, N, topk]
   int B, N, V, C, CS, topk;
+  int cstride, ckeep;        // candidate entries per chunk; logits a chunk lists at least
 };
 
 template <typename ET>
@@ -76,8 +77,8 @@ __device__ __forceinline__ void tree_slot_stats(const TreeArgs& a, int b, int no
   if (is_draft && a.topk > 0) {
     // A truncated draft: the chunk's candidates for the node's top k.
     const size_t chunk = ((size_t)b * N + node) * a.C + c;
-    topk_chunk<ET>(r, lo, len, a.topk, reinterpret_cast<typename Cand<ET>::T*>(a.cand) + chunk * NWAVE * WCAP,
-                   a.ccnt + chunk, shf);
+    topk_chunk<ET>(r, lo, len, a.topk, a.ckeep, a.cstride,
+                   reinterpret_cast<typename Cand<ET>::T*>(a.cand) + chunk * a.cstride, a.ccnt + 2 * chunk, shf);
     return;
   }
   uint32_t* dst = tree_part(a, b, is_draft ? N + node : node, c);
