@@ -206,7 +206,7 @@ __device__ __forceinline__ float tile_max<float, NV_TILE>(const u32x4 (&r)[NV_TI
 // Sparse draft truncation ([RheoSampling] section 3).  The global top k of a
 // draft position takes about k / C logits from each of its C chunks, so a
 // chunk lists only its best logits down to a bound: every logit at or above
-// the bound, at least `keep` of them (keep = min(k, ceil(2k/C) + 16)).  With
+// the bound, at least `keep` of them (keep = min(k, ceil(1.5k/C) + 8)).  With
 // the list goes the bound's order key, or 0 when the list holds the chunk's
 // whole top k (keep = k, the bound is -inf, or the exact path ran).  The
 // merge kernel selects the k-th largest of the union and checks that it is
@@ -1880,15 +1880,15 @@ bool vocab_split(int V, int dtype, int& C, int& CS) {
   return true;
 }
 
-// Sparse drafts: the logits each chunk lists at least, about twice a chunk's
-// share of the top k plus a margin (a chunk holding more of the top k than
-// that is read again by the merge kernel), and the entries of a chunk's
+// Sparse drafts: the logits each chunk lists at least, one and a half times
+// a chunk's share of the top k plus 8 (a chunk holding more of the top k
+// than its list is read again by the merge kernel), and the entries of a chunk's
 // candidate area: room for three times that (a fast-path list over it takes
 // the exact path), for the exact path's min(k, len) and for the merge
 // kernel's fixed windows of NWAVE * 64 entries.
 void cand_layout(int topk, int V, int C, int& keep, int& stride) {
   const int kk = std::min(topk, V);
-  keep = std::min(kk, (2 * kk + C - 1) / C + 16);
+  keep = std::min(kk, (3 * kk + 2 * C - 1) / (2 * C) + 8);
   const int st = std::max(std::max(NWAVE * 64, kk), 3 * keep);
   stride = (st + 63) / 64 * 64;
 }

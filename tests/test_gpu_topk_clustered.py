@@ -1,8 +1,8 @@
 """Truncated drafts whose best logits crowd into a few vocabulary chunks.
 
-Each chunk of a draft position lists only about twice its share of the top k
-(at least keep = min(k, ceil(2k/C) + 16) logits, all those at or above a
-bound).  When one chunk holds more of the top k than that, the union of the
+Each chunk of a draft position lists only about one and a half times its
+share of the top k (at least keep = min(k, ceil(1.5k/C) + 8) logits, all
+those at or above a bound).  When one chunk holds more of the top k than that, the union of the
 lists misses some of them; the merge kernel detects it (the union's k-th
 largest lies below that chunk's bound) and selects again with the chunk's
 logits read from the draft row.  These cases build such drafts, check on the
@@ -43,7 +43,7 @@ def _store(vals, dtype):
 
 def _layout(k, V, C):
     kk = min(k, V)
-    keep = min(kk, (2 * kk + C - 1) // C + 16)
+    keep = min(kk, (3 * kk + 2 * C - 1) // (2 * C) + 8)
     stride = -(-max(NWAVE * 64, kk, 3 * keep) // 64) * 64
     return kk, keep, stride
 
