@@ -1486,16 +1486,25 @@ __device__ __forceinline__ int merge_body(const Args& a, int b, int i, int d) {
   float m, z = 0.f;
   bool held;
   if (C <= MERGE_REG) {
-    // One round of loads: the list lengths (lane r holds chunk r's) and a
-    // window of 64 entries of each list (wave w: entries [64 w, 64 w + 64),
-    // read whole: a list area holds at least NWAVE * 64 entries).
+    // The list lengths (lane r holds chunk r's) and a window of 64 entries
+    // of each list (wave w: entries [64 w, 64 w + 64), read whole: a list
+    // area holds at least NWAVE * 64 entries).  Wave 0's windows come in the
+    // lengths' round of loads; the other waves load theirs only where a list
+    // reaches them (lists are usually shorter than 64).
     constexpr int HELD = NWAVE * 64;  // entries of a list held in registers
     RegCands<ET> rc;
     rc.CS = a.CS;
     const int my_cnt = lane < C ? *(gcnt + 2 * lane) : 0;
+    if (wave == 0) {
 #pragma unroll
-    for (int r = 0; r < MERGE_REG; ++r)
-      rc.v[r] = r < C ? *(g + (size_t)r * a.cstride + wave * 64 + lane) : CT(0);
+      for (int r = 0; r < MERGE_REG; ++r) rc.v[r] = r < C ? *(g + (size_t)r * a.cstride + lane) : CT(0);
+    } else {
+#pragma unroll
+      for (int r = 0; r < MERGE_REG; ++r) {
+        const int n = r < C ? __builtin_amdgcn_readlane(my_cnt, r) : 0;
+        rc.v[r] = wave * 64 < n ? *(g + (size_t)r * a.cstride + wave * 64 + lane) : CT(0);
+      }
+    }
     __syncthreads();  // s_n / s_novf / rank initialised
     // Entries past the first HELD of a list go to the overflow buffer: wave
     // w takes those of chunks w, w + NWAVE, ... (rare).
