@@ -364,7 +364,9 @@ int spec_verify_timed(const void* target_logits, const void* draft_logits,
  * Returns SV_ERR_SCRATCH, before enqueuing anything, when the shape's
  * workspace (spec_verify's size query) exceeds SV_SCRATCH_BYTES -- a dense
  * draft of 256 rows, K = 7, V = 201,088 needs about 1.7 MB; truncated drafts
- * need about 8 KB per (row, position, vocabulary chunk) more.  SV_ERR_HIP if
+ * need about 2 KB per (row, position, vocabulary chunk) more up to
+ * topk_draft = 128 (8 bytes per candidate entry, max(256, topk_draft, about
+ * 4.5 topk_draft / C + 24) entries per chunk).  SV_ERR_HIP if
  * the scratch's address cannot be obtained.  Other codes as spec_verify.
  */
 int spec_verify_noalloc(const void* target_logits, const void* draft_logits,
