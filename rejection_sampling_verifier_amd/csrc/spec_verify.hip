@@ -1619,9 +1619,10 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(8, 8))) void
 // with m the smallest count for which the sampling rows' work-groups are
 // all resident at once (greedy rows need one work-group each, briefly).
 constexpr int FINISH_COUNT_MAX = 4096;  // rows whose temperatures a work-group counts
-__device__ __forceinline__ int finish_groups(int nsamp, int C, int resident) {
+__host__ __device__ __forceinline__ int finish_groups(int nsamp, int C, int resident) {
   if (resident <= 0 || nsamp <= 0) return C;
-  const long long m = max(1LL, ((long long)nsamp * C + resident - 1) / resident);
+  const long long q = ((long long)nsamp * C + resident - 1) / resident;
+  const long long m = q > 1 ? q : 1;
   return (int)((C + m - 1) / m);
 }
 
@@ -1632,12 +1633,18 @@ __device__ __forceinline__ int finish_groups(int nsamp, int C, int resident) {
 // work-group publishes the 32 sub-block sums of max(0, p_n - q_n) over its
 // chunks j, j + G, j + 2G, ..., and the last of the row's G work-groups to
 // arrive (atomic counter) draws the correction token and clears the row's
-// published words.  The grid has C work-groups per row; G of them take part
-// (the others leave at once), with G chosen from the number of sampling rows
-// so that the working grid is about what the chip holds at once: every
-// work-group decides once and then streams, and no late generation of
-// work-groups drains after the others.  Greedy rows need their work-group 0
-// only; the others leave before deciding.
+// published words.  G is chosen from the number of sampling rows so that the
+// working grid is about what the chip holds at once: every work-group
+// decides once and then streams, and no late generation of work-groups
+// drains after the others.
+//
+// Numbering.  Work-group x < B is work-group 0 of row x (every row has one).
+// Work-group x >= B is work-group 1 + (x - B) / ns of the ((x - B) % ns)-th
+// sampling row in row order (ns sampling rows), so the working work-groups
+// come first in dispatch order and greedy rows take no slot beyond their
+// first; those past the working set leave at once.  Each work-group first
+// loads the row it would serve if every row sampled, which is its row
+// whenever that is so, and loads its own row again otherwise.
 // ============================================================================
 __device__ __forceinline__ void write_failed_row(const Args& a, int b) {
   // Reached only if a wait ran past its deadline: num_accepted = -1 marks it.
@@ -1653,10 +1660,9 @@ __global__ __launch_bounds__(WG) void finish_kernel(Args a) {
   __shared__ float shsub[NSUB];
   __shared__ int sh_last;
   __shared__ int sh_ns[NWAVE];
-  // Numbered j-major: the work-groups that take part (j < G) come first, and
-  // those past G, which leave at once, last.
-  const int j0 = blockIdx.x / a.B;
-  const int b = blockIdx.x % a.B;
+  __shared__ int sh_row;
+  const int x = blockIdx.x, B = a.B;
+  int b = x < B ? x : (x - B) % B;  // the row if every row samples
   const int K = a.K, C = a.C, S = 2 * K + 1, t = threadIdx.x, lane = t & 63, wave = t >> 6;
   // Sparse draft: the row's kept list at the rejected position (ids and q~
   // values, for the residual and the final draw) and the corrections
@@ -1666,30 +1672,58 @@ __global__ __launch_bounds__(WG) void finish_kernel(Args a) {
   __shared__ int kid[SV_MAX_TOPK];
   uint32_t* cache_pw = CACHED ? row_cache : nullptr;
   uint32_t* cache_sub = CACHED ? cache_pw + (size_t)S * C * 4 : nullptr;
-  const RowIn in = load_row_in(a, b);
-  // The sampling rows of the batch, counted in the round of loads that
-  // brings the row's partials.
-  int ns = 0;
-  if (a.B <= FINISH_COUNT_MAX)
-    for (int i = t; i < a.B; i += WG) ns += is_sampling_temperature(a.temp[i]) ? 1 : 0;
-  if (CACHED) {
-    // All partials of the row in one round of loads (also the draft-token
-    // logits, which the decision reads at a token-dependent chunk).
-    const u32x4* src = reinterpret_cast<const u32x4*>(part_words(a, b, 0, 0));
-    for (int i = t; i < S * C; i += WG) reinterpret_cast<u32x4*>(cache_pw)[i] = src[i];
-  }
-  ns = (int)wave_sum((float)ns);  // exact: at most FINISH_COUNT_MAX
-  if (lane == 0) sh_ns[wave] = ns;
-  __syncthreads();
-  ns = a.B;
-  if (a.B <= FINISH_COUNT_MAX) {
-    ns = 0;
-#pragma unroll
-    for (int w = 0; w < NWAVE; ++w) ns += sh_ns[w];
-  }
+  RowIn in = load_row_in(a, b);
+  // All partials of the row in one round of loads (also the draft-token
+  // logits, which the decision reads at a token-dependent chunk).
+  auto cache_partials = [&]() {
+    if (CACHED) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(part_words(a, b, 0, 0));
+      for (int i = t; i < S * C; i += WG) reinterpret_cast<u32x4*>(cache_pw)[i] = src[i];
+    }
+  };
+  // The sampling rows of the batch, counted in the same round of loads:
+  // thread t flags rows [t R, t R + R), so a scan of the counts ranks the
+  // sampling rows in row order.
+  const bool counted = B <= FINISH_COUNT_MAX;
+  const int R = (B + WG - 1) / WG;  // at most 16 when counted
+  uint32_t flags = 0u;
+  if (counted)
+    for (int i = 0; i < R; ++i) {
+      const int r = t * R + i;
+      if (r < B && is_sampling_temperature(a.temp[r])) flags |= 1u << i;
+    }
+  cache_partials();
+  int total;
+  const int mine = __popc(flags);
+  const int before = block_count_scan(mine, sh_ns, total);  // exact: counts below 2^24
+  const int ns = counted ? total : B;
   const int G = finish_groups(ns, C, a.resident);
-  // Work-groups past G, and a greedy row's past the first, have nothing to do.
-  if (j0 >= G || (j0 != 0 && !is_sampling_temperature(in.T))) return;
+  int j0 = 0;
+  if (x >= B) {
+    // Work-groups past the working set have nothing to do.
+    const int y = x - B;
+    if (ns == 0 || 1 + y / ns >= G) return;
+    j0 = 1 + y / ns;
+    if (ns < B) {
+      // Serve the (y % ns)-th sampling row: its thread finds it.
+      const int k = y % ns - before;
+      if (k >= 0 && k < mine) {
+        uint32_t f = flags;
+        for (int i = 0; i < k; ++i) f &= f - 1u;
+        sh_row = t * R + __builtin_ctz(f);
+      }
+      __syncthreads();
+      if (sh_row != b) {
+        b = sh_row;
+        in = load_row_in(a, b);
+        cache_partials();
+        __syncthreads();
+      }
+    }
+  }
+  // A greedy row's work-groups past the first have nothing to do (reached
+  // only when the rows were not counted).
+  if (j0 != 0 && !is_sampling_temperature(in.T)) return;
   RowView<CACHED> view{cache_pw, cache_sub, false};
   decide_row(a, b, rs, view, in);
   const int n = rs.n;
@@ -1987,6 +2021,30 @@ int resident_groups(const void* kernel, size_t lds) {
   return groups;
 }
 
+// Finishing grid: B work-groups (one per row) plus the largest number that
+// serve sampling rows past their first, over every count of sampling rows
+// the batch may hold (the kernel counts them).  Remembered per shape.
+int finish_grid(int B, int C, int resident) {
+  if (B > FINISH_COUNT_MAX) return B * finish_groups(B, C, resident);  // rows not counted: all sample
+  struct Entry {
+    int B, C, resident, grid;
+  };
+  constexpr int N = 64;
+  static Entry seen[N];
+  static int used = 0, next = 0;
+  static std::mutex mu;
+  std::lock_guard<std::mutex> lock(mu);
+  for (int i = 0; i < used; ++i)
+    if (seen[i].B == B && seen[i].C == C && seen[i].resident == resident) return seen[i].grid;
+  long long w = B;
+  for (int ns = 1; ns <= B; ++ns) w = std::max(w, B + (long long)(finish_groups(ns, C, resident) - 1) * ns);
+  const int grid = (int)w;
+  seen[next] = Entry{B, C, resident, grid};
+  next = (next + 1) % N;
+  used = std::min(used + 1, N);
+  return grid;
+}
+
 template <typename ET, bool AL>
 int launch_typed(const Args& a, size_t lds, size_t merge_lds, hipStream_t st, hipEvent_t* ev) {
   int rc = a.kl ? launch(paired_kernel<ET, AL>, a.B * (a.K + 1) * a.C, 0, st, ev, a)
@@ -2002,7 +2060,7 @@ int launch_typed(const Args& a, size_t lds, size_t merge_lds, hipStream_t st, hi
   void (*const fk)(Args) = a.cache ? finish_kernel<ET, AL, true> : finish_kernel<ET, AL, false>;
   Args af = a;
   af.resident = resident_groups(reinterpret_cast<const void*>(fk), lds);
-  return launch(fk, a.B * a.C, lds, st, ev ? ev + 4 : nullptr, af);
+  return launch(fk, finish_grid(a.B, a.C, af.resident), lds, st, ev ? ev + 4 : nullptr, af);
 }
 
 struct RelaxedRule {
