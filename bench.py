@@ -15,6 +15,12 @@ the fp64 CPU oracle's rate on a bounded sample of the same workload
 (``cpu_baseline``) and how the timed call's outputs compare with it.
 
     python bench.py [--steps K] [--warmup W] [--config C] [--no-cpu]
+
+Warm-up: W untimed calls before each timed pass.  By default W is sized so
+that the warm-up keeps the GPU busy for about WARMUP_S seconds (estimated
+from a few calls), which brings the clocks to their steady state; a GPU
+that has been idle while the host generated the inputs runs a short burst
+several percent slower.
 """
 
 from __future__ import annotations
@@ -33,6 +39,32 @@ sys.path.insert(0, ROOT)
 METRIC = "verified draft positions/sec at 1 GPU + achieved HBM GB/s vs peak"
 HBM_PEAK_GBPS = 8000.0
 MALL_BYTES = 256 << 20
+WARMUP_S = 0.3
+
+
+def warmup_calls(args, step, torch) -> int:
+    """W: args.warmup if given, else enough calls to fill about WARMUP_S
+    seconds (the calls made to estimate it are among the W).  Runs the first
+    warm-up pass."""
+    if args.warmup is not None:
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        return args.warmup
+    probe = 5
+    for i in range(probe):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(probe):
+        step(i)
+    torch.cuda.synchronize()
+    per_call = (time.perf_counter() - t0) / probe
+    w = max(20, min(20000, int(WARMUP_S / max(per_call, 1e-6)) + 1))
+    for i in range(2 * probe, w):
+        step(i)
+    torch.cuda.synchronize()
+    return max(w, 2 * probe)
 
 
 def kernel_source_hash() -> str:
@@ -171,7 +203,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help=f"untimed calls before each timed pass (default: about {WARMUP_S} s of calls)")
     ap.add_argument("--config", type=int, default=2,
                     help="workload index (2 = the default bench line: B256 K7 V201088)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -273,9 +306,7 @@ def main():
         fn(x["target"], x["draft"], x["tokens"], x["uniforms"], x["temperature"], d["topk"],
            out_tokens=out, num_accepted=nacc, workspace=ws, stream=stream.cuda_stream)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    args.warmup = warmup_calls(args, step, torch)
 
     # Timed region 1: plain calls, bracketed by events and wall clock, with
     # nothing else enqueued between them.
@@ -493,9 +524,7 @@ def tree_main(args, W, rsv, np, torch):
            out_tokens=out, out_nodes=nodes, num_accepted=nacc, workspace=ws,
            stream=stream.cuda_stream)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    args.warmup = warmup_calls(args, step, torch)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     w0 = time.perf_counter()
     ev0.record(stream)

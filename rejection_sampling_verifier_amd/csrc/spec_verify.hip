@@ -1663,6 +1663,10 @@ __global__ __launch_bounds__(WG) void finish_kernel(Args a) {
   __shared__ int sh_row;
   const int x = blockIdx.x, B = a.B;
   int b = x < B ? x : (x - B) % B;  // the row if every row samples
+  // Waves issue at high priority while they decide and draw (a dependent
+  // chain), and at the lowest while they stream the residual, so that the
+  // streaming waves sharing a SIMD do not slow the decisions.
+  __builtin_amdgcn_s_setprio(3);
   const int K = a.K, C = a.C, S = 2 * K + 1, t = threadIdx.x, lane = t & 63, wave = t >> 6;
   // Sparse draft: the row's kept list at the rejected position (ids and q~
   // values, for the residual and the final draw) and the corrections
@@ -1773,6 +1777,7 @@ __global__ __launch_bounds__(WG) void finish_kernel(Args a) {
   uint32_t* subR_row = a.subR + (size_t)b * C * NSUB;
   float MSq, rZq;
   int nkept = 0;
+  __builtin_amdgcn_s_setprio(0);
   if (a.topk > 0) {
     // Sparse draft: q~ is non-zero only at the kept ids, so the residual of
     // a sub-block is sum(p) - sum over its kept ids of min(p, q~).  Only the
@@ -1869,6 +1874,7 @@ __global__ __launch_bounds__(WG) void finish_kernel(Args a) {
       __syncthreads();  // shsub is reused by the next chunk
     }
   }
+  __builtin_amdgcn_s_setprio(3);
   // Count this work-group.  Its sums need no ordering with the count: the
   // last work-group polls them until they are published (each of its peers
   // has already issued its stores, so the wait ends).
