@@ -98,15 +98,16 @@ __device__ __forceinline__ void ee_stats_chunk(const Args& a, int b, int pos, in
 #pragma unroll
   for (int j = 1; j < NV_TILE; ++j) zl += zj[j];
   const float z = block_sum(zl, shf);
-  if (!draft && pos == K) {
-    // Bonus position: the 32 sub-block sums for the draw.
+  if (!draft && (pos == K || a.topk > 0)) {
+    // The 32 sub-block sums of the bonus position for the draw, and with a
+    // truncated draft of every target position (its residual's mass).
 #pragma unroll
     for (int j = 0; j < NV_TILE; ++j) {
       const float v = wave_sum(zj[j]);
       if (lane == 0) shsub[j * NWAVE + wave] = v;
     }
     __syncthreads();
-    if (t < NSUB) pub_f32(a.subK + ((size_t)b * a.C + c) * NSUB + t, shsub[t]);
+    if (t < NSUB) pub_f32(sub_words(a, b, pos, c) + t, shsub[t]);
   }
   if (t < 4) {
     uint32_t w = 0u;
@@ -157,57 +158,6 @@ __device__ __forceinline__ void ee_residual_chunk(const Args& a, int b, int n, i
   }
   __syncthreads();
   if (t < NSUB) pub_f32(a.subR + ((size_t)b * a.C + c) * NSUB + t, shsub[t]);
-}
-
-// Sparse drafts: the residual sums of one chunk, as finish_kernel's sparse
-// branch (the sum of p over a sub-block less min(p, q~) at its kept ids);
-// the kept ids and q~ values are in kid / kq (LDS, ascending id).
-template <typename ET, bool ALIGNED>
-__device__ __forceinline__ void ee_residual_chunk_sparse(const Args& a, int b, int n, int c, float s, float MSt,
-                                                         float rZt, const int* kid, const float* kq, float* corr,
-                                                         int nkept, float* shsub) {
-  constexpr int VEC = Tr<ET>::VEC;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int lo = c * a.CS;
-  const int len = min(a.CS, a.V - lo);
-  const ET* trow = target_row<ET>(a, b, n);
-  u32x4 rt[NV_TILE];
-  load_tile<ET, ALIGNED, NV_TILE>(trow, lo, len, rt);
-  for (int j = t; j < nkept; j += WG) {
-    const int id = kid[j];
-    float cv = 0.f;
-    if (id >= lo && id < lo + len) {
-      const float pv = exp2_fast(fmaf(Tr<ET>::load1(trow + id), s, -MSt)) * rZt;
-      cv = fminf(pv, kq[j]);
-    }
-    corr[j] = cv;
-  }
-#pragma unroll
-  for (int j = 0; j < NV_TILE; ++j) {
-    float w0 = 0.f, w1 = 0.f;
-#pragma unroll
-    for (int k = 0; k < VEC; k += 2) {
-      w0 += exp2_fast(fmaf(Tr<ET>::at(rt[j], k), s, -MSt)) * rZt;
-      w1 += exp2_fast(fmaf(Tr<ET>::at(rt[j], k + 1), s, -MSt)) * rZt;
-    }
-    const float v = wave_sum(w0 + w1);
-    if (lane == 0) shsub[j * NWAVE + wave] = v;
-  }
-  __syncthreads();
-  if (t < NSUB) {
-    auto lower = [&](int x) {
-      int l0 = 0, h0 = nkept;
-      while (l0 < h0) {
-        const int mid = (l0 + h0) >> 1;
-        if (kid[mid] < x) l0 = mid + 1; else h0 = mid;
-      }
-      return l0;
-    };
-    const int j0 = lower(lo + t * 64 * VEC), j1 = lower(lo + (t + 1) * 64 * VEC);
-    float cs = 0.f;
-    for (int j = j0; j < j1; ++j) cs += corr[j];
-    pub_f32(a.subR + ((size_t)b * a.C + c) * NSUB + t, fmaxf(0.f, shsub[t] - cs));
-  }
 }
 
 // Merge of one slot's decoded chunk words (LDS) by one wave, in the order of
@@ -302,9 +252,6 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4))) void ea
       const int k = (int)(ticket - base);
       if (phase == STATS) {
         ee_stats_chunk<ET, ALIGNED>(a, b, pos, k % C, greedy, !SPARSE && k >= C, s, shf, shi, shsub);
-      } else if (sparse) {
-        const float MSt = mul_rn(rs.M[pos], s), rZt = 1.f / rs.Z[pos];
-        ee_residual_chunk_sparse<ET, ALIGNED>(a, b, pos, k, s, MSt, rZt, kid, kq, kcorr, (int)s_qs.w, shsub);
       } else {
         const float MSt = mul_rn(rs.M[pos], s), rZt = 1.f / rs.Z[pos];
         const float MSq = mul_rn(rs.M[K + 1 + pos], s), rZq = 1.f / rs.Z[K + 1 + pos];
@@ -317,15 +264,19 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4))) void ea
     // Every chunk of the current stage has been handed out: collect it.
     if (phase == STATS) {
       const bool draft = !greedy && pos < K && !sparse;
-      const bool bonus = !greedy && pos == K;
+      // The position's sub-block sums: the bonus position's for its draw,
+      // and with a truncated draft every position's (its residual's mass).
+      const bool sums = !greedy && (pos == K || sparse);
       if (SPARSE && pos == 0) {
         // Written by the statistics launch before this one: plain words.
         for (int i = t; i < C * 4; i += WG) pw[i] = part_words(a, b, 0, 0)[i];
+        if (sums)
+          for (int i = t; i < C * NSUB; i += WG) sub[i] = sub_words(a, b, 0, 0)[i];
       } else {
         ok = wait_words(part_words(a, b, pos, 0), C * 4, pw + (size_t)pos * C * 4,
-                        draft ? part_words(a, b, K + 1 + pos, 0) : (bonus ? a.subK + (size_t)b * C * NSUB : nullptr),
-                        draft ? C * 4 : (bonus ? C * NSUB : 0),
-                        draft ? pw + (size_t)(K + 1 + pos) * C * 4 : (bonus ? sub : nullptr),
+                        draft ? part_words(a, b, K + 1 + pos, 0) : (sums ? sub_words(a, b, pos, 0) : nullptr),
+                        draft ? C * 4 : (sums ? C * NSUB : 0),
+                        draft ? pw + (size_t)(K + 1 + pos) * C * 4 : (sums ? sub : nullptr),
                         wall_clock64() + WAIT_TICKS);
       }
       if (!ok) break;
@@ -385,7 +336,8 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4))) void ea
       if (s_acc) {
         ++pos;
       } else {
-        phase = (greedy || pos == K) ? DONE : RESID;
+        // A truncated draft's residual is formed by the drawer (no pass).
+        phase = (greedy || pos == K || sparse) ? DONE : RESID;
       }
     } else {
       ok = wait_words(a.subR + (size_t)b * C * NSUB, C * NSUB, sub, nullptr, 0, nullptr,
@@ -414,11 +366,22 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4))) void ea
       const float MSq = n < K ? mul_rn(rs.M[K + 1 + n], s) : 0.f;
       const float rZq = n < K ? 1.f / rs.Z[K + 1 + n] : 0.f;
       const RowView<true> view{pw, sub, true};
-      if constexpr (SPARSE)
-        final_draw<ET, ALIGNED, true>(a, b, n, s, MSt, rZt, MSq, rZq, rs, view, sparse ? kid : nullptr, kq,
-                                      sparse && n < K ? (int)s_qs.w : 0);
-      else
+      if constexpr (SPARSE) {
+        const int nkept = sparse && n < K ? (int)s_qs.w : 0;
+        if (sparse && n < K) {
+          // The residual's sub-block sums from position n's sums (in `sub`)
+          // and its kept list, in place.
+          float* R = reinterpret_cast<float*>(sub);
+          sparse_residual<ET>(
+              target_row<ET>(a, b, n), a.V, C, a.CS, s, MSt, rZt, kid, kq, nkept, kcorr,
+              [&](int cc, int u) { return R[cc * NSUB + u]; },
+              [&](int cc) { return __uint_as_float(pw[((size_t)n * C + cc) * 4]); },
+              [&](int i, float r) { R[i] = r; });
+        }
+        final_draw<ET, ALIGNED, true>(a, b, n, s, MSt, rZt, MSq, rZq, rs, view, sparse ? kid : nullptr, kq, nkept);
+      } else {
         final_draw<ET, ALIGNED, true>(a, b, n, s, MSt, rZt, MSq, rZq, rs, view, nullptr, nullptr, 0);
+      }
     }
   }
   // The last work-group of the row to finish clears its published words.
@@ -431,8 +394,12 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4))) void ea
   for (int i = t; i < (last + 1) * C * 4; i += WG) clear_word(part_words(a, b, 0, 0) + i);
   if (!greedy || !ok)
     for (int i = t; i < min(last + 1, K) * C * 4; i += WG) clear_word(part_words(a, b, K + 1, 0) + i);
-  if (!ok || (!greedy && pos == K))
-    for (int i = t; i < C * NSUB; i += WG) clear_word(a.subK + (size_t)b * C * NSUB + i);
+  if (SPARSE && (!ok || !greedy)) {
+    // Every position reached published its sums (position 0's are plain).
+    for (int i = t; i < (last + 1) * C * NSUB; i += WG) clear_word(sub_words(a, b, 0, 0) + i);
+  } else if (!ok || (!greedy && pos == K)) {
+    for (int i = t; i < C * NSUB; i += WG) clear_word(sub_words(a, b, K, 0) + i);
+  }
   if (!ok || (!greedy && pos < K))
     for (int i = t; i < C * NSUB; i += WG) clear_word(a.subR + (size_t)b * C * NSUB + i);
   if (t == 0) {

@@ -96,7 +96,7 @@ struct Args {
   float* probs;              // [B, K, 2] or null
   float* mass;               // [B] or null
   uint32_t* part;            // [B, 2K+1, C, 4] published {max | argmax value, sum, argmax id, l(d)}
-  uint32_t* subK;            // [B, C, NSUB] published bonus-position sub-block sums (vs chunk max)
+  uint32_t* subK;            // [B, NT, C, NSUB] target sub-block sums (vs chunk max), see sub_words
   uint32_t* subR;            // [B, C, NSUB] published residual sub-block sums
   unsigned* cnt;             // [B] finishing work-groups that have arrived
   void* cand;                // [B, K, C, cstride] chunk candidate lists of sparse drafts (Cand<ET>::T)
@@ -143,6 +143,14 @@ __device__ __forceinline__ void clear_word(uint32_t* p) {
 // merge kernel, a later launch (streaming stores, plain loads).
 __device__ __forceinline__ void cand_st(uint64_t* p, uint64_t v) { __builtin_nontemporal_store(v, p); }
 
+// Sub-block sums of a target position (vs the chunk max), [B, NT, C, NSUB]:
+// with a truncated draft every target position's (NT = K + 1), else the
+// bonus position's only (NT = 1).
+__device__ __forceinline__ uint32_t* sub_words(const Args& a, int b, int slot, int c) {
+  const int nt = a.topk > 0 ? a.K + 1 : 1;
+  const int sl = a.topk > 0 ? slot : 0;
+  return a.subK + (((size_t)b * nt + sl) * a.C + c) * NSUB;
+}
 __device__ __forceinline__ uint32_t* part_words(const Args& a, int b, int slot, int c) {
   return a.part + (((size_t)b * (2 * a.K + 1) + slot) * (size_t)a.C + c) * 4;
 }
@@ -653,16 +661,18 @@ __device__ __forceinline__ void stats_body(const Args& a, int b, int slot, int c
   } else {
     z = block_sum(zl, shf);
   }
-  if (slot == a.K) {
-    // Sub-block sums of the bonus position: sub-block (j, wave) holds the
-    // 64 * VEC consecutive ids of vector row j owned by that wave.
+  if (slot == a.K || (a.topk > 0 && !is_draft)) {
+    // Sub-block sums of the bonus position, and with a truncated draft of
+    // every target position (its residual's mass outside the kept ids):
+    // sub-block (j, wave) holds the 64 * VEC consecutive ids of vector row
+    // j owned by that wave.
 #pragma unroll
     for (int j = 0; j < NV_TILE; ++j) {
       const float v = wave_sum(zj[j]);
       if (lane == 0) shsub[j * NWAVE + wave] = v;
     }
     __syncthreads();
-    if (t < NSUB) a.subK[((size_t)b * a.C + c) * NSUB + t] = __float_as_uint(shsub[t]);
+    if (t < NSUB) sub_words(a, b, slot, c)[t] = __float_as_uint(shsub[t]);
   }
   if (t == 0) {
     uint32_t ld = 0u;
@@ -1073,6 +1083,52 @@ __device__ __forceinline__ SegResult segment_search(const ET* __restrict__ trow,
 }
 
 // ============================================================================
+// Residual of a truncated draft ([RheoSampling] sections 3 and 4): the
+// sub-block sums of max(0, p - q~) over a position, by the calling
+// work-group (all threads), with no pass over the logits.  q~ is zero
+// outside its kept ids, so the sum over sub-block (c, u) is
+//   R(c, u) = max(0, P(c, u) - sum over its kept ids x, in list order, of min(p(x), kq[x])),
+// where P(c, u) = sub(c, u) * exp2(fl(m_c s) - MSt) * rZt is the target's
+// mass over the sub-block, from the statistics pass's sum of
+// exp2(fma(l, s, -fl(m_c s))) there and the chunk max m_c.  Only the target
+// logits at the kept ids are read.  kid / kq: the kept ids (ascending) and
+// their q~ values (or c q~ for a tree's later residual), in LDS; corr: LDS
+// scratch of nkept floats.  sub(c, u) and chunk_max(c) read the position's
+// statistics; out(i, R) stores R(c, u) at i = c * NSUB + u.  Sub-block u of
+// chunk c holds the ids c * CS + [u, u + 1) * 64 * VEC below the chunk's end
+// min((c + 1) * CS, V).
+// ============================================================================
+template <typename ET, typename SubF, typename MaxF, typename OutF>
+__device__ __forceinline__ void sparse_residual(const ET* __restrict__ trow, int V, int C, int CS, float s, float MSt,
+                                                float rZt, const int* kid, const float* kq, int nkept,
+                                                float* corr, SubF&& sub, MaxF&& chunk_max, OutF&& out) {
+  constexpr int VEC = Tr<ET>::VEC;
+  for (int j = threadIdx.x; j < nkept; j += WG)
+    corr[j] = fminf(exp2_fast(fmaf(Tr<ET>::load1(trow + kid[j]), s, -MSt)) * rZt, kq[j]);
+  __syncthreads();
+  auto lower = [&](int x) {
+    int l0 = 0, h0 = nkept;
+    while (l0 < h0) {
+      const int mid = (l0 + h0) >> 1;
+      if (kid[mid] < x) l0 = mid + 1; else h0 = mid;
+    }
+    return l0;
+  };
+  for (int i = threadIdx.x; i < C * NSUB; i += WG) {
+    const int c = i / NSUB, u = i % NSUB;
+    const int end = min((c + 1) * CS, V);
+    const int x0 = min(c * CS + u * 64 * VEC, end);
+    const int j0 = lower(x0), j1 = lower(min(x0 + 64 * VEC, end));
+    float cs = 0.f;
+    for (int j = j0; j < j1; ++j) cs += corr[j];
+    const float mc = chunk_max(c);
+    const float sc = mc == NEG_INF ? 0.f : exp2_fast(mul_rn(mc, s) - MSt) * rZt;
+    out(i, fmaxf(0.f, sub(c, u) * sc - cs));
+  }
+  __syncthreads();
+}
+
+// ============================================================================
 // Final draw for a sampling row ([RheoSampling] section 4 step 3), by wave 0
 // of the calling work-group alone (no block barriers).  The weights are the
 // residual max(0, p_n - q_n) after a rejection at n < K, or the bonus
@@ -1100,7 +1156,7 @@ __device__ __forceinline__ void final_draw(const Args& a, int b, int n, float s,
   const int K = a.K, C = a.C, l = threadIdx.x;
   if (l >= 64) return;
   const bool reject = n < K;
-  const uint32_t* gsub = (reject ? a.subR : a.subK) + (size_t)b * C * NSUB;
+  const uint32_t* gsub = reject ? a.subR + (size_t)b * C * NSUB : sub_words(a, b, K, 0);
   auto bonus_scale = [&](int c) {
     const float mc = view_part(a, v, b, K, c, 0);
     return mc == NEG_INF ? 0.f : exp2_fast(mul_rn(mc, s) - MSt) * rZt;
@@ -1701,7 +1757,9 @@ __global__ __launch_bounds__(WG) void finish_kernel(Args a) {
   const int mine = __popc(flags);
   const int before = block_count_scan(mine, sh_ns, total);  // exact: counts below 2^24
   const int ns = counted ? total : B;
-  const int G = finish_groups(ns, C, a.resident);
+  // A truncated draft's residual needs no pass over the logits: one
+  // work-group per row.
+  const int G = a.topk > 0 ? 1 : finish_groups(ns, C, a.resident);
   int j0 = 0;
   if (x >= B) {
     // Work-groups past the working set have nothing to do.
@@ -1772,107 +1830,73 @@ __global__ __launch_bounds__(WG) void finish_kernel(Args a) {
     if (j0 == 0) final_draw<ET, ALIGNED, CACHED>(a, b, n, s, MSt, rZt, 0.f, 0.f, rs, view, nullptr, nullptr, 0);
     return;
   }
-  // Rejected at position n: residual max(0, p_n - q_n) over the
-  // work-group's chunks, each published as 32 sub-block sums.
   uint32_t* subR_row = a.subR + (size_t)b * C * NSUB;
-  float MSq, rZq;
-  int nkept = 0;
-  __builtin_amdgcn_s_setprio(0);
   if (a.topk > 0) {
-    // Sparse draft: q~ is non-zero only at the kept ids, so the residual of
-    // a sub-block is sum(p) - sum over its kept ids of min(p, q~).  Only the
-    // target row is re-read.  The kept list (ids and q~ values, ascending
-    // id) goes to LDS once; its first entries, its statistics and the first
-    // chunk's tile are loaded in one round.
+    // Rejected at position n with a truncated draft: the row's single
+    // work-group forms the residual's sub-block sums from the statistics
+    // pass's sums and the kept list (no pass over the logits) and draws.
     const uint2* kept = a.kept + ((size_t)b * K + n) * a.topk;
     const float4 qs = a.qstat[(size_t)b * K + n];
-    uint2 e0 = make_uint2(0xFFFFFFFFu, 0u);
-    if (t < a.topk) e0 = kept[t];
-    const ET* trow = target_row<ET>(a, b, n);
-    MSq = mul_rn(qs.x, s);
-    rZq = 1.f / qs.y;
-    nkept = (int)qs.w;
-    for (int c = j0; c < C; c += G) {
-      const int lo = c * a.CS;
-      const int len = min(a.CS, a.V - lo);
-      u32x4 rt[NV_TILE];
-      load_tile<ET, ALIGNED, NV_TILE>(trow, lo, len, rt);
-      if (c == j0) {
-        for (int jj = t; jj < nkept; jj += WG) {
-          const uint2 e = jj == t ? e0 : kept[jj];
-          kid[jj] = (int)e.x;
-          kq[jj] = exp2_fast(fmaf(__uint_as_float(e.y), s, -MSq)) * rZq;
-        }
-        __syncthreads();
-      }
-      // Correction min(p, q~) of each kept id in this chunk (0 elsewhere).
-      for (int jj = t; jj < nkept; jj += WG) {
-        const int id = kid[jj];
-        float cv = 0.f;
-        if (id >= lo && id < lo + len) {
-          const float pv = exp2_fast(fmaf(Tr<ET>::load1(trow + id), s, -MSt)) * rZt;
-          cv = fminf(pv, kq[jj]);
-        }
-        kcorr[jj] = cv;
-      }
-#pragma unroll
-      for (int jv = 0; jv < NV_TILE; ++jv) {
-        float w0 = 0.f, w1 = 0.f;
-#pragma unroll
-        for (int k = 0; k < VEC; k += 2) {
-          w0 += exp2_fast(fmaf(Tr<ET>::at(rt[jv], k), s, -MSt)) * rZt;
-          w1 += exp2_fast(fmaf(Tr<ET>::at(rt[jv], k + 1), s, -MSt)) * rZt;
-        }
-        const float v = wave_sum(w0 + w1);
-        if (lane == 0) shsub[jv * NWAVE + wave] = v;
-      }
-      __syncthreads();
-      if (t < NSUB) {
-        // Sub-block t holds the ids lo + [t, t+1) * 64 * VEC: a contiguous
-        // run of the sorted kept list, summed in list order.
-        auto lower = [&](int x) {
-          int l0 = 0, h0 = nkept;
-          while (l0 < h0) {
-            const int mid = (l0 + h0) >> 1;
-            if (kid[mid] < x) l0 = mid + 1; else h0 = mid;
-          }
-          return l0;
-        };
-        const int i0 = lower(lo + t * 64 * VEC), i1 = lower(lo + (t + 1) * 64 * VEC);
-        float cs = 0.f;
-        for (int i = i0; i < i1; ++i) cs += kcorr[i];
-        pub_f32(subR_row + (size_t)c * NSUB + t, fmaxf(0.f, shsub[t] - cs));
-      }
-      __syncthreads();  // shsub and kcorr are reused by the next chunk
+    const float MSq = mul_rn(qs.x, s), rZq = 1.f / qs.y;
+    const int nkept = (int)qs.w;
+    // The kept list and the position's sub-block sums in one round of loads.
+    float* R = reinterpret_cast<float*>(cache_sub);
+    for (int j = t; j < nkept; j += WG) {
+      const uint2 e = kept[j];
+      kid[j] = (int)e.x;
+      kq[j] = exp2_fast(fmaf(__uint_as_float(e.y), s, -MSq)) * rZq;
     }
-  } else {
-    MSq = mul_rn(rs.M[K + 1 + n], s);
-    rZq = 1.f / rs.Z[K + 1 + n];
-    for (int c = j0; c < C; c += G) {
-      const int lo = c * a.CS;
-      const int len = min(a.CS, a.V - lo);
-      u32x4 rt[NV_TILE], rq[NV_TILE];
-      load_tile<ET, ALIGNED, NV_TILE>(target_row<ET>(a, b, n), lo, len, rt);
-      load_tile<ET, ALIGNED, NV_TILE>(draft_row<ET>(a, b, n), lo, len, rq);
-#pragma unroll
-      for (int jv = 0; jv < NV_TILE; ++jv) {
-        float w0 = 0.f, w1 = 0.f;
-#pragma unroll
-        for (int k = 0; k < VEC; k += 2) {
-          const float p0 = exp2_fast(fmaf(Tr<ET>::at(rt[jv], k), s, -MSt)) * rZt;
-          const float q0 = exp2_fast(fmaf(Tr<ET>::at(rq[jv], k), s, -MSq)) * rZq;
-          const float p1 = exp2_fast(fmaf(Tr<ET>::at(rt[jv], k + 1), s, -MSt)) * rZt;
-          const float q1 = exp2_fast(fmaf(Tr<ET>::at(rq[jv], k + 1), s, -MSq)) * rZq;
-          w0 += fmaxf(0.f, p0 - q0);
-          w1 += fmaxf(0.f, p1 - q1);
-        }
-        const float v = wave_sum(w0 + w1);
-        if (lane == 0) shsub[jv * NWAVE + wave] = v;
-      }
+    if (CACHED)
+      for (int i = t; i < C * NSUB; i += WG) R[i] = __uint_as_float(sub_words(a, b, n, 0)[i]);
+    __syncthreads();
+    sparse_residual<ET>(
+        target_row<ET>(a, b, n), a.V, C, a.CS, s, MSt, rZt, kid, kq, nkept, kcorr,
+        [&](int c, int u) { return CACHED ? R[c * NSUB + u] : __uint_as_float(sub_words(a, b, n, c)[u]); },
+        [&](int c) { return view_part(a, view, b, n, c, 0); },
+        [&](int i, float r) {
+          if (CACHED) R[i] = r;
+          else pub_f32(subR_row + i, r);
+        });
+    bool ok = true;
+    if (!CACHED)  // this work-group's own published sums, read back as published words
+      ok = wait_words(subR_row, C * NSUB, nullptr, nullptr, 0, nullptr, wall_clock64() + WAIT_TICKS);
+    view.sub_loaded = CACHED;
+    if (ok) final_draw<ET, ALIGNED, CACHED>(a, b, n, s, MSt, rZt, MSq, rZq, rs, view, kid, kq, nkept);
+    else write_failed_row(a, b);
+    if (!CACHED) {
       __syncthreads();
-      if (t < NSUB) pub_f32(subR_row + (size_t)c * NSUB + t, shsub[t]);
-      __syncthreads();  // shsub is reused by the next chunk
+      for (int i = t; i < C * NSUB; i += WG) clear_word(subR_row + i);
     }
+    return;
+  }
+  // Rejected at position n: residual max(0, p_n - q_n) over the
+  // work-group's chunks, each published as 32 sub-block sums.
+  const float MSq = mul_rn(rs.M[K + 1 + n], s), rZq = 1.f / rs.Z[K + 1 + n];
+  __builtin_amdgcn_s_setprio(0);
+  for (int c = j0; c < C; c += G) {
+    const int lo = c * a.CS;
+    const int len = min(a.CS, a.V - lo);
+    u32x4 rt[NV_TILE], rq[NV_TILE];
+    load_tile<ET, ALIGNED, NV_TILE>(target_row<ET>(a, b, n), lo, len, rt);
+    load_tile<ET, ALIGNED, NV_TILE>(draft_row<ET>(a, b, n), lo, len, rq);
+#pragma unroll
+    for (int jv = 0; jv < NV_TILE; ++jv) {
+      float w0 = 0.f, w1 = 0.f;
+#pragma unroll
+      for (int k = 0; k < VEC; k += 2) {
+        const float p0 = exp2_fast(fmaf(Tr<ET>::at(rt[jv], k), s, -MSt)) * rZt;
+        const float q0 = exp2_fast(fmaf(Tr<ET>::at(rq[jv], k), s, -MSq)) * rZq;
+        const float p1 = exp2_fast(fmaf(Tr<ET>::at(rt[jv], k + 1), s, -MSt)) * rZt;
+        const float q1 = exp2_fast(fmaf(Tr<ET>::at(rq[jv], k + 1), s, -MSq)) * rZq;
+        w0 += fmaxf(0.f, p0 - q0);
+        w1 += fmaxf(0.f, p1 - q1);
+      }
+      const float v = wave_sum(w0 + w1);
+      if (lane == 0) shsub[jv * NWAVE + wave] = v;
+    }
+    __syncthreads();
+    if (t < NSUB) pub_f32(subR_row + (size_t)c * NSUB + t, shsub[t]);
+    __syncthreads();  // shsub is reused by the next chunk
   }
   __builtin_amdgcn_s_setprio(3);
   // Count this work-group.  Its sums need no ordering with the count: the
@@ -1885,9 +1909,7 @@ __global__ __launch_bounds__(WG) void finish_kernel(Args a) {
   if (!sh_last) return;
   const bool ok = wait_words(subR_row, C * NSUB, cache_sub, nullptr, 0, nullptr, wall_clock64() + WAIT_TICKS);
   view.sub_loaded = CACHED;
-  // A sparse draft's kept list (ids and q~ values) is still in LDS from the
-  // residual pass.
-  final_draw<ET, ALIGNED, CACHED>(a, b, n, s, MSt, rZt, MSq, rZq, rs, view, kid, kq, nkept);
+  final_draw<ET, ALIGNED, CACHED>(a, b, n, s, MSt, rZt, MSq, rZq, rs, view, nullptr, nullptr, 0);
   // With the sums in LDS the other waves clear the published words while
   // wave 0 draws; otherwise the draw reads them, so the clear waits.
   if (!CACHED || !ok) __syncthreads();
@@ -1959,8 +1981,8 @@ int make_plan(int B, int K, int V, int topk, int dtype, Plan& pl) {
   off = align256(off + sizeof(unsigned) * (size_t)B);
   pl.off_part = off;
   off = align256(off + 4 * sizeof(uint32_t) * (size_t)B * S * C);
-  pl.off_subK = off;
-  off = align256(off + sizeof(uint32_t) * (size_t)B * C * NSUB);
+  pl.off_subK = off;  // target sub-block sums: every position's with a truncated draft, else the bonus's
+  off = align256(off + sizeof(uint32_t) * (size_t)B * (topk > 0 ? K + 1 : 1) * C * NSUB);
   pl.off_subR = off;
   off = align256(off + sizeof(uint32_t) * (size_t)B * C * NSUB);
   if (topk > 0) {
@@ -2030,7 +2052,8 @@ int resident_groups(const void* kernel, size_t lds) {
 // Finishing grid: B work-groups (one per row) plus the largest number that
 // serve sampling rows past their first, over every count of sampling rows
 // the batch may hold (the kernel counts them).  Remembered per shape.
-int finish_grid(int B, int C, int resident) {
+int finish_grid(int B, int C, int resident, int topk) {
+  if (topk > 0) return B;  // one work-group per row
   if (B > FINISH_COUNT_MAX) return B * finish_groups(B, C, resident);  // rows not counted: all sample
   struct Entry {
     int B, C, resident, grid;
@@ -2066,7 +2089,7 @@ int launch_typed(const Args& a, size_t lds, size_t merge_lds, hipStream_t st, hi
   void (*const fk)(Args) = a.cache ? finish_kernel<ET, AL, true> : finish_kernel<ET, AL, false>;
   Args af = a;
   af.resident = resident_groups(reinterpret_cast<const void*>(fk), lds);
-  return launch(fk, finish_grid(a.B, a.C, af.resident), lds, st, ev ? ev + 4 : nullptr, af);
+  return launch(fk, finish_grid(a.B, a.C, af.resident, a.topk), lds, st, ev ? ev + 4 : nullptr, af);
 }
 
 struct RelaxedRule {
@@ -2161,8 +2184,8 @@ int make_ee_plan(int B, int K, int V, int dtype, int topk, EEPlan& pl) {
   off = align256(off + 2 * sizeof(unsigned) * (size_t)B);
   pl.off_part = off;
   off = align256(off + 4 * sizeof(uint32_t) * (size_t)B * S * C);
-  pl.off_subK = off;
-  off = align256(off + sizeof(uint32_t) * (size_t)B * C * NSUB);
+  pl.off_subK = off;  // target sub-block sums: every position's with a truncated draft, else the bonus's
+  off = align256(off + sizeof(uint32_t) * (size_t)B * (topk > 0 ? K + 1 : 1) * C * NSUB);
   pl.off_subR = off;
   off = align256(off + sizeof(uint32_t) * (size_t)B * C * NSUB);
   if (topk > 0) {

@@ -37,7 +37,7 @@ struct TreeArgs {
   int32_t* onodes;           // [B, N]
   int32_t* nacc;             // [B]
   uint32_t* part;            // [B, 2N, C, 4] chunk partials {max | argmax value, sum, argmax id, 0}
-  uint32_t* subK;            // [B, N, C, NSUB] leaf target sub-block sums (vs chunk max)
+  uint32_t* subK;            // [B, N, C, NSUB] target sub-block sums (vs chunk max): leaves', every node's when sparse
   uint32_t* subR;            // [B, N, C, NSUB] published residual sub-block sums, one set per pass
   unsigned* claim;           // [B] residual-pass tickets handed out
   unsigned* leave;           // [B] work-groups of the row that have finished
@@ -115,8 +115,9 @@ __device__ __forceinline__ void tree_slot_stats(const TreeArgs& a, int b, int no
 #pragma unroll
   for (int j = 1; j < NV_TILE; ++j) zl += zj[j];
   const float z = block_sum(zl, shf);
-  if (!is_draft && kids == 0) {
-    // A leaf: sub-block sums of its target for a bonus draw there.
+  if (!is_draft && (kids == 0 || a.topk > 0)) {
+    // A leaf: sub-block sums of its target for a bonus draw there; with a
+    // truncated draft every node's, for its residuals' mass.
 #pragma unroll
     for (int j = 0; j < NV_TILE; ++j) {
       const float v = wave_sum(zj[j]);
@@ -482,62 +483,6 @@ __device__ __forceinline__ int tree_load_kept(const TreeArgs& a, const TreeRow& 
   return nkept;
 }
 
-// Sparse drafts: sub-block sums of max(0, p_v - c q~_v) over one chunk (all
-// threads), as spec_verify's sparse residual: the sum of p over the
-// sub-block less, at its kept ids, min(p, c q~).  Only the target is read.
-template <typename ET, bool ALIGNED>
-__device__ __forceinline__ void tree_chunk_residual_sparse(const TreeArgs& a, const TreeRow& tr, int b, int v,
-                                                           int chunk, float* dst, const int* kid, const float* kq,
-                                                           float* kcorr, int nkept) {
-  constexpr int VEC = Tr<ET>::VEC;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const float s = tr.s;
-  const float MSt = mul_rn(tr.M[v], s), rZt = 1.f / tr.Z[v];
-  const int lo = chunk * a.CS;
-  const int len = min(a.CS, a.V - lo);
-  const ET* trow = tree_row<ET>(a, false, b, v);
-  u32x4 rt[NV_TILE];
-  load_tile<ET, ALIGNED, NV_TILE, false>(trow, lo, len, rt);
-  for (int j = t; j < nkept; j += WG) {
-    const int id = kid[j];
-    float cv = 0.f;
-    if (id >= lo && id < lo + len) {
-      const float pv = exp2_fast(fmaf(Tr<ET>::load1(trow + id), s, -MSt)) * rZt;
-      cv = fminf(pv, kq[j]);
-    }
-    kcorr[j] = cv;
-  }
-#pragma unroll
-  for (int j = 0; j < NV_TILE; ++j) {
-    float w0 = 0.f, w1 = 0.f;
-#pragma unroll
-    for (int k = 0; k < VEC; k += 2) {
-      w0 += exp2_fast(fmaf(Tr<ET>::at(rt[j], k), s, -MSt)) * rZt;
-      w1 += exp2_fast(fmaf(Tr<ET>::at(rt[j], k + 1), s, -MSt)) * rZt;
-    }
-    const float sum = wave_sum(w0 + w1);
-    if (lane == 0) dst[j * NWAVE + wave] = sum;
-  }
-  __syncthreads();
-  if (t < NSUB) {
-    // Sub-block t holds the ids lo + [t, t+1) * 64 * VEC: a contiguous run of
-    // the sorted kept list, summed in list order.
-    auto lower = [&](int x) {
-      int l0 = 0, h0 = nkept;
-      while (l0 < h0) {
-        const int mid = (l0 + h0) >> 1;
-        if (kid[mid] < x) l0 = mid + 1; else h0 = mid;
-      }
-      return l0;
-    };
-    const int j0 = lower(lo + t * 64 * VEC), j1 = lower(lo + (t + 1) * 64 * VEC);
-    float cs = 0.f;
-    for (int j = j0; j < j1; ++j) cs += kcorr[j];
-    dst[t] = fmaxf(0.f, dst[t] - cs);
-  }
-  __syncthreads();
-}
-
 // Sub-block sums of max(0, p_v - c q_v) over one chunk (all threads); the 32
 // sums go to dst[0..NSUB).
 template <typename ET, bool ALIGNED>
@@ -671,7 +616,49 @@ __global__ __launch_bounds__(WG) void tree_finish_kernel(TreeArgs a) {
   int pass = 0;            // passes applied to the walk so far
   unsigned ticket = NONE;  // held ticket
   bool ok = true;
-  for (;;) {
+  if (sparse) {
+    // A truncated draft: a pass needs no logits but the target's at the
+    // kept ids (sparse_residual), so the chunk-0 work-group makes every pass
+    // and the draw alone; the others only leave.
+    if (c == 0) {
+      int nk = 0;
+      for (;;) {
+        const int v = tr.v;
+        nk = tree_load_kept(a, tr, b, v, tr.c, kid, kq);
+        const float MSt = mul_rn(tr.M[v], s), rZt = 1.f / tr.Z[v];
+        const uint32_t* gsub = a.subK + ((size_t)b * N + v) * C * NSUB;
+        sparse_residual<ET>(
+            tree_row<ET>(a, false, b, v), a.V, C, a.CS, s, MSt, rZt, kid, kq, nk, kcorr,
+            [&](int cc, int u) { return __uint_as_float(gsub[cc * NSUB + u]); },
+            [&](int cc) { return __uint_as_float(pw[((size_t)v * C + cc) * 4]); },
+            [&](int i, float r) { csub[i] = r; });
+        if (wave == 0) {
+          float S;
+          tree_draw<ET, ALIGNED>(a, tr, pw, csub, b, v, W_RESID, tr.c, -1.f, &S);
+          if (lane == 0) s_W = S;
+        }
+        __syncthreads();
+        if (t == 0) {
+          if (s_W == 0.f)  // only through rounding: draw from the node's target
+            tr.status = W_FALLBACK;
+          else
+            tree_walk(tr, N, a.V, tr.v, tr.j, tr.c, s_W, probe);
+        }
+        __syncthreads();
+        if (tr.status != W_PASS) break;
+      }
+      // A residual draw uses the last pass's sums and kept list (its node
+      // and scale are the walk's).
+      if (wave == 0) {
+        float S;
+        const bool resid = tr.status == W_RESID;
+        const int x = tree_draw<ET, ALIGNED>(a, tr, pw, csub, b, tr.v, tr.status, tr.c, tr.u[0], &S,
+                                             resid ? kid : nullptr, kq, resid ? nk : 0);
+        emit(x, S);
+      }
+    }
+  }
+  for (; !sparse;) {
     if (ticket == NONE) {
       if (t == 0) s_ticket = __hip_atomic_fetch_add(a.claim + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __syncthreads();
@@ -681,12 +668,7 @@ __global__ __launch_bounds__(WG) void tree_finish_kernel(TreeArgs a) {
     if (tp == pass) {
       // A chunk of the current pass: its sums of max(0, p_v - c q_v).
       const int tc = (int)(ticket % (unsigned)C);
-      if (sparse) {
-        const int nk = tree_load_kept(a, tr, b, tr.v, tr.c, kid, kq);
-        tree_chunk_residual_sparse<ET, ALIGNED>(a, tr, b, tr.v, tc, shsub, kid, kq, kcorr, nk);
-      } else {
-        tree_chunk_residual<ET, ALIGNED>(a, tr, b, tr.v, tr.c, tc, shsub);
-      }
+      tree_chunk_residual<ET, ALIGNED>(a, tr, b, tr.v, tr.c, tc, shsub);
       if (t < NSUB) pub_f32(subR_row + ((size_t)pass * C + tc) * NSUB + t, shsub[t]);
       ticket = NONE;
       continue;
@@ -718,13 +700,10 @@ __global__ __launch_bounds__(WG) void tree_finish_kernel(TreeArgs a) {
       a.onodes[(size_t)b * N + i] = -1;
     }
     if (t == 0) a.nacc[b] = -1;
-  } else if (ticket == (unsigned)pass * (unsigned)C) {
-    // A sparse residual draw needs the node's kept list (scaled by c).
-    const int nk = (sparse && tr.status == W_RESID) ? tree_load_kept(a, tr, b, tr.v, tr.c, kid, kq) : 0;
+  } else if (!sparse && ticket == (unsigned)pass * (unsigned)C) {
     if (wave == 0) {
       float S;
-      const int x = tree_draw<ET, ALIGNED>(a, tr, pw, csub, b, tr.v, tr.status, tr.c, tr.u[0], &S,
-                                           nk ? kid : nullptr, kq, nk);
+      const int x = tree_draw<ET, ALIGNED>(a, tr, pw, csub, b, tr.v, tr.status, tr.c, tr.u[0], &S);
       emit(x, S);
     }
   }
