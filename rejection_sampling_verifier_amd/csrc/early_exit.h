@@ -234,6 +234,14 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4))) void ea
   unsigned base = 0;       // first ticket of the current stage
   unsigned ticket = NONE;  // held ticket
   bool ok = true;
+  // A truncated draft's later stages hold the target only, and every
+  // sampling row needs position i + 1's statistics once it accepts at i.
+  // A work-group holding a ticket of the next stage computes that chunk
+  // before it collects the current stage (one stage ahead at most), so the
+  // next stage's loads overlap the current decision.  `ahead`: the held
+  // ticket's chunk is computed; `went_ahead`: this work-group published a
+  // chunk that may never be collected.
+  bool ahead = false, went_ahead = false;
   // Tickets of the current stage: one per chunk and slot (a sampling
   // position below K has a target and a draft slot; with a truncated draft
   // position 0 is computed already and later positions hold the target only).
@@ -260,6 +268,13 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4))) void ea
       __syncthreads();  // the chunk's shared scratch is reused by the next one
       ticket = NONE;
       continue;
+    }
+    if (SPARSE && sparse && phase == STATS && !ahead && pos < K && ticket - base - size < (unsigned)C) {
+      // A ticket of the next stage (position pos + 1, target only): its
+      // chunk is the same whatever the current decision.
+      ee_stats_chunk<ET, ALIGNED>(a, b, pos + 1, (int)(ticket - base - size), false, false, s, shf, shi, shsub);
+      __syncthreads();
+      ahead = went_ahead = true;
     }
     // Every chunk of the current stage has been handed out: collect it.
     if (phase == STATS) {
@@ -348,6 +363,11 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4))) void ea
     }
     if (phase == DONE) break;
     size = stage_size();
+    if (ahead) {
+      // The held ticket is in the new current stage and already computed.
+      ahead = false;
+      ticket = NONE;
+    }
   }
   if (!ok) {
     write_failed_row(a, b);
@@ -385,12 +405,17 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4))) void ea
     }
   }
   // The last work-group of the row to finish clears its published words.
+  // A chunk computed ahead may be one nobody collects: its stores complete
+  // before this work-group counts itself, so the clear comes after them.
+  if (went_ahead) wait_vmem();
   __syncthreads();
   if (t == 0)
     s_ticket = __hip_atomic_fetch_add(a.leave + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)C - 1u;
   __syncthreads();
   if (!s_ticket) return;
-  const int last = ok ? pos : K;  // positions whose words may have been published
+  // Positions whose words may have been published (with a truncated
+  // draft, one past the last decision: a chunk computed ahead).
+  const int last = ok ? (SPARSE && sparse ? min(pos + 1, K) : pos) : K;
   for (int i = t; i < (last + 1) * C * 4; i += WG) clear_word(part_words(a, b, 0, 0) + i);
   if (!greedy || !ok)
     for (int i = t; i < min(last + 1, K) * C * 4; i += WG) clear_word(part_words(a, b, K + 1, 0) + i);
