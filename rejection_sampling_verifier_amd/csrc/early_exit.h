@@ -193,7 +193,7 @@ __device__ __forceinline__ void ee_merge_slot(const Args& a, RowShared& rs, cons
 template <typename ET, bool ALIGNED, bool SPARSE>
 __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4))) void early_exit_kernel(Args a) {
   // Dynamic LDS: [(2K+1) * C * 4] decoded words, [C * NSUB] sums, then for a
-  // sparse draft [topk] kept ids, logits, q~ values and corrections.
+  // sparse draft [topk] kept ids, q~ values and corrections.
   extern __shared__ __align__(16) uint32_t ee_cache[];
   __shared__ RowShared rs;
   __shared__ float shf[NWAVE];
@@ -210,15 +210,17 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4))) void ea
   uint32_t* pw = ee_cache;
   uint32_t* sub = ee_cache + (size_t)S * C * 4;
   int* kid = reinterpret_cast<int*>(sub + (size_t)C * NSUB);
-  float* kl = reinterpret_cast<float*>(kid + a.topk);
-  float* kq = kl + a.topk;
+  float* kq = reinterpret_cast<float*>(kid + a.topk);
   float* kcorr = kq + a.topk;
-  __shared__ float4 s_qs;  // sparse draft: {max kept logit, Z_q, q~(d), kept count} of the current position
+  // Sparse draft: every position's {max kept logit, Z_q, q~(d), kept count},
+  // loaded once; the kept list is read by the drawer only.
+  __shared__ float4 s_qst[SV_MAX_K];
   const float T = a.temp[b];
   const bool greedy = !is_sampling_temperature(T);
   const bool sparse = SPARSE && !greedy;
   const float s = greedy ? 0.f : LOG2E / T;
   if (t < K) rs.tok[t] = a.tok[(size_t)b * K + t];
+  if (SPARSE && sparse && t < K) s_qst[t] = a.qstat[(size_t)b * K + t];
   if (t == 0) {
     rs.uK = a.uni[(size_t)b * (K + 1) + K];
     rs.greedy = greedy;
@@ -295,23 +297,10 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4))) void ea
                         wall_clock64() + WAIT_TICKS);
       }
       if (!ok) break;
-      if constexpr (SPARSE) if (sparse && pos < K) {
-        // The position's selection, made by the merge kernel.
-        const size_t slot = (size_t)b * K + pos;
-        if (t == 0) s_qs = a.qstat[slot];
-        for (int j = t; j < a.topk; j += WG) {
-          const uint2 e = a.kept[slot * a.topk + j];
-          kid[j] = (int)e.x;
-          kl[j] = __uint_as_float(e.y);
-        }
-        __syncthreads();
-        const float4 qs = s_qs;
-        const float MSq = mul_rn(qs.x, s), rZq = 1.f / qs.y;
-        for (int j = t; j < (int)qs.w; j += WG) kq[j] = exp2_fast(fmaf(kl[j], s, -MSq)) * rZq;
-        if (t == 0) {
-          rs.M[K + 1 + pos] = qs.x;
-          rs.Z[K + 1 + pos] = qs.y;
-        }
+      if constexpr (SPARSE) if (sparse && pos < K && t == 0) {
+        // The position's selection statistics, made by the merge kernel.
+        rs.M[K + 1 + pos] = s_qst[pos].x;
+        rs.Z[K + 1 + pos] = s_qst[pos].y;
       }
       if (wave == 0) ee_merge_slot(a, rs, pw, pos, greedy, s);
       if (wave == 1 && draft) ee_merge_slot(a, rs, pw, K + 1 + pos, greedy, s);
@@ -330,7 +319,7 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4))) void ea
               const float lt = __uint_as_float(pw[((size_t)pos * C + cd) * 4 + 3]);
               p = exp2_fast(fmaf(lt, s, -mul_rn(rs.M[pos], s))) / rs.Z[pos];
               if (sparse) {
-                q = s_qs.z;  // q~(d) of the truncated draft
+                q = s_qst[pos].z;  // q~(d) of the truncated draft
               } else {
                 const float lq = __uint_as_float(pw[((size_t)(K + 1 + pos) * C + cd) * 4 + 3]);
                 q = exp2_fast(fmaf(lq, s, -mul_rn(rs.M[K + 1 + pos], s))) / rs.Z[K + 1 + pos];
@@ -387,10 +376,17 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4))) void ea
       const float rZq = n < K ? 1.f / rs.Z[K + 1 + n] : 0.f;
       const RowView<true> view{pw, sub, true};
       if constexpr (SPARSE) {
-        const int nkept = sparse && n < K ? (int)s_qs.w : 0;
+        const int nkept = sparse && n < K ? (int)s_qst[n].w : 0;
         if (sparse && n < K) {
-          // The residual's sub-block sums from position n's sums (in `sub`)
-          // and its kept list, in place.
+          // Position n's kept list (ids and q~ values), then the residual's
+          // sub-block sums from its sums (in `sub`) and the list, in place.
+          const uint2* kept = a.kept + ((size_t)b * K + n) * a.topk;
+          for (int j = t; j < nkept; j += WG) {
+            const uint2 e = kept[j];
+            kid[j] = (int)e.x;
+            kq[j] = exp2_fast(fmaf(__uint_as_float(e.y), s, -MSq)) * rZq;
+          }
+          __syncthreads();
           float* R = reinterpret_cast<float*>(sub);
           sparse_residual<ET>(
               target_row<ET>(a, b, n), a.V, C, a.CS, s, MSt, rZt, kid, kq, nkept, kcorr,

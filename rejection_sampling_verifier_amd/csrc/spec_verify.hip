@@ -2172,7 +2172,7 @@ int make_ee_plan(int B, int K, int V, int dtype, int topk, EEPlan& pl) {
   if (!vocab_split(V, dtype, C, CS)) return SV_ERR_UNSUPPORTED;
   if ((long long)B * (K + 1) * C > INT_MAX) return SV_ERR_UNSUPPORTED;
   const size_t S = 2 * (size_t)K + 1;
-  const size_t words = S * C * 4 + (size_t)C * NSUB + 4 * (size_t)topk;
+  const size_t words = S * C * 4 + (size_t)C * NSUB + 3 * (size_t)topk;
   if (words > (size_t)EE_MAX_LDS_WORDS) return SV_ERR_UNSUPPORTED;
   pl.C = C;
   pl.CS = CS;
