@@ -388,8 +388,10 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4))) void ea
           }
           __syncthreads();
           float* R = reinterpret_cast<float*>(sub);
+          const ET* trow = target_row<ET>(a, b, n);
           sparse_residual<ET>(
-              target_row<ET>(a, b, n), a.V, C, a.CS, s, MSt, rZt, kid, kq, nkept, kcorr,
+              a.V, C, a.CS, s, MSt, rZt, kid, kq, nkept, kcorr,
+              [&](int j) { return exp2_fast(fmaf(Tr<ET>::load1(trow + kid[j]), s, -MSt)) * rZt; },
               [&](int cc, int u) { return R[cc * NSUB + u]; },
               [&](int cc) { return __uint_as_float(pw[((size_t)n * C + cc) * 4]); },
               [&](int i, float r) { R[i] = r; });

@@ -1091,20 +1091,20 @@ __device__ __forceinline__ SegResult segment_search(const ET* __restrict__ trow,
 // where P(c, u) = sub(c, u) * exp2(fl(m_c s) - MSt) * rZt is the target's
 // mass over the sub-block, from the statistics pass's sum of
 // exp2(fma(l, s, -fl(m_c s))) there and the chunk max m_c.  Only the target
-// logits at the kept ids are read.  kid / kq: the kept ids (ascending) and
-// their q~ values (or c q~ for a tree's later residual), in LDS; corr: LDS
-// scratch of nkept floats.  sub(c, u) and chunk_max(c) read the position's
-// statistics; out(i, R) stores R(c, u) at i = c * NSUB + u.  Sub-block u of
+// at the kept ids is needed: pk(j) = p(kid[j]) = exp2(fma(l, s, -MSt)) * rZt
+// (read from the logits, or kept from an earlier pass).  kid / kq: the kept
+// ids (ascending) and their q~ values (or c q~ for a tree's later residual),
+// in LDS; corr: LDS scratch of nkept floats.  sub(c, u) and chunk_max(c) read
+// the position's statistics; out(i, R) stores R(c, u) at i = c * NSUB + u.  Sub-block u of
 // chunk c holds the ids c * CS + [u, u + 1) * 64 * VEC below the chunk's end
 // min((c + 1) * CS, V).
 // ============================================================================
-template <typename ET, typename SubF, typename MaxF, typename OutF>
-__device__ __forceinline__ void sparse_residual(const ET* __restrict__ trow, int V, int C, int CS, float s, float MSt,
-                                                float rZt, const int* kid, const float* kq, int nkept,
-                                                float* corr, SubF&& sub, MaxF&& chunk_max, OutF&& out) {
+template <typename ET, typename PkF, typename SubF, typename MaxF, typename OutF>
+__device__ __forceinline__ void sparse_residual(int V, int C, int CS, float s, float MSt, float rZt, const int* kid,
+                                                const float* kq, int nkept, float* corr, PkF&& pk, SubF&& sub,
+                                                MaxF&& chunk_max, OutF&& out) {
   constexpr int VEC = Tr<ET>::VEC;
-  for (int j = threadIdx.x; j < nkept; j += WG)
-    corr[j] = fminf(exp2_fast(fmaf(Tr<ET>::load1(trow + kid[j]), s, -MSt)) * rZt, kq[j]);
+  for (int j = threadIdx.x; j < nkept; j += WG) corr[j] = fminf(pk(j), kq[j]);
   __syncthreads();
   auto lower = [&](int x) {
     int l0 = 0, h0 = nkept;
@@ -1849,8 +1849,10 @@ __global__ __launch_bounds__(WG) void finish_kernel(Args a) {
     if (CACHED)
       for (int i = t; i < C * NSUB; i += WG) R[i] = __uint_as_float(sub_words(a, b, n, 0)[i]);
     __syncthreads();
+    const ET* trow = target_row<ET>(a, b, n);
     sparse_residual<ET>(
-        target_row<ET>(a, b, n), a.V, C, a.CS, s, MSt, rZt, kid, kq, nkept, kcorr,
+        a.V, C, a.CS, s, MSt, rZt, kid, kq, nkept, kcorr,
+        [&](int j) { return exp2_fast(fmaf(Tr<ET>::load1(trow + kid[j]), s, -MSt)) * rZt; },
         [&](int c, int u) { return CACHED ? R[c * NSUB + u] : __uint_as_float(sub_words(a, b, n, c)[u]); },
         [&](int c) { return view_part(a, view, b, n, c, 0); },
         [&](int i, float r) {
@@ -2279,7 +2281,7 @@ int make_tree_plan(int B, int N, int V, int dtype, int topk, TreePlan& pl) {
   int C, CS;
   if (!vocab_split(V, dtype, C, CS)) return SV_ERR_UNSUPPORTED;
   if ((long long)B * 2 * N * C > INT_MAX) return SV_ERR_UNSUPPORTED;
-  const size_t words = (size_t)2 * N * C * 4 + (size_t)C * NSUB + 3 * (size_t)topk;
+  const size_t words = (size_t)2 * N * C * 4 + (size_t)C * NSUB + 5 * (size_t)topk;
   if (words > (size_t)TREE_MAX_LDS_WORDS) return SV_ERR_UNSUPPORTED;
   pl.C = C;
   pl.CS = CS;

@@ -223,6 +223,7 @@ struct TreeRow {
   float s;
   int greedy;
   // walk result
+  int nk[MAX_NODES];         // sparse draft: kept count of each node with children
   int status;                // W_PASS, W_LEAF, W_RESID, W_GREEDY, W_FALLBACK
   int v, j, n, x;
   float c, W;
@@ -465,24 +466,6 @@ __device__ __forceinline__ int tree_draw(const TreeArgs& a, const TreeRow& tr, c
   return r.found >= 0 ? r.found : (r.last_pos >= 0 ? r.last_pos : start);
 }
 
-// Sparse drafts: node v's kept list into LDS (all threads): ids ascending in
-// kid, c q~ values in kq.  Returns the kept count.
-__device__ __forceinline__ int tree_load_kept(const TreeArgs& a, const TreeRow& tr, int b, int v, float cscale,
-                                              int* kid, float* kq) {
-  const int N = a.N;
-  const float s = tr.s;
-  const float MSq = mul_rn(tr.M[N + v], s), rZq = cscale / tr.Z[N + v];
-  const int nkept = (int)a.qstat[(size_t)b * N + v].w;
-  const uint2* kept = a.kept + ((size_t)b * N + v) * a.topk;
-  for (int j = threadIdx.x; j < nkept; j += WG) {
-    const uint2 e = kept[j];
-    kid[j] = (int)e.x;
-    kq[j] = exp2_fast(fmaf(__uint_as_float(e.y), s, -MSq)) * rZq;
-  }
-  __syncthreads();
-  return nkept;
-}
-
 // Sub-block sums of max(0, p_v - c q_v) over one chunk (all threads); the 32
 // sums go to dst[0..NSUB).
 template <typename ET, bool ALIGNED>
@@ -534,7 +517,8 @@ __device__ __forceinline__ void tree_chunk_residual(const TreeArgs& a, const Tre
 template <typename ET, bool ALIGNED>
 __global__ __launch_bounds__(WG) void tree_finish_kernel(TreeArgs a) {
   // Dynamic LDS: [2N * C * 4] partial words, [C * NSUB] residual sums, then
-  // for a sparse draft [topk] kept ids, [topk] c q~ values, [topk] corrections.
+  // for a sparse draft [topk] kept ids, [topk] c q~ values, [topk]
+  // corrections, [topk] kept logits and [topk] target probabilities at them.
   extern __shared__ __align__(16) uint32_t tcache[];
   __shared__ TreeRow tr;
   __shared__ float shsub[NSUB];
@@ -548,6 +532,8 @@ __global__ __launch_bounds__(WG) void tree_finish_kernel(TreeArgs a) {
   int* kid = reinterpret_cast<int*>(csub + (size_t)C * NSUB);
   float* kq = reinterpret_cast<float*>(kid + a.topk);
   float* kcorr = kq + a.topk;
+  float* kl = kcorr + a.topk;
+  float* kp = kl + a.topk;
   float* probe = (c == 0 && a.probes) ? a.probes + (size_t)b * 3 * N : nullptr;
   // The row's partials and scalars in one round of loads.
   const u32x4* src = reinterpret_cast<const u32x4*>(tree_part(a, b, 0, 0));
@@ -579,6 +565,7 @@ __global__ __launch_bounds__(WG) void tree_finish_kernel(TreeArgs a) {
     const float4 q = a.qstat[(size_t)b * N + t];
     tr.M[N + t] = q.x;
     tr.Z[N + t] = q.y;
+    tr.nk[t] = (int)q.w;
   }
   __syncthreads();
   if (t == 0) {
@@ -621,14 +608,31 @@ __global__ __launch_bounds__(WG) void tree_finish_kernel(TreeArgs a) {
     // kept ids (sparse_residual), so the chunk-0 work-group makes every pass
     // and the draw alone; the others only leave.
     if (c == 0) {
-      int nk = 0;
+      int nk = 0, kv = -1;  // the node whose kept list and target probabilities are in LDS
       for (;;) {
         const int v = tr.v;
-        nk = tree_load_kept(a, tr, b, v, tr.c, kid, kq);
         const float MSt = mul_rn(tr.M[v], s), rZt = 1.f / tr.Z[v];
+        if (v != kv) {
+          // Node v's kept ids and logits, and the target's probabilities
+          // there: the same for every pass at the node.
+          nk = tr.nk[v];
+          const uint2* kept = a.kept + ((size_t)b * N + v) * a.topk;
+          const ET* trow = tree_row<ET>(a, false, b, v);
+          for (int j = t; j < nk; j += WG) {
+            const uint2 e = kept[j];
+            kid[j] = (int)e.x;
+            kl[j] = __uint_as_float(e.y);
+            kp[j] = exp2_fast(fmaf(Tr<ET>::load1(trow + e.x), s, -MSt)) * rZt;
+          }
+          kv = v;
+        }
+        // This pass's c q~ at the kept ids.
+        const float MSq = mul_rn(tr.M[N + v], s), rZq = tr.c / tr.Z[N + v];
+        for (int j = t; j < nk; j += WG) kq[j] = exp2_fast(fmaf(kl[j], s, -MSq)) * rZq;
+        __syncthreads();
         const uint32_t* gsub = a.subK + ((size_t)b * N + v) * C * NSUB;
         sparse_residual<ET>(
-            tree_row<ET>(a, false, b, v), a.V, C, a.CS, s, MSt, rZt, kid, kq, nk, kcorr,
+            a.V, C, a.CS, s, MSt, rZt, kid, kq, nk, kcorr, [&](int j) { return kp[j]; },
             [&](int cc, int u) { return __uint_as_float(gsub[cc * NSUB + u]); },
             [&](int cc) { return __uint_as_float(pw[((size_t)v * C + cc) * 4]); },
             [&](int i, float r) { csub[i] = r; });
