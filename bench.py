@@ -103,6 +103,25 @@ def traffic_from_profiles(workload: str, kernel: str = "stats_kernel"):
     return float(m_bytes.group(1))
 
 
+def call_traffic_from_profiles(workload: str):
+    """HBM bytes read and written per spec_verify call (every kernel of the
+    call) from the committed counter summary, if it was taken on the current
+    kernel source."""
+    path = os.path.join(ROOT, "profiles", f"stats_kernel_{workload}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"kernel_source_hash:\s*(\w+)", text)
+    if not m_hash or m_hash.group(1) != kernel_source_hash():
+        return None
+    per = {k: (float(r), float(w)) for k, r, w in
+           re.findall(r"^(\w+_kernel): \d+ dispatches; read ([0-9.]+) B, written ([0-9.]+) B", text, re.M)}
+    if "stats_kernel" not in per or "finish_kernel" not in per:
+        return None
+    return {"read": sum(r for r, _ in per.values()), "written": sum(w for _, w in per.values()),
+            "kernels": sorted(per)}
+
+
 # Threads of the CPU baseline: the host CPU share of one GPU on the
 # measurement machines (16), whatever os.cpu_count() reports there.
 CPU_THREADS = 16
@@ -382,6 +401,8 @@ def main():
         roof_kernel, roof_bytes, roof_ms = "early_exit_kernel", int(rows.sum()) * V * esz, ms_per_step
         achieved = roof_bytes / (roof_ms * 1e-3) / 1e9
     traffic = traffic_from_profiles(f"B{B}K{K}V{V}", roof_kernel)
+    plain = not (args.early_exit or args.kl or rule is not None)
+    call_traffic = call_traffic_from_profiles(f"B{B}K{K}V{V}") if plain else None
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -410,6 +431,16 @@ def main():
                        "bytes": by["m_min"], "ms": round(ms_per_step, 5),
                        "note": "algorithmic bytes of the whole call (every logit it must read once, tokens, "
                                "uniforms, temperatures, outputs) over the per-call time of all its kernels"},
+        # The call's HBM traffic from the committed counter summary (FETCH_SIZE and
+        # WRITE_SIZE of every kernel of the call, calibrated), while the kernel
+        # sources are those it was taken on; null otherwise.
+        "whole_call_counters": None if call_traffic is None else {
+            "read_bytes": round(call_traffic["read"]), "written_bytes": round(call_traffic["written"]),
+            "GBps": round((call_traffic["read"] + call_traffic["written"]) / (ms_per_step * 1e-3) / 1e9, 1),
+            "frac": round((call_traffic["read"] + call_traffic["written"]) / (ms_per_step * 1e-3) / 1e9
+                          / HBM_PEAK_GBPS, 4),
+            "read_over_m_min": round(call_traffic["read"] / by["m_min"], 4),
+            "kernels": call_traffic["kernels"]},
         "ms_per_call_spread": spread,
         "m_min_bytes": by["m_min"],
         "kernel_ms": {"stats_kernel": round(float(stage_ms[0]), 5),

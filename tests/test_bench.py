@@ -1,5 +1,6 @@
 """Host logic of bench.py (CPU only): the algorithmic byte counts behind the
-roofline figure, the guard on counter summaries, and the one-GPU limit."""
+roofline figure, the counter summaries (per kernel and per call) and their
+guard, and the one-GPU limit."""
 
 from __future__ import annotations
 
@@ -64,6 +65,22 @@ def test_counter_summary_is_used_only_for_its_own_kernel_source(tmp_path, monkey
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "fedcba9876543210")
     assert bench.traffic_from_profiles("B1K1V1") is None
     assert bench.traffic_from_profiles("B2K2V2") is None
+
+
+def test_whole_call_counters_sum_every_kernel_of_the_call(tmp_path, monkeypatch):
+    (tmp_path / "profiles").mkdir()
+    (tmp_path / "profiles" / "stats_kernel_B1K1V1_pmc.txt").write_text(
+        "kernel_source_hash: 0123456789abcdef\n"
+        "stats_kernel: 36 dispatches; read 1000 B, written 10 B; VALUBusy 50.0%\n"
+        "hbm_bytes_per_launch: 1010\n"
+        "merge_kernel: 36 dispatches; read 200 B, written 20 B; VALUBusy 40.0%\n"
+        "finish_kernel: 36 dispatches; read 30 B, written 3 B; VALUBusy 4.0%\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0123456789abcdef")
+    t = bench.call_traffic_from_profiles("B1K1V1")
+    assert t == {"read": 1230.0, "written": 33.0, "kernels": ["finish_kernel", "merge_kernel", "stats_kernel"]}
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "fedcba9876543210")
+    assert bench.call_traffic_from_profiles("B1K1V1") is None
 
 
 def test_kernel_source_hash_is_stable():
