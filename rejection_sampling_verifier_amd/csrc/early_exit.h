@@ -107,7 +107,7 @@ __device__ __forceinline__ void ee_stats_chunk(const Args& a, int b, int pos, in
       if (lane == 0) shsub[j * NWAVE + wave] = v;
     }
     __syncthreads();
-    if (t < NSUB) pub_f32(sub_words(a, b, pos, c) + t, shsub[t]);
+    if (t < NSUB) pub_f32(uniform_ptr(sub_words(a, b, pos, c)) + t, shsub[t]);
   }
   if (t < 4) {
     uint32_t w = 0u;
@@ -157,7 +157,7 @@ __device__ __forceinline__ void ee_residual_chunk(const Args& a, int b, int n, i
     }
   }
   __syncthreads();
-  if (t < NSUB) pub_f32(a.subR + ((size_t)b * a.C + c) * NSUB + t, shsub[t]);
+  if (t < NSUB) pub_f32(uniform_ptr(a.subR + ((size_t)b * a.C + c) * NSUB) + t, shsub[t]);
 }
 
 // Merge of one slot's decoded chunk words (LDS) by one wave, in the order of
@@ -189,9 +189,13 @@ __device__ __forceinline__ void ee_merge_slot(const Args& a, RowShared& rs, cons
 
 // SPARSE: the instantiation for truncated drafts, whose position-0
 // statistics (plain words) and selections (qstat, kept) were written by the
-// two launches before it.
+// two launches before it.  Four waves per SIMD, two for truncated drafts
+// over rows that are not 16-byte aligned (their element-wise loads need more
+// registers; at four they would spill).  Stages go by ticket, so nothing
+// here depends on how many work-groups are resident.
 template <typename ET, bool ALIGNED, bool SPARSE>
-__global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4))) void early_exit_kernel(Args a) {
+__global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(SPARSE && !ALIGNED ? 2 : 4))) void
+early_exit_kernel(Args a) {
   // Dynamic LDS: [(2K+1) * C * 4] decoded words, [C * NSUB] sums, then for a
   // sparse draft [topk] kept ids, q~ values and corrections.
   extern __shared__ __align__(16) uint32_t ee_cache[];

@@ -131,6 +131,16 @@ __device__ __forceinline__ void pub_u32(uint32_t* p, uint32_t bits) {
   __hip_atomic_store(p, ~bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void pub_f32(uint32_t* p, float v) { pub_u32(p, __float_as_uint(v)); }
+// A uniform pointer taken into scalar registers where it is used: a store to
+// uniform_ptr(base) + lane is then addressed as a scalar base plus a 32-bit
+// lane offset, instead of the compiler keeping base's lane-dependent part as
+// a 64-bit address live across a loop.
+__device__ __forceinline__ uint32_t* uniform_ptr(uint32_t* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<uint32_t*>(((uint64_t)hi << 32) | lo);
+}
 __device__ __forceinline__ uint32_t peek(const uint32_t* p) {
   return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -1384,7 +1394,9 @@ struct MixedCands {
 constexpr int RADIX_BITS = 11;
 constexpr int RADIX_BINS = 1 << RADIX_BITS;  // 2048 bins, 8 per thread
 
-template <typename Src>
+// REREAD: the bins are read again after the block scan rather than held
+// through it (eight fewer live registers, for a kernel bound to 64).
+template <bool REREAD, typename Src>
 __device__ uint64_t select_threshold(const Src& src, int kk, uint32_t* sh32, float* red, int* ired,
                                      uint32_t* hist, float* vmax) {
   __shared__ int s_digit, s_above, s_count;
@@ -1422,7 +1434,9 @@ __device__ uint64_t select_threshold(const Src& src, int kk, uint32_t* sh32, flo
     any_or |= ((uint64_t)sh32[3 * NWAVE + w] << 32) | sh32[2 * NWAVE + w];
     mx = fmaxf(mx, red[w]);
   }
-  *vmax = mx;
+  // Uniform: taken into a scalar register here, so that the compiler does
+  // not keep the four partial maxima live (and spilled) through the windows.
+  *vmax = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(mx)));
   uint64_t var = all_and ^ any_or;  // bits that differ between candidates
   uint64_t tau = all_and;           // constant bits; variable bits start at 0
   int need = kk;
@@ -1450,12 +1464,13 @@ __device__ uint64_t select_threshold(const Src& src, int kk, uint32_t* sh32, flo
     int above = block_count_scan(local, ired, tot);
 #pragma unroll
     for (int i = PER - 1; i >= 0; --i) {
-      if (above < need && need <= above + (int)h[i]) {
+      const int hi = REREAD ? (int)hist[g * PER + i] : (int)h[i];
+      if (above < need && need <= above + hi) {
         s_digit = g * PER + i;
         s_above = above;
-        s_count = (int)h[i];
+        s_count = hi;
       }
-      above += (int)h[i];
+      above += hi;
     }
 #pragma unroll
     for (int i = 0; i < PER; ++i) hist[g * PER + i] = 0u;  // ready for the next window
@@ -1512,7 +1527,7 @@ __device__ __forceinline__ bool lists_hold_top(const int* gcnt, int C, uint64_t 
 // recorded (-1 for none).  Writes {max kept logit, Z_q, q~(d), kk} to qstat
 // and the kept ids and logits in ascending id order to kept; returns kk,
 // the number of kept ids.
-template <typename ET>
+template <typename ET, bool REREAD = false>
 __device__ __forceinline__ int merge_body(const Args& a, int b, int i, int d) {
   __shared__ __align__(16) uint64_t sel[SV_MAX_TOPK + 2];  // kept composites (+ a zero pad entry)
   __shared__ uint64_t ovf[MERGE_OVF];
@@ -1598,19 +1613,19 @@ __device__ __forceinline__ int merge_body(const Args& a, int b, int i, int d) {
     rc.ovf = ovf;
     rc.novf = s_novf;
     if (rc.novf <= MERGE_OVF) {
-      thr = select_threshold(rc, kk, sh32, red, ired, hist, &m);
+      thr = select_threshold<REREAD>(rc, kk, sh32, red, ired, hist, &m);
       held = lists_hold_top(gcnt, C, thr, ired);
       if (held) z = take_kept(rc, thr, d, s, mul_rn(m, s), sel, &s_n, &s_ld);
     } else {
       const ListCands<ET> lc{g, gcnt, C, a.CS, a.cstride};
-      thr = select_threshold(lc, kk, sh32, red, ired, hist, &m);
+      thr = select_threshold<REREAD>(lc, kk, sh32, red, ired, hist, &m);
       held = lists_hold_top(gcnt, C, thr, ired);
       if (held) z = take_kept(lc, thr, d, s, mul_rn(m, s), sel, &s_n, &s_ld);
     }
   } else {
     __syncthreads();
     const ListCands<ET> lc{g, gcnt, C, a.CS, a.cstride};
-    thr = select_threshold(lc, kk, sh32, red, ired, hist, &m);
+    thr = select_threshold<REREAD>(lc, kk, sh32, red, ired, hist, &m);
     held = lists_hold_top(gcnt, C, thr, ired);
     if (held) z = take_kept(lc, thr, d, s, mul_rn(m, s), sel, &s_n, &s_ld);
   }
@@ -1622,7 +1637,7 @@ __device__ __forceinline__ int merge_body(const Args& a, int b, int i, int d) {
     // global one).  The largest logit is always listed, so m stands.
     const MixedCands<ET> mc{g, gcnt, draft_row<ET>(a, b, i), C, a.CS, a.V, a.cstride, (uint32_t)(thr >> 32)};
     float m2;
-    thr = select_threshold(mc, kk, sh32, red, ired, hist, &m2);
+    thr = select_threshold<REREAD>(mc, kk, sh32, red, ired, hist, &m2);
     z = take_kept(mc, thr, d, s, mul_rn(m, s), sel, &s_n, &s_ld);
   }
   const float Z = block_sum(z, red);  // also orders sel[] and s_ld before their reads
@@ -1662,13 +1677,13 @@ __device__ __forceinline__ int merge_body(const Args& a, int b, int i, int d) {
   return kk;
 }
 
-// Eight waves per SIMD (64 VGPRs, a few spills): the 2048 work-groups of a
+// Eight waves per SIMD (64 VGPRs, no spills): the 2048 work-groups of a
 // 256-row, 8-draft batch are resident at once.
 template <typename ET>
 __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(8, 8))) void merge_kernel(Args a) {
   const int i = blockIdx.x % a.K, b = blockIdx.x / a.K;
   if (!is_sampling_temperature(a.temp[b])) return;
-  merge_body<ET>(a, b, i, a.tok[(size_t)b * a.K + i]);
+  merge_body<ET, true>(a, b, i, a.tok[(size_t)b * a.K + i]);
 }
 
 // Finishing work-groups that take part per row, G <= C: each takes m chunks,
