@@ -1308,7 +1308,7 @@ __device__ __forceinline__ void final_draw(const Args& a, int b, int n, float s,
 // order, the max kept logit, Z_q = sum over kept of exp2(fma(l, s, -fl(max*s)))
 // (summed in id order) and q~(d_i).
 //
-// The kk-th largest composite is found by a radix select with 11-bit
+// The kk-th largest composite is found by a radix select with 10-bit
 // windows over the bits in which the candidates differ.  Composites are
 // distinct, so exactly kk candidates are at or above it.  The candidates are
 // held in registers (one per list and lane) when the lists are few enough,
@@ -1384,19 +1384,18 @@ struct MixedCands {
 
 // Threshold composite: exactly kk candidates are >= it.  A radix select over
 // the bits in which the candidates differ: the highest undecided differing
-// bit starts an 11-bit window, the window's digits of the candidates that
+// bit starts a 10-bit window, the window's digits of the candidates that
 // match the prefix decided so far are counted in an LDS histogram, and the
 // digit at which the count of larger candidates reaches kk is appended to
 // the prefix.  Bits equal in every candidate are taken as they are.  It stops
 // once every candidate with the chosen digit is needed (usually after the
 // first window; ties in value continue into the id bits).  Also returns the
 // largest candidate value (the largest kept logit) in *vmax.
-constexpr int RADIX_BITS = 11;
-constexpr int RADIX_BINS = 1 << RADIX_BITS;  // 2048 bins, 8 per thread
+constexpr int RADIX_BITS = 10;  // wider windows need fewer passes, but clearing and
+                                // scanning their bins costs more LDS traffic per pass
+constexpr int RADIX_BINS = 1 << RADIX_BITS;  // 1024 bins, 4 per thread
 
-// REREAD: the bins are read again after the block scan rather than held
-// through it (eight fewer live registers, for a kernel bound to 64).
-template <bool REREAD, typename Src>
+template <typename Src>
 __device__ uint64_t select_threshold(const Src& src, int kk, uint32_t* sh32, float* red, int* ired,
                                      uint32_t* hist, float* vmax) {
   __shared__ int s_digit, s_above, s_count;
@@ -1464,13 +1463,12 @@ __device__ uint64_t select_threshold(const Src& src, int kk, uint32_t* sh32, flo
     int above = block_count_scan(local, ired, tot);
 #pragma unroll
     for (int i = PER - 1; i >= 0; --i) {
-      const int hi = REREAD ? (int)hist[g * PER + i] : (int)h[i];
-      if (above < need && need <= above + hi) {
+      if (above < need && need <= above + (int)h[i]) {
         s_digit = g * PER + i;
         s_above = above;
-        s_count = hi;
+        s_count = (int)h[i];
       }
-      above += hi;
+      above += (int)h[i];
     }
 #pragma unroll
     for (int i = 0; i < PER; ++i) hist[g * PER + i] = 0u;  // ready for the next window
@@ -1527,12 +1525,12 @@ __device__ __forceinline__ bool lists_hold_top(const int* gcnt, int C, uint64_t 
 // recorded (-1 for none).  Writes {max kept logit, Z_q, q~(d), kk} to qstat
 // and the kept ids and logits in ascending id order to kept; returns kk,
 // the number of kept ids.
-template <typename ET, bool REREAD = false>
+template <typename ET>
 __device__ __forceinline__ int merge_body(const Args& a, int b, int i, int d) {
   __shared__ __align__(16) uint64_t sel[SV_MAX_TOPK + 2];  // kept composites (+ a zero pad entry)
   __shared__ uint64_t ovf[MERGE_OVF];
-  __shared__ uint32_t hist[RADIX_BINS];  // radix histogram, then the ranks of the kept entries
-  static_assert(RADIX_BINS >= SV_MAX_TOPK, "ranks reuse the histogram");
+  __shared__ uint32_t hist[RADIX_BINS > SV_MAX_TOPK ? RADIX_BINS : SV_MAX_TOPK];  // radix histogram, then the
+                                                                             // ranks of the kept entries
   int* rank = reinterpret_cast<int*>(hist);
   __shared__ uint32_t sh32[4 * NWAVE];
   __shared__ float red[NWAVE];
@@ -1613,19 +1611,19 @@ __device__ __forceinline__ int merge_body(const Args& a, int b, int i, int d) {
     rc.ovf = ovf;
     rc.novf = s_novf;
     if (rc.novf <= MERGE_OVF) {
-      thr = select_threshold<REREAD>(rc, kk, sh32, red, ired, hist, &m);
+      thr = select_threshold(rc, kk, sh32, red, ired, hist, &m);
       held = lists_hold_top(gcnt, C, thr, ired);
       if (held) z = take_kept(rc, thr, d, s, mul_rn(m, s), sel, &s_n, &s_ld);
     } else {
       const ListCands<ET> lc{g, gcnt, C, a.CS, a.cstride};
-      thr = select_threshold<REREAD>(lc, kk, sh32, red, ired, hist, &m);
+      thr = select_threshold(lc, kk, sh32, red, ired, hist, &m);
       held = lists_hold_top(gcnt, C, thr, ired);
       if (held) z = take_kept(lc, thr, d, s, mul_rn(m, s), sel, &s_n, &s_ld);
     }
   } else {
     __syncthreads();
     const ListCands<ET> lc{g, gcnt, C, a.CS, a.cstride};
-    thr = select_threshold<REREAD>(lc, kk, sh32, red, ired, hist, &m);
+    thr = select_threshold(lc, kk, sh32, red, ired, hist, &m);
     held = lists_hold_top(gcnt, C, thr, ired);
     if (held) z = take_kept(lc, thr, d, s, mul_rn(m, s), sel, &s_n, &s_ld);
   }
@@ -1637,7 +1635,7 @@ __device__ __forceinline__ int merge_body(const Args& a, int b, int i, int d) {
     // global one).  The largest logit is always listed, so m stands.
     const MixedCands<ET> mc{g, gcnt, draft_row<ET>(a, b, i), C, a.CS, a.V, a.cstride, (uint32_t)(thr >> 32)};
     float m2;
-    thr = select_threshold<REREAD>(mc, kk, sh32, red, ired, hist, &m2);
+    thr = select_threshold(mc, kk, sh32, red, ired, hist, &m2);
     z = take_kept(mc, thr, d, s, mul_rn(m, s), sel, &s_n, &s_ld);
   }
   const float Z = block_sum(z, red);  // also orders sel[] and s_ld before their reads
@@ -1683,7 +1681,7 @@ template <typename ET>
 __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(8, 8))) void merge_kernel(Args a) {
   const int i = blockIdx.x % a.K, b = blockIdx.x / a.K;
   if (!is_sampling_temperature(a.temp[b])) return;
-  merge_body<ET, true>(a, b, i, a.tok[(size_t)b * a.K + i]);
+  merge_body<ET>(a, b, i, a.tok[(size_t)b * a.K + i]);
 }
 
 // Finishing work-groups that take part per row, G <= C: each takes m chunks,
