@@ -70,9 +70,13 @@ namespace {
 // Waves per SIMD of the statistics kernels (a cap: more in flight measured
 // slower), for dense drafts and for truncated ones, whose draft work-groups
 // hold their slots longer (candidate filter and list stores).  The tree's
-// statistics kernel keeps STATS_WAVES: at five it spills.
+// statistics kernel keeps STATS_WAVES: at five it spills.  Early exit's first
+// launch over a truncated draft (position 0's target, then draft slots only:
+// eight of every nine work-groups run the candidate filter) is fastest at
+// six.
 constexpr int STATS_WAVES = 4;
 constexpr int STATS_WAVES_TOPK = 5;
+constexpr int EE_FIRST_WAVES = 6;
 constexpr int NV_TILE = SV_NV_TILE;        // 16-byte vectors per thread per chunk
 constexpr int NSUB = NV_TILE * NWAVE;      // sub-blocks per chunk (one wave x one vector row)
 constexpr int MAX_C = 2048;                // vocabulary chunks per position
@@ -2225,7 +2229,7 @@ int make_ee_plan(int B, int K, int V, int dtype, int topk, EEPlan& pl) {
 template <typename ET, bool AL>
 int launch_early_exit(const Args& a, size_t lds, hipStream_t st) {
   if (a.topk > 0) {
-    int rc = launch(ee_first_kernel<ET, AL, STATS_WAVES_TOPK>, a.B * (a.K + 1) * a.C, 0, st, nullptr, a);
+    int rc = launch(ee_first_kernel<ET, AL, EE_FIRST_WAVES>, a.B * (a.K + 1) * a.C, 0, st, nullptr, a);
     if (rc == SV_OK) rc = launch(merge_kernel<ET>, a.B * a.K, 0, st, nullptr, a);
     if (rc != SV_OK) return rc;
     return launch(early_exit_kernel<ET, AL, true>, a.B * a.C, lds, st, nullptr, a);
