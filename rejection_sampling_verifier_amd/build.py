@@ -13,6 +13,9 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libspecverify.so")
+# The compiler's per-kernel resource report (registers, spills, scratch, LDS,
+# occupancy) of the last build, written next to the library.
+RESOURCES = os.path.join(PKG, "libspecverify.resources.txt")
 SOURCES = [os.path.join(PKG, "csrc", "spec_verify.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -29,6 +32,7 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I" + os.path.join(ROOT, "include"),
     "-I" + os.path.join(PKG, "csrc"),
+    "-Rpass-analysis=kernel-resource-usage",
 ]
 
 
@@ -42,6 +46,8 @@ def build(verbose: bool = False) -> str:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
     os.replace(tmp, LIB)
+    with open(RESOURCES, "w") as f:
+        f.write(res.stderr)
     return LIB
 
 

@@ -140,10 +140,13 @@ __device__ __forceinline__ void tree_slot_stats(const TreeArgs& a, int b, int no
 // were drawn from).  The target's tile, the temperature and the parents are
 // loaded at once; the draft's loads are issued as soon as the children mask
 // is known and overlap the target's statistics.  Leaves and greedy rows read
-// no draft.
+// no draft.  Four waves per SIMD; three for bf16 rows that are not 16-byte
+// aligned (odd V), whose element-wise loads need one register more than
+// four waves allow.
 // ============================================================================
 template <typename ET, bool ALIGNED>
-__global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(STATS_WAVES, STATS_WAVES)))
+__global__ __launch_bounds__(WG) __attribute__((
+    amdgpu_waves_per_eu(ALIGNED || sizeof(ET) == 4 ? STATS_WAVES : 3, ALIGNED || sizeof(ET) == 4 ? STATS_WAVES : 3)))
 void tree_stats_kernel(TreeArgs a) {
   const int N = a.N;
   const int c = blockIdx.x % a.C;
