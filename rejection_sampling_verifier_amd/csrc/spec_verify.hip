@@ -1480,9 +1480,9 @@ __device__ uint64_t select_threshold(const Src& src, int kk, uint32_t* sh32, flo
     need -= s_above;
     tau |= (uint64_t)s_digit << lo;
     var &= ~((uint64_t)dmask << lo);
-    const bool done = s_count == need;
-    __syncthreads();  // s_* are rewritten by the next window
-    if (done) break;
+    // No barrier before the next window: s_* are rewritten only after its
+    // first barrier, which every thread reaches after reading them here.
+    if (s_count == need) break;
   }
   return tau;
 }
