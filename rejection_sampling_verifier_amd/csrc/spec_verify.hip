@@ -1510,7 +1510,9 @@ __device__ __forceinline__ float take_kept(const Src& src, uint64_t thr, int d, 
 // Whether every chunk's list reaches down to the union's kk-th largest
 // composite thr: each chunk's bound key (0 for a list holding the chunk's
 // top k) is at most thr's value key.  Uniform over the block; the vote goes
-// through vote[NWAVE] (LDS), which is free again on return.
+// through vote[NWAVE] (LDS), which every thread has read when it returns:
+// the caller must pass a barrier before writing vote again (the merge next
+// writes it inside a selection, after that selection's first barrier).
 __device__ __forceinline__ bool lists_hold_top(const int* gcnt, int C, uint64_t thr, int* vote) {
   const uint32_t key = (uint32_t)(thr >> 32);
   bool ok = true;
@@ -1521,7 +1523,6 @@ __device__ __forceinline__ bool lists_hold_top(const int* gcnt, int C, uint64_t 
   bool all = true;
 #pragma unroll
   for (int w = 0; w < NWAVE; ++w) all &= vote[w] != 0;
-  __syncthreads();
   return all;
 }
 
@@ -1644,15 +1645,15 @@ __device__ __forceinline__ int merge_body(const Args& a, int b, int i, int d) {
   }
   const float Z = block_sum(z, red);  // also orders sel[] and s_ld before their reads
   const float ms = mul_rn(m, s);
-  for (int j = t; j < kk; j += WG) rank[j] = 0;
-  __syncthreads();
   // Rank of each kept composite in id order (~id is larger for lower ids):
   // work items (entry j, block of 64 others) add their counts to rank[j].
-  // Entries are read two at a time (16-byte LDS reads); sel[kk] is zeroed
-  // first so that an odd kk reads a zero (never larger) in its last pair.
-  const int nblk = (kk + 63) / 64;
+  // Entries are read two at a time (16-byte LDS reads); sel[kk] (no kept
+  // entry is written there) is zeroed first so that an odd kk reads a zero
+  // (never larger) in its last pair.
+  for (int j = t; j < kk; j += WG) rank[j] = 0;
   if (t == 0) sel[kk] = 0ull;  // kk < SV_MAX_TOPK + 1 entries: see the declaration
   __syncthreads();
+  const int nblk = (kk + 63) / 64;
   const uint4* s4 = reinterpret_cast<const uint4*>(sel);
   for (int w = t; w < kk * nblk; w += WG) {
     const int j = w % kk, p0 = (w / kk) * 32, p1 = min(p0 + 32, (kk + 1) / 2);
