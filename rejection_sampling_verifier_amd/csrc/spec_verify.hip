@@ -20,16 +20,20 @@
 //      exp2((l - max) * log2(e)/T) -- or, for greedy rows, the chunk argmax.
 //      The chunk holding a position's draft token records that token's
 //      logit; the bonus position also writes 32 sub-block sums for the final
-//      draw.  A truncated draft's chunks write candidate lists instead, and
+//      draw (with a truncated draft every target position does).  A
+//      truncated draft's chunks write candidate lists instead of sums, and
 //      merge_kernel (one work-group per (row, position)) selects exactly.
 //   B. finish_kernel, up to C work-groups per row.  Each loads its row's
 //      partials into LDS in one round of loads, merges them and runs the
 //      first-rejection scan.  Greedy rows and rows that accepted every draft
-//      are completed by the row's work-group 0.  For a rejected row, the
-//      row's first G work-groups re-read target and draft logits of the
-//      rejected position, chunk j, j + G, ... each, and publish 32 sub-block
-//      sums of max(0, p_n - q_n) per chunk; the last of them to arrive
-//      (atomic counter) draws the correction token.
+//      are completed by the row's work-group 0.  For a row rejected with a
+//      dense draft, the row's first G work-groups re-read target and draft
+//      logits of the rejected position, chunk j, j + G, ... each, and
+//      publish 32 sub-block sums of max(0, p_n - q_n) per chunk; the last of
+//      them to arrive (atomic counter) draws the correction token.  With a
+//      truncated draft the row's single work-group forms those sums from the
+//      statistics pass's sub-block sums and the kept list, reading no logits
+//      but the target's at the kept ids, and draws.
 //
 // The final draw is an inverse CDF over a three-level hierarchy: chunk
 // masses (a wave scan), the 32 sub-block sums of the selected chunk, and a
